@@ -1,0 +1,258 @@
+"""Kaczmarz Linear Attention forward pass on MI355X (gfx950): Python binding of libkla.so.
+
+The binding only marshals arguments: it checks tensor placement, dtypes and
+shapes, allocates outputs and the workspace with torch, and calls the C ABI of
+``include/kla.h`` on torch's current HIP stream.  Every step of the computation
+runs in the HIP kernels of ``csrc/``; there is no fallback.  If libkla.so is
+missing the first call raises an error naming the build step.
+
+Functions mirror the C entry points:
+
+* :func:`kla_prefill_chunked` -- chunkwise prefill (q, k, v, g, eta, eps, S0) -> (o, S_T)
+* :func:`kla_decode_step`     -- one decode step (q, k, v, g, eta, eps, S) -> (o, S')
+* :func:`kla_prefill_chunk_stage` -- per-chunk b, G, T (and W, U~) for unit checks
+* :func:`kla_prefill_workspace_bytes`
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["kla_prefill_chunked", "kla_decode_step", "kla_prefill_chunk_stage",
+           "kla_prefill_workspace_bytes", "library_path", "load_library", "CHUNK", "KlaError"]
+
+CHUNK = 64
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkla.so")
+_lib = None
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class KlaError(RuntimeError):
+    """A non-OK kla_status returned by libkla.so."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkla.so (once).  Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()' or "
+            "python gated_delta_rule_kla_amd/build.py)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.kla_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.kla_prefill_workspace_bytes.restype = sz
+    lib.kla_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                        i32, i32, ctypes.c_int, vp, sz, vp]
+    lib.kla_prefill_chunked.restype = ctypes.c_int
+    lib.kla_prefill_chunk_stage.argtypes = [vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, i32,
+                                            i32, i32, i32, i32, ctypes.c_int, vp, sz, vp]
+    lib.kla_prefill_chunk_stage.restype = ctypes.c_int
+    lib.kla_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32,
+                                    ctypes.c_int, vp]
+    lib.kla_decode_step.restype = ctypes.c_int
+    lib.kla_status_string.argtypes = [ctypes.c_int]
+    lib.kla_status_string.restype = ctypes.c_char_p
+    lib.kla_last_error.argtypes = []
+    lib.kla_last_error.restype = ctypes.c_char_p
+    lib.kla_version.argtypes = []
+    lib.kla_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise KlaError(status, f"{lib.kla_status_string(status).decode()}: "
+                               f"{lib.kla_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (HIP) tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def kla_prefill_workspace_bytes(n_seq: int, total_tokens: int, n_heads: int, d_k: int,
+                                d_v: int) -> int:
+    return int(load_library().kla_prefill_workspace_bytes(n_seq, total_tokens, n_heads, d_k, d_v))
+
+
+def _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq):
+    """Accept dense [B, T, H, d] or flat [n_tok, H, d] token-major tensors."""
+    if q.dim() == 4:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens needs flat [n_tok, H, d] inputs")
+        B, T = q.shape[:2]
+        n_seq = B
+        q, k, v = (x.reshape(B * T, *x.shape[2:]) for x in (q, k, v))
+        g, eta = (x.reshape(B * T, x.shape[-1]) for x in (g, eta))
+    elif q.dim() != 3:
+        raise ValueError("q must be [n_tok, H, d_k] or [B, T, H, d_k]")
+    if n_seq is None:
+        n_seq = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    return q, k, v, g, eta, n_seq
+
+
+def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=None,
+                        n_seq=None, *, cu_seqlens_host=None, output_final_state=True, o=None,
+                        S_T=None, workspace=None):
+    """Chunkwise KLA prefill (paper section 4, Eq. (7)-(9); chunk = 64 tokens).
+
+    q, k: [n_tok, H, d_k] or [B, T, H, d_k] (fp32 or bf16); v like q with d_v;
+    g, eta: [n_tok, H] / [B, T, H] fp32; S0: [n_seq, H, d_k, d_v] fp32 or None;
+    cu_seqlens: int32 device [n_seq + 1] for packed sequences, or None (dense;
+    n_seq sequences of equal length).  Returns (o, S_T); S_T is None when
+    output_final_state is False.  Pass S_T=S0 to update the state in place.
+    """
+    shape_v = v.shape
+    q, k, v, g, eta, n_seq = _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq)
+    dev = q.device
+    _need(q, "q", device=dev)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    _need(k, "k", dt, dev)
+    _need(v, "v", dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(eta, "eta", torch.float32, dev)
+    n_tok, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if k.shape != q.shape or v.shape[:2] != (n_tok, H) or g.shape != (n_tok, H) or eta.shape != (n_tok, H):
+        raise ValueError("inconsistent q/k/v/g/eta shapes")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        if cu_seqlens.numel() != n_seq + 1:
+            raise ValueError("cu_seqlens must have n_seq + 1 entries")
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous().cpu()
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, dev)
+        if S0.shape != (n_seq, H, d_k, d_v):
+            raise ValueError(f"S0 must be [{n_seq}, {H}, {d_k}, {d_v}]")
+    if o is None:
+        o = torch.empty((n_tok, H, d_v), dtype=dt, device=dev)
+    else:
+        _need(o, "o", dt, dev)
+    if output_final_state and S_T is None:
+        S_T = torch.empty((n_seq, H, d_k, d_v), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _need(S_T, "S_T", torch.float32, dev)
+    lib = load_library()
+    ws_bytes = int(lib.kla_prefill_workspace_bytes(n_seq, n_tok, H, d_k, d_v))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    host_ptr = None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr())
+    _check(lib.kla_prefill_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S0), _ptr(o), _ptr(S_T),
+        _ptr(cu_seqlens), host_ptr, n_seq, n_tok, H, d_k, d_v, _DTYPES[dt], _ptr(workspace),
+        workspace.numel(), _stream(dev)))
+    return o.reshape(shape_v), S_T
+
+
+def kla_decode_step(q, k, v, g, eta, eps: float, S, *, o=None, S_new=None, inplace=False):
+    """One KLA decode step per sequence (paper Algorithm 1, tokenwise panel).
+
+    q, k: [B, H, d_k]; v: [B, H, d_v] (fp32 or bf16); g, eta: [B, H] fp32;
+    S: [B, H, d_k, d_v] fp32.  Returns (o, S_new); inplace=True writes S' into S.
+    """
+    dev = q.device
+    _need(q, "q", device=dev)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    _need(k, "k", dt, dev)
+    _need(v, "v", dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(eta, "eta", torch.float32, dev)
+    _need(S, "S", torch.float32, dev)
+    B, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if S.shape != (B, H, d_k, d_v) or g.shape != (B, H) or eta.shape != (B, H):
+        raise ValueError("inconsistent decode shapes")
+    if o is None:
+        o = torch.empty((B, H, d_v), dtype=dt, device=dev)
+    if inplace:
+        S_new = S
+    elif S_new is None:
+        S_new = torch.empty_like(S)
+    _need(S_new, "S_new", torch.float32, dev)
+    _check(load_library().kla_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S), _ptr(o), _ptr(S_new),
+        B, H, d_k, d_v, _DTYPES[dt], _stream(dev)))
+    return o, S_new
+
+
+def kla_prefill_chunk_stage(k, v, g, eta, eps: float = 1e-6, cu_seqlens=None, n_seq=None, *,
+                            want_wy=False):
+    """Per-chunk stage of the prefill (b, G, T; optionally W and U~), for unit checks.
+
+    Returns dict(beta [n_tok, H], G [n_tok, H], T [n_chunks, H, 64, 64], W, Ut).
+    """
+    dev = k.device
+    if k.dim() == 4:
+        B, T = k.shape[:2]
+        n_seq = B
+        k, v = (x.reshape(B * T, *x.shape[2:]) for x in (k, v))
+        g, eta = (x.reshape(B * T, x.shape[-1]) for x in (g, eta))
+    dt = k.dtype
+    _need(k, "k", device=dev)
+    _need(v, "v", dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(eta, "eta", torch.float32, dev)
+    n_tok, H, d_k = k.shape
+    d_v = v.shape[-1]
+    if n_seq is None:
+        n_seq = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is None:
+        Tn = n_tok // n_seq
+        n_chunks = n_seq * ((Tn + CHUNK - 1) // CHUNK)
+    else:
+        cu = cu_seqlens.cpu().tolist()
+        n_chunks = sum((cu[i + 1] - cu[i] + CHUNK - 1) // CHUNK for i in range(n_seq))
+    lib = load_library()
+    beta = torch.zeros((n_tok, H), dtype=torch.float32, device=dev)
+    G = torch.zeros((n_tok, H), dtype=torch.float32, device=dev)
+    T = torch.zeros((max(n_chunks, 1), H, CHUNK, CHUNK), dtype=torch.float32, device=dev)
+    W = torch.zeros((n_tok, H, d_k), dtype=torch.float32, device=dev) if want_wy else None
+    Ut = torch.zeros((n_tok, H, d_v), dtype=torch.float32, device=dev) if want_wy else None
+    ws_bytes = int(lib.kla_prefill_workspace_bytes(n_seq, n_tok, H, d_k, d_v))
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    # chunk indices written by the kernel are below the true chunk count, which sizes T
+    _check(lib.kla_prefill_chunk_stage(
+        _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(beta), _ptr(G), _ptr(T), _ptr(W),
+        _ptr(Ut), _ptr(cu_seqlens), None, n_seq, n_tok, H, d_k, d_v, _DTYPES[dt], _ptr(workspace),
+        workspace.numel(), _stream(dev)))
+    return dict(beta=beta, G=G, T=T[:n_chunks], W=W, Ut=Ut)

@@ -1,0 +1,256 @@
+// kla_api.hip -- the extern "C" boundary of libkla.so (declared in include/kla.h).
+//
+// Validates arguments, carves the caller's workspace, and enqueues the kernels
+// on the caller's stream.  Nothing here synchronises with the device or
+// allocates device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kla.h"
+#include "kla_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kla_status fail(kla_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kla_status ok() {
+  g_last_error[0] = '\0';
+  return KLA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool supported_dk(int32_t d) { return d == 64 || d == 128; }
+bool supported_dv(int32_t d) { return d == 64 || d == 128 || d == 256; }
+
+size_t elem_size(kla_dtype dt) { return dt == KLA_DTYPE_BF16 ? 2 : 4; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Workspace layout: [cu: n_seq+1 int32][chunk_off: n_seq+1 int32][G: total*H fp32]
+//                   [T: n_chunks_ub * H * 64 * 64 fp32], each part 256-byte aligned.
+struct WsLayout {
+  size_t off_cu, off_co, off_G, off_T, total;
+};
+
+WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H) {
+  WsLayout w;
+  w.off_cu = 0;
+  w.off_co = align256(w.off_cu + sizeof(int32_t) * (size_t)(n_seq + 1));
+  w.off_G = align256(w.off_co + sizeof(int32_t) * (size_t)(n_seq + 1));
+  w.off_T = align256(w.off_G + sizeof(float) * (size_t)total_tokens * (size_t)H);
+  const int64_t nch = kla::chunk_upper_bound(n_seq, total_tokens);
+  w.total = align256(w.off_T + sizeof(float) * (size_t)nch * (size_t)H * KLA_CHUNK * KLA_CHUNK);
+  return w;
+}
+
+// Checks shared by the prefill entry points.  Returns KLA_OK or an error status.
+kla_status check_prefill_shape(const int32_t *cu_seqlens_host, int32_t n_seq, int32_t total_tokens,
+                               int32_t n_heads, int32_t d_k, int32_t d_v, kla_dtype dtype,
+                               float eps) {
+  if (dtype != KLA_DTYPE_F32 && dtype != KLA_DTYPE_BF16)
+    return fail(KLA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (n_seq <= 0 || total_tokens < 0 || n_heads <= 0)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "need n_seq > 0, total_tokens >= 0, n_heads > 0 (got %d, %d, %d)",
+                n_seq, total_tokens, n_heads);
+  if (n_heads > 65535) return fail(KLA_ERR_INVALID_ARGUMENT, "n_heads > 65535");
+  if (!supported_dk(d_k)) return fail(KLA_ERR_UNSUPPORTED, "d_k = %d not in {64, 128}", d_k);
+  if (!supported_dv(d_v)) return fail(KLA_ERR_UNSUPPORTED, "d_v = %d not in {64, 128, 256}", d_v);
+  if (!(eps >= 0.f) || !isfinite(eps))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if ((int64_t)n_seq * n_heads * (d_v / 32) > 0x7fffffff)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "n_seq * n_heads too large");
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0)
+      return fail(KLA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] must be 0");
+    for (int32_t i = 0; i < n_seq; ++i)
+      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+        return fail(KLA_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %d", i);
+    if (cu_seqlens_host[n_seq] != total_tokens)
+      return fail(KLA_ERR_INVALID_ARGUMENT, "cu_seqlens[n_seq] = %d != total_tokens = %d",
+                  cu_seqlens_host[n_seq], total_tokens);
+  }
+  return KLA_OK;
+}
+
+kla_status check_dense(const int32_t *cu_seqlens, int32_t n_seq, int32_t total_tokens) {
+  if (!cu_seqlens && total_tokens % n_seq != 0)
+    return fail(KLA_ERR_INVALID_ARGUMENT,
+                "dense input needs total_tokens (%d) divisible by n_seq (%d); pass cu_seqlens",
+                total_tokens, n_seq);
+  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  return KLA_OK;
+}
+
+kla::Dtype to_dt(kla_dtype d) { return d == KLA_DTYPE_BF16 ? kla::Dtype::BF16 : kla::Dtype::F32; }
+
+kla_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return KLA_OK;
+  return fail(KLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                                   int32_t d_k, int32_t d_v) {
+  if (n_seq <= 0 || total_tokens < 0 || n_heads <= 0 || !supported_dk(d_k) || !supported_dv(d_v))
+    return 0;
+  return ws_layout(n_seq, total_tokens, n_heads).total;
+}
+
+kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
+                               const float *eta, float eps, const float *S0, void *o,
+                               float *S_T, const int32_t *cu_seqlens,
+                               const int32_t *cu_seqlens_host, int32_t n_seq,
+                               int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                               int32_t d_v, kla_dtype dtype, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  kla_status st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v,
+                                      dtype, eps);
+  if (st != KLA_OK) return st;
+  if (total_tokens > 0 && (!q || !k || !v || !g || !eta || !o))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v, g, eta and o are required");
+  if ((st = check_dense(cu_seqlens, n_seq, total_tokens)) != KLA_OK) return st;
+  const void *ptrs[] = {q, k, v, g, eta, S0, o, S_T, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)total_tokens * n_heads * d_k * es;
+  const size_t nv = (size_t)total_tokens * n_heads * d_v * es;
+  if (overlap(o, nv, q, nq) || overlap(o, nv, k, nq) || overlap(o, nv, v, nv))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "o must not overlap q, k or v");
+  const size_t nS = (size_t)n_seq * n_heads * d_k * d_v * sizeof(float);
+  if (S_T && S_T != S0 && overlap(S_T, nS, S0, nS))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "S_T may equal S0 but must not partially overlap it");
+  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+
+  char *ws = static_cast<char *>(workspace);
+  kla::SeqTables tabs{reinterpret_cast<int32_t *>(ws + w.off_cu),
+                      reinterpret_cast<int32_t *>(ws + w.off_co)};
+  float *G = reinterpret_cast<float *>(ws + w.off_G);
+  float *T = reinterpret_cast<float *>(ws + w.off_T);
+  const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear any stale error from unrelated work
+  const kla::Dtype dt = to_dt(dtype);
+  if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, tabs, s), "plan")) != KLA_OK)
+    return st;
+  if ((st = hip_status(kla::launch_prep(dt, d_k, k, g, eta, eps, tabs, n_seq, nch_ub, n_heads, G,
+                                        nullptr, T, s), "prep")) != KLA_OK)
+    return st;
+  if ((st = hip_status(kla::launch_scan(dt, d_k, d_v, q, k, v, G, T, S0, o, S_T, tabs, n_seq,
+                                        n_heads, s), "scan")) != KLA_OK)
+    return st;
+  return ok();
+}
+
+kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
+                                   const float *eta, float eps, float *beta, float *G,
+                                   float *T, float *W, float *Ut, const int32_t *cu_seqlens,
+                                   const int32_t *cu_seqlens_host, int32_t n_seq,
+                                   int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                                   int32_t d_v, kla_dtype dtype, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  kla_status st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v,
+                                      dtype, eps);
+  if (st != KLA_OK) return st;
+  if (total_tokens > 0 && (!k || !g || !eta || !T || (Ut && !v)))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "k, g, eta, T (and v when Ut is requested) are required");
+  if ((st = check_dense(cu_seqlens, n_seq, total_tokens)) != KLA_OK) return st;
+  const void *ptrs[] = {k, v, g, eta, beta, G, T, W, Ut, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads);
+  // this entry point writes G into the caller's buffer when given, else into the workspace
+  if (!workspace || workspace_bytes < w.total)
+    return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  char *ws = static_cast<char *>(workspace);
+  kla::SeqTables tabs{reinterpret_cast<int32_t *>(ws + w.off_cu),
+                      reinterpret_cast<int32_t *>(ws + w.off_co)};
+  float *Gbuf = G ? G : reinterpret_cast<float *>(ws + w.off_G);
+  const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const kla::Dtype dt = to_dt(dtype);
+  if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, tabs, s), "plan")) != KLA_OK)
+    return st;
+  if ((st = hip_status(kla::launch_prep(dt, d_k, k, g, eta, eps, tabs, n_seq, nch_ub, n_heads,
+                                        Gbuf, beta, T, s), "prep")) != KLA_OK)
+    return st;
+  if ((st = hip_status(kla::launch_wy(dt, d_k, d_v, k, v, Gbuf, T, tabs, n_seq, nch_ub, n_heads,
+                                      W, Ut, s), "wy")) != KLA_OK)
+    return st;
+  return ok();
+}
+
+kla_status kla_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *eta, float eps, const float *S, void *o,
+                           float *S_new, int32_t batch, int32_t n_heads, int32_t d_k,
+                           int32_t d_v, kla_dtype dtype, void *stream) {
+  if (dtype != KLA_DTYPE_F32 && dtype != KLA_DTYPE_BF16)
+    return fail(KLA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (batch < 0 || n_heads <= 0)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "need batch >= 0 and n_heads > 0");
+  if (!supported_dk(d_k)) return fail(KLA_ERR_UNSUPPORTED, "d_k = %d not in {64, 128}", d_k);
+  if (!supported_dv(d_v)) return fail(KLA_ERR_UNSUPPORTED, "d_v = %d not in {64, 128, 256}", d_v);
+  if (!(eps >= 0.f) || !isfinite(eps))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if ((int64_t)batch * n_heads > 0x7fffffff)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "batch * n_heads too large");
+  if (!q || !k || !v || !g || !eta || !S || !o || !S_new)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v, g, eta, S, o and S_new are required");
+  const void *ptrs[] = {q, k, v, g, eta, S, o, S_new};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  const size_t nS = (size_t)batch * n_heads * d_k * d_v * sizeof(float);
+  if (S_new != S && overlap(S_new, nS, S, nS))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "S_new may equal S but must not partially overlap it");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  kla_status st = hip_status(kla::launch_decode(to_dt(dtype), d_k, d_v, q, k, v, g, eta, eps, S, o,
+                                                S_new, batch, n_heads, s), "decode");
+  if (st != KLA_OK) return st;
+  return ok();
+}
+
+const char *kla_status_string(kla_status status) {
+  switch (status) {
+    case KLA_OK: return "KLA_OK";
+    case KLA_ERR_INVALID_ARGUMENT: return "KLA_ERR_INVALID_ARGUMENT: invalid argument";
+    case KLA_ERR_UNSUPPORTED: return "KLA_ERR_UNSUPPORTED: unsupported size or dtype";
+    case KLA_ERR_WORKSPACE: return "KLA_ERR_WORKSPACE: workspace missing or too small";
+    case KLA_ERR_HIP: return "KLA_ERR_HIP: HIP launch failed";
+  }
+  return "unknown kla_status";
+}
+
+const char *kla_last_error(void) { return g_last_error; }
+
+int32_t kla_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// kla_device.h -- device helpers shared by the gfx950 KLA kernels.
+//
+// Matrix-core convention (CDNA3/CDNA4 16x16 MFMA layouts, 64-lane wavefront):
+// a "k-step" contracts 32 values of the inner dimension.  Lane l = r + 16*kg
+// (r = l % 16, kg = l / 16) supplies
+//   A fragment: A[r][8*kg + s], s = 0..7     (row r of a 16 x 32 tile)
+//   B fragment: B[8*kg + s][r], s = 0..7     (column r of a 32 x 16 tile)
+// and receives the 16 x 16 fp32 result as
+//   D fragment: D[4*kg + i][r], i = 0..3.
+// bf16 operands use one v_mfma_f32_16x16x32_bf16 per k-step; fp32 operands use
+// eight v_mfma_f32_16x16x4_f32, one per s.  Both sides of a product always use
+// the same (kg, s) -> k assignment, so the contraction covers each k exactly once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kla {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kChunk = 64;
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- element types
+template <typename T> struct Frag;
+template <> struct Frag<__bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// float -> bf16 with round-to-nearest-even (NaN stays NaN)
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) {
+  return static_cast<__bf16>(x);
+}
+
+// ---------------------------------------------------------------- MFMA k-step
+__device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const f32x8 &a, const f32x8 &b, f32x4 c) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+
+// ---------------------------------------------------------------- fragment loads
+// 8 consecutive elements (16 B for bf16, 32 B for fp32) starting at p.
+template <typename T> __device__ __forceinline__ typename Frag<T>::type load8(const T *p);
+template <> __device__ __forceinline__ bf16x8 load8<__bf16>(const __bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+template <> __device__ __forceinline__ f32x8 load8<float>(const float *p) {
+  const f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 4);
+  f32x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// 8 consecutive fp32 values converted to the operand type T.
+template <typename T> __device__ __forceinline__ typename Frag<T>::type load8_cvt(const float *p);
+template <> __device__ __forceinline__ f32x8 load8_cvt<float>(const float *p) {
+  return load8<float>(p);
+}
+template <> __device__ __forceinline__ bf16x8 load8_cvt<__bf16>(const float *p) {
+  const f32x8 x = load8<float>(p);
+  bf16x8 r;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) r[s] = static_cast<__bf16>(x[s]);
+  return r;
+}
+
+template <typename T> __device__ __forceinline__ typename Frag<T>::type zero8() {
+  typename Frag<T>::type r;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) r[s] = from_f32<T>(0.0f);
+  return r;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+}  // namespace kla

@@ -1,0 +1,48 @@
+// kla_launch.h -- host-side launchers of the gfx950 KLA kernels (internal to libkla.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kla {
+
+enum class Dtype { F32 = 0, BF16 = 1 };
+
+// Sequence tables the plan kernel writes into the workspace:
+//   cu[n]        sanitised token offset of sequence n (n = 0..n_seq)
+//   chunk_off[n] index of sequence n's first chunk; chunk_off[n_seq] = chunk count
+struct SeqTables {
+  int32_t *cu;
+  int32_t *chunk_off;
+};
+
+// Upper bound on the number of 64-token chunks for any packing of these totals.
+inline int64_t chunk_upper_bound(int64_t n_seq, int64_t total_tokens) {
+  return (total_tokens + 63) / 64 + n_seq;
+}
+
+hipError_t launch_plan(const int32_t *cu_in, int32_t n_seq, int32_t total_tokens, SeqTables t,
+                       hipStream_t stream);
+
+// a1 + a2: b, G, Gram, L, T = (I + L)^{-1} Diag(b) per chunk-head.
+hipError_t launch_prep(Dtype dt, int d_k, const void *k, const float *g, const float *eta,
+                       float eps, SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
+                       float *G_out, float *beta_out, float *T_out, hipStream_t stream);
+
+// Optional WY factors W = T Diag(exp G) K and U~ = T V (unit-check path).
+hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, const float *G,
+                     const float *T, SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
+                     float *W, float *Ut, hipStream_t stream);
+
+// a3 + a4: sequential chunk scan with the output fused in.
+hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
+                       const float *G, const float *T, const float *S0, void *o, float *S_T,
+                       SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream);
+
+// a5: one decode step.
+hipError_t launch_decode(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
+                         const float *g, const float *eta, float eps, const float *S, void *o,
+                         float *S_new, int32_t batch, int32_t H, hipStream_t stream);
+
+}  // namespace kla

@@ -1,0 +1,165 @@
+/*
+ * kla.h -- C ABI of the MI355X (gfx950) Kaczmarz Linear Attention forward pass.
+ *
+ * The operation (paper "Kaczmarz Linear Attention", arXiv 2605.08587) is the
+ * gated delta-rule recurrence that first forgets and then projects, per
+ * (sequence, head), in the row-vector convention (state S is d_k x d_v, keys
+ * and queries are 1 x d_k rows, values 1 x d_v rows):
+ *
+ *   a_t = exp(g_t)                                 (g_t is a log-decay, <= 0)
+ *   b_t = eta_t / (||k_t||^2 + eps)                Eq. (3); b_t = 0 if the
+ *                                                  denominator is exactly 0
+ *   S_t = a_t S_{t-1} + b_t k_t^T (v_t - a_t k_t S_{t-1})
+ *                                                  Algorithm 1, tokenwise panel
+ *   o_t = q_t S_t                                  readout on the q passed in
+ *                                                  (the 1/||q_t|| of section 3.3
+ *                                                  is left to the caller)
+ *
+ * kla_prefill_chunked evaluates it with the chunkwise solve of section 4
+ * (Proposition 3, Eq. (7); Proposition 4, Eq. (8)-(9)) in chunks of
+ * KLA_CHUNK tokens; kla_decode_step applies one tokenwise step.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or retains them.  Tensors are dense, row-major,
+ *     with the last named dimension fastest, base addresses 16-byte aligned.
+ *   - q, k, v, o use the element type `dtype` (fp32 or bf16); g, eta, S0, S_T,
+ *     S and S_new are always fp32.  Accumulation and the state are fp32.
+ *   - Calls are asynchronous: they validate, enqueue kernels on `stream` (a
+ *     hipStream_t; NULL = the legacy default stream) and return.  Buffers must
+ *     stay alive until the stream has passed the call.
+ *   - On any non-OK status nothing has been enqueued (except KLA_ERR_HIP, which
+ *     reports a failed launch).  kla_last_error() gives a human-readable
+ *     reason for the last failure on the calling thread.
+ *   - Preconditions that are documented but not checked (checking would cost a
+ *     pass over the data): g finite and <= 0, eta finite (normally in (0, 1]),
+ *     no NaN/Inf in q, k, v, S0 (NaN propagates).
+ *   - The library is stateless and thread-safe; concurrent calls on different
+ *     streams are independent provided their buffers do not overlap.
+ */
+#ifndef KLA_H_
+#define KLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Tokens per chunk of the chunkwise solve (fixed). */
+#define KLA_CHUNK 64
+
+typedef enum kla_status {
+  KLA_OK = 0,
+  KLA_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad size, eps < 0 or
+                                   non-finite, misaligned base, bad cu_seqlens */
+  KLA_ERR_UNSUPPORTED = 2,      /* d_k not in {64, 128}, d_v not in {64, 128, 256},
+                                   or an unknown dtype */
+  KLA_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than required */
+  KLA_ERR_HIP = 4               /* a kernel launch failed */
+} kla_status;
+
+typedef enum kla_dtype {
+  KLA_DTYPE_F32 = 0,  /* IEEE fp32 */
+  KLA_DTYPE_BF16 = 1  /* bfloat16; outputs rounded to nearest even */
+} kla_dtype;
+
+/* Bytes of device workspace kla_prefill_chunked needs for this problem size
+ * (an upper bound valid for any cu_seqlens with these totals).  Returns 0 for
+ * an unsupported or invalid size. */
+size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                                   int32_t d_k, int32_t d_v);
+
+/*
+ * Chunkwise prefill: (q, k, v, g, eta, eps, S0) -> (o, S_T).
+ * Paper section 4, Algorithm 1 chunkwise panel, Eq. (7)-(9); chunks of
+ * KLA_CHUNK tokens restart at every sequence start, the last chunk of a
+ * sequence may be short, and the outgoing state of one chunk is the incoming
+ * state of the next.
+ *
+ *   q, k        [total_tokens, n_heads, d_k]   dtype
+ *   v           [total_tokens, n_heads, d_v]   dtype
+ *   g, eta      [total_tokens, n_heads]        fp32  (log-decay, relaxation)
+ *   eps         >= 0 and finite (the pages use 1e-6)
+ *   S0          [n_seq, n_heads, d_k, d_v] fp32, or NULL for all-zero states
+ *   o           [total_tokens, n_heads, d_v]   dtype (written)
+ *   S_T         [n_seq, n_heads, d_k, d_v] fp32, or NULL (not stored);
+ *               may be the same pointer as S0 (in-place state update)
+ *   cu_seqlens  device int32 [n_seq + 1] token offsets of packed sequences
+ *               (cu_seqlens[0] = 0, non-decreasing, cu_seqlens[n_seq] =
+ *               total_tokens), or NULL for dense input where every sequence
+ *               has total_tokens / n_seq tokens (must divide evenly).
+ *               Device offsets are not validated; out-of-range values are
+ *               clamped into [0, total_tokens] and made non-decreasing, so a
+ *               bad table gives wrong results but no out-of-bounds access.
+ *   cu_seqlens_host  optional host copy of cu_seqlens (NULL allowed); when
+ *               given it is validated and a bad table is rejected.
+ *   workspace   device buffer of at least kla_prefill_workspace_bytes(...)
+ *               bytes, 256-byte aligned; contents are scratch.
+ * Zero-length sequences are allowed (their S_T is S0, or zeros).  When
+ * total_tokens is 0 the token buffers q, k, v, g, eta and o may be NULL.
+ * q, k, v, g, eta and o must not overlap each other or the workspace.
+ */
+kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
+                               const float *eta, float eps, const float *S0, void *o,
+                               float *S_T, const int32_t *cu_seqlens,
+                               const int32_t *cu_seqlens_host, int32_t n_seq,
+                               int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                               int32_t d_v, kla_dtype dtype, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step per sequence: (q, k, v, g, eta, eps, S) -> (o, S').
+ * Paper Algorithm 1 tokenwise panel steps 2-6 (with Eq. (3)), evaluated with
+ * a single read and a single write of S:  r = k S, p = q S,
+ * e = v - a r, S' = a S + b k^T e, o = a p + b (q . k) e.
+ *
+ *   q, k     [batch, n_heads, d_k]  dtype      v, o  [batch, n_heads, d_v]  dtype
+ *   g, eta   [batch, n_heads]       fp32       eps   >= 0 and finite
+ *   S        [batch, n_heads, d_k, d_v] fp32 (read)
+ *   S_new    [batch, n_heads, d_k, d_v] fp32 (written); may equal S
+ */
+kla_status kla_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *eta, float eps, const float *S, void *o,
+                           float *S_new, int32_t batch, int32_t n_heads, int32_t d_k,
+                           int32_t d_v, kla_dtype dtype, void *stream);
+
+/*
+ * Per-chunk stage only (unit checks of the prefill's first kernel): the
+ * Kaczmarz step b and chunk-local inclusive log-decay G of every token, and
+ * per chunk T = (I + L)^{-1} Diag(b) with L = Diag(b)(A^- o K K^T) strictly
+ * lower triangular (Proposition 3 / Appendix B.2), so that the chunk's
+ * U = T (V - Diag(exp G) K S0).  Optionally also the WY factors
+ * W = T Diag(exp G) K and U~ = T V (then U = U~ - W S0).
+ *
+ *   beta, G  [total_tokens, n_heads] fp32 (written; either may be NULL)
+ *   T        [n_chunks, n_heads, KLA_CHUNK, KLA_CHUNK] fp32 (written), chunks
+ *            numbered sequence by sequence; n_chunks = sum_n ceil(T_n / 64).
+ *            Rows/columns past a short chunk's end are zero.
+ *   W        [total_tokens, n_heads, d_k] fp32 or NULL
+ *   Ut       [total_tokens, n_heads, d_v] fp32 or NULL
+ * Other arguments as for kla_prefill_chunked (v may be NULL if Ut is NULL).
+ */
+kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
+                                   const float *eta, float eps, float *beta, float *G,
+                                   float *T, float *W, float *Ut, const int32_t *cu_seqlens,
+                                   const int32_t *cu_seqlens_host, int32_t n_seq,
+                                   int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                                   int32_t d_v, kla_dtype dtype, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *kla_status_string(kla_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *kla_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t kla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLA_H_ */

@@ -29,12 +29,12 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile ``kla_oracle.c`` with gcc (-O2, OpenMP) into ``libkla_oracle.so``."""
+    """Compile ``kla_oracle.c`` with gcc (-O3, no fast-math, OpenMP) into ``libkla_oracle.so``."""
     global _lib
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+            ["gcc", "-O3", "-std=c99", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
         _lib = None
     return _LIB

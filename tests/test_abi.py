@@ -1,0 +1,134 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every symbol that
+include/kla.h declares, and rejects bad arguments with the documented status before any
+HIP call is made (validation happens on the host before the first launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_kla_amd as kla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kla.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kla_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kla.load_library()
+
+
+def test_header_declares_the_two_calls():
+    names = declared_functions()
+    assert "kla_prefill_chunked" in names and "kla_decode_step" in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", kla.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(kla_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for st in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR):
+        assert lib.kla_status_string(st).decode().startswith("KLA_")
+    assert lib.kla_version() >= 100
+
+
+def test_workspace_bytes_formula(lib):
+    # cu + chunk offsets + G (fp32 per token-head) + T (64x64 fp32 per chunk-head upper bound)
+    n_seq, n_tok, H = 4, 16384, 16
+    nb = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, 128, 128)
+    nch = (n_tok + 63) // 64 + n_seq
+    assert nb >= 4 * n_tok * H + 4 * nch * H * 64 * 64
+    assert nb % 256 == 0
+    assert kla.kla_prefill_workspace_bytes(4, 100, 16, 96, 128) == 0
+    assert kla.kla_prefill_workspace_bytes(0, 100, 16, 128, 128) == 0
+
+
+FAKE = 1 << 32  # 16-byte aligned non-NULL addresses 4 GiB apart; never dereferenced on error paths
+
+
+def _prefill(lib, **over):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, eta=FAKE * 5, eps=1e-6, S0=None, o=FAKE * 6,
+             S_T=None, cu=None, cu_host=None, n_seq=2, total=256, H=4, dk=128, dv=128, dtype=BF16,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return lib.kla_prefill_chunked(a["q"], a["k"], a["v"], a["g"], a["eta"], a["eps"], a["S0"],
+                                   a["o"], a["S_T"], a["cu"], a["cu_host"], a["n_seq"], a["total"],
+                                   a["H"], a["dk"], a["dv"], a["dtype"], a["ws"], a["ws_bytes"],
+                                   a["stream"])
+
+
+def _decode(lib, **over):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, eta=FAKE * 5, eps=1e-6, S=FAKE * 7,
+             o=FAKE * 6, S_new=FAKE * 7, B=4, H=2, dk=128, dv=128, dtype=BF16, stream=None)
+    a.update(over)
+    return lib.kla_decode_step(a["q"], a["k"], a["v"], a["g"], a["eta"], a["eps"], a["S"], a["o"],
+                               a["S_new"], a["B"], a["H"], a["dk"], a["dv"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(n_seq=0), INVALID),
+    (dict(H=0), INVALID),
+    (dict(total=-1), INVALID),
+    (dict(eps=-1.0), INVALID),
+    (dict(eps=float("inf")), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(dk=96), UNSUPPORTED),
+    (dict(dv=512), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(total=255), INVALID),          # dense: not divisible by n_seq
+    (dict(q=FAKE + 4), INVALID),         # misaligned
+    (dict(o=FAKE), INVALID),             # o overlaps q
+    (dict(ws=None), WORKSPACE),
+    (dict(ws=FAKE * 64, ws_bytes=16), WORKSPACE),
+])
+def test_prefill_argument_errors(lib, over, status):
+    assert _prefill(lib, **over) == status
+    assert lib.kla_last_error().decode() != ""
+
+
+def test_prefill_host_cu_seqlens_validated(lib):
+    bad = [(0, 100, 90), (1, 100, 256), (0, 100, 200)]
+    for cu in bad:
+        arr = (ctypes.c_int32 * 3)(*cu)
+        st = _prefill(lib, cu=FAKE * 8, cu_host=ctypes.cast(arr, ctypes.c_void_p), total=256)
+        assert st == INVALID, cu
+    # a good table gets past the host checks and stops at the missing workspace
+    arr = (ctypes.c_int32 * 3)(0, 100, 256)
+    assert _prefill(lib, cu=FAKE * 8, cu_host=ctypes.cast(arr, ctypes.c_void_p)) == WORKSPACE
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(S=None), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(dk=32), UNSUPPORTED),
+    (dict(dv=100), UNSUPPORTED),
+    (dict(eps=-0.5), INVALID),
+    (dict(dtype=3), UNSUPPORTED),
+    (dict(S_new=FAKE * 7 + 16), INVALID),  # partial overlap with S
+    (dict(v=FAKE * 3 + 2), INVALID),
+])
+def test_decode_argument_errors(lib, over, status):
+    assert _decode(lib, **over) == status
+
+
+def test_last_error_is_thread_local_text(lib):
+    _decode(lib, dk=32)
+    assert "d_k" in lib.kla_last_error().decode()

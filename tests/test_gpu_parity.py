@@ -1,0 +1,350 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on seeded inputs.
+
+Bars (per tensor, err = max|x - y| / max|y| with y the oracle):
+  fp32 inputs: 1e-4;  bf16 inputs with fp32 accumulation and state: 2e-2.
+Both o and the final state are checked.  Sizes span several chunks and a ragged
+tail, packed sequences with empty and one-token members, the workloads' full
+sizes (sampled where the oracle would take too long), and the method's
+degenerate cases.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kla_inputs as ki
+import oracle
+from oracle import chunkwise
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+DEV = "cuda"
+
+
+def err(x, y):
+    x = x.detach().double().cpu().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    assert x.shape == y.shape, (x.shape, y.shape)
+    assert np.all(np.isfinite(x)), "non-finite values in device output"
+    return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
+
+
+@pytest.fixture(scope="module")
+def kla():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import gated_delta_rule_kla_amd as m
+    m.load_library()
+    oracle.build(force=False)
+    return m
+
+
+def to_dev(inp):
+    out = {}
+    for key, val in inp.items():
+        out[key] = val.to(DEV) if isinstance(val, torch.Tensor) else val
+    return out
+
+
+def run_prefill(kla, d, S0=True):
+    o, ST = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                    S0=d["S0"] if S0 else None, cu_seqlens=d["cu_seqlens"],
+                                    n_seq=d["n_seq"])
+    torch.cuda.synchronize()
+    return o, ST
+
+
+def oracle_prefill(d, S0=True):
+    cu = d["cu_seqlens"]
+    if cu is None:
+        T = d["q"].shape[0] // d["n_seq"]
+        cu = np.arange(d["n_seq"] + 1) * T
+    else:
+        cu = cu.cpu().numpy()
+    return oracle.prefill(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                          S0=d["S0"] if S0 else None, cu_seqlens=cu)
+
+
+# ------------------------------------------------------------------------------------ decode
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 256), (64, 256)])
+def test_decode_step_parity(kla, dtype, dk, dv):
+    w = ki.Workload(90, "decode-unit", 6, 3, dk, dv, dtype, T=1, s0_var=0.05, decode_steps=5)
+    d = to_dev(ki.decode_inputs(w))
+    S = d["S"].clone()
+    So = d["S"].double().cpu().numpy()
+    for t in range(5):
+        o, S = kla.kla_decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t],
+                                   d["eps"], S, inplace=(t % 2 == 1))
+        oo, So = oracle.decode(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t], d["eps"], So)
+        torch.cuda.synchronize()
+        assert err(o, oo) < TOL[dtype], t
+        assert err(S, So) < TOL[dtype], t
+
+
+def test_decode_full_batch(kla):
+    """Decode workload: B=256, H=16, d=128 from an N(0, 0.05) state, 4 steps, in place."""
+    w = ki.WORKLOADS[3]
+    d = to_dev(ki.decode_inputs(w, steps=4))
+    S = d["S"].clone()
+    So = d["S"].double().cpu().numpy()
+    for t in range(4):
+        o, _ = kla.kla_decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t],
+                                   d["eps"], S, inplace=True)
+        oo, So = oracle.decode(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t], d["eps"], So)
+        torch.cuda.synchronize()
+        assert err(o, oo) < 2e-2
+        assert err(S, So) < 2e-2
+
+
+# ------------------------------------------------------------------------------------ prefill
+def test_prefill_tiny_fp32(kla):
+    """Workload 0 (fp32, T=256, d=64) at the 1e-4 bar."""
+    d = to_dev(ki.prefill_inputs(0))
+    o, ST = run_prefill(kla, d)
+    oo, So = oracle_prefill(d)
+    assert err(o, oo) < 1e-4
+    assert err(ST, So) < 1e-4
+
+
+def test_prefill_tiny_fp32_hard_projection(kla):
+    """Workload 0, hard variant (eta=1, g=0, eps=0, q := k): every o_t must be v_t
+    (Theorem 1: k_t S_t = v_t), and the whole output must match the oracle."""
+    d = to_dev(ki.hard_variant(ki.prefill_inputs(0)))
+    o, ST = run_prefill(kla, d)
+    oo, So = oracle_prefill(d)
+    assert err(oo, d["v"].double().cpu().numpy()) < 1e-9   # the oracle itself
+    assert err(o, d["v"].double().cpu().numpy()) < 1e-4
+    assert err(o, oo) < 1e-4
+    # the state itself: ill-conditioned without decay (C = d_k = 64 projections per chunk)
+    assert err(ST, So) < 1e-3
+
+
+@pytest.mark.parametrize("n_seq,T,H,dk,dv", [
+    (2, 200, 3, 128, 128),   # 3 full chunks + ragged tail of 8
+    (1, 64, 2, 64, 64),      # exactly one chunk
+    (3, 130, 2, 128, 256),   # wide heads, tail of 2
+    (1, 1, 1, 128, 128),     # a single token
+    (2, 127, 2, 64, 128),
+])
+def test_prefill_bf16_shapes(kla, n_seq, T, H, dk, dv):
+    w = ki.Workload(91, "unit", n_seq, H, dk, dv, torch.bfloat16, T=T, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    o, ST = run_prefill(kla, d)
+    oo, So = oracle_prefill(d)
+    assert err(o, oo) < 2e-2
+    assert err(ST, So) < 2e-2
+
+
+@pytest.mark.parametrize("n_seq,T,H,dk,dv", [(2, 200, 2, 128, 128), (1, 150, 1, 64, 256)])
+def test_prefill_fp32_shapes(kla, n_seq, T, H, dk, dv):
+    w = ki.Workload(92, "unit", n_seq, H, dk, dv, torch.float32, T=T, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    o, ST = run_prefill(kla, d)
+    oo, So = oracle_prefill(d)
+    assert err(o, oo) < 1e-4
+    assert err(ST, So) < 1e-4
+
+
+def test_prefill_packed_ragged(kla):
+    """Packed sequences with empty, one-token, chunk-edge and multi-chunk members, strong
+    decay and 5% near-zero keys (the eps guard)."""
+    lens = [1, 0, 63, 64, 65, 200, 0, 129]
+    w = ki.Workload(93, "packed-unit", len(lens), 2, 128, 256, torch.bfloat16, lens=tuple(lens),
+                    g_low=-2.0, tiny_key_frac=0.05, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    o, ST = run_prefill(kla, d)
+    oo, So = oracle_prefill(d)
+    assert err(o, oo) < 2e-2
+    assert err(ST, So) < 2e-2
+    # empty sequences keep their state
+    assert torch.equal(ST[1], d["S0"][1]) and torch.equal(ST[6], d["S0"][6])
+
+
+def test_prefill_layer_workload_full(kla):
+    """Workload 1 (B=4, H=16, T=4096, d=128, bf16, random S0) at full size, every output."""
+    d = to_dev(ki.prefill_inputs(1))
+    o, ST = run_prefill(kla, d)
+    oo, So = oracle_prefill(d)
+    assert err(o, oo) < 2e-2
+    assert err(ST, So) < 2e-2
+
+
+def test_prefill_long_context_full(kla):
+    """Workload 2 (T=65536, H=16, bf16): o on the first 4096 tokens, the last chunk, and S_T."""
+    d = to_dev(ki.prefill_inputs(2))
+    o, ST = run_prefill(kla, d)
+    oo, So = oracle_prefill(d)
+    assert err(o[:4096], oo[:4096]) < 2e-2
+    assert err(o[-64:], oo[-64:]) < 2e-2
+    assert err(ST, So) < 2e-2
+
+
+def test_packed_workload_sampled_with_decode(kla):
+    """Workload 4 (16 packed sequences of 1024..16384 tokens, H=8, d_v=256, g ~ U(-2,0),
+    tiny keys) on the device in full; the oracle checks three sampled sequences, then 8 of
+    the 128 decode steps that continue from the prefill state."""
+    d = to_dev(ki.prefill_inputs(4))
+    o, ST = run_prefill(kla, d, S0=False)
+    cu = d["cu_seqlens"].cpu().numpy()
+    dd = to_dev(ki.decode_inputs(4, steps=8, S=ST))
+    S = ST.clone()
+    outs = []
+    for t in range(8):
+        od, S = kla.kla_decode_step(dd["q"][t], dd["k"][t], dd["v"][t], dd["g"][t], dd["eta"][t],
+                                    dd["eps"], S, inplace=True)
+        outs.append(od.clone())
+    torch.cuda.synchronize()
+    for n in (0, 7, 15):
+        a, b = int(cu[n]), int(cu[n + 1])
+        oo, So = oracle.prefill(d["q"][a:b], d["k"][a:b], d["v"][a:b], d["g"][a:b], d["eta"][a:b],
+                                d["eps"])
+        assert err(o[a:b], oo) < 2e-2, n
+        assert err(ST[n], So[0]) < 2e-2, n
+        Sd = So
+        for t in range(8):
+            od, Sd = oracle.decode(dd["q"][t][n:n + 1], dd["k"][t][n:n + 1], dd["v"][t][n:n + 1],
+                                   dd["g"][t][n:n + 1], dd["eta"][t][n:n + 1], dd["eps"], Sd)
+            assert err(outs[t][n:n + 1], od) < 2e-2, (n, t)
+        assert err(S[n], Sd[0]) < 2e-2, n
+
+
+# ------------------------------------------------------------------------------------ invariants
+def test_one_hot_keys_long_context_closed_form(kla):
+    """Keys c e_i (exact in bf16): every slot is an independent relaxed update, so the
+    state after 65536 tokens has a closed form (no oracle run needed at this length)."""
+    T, dk, dv = 65536, 128, 128
+    gen = torch.Generator().manual_seed(7)
+    slots = torch.randint(0, dk, (T,), generator=gen)
+    c = torch.tensor([0.5, 1.0, 2.0, 4.0])[torch.randint(0, 4, (T,), generator=gen)]
+    k = torch.zeros(T, 1, dk)
+    k[torch.arange(T), 0, slots] = c
+    v = torch.randn(T, 1, dv, generator=gen).to(torch.bfloat16)
+    q = torch.randn(T, 1, dk, generator=gen).to(torch.bfloat16)
+    eta = torch.rand(T, 1, generator=gen) * 0.9 + 0.1
+    g = -0.01 * torch.rand(T, 1, generator=gen)
+    eps = 1e-6
+    d = dict(q=q, k=k.to(torch.bfloat16), v=v, g=g, eta=eta, eps=eps, S0=None, cu_seqlens=None,
+             n_seq=1)
+    o, ST = run_prefill(kla, to_dev(d), S0=False)
+    X = np.zeros((dk, dv))
+    vv, gg, ee = v[:, 0].double().numpy(), g[:, 0].double().numpy(), eta[:, 0].double().numpy()
+    ss, cc = slots.numpy(), c.double().numpy()
+    for t in range(T):
+        X *= math.exp(gg[t])
+        rho = ee[t] * cc[t] ** 2 / (cc[t] ** 2 + eps)
+        X[ss[t]] = (1 - rho) * X[ss[t]] + rho * vv[t] / cc[t]
+    assert err(ST[0, 0], X) < 2e-2
+
+
+def test_hard_projection_bf16_reads_back_values(kla):
+    """eta = 1, g = 0, eps = 0 and q := k on bf16 inputs: o_t = v_t (Theorem 1)."""
+    w = ki.Workload(94, "unit", 1, 4, 128, 128, torch.bfloat16, T=300)
+    d = to_dev(ki.hard_variant(ki.prefill_inputs(w)))
+    o, _ = run_prefill(kla, d, S0=False)
+    assert err(o, d["v"].double().cpu().numpy()) < 2e-2
+
+
+def test_split_resume_and_prefill_decode_chain(kla):
+    """prefill(T) == prefill(T1) + prefill(rest, S0 = S_T1) for a split inside a chunk, and
+    prefill(T) + m decode steps == prefill(T + m)."""
+    w = ki.Workload(95, "unit", 1, 4, 128, 128, torch.bfloat16, T=300, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    o, ST = run_prefill(kla, d)
+    sl = lambda x, a, b: x[a:b].contiguous()
+    o1, S1 = kla.kla_prefill_chunked(sl(d["q"], 0, 101), sl(d["k"], 0, 101), sl(d["v"], 0, 101),
+                                     sl(d["g"], 0, 101), sl(d["eta"], 0, 101), d["eps"], S0=d["S0"])
+    o2, S2 = kla.kla_prefill_chunked(sl(d["q"], 101, 300), sl(d["k"], 101, 300),
+                                     sl(d["v"], 101, 300), sl(d["g"], 101, 300),
+                                     sl(d["eta"], 101, 300), d["eps"], S0=S1)
+    ref = lambda x: x.double().cpu().numpy()
+    assert err(torch.cat([o1, o2]), ref(o)) < 2e-2
+    assert err(S2, ref(ST)) < 2e-2
+    o3, S3 = kla.kla_prefill_chunked(sl(d["q"], 0, 290), sl(d["k"], 0, 290), sl(d["v"], 0, 290),
+                                     sl(d["g"], 0, 290), sl(d["eta"], 0, 290), d["eps"], S0=d["S0"])
+    for t in range(290, 300):
+        od, S3 = kla.kla_decode_step(d["q"][t:t + 1], d["k"][t:t + 1], d["v"][t:t + 1],
+                                     d["g"][t:t + 1], d["eta"][t:t + 1], d["eps"], S3, inplace=True)
+        assert err(od, ref(o[t:t + 1])) < 2e-2
+    assert err(S3, ref(ST)) < 2e-2
+
+
+def test_packed_equals_per_sequence_and_deterministic(kla):
+    lens = [70, 0, 129, 5]
+    w = ki.Workload(96, "unit", 4, 2, 128, 128, torch.bfloat16, lens=tuple(lens), s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    o, ST = run_prefill(kla, d)
+    o_again, ST_again = run_prefill(kla, d)
+    assert torch.equal(o, o_again) and torch.equal(ST, ST_again)  # run-to-run bitwise
+    cu = d["cu_seqlens"].cpu().tolist()
+    for n in range(4):
+        a, b = cu[n], cu[n + 1]
+        if a == b:
+            continue
+        on, Sn = kla.kla_prefill_chunked(d["q"][a:b].contiguous(), d["k"][a:b].contiguous(),
+                                         d["v"][a:b].contiguous(), d["g"][a:b].contiguous(),
+                                         d["eta"][a:b].contiguous(), d["eps"],
+                                         S0=d["S0"][n:n + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(on, o[a:b]) and torch.equal(Sn[0], ST[n])
+
+
+def test_in_place_state_and_null_state(kla):
+    w = ki.Workload(97, "unit", 2, 2, 64, 64, torch.float32, T=100, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    o_ref, ST_ref = run_prefill(kla, d)
+    S = d["S0"].clone()
+    o, ST = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"], S0=S,
+                                    n_seq=2, S_T=S)
+    torch.cuda.synchronize()
+    assert ST.data_ptr() == S.data_ptr()
+    assert torch.equal(S, ST_ref) and torch.equal(o, o_ref)
+    o0, _ = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"], n_seq=2,
+                                    output_final_state=False)
+    oo, _ = oracle_prefill(d, S0=False)
+    assert err(o0, oo) < 1e-4
+
+
+def test_zero_tokens(kla):
+    """No tokens at all: S_T = S0."""
+    S0 = torch.randn(3, 2, 128, 128, device=DEV)
+    e = torch.empty(0, 2, 128, device=DEV, dtype=torch.bfloat16)
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    o, ST = kla.kla_prefill_chunked(e, e, e, torch.empty(0, 2, device=DEV),
+                                    torch.empty(0, 2, device=DEV), 1e-6, S0=S0, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 2, 128) and torch.equal(ST, S0)
+
+
+def test_chunk_stage_intermediates(kla):
+    """Per-chunk b, G and T = (I + L)^{-1} Diag(b), and the WY factors W, U~, against the
+    chunkwise fp64 reference (fp32 inputs, so the bar is fp32-level)."""
+    lens = [150, 64, 3]
+    w = ki.Workload(98, "unit", 3, 2, 64, 64, torch.float32, lens=tuple(lens))
+    d = to_dev(ki.prefill_inputs(w))
+    r = kla.kla_prefill_chunk_stage(d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                    cu_seqlens=d["cu_seqlens"], want_wy=True)
+    torch.cuda.synchronize()
+    q, k, v, g, eta = (d[x].double().cpu().numpy() for x in ("q", "k", "v", "g", "eta"))
+    cu = d["cu_seqlens"].cpu().numpy()
+    _, _, inter = chunkwise.prefill(q, k, v, g, eta, d["eps"], cu_seqlens=cu, chunk=64)
+    ci = 0
+    for n in range(3):
+        for c, t0 in enumerate(range(int(cu[n]), int(cu[n + 1]), 64)):
+            t1 = min(t0 + 64, int(cu[n + 1]))
+            m = t1 - t0
+            for h in range(2):
+                ref = inter[(n, h, c)]
+                assert err(r["beta"][t0:t1, h], ref["b"]) < 1e-5
+                assert err(r["G"][t0:t1, h], ref["G"]) < 1e-5
+                Tdev = r["T"][ci, h]
+                assert err(Tdev[:m, :m], ref["T"]) < 1e-4
+                assert torch.count_nonzero(Tdev[m:, :]) == 0 and torch.count_nonzero(Tdev[:, m:]) == 0
+                gam = np.exp(ref["G"])
+                W_ref = ref["T"] @ (gam[:, None] * k[t0:t1, h])
+                U_ref = ref["T"] @ v[t0:t1, h]
+                assert err(r["W"][t0:t1, h], W_ref) < 1e-4
+                assert err(r["Ut"][t0:t1, h], U_ref) < 1e-4
+            ci += 1
