@@ -94,7 +94,8 @@ def _decode(lib, **over):
     (dict(dv=512), UNSUPPORTED),
     (dict(dtype=7), UNSUPPORTED),
     (dict(total=255), INVALID),          # dense: not divisible by n_seq
-    (dict(q=FAKE + 4), INVALID),         # misaligned
+    (dict(q=FAKE + 4), INVALID),         # misaligned (16-byte vector loads)
+    (dict(g=FAKE * 4 + 2), INVALID),     # fp32 needs 4-byte alignment
     (dict(o=FAKE), INVALID),             # o overlaps q
     (dict(ws=None), WORKSPACE),
     (dict(ws=FAKE * 64, ws_bytes=16), WORKSPACE),
@@ -123,7 +124,8 @@ def test_prefill_host_cu_seqlens_validated(lib):
     (dict(eps=-0.5), INVALID),
     (dict(dtype=3), UNSUPPORTED),
     (dict(S_new=FAKE * 7 + 16), INVALID),  # partial overlap with S
-    (dict(v=FAKE * 3 + 2), INVALID),
+    (dict(v=FAKE * 3 + 1), INVALID),      # bf16 needs 2-byte alignment
+    (dict(S=FAKE * 9 + 4, S_new=FAKE * 10), INVALID),  # the state streams as float4
 ])
 def test_decode_argument_errors(lib, over, status):
     assert _decode(lib, **over) == status

@@ -24,11 +24,18 @@ DEV = "cuda"
 
 
 def err(x, y):
+    """Per-tensor error max|x - y| / max|y| (y is the reference)."""
     x = x.detach().double().cpu().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
-    y = np.asarray(y, np.float64)
+    y = y.detach().double().cpu().numpy() if hasattr(y, "detach") else np.asarray(y, np.float64)
     assert x.shape == y.shape, (x.shape, y.shape)
     assert np.all(np.isfinite(x)), "non-finite values in device output"
     return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
+
+
+def check(x, y, tol, what=""):
+    e = err(x, y)
+    print(f"  {what}: err {e:.3e} (bar {tol:g})", flush=True)
+    assert e < tol, f"{what}: err {e:.3e} >= {tol:g}"
 
 
 @pytest.fixture(scope="module")
@@ -80,8 +87,8 @@ def test_decode_step_parity(kla, dtype, dk, dv):
                                    d["eps"], S, inplace=(t % 2 == 1))
         oo, So = oracle.decode(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t], d["eps"], So)
         torch.cuda.synchronize()
-        assert err(o, oo) < TOL[dtype], t
-        assert err(S, So) < TOL[dtype], t
+        check(o, oo, TOL[dtype], "o t")
+        check(S, So, TOL[dtype], "S t")
 
 
 def test_decode_full_batch(kla):
@@ -95,8 +102,8 @@ def test_decode_full_batch(kla):
                                    d["eps"], S, inplace=True)
         oo, So = oracle.decode(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t], d["eps"], So)
         torch.cuda.synchronize()
-        assert err(o, oo) < 2e-2
-        assert err(S, So) < 2e-2
+        check(o, oo, 2e-2, "o")
+        check(S, So, 2e-2, "S")
 
 
 # ------------------------------------------------------------------------------------ prefill
@@ -105,8 +112,8 @@ def test_prefill_tiny_fp32(kla):
     d = to_dev(ki.prefill_inputs(0))
     o, ST = run_prefill(kla, d)
     oo, So = oracle_prefill(d)
-    assert err(o, oo) < 1e-4
-    assert err(ST, So) < 1e-4
+    check(o, oo, 1e-4, "o")
+    check(ST, So, 1e-4, "ST")
 
 
 def test_prefill_tiny_fp32_hard_projection(kla):
@@ -115,11 +122,10 @@ def test_prefill_tiny_fp32_hard_projection(kla):
     d = to_dev(ki.hard_variant(ki.prefill_inputs(0)))
     o, ST = run_prefill(kla, d)
     oo, So = oracle_prefill(d)
-    assert err(oo, d["v"].double().cpu().numpy()) < 1e-9   # the oracle itself
-    assert err(o, d["v"].double().cpu().numpy()) < 1e-4
-    assert err(o, oo) < 1e-4
-    # the state itself: ill-conditioned without decay (C = d_k = 64 projections per chunk)
-    assert err(ST, So) < 1e-3
+    check(oo, d["v"].double().cpu().numpy(), 1e-9, "oo")   # the oracle itself
+    check(o, d["v"].double().cpu().numpy(), 1e-4, "o")
+    check(o, oo, 1e-4, "o")
+    check(ST, So, 1e-4, "ST")
 
 
 @pytest.mark.parametrize("n_seq,T,H,dk,dv", [
@@ -134,8 +140,8 @@ def test_prefill_bf16_shapes(kla, n_seq, T, H, dk, dv):
     d = to_dev(ki.prefill_inputs(w))
     o, ST = run_prefill(kla, d)
     oo, So = oracle_prefill(d)
-    assert err(o, oo) < 2e-2
-    assert err(ST, So) < 2e-2
+    check(o, oo, 2e-2, "o")
+    check(ST, So, 2e-2, "ST")
 
 
 @pytest.mark.parametrize("n_seq,T,H,dk,dv", [(2, 200, 2, 128, 128), (1, 150, 1, 64, 256)])
@@ -144,8 +150,8 @@ def test_prefill_fp32_shapes(kla, n_seq, T, H, dk, dv):
     d = to_dev(ki.prefill_inputs(w))
     o, ST = run_prefill(kla, d)
     oo, So = oracle_prefill(d)
-    assert err(o, oo) < 1e-4
-    assert err(ST, So) < 1e-4
+    check(o, oo, 1e-4, "o")
+    check(ST, So, 1e-4, "ST")
 
 
 def test_prefill_packed_ragged(kla):
@@ -157,8 +163,8 @@ def test_prefill_packed_ragged(kla):
     d = to_dev(ki.prefill_inputs(w))
     o, ST = run_prefill(kla, d)
     oo, So = oracle_prefill(d)
-    assert err(o, oo) < 2e-2
-    assert err(ST, So) < 2e-2
+    check(o, oo, 2e-2, "o")
+    check(ST, So, 2e-2, "ST")
     # empty sequences keep their state
     assert torch.equal(ST[1], d["S0"][1]) and torch.equal(ST[6], d["S0"][6])
 
@@ -168,8 +174,8 @@ def test_prefill_layer_workload_full(kla):
     d = to_dev(ki.prefill_inputs(1))
     o, ST = run_prefill(kla, d)
     oo, So = oracle_prefill(d)
-    assert err(o, oo) < 2e-2
-    assert err(ST, So) < 2e-2
+    check(o, oo, 2e-2, "o")
+    check(ST, So, 2e-2, "ST")
 
 
 def test_prefill_long_context_full(kla):
@@ -177,9 +183,9 @@ def test_prefill_long_context_full(kla):
     d = to_dev(ki.prefill_inputs(2))
     o, ST = run_prefill(kla, d)
     oo, So = oracle_prefill(d)
-    assert err(o[:4096], oo[:4096]) < 2e-2
-    assert err(o[-64:], oo[-64:]) < 2e-2
-    assert err(ST, So) < 2e-2
+    check(o[:4096], oo[:4096], 2e-2, "o[:4096]")
+    check(o[-64:], oo[-64:], 2e-2, "o[-64:]")
+    check(ST, So, 2e-2, "ST")
 
 
 def test_packed_workload_sampled_with_decode(kla):
@@ -201,14 +207,14 @@ def test_packed_workload_sampled_with_decode(kla):
         a, b = int(cu[n]), int(cu[n + 1])
         oo, So = oracle.prefill(d["q"][a:b], d["k"][a:b], d["v"][a:b], d["g"][a:b], d["eta"][a:b],
                                 d["eps"])
-        assert err(o[a:b], oo) < 2e-2, n
-        assert err(ST[n], So[0]) < 2e-2, n
+        check(o[a:b], oo, 2e-2, "o[a:b] n")
+        check(ST[n], So[0], 2e-2, "ST[n] n")
         Sd = So
         for t in range(8):
             od, Sd = oracle.decode(dd["q"][t][n:n + 1], dd["k"][t][n:n + 1], dd["v"][t][n:n + 1],
                                    dd["g"][t][n:n + 1], dd["eta"][t][n:n + 1], dd["eps"], Sd)
-            assert err(outs[t][n:n + 1], od) < 2e-2, (n, t)
-        assert err(S[n], Sd[0]) < 2e-2, n
+            check(outs[t][n:n + 1], od, 2e-2, "outs[t][n:n + 1] (n, t)")
+        check(S[n], Sd[0], 2e-2, "S[n] n")
 
 
 # ------------------------------------------------------------------------------------ invariants
@@ -236,15 +242,20 @@ def test_one_hot_keys_long_context_closed_form(kla):
         X *= math.exp(gg[t])
         rho = ee[t] * cc[t] ** 2 / (cc[t] ** 2 + eps)
         X[ss[t]] = (1 - rho) * X[ss[t]] + rho * vv[t] / cc[t]
-    assert err(ST[0, 0], X) < 2e-2
+    check(ST[0, 0], X, 2e-2, "ST[0, 0]")
 
 
 def test_hard_projection_bf16_reads_back_values(kla):
-    """eta = 1, g = 0, eps = 0 and q := k on bf16 inputs: o_t = v_t (Theorem 1)."""
-    w = ki.Workload(94, "unit", 1, 4, 128, 128, torch.bfloat16, T=300)
+    """eta = 1, g = 0, eps = 0 and q := k on bf16 inputs: o_t = v_t (Theorem 1).
+
+    Keys are unit vectors scaled by loguniform[0.5, 2] (the long-context workload's keys).
+    With keys whose norms span 100x, o_t = k_t S~ + e_t cancels terms ~||k|| |S| down to
+    |v|, which amplifies bf16 operand rounding (2^-9) past the bar; that spread is covered
+    in fp32 by the tiny-workload hard case above."""
+    w = ki.Workload(94, "unit", 1, 4, 128, 128, torch.bfloat16, T=300, key_mode="unit_loguniform")
     d = to_dev(ki.hard_variant(ki.prefill_inputs(w)))
     o, _ = run_prefill(kla, d, S0=False)
-    assert err(o, d["v"].double().cpu().numpy()) < 2e-2
+    check(o, d["v"].double().cpu().numpy(), 2e-2, "o")
 
 
 def test_split_resume_and_prefill_decode_chain(kla):
@@ -260,15 +271,15 @@ def test_split_resume_and_prefill_decode_chain(kla):
                                      sl(d["v"], 101, 300), sl(d["g"], 101, 300),
                                      sl(d["eta"], 101, 300), d["eps"], S0=S1)
     ref = lambda x: x.double().cpu().numpy()
-    assert err(torch.cat([o1, o2]), ref(o)) < 2e-2
-    assert err(S2, ref(ST)) < 2e-2
+    check(torch.cat([o1, o2]), ref(o), 2e-2, "torch.cat([o1, o2])")
+    check(S2, ref(ST), 2e-2, "S2")
     o3, S3 = kla.kla_prefill_chunked(sl(d["q"], 0, 290), sl(d["k"], 0, 290), sl(d["v"], 0, 290),
                                      sl(d["g"], 0, 290), sl(d["eta"], 0, 290), d["eps"], S0=d["S0"])
     for t in range(290, 300):
         od, S3 = kla.kla_decode_step(d["q"][t:t + 1], d["k"][t:t + 1], d["v"][t:t + 1],
                                      d["g"][t:t + 1], d["eta"][t:t + 1], d["eps"], S3, inplace=True)
-        assert err(od, ref(o[t:t + 1])) < 2e-2
-    assert err(S3, ref(ST)) < 2e-2
+        check(od, ref(o[t:t + 1]), 2e-2, "od")
+    check(S3, ref(ST), 2e-2, "S3")
 
 
 def test_packed_equals_per_sequence_and_deterministic(kla):
@@ -304,7 +315,7 @@ def test_in_place_state_and_null_state(kla):
     o0, _ = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"], n_seq=2,
                                     output_final_state=False)
     oo, _ = oracle_prefill(d, S0=False)
-    assert err(o0, oo) < 1e-4
+    check(o0, oo, 1e-4, "o0")
 
 
 def test_zero_tokens(kla):
@@ -337,14 +348,14 @@ def test_chunk_stage_intermediates(kla):
             m = t1 - t0
             for h in range(2):
                 ref = inter[(n, h, c)]
-                assert err(r["beta"][t0:t1, h], ref["b"]) < 1e-5
-                assert err(r["G"][t0:t1, h], ref["G"]) < 1e-5
+                check(r["beta"][t0:t1, h], ref["b"], 1e-5, "r['beta'][t0:t1, h]")
+                check(r["G"][t0:t1, h], ref["G"], 1e-5, "r['G'][t0:t1, h]")
                 Tdev = r["T"][ci, h]
-                assert err(Tdev[:m, :m], ref["T"]) < 1e-4
+                check(Tdev[:m, :m], ref["T"], 1e-4, "Tdev[:m, :m]")
                 assert torch.count_nonzero(Tdev[m:, :]) == 0 and torch.count_nonzero(Tdev[:, m:]) == 0
                 gam = np.exp(ref["G"])
                 W_ref = ref["T"] @ (gam[:, None] * k[t0:t1, h])
                 U_ref = ref["T"] @ v[t0:t1, h]
-                assert err(r["W"][t0:t1, h], W_ref) < 1e-4
-                assert err(r["Ut"][t0:t1, h], U_ref) < 1e-4
+                check(r["W"][t0:t1, h], W_ref, 1e-4, "r['W'][t0:t1, h]")
+                check(r["Ut"][t0:t1, h], U_ref, 1e-4, "r['Ut'][t0:t1, h]")
             ci += 1
