@@ -9,6 +9,7 @@ missing the first call raises an error naming the build step.
 Functions mirror the C entry points:
 
 * :func:`kla_prefill_chunked` -- chunkwise prefill (q, k, v, g, eta, eps, S0) -> (o, S_T)
+* :func:`kla_prefill_prepare` / :func:`kla_prefill_scan` -- its two halves
 * :func:`kla_decode_step`     -- one decode step (q, k, v, g, eta, eps, S) -> (o, S')
 * :func:`kla_prefill_chunk_stage` -- per-chunk b, G, T (and W, U~) for unit checks
 * :func:`kla_prefill_workspace_bytes`
@@ -20,8 +21,9 @@ import os
 
 import torch
 
-__all__ = ["kla_prefill_chunked", "kla_decode_step", "kla_prefill_chunk_stage",
-           "kla_prefill_workspace_bytes", "library_path", "load_library", "CHUNK", "KlaError"]
+__all__ = ["kla_prefill_chunked", "kla_prefill_prepare", "kla_prefill_scan", "kla_decode_step",
+           "kla_prefill_chunk_stage", "kla_prefill_workspace_bytes", "library_path",
+           "load_library", "CHUNK", "KlaError"]
 
 CHUNK = 64
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +62,12 @@ def load_library():
     lib.kla_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i32, i32,
                                         i32, i32, ctypes.c_int, vp, sz, vp]
     lib.kla_prefill_chunked.restype = ctypes.c_int
+    lib.kla_prefill_prepare.argtypes = [vp, vp, vp, f32, vp, vp, i32, i32, i32, i32, i32,
+                                        ctypes.c_int, vp, sz, vp]
+    lib.kla_prefill_prepare.restype = ctypes.c_int
+    lib.kla_prefill_scan.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                     vp, sz, vp]
+    lib.kla_prefill_scan.restype = ctypes.c_int
     lib.kla_prefill_chunk_stage.argtypes = [vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, i32,
                                             i32, i32, i32, i32, ctypes.c_int, vp, sz, vp]
     lib.kla_prefill_chunk_stage.restype = ctypes.c_int
@@ -180,6 +188,47 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
         _ptr(cu_seqlens), host_ptr, n_seq, n_tok, H, d_k, d_v, _DTYPES[dt], _ptr(workspace),
         workspace.numel(), _stream(dev)))
     return o.reshape(shape_v), S_T
+
+
+def kla_prefill_prepare(k, g, eta, eps, workspace, *, n_seq, d_v, cu_seqlens=None):
+    """First half of the prefill: sequence tables, G and T of every chunk into ``workspace``
+    (a uint8 device tensor of at least kla_prefill_workspace_bytes(...) bytes).
+    k: [n_tok, H, d_k]; g, eta: [n_tok, H]."""
+    dev = k.device
+    _need(k, "k", device=dev)
+    if k.dtype not in _DTYPES:
+        raise TypeError("k must be float32 or bfloat16")
+    _need(g, "g", torch.float32, dev)
+    _need(eta, "eta", torch.float32, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    n_tok, H, d_k = k.shape
+    _check(load_library().kla_prefill_prepare(
+        _ptr(k), _ptr(g), _ptr(eta), float(eps), _ptr(cu_seqlens), None, n_seq, n_tok, H, d_k, d_v,
+        _DTYPES[k.dtype], _ptr(workspace), workspace.numel(), _stream(dev)))
+
+
+def kla_prefill_scan(q, k, v, workspace, *, n_seq, S0=None, o=None, S_T=None):
+    """Second half of the prefill: the chunk scan with outputs, reading the workspace that
+    kla_prefill_prepare filled for the same k, g, eta and sizes.  Returns (o, S_T)."""
+    dev = q.device
+    dt = q.dtype
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, dt, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    n_tok, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if o is None:
+        o = torch.empty((n_tok, H, d_v), dtype=dt, device=dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, dev)
+    if S_T is not None:
+        _need(S_T, "S_T", torch.float32, dev)
+    _check(load_library().kla_prefill_scan(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(o), _ptr(S_T), n_seq, n_tok, H, d_k, d_v,
+        _DTYPES[dt], _ptr(workspace), workspace.numel(), _stream(dev)))
+    return o, S_T
 
 
 def kla_decode_step(q, k, v, g, eta, eps: float, S, *, o=None, S_new=None, inplace=False):

@@ -29,6 +29,7 @@ kla_status ok() {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -117,23 +118,35 @@ size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t 
   return ws_layout(n_seq, total_tokens, n_heads).total;
 }
 
-kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
-                               const float *eta, float eps, const float *S0, void *o,
-                               float *S_T, const int32_t *cu_seqlens,
-                               const int32_t *cu_seqlens_host, int32_t n_seq,
-                               int32_t total_tokens, int32_t n_heads, int32_t d_k,
-                               int32_t d_v, kla_dtype dtype, void *workspace,
-                               size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation of the prefill arguments shared by the three prefill entry points.  Token
+// buffers that a given entry point does not use are passed as nullptr with need_* = false.
+kla_status check_prefill_args(const void *q, const void *k, const void *v, const float *g,
+                              const float *eta, float eps, const float *S0, const void *o,
+                              const float *S_T, const int32_t *cu_seqlens,
+                              const int32_t *cu_seqlens_host, int32_t n_seq, int32_t total_tokens,
+                              int32_t n_heads, int32_t d_k, int32_t d_v, kla_dtype dtype,
+                              const void *workspace, size_t workspace_bytes, bool need_prep,
+                              bool need_scan, bool check_tables = true) {
   kla_status st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v,
                                       dtype, eps);
   if (st != KLA_OK) return st;
-  if (total_tokens > 0 && (!q || !k || !v || !g || !eta || !o))
-    return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v, g, eta and o are required");
-  if ((st = check_dense(cu_seqlens, n_seq, total_tokens)) != KLA_OK) return st;
-  const void *ptrs[] = {q, k, v, g, eta, S0, o, S_T, workspace};
-  for (const void *p : ptrs)
-    if (p && !aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  if (total_tokens > 0) {
+    if (!k || (need_prep && (!g || !eta)) || (need_scan && (!q || !v || !o)))
+      return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v, g, eta and o are required");
+  }
+  if (check_tables && (st = check_dense(cu_seqlens, n_seq, total_tokens)) != KLA_OK) return st;
   const size_t es = elem_size(dtype);
+  // q, k, v are read with 16-byte vector loads; the rest element by element
+  for (const void *p : {q, k, v})
+    if (p && !aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v must be 16-byte aligned");
+  for (const void *p : {static_cast<const void *>(g), static_cast<const void *>(eta),
+                        static_cast<const void *>(S0), static_cast<const void *>(S_T)})
+    if (p && !aligned_to(p, 4)) return fail(KLA_ERR_INVALID_ARGUMENT, "g, eta, S0, S_T must be 4-byte aligned");
+  if (o && !aligned_to(o, es)) return fail(KLA_ERR_INVALID_ARGUMENT, "o must be element aligned");
   const size_t nq = (size_t)total_tokens * n_heads * d_k * es;
   const size_t nv = (size_t)total_tokens * n_heads * d_v * es;
   if (overlap(o, nv, q, nq) || overlap(o, nv, k, nq) || overlap(o, nv, v, nv))
@@ -147,23 +160,98 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
                 workspace ? workspace_bytes : (size_t)0);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(KLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  return KLA_OK;
+}
 
+struct WsViews {
+  kla::SeqTables tabs;
+  float *G, *T;
+};
+
+WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n_heads) {
+  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads);
   char *ws = static_cast<char *>(workspace);
-  kla::SeqTables tabs{reinterpret_cast<int32_t *>(ws + w.off_cu),
-                      reinterpret_cast<int32_t *>(ws + w.off_co)};
-  float *G = reinterpret_cast<float *>(ws + w.off_G);
-  float *T = reinterpret_cast<float *>(ws + w.off_T);
+  return WsViews{{reinterpret_cast<int32_t *>(ws + w.off_cu),
+                  reinterpret_cast<int32_t *>(ws + w.off_co)},
+                 reinterpret_cast<float *>(ws + w.off_G), reinterpret_cast<float *>(ws + w.off_T)};
+}
+
+kla_status enqueue_prepare(const void *k, const float *g, const float *eta, float eps,
+                           const int32_t *cu_seqlens, int32_t n_seq, int32_t total_tokens,
+                           int32_t n_heads, int32_t d_k, kla_dtype dtype, void *workspace,
+                           hipStream_t s) {
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
+  kla_status st;
+  if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan")) != KLA_OK)
+    return st;
+  return hip_status(kla::launch_prep(to_dt(dtype), d_k, k, g, eta, eps, wv.tabs, n_seq, nch_ub,
+                                     n_heads, wv.G, nullptr, wv.T, s), "prep");
+}
+
+kla_status enqueue_scan(const void *q, const void *k, const void *v, const float *S0, void *o,
+                        float *S_T, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                        int32_t d_k, int32_t d_v, kla_dtype dtype, void *workspace, hipStream_t s) {
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
+  return hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.G, wv.T, S0, o, S_T,
+                                     wv.tabs, n_seq, n_heads, s), "scan");
+}
+
+}  // namespace
+
+extern "C" {
+
+kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
+                               const float *eta, float eps, const float *S0, void *o,
+                               float *S_T, const int32_t *cu_seqlens,
+                               const int32_t *cu_seqlens_host, int32_t n_seq,
+                               int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                               int32_t d_v, kla_dtype dtype, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  kla_status st = check_prefill_args(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
+                                     n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
+                                     workspace_bytes, true, true);
+  if (st != KLA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear any stale error from unrelated work
-  const kla::Dtype dt = to_dt(dtype);
-  if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, tabs, s), "plan")) != KLA_OK)
+  if ((st = enqueue_prepare(k, g, eta, eps, cu_seqlens, n_seq, total_tokens, n_heads, d_k, dtype,
+                            workspace, s)) != KLA_OK)
     return st;
-  if ((st = hip_status(kla::launch_prep(dt, d_k, k, g, eta, eps, tabs, n_seq, nch_ub, n_heads, G,
-                                        nullptr, T, s), "prep")) != KLA_OK)
+  if ((st = enqueue_scan(q, k, v, S0, o, S_T, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
+                         workspace, s)) != KLA_OK)
     return st;
-  if ((st = hip_status(kla::launch_scan(dt, d_k, d_v, q, k, v, G, T, S0, o, S_T, tabs, n_seq,
-                                        n_heads, s), "scan")) != KLA_OK)
+  return ok();
+}
+
+kla_status kla_prefill_prepare(const void *k, const float *g, const float *eta, float eps,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                               int32_t n_seq, int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                               int32_t d_v, kla_dtype dtype, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  kla_status st = check_prefill_args(nullptr, k, nullptr, g, eta, eps, nullptr, nullptr, nullptr,
+                                     cu_seqlens, cu_seqlens_host, n_seq, total_tokens, n_heads,
+                                     d_k, d_v, dtype, workspace, workspace_bytes, true, false);
+  if (st != KLA_OK) return st;
+  (void)hipGetLastError();
+  if ((st = enqueue_prepare(k, g, eta, eps, cu_seqlens, n_seq, total_tokens, n_heads, d_k, dtype,
+                            workspace, static_cast<hipStream_t>(stream))) != KLA_OK)
+    return st;
+  return ok();
+}
+
+kla_status kla_prefill_scan(const void *q, const void *k, const void *v, const float *S0, void *o,
+                            float *S_T, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                            int32_t d_k, int32_t d_v, kla_dtype dtype, const void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  // eps only matters to the prepare stage (pass a valid value through the shared checks);
+  // the sequence tables come from the workspace the prepare call filled
+  kla_status st = check_prefill_args(q, k, v, nullptr, nullptr, 0.f, S0, o, S_T, nullptr, nullptr,
+                                     n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
+                                     workspace_bytes, false, true, false);
+  if (st != KLA_OK) return st;
+  (void)hipGetLastError();
+  if ((st = enqueue_scan(q, k, v, S0, o, S_T, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
+                         const_cast<void *>(workspace), static_cast<hipStream_t>(stream))) != KLA_OK)
     return st;
   return ok();
 }
@@ -181,9 +269,15 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
   if (total_tokens > 0 && (!k || !g || !eta || !T || (Ut && !v)))
     return fail(KLA_ERR_INVALID_ARGUMENT, "k, g, eta, T (and v when Ut is requested) are required");
   if ((st = check_dense(cu_seqlens, n_seq, total_tokens)) != KLA_OK) return st;
-  const void *ptrs[] = {k, v, g, eta, beta, G, T, W, Ut, workspace};
-  for (const void *p : ptrs)
-    if (p && !aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  for (const void *p : {k, v})
+    if (p && !aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "k, v must be 16-byte aligned");
+  for (const void *p : {static_cast<const void *>(g), static_cast<const void *>(eta),
+                        static_cast<const void *>(beta), static_cast<const void *>(G),
+                        static_cast<const void *>(T), static_cast<const void *>(W),
+                        static_cast<const void *>(Ut)})
+    if (p && !aligned_to(p, 4)) return fail(KLA_ERR_INVALID_ARGUMENT, "fp32 buffers must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   const WsLayout w = ws_layout(n_seq, total_tokens, n_heads);
   // this entry point writes G into the caller's buffer when given, else into the workspace
   if (!workspace || workspace_bytes < w.total)
@@ -224,9 +318,14 @@ kla_status kla_decode_step(const void *q, const void *k, const void *v, const fl
     return fail(KLA_ERR_INVALID_ARGUMENT, "batch * n_heads too large");
   if (!q || !k || !v || !g || !eta || !S || !o || !S_new)
     return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v, g, eta, S, o and S_new are required");
-  const void *ptrs[] = {q, k, v, g, eta, S, o, S_new};
-  for (const void *p : ptrs)
-    if (!aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  // the state streams as float4; the token vectors are read element by element
+  if (!aligned16(S) || !aligned16(S_new))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "S and S_new must be 16-byte aligned");
+  const size_t es = elem_size(dtype);
+  for (const void *p : {q, k, v, static_cast<const void *>(o)})
+    if (!aligned_to(p, es)) return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v, o must be element aligned");
+  if (!aligned_to(g, 4) || !aligned_to(eta, 4))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "g and eta must be 4-byte aligned");
   const size_t nS = (size_t)batch * n_heads * d_k * d_v * sizeof(float);
   if (S_new != S && overlap(S_new, nS, S, nS))
     return fail(KLA_ERR_INVALID_ARGUMENT, "S_new may equal S but must not partially overlap it");

@@ -79,6 +79,16 @@ template <> __device__ __forceinline__ bf16x8 load8_cvt<__bf16>(const float *p) 
   return r;
 }
 
+// Convert 8 fp32 values to the operand type T.
+template <typename T> __device__ __forceinline__ typename Frag<T>::type cvt8(const f32x8 &x);
+template <> __device__ __forceinline__ f32x8 cvt8<float>(const f32x8 &x) { return x; }
+template <> __device__ __forceinline__ bf16x8 cvt8<__bf16>(const f32x8 &x) {
+  bf16x8 r;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) r[s] = static_cast<__bf16>(x[s]);
+  return r;
+}
+
 template <typename T> __device__ __forceinline__ typename Frag<T>::type zero8() {
   typename Frag<T>::type r;
 #pragma unroll

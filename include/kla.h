@@ -22,7 +22,9 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates, frees or retains them.  Tensors are dense, row-major,
- *     with the last named dimension fastest, base addresses 16-byte aligned.
+ *     with the last named dimension fastest.  Alignment: the prefill's q, k, v
+ *     and the decode's S, S_new need 16-byte aligned bases (vector loads); every
+ *     other buffer needs its element alignment; the workspace 256 bytes.
  *   - q, k, v, o use the element type `dtype` (fp32 or bf16); g, eta, S0, S_T,
  *     S and S_new are always fp32.  Accumulation and the state are fp32.
  *   - Calls are asynchronous: they validate, enqueue kernels on `stream` (a
@@ -108,6 +110,33 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
                                int32_t total_tokens, int32_t n_heads, int32_t d_k,
                                int32_t d_v, kla_dtype dtype, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/*
+ * The two halves of kla_prefill_chunked, for callers that schedule them apart
+ * (and for timing each kernel).  kla_prefill_chunked(...) is exactly
+ * kla_prefill_prepare(...) followed by kla_prefill_scan(...) on one stream.
+ *
+ * kla_prefill_prepare: per-chunk stage (paper section 4, Algorithm 1 chunkwise
+ *   panel steps 2-6 up to the triangular solve): sequence tables, the chunk-local
+ *   log-decay G and T = (I + L)^{-1} Diag(b) of every chunk, written into
+ *   `workspace`.  Arguments as for kla_prefill_chunked.
+ * kla_prefill_scan: the sequential chunk scan with the outputs (Eq. (7)-(9)),
+ *   reading the workspace a kla_prefill_prepare call with the same k, g, eta,
+ *   cu_seqlens and sizes filled earlier on the same stream (not checkable: a
+ *   workspace from another problem gives wrong results, never out-of-bounds
+ *   access as long as the sizes match).  q, k, v, S0, o, S_T as for
+ *   kla_prefill_chunked.
+ */
+kla_status kla_prefill_prepare(const void *k, const float *g, const float *eta, float eps,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                               int32_t n_seq, int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                               int32_t d_v, kla_dtype dtype, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+kla_status kla_prefill_scan(const void *q, const void *k, const void *v, const float *S0, void *o,
+                            float *S_T, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                            int32_t d_k, int32_t d_v, kla_dtype dtype, const void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /*
  * One decode step per sequence: (q, k, v, g, eta, eps, S) -> (o, S').
