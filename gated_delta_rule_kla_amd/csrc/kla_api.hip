@@ -140,13 +140,12 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
   }
   if (check_tables && (st = check_dense(cu_seqlens, n_seq, total_tokens)) != KLA_OK) return st;
   const size_t es = elem_size(dtype);
-  // q, k, v are read with 16-byte vector loads; the rest element by element
-  for (const void *p : {q, k, v})
-    if (p && !aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v must be 16-byte aligned");
+  // q, k, v are read and o is written with vector accesses; the rest element by element
+  for (const void *p : {q, k, v, o})
+    if (p && !aligned16(p)) return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v, o must be 16-byte aligned");
   for (const void *p : {static_cast<const void *>(g), static_cast<const void *>(eta),
                         static_cast<const void *>(S0), static_cast<const void *>(S_T)})
     if (p && !aligned_to(p, 4)) return fail(KLA_ERR_INVALID_ARGUMENT, "g, eta, S0, S_T must be 4-byte aligned");
-  if (o && !aligned_to(o, es)) return fail(KLA_ERR_INVALID_ARGUMENT, "o must be element aligned");
   const size_t nq = (size_t)total_tokens * n_heads * d_k * es;
   const size_t nv = (size_t)total_tokens * n_heads * d_v * es;
   if (overlap(o, nv, q, nq) || overlap(o, nv, k, nq) || overlap(o, nv, v, nv))
@@ -186,7 +185,7 @@ kla_status enqueue_prepare(const void *k, const float *g, const float *eta, floa
   if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan")) != KLA_OK)
     return st;
   return hip_status(kla::launch_prep(to_dt(dtype), d_k, k, g, eta, eps, wv.tabs, n_seq, nch_ub,
-                                     n_heads, wv.G, nullptr, wv.T, s), "prep");
+                                     n_heads, wv.G, nullptr, wv.T, false, s), "prep");
 }
 
 kla_status enqueue_scan(const void *q, const void *k, const void *v, const float *S0, void *o,
@@ -294,7 +293,7 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
   if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, tabs, s), "plan")) != KLA_OK)
     return st;
   if ((st = hip_status(kla::launch_prep(dt, d_k, k, g, eta, eps, tabs, n_seq, nch_ub, n_heads,
-                                        Gbuf, beta, T, s), "prep")) != KLA_OK)
+                                        Gbuf, beta, T, true, s), "prep")) != KLA_OK)
     return st;
   if ((st = hip_status(kla::launch_wy(dt, d_k, d_v, k, v, Gbuf, T, tabs, n_seq, nch_ub, n_heads,
                                       W, Ut, s), "wy")) != KLA_OK)

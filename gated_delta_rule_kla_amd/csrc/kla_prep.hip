@@ -104,11 +104,11 @@ struct PrepSmem {
   alignas(16) float G[kChunk];
 };
 
-template <typename Tin, int DK>
+template <typename Tin, int DK, typename TOut>
 __global__ __launch_bounds__(256) void kla_prep_kernel(
     const Tin *__restrict__ k, const float *__restrict__ g, const float *__restrict__ eta,
     float eps, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq,
-    int H, float *__restrict__ G_out, float *__restrict__ beta_out, float *__restrict__ T_out) {
+    int H, float *__restrict__ G_out, float *__restrict__ beta_out, TOut *__restrict__ T_out) {
   __shared__ PrepSmem<Tin, DK> sm;
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= chunk_off[n_seq]) return;
@@ -201,38 +201,46 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
       x[i] = acc;
     }
     const float bc = sm.beta[lane];
-    float *Tc = T_out + ((size_t)c * H + h) * (kChunk * kChunk);
+    TOut *Tc = T_out + ((size_t)c * H + h) * (kChunk * kChunk);
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) Tc[i * kChunk + lane] = x[i] * bc;
+    for (int i = 0; i < kChunk; ++i) Tc[i * kChunk + lane] = from_f32<TOut>(x[i] * bc);
   }
 }
 
 template <typename Tin, int DK>
 static hipError_t launch_prep_t(const void *k, const float *g, const float *eta, float eps,
                                 SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
-                                float *G_out, float *beta_out, float *T_out, hipStream_t stream) {
+                                float *G_out, float *beta_out, void *T_out, bool t_fp32,
+                                hipStream_t stream) {
   if (n_chunks_ub <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kla_prep_kernel<Tin, DK>), dim3((unsigned)n_chunks_ub, H), dim3(256), 0,
-                     stream, static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                     G_out, beta_out, T_out);
+  const dim3 grid((unsigned)n_chunks_ub, H);
+  if (t_fp32 || sizeof(Tin) == 4)
+    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(256), 0, stream,
+                       static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
+                       G_out, beta_out, static_cast<float *>(T_out));
+  else
+    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(256), 0, stream,
+                       static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
+                       G_out, beta_out, static_cast<Tin *>(T_out));
   return hipGetLastError();
 }
 
 hipError_t launch_prep(Dtype dt, int d_k, const void *k, const float *g, const float *eta,
                        float eps, SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
-                       float *G_out, float *beta_out, float *T_out, hipStream_t stream) {
+                       float *G_out, float *beta_out, void *T_out, bool t_fp32,
+                       hipStream_t stream) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
       return launch_prep_t<__bf16, 128>(k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                        T_out, stream);
+                                        T_out, t_fp32, stream);
     return launch_prep_t<__bf16, 64>(k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                     T_out, stream);
+                                     T_out, t_fp32, stream);
   }
   if (d_k == 128)
     return launch_prep_t<float, 128>(k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                     T_out, stream);
+                                     T_out, t_fp32, stream);
   return launch_prep_t<float, 64>(k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                  T_out, stream);
+                                  T_out, t_fp32, stream);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -22,8 +22,8 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates, frees or retains them.  Tensors are dense, row-major,
- *     with the last named dimension fastest.  Alignment: the prefill's q, k, v
- *     and the decode's S, S_new need 16-byte aligned bases (vector loads); every
+ *     with the last named dimension fastest.  Alignment: the prefill's q, k, v, o
+ *     and the decode's S, S_new need 16-byte aligned bases (vector accesses); every
  *     other buffer needs its element alignment; the workspace 256 bytes.
  *   - q, k, v, o use the element type `dtype` (fp32 or bf16); g, eta, S0, S_T,
  *     S and S_new are always fp32.  Accumulation and the state are fp32.

@@ -95,6 +95,7 @@ def _decode(lib, **over):
     (dict(dtype=7), UNSUPPORTED),
     (dict(total=255), INVALID),          # dense: not divisible by n_seq
     (dict(q=FAKE + 4), INVALID),         # misaligned (16-byte vector loads)
+    (dict(o=FAKE * 6 + 8), INVALID),     # o is written with vector stores
     (dict(g=FAKE * 4 + 2), INVALID),     # fp32 needs 4-byte alignment
     (dict(o=FAKE), INVALID),             # o overlaps q
     (dict(ws=None), WORKSPACE),
