@@ -109,7 +109,7 @@ def main():
                          ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
 
     def step(s):
-        kla.kla_prefill_prepare(s["k"], s["g"], s["eta"], base["eps"], s["ws"], n_seq=n_seq, d_v=dv)
+        kla.kla_prefill_prepare(s["q"], s["k"], s["g"], s["eta"], base["eps"], s["ws"], n_seq=n_seq, d_v=dv)
         ev_mid = torch.cuda.Event(enable_timing=True)
         ev_mid.record()
         kla.kla_prefill_scan(s["q"], s["k"], s["v"], s["ws"], n_seq=n_seq, S0=s["S0"], o=s["o"],

@@ -62,7 +62,7 @@ def load_library():
     lib.kla_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i32, i32,
                                         i32, i32, ctypes.c_int, vp, sz, vp]
     lib.kla_prefill_chunked.restype = ctypes.c_int
-    lib.kla_prefill_prepare.argtypes = [vp, vp, vp, f32, vp, vp, i32, i32, i32, i32, i32,
+    lib.kla_prefill_prepare.argtypes = [vp, vp, vp, vp, f32, vp, vp, i32, i32, i32, i32, i32,
                                         ctypes.c_int, vp, sz, vp]
     lib.kla_prefill_prepare.restype = ctypes.c_int
     lib.kla_prefill_scan.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
@@ -190,14 +190,15 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
     return o.reshape(shape_v), S_T
 
 
-def kla_prefill_prepare(k, g, eta, eps, workspace, *, n_seq, d_v, cu_seqlens=None):
-    """First half of the prefill: sequence tables, G and T of every chunk into ``workspace``
+def kla_prefill_prepare(q, k, g, eta, eps, workspace, *, n_seq, d_v, cu_seqlens=None):
+    """First half of the prefill: sequence tables, G, T and P of every chunk into ``workspace``
     (a uint8 device tensor of at least kla_prefill_workspace_bytes(...) bytes).
-    k: [n_tok, H, d_k]; g, eta: [n_tok, H]."""
+    q, k: [n_tok, H, d_k]; g, eta: [n_tok, H]."""
     dev = k.device
     _need(k, "k", device=dev)
     if k.dtype not in _DTYPES:
         raise TypeError("k must be float32 or bfloat16")
+    _need(q, "q", k.dtype, dev)
     _need(g, "g", torch.float32, dev)
     _need(eta, "eta", torch.float32, dev)
     _need(workspace, "workspace", torch.uint8, dev)
@@ -205,7 +206,7 @@ def kla_prefill_prepare(k, g, eta, eps, workspace, *, n_seq, d_v, cu_seqlens=Non
         _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     n_tok, H, d_k = k.shape
     _check(load_library().kla_prefill_prepare(
-        _ptr(k), _ptr(g), _ptr(eta), float(eps), _ptr(cu_seqlens), None, n_seq, n_tok, H, d_k, d_v,
+        _ptr(q), _ptr(k), _ptr(g), _ptr(eta), float(eps), _ptr(cu_seqlens), None, n_seq, n_tok, H, d_k, d_v,
         _DTYPES[k.dtype], _ptr(workspace), workspace.numel(), _stream(dev)))
 
 

@@ -45,9 +45,10 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 // Workspace layout: [cu: n_seq+1 int32][chunk_off: n_seq+1 int32][G: total*H fp32]
-//                   [T: n_chunks_ub * H * 64 * 64 fp32], each part 256-byte aligned.
+//                   [T: n_chunks_ub * H * 64 * 64][P: same], each part 256-byte aligned and
+// T, P sized for fp32 (the scan reads them in the operand type).
 struct WsLayout {
-  size_t off_cu, off_co, off_G, off_T, total;
+  size_t off_cu, off_co, off_G, off_T, off_P, total;
 };
 
 WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H) {
@@ -57,7 +58,9 @@ WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H) {
   w.off_G = align256(w.off_co + sizeof(int32_t) * (size_t)(n_seq + 1));
   w.off_T = align256(w.off_G + sizeof(float) * (size_t)total_tokens * (size_t)H);
   const int64_t nch = kla::chunk_upper_bound(n_seq, total_tokens);
-  w.total = align256(w.off_T + sizeof(float) * (size_t)nch * (size_t)H * KLA_CHUNK * KLA_CHUNK);
+  const size_t tile_bytes = sizeof(float) * (size_t)nch * (size_t)H * KLA_CHUNK * KLA_CHUNK;
+  w.off_P = align256(w.off_T + tile_bytes);
+  w.total = align256(w.off_P + tile_bytes);
   return w;
 }
 
@@ -164,7 +167,8 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
 
 struct WsViews {
   kla::SeqTables tabs;
-  float *G, *T;
+  float *G;
+  void *T, *P;
 };
 
 WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n_heads) {
@@ -172,10 +176,10 @@ WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n
   char *ws = static_cast<char *>(workspace);
   return WsViews{{reinterpret_cast<int32_t *>(ws + w.off_cu),
                   reinterpret_cast<int32_t *>(ws + w.off_co)},
-                 reinterpret_cast<float *>(ws + w.off_G), reinterpret_cast<float *>(ws + w.off_T)};
+                 reinterpret_cast<float *>(ws + w.off_G), ws + w.off_T, ws + w.off_P};
 }
 
-kla_status enqueue_prepare(const void *k, const float *g, const float *eta, float eps,
+kla_status enqueue_prepare(const void *q, const void *k, const float *g, const float *eta, float eps,
                            const int32_t *cu_seqlens, int32_t n_seq, int32_t total_tokens,
                            int32_t n_heads, int32_t d_k, kla_dtype dtype, void *workspace,
                            hipStream_t s) {
@@ -184,16 +188,16 @@ kla_status enqueue_prepare(const void *k, const float *g, const float *eta, floa
   kla_status st;
   if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan")) != KLA_OK)
     return st;
-  return hip_status(kla::launch_prep(to_dt(dtype), d_k, k, g, eta, eps, wv.tabs, n_seq, nch_ub,
-                                     n_heads, wv.G, nullptr, wv.T, false, s), "prep");
+  return hip_status(kla::launch_prep(to_dt(dtype), d_k, q, k, g, eta, eps, wv.tabs, n_seq, nch_ub,
+                                     n_heads, wv.G, nullptr, wv.T, false, wv.P, s), "prep");
 }
 
 kla_status enqueue_scan(const void *q, const void *k, const void *v, const float *S0, void *o,
                         float *S_T, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
                         int32_t d_k, int32_t d_v, kla_dtype dtype, void *workspace, hipStream_t s) {
   const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
-  return hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.G, wv.T, S0, o, S_T,
-                                     wv.tabs, n_seq, n_heads, s), "scan");
+  return hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.G, wv.T, wv.P, S0, o,
+                                     S_T, wv.tabs, n_seq, n_heads, s), "scan");
 }
 
 }  // namespace
@@ -213,8 +217,8 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
   if (st != KLA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear any stale error from unrelated work
-  if ((st = enqueue_prepare(k, g, eta, eps, cu_seqlens, n_seq, total_tokens, n_heads, d_k, dtype,
-                            workspace, s)) != KLA_OK)
+  if ((st = enqueue_prepare(q, k, g, eta, eps, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
+                            dtype, workspace, s)) != KLA_OK)
     return st;
   if ((st = enqueue_scan(q, k, v, S0, o, S_T, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
                          workspace, s)) != KLA_OK)
@@ -222,18 +226,20 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
   return ok();
 }
 
-kla_status kla_prefill_prepare(const void *k, const float *g, const float *eta, float eps,
-                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
-                               int32_t n_seq, int32_t total_tokens, int32_t n_heads, int32_t d_k,
-                               int32_t d_v, kla_dtype dtype, void *workspace,
-                               size_t workspace_bytes, void *stream) {
-  kla_status st = check_prefill_args(nullptr, k, nullptr, g, eta, eps, nullptr, nullptr, nullptr,
+kla_status kla_prefill_prepare(const void *q, const void *k, const float *g, const float *eta,
+                               float eps, const int32_t *cu_seqlens,
+                               const int32_t *cu_seqlens_host, int32_t n_seq, int32_t total_tokens,
+                               int32_t n_heads, int32_t d_k, int32_t d_v, kla_dtype dtype,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  kla_status st = check_prefill_args(q, k, nullptr, g, eta, eps, nullptr, nullptr, nullptr,
                                      cu_seqlens, cu_seqlens_host, n_seq, total_tokens, n_heads,
                                      d_k, d_v, dtype, workspace, workspace_bytes, true, false);
   if (st != KLA_OK) return st;
+  if (total_tokens > 0 && !q)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, g and eta are required");
   (void)hipGetLastError();
-  if ((st = enqueue_prepare(k, g, eta, eps, cu_seqlens, n_seq, total_tokens, n_heads, d_k, dtype,
-                            workspace, static_cast<hipStream_t>(stream))) != KLA_OK)
+  if ((st = enqueue_prepare(q, k, g, eta, eps, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
+                            dtype, workspace, static_cast<hipStream_t>(stream))) != KLA_OK)
     return st;
   return ok();
 }
@@ -292,8 +298,8 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
   const kla::Dtype dt = to_dt(dtype);
   if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, tabs, s), "plan")) != KLA_OK)
     return st;
-  if ((st = hip_status(kla::launch_prep(dt, d_k, k, g, eta, eps, tabs, n_seq, nch_ub, n_heads,
-                                        Gbuf, beta, T, true, s), "prep")) != KLA_OK)
+  if ((st = hip_status(kla::launch_prep(dt, d_k, nullptr, k, g, eta, eps, tabs, n_seq, nch_ub,
+                                        n_heads, Gbuf, beta, T, true, nullptr, s), "prep")) != KLA_OK)
     return st;
   if ((st = hip_status(kla::launch_wy(dt, d_k, d_v, k, v, Gbuf, T, tabs, n_seq, nch_ub, n_heads,
                                       W, Ut, s), "wy")) != KLA_OK)

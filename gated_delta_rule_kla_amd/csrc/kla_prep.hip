@@ -93,22 +93,52 @@ __device__ __forceinline__ int find_sequence(const int32_t *__restrict__ chunk_o
 
 // ---------------------------------------------------------------------------------------------
 // Prep / UT kernel: one workgroup (4 wavefronts) per (chunk, head).
+//
+// (I + L)^{-1} is formed blockwise on 16 x 16 blocks (X = (I + L)^{-1} is unit lower
+// triangular): every wavefront inverts one diagonal block by substitution, then the
+// sub-diagonal blocks follow level by level,
+//   X_ij = -X_ii (sum_{k=j}^{i-1} L_ik X_kj),  i > j,
+// with the 16 x 16 x 16 products on the fp32 matrix cores.  T = X Diag(b).
+// When q is given the kernel also writes P = (A o Q K^T) (Eq. (8)'s intra-chunk matrix,
+// A_ij = exp(G_i - G_j) for j <= i, zero above the diagonal) for the scan.
 // ---------------------------------------------------------------------------------------------
 template <typename Tin, int DK>
 struct PrepSmem {
   static constexpr int PAD = 8;
   alignas(16) Tin K[kChunk][DK + PAD];   // chunk keys, token-major
+  alignas(16) Tin Q[kChunk][DK + PAD];   // chunk queries, token-major (only when P is wanted)
   alignas(16) float L[kChunk][kChunk + 4];
+  alignas(16) float X[kChunk][kChunk + 4];
   alignas(16) float norm2[kChunk];
   alignas(16) float beta[kChunk];
   alignas(16) float G[kChunk];
 };
 
+// D += A B for 16 x 16 fp32 blocks in LDS (row strides lda, ldb), on v_mfma_f32_16x16x4_f32.
+__device__ __forceinline__ f32x4 mm16(const float *A, int lda, const float *B, int ldb, f32x4 acc,
+                                      int r16, int kg) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r16 * lda + 4 * s + kg],
+                                               B[(4 * s + kg) * ldb + r16], acc, 0, 0, 0);
+  return acc;
+}
+// D += A Y with Y a 16 x 16 block held in accumulator layout (lane (r16, kg) holds rows
+// 4 kg + e of column r16): the contraction index is taken in the order the lanes hold it.
+__device__ __forceinline__ f32x4 mm16_acc(const float *A, int lda, const f32x4 &Y, f32x4 acc,
+                                          int r16, int kg) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r16 * lda + 4 * kg + s], Y[s], acc, 0, 0, 0);
+  return acc;
+}
+
 template <typename Tin, int DK, typename TOut>
 __global__ __launch_bounds__(256) void kla_prep_kernel(
-    const Tin *__restrict__ k, const float *__restrict__ g, const float *__restrict__ eta,
-    float eps, const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq,
-    int H, float *__restrict__ G_out, float *__restrict__ beta_out, TOut *__restrict__ T_out) {
+    const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ eta, float eps, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
+    float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out) {
   __shared__ PrepSmem<Tin, DK> sm;
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= chunk_off[n_seq]) return;
@@ -117,16 +147,22 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
   const int len = min(kChunk, cu[n + 1] - t0);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kg = lane >> 4;
+  const bool want_p = (q != nullptr) && (P_out != nullptr);
+  using FragT = typename Frag<Tin>::type;
 
-  // ---- stage K rows (zero past the chunk end) and ||k_i||^2 by a lane-group reduction
+  // ---- stage K (and Q) rows (zero past the chunk end); ||k_i||^2 by a lane-group reduction
   constexpr int CPR = DK / 8;       // 8-element groups per key row
   constexpr int RPP = 256 / CPR;    // rows per pass
 #pragma unroll
   for (int pass = 0; pass < kChunk / RPP; ++pass) {
     const int row = pass * RPP + tid / CPR, cg = tid % CPR;
-    typename Frag<Tin>::type x = zero8<Tin>();
-    if (row < len) x = load8<Tin>(k + ((size_t)(t0 + row) * H + h) * DK + cg * 8);
-    *reinterpret_cast<typename Frag<Tin>::type *>(&sm.K[row][cg * 8]) = x;
+    FragT x = zero8<Tin>(), y = zero8<Tin>();
+    if (row < len) {
+      x = load8<Tin>(k + ((size_t)(t0 + row) * H + h) * DK + cg * 8);
+      if (want_p) y = load8<Tin>(q + ((size_t)(t0 + row) * H + h) * DK + cg * 8);
+    }
+    *reinterpret_cast<FragT *>(&sm.K[row][cg * 8]) = x;
+    if (want_p) *reinterpret_cast<FragT *>(&sm.Q[row][cg * 8]) = y;
     float ss = 0.f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -156,91 +192,142 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
   }
   __syncthreads();
 
-  // ---- Gram K K^T on the matrix cores, rows [16 wid, 16 wid + 16); then L
+  const int i0 = 16 * wid;  // this wave's 16 rows
+  // ---- Gram K K^T on the matrix cores (causal tiles only), then the strictly lower L
   {
-    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      const auto a = load8<Tin>(&sm.K[16 * wid + r16][32 * ks + 8 * kg]);
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const auto b = load8<Tin>(&sm.K[16 * jt + r16][32 * ks + 8 * kg]);
-        acc[jt] = mma(a, b, acc[jt]);
-      }
-    }
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
+      f32x4 acc = zero4();
+      if (jt <= wid) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wid + 4 * kg + i, col = 16 * jt + r16;
+        for (int ks = 0; ks < DK / 32; ++ks) {
+          const FragT a = load8<Tin>(&sm.K[i0 + r16][32 * ks + 8 * kg]);
+          const FragT b = load8<Tin>(&sm.K[16 * jt + r16][32 * ks + 8 * kg]);
+          acc = mma(a, b, acc);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = i0 + 4 * kg + e, col = 16 * jt + r16;
         float val = 0.f;
-        if (col < row) val = sm.beta[row] * __expf(sm.G[row] - sm.G[col]) * acc[jt][i];
+        if (col < row) val = sm.beta[row] * __expf(sm.G[row] - sm.G[col]) * acc[e];
         sm.L[row][col] = val;
+      }
+    }
+  }
+  // ---- P = A o Q K^T, as P^T = K Q^T so each lane holds 4 consecutive columns of a row
+  if (want_p) {
+    const int i = i0 + r16;
+    Tin *Pc = P_out + ((size_t)c * H + h) * (kChunk * kChunk) + (size_t)i * kChunk;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int j0 = 16 * jt + 4 * kg;
+      float pv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (jt <= wid) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) {
+          const FragT a = load8<Tin>(&sm.K[16 * jt + r16][32 * ks + 8 * kg]);
+          const FragT b = load8<Tin>(&sm.Q[i][32 * ks + 8 * kg]);
+          acc = mma(a, b, acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pv[e] = (j0 + e <= i) ? __expf(sm.G[i] - sm.G[j0 + e]) * acc[e] : 0.f;
+      }
+      if constexpr (sizeof(Tin) == 2) {
+        bf16x4 x4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x4[e] = from_f32<Tin>(pv[e]);
+        *reinterpret_cast<bf16x4 *>(Pc + j0) = x4;
+      } else {
+        *reinterpret_cast<f32x4 *>(Pc + j0) = f32x4{pv[0], pv[1], pv[2], pv[3]};
       }
     }
   }
   __syncthreads();
 
-  // ---- X = (I + L)^{-1} by forward substitution; lane = column, rows in registers.
-  // x_i = delta_ic - sum_{j<i} L_ij x_j  (x_j = 0 for j < c by construction), T_ic = x_i b_c.
-  if (wid == 0) {
-    float x[kChunk];
+  // ---- diagonal blocks: wave w inverts I + L_ww by substitution, lane = column r16
+  {
+    float x[16];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      float acc = (i == lane) ? 1.f : 0.f;
+    for (int i = 0; i < 16; ++i) {
+      float acc = (i == r16) ? 1.f : 0.f;
+      const float *Lrow = &sm.L[i0 + i][i0];
 #pragma unroll
-      for (int j = 0; j < (i & ~3); j += 4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sm.L[i][j]);
-        acc = fmaf(-l4[0], x[j + 0], acc);
-        acc = fmaf(-l4[1], x[j + 1], acc);
-        acc = fmaf(-l4[2], x[j + 2], acc);
-        acc = fmaf(-l4[3], x[j + 3], acc);
-      }
-#pragma unroll
-      for (int j = (i & ~3); j < i; ++j) acc = fmaf(-sm.L[i][j], x[j], acc);
+      for (int j = 0; j < i; ++j) acc = fmaf(-Lrow[j], x[j], acc);
       x[i] = acc;
     }
-    const float bc = sm.beta[lane];
+    if (kg == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm.X[i0 + i][i0 + r16] = x[i];
+    }
+  }
+  __syncthreads();
+  // ---- sub-diagonal blocks, one level (distance) at a time
+  constexpr int LDL = kChunk + 4;
+#pragma unroll
+  for (int dist = 1; dist < 4; ++dist) {
+    const int jb = wid, ib = wid + dist;  // block (ib, jb)
+    if (ib < 4) {
+      f32x4 Y = zero4();
+      for (int kb = jb; kb < ib; ++kb)
+        Y = mm16(&sm.L[16 * ib][16 * kb], LDL, &sm.X[16 * kb][16 * jb], LDL, Y, r16, kg);
+      f32x4 Z = mm16_acc(&sm.X[16 * ib][16 * ib], LDL, Y, zero4(), r16, kg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.X[16 * ib + 4 * kg + e][16 * jb + r16] = -Z[e];
+    }
+    __syncthreads();
+  }
+
+  // ---- T = X Diag(b), zero above the diagonal (blocks above the diagonal were never written)
+  {
     TOut *Tc = T_out + ((size_t)c * H + h) * (kChunk * kChunk);
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) Tc[i * kChunk + lane] = from_f32<TOut>(x[i] * bc);
+    for (int kk = 0; kk < kChunk * kChunk / 256; ++kk) {
+      const int e = tid + 256 * kk, row = e >> 6, j = e & 63;
+      const float val = (j <= row) ? sm.X[row][j] * sm.beta[j] : 0.f;
+      Tc[e] = from_f32<TOut>(val);
+    }
   }
 }
 
 template <typename Tin, int DK>
-static hipError_t launch_prep_t(const void *k, const float *g, const float *eta, float eps,
-                                SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
-                                float *G_out, float *beta_out, void *T_out, bool t_fp32,
-                                hipStream_t stream) {
+static hipError_t launch_prep_t(const void *q, const void *k, const float *g, const float *eta,
+                                float eps, SeqTables t, int32_t n_seq, int64_t n_chunks_ub,
+                                int32_t H, float *G_out, float *beta_out, void *T_out, bool t_fp32,
+                                void *P_out, hipStream_t stream) {
   if (n_chunks_ub <= 0) return hipSuccess;
   const dim3 grid((unsigned)n_chunks_ub, H);
+  const Tin *qq = static_cast<const Tin *>(q);
+  Tin *pp = static_cast<Tin *>(P_out);
   if (t_fp32 || sizeof(Tin) == 4)
-    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(256), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<float *>(T_out));
+                       G_out, beta_out, static_cast<float *>(T_out), pp);
   else
-    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(256), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<Tin *>(T_out));
+                       G_out, beta_out, static_cast<Tin *>(T_out), pp);
   return hipGetLastError();
 }
 
-hipError_t launch_prep(Dtype dt, int d_k, const void *k, const float *g, const float *eta,
-                       float eps, SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
-                       float *G_out, float *beta_out, void *T_out, bool t_fp32,
-                       hipStream_t stream) {
+hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const float *g,
+                       const float *eta, float eps, SeqTables t, int32_t n_seq,
+                       int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out, void *T_out,
+                       bool t_fp32, void *P_out, hipStream_t stream) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
-      return launch_prep_t<__bf16, 128>(k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                        T_out, t_fp32, stream);
-    return launch_prep_t<__bf16, 64>(k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                     T_out, t_fp32, stream);
+      return launch_prep_t<__bf16, 128>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out,
+                                        beta_out, T_out, t_fp32, P_out, stream);
+    return launch_prep_t<__bf16, 64>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
+                                     T_out, t_fp32, P_out, stream);
   }
   if (d_k == 128)
-    return launch_prep_t<float, 128>(k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                     T_out, t_fp32, stream);
-  return launch_prep_t<float, 64>(k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                  T_out, t_fp32, stream);
+    return launch_prep_t<float, 128>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
+                                     T_out, t_fp32, P_out, stream);
+  return launch_prep_t<float, 64>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
+                                  T_out, t_fp32, P_out, stream);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -1,394 +1,497 @@
 // kla_scan.hip -- inter-chunk state scan with the chunk output fused in.
 //
 // Paper "Kaczmarz Linear Attention" (arXiv 2605.08587), section 4, Propositions 3
-// and 4.  With the per-chunk T = (I + L)^{-1} Diag(b) and chunk-local log-decay G
-// from the prep stage, each chunk of a (sequence, head) is, given its incoming
-// state S (d_k x d_v, fp32):
+// and 4.  With the per-chunk T = (I + L)^{-1} Diag(b), the intra-chunk matrix
+// P = A o Q K^T and the chunk-local log-decay G from the prep stage, each chunk of a
+// (sequence, head) is, given its incoming state S (d_k x d_v, fp32):
 //   U     = T (V - Diag(exp G) K S)                      Eq. (7)
-//   O     = Diag(exp G) Q S + (A o Q K^T) U              Eq. (8), A_ij = exp(G_i - G_j), j <= i
+//   O     = Diag(exp G) Q S + P U                        Eq. (8)
 //   S_out = exp(G_last) S + K^T Diag(exp(G_last - G)) U  Eq. (9)
-// and S_out is the next chunk's S.  The chunks of one sequence are processed in
-// order by one workgroup; the d_v columns of S are independent given K, G and T,
-// so a (sequence, head) is split over d_v / 32 workgroups.
+// and S_out is the next chunk's S.  The chunks of one sequence are processed in order
+// by one workgroup; the d_v columns of S are independent given K, G, T and P, so a
+// (sequence, head) is split over d_v / 32 workgroups.
 //
-// Work split inside the workgroup (8 wavefronts, 2 per SIMD, BV = 32 state columns):
-// wave w = (mw, nw) with mw = w % 4, nw = w / 4 owns
-//   chunk rows [16 mw, 16 mw + 16) x state columns [16 nw, 16 nw + 16) for K S, Q S,
-//   T R and P U, every other j-tile of P^T = K Q^T for its chunk rows, and
-//   state rows [mw d_k / 4, (mw + 1) d_k / 4) x the same 16 columns for K^T U,
-//   which it keeps in fp32 accumulator registers for the whole sequence.
-// The next chunk's K, Q, T and V tiles are fetched once per workgroup with 16-byte
-// loads while the current chunk computes, and land in the other half of a double
-// buffer in LDS.  K^T operands, V in accumulator layout and the output rows are read
-// with the LDS transpose read (ds_read_b64_tr_b16) for 16-bit data, so no transposed
-// copy of the keys is kept; every other cross-wave operand is written with packed
-// 4-element stores because an accumulator fragment holds 4 consecutive rows of a column.
+// Workgroup = 4 wavefronts with two roles:
+//   consumers (waves 0, 1) each own 16 state columns.  The whole dependent chain
+//     S -> K S -> R -> T R -> U -> K^T U -> S stays in registers: an MFMA accumulator
+//     fragment (lane holds rows 4 kg .. 4 kg + 3 of a column) is fed straight back as
+//     the B operand of the next product, with the contraction index taken in the order
+//     the lanes hold it (k = 4 kg + s, then 16 + 4 kg + s, within each 32-wide step) and
+//     the A operand read from LDS in that same order.
+//   producers (waves 2, 3) fetch the next chunk's K, Q, T, P, V tiles with 16-byte
+//     loads one chunk ahead, write them into the other half of a double buffer in LDS,
+//     and write the previous chunk's outputs back to HBM.
+// One workgroup barrier per chunk hands a buffer from producers to consumers.
+// K, Q, T, P and the output staging buffer use an XOR-swizzled LDS layout (8-byte
+// chunk c of row r lives at chunk c ^ h(r), h(r) = 4 (r & 3) + ((r >> 2) & 3)), which
+// keeps both the 8-byte fragment reads (16 rows, one column) and the gfx950 LDS
+// transpose reads (4 rows x 4 chunks) free of bank conflicts.
 #include "kla_device.h"
 #include "kla_launch.h"
 
 namespace kla {
 
-constexpr int kBV = 32;        // state columns per workgroup
-constexpr int kScanThreads = 512;
+constexpr int kBV = 32;           // state columns per workgroup
+constexpr int kScanThreads = 256; // 2 consumer + 2 producer wavefronts
 
 // LDS-only workgroup barrier: orders LDS traffic without waiting for the global
-// loads that are deliberately left in flight (the next chunk's prefetch).
+// loads that are deliberately left in flight (the prefetch of a later chunk).
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// 4 consecutive elements of T (packed LDS store of 8 or 16 bytes).
 template <typename T> struct Vec4;
 template <> struct Vec4<__bf16> { typedef bf16x4 type; };
 template <> struct Vec4<float> { typedef f32x4 type; };
 
-template <typename T>
-__device__ __forceinline__ void store4(T *p, float a, float b, float c, float d) {
-  typename Vec4<T>::type x;
-  x[0] = from_f32<T>(a); x[1] = from_f32<T>(b); x[2] = from_f32<T>(c); x[3] = from_f32<T>(d);
-  *reinterpret_cast<typename Vec4<T>::type *>(p) = x;
+// ---- swizzled tiles (rows of ROWB bytes, ROWB a multiple of 128)
+__device__ __forceinline__ int swz_h(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+template <int ROWB>
+__device__ __forceinline__ int swz(int r, int byte) {
+  const int c8 = byte >> 3;
+  return r * ROWB + ((((c8 & ~15) | ((c8 & 15) ^ swz_h(r)))) << 3) + (byte & 7);
 }
 
-// LDS transpose read of 4 x 16-bit values (gfx950).  Within each group of 16 lanes,
-// destination lane d receives element (d & 3) of the 8-byte chunks addressed by source
-// lanes (d >> 2) + 4 i, i = 0..3.
+// 4 consecutive elements starting at element e0 (a multiple of 4) of row r.
+template <typename Tin, int ROWB>
+__device__ __forceinline__ typename Vec4<Tin>::type rd4(const unsigned char *tile, int r, int e0) {
+  if constexpr (sizeof(Tin) == 2) {
+    return *reinterpret_cast<const bf16x4 *>(tile + swz<ROWB>(r, 2 * e0));
+  } else {
+    // 16 bytes = chunks c8, c8 + 1; they share one 16-byte slot, in swapped order if h(r) is odd
+    const int c8 = e0 >> 1, h = swz_h(r);
+    const int pc = (c8 & ~15) | ((c8 & 15) ^ h);
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(tile + r * ROWB + ((pc & ~1) << 3));
+    return (h & 1) ? f32x4{x[2], x[3], x[0], x[1]} : x;
+  }
+}
+// Write one 16-byte piece (piece p = bytes 16 p .. 16 p + 15 of row r); x holds its bits.
+template <int ROWB>
+__device__ __forceinline__ void wr16(unsigned char *tile, int r, int p, f32x4 x) {
+  const int c8 = 2 * p, h = swz_h(r);
+  const int pc = (c8 & ~15) | ((c8 & 15) ^ h);
+  if (h & 1) x = f32x4{x[2], x[3], x[0], x[1]};
+  *reinterpret_cast<f32x4 *>(tile + r * ROWB + ((pc & ~1) << 3)) = x;
+}
+
+// MFMA A fragment of rows r of a swizzled tile for k-step ks, in the lane-held order
+// k = 32 ks + {4 kg .. 4 kg + 3, 16 + 4 kg .. 16 + 4 kg + 3}.
+template <typename Tin, int ROWB>
+__device__ __forceinline__ typename Frag<Tin>::type rdA(const unsigned char *tile, int r, int ks,
+                                                        int kg) {
+  const auto lo = rd4<Tin, ROWB>(tile, r, 32 * ks + 4 * kg);
+  const auto hi = rd4<Tin, ROWB>(tile, r, 32 * ks + 16 + 4 * kg);
+  typename Frag<Tin>::type a;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[e + 4] = hi[e]; }
+  return a;
+}
+
+// Accumulator tiles lo (rows 4 kg + e) and hi (rows 16 + 4 kg + e) as a B fragment.
+template <typename Tin>
+__device__ __forceinline__ typename Frag<Tin>::type accB(const f32x4 &lo, const f32x4 &hi) {
+  typename Frag<Tin>::type b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { b[e] = from_f32<Tin>(lo[e]); b[e + 4] = from_f32<Tin>(hi[e]); }
+  return b;
+}
+
+// LDS transpose read of 4 x 16-bit values (gfx950 ds_read_b64_tr_b16).  Within each group
+// of 16 lanes, destination lane d receives element (d & 3) of the 8-byte chunks addressed
+// by source lanes (d >> 2) + 4 i, i = 0..3.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4 *)(reinterpret_cast<const void *>(p)));
+__device__ __forceinline__ bf16x4 lds_read_tr(const void *p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// fp32 chunk operands are single-buffered so the tiles fit in LDS.
-template <typename Tin>
-constexpr int scan_nbuf() { return sizeof(Tin) == 4 ? 1 : 2; }
-
-template <typename Tin, int DK, int NBUF>
-struct ScanSmem {
-  static constexpr int PAD = 8;
-  static constexpr int OT = sizeof(Tin) == 2 ? kBV : 1;  // output staging (16-bit only)
-  alignas(16) Tin K[NBUF][kChunk][DK + PAD];     // chunk keys, token-major
-  alignas(16) Tin Q[NBUF][kChunk][DK + PAD];     // chunk queries, token-major
-  alignas(16) Tin T[NBUF][kChunk][kChunk + PAD]; // T = (I + L)^{-1} Diag(b), row-major
-  alignas(16) Tin V[NBUF][kChunk][kBV + PAD];    // value slice, token-major
-  alignas(16) float G[NBUF][kChunk];             // chunk-local log-decay (tail repeats G[len-1])
-  alignas(16) float gam[NBUF][kChunk];           // exp(G_i)
-  alignas(16) float dec[NBUF][kChunk];           // exp(G_last - G_i)
-  alignas(16) Tin St[kBV][DK + PAD];             // state operand copy, column-major
-  alignas(16) Tin Rt[kBV][kChunk + PAD];         // R = V - Diag(gamma) K S, column-major
-  alignas(16) Tin Ut[kBV][kChunk + PAD];         // U, column-major
-  alignas(16) Tin Udt[kBV][kChunk + PAD];        // Diag(exp(G_last - G)) U, column-major
-  alignas(16) Tin P[kChunk][kChunk + PAD];       // A o Q K^T, row-major
-  alignas(16) Tin Ot[OT][kChunk + PAD];          // output staging, column-major
+// ---- LDS layout
+template <typename Tin, int DK>
+struct ScanSlot {
+  static constexpr int KROWB = DK * (int)sizeof(Tin);        // key / query row bytes
+  static constexpr int TROWB = kChunk * (int)sizeof(Tin);    // T / P row bytes
+  static constexpr int VROW = sizeof(Tin) == 2 ? 48 : 40;    // value row (elements, padded)
+  alignas(16) unsigned char K[kChunk * KROWB];
+  alignas(16) unsigned char Q[kChunk * KROWB];
+  alignas(16) unsigned char T[kChunk * TROWB];
+  alignas(16) unsigned char P[kChunk * TROWB];
+  alignas(16) Tin V[kChunk][VROW];
+  alignas(16) float gam[kChunk];   // exp(G_i)
+  alignas(16) float dec[kChunk];   // exp(G_last - G_i)
 };
 
-// One chunk's K, Q, T, V tiles in flight: 16-byte pieces spread over the 512 threads.
+template <typename Tin>
+constexpr int scan_nslot() { return sizeof(Tin) == 2 ? 2 : 1; }
+
 template <typename Tin, int DK>
-struct ChunkRegs {
-  static constexpr int EP = 16 / sizeof(Tin);                     // elements per piece
-  static constexpr int KP = kChunk * DK / EP / kScanThreads;       // K (and Q) pieces per thread
-  static constexpr int TP = (kChunk * kChunk / EP + kScanThreads - 1) / kScanThreads;
-  static constexpr int VP = (kChunk * kBV / EP + kScanThreads - 1) / kScanThreads;
-  typedef u16x8 Piece __attribute__((unused));
-  f32x4 k[KP], q[KP], t[TP], v[VP];   // raw 16-byte pieces (bit patterns)
-  float gr, glast;                    // G of row lane and of the last row (wave 0)
+struct ScanSmem {
+  static constexpr int NSLOT = scan_nslot<Tin>();
+  // output staging for 16-bit outputs: [column][row] swizzled, rows of 64 elements
+  static constexpr int OBYTES = sizeof(Tin) == 2 ? kBV * kChunk * 2 : 16;
+  ScanSlot<Tin, DK> slot[NSLOT];
+  alignas(16) unsigned char O[NSLOT][OBYTES];
+};
+
+// Producer registers holding one chunk's tiles between their global load and the LDS write.
+template <typename Tin, int DK>
+struct ProdRegs {
+  static constexpr int EP = 16 / (int)sizeof(Tin);            // elements per 16-byte piece
+  static constexpr int KPP = kChunk * DK / EP / 128;          // K (and Q) pieces per lane
+  static constexpr int TPP = kChunk * kChunk / EP / 128;      // T (and P) pieces per lane
+  static constexpr int VPP = kChunk * kBV / EP / 128;         // V pieces per lane
+  f32x4 k[KPP], q[KPP], t[TPP], p[TPP], v[VPP];
+  float g, glast;
 };
 
 template <typename Tin, int DK>
 __global__ __launch_bounds__(kScanThreads) void kla_scan_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
-    const float *__restrict__ Gtok, const Tin *__restrict__ Tm, const float *S0,
-    Tin *__restrict__ o, float *S_T, const int32_t *__restrict__ cu,
+    const float *__restrict__ Gtok, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
+    const float *S0, Tin *__restrict__ o, float *S_T, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int n_seq, int H, int DV) {
-  constexpr int NBUF = scan_nbuf<Tin>();
-  constexpr bool B16 = sizeof(Tin) == 2;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  ScanSmem<Tin, DK, NBUF> &sm = *reinterpret_cast<ScanSmem<Tin, DK, NBUF> *>(smem_raw);
+  using SM = ScanSmem<Tin, DK>;
+  using SL = ScanSlot<Tin, DK>;
+  using PR = ProdRegs<Tin, DK>;
   using FragT = typename Frag<Tin>::type;
-  using CR = ChunkRegs<Tin, DK>;
-  constexpr int EP = CR::EP;
+  constexpr bool B16 = sizeof(Tin) == 2;
+  constexpr int NSLOT = SM::NSLOT;
+  constexpr int KROWB = SL::KROWB, TROWB = SL::TROWB;
+  constexpr int EP = PR::EP;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  SM &sm = *reinterpret_cast<SM *>(smem_raw);
 
   // XCD-aware mapping: workgroup b runs on XCD b % 8; give the d_v slices of one
   // (sequence, head) consecutive logical ids on the same XCD so they share its L2.
   const int nsl = DV / kBV;
   const int nblk = gridDim.x, b = blockIdx.x;
-  const int p = (nblk % 8 == 0) ? (b % 8) * (nblk / 8) + b / 8 : b;
-  const int slice = p % nsl, sh = p / nsl;
+  const int pidx = (nblk % 8 == 0) ? (b % 8) * (nblk / 8) + b / 8 : b;
+  const int slice = pidx % nsl, sh = pidx / nsl;
   const int h = sh % H, n = sh / H;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int mw = wid & 3, nw = wid >> 2;
+  const bool consumer = wid < 2;
   const int v0 = slice * kBV;
-  const int col = 16 * nw + r16;    // this lane's state column within the slice
   const int tb = cu[n], te = cu[n + 1];
   const int cbase = chunk_off[n];
+  const int nchunks = (te - tb + kChunk - 1) / kChunk;
 
-  constexpr int SROWS = DK / 4;     // state rows per wave
-  constexpr int SM = SROWS / 16;    // 16-row tiles per wave
-  const int srow0 = mw * SROWS;
-  const int i0 = mw * 16;           // chunk rows of this wave
-  const int nks = (i0 + 16 + 31) / 32;  // k-steps over chunk columns j < i0 + 16
-
-  // ---- one chunk's tiles: global -> registers (issued early), registers -> LDS.
-  // Rows past the chunk end are loaded from the last valid row (always in bounds) and
-  // zeroed on the way into LDS.
-  constexpr int KPR = DK / EP;      // pieces per key row
-  constexpr int TPR = kChunk / EP;  // pieces per T row
-  constexpr int VPR = kBV / EP;     // pieces per value-slice row
-  auto load_chunk = [&](CR &R, int c) {
+  // =========================== producer side ===========================
+  const int pl = tid - 128;  // producer lane 0..127
+  constexpr int KPR = DK / EP, TPR = kChunk / EP, VPR = kBV / EP;  // pieces per row
+  auto p_load = [&](PR &R, int c) {
     const int t0 = tb + c * kChunk;
     const int len = min(kChunk, te - t0);
 #pragma unroll
-    for (int j = 0; j < CR::KP; ++j) {
-      const int e = tid + kScanThreads * j, row = min(e / KPR, len - 1), pc = e % KPR;
+    for (int j = 0; j < PR::KPP; ++j) {
+      const int e = pl + 128 * j, row = min(e / KPR, len - 1), pc = e % KPR;
       const size_t off = ((size_t)(t0 + row) * H + h) * DK + pc * EP;
       R.k[j] = *reinterpret_cast<const f32x4 *>(k + off);
       R.q[j] = *reinterpret_cast<const f32x4 *>(q + off);
     }
-    const Tin *Tc = Tm + ((size_t)(cbase + c) * H + h) * (kChunk * kChunk);
+    const size_t tbase = ((size_t)(cbase + c) * H + h) * (kChunk * kChunk);
 #pragma unroll
-    for (int j = 0; j < CR::TP; ++j) {
-      const int e = tid + kScanThreads * j;
-      if (e < kChunk * TPR) R.t[j] = *reinterpret_cast<const f32x4 *>(Tc + e * EP);
+    for (int j = 0; j < PR::TPP; ++j) {
+      const int e = pl + 128 * j;
+      R.t[j] = *reinterpret_cast<const f32x4 *>(Tm + tbase + e * EP);
+      R.p[j] = *reinterpret_cast<const f32x4 *>(Pm + tbase + e * EP);
     }
 #pragma unroll
-    for (int j = 0; j < CR::VP; ++j) {
-      const int e = tid + kScanThreads * j;
-      if (e < kChunk * VPR) {
-        const int row = min(e / VPR, len - 1), pc = e % VPR;
-        R.v[j] = *reinterpret_cast<const f32x4 *>(v + ((size_t)(t0 + row) * H + h) * DV + v0 +
-                                                  pc * EP);
-      }
+    for (int j = 0; j < PR::VPP; ++j) {
+      const int e = pl + 128 * j, row = min(e / VPR, len - 1), pc = e % VPR;
+      R.v[j] = *reinterpret_cast<const f32x4 *>(v + ((size_t)(t0 + row) * H + h) * DV + v0 +
+                                                pc * EP);
     }
-    if (wid == 0) {
-      R.gr = Gtok[(size_t)(t0 + min(lane, len - 1)) * H + h];
+    if (pl < kChunk) {
+      R.g = Gtok[(size_t)(t0 + min(pl, len - 1)) * H + h];
       R.glast = Gtok[(size_t)(t0 + len - 1) * H + h];
     }
   };
-  auto store_chunk = [&](const CR &R, int c, int buf) {
+  auto p_store = [&](const PR &R, int c, SL &s) {
     const int len = min(kChunk, te - (tb + c * kChunk));
     const f32x4 z = zero4();
 #pragma unroll
-    for (int j = 0; j < CR::KP; ++j) {
-      const int e = tid + kScanThreads * j, row = e / KPR, pc = e % KPR;
-      *reinterpret_cast<f32x4 *>(&sm.K[buf][row][pc * EP]) = row < len ? R.k[j] : z;
-      *reinterpret_cast<f32x4 *>(&sm.Q[buf][row][pc * EP]) = row < len ? R.q[j] : z;
+    for (int j = 0; j < PR::KPP; ++j) {
+      const int e = pl + 128 * j, row = e / KPR, pc = e % KPR;
+      wr16<KROWB>(s.K, row, pc, row < len ? R.k[j] : z);
+      wr16<KROWB>(s.Q, row, pc, row < len ? R.q[j] : z);
     }
 #pragma unroll
-    for (int j = 0; j < CR::TP; ++j) {
-      const int e = tid + kScanThreads * j;
-      if (e < kChunk * TPR)
-        *reinterpret_cast<f32x4 *>(&sm.T[buf][e / TPR][(e % TPR) * EP]) = R.t[j];
+    for (int j = 0; j < PR::TPP; ++j) {
+      const int e = pl + 128 * j;
+      wr16<TROWB>(s.T, e / TPR, e % TPR, R.t[j]);
+      wr16<TROWB>(s.P, e / TPR, e % TPR, R.p[j]);
     }
 #pragma unroll
-    for (int j = 0; j < CR::VP; ++j) {
-      const int e = tid + kScanThreads * j;
-      if (e < kChunk * VPR) {
-        const int row = e / VPR;
-        *reinterpret_cast<f32x4 *>(&sm.V[buf][row][(e % VPR) * EP]) = row < len ? R.v[j] : z;
-      }
+    for (int j = 0; j < PR::VPP; ++j) {
+      const int e = pl + 128 * j, row = e / VPR;
+      *reinterpret_cast<f32x4 *>(&s.V[row][(e % VPR) * EP]) = row < len ? R.v[j] : z;
     }
-    if (wid == 0) {
-      sm.G[buf][lane] = R.gr;
-      sm.gam[buf][lane] = __expf(R.gr);
-      sm.dec[buf][lane] = __expf(R.glast - R.gr);
+    if (pl < kChunk) {
+      s.gam[pl] = __expf(R.g);
+      s.dec[pl] = __expf(R.glast - R.g);
     }
   };
-
-  // ---- state: fp32 accumulator tiles for rows [srow0, srow0 + SROWS) x column `col`
-  const size_t sbase = ((size_t)n * H + h) * DK * (size_t)DV;
-  f32x4 Sacc[SM];
-#pragma unroll
-  for (int mt = 0; mt < SM; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = srow0 + 16 * mt + 4 * kg + i;
-      Sacc[mt][i] = S0 ? S0[sbase + (size_t)row * DV + v0 + col] : 0.f;
-    }
-  auto write_state_operand = [&]() {
-#pragma unroll
-    for (int mt = 0; mt < SM; ++mt)
-      store4<Tin>(&sm.St[col][srow0 + 16 * mt + 4 * kg], Sacc[mt][0], Sacc[mt][1], Sacc[mt][2],
-                  Sacc[mt][3]);
-  };
-  // output rows of a finished chunk, staged column-major in sm.Ot (16-bit types): each
-  // 16-lane group reads 16 rows x 4 columns back row-major and stores 8 bytes per lane
-  auto flush_output = [&](int c) {
+  // outputs of chunk c from the staging buffer (16-bit types): each group of 16 lanes
+  // reads 16 rows x 4 columns back row-major and stores 8 bytes per lane
+  auto p_flush = [&](int c, int osl) {
     if constexpr (B16) {
       const int t0 = tb + c * kChunk;
       const int len = min(kChunk, te - t0);
-      const int G4 = 4 * wid + kg;                  // 0..31
-      const int rowbase = 16 * (G4 & 3), cb = 4 * (G4 >> 2);
-      const bf16x4 x = lds_read_tr(&sm.Ot[cb + (r16 >> 2)][rowbase + 4 * (r16 & 3)]);
-      const int row = rowbase + r16;
-      if (row < len)
-        *reinterpret_cast<bf16x4 *>(o + ((size_t)(t0 + row) * H + h) * DV + v0 + cb) = x;
+      const int G8 = pl >> 4;  // group 0..7
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int blk = G8 + 8 * jj;                 // 32 blocks of 16 rows x 4 columns
+        const int rowbase = 16 * (blk & 3), cb = 4 * (blk >> 2);
+        const bf16x4 x = lds_read_tr(
+            sm.O[osl] + swz<kChunk * 2>(cb + (r16 >> 2), 2 * (rowbase + 4 * (r16 & 3))));
+        const int row = rowbase + r16;
+        if (row < len)
+          *reinterpret_cast<bf16x4 *>(o + ((size_t)(t0 + row) * H + h) * DV + v0 + cb) = x;
+      }
     }
   };
 
-  const int nchunks = (te - tb + kChunk - 1) / kChunk;
-  CR nxt;
-  if (nchunks > 0) {
-    load_chunk(nxt, 0);
-    store_chunk(nxt, 0, 0);
+  // =========================== consumer side ===========================
+  const int cw = wid & 1;
+  const int col = 16 * cw + r16;  // this lane's state column within the slice
+  constexpr int NM = DK / 16;     // 16-row state tiles
+  const size_t sbase = ((size_t)n * H + h) * DK * (size_t)DV;
+  f32x4 Sacc[NM];
+  if (consumer) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Sacc[m][e] = S0 ? S0[sbase + (size_t)(16 * m + 4 * kg + e) * DV + v0 + col] : 0.f;
   }
-  write_state_operand();
-  lds_barrier();
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = (NBUF == 2) ? (c & 1) : 0;
+  // One chunk for one consumer wave, in four phases; each phase first issues all of its
+  // LDS fragment reads, then its MFMAs, so LDS latency is paid once per phase.  The
+  // dependent chain (phases 1-3) goes first; Q S and the output (phase 4) follow.
+  auto c_step = [&](int c, const SL &s, unsigned char *ostage) {
     const int t0 = tb + c * kChunk;
     const int len = min(kChunk, te - t0);
-    const bool has_next = c + 1 < nchunks;
-    if (c > 0) flush_output(c - 1);
-    if (has_next) load_chunk(nxt, c + 1);  // in flight while this chunk computes
+    // state as B operand, k-steps of 32 state rows (kept until phase 4)
+    FragT Sop[DK / 32];
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) Sop[ks] = accB<Tin>(Sacc[2 * ks], Sacc[2 * ks + 1]);
 
-    // ---- phase A: Y = K S and QS = Q S (16 rows x 16 columns); R = V - Diag(gamma) Y
-    f32x4 Y = zero4(), QS = zero4();
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      const FragT ak = load8<Tin>(&sm.K[buf][i0 + r16][32 * ks + 8 * kg]);
-      const FragT aq = load8<Tin>(&sm.Q[buf][i0 + r16][32 * ks + 8 * kg]);
-      const FragT bs = load8<Tin>(&sm.St[col][32 * ks + 8 * kg]);
-      Y = mma(ak, bs, Y);
-      QS = mma(aq, bs, QS);
-    }
+    // ---- phase 1: Y = K S (row tiles t of 16 chunk rows)
+    f32x4 Y[4];
     {
-      float vv[4];
-      if constexpr (B16) {
-        const bf16x4 x = lds_read_tr(&sm.V[buf][i0 + 4 * kg + (r16 >> 2)][16 * nw + 4 * (r16 & 3)]);
+      FragT aK[4][DK / 32];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = to_f32(x[e]);
-      } else {
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = to_f32(sm.V[buf][i0 + 4 * kg + e][col]);
+        for (int ks = 0; ks < DK / 32; ++ks) aK[t][ks] = rdA<Tin, KROWB>(s.K, 16 * t + r16, ks, kg);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        Y[t] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) Y[t] = mma(aK[t][ks], Sop[ks], Y[t]);
       }
-      const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&sm.gam[buf][i0 + 4 * kg]);
-      store4<Tin>(&sm.Rt[col][i0 + 4 * kg], vv[0] - g4[0] * Y[0], vv[1] - g4[1] * Y[1],
-                  vv[2] - g4[2] * Y[2], vv[3] - g4[3] * Y[3]);
     }
-    lds_barrier();
-
-    // ---- phase B: U = T R; P^T = K Q^T for every other causal j-tile of this wave's rows
+    // ---- phase 2: R = V - Diag(gamma) Y, then U = T R (row tile t needs k-steps ks <= t / 2)
+    FragT Uop0, Uop1, Udop0, Udop1;
     {
-      f32x4 U = zero4();
+      FragT aT[6];
+      aT[0] = rdA<Tin, TROWB>(s.T, r16, 0, kg);
+      aT[1] = rdA<Tin, TROWB>(s.T, 16 + r16, 0, kg);
+      aT[2] = rdA<Tin, TROWB>(s.T, 32 + r16, 0, kg);
+      aT[3] = rdA<Tin, TROWB>(s.T, 32 + r16, 1, kg);
+      aT[4] = rdA<Tin, TROWB>(s.T, 48 + r16, 0, kg);
+      aT[5] = rdA<Tin, TROWB>(s.T, 48 + r16, 1, kg);
+      float vv[4][4];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks < nks) {
-          const FragT at = load8<Tin>(&sm.T[buf][i0 + r16][32 * ks + 8 * kg]);
-          const FragT br = load8<Tin>(&sm.Rt[col][32 * ks + 8 * kg]);
-          U = mma(at, br, U);
+      for (int t = 0; t < 4; ++t) {
+        const int r0 = 16 * t + 4 * kg;
+        if constexpr (B16) {
+          const bf16x4 x = lds_read_tr(&s.V[r0 + (r16 >> 2)][16 * cw + 4 * (r16 & 3)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[t][e] = to_f32(x[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[t][e] = s.V[r0 + e][col];
         }
       }
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sm.dec[buf][i0 + 4 * kg]);
-      store4<Tin>(&sm.Ut[col][i0 + 4 * kg], U[0], U[1], U[2], U[3]);
-      store4<Tin>(&sm.Udt[col][i0 + 4 * kg], d4[0] * U[0], d4[1] * U[1], d4[2] * U[2],
-                  d4[3] * U[3]);
+      f32x4 R[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gam[16 * t + 4 * kg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R[t][e] = vv[t][e] - g4[e] * Y[t][e];
+      }
+      const FragT Rop0 = accB<Tin>(R[0], R[1]), Rop1 = accB<Tin>(R[2], R[3]);
+      f32x4 U[4];
+      U[0] = mma(aT[0], Rop0, zero4());
+      U[1] = mma(aT[1], Rop0, zero4());
+      U[2] = mma(aT[3], Rop1, mma(aT[2], Rop0, zero4()));
+      U[3] = mma(aT[5], Rop1, mma(aT[4], Rop0, zero4()));
+      f32x4 Ud[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[16 * t + 4 * kg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ud[t][e] = d4[e] * U[t][e];
+      }
+      Uop0 = accB<Tin>(U[0], U[1]);
+      Uop1 = accB<Tin>(U[2], U[3]);
+      Udop0 = accB<Tin>(Ud[0], Ud[1]);
+      Udop1 = accB<Tin>(Ud[2], Ud[3]);
     }
+    // ---- phase 3: S = exp(G_last) S + K^T Diag(exp(G_last - G)) U
     {
-      const int i = i0 + r16;  // query row held by this lane in the P^T fragments
-      const float Gi = sm.G[buf][i];
+      const float dl = s.gam[kChunk - 1];  // tail rows repeat G[len - 1]
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        if (jt <= mw && (jt & 1) == nw) {
-          f32x4 Pt = zero4();
+      for (int mh = 0; mh < NM; mh += 4) {  // 4 state tiles per batch
+        FragT aKt[4][2];
 #pragma unroll
-          for (int ks = 0; ks < DK / 32; ++ks) {
-            const FragT ak = load8<Tin>(&sm.K[buf][16 * jt + r16][32 * ks + 8 * kg]);
-            const FragT bq = load8<Tin>(&sm.Q[buf][i][32 * ks + 8 * kg]);
-            Pt = mma(ak, bq, Pt);
+        for (int mm = 0; mm < 4; ++mm) {
+          const int m = mh + mm;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            if constexpr (B16) {
+              // K^T rows 16 m + r16 over tokens 32 ks + {4 kg + i, 16 + 4 kg + i}
+              const int tok = 32 * ks + 4 * kg + (r16 >> 2);
+              const int byte = 2 * (16 * m + 4 * (r16 & 3));
+              const bf16x4 lo = lds_read_tr(s.K + swz<KROWB>(tok, byte));
+              const bf16x4 hi = lds_read_tr(s.K + swz<KROWB>(tok + 16, byte));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) { aKt[mm][ks][e] = lo[e]; aKt[mm][ks][e + 4] = hi[e]; }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                aKt[mm][ks][e] =
+                    rd4<Tin, KROWB>(s.K, 32 * ks + 4 * kg + e, (16 * m + r16) & ~3)[r16 & 3];
+                aKt[mm][ks][e + 4] =
+                    rd4<Tin, KROWB>(s.K, 32 * ks + 16 + 4 * kg + e, (16 * m + r16) & ~3)[r16 & 3];
+              }
+            }
           }
-          // Pt[e] = (Q K^T)[i][j], j = 16 jt + 4 kg + e; decay mask for j <= i
-          const int j0 = 16 * jt + 4 * kg;
-          const f32x4 gj = *reinterpret_cast<const f32x4 *>(&sm.G[buf][j0]);
-          float pv[4];
+        }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pv[e] = (j0 + e <= i) ? __expf(Gi - gj[e]) * Pt[e] : 0.f;
-          store4<Tin>(&sm.P[i][j0], pv[0], pv[1], pv[2], pv[3]);
-        } else if (jt > mw && nw == 0) {
-          store4<Tin>(&sm.P[i][16 * jt + 4 * kg], 0.f, 0.f, 0.f, 0.f);
+        for (int mm = 0; mm < 4; ++mm) {
+          const int m = mh + mm;
+          Sacc[m] *= dl;
+          Sacc[m] = mma(aKt[mm][0], Udop0, Sacc[m]);
+          Sacc[m] = mma(aKt[mm][1], Udop1, Sacc[m]);
         }
       }
     }
-    lds_barrier();
+    // ---- phase 4: O = Diag(gamma) Q S + P U (off the dependent chain)
+    {
+      FragT aP[6];
+      aP[0] = rdA<Tin, TROWB>(s.P, r16, 0, kg);
+      aP[1] = rdA<Tin, TROWB>(s.P, 16 + r16, 0, kg);
+      aP[2] = rdA<Tin, TROWB>(s.P, 32 + r16, 0, kg);
+      aP[3] = rdA<Tin, TROWB>(s.P, 32 + r16, 1, kg);
+      aP[4] = rdA<Tin, TROWB>(s.P, 48 + r16, 0, kg);
+      aP[5] = rdA<Tin, TROWB>(s.P, 48 + r16, 1, kg);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        FragT aQ[DK / 32];
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) aQ[ks] = rdA<Tin, KROWB>(s.Q, 16 * t + r16, ks, kg);
+        f32x4 QS = zero4();
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) QS = mma(aQ[ks], Sop[ks], QS);
+        const int r0 = 16 * t + 4 * kg;
+        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gam[r0]);
+        f32x4 O;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[e] = g4[e] * QS[e];
+        if (t < 2) {
+          O = mma(aP[t], Uop0, O);
+        } else {
+          O = mma(aP[2 * t - 2], Uop0, O);
+          O = mma(aP[2 * t - 1], Uop1, O);
+        }
+        if constexpr (B16) {
+          bf16x4 x4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x4[e] = from_f32<Tin>(O[e]);
+          *reinterpret_cast<bf16x4 *>(ostage + swz<kChunk * 2>(col, 2 * r0)) = x4;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (r0 + e < len) o[((size_t)(t0 + r0 + e) * H + h) * DV + v0 + col] = O[e];
+        }
+      }
+    }
+  };
 
-    // ---- phase C: O = Diag(gamma) QS + P U;  S = exp(G_last) S + K^T Udt
-    {
-      f32x4 O;
-      const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&sm.gam[buf][i0 + 4 * kg]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) O[e] = g4[e] * QS[e];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks < nks) {
-          const FragT ap = load8<Tin>(&sm.P[i0 + r16][32 * ks + 8 * kg]);
-          const FragT bu = load8<Tin>(&sm.Ut[col][32 * ks + 8 * kg]);
-          O = mma(ap, bu, O);
-        }
+  // =========================== the chunk loops ===========================
+  // The two roles run separate loops (so their registers are allocated independently)
+  // that meet at the same number of workgroup barriers.
+  if constexpr (NSLOT == 2) {
+    if (consumer) {
+      lds_barrier();  // chunk 0 staged
+      for (int c = 0; c < nchunks; ++c) {
+        c_step(c, sm.slot[c & 1], sm.O[c & 1]);
+        lds_barrier();
       }
-      if constexpr (B16) {
-        store4<Tin>(&sm.Ot[col][i0 + 4 * kg], O[0], O[1], O[2], O[3]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = i0 + 4 * kg + e;
-          if (row < len) o[((size_t)(t0 + row) * H + h) * DV + v0 + col] = from_f32<Tin>(O[e]);
-        }
+    } else {
+      PR A, B;
+      if (nchunks > 0) {
+        p_load(A, 0);
+        if (nchunks > 1) p_load(B, 1);
+        p_store(A, 0, sm.slot[0]);
+      }
+      lds_barrier();
+      // step c: fetch chunk c + 2, write out chunk c - 1's outputs, stage chunk c + 1
+      auto step = [&](int c, PR &Rstore, PR &Rload) {
+        if (c + 2 < nchunks) p_load(Rload, c + 2);
+        if (c >= 1) p_flush(c - 1, (c - 1) & 1);
+        if (c + 1 < nchunks) p_store(Rstore, c + 1, sm.slot[(c + 1) & 1]);
+        lds_barrier();
+      };
+      for (int c = 0; c < nchunks; c += 2) {
+        step(c, B, A);
+        if (c + 1 < nchunks) step(c + 1, A, B);
+      }
+      if (nchunks > 0) p_flush(nchunks - 1, (nchunks - 1) & 1);
+    }
+  } else {
+    if (consumer) {
+      lds_barrier();
+      for (int c = 0; c < nchunks; ++c) {
+        c_step(c, sm.slot[0], sm.O[0]);
+        lds_barrier();  // every consumer is done with the single buffer
+        lds_barrier();  // next chunk staged
+      }
+    } else {
+      PR A;
+      if (nchunks > 0) {
+        p_load(A, 0);
+        p_store(A, 0, sm.slot[0]);
+      }
+      lds_barrier();
+      for (int c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) p_load(A, c + 1);
+        lds_barrier();
+        if (c + 1 < nchunks) p_store(A, c + 1, sm.slot[0]);
+        lds_barrier();
       }
     }
-    {
-      const float dl = sm.gam[buf][kChunk - 1];  // exp(G_last): tail rows repeat G[len-1]
-#pragma unroll
-      for (int mt = 0; mt < SM; ++mt) Sacc[mt] *= dl;
-#pragma unroll
-      for (int ks = 0; ks < kChunk / 32; ++ks) {
-        const FragT bu = load8<Tin>(&sm.Udt[col][32 * ks + 8 * kg]);
-#pragma unroll
-        for (int mt = 0; mt < SM; ++mt) {
-          const int mb = srow0 + 16 * mt;
-          FragT a;
-          if constexpr (B16) {
-            // K^T fragment: row r16 of the 16 x 32 tile = dimension mb + r16 over 8 tokens
-            const int tok = 32 * ks + 8 * kg + (r16 >> 2);
-            const bf16x4 lo = lds_read_tr(&sm.K[buf][tok][mb + 4 * (r16 & 3)]);
-            const bf16x4 hi = lds_read_tr(&sm.K[buf][tok + 4][mb + 4 * (r16 & 3)]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[e + 4] = hi[e]; }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = sm.K[buf][32 * ks + 8 * kg + e][mb + r16];
-          }
-          Sacc[mt] = mma(a, bu, Sacc[mt]);
-        }
-      }
-    }
-    if (NBUF == 1) lds_barrier();  // single buffer: every wave is done reading this chunk
-    write_state_operand();
-    if (has_next) store_chunk(nxt, c + 1, (NBUF == 2) ? ((c + 1) & 1) : 0);
-    lds_barrier();
   }
-  if (nchunks > 0) flush_output(nchunks - 1);
 
-  if (S_T) {
+  if (consumer && S_T) {
 #pragma unroll
-    for (int mt = 0; mt < SM; ++mt)
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = srow0 + 16 * mt + 4 * kg + i;
-        S_T[sbase + (size_t)row * DV + v0 + col] = Sacc[mt][i];
-      }
+      for (int e = 0; e < 4; ++e)
+        S_T[sbase + (size_t)(16 * m + 4 * kg + e) * DV + v0 + col] = Sacc[m][e];
   }
 }
 
 template <typename Tin, int DK>
 static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const void *v,
-                                const float *G, const void *T, const float *S0, void *o,
-                                float *S_T, SeqTables t, int32_t n_seq, int32_t H,
+                                const float *G, const void *T, const void *P, const float *S0,
+                                void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
                                 hipStream_t stream) {
-  const size_t smem = sizeof(ScanSmem<Tin, DK, scan_nbuf<Tin>()>);
+  const size_t smem = sizeof(ScanSmem<Tin, DK>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK>),
@@ -400,22 +503,23 @@ static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const voi
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((kla_scan_kernel<Tin, DK>), dim3((unsigned)blocks), dim3(kScanThreads), smem,
                      stream, static_cast<const Tin *>(q), static_cast<const Tin *>(k),
-                     static_cast<const Tin *>(v), G, static_cast<const Tin *>(T), S0,
-                     static_cast<Tin *>(o), S_T, t.cu, t.chunk_off, n_seq, H, d_v);
+                     static_cast<const Tin *>(v), G, static_cast<const Tin *>(T),
+                     static_cast<const Tin *>(P), S0, static_cast<Tin *>(o), S_T, t.cu,
+                     t.chunk_off, n_seq, H, d_v);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
-                       const float *G, const void *T, const float *S0, void *o, float *S_T,
-                       SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream) {
+                       const float *G, const void *T, const void *P, const float *S0, void *o,
+                       float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
-      return launch_scan_t<__bf16, 128>(d_v, q, k, v, G, T, S0, o, S_T, t, n_seq, H, stream);
-    return launch_scan_t<__bf16, 64>(d_v, q, k, v, G, T, S0, o, S_T, t, n_seq, H, stream);
+      return launch_scan_t<__bf16, 128>(d_v, q, k, v, G, T, P, S0, o, S_T, t, n_seq, H, stream);
+    return launch_scan_t<__bf16, 64>(d_v, q, k, v, G, T, P, S0, o, S_T, t, n_seq, H, stream);
   }
   if (d_k == 128)
-    return launch_scan_t<float, 128>(d_v, q, k, v, G, T, S0, o, S_T, t, n_seq, H, stream);
-  return launch_scan_t<float, 64>(d_v, q, k, v, G, T, S0, o, S_T, t, n_seq, H, stream);
+    return launch_scan_t<float, 128>(d_v, q, k, v, G, T, P, S0, o, S_T, t, n_seq, H, stream);
+  return launch_scan_t<float, 64>(d_v, q, k, v, G, T, P, S0, o, S_T, t, n_seq, H, stream);
 }
 
 }  // namespace kla

@@ -118,20 +118,21 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
  *
  * kla_prefill_prepare: per-chunk stage (paper section 4, Algorithm 1 chunkwise
  *   panel steps 2-6 up to the triangular solve): sequence tables, the chunk-local
- *   log-decay G and T = (I + L)^{-1} Diag(b) of every chunk, written into
- *   `workspace`.  Arguments as for kla_prefill_chunked.
+ *   log-decay G, T = (I + L)^{-1} Diag(b) and the intra-chunk matrix
+ *   P = A o Q K^T of Eq. (8) for every chunk, written into `workspace`.
+ *   Arguments as for kla_prefill_chunked.
  * kla_prefill_scan: the sequential chunk scan with the outputs (Eq. (7)-(9)),
- *   reading the workspace a kla_prefill_prepare call with the same k, g, eta,
+ *   reading the workspace a kla_prefill_prepare call with the same q, k, g, eta,
  *   cu_seqlens and sizes filled earlier on the same stream (not checkable: a
  *   workspace from another problem gives wrong results, never out-of-bounds
  *   access as long as the sizes match).  q, k, v, S0, o, S_T as for
  *   kla_prefill_chunked.
  */
-kla_status kla_prefill_prepare(const void *k, const float *g, const float *eta, float eps,
-                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
-                               int32_t n_seq, int32_t total_tokens, int32_t n_heads, int32_t d_k,
-                               int32_t d_v, kla_dtype dtype, void *workspace,
-                               size_t workspace_bytes, void *stream);
+kla_status kla_prefill_prepare(const void *q, const void *k, const float *g, const float *eta,
+                               float eps, const int32_t *cu_seqlens,
+                               const int32_t *cu_seqlens_host, int32_t n_seq, int32_t total_tokens,
+                               int32_t n_heads, int32_t d_k, int32_t d_v, kla_dtype dtype,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 kla_status kla_prefill_scan(const void *q, const void *k, const void *v, const float *S0, void *o,
                             float *S_T, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
