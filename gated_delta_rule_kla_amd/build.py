@@ -1,7 +1,7 @@
 """Build libkla.so (gfx950) in-tree with hipcc.
 
 Every HIP source under csrc/ is compiled for gfx950 only, with packed-fp32
-instruction selection disabled, and linked into gated_delta_rule_kla_amd/libkla.so.
+instruction selection disabled and MFMA results kept in architectural VGPRs, and linked into gated_delta_rule_kla_amd/libkla.so.
 """
 from __future__ import annotations
 
@@ -21,6 +21,9 @@ ARCH = "gfx950"
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in the architectural VGPRs: the kernels feed them straight back
+    # into VALU work and other MFMAs, which the AGPR form would route through copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

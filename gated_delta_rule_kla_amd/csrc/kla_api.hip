@@ -45,10 +45,11 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 // Workspace layout: [cu: n_seq+1 int32][chunk_off: n_seq+1 int32][G: total*H fp32]
-//                   [T: n_chunks_ub * H * 64 * 64][P: same], each part 256-byte aligned and
-// T, P sized for fp32 (the scan reads them in the operand type).
+//                   [GD: n_chunks_ub * H * 128 fp32][T: n_chunks_ub * H * 64 * 64][P: same],
+// each part 256-byte aligned and T, P sized for fp32 (the scan reads them in the operand
+// type).
 struct WsLayout {
-  size_t off_cu, off_co, off_G, off_T, off_P, total;
+  size_t off_cu, off_co, off_G, off_GD, off_T, off_P, total;
 };
 
 WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H) {
@@ -56,8 +57,9 @@ WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H) {
   w.off_cu = 0;
   w.off_co = align256(w.off_cu + sizeof(int32_t) * (size_t)(n_seq + 1));
   w.off_G = align256(w.off_co + sizeof(int32_t) * (size_t)(n_seq + 1));
-  w.off_T = align256(w.off_G + sizeof(float) * (size_t)total_tokens * (size_t)H);
   const int64_t nch = kla::chunk_upper_bound(n_seq, total_tokens);
+  w.off_GD = align256(w.off_G + sizeof(float) * (size_t)total_tokens * (size_t)H);
+  w.off_T = align256(w.off_GD + sizeof(float) * (size_t)nch * (size_t)H * 2 * KLA_CHUNK);
   const size_t tile_bytes = sizeof(float) * (size_t)nch * (size_t)H * KLA_CHUNK * KLA_CHUNK;
   w.off_P = align256(w.off_T + tile_bytes);
   w.total = align256(w.off_P + tile_bytes);
@@ -80,6 +82,10 @@ kla_status check_prefill_shape(const int32_t *cu_seqlens_host, int32_t n_seq, in
     return fail(KLA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
   if ((int64_t)n_seq * n_heads * (d_v / 32) > 0x7fffffff)
     return fail(KLA_ERR_INVALID_ARGUMENT, "n_seq * n_heads too large");
+  // the scan addresses one 64-token chunk of a tensor with 32-bit buffer offsets
+  if ((int64_t)KLA_CHUNK * n_heads * (d_k > d_v ? d_k : d_v) * (int64_t)elem_size(dtype) > 0x7fffffff)
+    return fail(KLA_ERR_UNSUPPORTED,
+                "64 * n_heads * max(d_k, d_v) * element size must be below 2^31 bytes");
   if (cu_seqlens_host) {
     if (cu_seqlens_host[0] != 0)
       return fail(KLA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] must be 0");
@@ -167,7 +173,7 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
 
 struct WsViews {
   kla::SeqTables tabs;
-  float *G;
+  float *G, *GD;
   void *T, *P;
 };
 
@@ -176,7 +182,8 @@ WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n
   char *ws = static_cast<char *>(workspace);
   return WsViews{{reinterpret_cast<int32_t *>(ws + w.off_cu),
                   reinterpret_cast<int32_t *>(ws + w.off_co)},
-                 reinterpret_cast<float *>(ws + w.off_G), ws + w.off_T, ws + w.off_P};
+                 reinterpret_cast<float *>(ws + w.off_G), reinterpret_cast<float *>(ws + w.off_GD),
+                 ws + w.off_T, ws + w.off_P};
 }
 
 kla_status enqueue_prepare(const void *q, const void *k, const float *g, const float *eta, float eps,
@@ -189,14 +196,15 @@ kla_status enqueue_prepare(const void *q, const void *k, const float *g, const f
   if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan")) != KLA_OK)
     return st;
   return hip_status(kla::launch_prep(to_dt(dtype), d_k, q, k, g, eta, eps, wv.tabs, n_seq, nch_ub,
-                                     n_heads, wv.G, nullptr, wv.T, false, wv.P, s), "prep");
+                                     n_heads, nullptr, nullptr, wv.T, false, wv.P, wv.GD, s),
+                    "prep");
 }
 
 kla_status enqueue_scan(const void *q, const void *k, const void *v, const float *S0, void *o,
                         float *S_T, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
                         int32_t d_k, int32_t d_v, kla_dtype dtype, void *workspace, hipStream_t s) {
   const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
-  return hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.G, wv.T, wv.P, S0, o,
+  return hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0, o,
                                      S_T, wv.tabs, n_seq, n_heads, s), "scan");
 }
 
@@ -299,7 +307,8 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
   if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, tabs, s), "plan")) != KLA_OK)
     return st;
   if ((st = hip_status(kla::launch_prep(dt, d_k, nullptr, k, g, eta, eps, tabs, n_seq, nch_ub,
-                                        n_heads, Gbuf, beta, T, true, nullptr, s), "prep")) != KLA_OK)
+                                        n_heads, Gbuf, beta, T, true, nullptr, nullptr, s),
+                       "prep")) != KLA_OK)
     return st;
   if ((st = hip_status(kla::launch_wy(dt, d_k, d_v, k, v, Gbuf, T, tabs, n_seq, nch_ub, n_heads,
                                       W, Ut, s), "wy")) != KLA_OK)

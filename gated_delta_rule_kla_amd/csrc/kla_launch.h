@@ -28,19 +28,22 @@ hipError_t launch_plan(const int32_t *cu_in, int32_t n_seq, int32_t total_tokens
 // a1 + a2: b, G, Gram, L, T = (I + L)^{-1} Diag(b) per chunk-head.  T is written in fp32
 // when t_fp32 is set, else in the operand type (what the scan kernel reads).  With q and
 // P_out given, also P = A o Q K^T per chunk-head (operand type, zero above the diagonal).
+// G_out / beta_out (per token) and GD_out (per chunk-head: exp(G_i) for the 64 rows, then
+// exp(G_last - G_i)) are each optional.
 hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const float *g,
                        const float *eta, float eps, SeqTables t, int32_t n_seq,
                        int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out, void *T_out,
-                       bool t_fp32, void *P_out, hipStream_t stream);
+                       bool t_fp32, void *P_out, float *GD_out, hipStream_t stream);
 
 // Optional WY factors W = T Diag(exp G) K and U~ = T V (unit-check path).
 hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, const float *G,
                      const float *T, SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                      float *W, float *Ut, hipStream_t stream);
 
-// a3 + a4: sequential chunk scan with the output fused in.
+// a3 + a4: sequential chunk scan with the output fused in; reads T, P and the per-chunk
+// decays GD that launch_prep wrote.
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
-                       const float *G, const void *T, const void *P, const float *S0, void *o,
+                       const float *GD, const void *T, const void *P, const float *S0, void *o,
                        float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream);
 
 // a5: one decode step.

@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ eta, float eps, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
-    float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out) {
+    float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out,
+    float *__restrict__ GD_out) {
   __shared__ PrepSmem<Tin, DK> sm;
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= chunk_off[n_seq]) return;
@@ -188,6 +189,14 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
     if (valid) {
       if (G_out) G_out[th] = Gi;
       if (beta_out) beta_out[th] = bi;
+    }
+    // per-chunk decays for the scan: exp(G_i) and exp(G_last - G_i); rows past a ragged
+    // end carry G_last (their g is taken as 0), so they read exp(G_last) and 1
+    if (GD_out) {
+      const float Glast = __shfl(Gi, kChunk - 1, kWave);
+      float *gd = GD_out + ((size_t)c * H + h) * (2 * kChunk);
+      gd[lane] = __expf(Gi);
+      gd[kChunk + lane] = __expf(Glast - Gi);
     }
   }
   __syncthreads();
@@ -296,7 +305,7 @@ template <typename Tin, int DK>
 static hipError_t launch_prep_t(const void *q, const void *k, const float *g, const float *eta,
                                 float eps, SeqTables t, int32_t n_seq, int64_t n_chunks_ub,
                                 int32_t H, float *G_out, float *beta_out, void *T_out, bool t_fp32,
-                                void *P_out, hipStream_t stream) {
+                                void *P_out, float *GD_out, hipStream_t stream) {
   if (n_chunks_ub <= 0) return hipSuccess;
   const dim3 grid((unsigned)n_chunks_ub, H);
   const Tin *qq = static_cast<const Tin *>(q);
@@ -304,30 +313,30 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
   if (t_fp32 || sizeof(Tin) == 4)
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(256), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<float *>(T_out), pp);
+                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out);
   else
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(256), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<Tin *>(T_out), pp);
+                       G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const float *g,
                        const float *eta, float eps, SeqTables t, int32_t n_seq,
                        int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out, void *T_out,
-                       bool t_fp32, void *P_out, hipStream_t stream) {
+                       bool t_fp32, void *P_out, float *GD_out, hipStream_t stream) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
       return launch_prep_t<__bf16, 128>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out,
-                                        beta_out, T_out, t_fp32, P_out, stream);
+                                        beta_out, T_out, t_fp32, P_out, GD_out, stream);
     return launch_prep_t<__bf16, 64>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                     T_out, t_fp32, P_out, stream);
+                                     T_out, t_fp32, P_out, GD_out, stream);
   }
   if (d_k == 128)
     return launch_prep_t<float, 128>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                     T_out, t_fp32, P_out, stream);
+                                     T_out, t_fp32, P_out, GD_out, stream);
   return launch_prep_t<float, 64>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                  T_out, t_fp32, P_out, stream);
+                                  T_out, t_fp32, P_out, GD_out, stream);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -2,100 +2,110 @@
 //
 // Paper "Kaczmarz Linear Attention" (arXiv 2605.08587), section 4, Propositions 3
 // and 4.  With the per-chunk T = (I + L)^{-1} Diag(b), the intra-chunk matrix
-// P = A o Q K^T and the chunk-local log-decay G from the prep stage, each chunk of a
-// (sequence, head) is, given its incoming state S (d_k x d_v, fp32):
-//   U     = T (V - Diag(exp G) K S)                      Eq. (7)
-//   O     = Diag(exp G) Q S + P U                        Eq. (8)
-//   S_out = exp(G_last) S + K^T Diag(exp(G_last - G)) U  Eq. (9)
+// P = A o Q K^T, gam_i = exp(G_i) and dec_i = exp(G_last - G_i) from the prep stage, each
+// chunk of a (sequence, head) is, given its incoming state S (d_k x d_v, fp32):
+//   U     = T (V - Diag(gam) K S)                        Eq. (7)
+//   O     = Diag(gam) Q S + P U                          Eq. (8)
+//   S_out = exp(G_last) S + K^T Diag(dec) U              Eq. (9)
 // and S_out is the next chunk's S.  The chunks of one sequence are processed in order
-// by one workgroup; the d_v columns of S are independent given K, G, T and P, so a
-// (sequence, head) is split over d_v / 32 workgroups.
+// by one workgroup; the d_v columns of S are independent given K, T, P and the decays,
+// so a (sequence, head) is split over d_v / 32 workgroups.
 //
 // Workgroup = 4 wavefronts with two roles:
-//   consumers (waves 0, 1) each own 16 state columns.  The whole dependent chain
-//     S -> K S -> R -> T R -> U -> K^T U -> S stays in registers: an MFMA accumulator
-//     fragment (lane holds rows 4 kg .. 4 kg + 3 of a column) is fed straight back as
-//     the B operand of the next product, with the contraction index taken in the order
-//     the lanes hold it (k = 4 kg + s, then 16 + 4 kg + s, within each 32-wide step) and
-//     the A operand read from LDS in that same order.
-//   producers (waves 2, 3) fetch the next chunk's K, Q, T, P, V tiles with 16-byte
-//     loads one chunk ahead, write them into the other half of a double buffer in LDS,
-//     and write the previous chunk's outputs back to HBM.
-// One workgroup barrier per chunk hands a buffer from producers to consumers.
-// K, Q, T, P and the output staging buffer use an XOR-swizzled LDS layout (8-byte
-// chunk c of row r lives at chunk c ^ h(r), h(r) = 4 (r & 3) + ((r >> 2) & 3)), which
-// keeps both the 8-byte fragment reads (16 rows, one column) and the gfx950 LDS
-// transpose reads (4 rows x 4 chunks) free of bank conflicts.
+//   consumers (waves 0, 1) each own 16 state columns and keep them in registers for the
+//     whole sequence.  Every product is a 16 x 16 x 32 MFMA whose register operand is an
+//     accumulator of the previous product: a D fragment holds rows 4 kg .. 4 kg + 3 of a
+//     16-row tile, so two tiles together hold 8 contraction indices per lane, and the
+//     tiles are given index maps under which those 8 are consecutive:
+//       chunk tile t, row slot 4 a + i  <->  token 32 (t >> 1) + 8 a + 4 (t & 1) + i
+//       state tile m, row slot 4 a + i  <->  key dim 32 (m >> 1) + 8 a + 4 (m & 1) + i.
+//     The LDS operand of every product is then one 16-byte row piece of K, Q, T or P
+//     (or, for K^T, two gfx950 LDS transpose reads).  The output is formed transposed
+//     (O^T = S^T Q^T + U^T P^T, the same registers in the other operand slot), so each
+//     lane ends with 4 consecutive output columns of one token and stores them directly.
+//   producers (waves 2, 3) stream the tiles of later chunks into a ring of LDS slots
+//     with buffer loads that write LDS directly (no register staging).  Each chunk's
+//     buffer descriptors end at the sequence's last token, so rows past a ragged end
+//     read as zero, and output stores past it are dropped.
+// One workgroup barrier per chunk hands a slot from producers to consumers.
+//
+// LDS tiles are stored in 16-byte units, unit u of row r at u ^ sw(r) (twice sw for fp32
+// tiles), with sw chosen so that each half-wavefront's 16-byte fragment reads and the
+// transpose reads of K^T hit distinct bank groups.
+#include <type_traits>
+
 #include "kla_device.h"
 #include "kla_launch.h"
 
 namespace kla {
 
-constexpr int kBV = 32;           // state columns per workgroup
-constexpr int kScanThreads = 256; // 2 consumer + 2 producer wavefronts
+constexpr int kBV = 32;            // state columns per workgroup
+constexpr int kScanThreads = 256;  // 2 consumer + 2 producer wavefronts
+constexpr int kLdsBytes = 160 * 1024;
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0, byte-addressed, range checked against `bytes`).
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(Rsrc r, const void *lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lds), 16, voff, 0, 0, 0);
+}
+// Buffer stores of 8 and 16 bytes (dropped beyond the descriptor's range).
+__device__ __forceinline__ void store8(u32x2 x, Rsrc r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, 0);
+}
+__device__ __forceinline__ void store16(u32x4 x, Rsrc r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
+}
 
 // LDS-only workgroup barrier: orders LDS traffic without waiting for the global
-// loads that are deliberately left in flight (the prefetch of a later chunk).
+// loads that are deliberately left in flight.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <typename T> struct Vec4;
-template <> struct Vec4<__bf16> { typedef bf16x4 type; };
-template <> struct Vec4<float> { typedef f32x4 type; };
+// Barrier for the producer waves.  They touch LDS only through buffer-to-LDS loads, whose
+// completion they establish themselves with wait_vmcnt before arriving; the bare s_barrier
+// (a compiler barrier for memory operations) avoids the release fence, which would wait
+// for the later chunks' loads as well.
+__device__ __forceinline__ void producer_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// ---- swizzled tiles (rows of ROWB bytes, ROWB a multiple of 128)
-__device__ __forceinline__ int swz_h(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-template <int ROWB>
-__device__ __forceinline__ int swz(int r, int byte) {
-  const int c8 = byte >> 3;
-  return r * ROWB + ((((c8 & ~15) | ((c8 & 15) ^ swz_h(r)))) << 3) + (byte & 7);
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// 4 consecutive elements starting at element e0 (a multiple of 4) of row r.
-template <typename Tin, int ROWB>
-__device__ __forceinline__ typename Vec4<Tin>::type rd4(const unsigned char *tile, int r, int e0) {
-  if constexpr (sizeof(Tin) == 2) {
-    return *reinterpret_cast<const bf16x4 *>(tile + swz<ROWB>(r, 2 * e0));
-  } else {
-    // 16 bytes = chunks c8, c8 + 1; they share one 16-byte slot, in swapped order if h(r) is odd
-    const int c8 = e0 >> 1, h = swz_h(r);
-    const int pc = (c8 & ~15) | ((c8 & 15) ^ h);
-    const f32x4 x = *reinterpret_cast<const f32x4 *>(tile + r * ROWB + ((pc & ~1) << 3));
-    return (h & 1) ? f32x4{x[2], x[3], x[0], x[1]} : x;
-  }
-}
-// Write one 16-byte piece (piece p = bytes 16 p .. 16 p + 15 of row r); x holds its bits.
-template <int ROWB>
-__device__ __forceinline__ void wr16(unsigned char *tile, int r, int p, f32x4 x) {
-  const int c8 = 2 * p, h = swz_h(r);
-  const int pc = (c8 & ~15) | ((c8 & 15) ^ h);
-  if (h & 1) x = f32x4{x[2], x[3], x[0], x[1]};
-  *reinterpret_cast<f32x4 *>(tile + r * ROWB + ((pc & ~1) << 3)) = x;
+// ---- swizzles, in 16-byte units of a bf16 row (fp32 rows use twice the value)
+template <int ROW_ELEMS>
+__device__ __forceinline__ int sw_rows(int r) {
+  if constexpr (ROW_ELEMS >= 128)  // 16 units: K, Q with d_k = 128
+    return (((r >> 4) & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3);
+  else if constexpr (ROW_ELEMS == 64)  // 8 units: T, P, and K, Q with d_k = 64
+    return (((r >> 3) & 1) << 2) | (((r >> 4) & 1) << 1);
+  else  // 4 units: a 32-column value slice
+    return ((r >> 3) & 1) << 1;
 }
 
-// MFMA A fragment of rows r of a swizzled tile for k-step ks, in the lane-held order
-// k = 32 ks + {4 kg .. 4 kg + 3, 16 + 4 kg .. 16 + 4 kg + 3}.
-template <typename Tin, int ROWB>
-__device__ __forceinline__ typename Frag<Tin>::type rdA(const unsigned char *tile, int r, int ks,
-                                                        int kg) {
-  const auto lo = rd4<Tin, ROWB>(tile, r, 32 * ks + 4 * kg);
-  const auto hi = rd4<Tin, ROWB>(tile, r, 32 * ks + 16 + 4 * kg);
-  typename Frag<Tin>::type a;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[e + 4] = hi[e]; }
-  return a;
-}
-
-// Accumulator tiles lo (rows 4 kg + e) and hi (rows 16 + 4 kg + e) as a B fragment.
-template <typename Tin>
-__device__ __forceinline__ typename Frag<Tin>::type accB(const f32x4 &lo, const f32x4 &hi) {
-  typename Frag<Tin>::type b;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { b[e] = from_f32<Tin>(lo[e]); b[e + 4] = from_f32<Tin>(hi[e]); }
-  return b;
+// Byte offset of element e of row r in a swizzled tile of ROW_ELEMS elements of type T.
+template <typename T, int ROW_ELEMS>
+__device__ __forceinline__ int tile_off(int r, int e) {
+  constexpr int ES = sizeof(T), ROWB = ROW_ELEMS * ES;
+  const int byte = e * ES;
+  const int u = (byte >> 4) ^ (sw_rows<ROW_ELEMS>(r) * (ES / 2));
+  return r * ROWB + (u << 4) + (byte & 15);
 }
 
 // LDS transpose read of 4 x 16-bit values (gfx950 ds_read_b64_tr_b16).  Within each group
@@ -108,58 +118,63 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const void *p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// Token (or key dim) of row slot 4 a + i of 16-row tile t.
+__device__ __forceinline__ int tmap(int t, int a, int i) {
+  return 32 * (t >> 1) + 8 * a + 4 * (t & 1) + i;
+}
+
 // ---- LDS layout
 template <typename Tin, int DK>
 struct ScanSlot {
-  static constexpr int KROWB = DK * (int)sizeof(Tin);        // key / query row bytes
-  static constexpr int TROWB = kChunk * (int)sizeof(Tin);    // T / P row bytes
-  static constexpr int VROW = sizeof(Tin) == 2 ? 48 : 40;    // value row (elements, padded)
-  alignas(16) unsigned char K[kChunk * KROWB];
-  alignas(16) unsigned char Q[kChunk * KROWB];
-  alignas(16) unsigned char T[kChunk * TROWB];
-  alignas(16) unsigned char P[kChunk * TROWB];
-  alignas(16) Tin V[kChunk][VROW];
-  alignas(16) float gam[kChunk];   // exp(G_i)
-  alignas(16) float dec[kChunk];   // exp(G_last - G_i)
+  alignas(16) unsigned char K[kChunk * DK * sizeof(Tin)];
+  alignas(16) unsigned char Q[kChunk * DK * sizeof(Tin)];
+  alignas(16) unsigned char T[kChunk * kChunk * sizeof(Tin)];
+  alignas(16) unsigned char P[kChunk * kChunk * sizeof(Tin)];
+  alignas(16) unsigned char V[kChunk * kBV * sizeof(Tin)];
+  alignas(16) float gam[kChunk];  // exp(G_i)
+  alignas(16) float dec[kChunk];  // exp(G_last - G_i)
 };
 
-template <typename Tin>
-constexpr int scan_nslot() { return sizeof(Tin) == 2 ? 2 : 1; }
+template <typename Tin, int DK>
+constexpr int scan_nslot() {
+  constexpr int n = kLdsBytes / (int)sizeof(ScanSlot<Tin, DK>);
+  return n >= 3 ? 3 : n;
+}
 
 template <typename Tin, int DK>
 struct ScanSmem {
-  static constexpr int NSLOT = scan_nslot<Tin>();
-  // output staging for 16-bit outputs: [column][row] swizzled, rows of 64 elements
-  static constexpr int OBYTES = sizeof(Tin) == 2 ? kBV * kChunk * 2 : 16;
+  static constexpr int NSLOT = scan_nslot<Tin, DK>();
   ScanSlot<Tin, DK> slot[NSLOT];
-  alignas(16) unsigned char O[NSLOT][OBYTES];
 };
 
-// Producer registers holding one chunk's tiles between their global load and the LDS write.
+// Buffer-load-to-LDS instructions per chunk (each moves 64 lanes x 16 bytes).
 template <typename Tin, int DK>
-struct ProdRegs {
-  static constexpr int EP = 16 / (int)sizeof(Tin);            // elements per 16-byte piece
-  static constexpr int KPP = kChunk * DK / EP / 128;          // K (and Q) pieces per lane
-  static constexpr int TPP = kChunk * kChunk / EP / 128;      // T (and P) pieces per lane
-  static constexpr int VPP = kChunk * kBV / EP / 128;         // V pieces per lane
-  f32x4 k[KPP], q[KPP], t[TPP], p[TPP], v[VPP];
-  float g, glast;
+struct DmaPlan {
+  static constexpr int ES = sizeof(Tin);
+  static constexpr int NK = kChunk * DK * ES / 1024;      // per K (and per Q) tile
+  static constexpr int NT = kChunk * kChunk * ES / 1024;  // per T (and per P) tile
+  static constexpr int NV = kChunk * kBV * ES / 1024;     // value slice
+  // per producer wave: half of every tile and half of the 512-byte decay block
+  static constexpr int PER_WAVE = NK + NT + NV / 2 + 1;
+  static_assert(NK % 2 == 0 && NT % 2 == 0 && NV % 2 == 0, "tiles split over two waves");
 };
 
 template <typename Tin, int DK>
 __global__ __launch_bounds__(kScanThreads) void kla_scan_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
-    const float *__restrict__ Gtok, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
+    const float *__restrict__ GD, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
     const float *S0, Tin *__restrict__ o, float *S_T, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int n_seq, int H, int DV) {
   using SM = ScanSmem<Tin, DK>;
   using SL = ScanSlot<Tin, DK>;
-  using PR = ProdRegs<Tin, DK>;
+  using DP = DmaPlan<Tin, DK>;
   using FragT = typename Frag<Tin>::type;
+  using KQ = std::integral_constant<int, DK>;
+  using TP = std::integral_constant<int, kChunk>;
   constexpr bool B16 = sizeof(Tin) == 2;
+  constexpr int ES = sizeof(Tin);
   constexpr int NSLOT = SM::NSLOT;
-  constexpr int KROWB = SL::KROWB, TROWB = SL::TROWB;
-  constexpr int EP = PR::EP;
+  constexpr int DIST = NSLOT > 1 ? NSLOT - 1 : 1;  // chunks in flight ahead of the consumers
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SM &sm = *reinterpret_cast<SM *>(smem_raw);
 
@@ -178,301 +193,273 @@ __global__ __launch_bounds__(kScanThreads) void kla_scan_kernel(
   const int cbase = chunk_off[n];
   const int nchunks = (te - tb + kChunk - 1) / kChunk;
 
+  // Zero the slots once, so a tile row that the range check drops holds zeros or an
+  // earlier chunk's finite data whatever the hardware does with dropped lanes.
+  for (int i = tid; i < (int)(sizeof(SM) / 16); i += kScanThreads)
+    reinterpret_cast<u32x4 *>(smem_raw)[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
   // =========================== producer side ===========================
-  const int pl = tid - 128;  // producer lane 0..127
-  constexpr int KPR = DK / EP, TPR = kChunk / EP, VPR = kBV / EP;  // pieces per row
-  auto p_load = [&](PR &R, int c) {
+  // Producer wave pw issues instructions J = 2 j + pw of every tile; lane l of instruction
+  // J writes tile bytes 1024 J + 16 l, i.e. physical unit pu of row r, which holds logical
+  // unit pu ^ sw(r) of that row.
+  const int pw = wid - 2;
+  int offK[DP::NK / 2], offT[DP::NT / 2], offV[DP::NV / 2];
+  auto dma_off = [&](int J, int row_elems, int gstride_bytes, int sw_of_row) {
+    const int pbyte = 1024 * J + 16 * lane, rowb = row_elems * ES;
+    const int row = pbyte / rowb, pu = (pbyte % rowb) >> 4;
+    return row * gstride_bytes + ((pu ^ sw_of_row) << 4);
+  };
+  if (!consumer) {
+#pragma unroll
+    for (int j = 0; j < DP::NK / 2; ++j) {
+      const int J = 2 * j + pw, row = (1024 * J + 16 * lane) / (DK * ES);
+      offK[j] = dma_off(J, DK, H * DK * ES, sw_rows<DK>(row) * (ES / 2));
+    }
+#pragma unroll
+    for (int j = 0; j < DP::NT / 2; ++j) {
+      const int J = 2 * j + pw, row = (1024 * J + 16 * lane) / (kChunk * ES);
+      offT[j] = dma_off(J, kChunk, kChunk * ES, sw_rows<kChunk>(row) * (ES / 2));
+    }
+#pragma unroll
+    for (int j = 0; j < DP::NV / 2; ++j) {
+      const int J = 2 * j + pw, row = (1024 * J + 16 * lane) / (kBV * ES);
+      offV[j] = dma_off(J, kBV, H * DV * ES, sw_rows<kBV>(row) * (ES / 2));
+    }
+  }
+  // issue this wave's half of every load of chunk c into slot s
+  auto p_issue = [&](int c, SL &s) {
     const int t0 = tb + c * kChunk;
     const int len = min(kChunk, te - t0);
+    const size_t tok = (size_t)t0 * H + h;
+    const uint32_t kq_bytes = (uint32_t)(((size_t)(len - 1) * H + 1) * DK * ES);
+    const Rsrc rk = make_rsrc(k + tok * DK, kq_bytes);
+    const Rsrc rq = make_rsrc(q + tok * DK, kq_bytes);
+    const Rsrc rv =
+        make_rsrc(v + tok * DV + v0, (uint32_t)(((size_t)(len - 1) * H * DV + kBV) * ES));
+    const size_t ch = (size_t)(cbase + c) * H + h;
+    const Rsrc rt = make_rsrc(Tm + ch * (kChunk * kChunk), kChunk * kChunk * ES);
+    const Rsrc rp = make_rsrc(Pm + ch * (kChunk * kChunk), kChunk * kChunk * ES);
+    const Rsrc rg = make_rsrc(GD + ch * (2 * kChunk), 2 * kChunk * sizeof(float));
 #pragma unroll
-    for (int j = 0; j < PR::KPP; ++j) {
-      const int e = pl + 128 * j, row = min(e / KPR, len - 1), pc = e % KPR;
-      const size_t off = ((size_t)(t0 + row) * H + h) * DK + pc * EP;
-      R.k[j] = *reinterpret_cast<const f32x4 *>(k + off);
-      R.q[j] = *reinterpret_cast<const f32x4 *>(q + off);
-    }
-    const size_t tbase = ((size_t)(cbase + c) * H + h) * (kChunk * kChunk);
-#pragma unroll
-    for (int j = 0; j < PR::TPP; ++j) {
-      const int e = pl + 128 * j;
-      R.t[j] = *reinterpret_cast<const f32x4 *>(Tm + tbase + e * EP);
-      R.p[j] = *reinterpret_cast<const f32x4 *>(Pm + tbase + e * EP);
-    }
-#pragma unroll
-    for (int j = 0; j < PR::VPP; ++j) {
-      const int e = pl + 128 * j, row = min(e / VPR, len - 1), pc = e % VPR;
-      R.v[j] = *reinterpret_cast<const f32x4 *>(v + ((size_t)(t0 + row) * H + h) * DV + v0 +
-                                                pc * EP);
-    }
-    if (pl < kChunk) {
-      R.g = Gtok[(size_t)(t0 + min(pl, len - 1)) * H + h];
-      R.glast = Gtok[(size_t)(t0 + len - 1) * H + h];
-    }
-  };
-  auto p_store = [&](const PR &R, int c, SL &s) {
-    const int len = min(kChunk, te - (tb + c * kChunk));
-    const f32x4 z = zero4();
-#pragma unroll
-    for (int j = 0; j < PR::KPP; ++j) {
-      const int e = pl + 128 * j, row = e / KPR, pc = e % KPR;
-      wr16<KROWB>(s.K, row, pc, row < len ? R.k[j] : z);
-      wr16<KROWB>(s.Q, row, pc, row < len ? R.q[j] : z);
+    for (int j = 0; j < DP::NK / 2; ++j) {
+      const int J = 2 * j + pw;
+      dma16(rk, s.K + 1024 * J, offK[j]);
+      dma16(rq, s.Q + 1024 * J, offK[j]);
     }
 #pragma unroll
-    for (int j = 0; j < PR::TPP; ++j) {
-      const int e = pl + 128 * j;
-      wr16<TROWB>(s.T, e / TPR, e % TPR, R.t[j]);
-      wr16<TROWB>(s.P, e / TPR, e % TPR, R.p[j]);
+    for (int j = 0; j < DP::NT / 2; ++j) {
+      const int J = 2 * j + pw;
+      dma16(rt, s.T + 1024 * J, offT[j]);
+      dma16(rp, s.P + 1024 * J, offT[j]);
     }
 #pragma unroll
-    for (int j = 0; j < PR::VPP; ++j) {
-      const int e = pl + 128 * j, row = e / VPR;
-      *reinterpret_cast<f32x4 *>(&s.V[row][(e % VPR) * EP]) = row < len ? R.v[j] : z;
+    for (int j = 0; j < DP::NV / 2; ++j) {
+      const int J = 2 * j + pw;
+      dma16(rv, s.V + 1024 * J, offV[j]);
     }
-    if (pl < kChunk) {
-      s.gam[pl] = __expf(R.g);
-      s.dec[pl] = __expf(R.glast - R.g);
-    }
-  };
-  // outputs of chunk c from the staging buffer (16-bit types): each group of 16 lanes
-  // reads 16 rows x 4 columns back row-major and stores 8 bytes per lane
-  auto p_flush = [&](int c, int osl) {
-    if constexpr (B16) {
-      const int t0 = tb + c * kChunk;
-      const int len = min(kChunk, te - t0);
-      const int G8 = pl >> 4;  // group 0..7
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int blk = G8 + 8 * jj;                 // 32 blocks of 16 rows x 4 columns
-        const int rowbase = 16 * (blk & 3), cb = 4 * (blk >> 2);
-        const bf16x4 x = lds_read_tr(
-            sm.O[osl] + swz<kChunk * 2>(cb + (r16 >> 2), 2 * (rowbase + 4 * (r16 & 3))));
-        const int row = rowbase + r16;
-        if (row < len)
-          *reinterpret_cast<bf16x4 *>(o + ((size_t)(t0 + row) * H + h) * DV + v0 + cb) = x;
-      }
-    }
+    // decays: wave 0 fetches gam (bytes 0..255), wave 1 dec (256..511), 16 lanes each
+    if (lane < 16)
+      dma16(rg, reinterpret_cast<unsigned char *>(s.gam) + 256 * pw, 256 * pw + 16 * lane);
   };
 
   // =========================== consumer side ===========================
   const int cw = wid & 1;
   const int col = 16 * cw + r16;  // this lane's state column within the slice
   constexpr int NM = DK / 16;     // 16-row state tiles
+  constexpr int NKS = DK / 32;    // k-steps over d_k
   const size_t sbase = ((size_t)n * H + h) * DK * (size_t)DV;
   f32x4 Sacc[NM];
   if (consumer) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Sacc[m][e] = S0 ? S0[sbase + (size_t)(16 * m + 4 * kg + e) * DV + v0 + col] : 0.f;
+      for (int i = 0; i < 4; ++i)
+        Sacc[m][i] = S0 ? S0[sbase + (size_t)tmap(m, kg, i) * DV + v0 + col] : 0.f;
   }
-  // One chunk for one consumer wave, in four phases; each phase first issues all of its
-  // LDS fragment reads, then its MFMAs, so LDS latency is paid once per phase.  The
-  // dependent chain (phases 1-3) goes first; Q S and the output (phase 4) follow.
-  auto c_step = [&](int c, const SL &s, unsigned char *ostage) {
+  // row of this lane's A/B operand fragments in 16-row tile t
+  auto frow = [&](int t) { return tmap(t, r16 >> 2, r16 & 3); };
+  // elements 32 ks + 8 kg .. + 7 of row r (16 bytes for bf16, 32 for fp32)
+  auto rd_frag = [&](const unsigned char *tile, auto row_elems, int r, int ks) {
+    constexpr int RE = decltype(row_elems)::value;
+    if constexpr (B16) {
+      return *reinterpret_cast<const bf16x8 *>(tile + tile_off<Tin, RE>(r, 32 * ks + 8 * kg));
+    } else {
+      const f32x4 lo =
+          *reinterpret_cast<const f32x4 *>(tile + tile_off<Tin, RE>(r, 32 * ks + 8 * kg));
+      const f32x4 hi =
+          *reinterpret_cast<const f32x4 *>(tile + tile_off<Tin, RE>(r, 32 * ks + 8 * kg + 4));
+      return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  // accumulator tiles lo (contraction slots 0..3) and hi (4..7) as one operand fragment
+  auto accB = [&](const f32x4 &lo, const f32x4 &hi) {
+    FragT r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = from_f32<Tin>(lo[i]); r[i + 4] = from_f32<Tin>(hi[i]); }
+    return r;
+  };
+
+  auto c_step = [&](int c, const SL &s) {
     const int t0 = tb + c * kChunk;
     const int len = min(kChunk, te - t0);
-    // state as B operand, k-steps of 32 state rows (kept until phase 4)
-    FragT Sop[DK / 32];
+    FragT Sop[NKS];
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) Sop[ks] = accB<Tin>(Sacc[2 * ks], Sacc[2 * ks + 1]);
+    for (int ks = 0; ks < NKS; ++ks) Sop[ks] = accB(Sacc[2 * ks], Sacc[2 * ks + 1]);
 
-    // ---- phase 1: Y = K S (row tiles t of 16 chunk rows)
-    f32x4 Y[4];
-    {
-      FragT aK[4][DK / 32];
+    // ---- Y = K S and (Q S)^T, both from the incoming state
+    f32x4 Y[4], OT[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      Y[t] = zero4();
+      OT[t] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) aK[t][ks] = rdA<Tin, KROWB>(s.K, 16 * t + r16, ks, kg);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        Y[t] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) Y[t] = mma(aK[t][ks], Sop[ks], Y[t]);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const FragT a = rd_frag(s.K, KQ{}, frow(t), ks);
+        const FragT bq = rd_frag(s.Q, KQ{}, frow(t), ks);
+        Y[t] = mma(a, Sop[ks], Y[t]);
+        OT[t] = mma(Sop[ks], bq, OT[t]);
       }
     }
-    // ---- phase 2: R = V - Diag(gamma) Y, then U = T R (row tile t needs k-steps ks <= t / 2)
-    FragT Uop0, Uop1, Udop0, Udop1;
+    // ---- R = V - Diag(gam) Y, U = T R (row tile t needs k-steps ks <= t / 2)
+    FragT Uop[2], Udop[2];
     {
-      FragT aT[6];
-      aT[0] = rdA<Tin, TROWB>(s.T, r16, 0, kg);
-      aT[1] = rdA<Tin, TROWB>(s.T, 16 + r16, 0, kg);
-      aT[2] = rdA<Tin, TROWB>(s.T, 32 + r16, 0, kg);
-      aT[3] = rdA<Tin, TROWB>(s.T, 32 + r16, 1, kg);
-      aT[4] = rdA<Tin, TROWB>(s.T, 48 + r16, 0, kg);
-      aT[5] = rdA<Tin, TROWB>(s.T, 48 + r16, 1, kg);
-      float vv[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r0 = 16 * t + 4 * kg;
-        if constexpr (B16) {
-          const bf16x4 x = lds_read_tr(&s.V[r0 + (r16 >> 2)][16 * cw + 4 * (r16 & 3)]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vv[t][e] = to_f32(x[e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vv[t][e] = s.V[r0 + e][col];
-        }
-      }
       f32x4 R[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gam[16 * t + 4 * kg]);
+        const int r0 = tmap(t, kg, 0);
+        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gam[r0]);
+        float vv[4];
+        if constexpr (B16) {
+          const bf16x4 x =
+              lds_read_tr(s.V + tile_off<Tin, kBV>(r0 + (r16 >> 2), 16 * cw + 4 * (r16 & 3)));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) R[t][e] = vv[t][e] - g4[e] * Y[t][e];
+          for (int i = 0; i < 4; ++i) vv[i] = to_f32(x[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vv[i] = *reinterpret_cast<const float *>(s.V + tile_off<Tin, kBV>(r0 + i, col));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) R[t][i] = vv[i] - g4[i] * Y[t][i];
       }
-      const FragT Rop0 = accB<Tin>(R[0], R[1]), Rop1 = accB<Tin>(R[2], R[3]);
+      const FragT Rop0 = accB(R[0], R[1]), Rop1 = accB(R[2], R[3]);
       f32x4 U[4];
-      U[0] = mma(aT[0], Rop0, zero4());
-      U[1] = mma(aT[1], Rop0, zero4());
-      U[2] = mma(aT[3], Rop1, mma(aT[2], Rop0, zero4()));
-      U[3] = mma(aT[5], Rop1, mma(aT[4], Rop0, zero4()));
+      U[0] = mma(rd_frag(s.T, TP{}, frow(0), 0), Rop0, zero4());
+      U[1] = mma(rd_frag(s.T, TP{}, frow(1), 0), Rop0, zero4());
+      U[2] = mma(rd_frag(s.T, TP{}, frow(2), 1), Rop1,
+                 mma(rd_frag(s.T, TP{}, frow(2), 0), Rop0, zero4()));
+      U[3] = mma(rd_frag(s.T, TP{}, frow(3), 1), Rop1,
+                 mma(rd_frag(s.T, TP{}, frow(3), 0), Rop0, zero4()));
       f32x4 Ud[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[16 * t + 4 * kg]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[tmap(t, kg, 0)]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Ud[t][e] = d4[e] * U[t][e];
+        for (int i = 0; i < 4; ++i) Ud[t][i] = d4[i] * U[t][i];
       }
-      Uop0 = accB<Tin>(U[0], U[1]);
-      Uop1 = accB<Tin>(U[2], U[3]);
-      Udop0 = accB<Tin>(Ud[0], Ud[1]);
-      Udop1 = accB<Tin>(Ud[2], Ud[3]);
+      Uop[0] = accB(U[0], U[1]);
+      Uop[1] = accB(U[2], U[3]);
+      Udop[0] = accB(Ud[0], Ud[1]);
+      Udop[1] = accB(Ud[2], Ud[3]);
     }
-    // ---- phase 3: S = exp(G_last) S + K^T Diag(exp(G_last - G)) U
+    // ---- S = exp(G_last) S + K^T Diag(dec) U; the A operand rows are the key dims of
+    //      state tile m, read from K with the transpose reads
     {
-      const float dl = s.gam[kChunk - 1];  // tail rows repeat G[len - 1]
+      const float dl = s.gam[kChunk - 1];  // rows past a ragged end repeat G_last
 #pragma unroll
-      for (int mh = 0; mh < NM; mh += 4) {  // 4 state tiles per batch
-        FragT aKt[4][2];
+      for (int m = 0; m < NM; ++m) {
+        FragT aKt[2];
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
-          const int m = mh + mm;
+        for (int ks = 0; ks < 2; ++ks) {
+          if constexpr (B16) {
+            // source lane r16 of group kg: token 32 ks + 8 kg + (r16 >> 2) (+ 4 for the
+            // second read), key dims 32 (m >> 1) + 8 (r16 & 3) + 4 (m & 1) .. + 3
+            const int dk0 = 32 * (m >> 1) + 8 * (r16 & 3) + 4 * (m & 1);
+            const int tk = 32 * ks + 8 * kg + (r16 >> 2);
+            const bf16x4 lo = lds_read_tr(s.K + tile_off<Tin, DK>(tk, dk0));
+            const bf16x4 hi = lds_read_tr(s.K + tile_off<Tin, DK>(tk + 4, dk0));
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            if constexpr (B16) {
-              // K^T rows 16 m + r16 over tokens 32 ks + {4 kg + i, 16 + 4 kg + i}
-              const int tok = 32 * ks + 4 * kg + (r16 >> 2);
-              const int byte = 2 * (16 * m + 4 * (r16 & 3));
-              const bf16x4 lo = lds_read_tr(s.K + swz<KROWB>(tok, byte));
-              const bf16x4 hi = lds_read_tr(s.K + swz<KROWB>(tok + 16, byte));
+            for (int i = 0; i < 4; ++i) { aKt[ks][i] = lo[i]; aKt[ks][i + 4] = hi[i]; }
+          } else {
+            const int dkr = frow(m);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) { aKt[mm][ks][e] = lo[e]; aKt[mm][ks][e + 4] = hi[e]; }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                aKt[mm][ks][e] =
-                    rd4<Tin, KROWB>(s.K, 32 * ks + 4 * kg + e, (16 * m + r16) & ~3)[r16 & 3];
-                aKt[mm][ks][e + 4] =
-                    rd4<Tin, KROWB>(s.K, 32 * ks + 16 + 4 * kg + e, (16 * m + r16) & ~3)[r16 & 3];
-              }
-            }
+            for (int e = 0; e < 8; ++e)
+              aKt[ks][e] = *reinterpret_cast<const float *>(
+                  s.K + tile_off<Tin, DK>(32 * ks + 8 * kg + e, dkr));
           }
         }
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
-          const int m = mh + mm;
-          Sacc[m] *= dl;
-          Sacc[m] = mma(aKt[mm][0], Udop0, Sacc[m]);
-          Sacc[m] = mma(aKt[mm][1], Udop1, Sacc[m]);
-        }
+        Sacc[m] *= dl;
+        Sacc[m] = mma(aKt[0], Udop[0], Sacc[m]);
+        Sacc[m] = mma(aKt[1], Udop[1], Sacc[m]);
       }
     }
-    // ---- phase 4: O = Diag(gamma) Q S + P U (off the dependent chain)
+    // ---- O^T = Diag(gam) (Q S)^T + U^T P^T: lane (r16, kg) holds token frow(t), columns
+    //      16 cw + 4 kg .. + 3 of this slice, stored straight to HBM
     {
-      FragT aP[6];
-      aP[0] = rdA<Tin, TROWB>(s.P, r16, 0, kg);
-      aP[1] = rdA<Tin, TROWB>(s.P, 16 + r16, 0, kg);
-      aP[2] = rdA<Tin, TROWB>(s.P, 32 + r16, 0, kg);
-      aP[3] = rdA<Tin, TROWB>(s.P, 32 + r16, 1, kg);
-      aP[4] = rdA<Tin, TROWB>(s.P, 48 + r16, 0, kg);
-      aP[5] = rdA<Tin, TROWB>(s.P, 48 + r16, 1, kg);
+      const size_t obase = ((size_t)t0 * H + h) * DV + v0;
+      const Rsrc ro = make_rsrc(o + obase, (uint32_t)(((size_t)(len - 1) * H * DV + kBV) * ES));
+      const int lrow = 8 * (r16 >> 2) + (r16 & 3);
+      const int voff = (lrow * H * DV + 16 * cw + 4 * kg) * ES;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        FragT aQ[DK / 32];
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) aQ[ks] = rdA<Tin, KROWB>(s.Q, 16 * t + r16, ks, kg);
-        f32x4 QS = zero4();
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) QS = mma(aQ[ks], Sop[ks], QS);
-        const int r0 = 16 * t + 4 * kg;
-        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gam[r0]);
-        f32x4 O;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[e] = g4[e] * QS[e];
-        if (t < 2) {
-          O = mma(aP[t], Uop0, O);
-        } else {
-          O = mma(aP[2 * t - 2], Uop0, O);
-          O = mma(aP[2 * t - 1], Uop1, O);
-        }
+        const float gt = s.gam[frow(t)];
+        f32x4 O = OT[t] * gt;
+        O = mma(Uop[0], rd_frag(s.P, TP{}, frow(t), 0), O);
+        if (t >= 2) O = mma(Uop[1], rd_frag(s.P, TP{}, frow(t), 1), O);
+        const int soff = (32 * (t >> 1) + 4 * (t & 1)) * H * DV * ES;
         if constexpr (B16) {
           bf16x4 x4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x4[e] = from_f32<Tin>(O[e]);
-          *reinterpret_cast<bf16x4 *>(ostage + swz<kChunk * 2>(col, 2 * r0)) = x4;
+          for (int i = 0; i < 4; ++i) x4[i] = from_f32<Tin>(O[i]);
+          store8(__builtin_bit_cast(u32x2, x4), ro, voff, soff);
         } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (r0 + e < len) o[((size_t)(t0 + r0 + e) * H + h) * DV + v0 + col] = O[e];
+          store16(__builtin_bit_cast(u32x4, O), ro, voff, soff);
         }
       }
     }
   };
 
   // =========================== the chunk loops ===========================
-  // The two roles run separate loops (so their registers are allocated independently)
-  // that meet at the same number of workgroup barriers.
-  if constexpr (NSLOT == 2) {
+  // The two roles run separate loops that meet at the same number of workgroup barriers.
+  if constexpr (NSLOT >= 2) {
+    // one barrier before the first chunk and one after each chunk
     if (consumer) {
       lds_barrier();  // chunk 0 staged
       for (int c = 0; c < nchunks; ++c) {
-        c_step(c, sm.slot[c & 1], sm.O[c & 1]);
+        c_step(c, sm.slot[c % NSLOT]);
         lds_barrier();
       }
     } else {
-      PR A, B;
-      if (nchunks > 0) {
-        p_load(A, 0);
-        if (nchunks > 1) p_load(B, 1);
-        p_store(A, 0, sm.slot[0]);
+      const int pro = min(DIST, nchunks);
+      for (int c = 0; c < pro; ++c) p_issue(c, sm.slot[c]);
+      // chunk 0 complete: only chunk 1's loads (when DIST == 2) may still be in flight
+      if (DIST == 2 && pro == 2) wait_vmcnt<DP::PER_WAVE>(); else wait_vmcnt<0>();
+      producer_barrier();
+      for (int c = 0; c < nchunks; ++c) {
+        // slot (c + DIST) % NSLOT held chunk c - 1, released at the barrier just passed
+        if (c + DIST < nchunks) p_issue(c + DIST, sm.slot[(c + DIST) % NSLOT]);
+        // chunk c + 1 must be in LDS before the barrier that starts it
+        if (DIST == 2 && c + 2 < nchunks) wait_vmcnt<DP::PER_WAVE>(); else wait_vmcnt<0>();
+        producer_barrier();
       }
-      lds_barrier();
-      // step c: fetch chunk c + 2, write out chunk c - 1's outputs, stage chunk c + 1
-      auto step = [&](int c, PR &Rstore, PR &Rload) {
-        if (c + 2 < nchunks) p_load(Rload, c + 2);
-        if (c >= 1) p_flush(c - 1, (c - 1) & 1);
-        if (c + 1 < nchunks) p_store(Rstore, c + 1, sm.slot[(c + 1) & 1]);
-        lds_barrier();
-      };
-      for (int c = 0; c < nchunks; c += 2) {
-        step(c, B, A);
-        if (c + 1 < nchunks) step(c + 1, A, B);
-      }
-      if (nchunks > 0) p_flush(nchunks - 1, (nchunks - 1) & 1);
     }
   } else {
+    // a single slot: one barrier before the loop, then two per chunk (staged, released)
     if (consumer) {
       lds_barrier();
       for (int c = 0; c < nchunks; ++c) {
-        c_step(c, sm.slot[0], sm.O[0]);
-        lds_barrier();  // every consumer is done with the single buffer
-        lds_barrier();  // next chunk staged
+        lds_barrier();
+        c_step(c, sm.slot[0]);
+        lds_barrier();
       }
     } else {
-      PR A;
-      if (nchunks > 0) {
-        p_load(A, 0);
-        p_store(A, 0, sm.slot[0]);
-      }
-      lds_barrier();
+      producer_barrier();
       for (int c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) p_load(A, c + 1);
-        lds_barrier();
-        if (c + 1 < nchunks) p_store(A, c + 1, sm.slot[0]);
-        lds_barrier();
+        p_issue(c, sm.slot[0]);
+        wait_vmcnt<0>();
+        producer_barrier();
+        producer_barrier();
       }
     }
   }
@@ -481,16 +468,17 @@ __global__ __launch_bounds__(kScanThreads) void kla_scan_kernel(
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        S_T[sbase + (size_t)(16 * m + 4 * kg + e) * DV + v0 + col] = Sacc[m][e];
+      for (int i = 0; i < 4; ++i)
+        S_T[sbase + (size_t)tmap(m, kg, i) * DV + v0 + col] = Sacc[m][i];
   }
 }
 
 template <typename Tin, int DK>
 static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const void *v,
-                                const float *G, const void *T, const void *P, const float *S0,
+                                const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
                                 hipStream_t stream) {
+  static_assert(sizeof(ScanSmem<Tin, DK>) <= kLdsBytes, "LDS budget");
   const size_t smem = sizeof(ScanSmem<Tin, DK>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
@@ -503,23 +491,23 @@ static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const voi
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((kla_scan_kernel<Tin, DK>), dim3((unsigned)blocks), dim3(kScanThreads), smem,
                      stream, static_cast<const Tin *>(q), static_cast<const Tin *>(k),
-                     static_cast<const Tin *>(v), G, static_cast<const Tin *>(T),
+                     static_cast<const Tin *>(v), GD, static_cast<const Tin *>(T),
                      static_cast<const Tin *>(P), S0, static_cast<Tin *>(o), S_T, t.cu,
                      t.chunk_off, n_seq, H, d_v);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
-                       const float *G, const void *T, const void *P, const float *S0, void *o,
+                       const float *GD, const void *T, const void *P, const float *S0, void *o,
                        float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
-      return launch_scan_t<__bf16, 128>(d_v, q, k, v, G, T, P, S0, o, S_T, t, n_seq, H, stream);
-    return launch_scan_t<__bf16, 64>(d_v, q, k, v, G, T, P, S0, o, S_T, t, n_seq, H, stream);
+      return launch_scan_t<__bf16, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream);
+    return launch_scan_t<__bf16, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream);
   }
   if (d_k == 128)
-    return launch_scan_t<float, 128>(d_v, q, k, v, G, T, P, S0, o, S_T, t, n_seq, H, stream);
-  return launch_scan_t<float, 64>(d_v, q, k, v, G, T, P, S0, o, S_T, t, n_seq, H, stream);
+    return launch_scan_t<float, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream);
+  return launch_scan_t<float, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream);
 }
 
 }  // namespace kla

@@ -102,6 +102,9 @@ size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t 
  * Zero-length sequences are allowed (their S_T is S0, or zeros).  When
  * total_tokens is 0 the token buffers q, k, v, g, eta and o may be NULL.
  * q, k, v, g, eta and o must not overlap each other or the workspace.
+ * Sizes: d_k in {64, 128}, d_v in {64, 128, 256}; one chunk of a token tensor,
+ * 64 * n_heads * max(d_k, d_v) * element size, must be below 2^31 bytes
+ * (KLA_ERR_UNSUPPORTED otherwise).
  */
 kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
                                const float *eta, float eps, const float *S0, void *o,
@@ -118,8 +121,9 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
  *
  * kla_prefill_prepare: per-chunk stage (paper section 4, Algorithm 1 chunkwise
  *   panel steps 2-6 up to the triangular solve): sequence tables, the chunk-local
- *   log-decay G, T = (I + L)^{-1} Diag(b) and the intra-chunk matrix
- *   P = A o Q K^T of Eq. (8) for every chunk, written into `workspace`.
+ *   decays exp(G_i) and exp(G_last - G_i), T = (I + L)^{-1} Diag(b) and the
+ *   intra-chunk matrix P = A o Q K^T of Eq. (8) for every chunk, written into
+ *   `workspace`.
  *   Arguments as for kla_prefill_chunked.
  * kla_prefill_scan: the sequential chunk scan with the outputs (Eq. (7)-(9)),
  *   reading the workspace a kla_prefill_prepare call with the same q, k, g, eta,

@@ -49,11 +49,12 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes_formula(lib):
-    # cu + chunk offsets + G (fp32 per token-head) + T (64x64 fp32 per chunk-head upper bound)
+    # cu + chunk offsets + G (fp32 per token-head) + decays (2 x 64 fp32 per chunk-head)
+    # + T and P (64x64 fp32 each per chunk-head), chunk count bounded by ceil(n/64) + n_seq
     n_seq, n_tok, H = 4, 16384, 16
     nb = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, 128, 128)
     nch = (n_tok + 63) // 64 + n_seq
-    assert nb >= 4 * n_tok * H + 4 * nch * H * 64 * 64
+    assert nb >= 4 * n_tok * H + 4 * nch * H * 128 + 2 * 4 * nch * H * 64 * 64
     assert nb % 256 == 0
     assert kla.kla_prefill_workspace_bytes(4, 100, 16, 96, 128) == 0
     assert kla.kla_prefill_workspace_bytes(0, 100, 16, 128, 128) == 0
@@ -100,6 +101,8 @@ def _decode(lib, **over):
     (dict(o=FAKE), INVALID),             # o overlaps q
     (dict(ws=None), WORKSPACE),
     (dict(ws=FAKE * 64, ws_bytes=16), WORKSPACE),
+    # one 64-token chunk of o would span 64 * 40000 * 256 * 4 bytes > 2^31
+    (dict(dtype=0, H=40000, dv=256, total=2, n_seq=2), UNSUPPORTED),
 ])
 def test_prefill_argument_errors(lib, over, status):
     assert _prefill(lib, **over) == status
