@@ -159,8 +159,11 @@ struct DmaPlan {
   static_assert(NK % 2 == 0 && NT % 2 == 0 && NV % 2 == 0, "tiles split over two waves");
 };
 
+// One workgroup fills a CU's LDS, so each SIMD runs a single wave: let the compiler use
+// the registers that frees to issue LDS reads well ahead of the MFMAs that consume them.
 template <typename Tin, int DK>
-__global__ __launch_bounds__(kScanThreads) void kla_scan_kernel(
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void kla_scan_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ GD, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
     const float *S0, Tin *__restrict__ o, float *S_T, const int32_t *__restrict__ cu,
@@ -300,12 +303,51 @@ __global__ __launch_bounds__(kScanThreads) void kla_scan_kernel(
     return r;
   };
 
+  // One chunk.  All LDS operands of a phase are read into registers before the phase's
+  // MFMAs, and the next phase's reads are issued while those MFMAs run.
   auto c_step = [&](int c, const SL &s) {
     const int t0 = tb + c * kChunk;
     const int len = min(kChunk, te - t0);
     FragT Sop[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) Sop[ks] = accB(Sacc[2 * ks], Sacc[2 * ks + 1]);
+
+    // ---- reads for Y = K S and (Q S)^T
+    FragT fk[4][NKS], fq[4][NKS];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        fk[t][ks] = rd_frag(s.K, KQ{}, frow(t), ks);
+        fq[t][ks] = rd_frag(s.Q, KQ{}, frow(t), ks);
+      }
+    // ---- reads for R = V - Diag(gam) Y and U = T R
+    FragT ft[6];
+    ft[0] = rd_frag(s.T, TP{}, frow(0), 0);
+    ft[1] = rd_frag(s.T, TP{}, frow(1), 0);
+    ft[2] = rd_frag(s.T, TP{}, frow(2), 0);
+    ft[3] = rd_frag(s.T, TP{}, frow(2), 1);
+    ft[4] = rd_frag(s.T, TP{}, frow(3), 0);
+    ft[5] = rd_frag(s.T, TP{}, frow(3), 1);
+    f32x4 g4[4], d4[4];
+    float vv[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r0 = tmap(t, kg, 0);
+      g4[t] = *reinterpret_cast<const f32x4 *>(&s.gam[r0]);
+      d4[t] = *reinterpret_cast<const f32x4 *>(&s.dec[r0]);
+      if constexpr (B16) {
+        const bf16x4 x =
+            lds_read_tr(s.V + tile_off<Tin, kBV>(r0 + (r16 >> 2), 16 * cw + 4 * (r16 & 3)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[t][i] = to_f32(x[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vv[t][i] = *reinterpret_cast<const float *>(s.V + tile_off<Tin, kBV>(r0 + i, col));
+      }
+    }
+    const float dl = s.gam[kChunk - 1];  // rows past a ragged end repeat G_last
 
     // ---- Y = K S and (Q S)^T, both from the incoming state
     f32x4 Y[4], OT[4];
@@ -315,84 +357,74 @@ __global__ __launch_bounds__(kScanThreads) void kla_scan_kernel(
       OT[t] = zero4();
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const FragT a = rd_frag(s.K, KQ{}, frow(t), ks);
-        const FragT bq = rd_frag(s.Q, KQ{}, frow(t), ks);
-        Y[t] = mma(a, Sop[ks], Y[t]);
-        OT[t] = mma(Sop[ks], bq, OT[t]);
+        Y[t] = mma(fk[t][ks], Sop[ks], Y[t]);
+        OT[t] = mma(Sop[ks], fq[t][ks], OT[t]);
       }
     }
+    // ---- reads for the state update: K^T rows = key dims of state tile m, by transpose
+    //      reads (source lane r16 of group kg: token 32 ks + 8 kg + (r16 >> 2), + 4 for the
+    //      second read; key dims 32 (m >> 1) + 8 (r16 & 3) + 4 (m & 1) .. + 3)
+    FragT fkt[NM][2];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if constexpr (B16) {
+          const int dk0 = 32 * (m >> 1) + 8 * (r16 & 3) + 4 * (m & 1);
+          const int tk = 32 * ks + 8 * kg + (r16 >> 2);
+          const bf16x4 lo = lds_read_tr(s.K + tile_off<Tin, DK>(tk, dk0));
+          const bf16x4 hi = lds_read_tr(s.K + tile_off<Tin, DK>(tk + 4, dk0));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { fkt[m][ks][i] = lo[i]; fkt[m][ks][i + 4] = hi[i]; }
+        } else {
+          const int dkr = frow(m);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            fkt[m][ks][e] = *reinterpret_cast<const float *>(
+                s.K + tile_off<Tin, DK>(32 * ks + 8 * kg + e, dkr));
+        }
+      }
     // ---- R = V - Diag(gam) Y, U = T R (row tile t needs k-steps ks <= t / 2)
     FragT Uop[2], Udop[2];
     {
       f32x4 R[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r0 = tmap(t, kg, 0);
-        const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gam[r0]);
-        float vv[4];
-        if constexpr (B16) {
-          const bf16x4 x =
-              lds_read_tr(s.V + tile_off<Tin, kBV>(r0 + (r16 >> 2), 16 * cw + 4 * (r16 & 3)));
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vv[i] = to_f32(x[i]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            vv[i] = *reinterpret_cast<const float *>(s.V + tile_off<Tin, kBV>(r0 + i, col));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) R[t][i] = vv[i] - g4[i] * Y[t][i];
-      }
+        for (int i = 0; i < 4; ++i) R[t][i] = vv[t][i] - g4[t][i] * Y[t][i];
       const FragT Rop0 = accB(R[0], R[1]), Rop1 = accB(R[2], R[3]);
       f32x4 U[4];
-      U[0] = mma(rd_frag(s.T, TP{}, frow(0), 0), Rop0, zero4());
-      U[1] = mma(rd_frag(s.T, TP{}, frow(1), 0), Rop0, zero4());
-      U[2] = mma(rd_frag(s.T, TP{}, frow(2), 1), Rop1,
-                 mma(rd_frag(s.T, TP{}, frow(2), 0), Rop0, zero4()));
-      U[3] = mma(rd_frag(s.T, TP{}, frow(3), 1), Rop1,
-                 mma(rd_frag(s.T, TP{}, frow(3), 0), Rop0, zero4()));
+      U[0] = mma(ft[0], Rop0, zero4());
+      U[1] = mma(ft[1], Rop0, zero4());
+      U[2] = mma(ft[3], Rop1, mma(ft[2], Rop0, zero4()));
+      U[3] = mma(ft[5], Rop1, mma(ft[4], Rop0, zero4()));
       f32x4 Ud[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[tmap(t, kg, 0)]);
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Ud[t][i] = d4[i] * U[t][i];
-      }
+        for (int i = 0; i < 4; ++i) Ud[t][i] = d4[t][i] * U[t][i];
       Uop[0] = accB(U[0], U[1]);
       Uop[1] = accB(U[2], U[3]);
       Udop[0] = accB(Ud[0], Ud[1]);
       Udop[1] = accB(Ud[2], Ud[3]);
     }
-    // ---- S = exp(G_last) S + K^T Diag(dec) U; the A operand rows are the key dims of
-    //      state tile m, read from K with the transpose reads
-    {
-      const float dl = s.gam[kChunk - 1];  // rows past a ragged end repeat G_last
+    // ---- reads for the output: P fragments and this lane's token decays
+    FragT fp[6];
+    fp[0] = rd_frag(s.P, TP{}, frow(0), 0);
+    fp[1] = rd_frag(s.P, TP{}, frow(1), 0);
+    fp[2] = rd_frag(s.P, TP{}, frow(2), 0);
+    fp[3] = rd_frag(s.P, TP{}, frow(2), 1);
+    fp[4] = rd_frag(s.P, TP{}, frow(3), 0);
+    fp[5] = rd_frag(s.P, TP{}, frow(3), 1);
+    float gt[4];
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        FragT aKt[2];
+    for (int t = 0; t < 4; ++t) gt[t] = s.gam[frow(t)];
+    // ---- S = exp(G_last) S + K^T Diag(dec) U
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if constexpr (B16) {
-            // source lane r16 of group kg: token 32 ks + 8 kg + (r16 >> 2) (+ 4 for the
-            // second read), key dims 32 (m >> 1) + 8 (r16 & 3) + 4 (m & 1) .. + 3
-            const int dk0 = 32 * (m >> 1) + 8 * (r16 & 3) + 4 * (m & 1);
-            const int tk = 32 * ks + 8 * kg + (r16 >> 2);
-            const bf16x4 lo = lds_read_tr(s.K + tile_off<Tin, DK>(tk, dk0));
-            const bf16x4 hi = lds_read_tr(s.K + tile_off<Tin, DK>(tk + 4, dk0));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { aKt[ks][i] = lo[i]; aKt[ks][i + 4] = hi[i]; }
-          } else {
-            const int dkr = frow(m);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              aKt[ks][e] = *reinterpret_cast<const float *>(
-                  s.K + tile_off<Tin, DK>(32 * ks + 8 * kg + e, dkr));
-          }
-        }
-        Sacc[m] *= dl;
-        Sacc[m] = mma(aKt[0], Udop[0], Sacc[m]);
-        Sacc[m] = mma(aKt[1], Udop[1], Sacc[m]);
-      }
+    for (int m = 0; m < NM; ++m) {
+      Sacc[m] *= dl;
+      Sacc[m] = mma(fkt[m][0], Udop[0], Sacc[m]);
+      Sacc[m] = mma(fkt[m][1], Udop[1], Sacc[m]);
     }
     // ---- O^T = Diag(gam) (Q S)^T + U^T P^T: lane (r16, kg) holds token frow(t), columns
     //      16 cw + 4 kg .. + 3 of this slice, stored straight to HBM
@@ -403,10 +435,13 @@ __global__ __launch_bounds__(kScanThreads) void kla_scan_kernel(
       const int voff = (lrow * H * DV + 16 * cw + 4 * kg) * ES;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float gt = s.gam[frow(t)];
-        f32x4 O = OT[t] * gt;
-        O = mma(Uop[0], rd_frag(s.P, TP{}, frow(t), 0), O);
-        if (t >= 2) O = mma(Uop[1], rd_frag(s.P, TP{}, frow(t), 1), O);
+        f32x4 O = OT[t] * gt[t];
+        if (t < 2) {
+          O = mma(Uop[0], fp[t], O);
+        } else {
+          O = mma(Uop[0], fp[2 * t - 2], O);
+          O = mma(Uop[1], fp[2 * t - 1], O);
+        }
         const int soff = (32 * (t >> 1) + 4 * (t & 1)) * H * DV * ES;
         if constexpr (B16) {
           bf16x4 x4;
