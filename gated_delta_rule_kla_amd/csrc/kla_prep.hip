@@ -92,27 +92,44 @@ __device__ __forceinline__ int find_sequence(const int32_t *__restrict__ chunk_o
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prep / UT kernel: one workgroup (4 wavefronts) per (chunk, head).
+// Prep / UT kernel: one workgroup (4 wavefronts) per (chunk, head); wavefront w owns the
+// 16 chunk rows 16 w .. 16 w + 15.
 //
-// (I + L)^{-1} is formed blockwise on 16 x 16 blocks (X = (I + L)^{-1} is unit lower
-// triangular): every wavefront inverts one diagonal block by substitution, then the
-// sub-diagonal blocks follow level by level,
+// Every wavefront loads its own key (and query) rows straight into MFMA fragments, takes
+// their norms from those registers, and scans the chunk's 64 log-decays itself; the key
+// rows are shared with the other wavefronts through one swizzled LDS tile for the Gram
+// and Q K^T tiles.  (I + L)^{-1} is formed blockwise on 16 x 16 blocks (X = (I + L)^{-1}
+// is unit lower triangular): every wavefront inverts its diagonal block by substitution,
+// then the sub-diagonal blocks follow level by level,
 //   X_ij = -X_ii (sum_{k=j}^{i-1} L_ik X_kj),  i > j,
-// with the 16 x 16 x 16 products on the fp32 matrix cores.  T = X Diag(b).
+// with the 16 x 16 x 16 products on the fp32 matrix cores; X reuses the key tile's LDS
+// once the Gram stage is done.  T = X Diag(b).
 // When q is given the kernel also writes P = (A o Q K^T) (Eq. (8)'s intra-chunk matrix,
 // A_ij = exp(G_i - G_j) for j <= i, zero above the diagonal) for the scan.
 // ---------------------------------------------------------------------------------------------
+constexpr int kLDL = kChunk + 4;  // padded row length of the fp32 L and X tiles
+
 template <typename Tin, int DK>
 struct PrepSmem {
-  static constexpr int PAD = 8;
-  alignas(16) Tin K[kChunk][DK + PAD];   // chunk keys, token-major
-  alignas(16) Tin Q[kChunk][DK + PAD];   // chunk queries, token-major (only when P is wanted)
-  alignas(16) float L[kChunk][kChunk + 4];
-  alignas(16) float X[kChunk][kChunk + 4];
-  alignas(16) float norm2[kChunk];
+  static constexpr int KBYTES = kChunk * DK * (int)sizeof(Tin);
+  static constexpr int XBYTES = kChunk * kLDL * (int)sizeof(float);
+  // key tile (swizzled 16-byte units) until the Gram stage ends, then X
+  alignas(16) unsigned char KX[KBYTES > XBYTES ? KBYTES : XBYTES];
+  alignas(16) float L[kChunk][kLDL];
   alignas(16) float beta[kChunk];
   alignas(16) float G[kChunk];
+  __device__ float (*X())[kLDL] { return reinterpret_cast<float (*)[kLDL]>(KX); }
 };
+
+// Byte offset of the 8-element fragment (row r, k-step ks, lane group kg) in the key tile:
+// 16-byte unit 4 ks + kg (two units for fp32) XOR-swizzled by row so that 16 consecutive
+// rows at one unit fall into distinct LDS bank groups.
+template <typename Tin, int DK>
+__device__ __forceinline__ int kfrag_off(int r, int ks, int kg) {
+  constexpr int ES = sizeof(Tin), UPF = ES / 2;
+  const int f = (DK >= 128 ? ((r >> 1) & 7) : ((r >> 2) & 3)) << 1;
+  return r * DK * ES + ((((4 * ks + kg) * UPF) ^ (f * UPF)) << 4);
+}
 
 // D += A B for 16 x 16 fp32 blocks in LDS (row strides lda, ldb), on v_mfma_f32_16x16x4_f32.
 __device__ __forceinline__ f32x4 mm16(const float *A, int lda, const float *B, int ldb, f32x4 acc,
@@ -148,102 +165,99 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
   const int len = min(kChunk, cu[n + 1] - t0);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kg = lane >> 4;
+  const int i0 = 16 * wid;  // this wavefront's rows
   const bool want_p = (q != nullptr) && (P_out != nullptr);
+  constexpr int NKS = DK / 32;
   using FragT = typename Frag<Tin>::type;
 
-  // ---- stage K (and Q) rows (zero past the chunk end); ||k_i||^2 by a lane-group reduction
-  constexpr int CPR = DK / 8;       // 8-element groups per key row
-  constexpr int RPP = 256 / CPR;    // rows per pass
+  // ---- loads: own key / query rows as fragments (zero past the chunk end), and the
+  //      chunk's g and eta one token per lane
+  const int my_row = i0 + r16;
+  const bool row_ok = my_row < len;
+  FragT kf[NKS], qf[NKS];
+  {
+    const size_t rbase = ((size_t)(t0 + (row_ok ? my_row : 0)) * H + h) * DK + 8 * kg;
 #pragma unroll
-  for (int pass = 0; pass < kChunk / RPP; ++pass) {
-    const int row = pass * RPP + tid / CPR, cg = tid % CPR;
-    FragT x = zero8<Tin>(), y = zero8<Tin>();
-    if (row < len) {
-      x = load8<Tin>(k + ((size_t)(t0 + row) * H + h) * DK + cg * 8);
-      if (want_p) y = load8<Tin>(q + ((size_t)(t0 + row) * H + h) * DK + cg * 8);
+    for (int ks = 0; ks < NKS; ++ks) {
+      kf[ks] = row_ok ? load8<Tin>(k + rbase + 32 * ks) : zero8<Tin>();
+      qf[ks] = (want_p && row_ok) ? load8<Tin>(q + rbase + 32 * ks) : zero8<Tin>();
     }
-    *reinterpret_cast<FragT *>(&sm.K[row][cg * 8]) = x;
-    if (want_p) *reinterpret_cast<FragT *>(&sm.Q[row][cg * 8]) = y;
-    float ss = 0.f;
+  }
+  const bool tok_ok = lane < len;
+  const size_t th = (size_t)(t0 + (tok_ok ? lane : 0)) * H + h;
+  const float g_l = tok_ok ? g[th] : 0.f;
+  const float eta_l = tok_ok ? eta[th] : 0.f;
+
+  // ---- b for the own rows, G for token `lane` (every wavefront scans all 64)
+  float ss = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const float xf = to_f32(x[s]);
-      ss = fmaf(xf, xf, ss);
+      const float x = to_f32(kf[ks][s]);
+      ss = fmaf(x, x, ss);
     }
-#pragma unroll
-    for (int off = CPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-    if (cg == 0) sm.norm2[row] = ss;
-  }
-  __syncthreads();
+  ss += __shfl_xor(ss, 16, kWave);
+  ss += __shfl_xor(ss, 32, kWave);
+  const float eta_r = __shfl(eta_l, my_row, kWave);
+  const float den = ss + eps;
+  const float b_r = (row_ok && den != 0.f) ? eta_r / den : 0.f;
+  const float G_l = wave_inclusive_scan(g_l, lane);  // rows past the end carry G_last
 
-  // ---- b and chunk-local inclusive log-decay (wavefront scan)
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    *reinterpret_cast<FragT *>(sm.KX + kfrag_off<Tin, DK>(my_row, ks, kg)) = kf[ks];
+  if (kg == 0) sm.beta[my_row] = b_r;
   if (wid == 0) {
-    const bool valid = lane < len;
-    const size_t th = (size_t)(t0 + lane) * H + h;
-    const float gi = valid ? g[th] : 0.f;
-    const float Gi = wave_inclusive_scan(gi, lane);
-    const float den = sm.norm2[lane] + eps;
-    const float bi = (valid && den != 0.f) ? eta[th] / den : 0.f;
-    sm.G[lane] = Gi;
-    sm.beta[lane] = bi;
-    if (valid) {
-      if (G_out) G_out[th] = Gi;
-      if (beta_out) beta_out[th] = bi;
-    }
-    // per-chunk decays for the scan: exp(G_i) and exp(G_last - G_i); rows past a ragged
-    // end carry G_last (their g is taken as 0), so they read exp(G_last) and 1
+    sm.G[lane] = G_l;
+    if (tok_ok && G_out) G_out[th] = G_l;
+    // per-chunk decays for the scan: exp(G_i) and exp(G_last - G_i)
     if (GD_out) {
-      const float Glast = __shfl(Gi, kChunk - 1, kWave);
+      const float Glast = __shfl(G_l, kChunk - 1, kWave);
       float *gd = GD_out + ((size_t)c * H + h) * (2 * kChunk);
-      gd[lane] = __expf(Gi);
-      gd[kChunk + lane] = __expf(Glast - Gi);
+      gd[lane] = __expf(G_l);
+      gd[kChunk + lane] = __expf(Glast - G_l);
     }
   }
+  if (beta_out && kg == 0 && row_ok) beta_out[((size_t)(t0 + my_row)) * H + h] = b_r;
   __syncthreads();
 
-  const int i0 = 16 * wid;  // this wave's 16 rows
-  // ---- Gram K K^T on the matrix cores (causal tiles only), then the strictly lower L
-  {
+  // ---- Gram K K^T (column blocks jt <= w) -> strictly lower L; P^T = K Q^T -> P
+  const f32x4 b_rows = *reinterpret_cast<const f32x4 *>(&sm.beta[i0 + 4 * kg]);
+  const f32x4 G_rows = *reinterpret_cast<const f32x4 *>(&sm.G[i0 + 4 * kg]);
+  const float G_me = sm.G[my_row];
+  Tin *Pc = want_p ? P_out + ((size_t)c * H + h) * (kChunk * kChunk) + (size_t)my_row * kChunk
+                   : nullptr;
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      f32x4 acc = zero4();
-      if (jt <= wid) {
+  for (int jt = 0; jt < 4; ++jt) {
+    const int j0 = 16 * jt + 4 * kg;
+    float pv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= wid) {
+      FragT bk[NKS];
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) {
-          const FragT a = load8<Tin>(&sm.K[i0 + r16][32 * ks + 8 * kg]);
-          const FragT b = load8<Tin>(&sm.K[16 * jt + r16][32 * ks + 8 * kg]);
-          acc = mma(a, b, acc);
-        }
+      for (int ks = 0; ks < NKS; ++ks)
+        bk[ks] = *reinterpret_cast<const FragT *>(sm.KX + kfrag_off<Tin, DK>(16 * jt + r16, ks, kg));
+      f32x4 acc = zero4(), accp = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        acc = mma(kf[ks], bk[ks], acc);   // rows i0 + 4 kg + e, column 16 jt + r16
+        if (want_p) accp = mma(bk[ks], qf[ks], accp);  // (Q K^T)[my_row][j0 + e]
       }
+      const int col = 16 * jt + r16;
+      const float G_col = sm.G[col];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = i0 + 4 * kg + e, col = 16 * jt + r16;
-        float val = 0.f;
-        if (col < row) val = sm.beta[row] * __expf(sm.G[row] - sm.G[col]) * acc[e];
-        sm.L[row][col] = val;
+        const int row = i0 + 4 * kg + e;
+        sm.L[row][col] = (col < row) ? b_rows[e] * __expf(G_rows[e] - G_col) * acc[e] : 0.f;
       }
-    }
-  }
-  // ---- P = A o Q K^T, as P^T = K Q^T so each lane holds 4 consecutive columns of a row
-  if (want_p) {
-    const int i = i0 + r16;
-    Tin *Pc = P_out + ((size_t)c * H + h) * (kChunk * kChunk) + (size_t)i * kChunk;
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      const int j0 = 16 * jt + 4 * kg;
-      float pv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (jt <= wid) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) {
-          const FragT a = load8<Tin>(&sm.K[16 * jt + r16][32 * ks + 8 * kg]);
-          const FragT b = load8<Tin>(&sm.Q[i][32 * ks + 8 * kg]);
-          acc = mma(a, b, acc);
-        }
+      if (want_p) {
+        const f32x4 G_cols = *reinterpret_cast<const f32x4 *>(&sm.G[j0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          pv[e] = (j0 + e <= i) ? __expf(sm.G[i] - sm.G[j0 + e]) * acc[e] : 0.f;
+          pv[e] = (j0 + e <= my_row) ? __expf(G_me - G_cols[e]) * accp[e] : 0.f;
       }
+    }
+    if (want_p) {
       if constexpr (sizeof(Tin) == 2) {
         bf16x4 x4;
 #pragma unroll
@@ -254,49 +268,81 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
       }
     }
   }
-  __syncthreads();
 
-  // ---- diagonal blocks: wave w inverts I + L_ww by substitution, lane = column r16
+  // ---- diagonal block: invert I + L_ww by substitution, lane = column r16 (the four lane
+  //      groups compute the same column); L rows are read four values at a time
+  float x[16];
   {
-    float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float acc = (i == r16) ? 1.f : 0.f;
-      const float *Lrow = &sm.L[i0 + i][i0];
+      float lr[16];
 #pragma unroll
-      for (int j = 0; j < i; ++j) acc = fmaf(-Lrow[j], x[j], acc);
-      x[i] = acc;
-    }
-    if (kg == 0) {
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&sm.L[i0 + i][i0 + 4 * q4]);
+        lr[4 * q4] = v4[0]; lr[4 * q4 + 1] = v4[1]; lr[4 * q4 + 2] = v4[2]; lr[4 * q4 + 3] = v4[3];
+      }
+      float a0 = (i == r16) ? 1.f : 0.f, a1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.X[i0 + i][i0 + r16] = x[i];
+      for (int j = 0; j < i; j += 2) {
+        a0 = fmaf(-lr[j], x[j], a0);
+        if (j + 1 < i) a1 = fmaf(-lr[j + 1], x[j + 1], a1);
+      }
+      x[i] = a0 + a1;
     }
   }
+  __syncthreads();  // every key-tile read and every L row is done; X takes the key tile
+  float(*X)[kLDL] = sm.X();
+  if (kg == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) X[i0 + i][i0 + r16] = x[i];
+  }
   __syncthreads();
+
   // ---- sub-diagonal blocks, one level (distance) at a time
-  constexpr int LDL = kChunk + 4;
 #pragma unroll
   for (int dist = 1; dist < 4; ++dist) {
     const int jb = wid, ib = wid + dist;  // block (ib, jb)
     if (ib < 4) {
       f32x4 Y = zero4();
       for (int kb = jb; kb < ib; ++kb)
-        Y = mm16(&sm.L[16 * ib][16 * kb], LDL, &sm.X[16 * kb][16 * jb], LDL, Y, r16, kg);
-      f32x4 Z = mm16_acc(&sm.X[16 * ib][16 * ib], LDL, Y, zero4(), r16, kg);
+        Y = mm16(&sm.L[16 * ib][16 * kb], kLDL, &X[16 * kb][16 * jb], kLDL, Y, r16, kg);
+      f32x4 Z = mm16_acc(&X[16 * ib][16 * ib], kLDL, Y, zero4(), r16, kg);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.X[16 * ib + 4 * kg + e][16 * jb + r16] = -Z[e];
+      for (int e = 0; e < 4; ++e) X[16 * ib + 4 * kg + e][16 * jb + r16] = -Z[e];
     }
     __syncthreads();
   }
 
-  // ---- T = X Diag(b), zero above the diagonal (blocks above the diagonal were never written)
+  // ---- T = X Diag(b), zero above the diagonal: thread tid writes 16 consecutive entries of
+  //      row tid / 4 (blocks above the diagonal of X were never written)
   {
     TOut *Tc = T_out + ((size_t)c * H + h) * (kChunk * kChunk);
+    const int row = tid >> 2, j0 = 16 * (tid & 3);
+    float tv[16];
 #pragma unroll
-    for (int kk = 0; kk < kChunk * kChunk / 256; ++kk) {
-      const int e = tid + 256 * kk, row = e >> 6, j = e & 63;
-      const float val = (j <= row) ? sm.X[row][j] * sm.beta[j] : 0.f;
-      Tc[e] = from_f32<TOut>(val);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 xv = *reinterpret_cast<const f32x4 *>(&X[row][j0 + 4 * q4]);
+      const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[j0 + 4 * q4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + 4 * q4 + e;
+        tv[4 * q4 + e] = (j <= row) ? xv[e] * bv[e] : 0.f;
+      }
+    }
+    TOut *dst = Tc + (size_t)row * kChunk + j0;
+    if constexpr (sizeof(TOut) == 2) {
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        bf16x8 o8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = from_f32<TOut>(tv[8 * h8 + e]);
+        *reinterpret_cast<bf16x8 *>(dst + 8 * h8) = o8;
+      }
+    } else {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4 *>(dst + 4 * q4) =
+            f32x4{tv[4 * q4], tv[4 * q4 + 1], tv[4 * q4 + 2], tv[4 * q4 + 3]};
     }
   }
 }
