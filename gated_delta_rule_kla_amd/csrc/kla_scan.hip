@@ -266,6 +266,28 @@ void kla_scan_kernel(
       dma16(rg, reinterpret_cast<unsigned char *>(s.gam) + 256 * pw, 256 * pw + 16 * lane);
   };
 
+  // chunk c's outputs, parked in slot s's value tile, back to HBM: 16 bytes per lane per
+  // piece, whole 64-byte value-tile rows per four lanes; rows past a ragged end are dropped
+  constexpr int PPR = kBV * ES / 16;                     // 16-byte pieces per value-tile row
+  constexpr int NST = kChunk * PPR / 128;                // store instructions per producer wave
+  auto p_flush = [&](int c, const SL &s) {
+    const int t0 = tb + c * kChunk;
+    const int len = min(kChunk, te - t0);
+    const Rsrc ro = make_rsrc(o + ((size_t)t0 * H + h) * DV + v0,
+                              (uint32_t)(((size_t)(len - 1) * H * DV + kBV) * ES));
+    u32x4 x[NST];
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int e = (tid - 128) + 128 * j, row = e / PPR, pc = e % PPR;
+      x[j] = *reinterpret_cast<const u32x4 *>(s.V + tile_off<Tin, kBV>(row, pc * (16 / ES)));
+    }
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int e = (tid - 128) + 128 * j, row = e / PPR, pc = e % PPR;
+      store16(x[j], ro, (row * H * DV) * ES + pc * 16, 0);
+    }
+  };
+
   // =========================== consumer side ===========================
   const int cw = wid & 1;
   const int col = 16 * cw + r16;  // this lane's state column within the slice
@@ -306,8 +328,6 @@ void kla_scan_kernel(
   // One chunk.  All LDS operands of a phase are read into registers before the phase's
   // MFMAs, and the next phase's reads are issued while those MFMAs run.
   auto c_step = [&](int c, const SL &s) {
-    const int t0 = tb + c * kChunk;
-    const int len = min(kChunk, te - t0);
     FragT Sop[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) Sop[ks] = accB(Sacc[2 * ks], Sacc[2 * ks + 1]);
@@ -349,17 +369,13 @@ void kla_scan_kernel(
     }
     const float dl = s.gam[kChunk - 1];  // rows past a ragged end repeat G_last
 
-    // ---- Y = K S and (Q S)^T, both from the incoming state
+    // ---- Y = K S first (the dependent chain continues from it)
     f32x4 Y[4], OT[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       Y[t] = zero4();
-      OT[t] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        Y[t] = mma(fk[t][ks], Sop[ks], Y[t]);
-        OT[t] = mma(Sop[ks], fq[t][ks], OT[t]);
-      }
+      for (int ks = 0; ks < NKS; ++ks) Y[t] = mma(fk[t][ks], Sop[ks], Y[t]);
     }
     // ---- reads for the state update: K^T rows = key dims of state tile m, by transpose
     //      reads (source lane r16 of group kg: token 32 ks + 8 kg + (r16 >> 2), + 4 for the
@@ -384,14 +400,19 @@ void kla_scan_kernel(
                 s.K + tile_off<Tin, DK>(32 * ks + 8 * kg + e, dkr));
         }
       }
-    // ---- R = V - Diag(gam) Y, U = T R (row tile t needs k-steps ks <= t / 2)
+    // ---- R = V - Diag(gam) Y, U = T R (row tile t needs k-steps ks <= t / 2); (Q S)^T,
+    //      which is off the chain, fills the matrix core while R is formed
     FragT Uop[2], Udop[2];
     {
       f32x4 R[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) {
+        OT[t] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) OT[t] = mma(Sop[ks], fq[t][ks], OT[t]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) R[t][i] = vv[t][i] - g4[t][i] * Y[t][i];
+      }
       const FragT Rop0 = accB(R[0], R[1]), Rop1 = accB(R[2], R[3]);
       f32x4 U[4];
       U[0] = mma(ft[0], Rop0, zero4());
@@ -427,12 +448,11 @@ void kla_scan_kernel(
       Sacc[m] = mma(fkt[m][1], Udop[1], Sacc[m]);
     }
     // ---- O^T = Diag(gam) (Q S)^T + U^T P^T: lane (r16, kg) holds token frow(t), columns
-    //      16 cw + 4 kg .. + 3 of this slice, stored straight to HBM
+    //      16 cw + 4 kg .. + 3 of this slice.  The block is parked in this wavefront's own
+    //      columns of the value tile (read above, and read by no other wavefront); the
+    //      producers write whole value-tile rows back to HBM before the slot is refilled.
     {
-      const size_t obase = ((size_t)t0 * H + h) * DV + v0;
-      const Rsrc ro = make_rsrc(o + obase, (uint32_t)(((size_t)(len - 1) * H * DV + kBV) * ES));
-      const int lrow = 8 * (r16 >> 2) + (r16 & 3);
-      const int voff = (lrow * H * DV + 16 * cw + 4 * kg) * ES;
+      unsigned char *vt = const_cast<unsigned char *>(s.V);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         f32x4 O = OT[t] * gt[t];
@@ -442,14 +462,14 @@ void kla_scan_kernel(
           O = mma(Uop[0], fp[2 * t - 2], O);
           O = mma(Uop[1], fp[2 * t - 1], O);
         }
-        const int soff = (32 * (t >> 1) + 4 * (t & 1)) * H * DV * ES;
+        unsigned char *dst = vt + tile_off<Tin, kBV>(frow(t), 16 * cw + 4 * kg);
         if constexpr (B16) {
           bf16x4 x4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) x4[i] = from_f32<Tin>(O[i]);
-          store8(__builtin_bit_cast(u32x2, x4), ro, voff, soff);
+          *reinterpret_cast<bf16x4 *>(dst) = x4;
         } else {
-          store16(__builtin_bit_cast(u32x4, O), ro, voff, soff);
+          *reinterpret_cast<f32x4 *>(dst) = O;
         }
       }
     }
@@ -472,12 +492,24 @@ void kla_scan_kernel(
       if (DIST == 2 && pro == 2) wait_vmcnt<DP::PER_WAVE>(); else wait_vmcnt<0>();
       producer_barrier();
       for (int c = 0; c < nchunks; ++c) {
-        // slot (c + DIST) % NSLOT held chunk c - 1, released at the barrier just passed
-        if (c + DIST < nchunks) p_issue(c + DIST, sm.slot[(c + DIST) % NSLOT]);
-        // chunk c + 1 must be in LDS before the barrier that starts it
-        if (DIST == 2 && c + 2 < nchunks) wait_vmcnt<DP::PER_WAVE>(); else wait_vmcnt<0>();
+        // slot (c + DIST) % NSLOT held chunk c - 1, released at the barrier just passed:
+        // write its outputs back, then refill it
+        const bool fl = c >= 1, is = c + DIST < nchunks;
+        if (fl) p_flush(c - 1, sm.slot[(c - 1) % NSLOT]);
+        if (is) p_issue(c + DIST, sm.slot[(c + DIST) % NSLOT]);
+        // chunk c + 1 must be in LDS before the barrier that starts it; what was issued
+        // after its loads (this step's stores and loads) may stay in flight
+        if (DIST == 2) {
+          if (fl && is) wait_vmcnt<NST + DP::PER_WAVE>();
+          else if (is) wait_vmcnt<DP::PER_WAVE>();
+          else if (fl) wait_vmcnt<NST>();
+          else wait_vmcnt<0>();
+        } else {
+          wait_vmcnt<0>();
+        }
         producer_barrier();
       }
+      if (nchunks > 0) p_flush(nchunks - 1, sm.slot[(nchunks - 1) % NSLOT]);
     }
   } else {
     // a single slot: one barrier before the loop, then two per chunk (staged, released)
@@ -491,11 +523,13 @@ void kla_scan_kernel(
     } else {
       producer_barrier();
       for (int c = 0; c < nchunks; ++c) {
+        if (c >= 1) p_flush(c - 1, sm.slot[0]);
         p_issue(c, sm.slot[0]);
         wait_vmcnt<0>();
         producer_barrier();
         producer_barrier();
       }
+      if (nchunks > 0) p_flush(nchunks - 1, sm.slot[0]);
     }
   }
 
