@@ -18,7 +18,8 @@ timed loop: the prefill is issued as its two halves (kla_prefill_prepare, then
 kla_prefill_scan), which is exactly what kla_prefill_chunked enqueues.
 
 Algorithmic work (per token-head, C = 64, d = d_k = d_v):
-  scan kernel bytes  = 2 d_k e (q, k) + d_v e (v) + d_v e (o) + 4 (G) + 4 C (a row of T)
+  scan kernel bytes  = 2 d_k e (q, k) + d_v e (v) + d_v e (o) + 2 C e (a row of T and of P)
+                       + 8 (the two decay factors)
                        + 8 d_k d_v per (sequence, head) for S0 in / S_T out,  e = 2 (bf16)
   prefill MFMA flops = 6 d_k d_v + (C-1) d_k + (C+1)(2 d_k + 2 d_v)
   decode bytes       = 8 d_k d_v + 2 (2 d_k + d_v) + 2 d_v + 8
@@ -79,6 +80,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="finally copy this many MiB device to device once: a kernel of known "
+                         "traffic for scaling hardware byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -138,7 +142,7 @@ def main():
     ms_per_step = total_ms / K
     tok_per_s = n_tok / (ms_per_step * 1e-3)
     th = n_tok * H
-    scan_bytes = th * (2 * dk * 2 + dv * 2 + dv * 2 + 4 + 4 * CHUNK) + 2 * n_seq * H * dk * dv * 4
+    scan_bytes = th * (2 * dk * 2 + dv * 2 + dv * 2 + 2 * CHUNK * 2 + 8) + 2 * n_seq * H * dk * dv * 4
     scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     flops_prefill = th * (6 * dk * dv + (CHUNK - 1) * dk + (CHUNK + 1) * (2 * dk + 2 * dv))
     mfma_frac = flops_prefill / (ms_per_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
@@ -190,6 +194,15 @@ def main():
                "sample": f"the whole prefill workload ({n_seq} seq x {H} heads x "
                          f"{n_tok // n_seq} tokens, d=128) through the fp64 tokenwise oracle, "
                          f"{cpu_s:.2f} s wall"}
+
+    if args.copy_calibration_mib > 0:
+        a = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_calibration_mib} MiB done")
+        del a, b
 
     traffic = measured_traffic()
     line = {
