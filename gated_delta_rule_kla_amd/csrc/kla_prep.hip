@@ -115,6 +115,7 @@ struct PrepSmem {
   static constexpr int XBYTES = kChunk * kLDL * (int)sizeof(float);
   // key tile (swizzled 16-byte units) until the Gram stage ends, then X
   alignas(16) unsigned char KX[KBYTES > XBYTES ? KBYTES : XBYTES];
+  alignas(16) float XT[kChunk][kLDL];  // X transposed, for 16-byte operand reads
   alignas(16) float L[kChunk][kLDL];
   alignas(16) float beta[kChunk];
   alignas(16) float G[kChunk];
@@ -131,22 +132,24 @@ __device__ __forceinline__ int kfrag_off(int r, int ks, int kg) {
   return r * DK * ES + ((((4 * ks + kg) * UPF) ^ (f * UPF)) << 4);
 }
 
-// D += A B for 16 x 16 fp32 blocks in LDS (row strides lda, ldb), on v_mfma_f32_16x16x4_f32.
-__device__ __forceinline__ f32x4 mm16(const float *A, int lda, const float *B, int ldb, f32x4 acc,
-                                      int r16, int kg) {
+// D += A B for 16 x 16 fp32 blocks in LDS, A row-major (stride lda) and B given as its
+// transpose Bt (stride ldbt): with the contraction index k = 4 kg + s in MFMA s, both
+// operands are one 16-byte read per lane.
+__device__ __forceinline__ f32x4 mm16t(const float *A, int lda, const float *Bt, int ldbt,
+                                       f32x4 acc, int r16, int kg) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r16 * lda + 4 * kg);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(Bt + r16 * ldbt + 4 * kg);
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r16 * lda + 4 * s + kg],
-                                               B[(4 * s + kg) * ldb + r16], acc, 0, 0, 0);
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
   return acc;
 }
 // D += A Y with Y a 16 x 16 block held in accumulator layout (lane (r16, kg) holds rows
 // 4 kg + e of column r16): the contraction index is taken in the order the lanes hold it.
 __device__ __forceinline__ f32x4 mm16_acc(const float *A, int lda, const f32x4 &Y, f32x4 acc,
                                           int r16, int kg) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r16 * lda + 4 * kg);
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r16 * lda + 4 * kg + s], Y[s], acc, 0, 0, 0);
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], Y[s], acc, 0, 0, 0);
   return acc;
 }
 
@@ -170,17 +173,22 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
   constexpr int NKS = DK / 32;
   using FragT = typename Frag<Tin>::type;
 
-  // ---- loads: own key / query rows as fragments (zero past the chunk end), and the
-  //      chunk's g and eta one token per lane
+  // ---- loads: own key rows and the query rows of block 3 - w as fragments (zero past the
+  //      chunk end), and the chunk's g and eta one token per lane.  Wavefront w forms the
+  //      Gram tiles of row block w (w + 1 tiles) and the Q K^T tiles of row block 3 - w
+  //      (4 - w tiles), five tiles each.
   const int my_row = i0 + r16;
   const bool row_ok = my_row < len;
+  const int p0 = 16 * (3 - wid), p_row = p0 + r16;
+  const bool prow_ok = p_row < len;
   FragT kf[NKS], qf[NKS];
   {
     const size_t rbase = ((size_t)(t0 + (row_ok ? my_row : 0)) * H + h) * DK + 8 * kg;
+    const size_t qbase = ((size_t)(t0 + (prow_ok ? p_row : 0)) * H + h) * DK + 8 * kg;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       kf[ks] = row_ok ? load8<Tin>(k + rbase + 32 * ks) : zero8<Tin>();
-      qf[ks] = (want_p && row_ok) ? load8<Tin>(q + rbase + 32 * ks) : zero8<Tin>();
+      qf[ks] = (want_p && prow_ok) ? load8<Tin>(q + qbase + 32 * ks) : zero8<Tin>();
     }
   }
   const bool tok_ok = lane < len;
@@ -222,27 +230,20 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
   if (beta_out && kg == 0 && row_ok) beta_out[((size_t)(t0 + my_row)) * H + h] = b_r;
   __syncthreads();
 
-  // ---- Gram K K^T (column blocks jt <= w) -> strictly lower L; P^T = K Q^T -> P
-  const f32x4 b_rows = *reinterpret_cast<const f32x4 *>(&sm.beta[i0 + 4 * kg]);
-  const f32x4 G_rows = *reinterpret_cast<const f32x4 *>(&sm.G[i0 + 4 * kg]);
-  const float G_me = sm.G[my_row];
-  Tin *Pc = want_p ? P_out + ((size_t)c * H + h) * (kChunk * kChunk) + (size_t)my_row * kChunk
-                   : nullptr;
+  // ---- Gram K K^T (row block w, column blocks jt <= w) -> strictly lower L
+  {
+    const f32x4 b_rows = *reinterpret_cast<const f32x4 *>(&sm.beta[i0 + 4 * kg]);
+    const f32x4 G_rows = *reinterpret_cast<const f32x4 *>(&sm.G[i0 + 4 * kg]);
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    const int j0 = 16 * jt + 4 * kg;
-    float pv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (jt <= wid) {
+    for (int jt = 0; jt < 4; ++jt) {
+      if (jt > wid) continue;
       FragT bk[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         bk[ks] = *reinterpret_cast<const FragT *>(sm.KX + kfrag_off<Tin, DK>(16 * jt + r16, ks, kg));
-      f32x4 acc = zero4(), accp = zero4();
+      f32x4 acc = zero4();
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        acc = mma(kf[ks], bk[ks], acc);   // rows i0 + 4 kg + e, column 16 jt + r16
-        if (want_p) accp = mma(bk[ks], qf[ks], accp);  // (Q K^T)[my_row][j0 + e]
-      }
+      for (int ks = 0; ks < NKS; ++ks) acc = mma(kf[ks], bk[ks], acc);  // rows i0 + 4 kg + e
       const int col = 16 * jt + r16;
       const float G_col = sm.G[col];
 #pragma unroll
@@ -250,14 +251,31 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
         const int row = i0 + 4 * kg + e;
         sm.L[row][col] = (col < row) ? b_rows[e] * __expf(G_rows[e] - G_col) * acc[e] : 0.f;
       }
-      if (want_p) {
+    }
+  }
+  // ---- P^T = K Q^T for row block 3 - w, so each lane holds 4 consecutive columns of P row
+  //      p_row; P = A o Q K^T is written row-major (zero above the diagonal)
+  if (want_p) {
+    Tin *Pc = P_out + ((size_t)c * H + h) * (kChunk * kChunk) + (size_t)p_row * kChunk;
+    const float G_me = sm.G[p_row];
+    const int pb = 3 - wid;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int j0 = 16 * jt + 4 * kg;
+      float pv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (jt <= pb) {
+        f32x4 accp = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const FragT bk =
+              *reinterpret_cast<const FragT *>(sm.KX + kfrag_off<Tin, DK>(16 * jt + r16, ks, kg));
+          accp = mma(bk, qf[ks], accp);  // (Q K^T)[p_row][j0 + e]
+        }
         const f32x4 G_cols = *reinterpret_cast<const f32x4 *>(&sm.G[j0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          pv[e] = (j0 + e <= my_row) ? __expf(G_me - G_cols[e]) * accp[e] : 0.f;
+          pv[e] = (j0 + e <= p_row) ? __expf(G_me - G_cols[e]) * accp[e] : 0.f;
       }
-    }
-    if (want_p) {
       if constexpr (sizeof(Tin) == 2) {
         bf16x4 x4;
 #pragma unroll
@@ -295,6 +313,10 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
   if (kg == 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) X[i0 + i][i0 + r16] = x[i];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<f32x4 *>(&sm.XT[i0 + r16][i0 + 4 * q4]) =
+          f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
   }
   __syncthreads();
 
@@ -305,10 +327,12 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
     if (ib < 4) {
       f32x4 Y = zero4();
       for (int kb = jb; kb < ib; ++kb)
-        Y = mm16(&sm.L[16 * ib][16 * kb], kLDL, &X[16 * kb][16 * jb], kLDL, Y, r16, kg);
+        Y = mm16t(&sm.L[16 * ib][16 * kb], kLDL, &sm.XT[16 * jb][16 * kb], kLDL, Y, r16, kg);
       f32x4 Z = mm16_acc(&X[16 * ib][16 * ib], kLDL, Y, zero4(), r16, kg);
 #pragma unroll
       for (int e = 0; e < 4; ++e) X[16 * ib + 4 * kg + e][16 * jb + r16] = -Z[e];
+      *reinterpret_cast<f32x4 *>(&sm.XT[16 * jb + r16][16 * ib + 4 * kg]) =
+          f32x4{-Z[0], -Z[1], -Z[2], -Z[3]};
     }
     __syncthreads();
   }
