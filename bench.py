@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant-steps", type=int, default=10,
+                    help="steps timed for each coefficient / readout variant (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finally copy this many MiB device to device once: a kernel of known "
                          "traffic for scaling hardware byte counters")
@@ -149,6 +151,33 @@ def main():
     prefill_bytes_min = th * (2 * (2 * dk + dv) + 8 + 2 * dv) + 2 * n_seq * H * dk * dv * 4
     log(f"prefill {ms_per_step:.3f} ms/step (prep {prep_ms:.3f}, scan {scan_ms:.3f}); "
         f"{tok_per_s:.3e} tok/s; wall {wall:.2f}s")
+
+    # ---------------------------------------------------------------- coefficient / readout
+    # variants on the same kernels: the gated delta rule's b = eta against the Kaczmarz
+    # coefficient, and the readout divided by ||q|| (unit-norm keys keep the gated rule bounded)
+    variants = None
+    if args.variant_steps > 0:
+        s0 = sets[0]
+        ku = (s0["k"].float() / s0["k"].float().norm(dim=-1, keepdim=True)).to(s0["k"].dtype)
+        variants = {}
+        for name, kw in (("kaczmarz", {}), ("gated", {"beta_mode": "gated"}),
+                         ("kaczmarz_normalized_readout", {"normalize_q": True})):
+            def vstep():
+                kla.kla_prefill_chunked(s0["q"], ku, s0["v"], s0["g"], s0["eta"], base["eps"],
+                                        S0=s0["S0"], n_seq=n_seq, o=s0["o"], S_T=s0["S_T"],
+                                        workspace=s0["ws"], **kw)
+            for _ in range(2):
+                vstep()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.variant_steps):
+                vstep()
+            e1.record()
+            torch.cuda.synchronize()
+            variants[name + "_ms_per_step"] = e0.elapsed_time(e1) / args.variant_steps
+        variants["note"] = ("same workload, one input set (cache-warm, unlike the headline), "
+                            "unit-norm keys; one kla_prefill_chunked call per step")
+        log(f"variants: {variants}")
     del sets
 
     # ---------------------------------------------------------------- decode
@@ -233,6 +262,7 @@ def main():
                    "roofline": {"kernel": "kla_decode_kernel", "bound": "hbm",
                                 "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": dec_gbs / PEAK_HBM_GBS}},
+        "variants": variants,
         "cpu_baseline": cpu,
         "context": "the pages report 3.54 vs 1.65 tok/s decode at 32K context (2.1x KLA/GDN) for "
                    "a whole 0.4B model at batch 1 on NVIDIA A100 80GB (FLA library); not this "

@@ -74,6 +74,16 @@ def load_library():
     lib.kla_decode_step.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32,
                                     ctypes.c_int, vp]
     lib.kla_decode_step.restype = ctypes.c_int
+    opt_p = ctypes.POINTER(KlaOptions)
+    lib.kla_prefill_chunked_ex.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i32,
+                                           i32, i32, i32, ctypes.c_int, vp, sz, opt_p, vp]
+    lib.kla_prefill_chunked_ex.restype = ctypes.c_int
+    lib.kla_prefill_prepare_ex.argtypes = [vp, vp, vp, vp, f32, vp, vp, i32, i32, i32, i32, i32,
+                                           ctypes.c_int, vp, sz, opt_p, vp]
+    lib.kla_prefill_prepare_ex.restype = ctypes.c_int
+    lib.kla_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32,
+                                       ctypes.c_int, opt_p, vp]
+    lib.kla_decode_step_ex.restype = ctypes.c_int
     lib.kla_status_string.argtypes = [ctypes.c_int]
     lib.kla_status_string.restype = ctypes.c_char_p
     lib.kla_last_error.argtypes = []
@@ -82,6 +92,32 @@ def load_library():
     lib.kla_version.restype = i32
     _lib = lib
     return lib
+
+
+# Write-coefficient variants (kla_beta_mode in include/kla.h).
+BETA_MODES = {"kaczmarz": 0, "gated": 1, "key_norm": 2, "inv_t": 3, "inv_sqrt_t": 4,
+              "inv_log_t": 5}
+
+
+class KlaOptions(ctypes.Structure):
+    """Mirror of ``kla_options``: the write-coefficient mode, the normalised readout and the
+    per-sequence position offsets (device int32 or NULL)."""
+    _fields_ = [("beta_mode", ctypes.c_int32), ("normalize_q", ctypes.c_int32),
+                ("pos_offset", ctypes.c_void_p)]
+
+
+def _options(beta_mode, normalize_q, pos_offset, n_rows, dev):
+    """ctypes pointer to a KlaOptions (None = the defaults).  beta_mode is a name from
+    BETA_MODES or its integer code; pos_offset an int32 device tensor of n_rows entries."""
+    mode = BETA_MODES[beta_mode] if isinstance(beta_mode, str) else int(beta_mode)
+    if mode == 0 and not normalize_q and pos_offset is None:
+        return None
+    if pos_offset is not None:
+        _need(pos_offset, "pos_offset", torch.int32, dev)
+        if pos_offset.numel() != n_rows:
+            raise ValueError(f"pos_offset must have {n_rows} entries")
+    return ctypes.pointer(KlaOptions(mode, 1 if normalize_q else 0,
+                                     None if pos_offset is None else pos_offset.data_ptr()))
 
 
 def _check(status: int):
@@ -135,7 +171,8 @@ def _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq):
 
 def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=None,
                         n_seq=None, *, cu_seqlens_host=None, output_final_state=True, o=None,
-                        S_T=None, workspace=None):
+                        S_T=None, workspace=None, beta_mode="kaczmarz", normalize_q=False,
+                        pos_offset=None):
     """Chunkwise KLA prefill (paper section 4, Eq. (7)-(9); chunk = 64 tokens).
 
     q, k: [n_tok, H, d_k] or [B, T, H, d_k] (fp32 or bf16); v like q with d_v;
@@ -143,6 +180,7 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
     cu_seqlens: int32 device [n_seq + 1] for packed sequences, or None (dense;
     n_seq sequences of equal length).  Returns (o, S_T); S_T is None when
     output_final_state is False.  Pass S_T=S0 to update the state in place.
+    beta_mode / normalize_q / pos_offset select the variants of kla_options.
     """
     shape_v = v.shape
     q, k, v, g, eta, n_seq = _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq)
@@ -183,17 +221,19 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     host_ptr = None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr())
-    _check(lib.kla_prefill_chunked(
+    opts = _options(beta_mode, normalize_q, pos_offset, n_seq, dev)
+    _check(lib.kla_prefill_chunked_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S0), _ptr(o), _ptr(S_T),
         _ptr(cu_seqlens), host_ptr, n_seq, n_tok, H, d_k, d_v, _DTYPES[dt], _ptr(workspace),
-        workspace.numel(), _stream(dev)))
+        workspace.numel(), opts, _stream(dev)))
     return o.reshape(shape_v), S_T
 
 
-def kla_prefill_prepare(q, k, g, eta, eps, workspace, *, n_seq, d_v, cu_seqlens=None):
-    """First half of the prefill: sequence tables, G, T and P of every chunk into ``workspace``
-    (a uint8 device tensor of at least kla_prefill_workspace_bytes(...) bytes).
-    q, k: [n_tok, H, d_k]; g, eta: [n_tok, H]."""
+def kla_prefill_prepare(q, k, g, eta, eps, workspace, *, n_seq, d_v, cu_seqlens=None,
+                        beta_mode="kaczmarz", normalize_q=False, pos_offset=None):
+    """First half of the prefill: sequence tables, decays, T and P of every chunk into
+    ``workspace`` (a uint8 device tensor of at least kla_prefill_workspace_bytes(...) bytes).
+    q, k: [n_tok, H, d_k]; g, eta: [n_tok, H]; variants as in kla_prefill_chunked."""
     dev = k.device
     _need(k, "k", device=dev)
     if k.dtype not in _DTYPES:
@@ -205,9 +245,10 @@ def kla_prefill_prepare(q, k, g, eta, eps, workspace, *, n_seq, d_v, cu_seqlens=
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     n_tok, H, d_k = k.shape
-    _check(load_library().kla_prefill_prepare(
-        _ptr(q), _ptr(k), _ptr(g), _ptr(eta), float(eps), _ptr(cu_seqlens), None, n_seq, n_tok, H, d_k, d_v,
-        _DTYPES[k.dtype], _ptr(workspace), workspace.numel(), _stream(dev)))
+    opts = _options(beta_mode, normalize_q, pos_offset, n_seq, dev)
+    _check(load_library().kla_prefill_prepare_ex(
+        _ptr(q), _ptr(k), _ptr(g), _ptr(eta), float(eps), _ptr(cu_seqlens), None, n_seq, n_tok,
+        H, d_k, d_v, _DTYPES[k.dtype], _ptr(workspace), workspace.numel(), opts, _stream(dev)))
 
 
 def kla_prefill_scan(q, k, v, workspace, *, n_seq, S0=None, o=None, S_T=None):
@@ -232,11 +273,14 @@ def kla_prefill_scan(q, k, v, workspace, *, n_seq, S0=None, o=None, S_T=None):
     return o, S_T
 
 
-def kla_decode_step(q, k, v, g, eta, eps: float, S, *, o=None, S_new=None, inplace=False):
+def kla_decode_step(q, k, v, g, eta, eps: float, S, *, o=None, S_new=None, inplace=False,
+                    beta_mode="kaczmarz", normalize_q=False, pos_offset=None):
     """One KLA decode step per sequence (paper Algorithm 1, tokenwise panel).
 
     q, k: [B, H, d_k]; v: [B, H, d_v] (fp32 or bf16); g, eta: [B, H] fp32;
     S: [B, H, d_k, d_v] fp32.  Returns (o, S_new); inplace=True writes S' into S.
+    Variants as in kla_prefill_chunked (pos_offset: int32 [B], this token is at
+    position pos_offset + 1).
     """
     dev = q.device
     _need(q, "q", device=dev)
@@ -259,9 +303,10 @@ def kla_decode_step(q, k, v, g, eta, eps: float, S, *, o=None, S_new=None, inpla
     elif S_new is None:
         S_new = torch.empty_like(S)
     _need(S_new, "S_new", torch.float32, dev)
-    _check(load_library().kla_decode_step(
+    opts = _options(beta_mode, normalize_q, pos_offset, B, dev)
+    _check(load_library().kla_decode_step_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S), _ptr(o), _ptr(S_new),
-        B, H, d_k, d_v, _DTYPES[dt], _stream(dev)))
+        B, H, d_k, d_v, _DTYPES[dt], opts, _stream(dev)))
     return o, S_new
 
 

@@ -45,7 +45,7 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 // Workspace layout: [cu: n_seq+1 int32][chunk_off: n_seq+1 int32][G: total*H fp32]
-//                   [GD: n_chunks_ub * H * 128 fp32][T: n_chunks_ub * H * 64 * 64][P: same],
+//                   [GD: n_chunks_ub * H * 192 fp32][T: n_chunks_ub * H * 64 * 64][P: same],
 // each part 256-byte aligned and T, P sized for fp32 (the scan reads them in the operand
 // type).
 struct WsLayout {
@@ -59,7 +59,7 @@ WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H) {
   w.off_G = align256(w.off_co + sizeof(int32_t) * (size_t)(n_seq + 1));
   const int64_t nch = kla::chunk_upper_bound(n_seq, total_tokens);
   w.off_GD = align256(w.off_G + sizeof(float) * (size_t)total_tokens * (size_t)H);
-  w.off_T = align256(w.off_GD + sizeof(float) * (size_t)nch * (size_t)H * 2 * KLA_CHUNK);
+  w.off_T = align256(w.off_GD + sizeof(float) * (size_t)nch * (size_t)H * kla::kGDFloats);
   const size_t tile_bytes = sizeof(float) * (size_t)nch * (size_t)H * KLA_CHUNK * KLA_CHUNK;
   w.off_P = align256(w.off_T + tile_bytes);
   w.total = align256(w.off_P + tile_bytes);
@@ -110,6 +110,18 @@ kla_status check_dense(const int32_t *cu_seqlens, int32_t n_seq, int32_t total_t
 }
 
 kla::Dtype to_dt(kla_dtype d) { return d == KLA_DTYPE_BF16 ? kla::Dtype::BF16 : kla::Dtype::F32; }
+
+// kla_options -> the kernels' CoefOpts (NULL = the defaults), validated.
+kla_status to_coef(const kla_options *opts, kla::CoefOpts *out) {
+  *out = kla::CoefOpts{kla::kBetaKaczmarz, 0, nullptr};
+  if (!opts) return KLA_OK;
+  if (opts->beta_mode < KLA_BETA_KACZMARZ || opts->beta_mode > KLA_BETA_INV_LOG_T)
+    return fail(KLA_ERR_UNSUPPORTED, "unknown beta_mode %d", (int)opts->beta_mode);
+  if (opts->pos_offset && !aligned_to(opts->pos_offset, 4))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "pos_offset must be 4-byte aligned");
+  *out = kla::CoefOpts{opts->beta_mode, opts->normalize_q != 0 ? 1 : 0, opts->pos_offset};
+  return KLA_OK;
+}
 
 kla_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return KLA_OK;
@@ -187,16 +199,17 @@ WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n
 }
 
 kla_status enqueue_prepare(const void *q, const void *k, const float *g, const float *eta, float eps,
-                           const int32_t *cu_seqlens, int32_t n_seq, int32_t total_tokens,
-                           int32_t n_heads, int32_t d_k, kla_dtype dtype, void *workspace,
-                           hipStream_t s) {
+                           const kla::CoefOpts &opts, const int32_t *cu_seqlens, int32_t n_seq,
+                           int32_t total_tokens, int32_t n_heads, int32_t d_k, kla_dtype dtype,
+                           void *workspace, hipStream_t s) {
   const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
   kla_status st;
   if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan")) != KLA_OK)
     return st;
-  return hip_status(kla::launch_prep(to_dt(dtype), d_k, q, k, g, eta, eps, wv.tabs, n_seq, nch_ub,
-                                     n_heads, nullptr, nullptr, wv.T, false, wv.P, wv.GD, s),
+  return hip_status(kla::launch_prep(to_dt(dtype), d_k, q, k, g, eta, eps, opts, wv.tabs, n_seq,
+                                     nch_ub, n_heads, nullptr, nullptr, wv.T, false, wv.P, wv.GD,
+                                     s),
                     "prep");
 }
 
@@ -212,6 +225,30 @@ kla_status enqueue_scan(const void *q, const void *k, const void *v, const float
 
 extern "C" {
 
+kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, const float *g,
+                                  const float *eta, float eps, const float *S0, void *o,
+                                  float *S_T, const int32_t *cu_seqlens,
+                                  const int32_t *cu_seqlens_host, int32_t n_seq,
+                                  int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                                  int32_t d_v, kla_dtype dtype, void *workspace,
+                                  size_t workspace_bytes, const kla_options *opts, void *stream) {
+  kla_status st = check_prefill_args(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
+                                     n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
+                                     workspace_bytes, true, true);
+  if (st != KLA_OK) return st;
+  kla::CoefOpts co;
+  if ((st = to_coef(opts, &co)) != KLA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear any stale error from unrelated work
+  if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
+                            dtype, workspace, s)) != KLA_OK)
+    return st;
+  if ((st = enqueue_scan(q, k, v, S0, o, S_T, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
+                         workspace, s)) != KLA_OK)
+    return st;
+  return ok();
+}
+
 kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, const float *g,
                                const float *eta, float eps, const float *S0, void *o,
                                float *S_T, const int32_t *cu_seqlens,
@@ -219,17 +256,28 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
                                int32_t total_tokens, int32_t n_heads, int32_t d_k,
                                int32_t d_v, kla_dtype dtype, void *workspace,
                                size_t workspace_bytes, void *stream) {
-  kla_status st = check_prefill_args(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
-                                     n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
-                                     workspace_bytes, true, true);
+  return kla_prefill_chunked_ex(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
+                                n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
+                                workspace_bytes, nullptr, stream);
+}
+
+kla_status kla_prefill_prepare_ex(const void *q, const void *k, const float *g,
+                                  const float *eta, float eps, const int32_t *cu_seqlens,
+                                  const int32_t *cu_seqlens_host, int32_t n_seq,
+                                  int32_t total_tokens, int32_t n_heads, int32_t d_k, int32_t d_v,
+                                  kla_dtype dtype, void *workspace, size_t workspace_bytes,
+                                  const kla_options *opts, void *stream) {
+  kla_status st = check_prefill_args(q, k, nullptr, g, eta, eps, nullptr, nullptr, nullptr,
+                                     cu_seqlens, cu_seqlens_host, n_seq, total_tokens, n_heads,
+                                     d_k, d_v, dtype, workspace, workspace_bytes, true, false);
   if (st != KLA_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();  // clear any stale error from unrelated work
-  if ((st = enqueue_prepare(q, k, g, eta, eps, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
-                            dtype, workspace, s)) != KLA_OK)
-    return st;
-  if ((st = enqueue_scan(q, k, v, S0, o, S_T, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
-                         workspace, s)) != KLA_OK)
+  if (total_tokens > 0 && !q)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, g and eta are required");
+  kla::CoefOpts co;
+  if ((st = to_coef(opts, &co)) != KLA_OK) return st;
+  (void)hipGetLastError();
+  if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
+                            dtype, workspace, static_cast<hipStream_t>(stream))) != KLA_OK)
     return st;
   return ok();
 }
@@ -239,17 +287,9 @@ kla_status kla_prefill_prepare(const void *q, const void *k, const float *g, con
                                const int32_t *cu_seqlens_host, int32_t n_seq, int32_t total_tokens,
                                int32_t n_heads, int32_t d_k, int32_t d_v, kla_dtype dtype,
                                void *workspace, size_t workspace_bytes, void *stream) {
-  kla_status st = check_prefill_args(q, k, nullptr, g, eta, eps, nullptr, nullptr, nullptr,
-                                     cu_seqlens, cu_seqlens_host, n_seq, total_tokens, n_heads,
-                                     d_k, d_v, dtype, workspace, workspace_bytes, true, false);
-  if (st != KLA_OK) return st;
-  if (total_tokens > 0 && !q)
-    return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, g and eta are required");
-  (void)hipGetLastError();
-  if ((st = enqueue_prepare(q, k, g, eta, eps, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
-                            dtype, workspace, static_cast<hipStream_t>(stream))) != KLA_OK)
-    return st;
-  return ok();
+  return kla_prefill_prepare_ex(q, k, g, eta, eps, cu_seqlens, cu_seqlens_host, n_seq,
+                                total_tokens, n_heads, d_k, d_v, dtype, workspace,
+                                workspace_bytes, nullptr, stream);
 }
 
 kla_status kla_prefill_scan(const void *q, const void *k, const void *v, const float *S0, void *o,
@@ -306,7 +346,8 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
   const kla::Dtype dt = to_dt(dtype);
   if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, tabs, s), "plan")) != KLA_OK)
     return st;
-  if ((st = hip_status(kla::launch_prep(dt, d_k, nullptr, k, g, eta, eps, tabs, n_seq, nch_ub,
+  const kla::CoefOpts co{kla::kBetaKaczmarz, 0, nullptr};
+  if ((st = hip_status(kla::launch_prep(dt, d_k, nullptr, k, g, eta, eps, co, tabs, n_seq, nch_ub,
                                         n_heads, Gbuf, beta, T, true, nullptr, nullptr, s),
                        "prep")) != KLA_OK)
     return st;
@@ -320,6 +361,15 @@ kla_status kla_decode_step(const void *q, const void *k, const void *v, const fl
                            const float *eta, float eps, const float *S, void *o,
                            float *S_new, int32_t batch, int32_t n_heads, int32_t d_k,
                            int32_t d_v, kla_dtype dtype, void *stream) {
+  return kla_decode_step_ex(q, k, v, g, eta, eps, S, o, S_new, batch, n_heads, d_k, d_v, dtype,
+                            nullptr, stream);
+}
+
+kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const float *g,
+                              const float *eta, float eps, const float *S, void *o,
+                              float *S_new, int32_t batch, int32_t n_heads, int32_t d_k,
+                              int32_t d_v, kla_dtype dtype, const kla_options *opts,
+                              void *stream) {
   if (dtype != KLA_DTYPE_F32 && dtype != KLA_DTYPE_BF16)
     return fail(KLA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   if (batch < 0 || n_heads <= 0)
@@ -343,10 +393,13 @@ kla_status kla_decode_step(const void *q, const void *k, const void *v, const fl
   const size_t nS = (size_t)batch * n_heads * d_k * d_v * sizeof(float);
   if (S_new != S && overlap(S_new, nS, S, nS))
     return fail(KLA_ERR_INVALID_ARGUMENT, "S_new may equal S but must not partially overlap it");
+  kla::CoefOpts co;
+  kla_status st = to_coef(opts, &co);
+  if (st != KLA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  kla_status st = hip_status(kla::launch_decode(to_dt(dtype), d_k, d_v, q, k, v, g, eta, eps, S, o,
-                                                S_new, batch, n_heads, s), "decode");
+  st = hip_status(kla::launch_decode(to_dt(dtype), d_k, d_v, q, k, v, g, eta, eps, co, S, o, S_new,
+                                     batch, n_heads, s), "decode");
   if (st != KLA_OK) return st;
   return ok();
 }
@@ -364,6 +417,6 @@ const char *kla_status_string(kla_status status) {
 
 const char *kla_last_error(void) { return g_last_error; }
 
-int32_t kla_version(void) { return 100; }
+int32_t kla_version(void) { return 200; }
 
 }  // extern "C"

@@ -98,6 +98,32 @@ template <typename T> __device__ __forceinline__ typename Frag<T>::type zero8() 
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// ---------------------------------------------------------------- write coefficient
+// Variants of the write coefficient b_t and of the readout (paper section 3.1, Eq. (3) for
+// the default; section 2 for the gated delta rule's b_t = eta_t; Appendix D and Table 5 for
+// the key-norm-only coefficient and the sequence factors 1/t, 1/sqrt(t), 1/log(t + 1) on
+// the Kaczmarz coefficient, t the absolute 1-based position in the sequence; section 3.3
+// and Algorithm 1 step 6 for the readout divided by ||q_t||).
+enum BetaMode { kBetaKaczmarz = 0, kBetaGated = 1, kBetaKeyNorm = 2, kBetaInvT = 3,
+                kBetaInvSqrtT = 4, kBetaInvLogT = 5 };
+struct CoefOpts {
+  int beta_mode;            // BetaMode
+  int normalize_q;          // nonzero: o_t = q_t S_t / ||q_t||
+  const int32_t *pos_offset;  // per sequence (prefill) or batch row (decode); may be null
+};
+
+// b_t from eta_t, den = ||k_t||^2 + eps and the absolute position t >= 1; a zero
+// denominator gives b_t = 0 wherever b_t divides by it.
+__device__ __forceinline__ float write_coef(int mode, float eta_t, float den, float t) {
+  if (mode == kBetaGated) return eta_t;
+  if (mode == kBetaKeyNorm) return den != 0.f ? 1.f / den : 0.f;
+  float b = den != 0.f ? eta_t / den : 0.f;
+  if (mode == kBetaInvT) b = b / t;
+  else if (mode == kBetaInvSqrtT) b = b / sqrtf(t);
+  else if (mode == kBetaInvLogT) b = b / logf(t + 1.f);
+  return b;
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kla_device.h"
+
 namespace kla {
 
 enum class Dtype { F32 = 0, BF16 = 1 };
@@ -25,15 +27,20 @@ inline int64_t chunk_upper_bound(int64_t n_seq, int64_t total_tokens) {
 hipError_t launch_plan(const int32_t *cu_in, int32_t n_seq, int32_t total_tokens, SeqTables t,
                        hipStream_t stream);
 
+// Decay factors per chunk-head, 3 x 64 fp32: exp(G_i), exp(G_last - G_i), and the output
+// factor exp(G_i) (divided by ||q_i|| under the normalised readout).
+constexpr int kGDFloats = 3 * 64;
+
 // a1 + a2: b, G, Gram, L, T = (I + L)^{-1} Diag(b) per chunk-head.  T is written in fp32
 // when t_fp32 is set, else in the operand type (what the scan kernel reads).  With q and
-// P_out given, also P = A o Q K^T per chunk-head (operand type, zero above the diagonal).
-// G_out / beta_out (per token) and GD_out (per chunk-head: exp(G_i) for the 64 rows, then
-// exp(G_last - G_i)) are each optional.
+// P_out given, also P = A o Q K^T per chunk-head (operand type, zero above the diagonal;
+// rows divided by ||q_i|| under the normalised readout).  G_out / beta_out (per token) and
+// GD_out (per chunk-head decay factors) are each optional.
 hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const float *g,
-                       const float *eta, float eps, SeqTables t, int32_t n_seq,
-                       int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out, void *T_out,
-                       bool t_fp32, void *P_out, float *GD_out, hipStream_t stream);
+                       const float *eta, float eps, const CoefOpts &opts, SeqTables t,
+                       int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
+                       float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
+                       hipStream_t stream);
 
 // Optional WY factors W = T Diag(exp G) K and U~ = T V (unit-check path).
 hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, const float *G,
@@ -48,7 +55,8 @@ hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k,
 
 // a5: one decode step.
 hipError_t launch_decode(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
-                         const float *g, const float *eta, float eps, const float *S, void *o,
-                         float *S_new, int32_t batch, int32_t H, hipStream_t stream);
+                         const float *g, const float *eta, float eps, const CoefOpts &opts,
+                         const float *S, void *o, float *S_new, int32_t batch, int32_t H,
+                         hipStream_t stream);
 
 }  // namespace kla

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
     const float *__restrict__ eta, float eps, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
     float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out,
-    float *__restrict__ GD_out) {
+    float *__restrict__ GD_out, CoefOpts opts) {
   __shared__ PrepSmem<Tin, DK> sm;
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= chunk_off[n_seq]) return;
@@ -209,8 +209,25 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
   ss += __shfl_xor(ss, 32, kWave);
   const float eta_r = __shfl(eta_l, my_row, kWave);
   const float den = ss + eps;
-  const float b_r = (row_ok && den != 0.f) ? eta_r / den : 0.f;
+  const float t_abs =
+      (float)(t0 - cu[n] + my_row + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
+  const float b_r = row_ok ? write_coef(opts.beta_mode, eta_r, den, t_abs) : 0.f;
   const float G_l = wave_inclusive_scan(g_l, lane);  // rows past the end carry G_last
+  // 1 / ||q|| of query row p_row under the normalised readout (0 for a zero query), else 1
+  float rq = 1.f;
+  if (opts.normalize_q) {
+    float qq = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float x = to_f32(qf[ks][s]);
+        qq = fmaf(x, x, qq);
+      }
+    qq += __shfl_xor(qq, 16, kWave);
+    qq += __shfl_xor(qq, 32, kWave);
+    rq = qq > 0.f ? 1.f / sqrtf(qq) : 0.f;
+  }
 
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
@@ -222,10 +239,16 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
     // per-chunk decays for the scan: exp(G_i) and exp(G_last - G_i)
     if (GD_out) {
       const float Glast = __shfl(G_l, kChunk - 1, kWave);
-      float *gd = GD_out + ((size_t)c * H + h) * (2 * kChunk);
+      float *gd = GD_out + ((size_t)c * H + h) * kGDFloats;
       gd[lane] = __expf(G_l);
       gd[kChunk + lane] = __expf(Glast - G_l);
     }
+  }
+  // the output factor exp(G_i) / ||q_i|| for the query rows this wavefront holds
+  {
+    const float G_p = __shfl(G_l, p_row, kWave);
+    if (GD_out && kg == 0)
+      GD_out[((size_t)c * H + h) * kGDFloats + 2 * kChunk + p_row] = __expf(G_p) * rq;
   }
   if (beta_out && kg == 0 && row_ok) beta_out[((size_t)(t0 + my_row)) * H + h] = b_r;
   __syncthreads();
@@ -274,7 +297,7 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
         const f32x4 G_cols = *reinterpret_cast<const f32x4 *>(&sm.G[j0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          pv[e] = (j0 + e <= p_row) ? __expf(G_me - G_cols[e]) * accp[e] : 0.f;
+          pv[e] = (j0 + e <= p_row) ? __expf(G_me - G_cols[e]) * accp[e] * rq : 0.f;
       }
       if constexpr (sizeof(Tin) == 2) {
         bf16x4 x4;
@@ -373,9 +396,10 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
 
 template <typename Tin, int DK>
 static hipError_t launch_prep_t(const void *q, const void *k, const float *g, const float *eta,
-                                float eps, SeqTables t, int32_t n_seq, int64_t n_chunks_ub,
-                                int32_t H, float *G_out, float *beta_out, void *T_out, bool t_fp32,
-                                void *P_out, float *GD_out, hipStream_t stream) {
+                                float eps, const CoefOpts &opts, SeqTables t, int32_t n_seq,
+                                int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out,
+                                void *T_out, bool t_fp32, void *P_out, float *GD_out,
+                                hipStream_t stream) {
   if (n_chunks_ub <= 0) return hipSuccess;
   const dim3 grid((unsigned)n_chunks_ub, H);
   const Tin *qq = static_cast<const Tin *>(q);
@@ -383,30 +407,31 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
   if (t_fp32 || sizeof(Tin) == 4)
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(256), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out);
+                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts);
   else
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(256), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out);
+                       G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out, opts);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const float *g,
-                       const float *eta, float eps, SeqTables t, int32_t n_seq,
-                       int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out, void *T_out,
-                       bool t_fp32, void *P_out, float *GD_out, hipStream_t stream) {
+                       const float *eta, float eps, const CoefOpts &opts, SeqTables t,
+                       int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
+                       float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
+                       hipStream_t stream) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
-      return launch_prep_t<__bf16, 128>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out,
+      return launch_prep_t<__bf16, 128>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
                                         beta_out, T_out, t_fp32, P_out, GD_out, stream);
-    return launch_prep_t<__bf16, 64>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                     T_out, t_fp32, P_out, GD_out, stream);
+    return launch_prep_t<__bf16, 64>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
+                                     beta_out, T_out, t_fp32, P_out, GD_out, stream);
   }
   if (d_k == 128)
-    return launch_prep_t<float, 128>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                     T_out, t_fp32, P_out, GD_out, stream);
-  return launch_prep_t<float, 64>(q, k, g, eta, eps, t, n_seq, n_chunks_ub, H, G_out, beta_out,
-                                  T_out, t_fp32, P_out, GD_out, stream);
+    return launch_prep_t<float, 128>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
+                                     beta_out, T_out, t_fp32, P_out, GD_out, stream);
+  return launch_prep_t<float, 64>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
+                                  beta_out, T_out, t_fp32, P_out, GD_out, stream);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -32,6 +32,8 @@
 // LDS tiles are stored in 16-byte units, unit u of row r at u ^ sw(r) (twice sw for fp32
 // tiles), with sw chosen so that each half-wavefront's 16-byte fragment reads and the
 // transpose reads of K^T hit distinct bank groups.
+#include <stddef.h>
+
 #include <type_traits>
 
 #include "kla_device.h"
@@ -131,8 +133,9 @@ struct ScanSlot {
   alignas(16) unsigned char T[kChunk * kChunk * sizeof(Tin)];
   alignas(16) unsigned char P[kChunk * kChunk * sizeof(Tin)];
   alignas(16) unsigned char V[kChunk * kBV * sizeof(Tin)];
-  alignas(16) float gam[kChunk];  // exp(G_i)
-  alignas(16) float dec[kChunk];  // exp(G_last - G_i)
+  alignas(16) float gam[kChunk];   // exp(G_i)
+  alignas(16) float dec[kChunk];   // exp(G_last - G_i)
+  alignas(16) float gamO[kChunk];  // output factor: exp(G_i), over ||q_i|| when normalised
 };
 
 template <typename Tin, int DK>
@@ -154,7 +157,7 @@ struct DmaPlan {
   static constexpr int NK = kChunk * DK * ES / 1024;      // per K (and per Q) tile
   static constexpr int NT = kChunk * kChunk * ES / 1024;  // per T (and per P) tile
   static constexpr int NV = kChunk * kBV * ES / 1024;     // value slice
-  // per producer wave: half of every tile and half of the 512-byte decay block
+  // per producer wave: half of every tile and one piece of the 768-byte decay block
   static constexpr int PER_WAVE = NK + NT + NV / 2 + 1;
   static_assert(NK % 2 == 0 && NT % 2 == 0 && NV % 2 == 0, "tiles split over two waves");
 };
@@ -243,7 +246,7 @@ void kla_scan_kernel(
     const size_t ch = (size_t)(cbase + c) * H + h;
     const Rsrc rt = make_rsrc(Tm + ch * (kChunk * kChunk), kChunk * kChunk * ES);
     const Rsrc rp = make_rsrc(Pm + ch * (kChunk * kChunk), kChunk * kChunk * ES);
-    const Rsrc rg = make_rsrc(GD + ch * (2 * kChunk), 2 * kChunk * sizeof(float));
+    const Rsrc rg = make_rsrc(GD + ch * kGDFloats, kGDFloats * sizeof(float));
 #pragma unroll
     for (int j = 0; j < DP::NK / 2; ++j) {
       const int J = 2 * j + pw;
@@ -261,9 +264,10 @@ void kla_scan_kernel(
       const int J = 2 * j + pw;
       dma16(rv, s.V + 1024 * J, offV[j]);
     }
-    // decays: wave 0 fetches gam (bytes 0..255), wave 1 dec (256..511), 16 lanes each
-    if (lane < 16)
-      dma16(rg, reinterpret_cast<unsigned char *>(s.gam) + 256 * pw, 256 * pw + 16 * lane);
+    // decays (gam, dec, gamO are consecutive in the slot): wave 0 fetches gam and dec
+    // (bytes 0..511, 32 lanes), wave 1 gamO (512..767, 16 lanes)
+    if (lane < 32 - 16 * pw)
+      dma16(rg, reinterpret_cast<unsigned char *>(s.gam) + 512 * pw, 512 * pw + 16 * lane);
   };
 
   // chunk c's outputs, parked in slot s's value tile, back to HBM: 16 bytes per lane per
@@ -439,7 +443,7 @@ void kla_scan_kernel(
     fp[5] = rd_frag(s.P, TP{}, frow(3), 1);
     float gt[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) gt[t] = s.gam[frow(t)];
+    for (int t = 0; t < 4; ++t) gt[t] = s.gamO[frow(t)];
     // ---- S = exp(G_last) S + K^T Diag(dec) U
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
@@ -548,6 +552,10 @@ static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const voi
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
                                 hipStream_t stream) {
   static_assert(sizeof(ScanSmem<Tin, DK>) <= kLdsBytes, "LDS budget");
+  using SLT = ScanSlot<Tin, DK>;
+  static_assert(offsetof(SLT, dec) == offsetof(SLT, gam) + 256 &&
+                    offsetof(SLT, gamO) == offsetof(SLT, gam) + 512,
+                "the decay block is fetched as one contiguous 768-byte piece");
   const size_t smem = sizeof(ScanSmem<Tin, DK>);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {

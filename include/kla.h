@@ -183,6 +183,67 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
                                    int32_t d_v, kla_dtype dtype, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/*
+ * Variants of the write coefficient and of the readout (the coverage of the
+ * pages' ablations; the default is the method itself):
+ *   KLA_BETA_KACZMARZ     b_t = eta_t / (||k_t||^2 + eps)      section 3.1, Eq. (3)
+ *   KLA_BETA_GATED        b_t = eta_t, the gated delta rule's learned coefficient
+ *                         (section 2; Table 5's "without normalization")
+ *   KLA_BETA_KEY_NORM     b_t = 1 / (||k_t||^2 + eps)          Table 5, key-norm only
+ *   KLA_BETA_INV_T        Kaczmarz coefficient x 1 / t          Appendix D,
+ *   KLA_BETA_INV_SQRT_T   Kaczmarz coefficient x 1 / sqrt(t)    sequence factors, with t
+ *   KLA_BETA_INV_LOG_T    Kaczmarz coefficient x 1 / log(t + 1) the absolute 1-based position
+ * Wherever b_t divides by ||k_t||^2 + eps, a zero denominator gives b_t = 0.
+ * normalize_q != 0 gives the readout o_t = q_t S_t / ||q_t||_2 of section 3.3 and
+ * Algorithm 1 step 6 (o_t = 0 for a zero query); 0 gives o_t = q_t S_t.
+ * pos_offset (device int32, [n_seq] for prefill, [batch] for decode, or NULL for
+ * all zeros) places a call's tokens in their sequences: the first token of
+ * sequence n in a prefill call is at position pos_offset[n] + 1, a decode step
+ * of batch row b is at position pos_offset[b] + 1.  Only the sequence-factor
+ * modes read it.  A NULL kla_options pointer means the defaults (Kaczmarz
+ * coefficient, o_t = q_t S_t).  An unknown mode gives KLA_ERR_UNSUPPORTED.
+ */
+typedef enum kla_beta_mode {
+  KLA_BETA_KACZMARZ = 0,
+  KLA_BETA_GATED = 1,
+  KLA_BETA_KEY_NORM = 2,
+  KLA_BETA_INV_T = 3,
+  KLA_BETA_INV_SQRT_T = 4,
+  KLA_BETA_INV_LOG_T = 5
+} kla_beta_mode;
+
+typedef struct kla_options {
+  int32_t beta_mode;          /* a kla_beta_mode value */
+  int32_t normalize_q;        /* nonzero: divide each readout by ||q_t||_2 */
+  const int32_t *pos_offset;  /* device, 4-byte aligned, or NULL */
+} kla_options;
+
+/* kla_prefill_chunked, kla_prefill_prepare and kla_decode_step with options
+ * (NULL = the defaults, which is what the calls without _ex use).  The scan
+ * half needs no options: kla_prefill_prepare_ex stores everything the variants
+ * change (b in T, the readout factor in P and the per-chunk decays) in the
+ * workspace. */
+kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, const float *g,
+                                  const float *eta, float eps, const float *S0, void *o,
+                                  float *S_T, const int32_t *cu_seqlens,
+                                  const int32_t *cu_seqlens_host, int32_t n_seq,
+                                  int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                                  int32_t d_v, kla_dtype dtype, void *workspace,
+                                  size_t workspace_bytes, const kla_options *opts, void *stream);
+
+kla_status kla_prefill_prepare_ex(const void *q, const void *k, const float *g,
+                                  const float *eta, float eps, const int32_t *cu_seqlens,
+                                  const int32_t *cu_seqlens_host, int32_t n_seq,
+                                  int32_t total_tokens, int32_t n_heads, int32_t d_k, int32_t d_v,
+                                  kla_dtype dtype, void *workspace, size_t workspace_bytes,
+                                  const kla_options *opts, void *stream);
+
+kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const float *g,
+                              const float *eta, float eps, const float *S, void *o,
+                              float *S_new, int32_t batch, int32_t n_heads, int32_t d_k,
+                              int32_t d_v, kla_dtype dtype, const kla_options *opts,
+                              void *stream);
+
 /* Static description of a status code. */
 const char *kla_status_string(kla_status status);
 

@@ -56,6 +56,13 @@ def _load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           dp, dp, ctypes.c_int]
         lib.kla_oracle_decode.restype = ctypes.c_int
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        lib.kla_oracle_prefill_v.argtypes = lib.kla_oracle_prefill.argtypes + [
+            ctypes.c_int, ctypes.c_int, i64p]
+        lib.kla_oracle_prefill_v.restype = ctypes.c_int
+        lib.kla_oracle_decode_v.argtypes = lib.kla_oracle_decode.argtypes + [
+            ctypes.c_int, ctypes.c_int, i64p]
+        lib.kla_oracle_decode_v.restype = ctypes.c_int
         lib.kla_oracle_max_threads.argtypes = []
         lib.kla_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -83,12 +90,32 @@ def max_threads() -> int:
     return int(_load().kla_oracle_max_threads())
 
 
-def prefill(q, k, v, g, eta, eps, S0=None, cu_seqlens=None, n_seq=None, nthreads=0):
+# Write-coefficient variants (the C oracle's `mode`; see the header of kla_oracle.c).
+MODES = {"kaczmarz": 0, "gated": 1, "key_norm": 2, "inv_t": 3, "inv_sqrt_t": 4, "inv_log_t": 5}
+
+
+def _mode(beta_mode) -> int:
+    return MODES[beta_mode] if isinstance(beta_mode, str) else int(beta_mode)
+
+
+def _i64(x, n):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(x.cpu() if hasattr(x, "cpu") else x, dtype=np.int64))
+    if a.shape != (n,):
+        raise ValueError(f"pos_offset must have {n} entries")
+    return a
+
+
+def prefill(q, k, v, g, eta, eps, S0=None, cu_seqlens=None, n_seq=None, nthreads=0,
+            beta_mode="kaczmarz", normalize_q=False, pos_offset=None):
     """Tokenwise fp64 prefill.
 
     q, k: [n_tok, H, d_k]; v: [n_tok, H, d_v]; g, eta: [n_tok, H];
     S0: [n_seq, H, d_k, d_v] or None (zeros); cu_seqlens: [n_seq+1] token offsets,
     or None for one sequence per leading batch row when q is [B, T, H, d_k].
+    beta_mode / normalize_q / pos_offset ([n_seq]: the first token of sequence n is at
+    position pos_offset[n] + 1) select the variants.
     Returns (o [n_tok, H, d_v], S_T [n_seq, H, d_k, d_v]) as float64 numpy arrays,
     with o shaped like v.
     """
@@ -119,19 +146,23 @@ def prefill(q, k, v, g, eta, eps, S0=None, cu_seqlens=None, n_seq=None, nthreads
     cu = np.ascontiguousarray(cu)
     o = np.empty((q.shape[0], H, dv), dtype=np.float64)
     ST = np.empty((ns, H, dk, dv), dtype=np.float64)
-    rc = _load().kla_oracle_prefill(
+    po = _i64(pos_offset, ns)
+    rc = _load().kla_oracle_prefill_v(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S0a),
         cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ns, H, dk, dv, _ptr(o), _ptr(ST),
-        int(nthreads))
+        int(nthreads), _mode(beta_mode), 1 if normalize_q else 0,
+        None if po is None else po.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
     if rc != 0:
         raise RuntimeError("kla_oracle_prefill failed")
     return o.reshape(out_shape), ST
 
 
-def decode(q, k, v, g, eta, eps, S, nthreads=0):
+def decode(q, k, v, g, eta, eps, S, nthreads=0, beta_mode="kaczmarz", normalize_q=False,
+           pos_offset=None):
     """One tokenwise fp64 step per sequence.
 
     q, k: [B, H, d_k]; v: [B, H, d_v]; g, eta: [B, H]; S: [B, H, d_k, d_v].
+    Variants as in prefill (pos_offset [B]: this token is at position pos_offset + 1).
     Returns (o [B, H, d_v], S_new [B, H, d_k, d_v]) as float64 numpy arrays.
     """
     q, k, v, g, eta, S = (_f64(x) for x in (q, k, v, g, eta, S))
@@ -139,8 +170,11 @@ def decode(q, k, v, g, eta, eps, S, nthreads=0):
     dv = v.shape[-1]
     o = np.empty((B, H, dv), dtype=np.float64)
     Sn = np.empty((B, H, dk, dv), dtype=np.float64)
-    rc = _load().kla_oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps),
-                                   _ptr(S), B, H, dk, dv, _ptr(o), _ptr(Sn), int(nthreads))
+    po = _i64(pos_offset, B)
+    rc = _load().kla_oracle_decode_v(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S), B, H, dk, dv,
+        _ptr(o), _ptr(Sn), int(nthreads), _mode(beta_mode), 1 if normalize_q else 0,
+        None if po is None else po.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
     if rc != 0:
         raise RuntimeError("kla_oracle_decode failed")
     return o, Sn

@@ -20,6 +20,18 @@
  *     o_t  = q_t S_t                        readout on the q given (no 1/||q||;
  *                                            normalising q is the caller's job)
  *
+ * Variants (the pages' ablations and readout, selected by `mode` / `normq`):
+ *   mode 0  b_t = eta_t / (||k_t||^2 + eps)           the method, Eq. (3)
+ *   mode 1  b_t = eta_t                               the gated delta rule's learned
+ *                                                     coefficient (s.2; Table 5 "without
+ *                                                     normalization")
+ *   mode 2  b_t = 1 / (||k_t||^2 + eps)               Table 5 "key-norm only"
+ *   mode 3, 4, 5  the mode-0 coefficient times 1/t, 1/sqrt(t), 1/log(t + 1),
+ *                 t the absolute 1-based position in the sequence (Appendix D,
+ *                 "sequence factor"; the second factor is printed without its
+ *                 root in the extracted text and read as 1/sqrt(t))
+ *   normq   o_t = q_t S_t / ||q_t||_2 (s.3.3, Algorithm 1 step 6), 0 for q_t = 0
+ *
  * Readings of points the pages leave open:
  *   - if ||k_t||^2 + eps == 0 the step is b_t = 0 (no write): the constraint
  *     0 = v_t cannot be met and the minimal-change state is S~ itself;
@@ -38,11 +50,13 @@
 #include <omp.h>
 #endif
 
-/* One tokenwise step on one head's state S (dk x dv, row-major, d_v fastest).
- * r is caller scratch of length dv. Writes o (length dv) if o != NULL. */
+/* One tokenwise step on one head's state S (dk x dv, row-major, d_v fastest) at
+ * absolute position t (1-based).  r is caller scratch of length dv.  Writes o
+ * (length dv) if o != NULL. */
 static void kla_oracle_token(double *S, const double *q, const double *k,
                              const double *v, double g, double eta, double eps,
-                             int dk, int dv, double *r, double *o) {
+                             int dk, int dv, double *r, double *o, int mode,
+                             int normq, double t) {
   const double a = exp(g);
   /* S~ = a S */
   for (int i = 0; i < dk; ++i)
@@ -57,18 +71,34 @@ static void kla_oracle_token(double *S, const double *q, const double *k,
   double kk = 0.0;
   for (int i = 0; i < dk; ++i) kk += k[i] * k[i];
   const double den = kk + eps;
-  const double b = (den == 0.0) ? 0.0 : eta / den;
+  double b;
+  if (mode == 1) {
+    b = eta;
+  } else if (mode == 2) {
+    b = (den == 0.0) ? 0.0 : 1.0 / den;
+  } else {
+    b = (den == 0.0) ? 0.0 : eta / den;
+    if (mode == 3) b /= t;
+    else if (mode == 4) b /= sqrt(t);
+    else if (mode == 5) b /= log(t + 1.0);
+  }
   /* S = S~ + b k^T e */
   for (int i = 0; i < dk; ++i) {
     const double bk = b * k[i];
     for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += bk * r[j];
   }
-  /* o = q S */
+  /* o = q S, or q S / ||q|| */
   if (o) {
+    double scale = 1.0;
+    if (normq) {
+      double qq = 0.0;
+      for (int i = 0; i < dk; ++i) qq += q[i] * q[i];
+      scale = (qq == 0.0) ? 0.0 : 1.0 / sqrt(qq);
+    }
     for (int j = 0; j < dv; ++j) {
       double acc = 0.0;
       for (int i = 0; i < dk; ++i) acc += q[i] * S[(size_t)i * dv + j];
-      o[j] = acc;
+      o[j] = acc * scale;
     }
   }
 }
@@ -81,10 +111,11 @@ static void kla_oracle_token(double *S, const double *q, const double *k,
  *   nthreads <= 0 uses the OpenMP default.
  * Returns 0, or -1 on a bad argument / allocation failure.
  */
-int kla_oracle_prefill(const double *q, const double *k, const double *v,
-                       const double *g, const double *eta, double eps,
-                       const double *S0, const int64_t *cu, int n_seq, int H,
-                       int dk, int dv, double *o, double *S_T, int nthreads) {
+int kla_oracle_prefill_v(const double *q, const double *k, const double *v,
+                         const double *g, const double *eta, double eps,
+                         const double *S0, const int64_t *cu, int n_seq, int H,
+                         int dk, int dv, double *o, double *S_T, int nthreads,
+                         int mode, int normq, const int64_t *pos_offset) {
   if (!q || !k || !v || !g || !eta || !cu || !o || !S_T) return -1;
   if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   const long pairs = (long)n_seq * H;
@@ -104,14 +135,25 @@ int kla_oracle_prefill(const double *q, const double *k, const double *v,
       memcpy(S, S0 + (size_t)p * dk * dv, sizeof(double) * (size_t)dk * dv);
     else
       memset(S, 0, sizeof(double) * (size_t)dk * dv);
+    const int64_t base = pos_offset ? pos_offset[n] : 0;
     for (int64_t t = cu[n]; t < cu[n + 1]; ++t) {
       const size_t th = (size_t)t * H + h;
       kla_oracle_token(S, q + th * dk, k + th * dk, v + th * dv, g[th], eta[th],
-                       eps, dk, dv, r, o + th * dv);
+                       eps, dk, dv, r, o + th * dv, mode, normq,
+                       (double)(base + (t - cu[n]) + 1));
     }
     free(r);
   }
   return failed ? -1 : 0;
+}
+
+/* The method itself: mode 0, o_t = q_t S_t. */
+int kla_oracle_prefill(const double *q, const double *k, const double *v,
+                       const double *g, const double *eta, double eps,
+                       const double *S0, const int64_t *cu, int n_seq, int H,
+                       int dk, int dv, double *o, double *S_T, int nthreads) {
+  return kla_oracle_prefill_v(q, k, v, g, eta, eps, S0, cu, n_seq, H, dk, dv, o,
+                              S_T, nthreads, 0, 0, NULL);
 }
 
 /*
@@ -119,10 +161,11 @@ int kla_oracle_prefill(const double *q, const double *k, const double *v,
  *   q, k [B, H, dk]   v, o [B, H, dv]   g, eta [B, H]   S, S_new [B, H, dk, dv]
  * S_new may equal S.
  */
-int kla_oracle_decode(const double *q, const double *k, const double *v,
-                      const double *g, const double *eta, double eps,
-                      const double *S, int B, int H, int dk, int dv, double *o,
-                      double *S_new, int nthreads) {
+int kla_oracle_decode_v(const double *q, const double *k, const double *v,
+                        const double *g, const double *eta, double eps,
+                        const double *S, int B, int H, int dk, int dv, double *o,
+                        double *S_new, int nthreads, int mode, int normq,
+                        const int64_t *pos_offset) {
   if (!q || !k || !v || !g || !eta || !S || !o || !S_new) return -1;
   if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   const long pairs = (long)B * H;
@@ -139,12 +182,22 @@ int kla_oracle_decode(const double *q, const double *k, const double *v,
     if (!r) { failed = 1; continue; }
     if (Sp != S + (size_t)p * dk * dv)
       memcpy(Sp, S + (size_t)p * dk * dv, sizeof(double) * (size_t)dk * dv);
+    const double t = (double)((pos_offset ? pos_offset[p / H] : 0) + 1);
     kla_oracle_token(Sp, q + (size_t)p * dk, k + (size_t)p * dk,
                      v + (size_t)p * dv, g[p], eta[p], eps, dk, dv, r,
-                     o + (size_t)p * dv);
+                     o + (size_t)p * dv, mode, normq, t);
     free(r);
   }
   return failed ? -1 : 0;
+}
+
+/* The method itself: mode 0, o_t = q_t S_t. */
+int kla_oracle_decode(const double *q, const double *k, const double *v,
+                      const double *g, const double *eta, double eps,
+                      const double *S, int B, int H, int dk, int dv, double *o,
+                      double *S_new, int nthreads) {
+  return kla_oracle_decode_v(q, k, v, g, eta, eps, S, B, H, dk, dv, o, S_new,
+                             nthreads, 0, 0, NULL);
 }
 
 /* Threads the OpenMP runtime would use (for reporting the CPU baseline). */

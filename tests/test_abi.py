@@ -138,3 +138,37 @@ def test_decode_argument_errors(lib, over, status):
 def test_last_error_is_thread_local_text(lib):
     _decode(lib, dk=32)
     assert "d_k" in lib.kla_last_error().decode()
+
+
+def _opts(mode=0, normq=0, pos=None):
+    return ctypes.pointer(kla.KlaOptions(mode, normq, pos))
+
+
+@pytest.mark.parametrize("opts,status", [
+    (lambda: _opts(mode=6), UNSUPPORTED),       # unknown coefficient mode
+    (lambda: _opts(mode=-1), UNSUPPORTED),
+    (lambda: _opts(mode=3, pos=FAKE + 2), INVALID),   # int32 offsets need 4-byte alignment
+])
+def test_options_errors(lib, opts, status):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, eta=FAKE * 5, o=FAKE * 6)
+    ws = FAKE * 64
+    nb = kla.kla_prefill_workspace_bytes(2, 256, 4, 128, 128)
+    st = lib.kla_prefill_chunked_ex(a["q"], a["k"], a["v"], a["g"], a["eta"], 1e-6, None, a["o"],
+                                    None, None, None, 2, 256, 4, 128, 128, BF16, ws, nb, opts(),
+                                    None)
+    assert st == status
+    st = lib.kla_prefill_prepare_ex(a["q"], a["k"], a["g"], a["eta"], 1e-6, None, None, 2, 256, 4,
+                                    128, 128, BF16, ws, nb, opts(), None)
+    assert st == status
+    st = lib.kla_decode_step_ex(a["q"], a["k"], a["v"], a["g"], a["eta"], 1e-6, FAKE * 7, a["o"],
+                                FAKE * 7, 4, 2, 128, 128, BF16, opts(), None)
+    assert st == status
+    assert lib.kla_last_error().decode() != ""
+
+
+def test_options_default_pointer_is_accepted_up_to_the_workspace_check(lib):
+    # NULL options are the defaults: argument checking proceeds to the missing workspace
+    st = lib.kla_prefill_chunked_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1e-6, None,
+                                    FAKE * 6, None, None, None, 2, 256, 4, 128, 128, BF16, None, 0,
+                                    None, None)
+    assert st == WORKSPACE
