@@ -204,12 +204,19 @@ kla_status enqueue_prepare(const void *q, const void *k, const float *g, const f
                            void *workspace, hipStream_t s) {
   const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
+  kla::PlanArgs pa{kla::kPlanTables, cu_seqlens, total_tokens};
+  if (!cu_seqlens)
+    pa.mode = kla::kPlanDense;
+  else if (n_seq <= kla::kPlanWaveMax)
+    pa.mode = kla::kPlanWave;
   kla_status st;
-  if ((st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan")) != KLA_OK)
+  if (pa.mode == kla::kPlanTables &&
+      (st = hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan")) !=
+          KLA_OK)
     return st;
   return hip_status(kla::launch_prep(to_dt(dtype), d_k, q, k, g, eta, eps, opts, wv.tabs, n_seq,
                                      nch_ub, n_heads, nullptr, nullptr, wv.T, false, wv.P, wv.GD,
-                                     s),
+                                     pa, s),
                     "prep");
 }
 
@@ -348,7 +355,8 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
     return st;
   const kla::CoefOpts co{kla::kBetaKaczmarz, 0, nullptr};
   if ((st = hip_status(kla::launch_prep(dt, d_k, nullptr, k, g, eta, eps, co, tabs, n_seq, nch_ub,
-                                        n_heads, Gbuf, beta, T, true, nullptr, nullptr, s),
+                                        n_heads, Gbuf, beta, T, true, nullptr, nullptr,
+                                        kla::PlanArgs{kla::kPlanTables, nullptr, total_tokens}, s),
                        "prep")) != KLA_OK)
     return st;
   if ((st = hip_status(kla::launch_wy(dt, d_k, d_v, k, v, Gbuf, T, tabs, n_seq, nch_ub, n_heads,

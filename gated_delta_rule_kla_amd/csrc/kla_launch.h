@@ -27,6 +27,18 @@ inline int64_t chunk_upper_bound(int64_t n_seq, int64_t total_tokens) {
 hipError_t launch_plan(const int32_t *cu_in, int32_t n_seq, int32_t total_tokens, SeqTables t,
                        hipStream_t stream);
 
+// How the prep kernel finds each chunk's sequence.  kPlanTables: from tables launch_plan
+// wrote.  kPlanDense (cu_in == NULL, equal lengths) and kPlanWave (n_seq <= kPlanWaveMax):
+// computed inside the prep kernel, which then also writes the tables for the scan, so that
+// no plan launch is needed.
+enum PlanMode { kPlanTables = 0, kPlanDense = 1, kPlanWave = 2 };
+constexpr int kPlanWaveMax = 63;
+struct PlanArgs {
+  int mode;
+  const int32_t *cu_in;  // raw offsets (kPlanWave)
+  int32_t total;         // total tokens
+};
+
 // Decay factors per chunk-head, 3 x 64 fp32: exp(G_i), exp(G_last - G_i), and the output
 // factor exp(G_i) (divided by ||q_i|| under the normalised readout).
 constexpr int kGDFloats = 3 * 64;
@@ -40,7 +52,7 @@ hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const fl
                        const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                        int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
-                       hipStream_t stream);
+                       const PlanArgs &pa, hipStream_t stream);
 
 // Optional WY factors W = T Diag(exp G) K and U~ = T V (unit-check path).
 hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, const float *G,

@@ -91,6 +91,82 @@ __device__ __forceinline__ int find_sequence(const int32_t *__restrict__ chunk_o
   return lo;
 }
 
+// Chunk c of the packed input: sequence n, the sequence's first token ts, the chunk's first
+// token t0 and its length.  Three ways to get there (PlanMode):
+//  - kPlanTables: read the tables the plan kernel wrote;
+//  - kPlanDense:  equal-length sequences (no offsets given), pure arithmetic; workgroups of
+//                 head 0 also write the tables (entry 256 c + tid) for the scan;
+//  - kPlanWave:   at most 63 sequences: every wavefront sanitises the offsets and counts
+//                 chunks itself, one sequence per lane, exactly as the plan kernel does;
+//                 wavefront 0 of workgroup (0, 0) writes the tables.
+// Returns false when c lies past the last chunk.
+struct ChunkLoc {
+  int n, ts, t0, len;
+};
+
+__device__ __forceinline__ int wave_max_scan_i(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x = max(x, y);
+  }
+  return x;
+}
+__device__ __forceinline__ int wave_sum_scan_i(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ bool locate_chunk(const PlanArgs &pa, SeqTables tabs, int n_seq, int c,
+                                             bool write_tables, ChunkLoc &loc) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (pa.mode == kPlanDense) {
+    const int L = pa.total / n_seq, cpc = (L + kChunk - 1) / kChunk;
+    if (write_tables) {
+      const int e = c * (int)blockDim.x + tid;
+      if (e <= n_seq) {
+        tabs.cu[e] = e * L;
+        tabs.chunk_off[e] = e * cpc;
+      }
+    }
+    if (cpc == 0 || c >= n_seq * cpc) return false;
+    loc.n = c / cpc;
+    loc.ts = loc.n * L;
+    loc.t0 = loc.ts + (c - loc.n * cpc) * kChunk;
+    loc.len = min(kChunk, loc.ts + L - loc.t0);
+    return true;
+  }
+  if (pa.mode == kPlanWave) {
+    // lane e holds offset e: running maximum of the clamped offsets, then chunk counts
+    const int raw = lane <= n_seq ? min(max(pa.cu_in[lane], 0), pa.total) : pa.total;
+    const int cs = wave_max_scan_i(raw, lane);
+    const int nxt = __shfl(cs, min(lane + 1, kWave - 1), kWave);
+    const int cnt = lane < n_seq ? (nxt - cs + kChunk - 1) / kChunk : 0;
+    const int co = wave_sum_scan_i(cnt, lane) - cnt;  // exclusive: chunk_off[lane]
+    if (write_tables && tid < kWave && lane <= n_seq) {
+      tabs.cu[lane] = cs;
+      tabs.chunk_off[lane] = co;
+    }
+    if (c >= __shfl(co, n_seq, kWave)) return false;
+    const unsigned long long below = __ballot(lane < n_seq && co <= c);
+    loc.n = __popcll(below) - 1;
+    loc.ts = __shfl(cs, loc.n, kWave);
+    loc.t0 = loc.ts + (c - __shfl(co, loc.n, kWave)) * kChunk;
+    loc.len = min(kChunk, __shfl(cs, loc.n + 1, kWave) - loc.t0);
+    return true;
+  }
+  if (c >= tabs.chunk_off[n_seq]) return false;
+  loc.n = find_sequence(tabs.chunk_off, n_seq, c);
+  loc.ts = tabs.cu[loc.n];
+  loc.t0 = loc.ts + (c - tabs.chunk_off[loc.n]) * kChunk;
+  loc.len = min(kChunk, tabs.cu[loc.n + 1] - loc.t0);
+  return true;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Prep / UT kernel: one workgroup (4 wavefronts) per (chunk, head); wavefront w owns the
 // 16 chunk rows 16 w .. 16 w + 15.
@@ -156,16 +232,18 @@ __device__ __forceinline__ f32x4 mm16_acc(const float *A, int lda, const f32x4 &
 template <typename Tin, int DK, typename TOut>
 __global__ __launch_bounds__(256) void kla_prep_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ eta, float eps, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
+    const float *__restrict__ eta, float eps, int32_t *__restrict__ cu,
+    int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
     float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out,
-    float *__restrict__ GD_out, CoefOpts opts) {
+    float *__restrict__ GD_out, CoefOpts opts, PlanArgs pa) {
   __shared__ PrepSmem<Tin, DK> sm;
   const int c = blockIdx.x, h = blockIdx.y;
-  if (c >= chunk_off[n_seq]) return;
-  const int n = find_sequence(chunk_off, n_seq, c);
-  const int t0 = cu[n] + (c - chunk_off[n]) * kChunk;
-  const int len = min(kChunk, cu[n + 1] - t0);
+  ChunkLoc loc;
+  const bool write_tables = pa.mode == kPlanDense ? h == 0 : (c == 0 && h == 0);
+  if (!locate_chunk(pa, SeqTables{cu, chunk_off},
+                    n_seq, c, write_tables, loc))
+    return;
+  const int n = loc.n, t0 = loc.t0, len = loc.len;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kg = lane >> 4;
   const int i0 = 16 * wid;  // this wavefront's rows
@@ -210,7 +288,7 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
   const float eta_r = __shfl(eta_l, my_row, kWave);
   const float den = ss + eps;
   const float t_abs =
-      (float)(t0 - cu[n] + my_row + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
+      (float)(t0 - loc.ts + my_row + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
   const float b_r = row_ok ? write_coef(opts.beta_mode, eta_r, den, t_abs) : 0.f;
   const float G_l = wave_inclusive_scan(g_l, lane);  // rows past the end carry G_last
   // 1 / ||q|| of query row p_row under the normalised readout (0 for a zero query), else 1
@@ -399,7 +477,7 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
                                 float eps, const CoefOpts &opts, SeqTables t, int32_t n_seq,
                                 int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out,
                                 void *T_out, bool t_fp32, void *P_out, float *GD_out,
-                                hipStream_t stream) {
+                                const PlanArgs &pa, hipStream_t stream) {
   if (n_chunks_ub <= 0) return hipSuccess;
   const dim3 grid((unsigned)n_chunks_ub, H);
   const Tin *qq = static_cast<const Tin *>(q);
@@ -407,11 +485,11 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
   if (t_fp32 || sizeof(Tin) == 4)
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(256), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts);
+                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts, pa);
   else
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(256), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out, opts);
+                       G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out, opts, pa);
   return hipGetLastError();
 }
 
@@ -419,19 +497,19 @@ hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const fl
                        const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                        int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
-                       hipStream_t stream) {
+                       const PlanArgs &pa, hipStream_t stream) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
       return launch_prep_t<__bf16, 128>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
-                                        beta_out, T_out, t_fp32, P_out, GD_out, stream);
+                                        beta_out, T_out, t_fp32, P_out, GD_out, pa, stream);
     return launch_prep_t<__bf16, 64>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
-                                     beta_out, T_out, t_fp32, P_out, GD_out, stream);
+                                     beta_out, T_out, t_fp32, P_out, GD_out, pa, stream);
   }
   if (d_k == 128)
     return launch_prep_t<float, 128>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
-                                     beta_out, T_out, t_fp32, P_out, GD_out, stream);
+                                     beta_out, T_out, t_fp32, P_out, GD_out, pa, stream);
   return launch_prep_t<float, 64>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
-                                  beta_out, T_out, t_fp32, P_out, GD_out, stream);
+                                  beta_out, T_out, t_fp32, P_out, GD_out, pa, stream);
 }
 
 // ---------------------------------------------------------------------------------------------

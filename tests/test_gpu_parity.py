@@ -169,6 +169,49 @@ def test_prefill_packed_ragged(kla):
     assert torch.equal(ST[1], d["S0"][1]) and torch.equal(ST[6], d["S0"][6])
 
 
+def test_prefill_many_sequences(kla):
+    """100 packed sequences (more than one wavefront can plan inside the prep kernel, so the
+    separate planning kernel runs) with empty, one-token and multi-chunk members."""
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.choice([0, 1, 7, 63, 64, 65, 130], size=100)]
+    w = ki.Workload(94, "packed-unit", len(lens), 2, 64, 64, torch.bfloat16, lens=tuple(lens),
+                    s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    o, ST = run_prefill(kla, d)
+    oo, So = oracle_prefill(d)
+    check(o, oo, 2e-2, "o")
+    check(ST, So, 2e-2, "ST")
+
+
+@pytest.mark.parametrize("n_seq", [5, 63, 64, 90])
+def test_prefill_malformed_offsets_are_sanitised(kla, n_seq):
+    """Offsets outside [0, total] or decreasing are clamped and made non-decreasing (running
+    maximum): the result equals, bit for bit, the run with the sanitised offsets, both where
+    the prep kernel plans the sequences itself (n_seq <= 63) and where the plan kernel does."""
+    rng = np.random.default_rng(n_seq)
+    total = 40 * n_seq
+    raw = np.sort(rng.integers(0, total, n_seq + 1)).astype(np.int64)
+    raw[0], raw[-1] = 0, total
+    bad = raw.copy()
+    bad[1::3] = bad[1::3] - 100      # dips below the previous offset (or below 0)
+    bad[-2] = total + 77             # past the end
+    clean = np.maximum.accumulate(np.clip(bad, 0, total))
+    assert clean[-1] == total and np.any(bad != clean)
+    w = ki.Workload(95, "unit", 1, 2, 64, 64, torch.bfloat16, T=total, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    S0 = torch.randn(n_seq, 2, 64, 64, device=DEV) * 0.1
+    outs = []
+    for cu in (bad, clean):
+        o, ST = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                        S0=S0, n_seq=n_seq,
+                                        cu_seqlens=torch.tensor(cu, dtype=torch.int32,
+                                                                device=DEV))
+        torch.cuda.synchronize()
+        outs.append((o.clone(), ST.clone()))
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][0], outs[1][0])
+
+
 def test_prefill_layer_workload_full(kla):
     """Workload 1 (B=4, H=16, T=4096, d=128, bf16, random S0) at full size, every output."""
     d = to_dev(ki.prefill_inputs(1))
