@@ -41,6 +41,32 @@ template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) {
   return static_cast<__bf16>(x);
 }
 
+// ---------------------------------------------------------------- buffer access
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0, byte-addressed, range checked against `bytes`): loads
+// beyond the range return zeros and stores beyond it are dropped.
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// 8 consecutive elements at byte offset voff (zeros out of range).
+template <typename T> __device__ __forceinline__ typename Frag<T>::type bload8(Rsrc r, int voff);
+template <> __device__ __forceinline__ bf16x8 bload8<__bf16>(Rsrc r, int voff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+template <> __device__ __forceinline__ f32x8 bload8<float>(Rsrc r, int voff) {
+  const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0);
+  const f32x4 fa = __builtin_bit_cast(f32x4, a), fb = __builtin_bit_cast(f32x4, b);
+  return f32x8{fa[0], fa[1], fa[2], fa[3], fb[0], fb[1], fb[2], fb[3]};
+}
+__device__ __forceinline__ float bload1(Rsrc r, int voff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
 // ---------------------------------------------------------------- MFMA k-step
 __device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -114,13 +140,15 @@ struct CoefOpts {
 
 // b_t from eta_t, den = ||k_t||^2 + eps and the absolute position t >= 1; a zero
 // denominator gives b_t = 0 wherever b_t divides by it.
+// Reciprocals use the hardware's approximate v_rcp_f32 / v_rsq_f32 (about 1 ulp).
 __device__ __forceinline__ float write_coef(int mode, float eta_t, float den, float t) {
   if (mode == kBetaGated) return eta_t;
-  if (mode == kBetaKeyNorm) return den != 0.f ? 1.f / den : 0.f;
-  float b = den != 0.f ? eta_t / den : 0.f;
-  if (mode == kBetaInvT) b = b / t;
-  else if (mode == kBetaInvSqrtT) b = b / sqrtf(t);
-  else if (mode == kBetaInvLogT) b = b / logf(t + 1.f);
+  const float rden = den != 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
+  if (mode == kBetaKeyNorm) return rden;
+  float b = eta_t * rden;
+  if (mode == kBetaInvT) b *= __builtin_amdgcn_rcpf(t);
+  else if (mode == kBetaInvSqrtT) b *= __builtin_amdgcn_rsqf(t);
+  else if (mode == kBetaInvLogT) b *= __builtin_amdgcn_rcpf(logf(t + 1.f));
   return b;
 }
 
@@ -129,6 +157,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
   return x;
+}
+
+// LDS-only workgroup barrier: orders LDS traffic without waiting for the global
+// loads that are deliberately left in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Inclusive prefix sum across the 64 lanes of a wavefront.

@@ -91,15 +91,13 @@ __device__ __forceinline__ int find_sequence(const int32_t *__restrict__ chunk_o
   return lo;
 }
 
-// Chunk c of the packed input: sequence n, the sequence's first token ts, the chunk's first
-// token t0 and its length.  Three ways to get there (PlanMode):
-//  - kPlanTables: read the tables the plan kernel wrote;
-//  - kPlanDense:  equal-length sequences (no offsets given), pure arithmetic; workgroups of
-//                 head 0 also write the tables (entry 256 c + tid) for the scan;
+// Where chunk c of the packed input lies: sequence n, the sequence's first token ts, the
+// chunk's first token t0 and its length.  Three ways to get there (PlanMode):
+//  - kPlanTables: the tables the plan kernel wrote;
+//  - kPlanDense:  equal-length sequences (no offsets given), pure arithmetic;
 //  - kPlanWave:   at most 63 sequences: every wavefront sanitises the offsets and counts
-//                 chunks itself, one sequence per lane, exactly as the plan kernel does;
-//                 wavefront 0 of workgroup (0, 0) writes the tables.
-// Returns false when c lies past the last chunk.
+//                 chunks itself, one sequence per lane, exactly as the plan kernel does.
+// In the last two modes the prep kernel also writes the tables, for the scan.
 struct ChunkLoc {
   int n, ts, t0, len;
 };
@@ -121,284 +119,380 @@ __device__ __forceinline__ int wave_sum_scan_i(int x, int lane) {
   return x;
 }
 
-__device__ __forceinline__ bool locate_chunk(const PlanArgs &pa, SeqTables tabs, int n_seq, int c,
-                                             bool write_tables, ChunkLoc &loc) {
-  const int tid = threadIdx.x, lane = tid & 63;
+struct Planner {
+  int mode, n_seq, n_chunks;
+  int L, cpc;   // kPlanDense: sequence length, chunks per sequence
+  int cs, co;   // kPlanWave: offset and first chunk of sequence `lane`
+  SeqTables tabs;
+};
+
+__device__ __forceinline__ Planner make_planner(const PlanArgs &pa, SeqTables tabs, int n_seq) {
+  Planner p;
+  p.mode = pa.mode;
+  p.n_seq = n_seq;
+  p.tabs = tabs;
+  p.L = p.cpc = p.cs = p.co = 0;
+  const int lane = threadIdx.x & 63;
   if (pa.mode == kPlanDense) {
-    const int L = pa.total / n_seq, cpc = (L + kChunk - 1) / kChunk;
-    if (write_tables) {
-      const int e = c * (int)blockDim.x + tid;
-      if (e <= n_seq) {
-        tabs.cu[e] = e * L;
-        tabs.chunk_off[e] = e * cpc;
-      }
-    }
-    if (cpc == 0 || c >= n_seq * cpc) return false;
-    loc.n = c / cpc;
-    loc.ts = loc.n * L;
-    loc.t0 = loc.ts + (c - loc.n * cpc) * kChunk;
-    loc.len = min(kChunk, loc.ts + L - loc.t0);
-    return true;
-  }
-  if (pa.mode == kPlanWave) {
+    p.L = pa.total / n_seq;
+    p.cpc = (p.L + kChunk - 1) / kChunk;
+    p.n_chunks = n_seq * p.cpc;
+  } else if (pa.mode == kPlanWave) {
     // lane e holds offset e: running maximum of the clamped offsets, then chunk counts
     const int raw = lane <= n_seq ? min(max(pa.cu_in[lane], 0), pa.total) : pa.total;
-    const int cs = wave_max_scan_i(raw, lane);
-    const int nxt = __shfl(cs, min(lane + 1, kWave - 1), kWave);
-    const int cnt = lane < n_seq ? (nxt - cs + kChunk - 1) / kChunk : 0;
-    const int co = wave_sum_scan_i(cnt, lane) - cnt;  // exclusive: chunk_off[lane]
-    if (write_tables && tid < kWave && lane <= n_seq) {
-      tabs.cu[lane] = cs;
-      tabs.chunk_off[lane] = co;
-    }
-    if (c >= __shfl(co, n_seq, kWave)) return false;
-    const unsigned long long below = __ballot(lane < n_seq && co <= c);
-    loc.n = __popcll(below) - 1;
-    loc.ts = __shfl(cs, loc.n, kWave);
-    loc.t0 = loc.ts + (c - __shfl(co, loc.n, kWave)) * kChunk;
-    loc.len = min(kChunk, __shfl(cs, loc.n + 1, kWave) - loc.t0);
-    return true;
+    p.cs = wave_max_scan_i(raw, lane);
+    const int nxt = __shfl(p.cs, min(lane + 1, kWave - 1), kWave);
+    const int cnt = lane < n_seq ? (nxt - p.cs + kChunk - 1) / kChunk : 0;
+    p.co = wave_sum_scan_i(cnt, lane) - cnt;  // exclusive: chunk_off[lane]
+    p.n_chunks = __shfl(p.co, n_seq, kWave);
+  } else {
+    p.n_chunks = tabs.chunk_off[n_seq];
   }
-  if (c >= tabs.chunk_off[n_seq]) return false;
-  loc.n = find_sequence(tabs.chunk_off, n_seq, c);
-  loc.ts = tabs.cu[loc.n];
-  loc.t0 = loc.ts + (c - tabs.chunk_off[loc.n]) * kChunk;
-  loc.len = min(kChunk, tabs.cu[loc.n + 1] - loc.t0);
-  return true;
+  return p;
+}
+
+// Tables for the scan, in the modes where no plan kernel ran (every thread of the grid
+// takes a share; entries n = 0..n_seq).
+__device__ __forceinline__ void write_tables(const Planner &p) {
+  const int tid = threadIdx.x;
+  if (p.mode == kPlanDense) {
+    for (int e = blockIdx.x * (int)blockDim.x + tid; e <= p.n_seq;
+         e += gridDim.x * (int)blockDim.x) {
+      p.tabs.cu[e] = e * p.L;
+      p.tabs.chunk_off[e] = e * p.cpc;
+    }
+  } else if (p.mode == kPlanWave) {
+    if (blockIdx.x == 0 && tid <= p.n_seq) {  // wavefront 0 (n_seq < 64)
+      p.tabs.cu[tid] = p.cs;
+      p.tabs.chunk_off[tid] = p.co;
+    }
+  }
+}
+
+// Chunk c < n_chunks.
+__device__ __forceinline__ ChunkLoc locate(const Planner &p, int c) {
+  ChunkLoc loc;
+  if (p.mode == kPlanDense) {
+    loc.n = c / p.cpc;
+    loc.ts = loc.n * p.L;
+    loc.t0 = loc.ts + (c - loc.n * p.cpc) * kChunk;
+    loc.len = min(kChunk, loc.ts + p.L - loc.t0);
+  } else if (p.mode == kPlanWave) {
+    const int lane = threadIdx.x & 63;
+    const unsigned long long below = __ballot(lane < p.n_seq && p.co <= c);
+    loc.n = __popcll(below) - 1;
+    loc.ts = __shfl(p.cs, loc.n, kWave);
+    loc.t0 = loc.ts + (c - __shfl(p.co, loc.n, kWave)) * kChunk;
+    loc.len = min(kChunk, __shfl(p.cs, loc.n + 1, kWave) - loc.t0);
+  } else {
+    loc.n = find_sequence(p.tabs.chunk_off, p.n_seq, c);
+    loc.ts = p.tabs.cu[loc.n];
+    loc.t0 = loc.ts + (c - p.tabs.chunk_off[loc.n]) * kChunk;
+    loc.len = min(kChunk, p.tabs.cu[loc.n + 1] - loc.t0);
+  }
+  return loc;
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prep / UT kernel: one workgroup (4 wavefronts) per (chunk, head); wavefront w owns the
-// 16 chunk rows 16 w .. 16 w + 15.
+// Prep / UT kernel: one wavefront per (chunk, head), no workgroup barriers.
 //
-// Every wavefront loads its own key (and query) rows straight into MFMA fragments, takes
-// their norms from those registers, and scans the chunk's 64 log-decays itself; the key
-// rows are shared with the other wavefronts through one swizzled LDS tile for the Gram
-// and Q K^T tiles.  (I + L)^{-1} is formed blockwise on 16 x 16 blocks (X = (I + L)^{-1}
-// is unit lower triangular): every wavefront inverts its diagonal block by substitution,
-// then the sub-diagonal blocks follow level by level,
-//   X_ij = -X_ii (sum_{k=j}^{i-1} L_ik X_kj),  i > j,
-// with the 16 x 16 x 16 products on the fp32 matrix cores; X reuses the key tile's LDS
-// once the Gram stage is done.  T = X Diag(b).
+// The wavefront holds the chunk's 64 key rows (and query rows) in registers as MFMA
+// fragments, four 16-row blocks.  A row-major key block is both the A fragment of its rows
+// and the B fragment of K^T, so every Gram tile and every Q K^T tile is a product of two
+// register fragments; taking them as K_j K_i^T (the transpose of the wanted tile) leaves
+// lane (r16, kg) with row 16 i + r16, columns 16 j + 4 kg + e -- four consecutive entries
+// of one row, which is both the A-operand layout of the fp32 MFMA and a row-contiguous
+// store.  With L = Diag(b) (A^- o K K^T) and X = (I + L)^{-1} (unit lower triangular):
+//  - the diagonal blocks X_kk by substitution out of LDS (lane group kg inverts block kg,
+//    one column per lane);
+//  - the sub-diagonal blocks by distance, X_ij = -X_ii Y with Y = sum_{k=j}^{i-1} L_ik X_kj,
+//    on the fp32 matrix cores with the L blocks straight from registers, and formed
+//    transposed (X_ij^T = Y^T X_ii^T) so that each lane ends with row entries of X_ij;
+//  - T = X Diag(b) stored from those registers.
 // When q is given the kernel also writes P = (A o Q K^T) (Eq. (8)'s intra-chunk matrix,
 // A_ij = exp(G_i - G_j) for j <= i, zero above the diagonal) for the scan.
 // ---------------------------------------------------------------------------------------------
-constexpr int kLDL = kChunk + 4;  // padded row length of the fp32 L and X tiles
 
-template <typename Tin, int DK>
+// Element (r, c) of a 16 x 16 fp32 block in LDS: rows of 64 bytes, the 16-byte units of
+// rows 8..15 XOR-swizzled by 2 so that a half-wavefront reading (row r16, unit kg) hits 32
+// distinct 16-byte positions.
+__device__ __forceinline__ int bidx(int r, int c) {
+  return r * 16 + ((((c >> 2) ^ (((r >> 3) & 1) << 1))) << 2) + (c & 3);
+}
+// LDS slot of the X block (i, j) that later products read: the diagonal blocks and the
+// sub-diagonal blocks of rows 1 and 2.
+__host__ __device__ constexpr int xslot(int i, int j) {
+  return i == j ? i : (i == 1 ? 4 : (j == 0 ? 5 : 6));
+}
+
+template <int STAGE_BYTES>
 struct PrepSmem {
-  static constexpr int KBYTES = kChunk * DK * (int)sizeof(Tin);
-  static constexpr int XBYTES = kChunk * kLDL * (int)sizeof(float);
-  // key tile (swizzled 16-byte units) until the Gram stage ends, then X
-  alignas(16) unsigned char KX[KBYTES > XBYTES ? KBYTES : XBYTES];
-  alignas(16) float XT[kChunk][kLDL];  // X transposed, for 16-byte operand reads
-  alignas(16) float L[kChunk][kLDL];
+  alignas(16) float Ld[4][256];  // diagonal blocks of L, row-major
+  alignas(16) float XT[7][256];  // X blocks transposed: XT(i, j)[c][r] = X[16 i + r][16 j + c]
+  alignas(16) float G2[kChunk];  // G * log2(e)
   alignas(16) float beta[kChunk];
-  alignas(16) float G[kChunk];
-  __device__ float (*X())[kLDL] { return reinterpret_cast<float (*)[kLDL]>(KX); }
+  alignas(16) unsigned char stage[STAGE_BYTES];  // P, then T, on their way out
 };
 
-// Byte offset of the 8-element fragment (row r, k-step ks, lane group kg) in the key tile:
-// 16-byte unit 4 ks + kg (two units for fp32) XOR-swizzled by row so that 16 consecutive
-// rows at one unit fall into distinct LDS bank groups.
-template <typename Tin, int DK>
-__device__ __forceinline__ int kfrag_off(int r, int ks, int kg) {
-  constexpr int ES = sizeof(Tin), UPF = ES / 2;
-  const int f = (DK >= 128 ? ((r >> 1) & 7) : ((r >> 2) & 3)) << 1;
-  return r * DK * ES + ((((4 * ks + kg) * UPF) ^ (f * UPF)) << 4);
+// 64 x 64 output tile of element type T staged in LDS: rows of 64 sizeof(T) bytes, 16-byte
+// units XOR-swizzled by row / 2 so that the fragment writes (16 rows x 4 lane groups) and
+// the whole-row reads are both free of bank conflicts.
+template <typename T>
+__device__ __forceinline__ int stage_off(int row, int col) {
+  constexpr int RB = kChunk * (int)sizeof(T);
+  const int byte = col * (int)sizeof(T);
+  const int sw = sizeof(T) == 2 ? ((row >> 1) & 7) : (((row >> 1) & 7) << 1);
+  return row * RB + ((((byte >> 4) ^ sw)) << 4) + (byte & 15);
+}
+// Entries (row, col .. col + 3), col a multiple of 4.
+template <typename T>
+__device__ __forceinline__ void stage_put(unsigned char *st, int row, int col, float a, float b,
+                                          float c, float d) {
+  T *p = reinterpret_cast<T *>(st + stage_off<T>(row, col));
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 x4;
+    x4[0] = from_f32<T>(a); x4[1] = from_f32<T>(b); x4[2] = from_f32<T>(c); x4[3] = from_f32<T>(d);
+    *reinterpret_cast<bf16x4 *>(p) = x4;
+  } else {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{a, b, c, d};
+  }
+}
+// The staged tile to dst (row-major, 64 x 64): every store instruction writes whole rows.
+template <typename T>
+__device__ __forceinline__ void stage_flush(const unsigned char *st, T *dst, int lane) {
+  constexpr int UPR = kChunk * (int)sizeof(T) / 16;  // 16-byte units per row: 8 or 16
+  constexpr int RPI = kWave / UPR;                   // rows per instruction
+#pragma unroll
+  for (int m = 0; m < kChunk / RPI; ++m) {
+    const int row = RPI * m + lane / UPR, u = lane % UPR;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(st + stage_off<T>(row, u * 16 / (int)sizeof(T)));
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(dst) + row * UPR * 16 + u * 16) = v;
+  }
 }
 
-// D += A B for 16 x 16 fp32 blocks in LDS, A row-major (stride lda) and B given as its
-// transpose Bt (stride ldbt): with the contraction index k = 4 kg + s in MFMA s, both
-// operands are one 16-byte read per lane.
-__device__ __forceinline__ f32x4 mm16t(const float *A, int lda, const float *Bt, int ldbt,
-                                       f32x4 acc, int r16, int kg) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r16 * lda + 4 * kg);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(Bt + r16 * ldbt + 4 * kg);
+// bf16 key or query rows of one chunk as MFMA fragments f[b][ks] (rows 16 b + r16, k-step
+// ks), loaded as whole 128-byte lines: for each block and line c, one load covers rows
+// 16 b + 0..7 and one rows 16 b + 8..15, lane (r16, kg) taking row r16 % 8 and 16-byte
+// unit kg + 4 (r16 / 8) of the line.  Exchanging lanes 8..15 of every 16-lane row between
+// the two loads (a row_ror:8 DPP move) leaves the fragments of k-steps 2 c and 2 c + 1.
+template <int NKS>
+__device__ __forceinline__ void load_rows_bf16(bf16x8 (&f)[4][NKS], Rsrc r, int rowb, int r16,
+                                               int kg) {
+  const int vrow = (r16 & 7) * rowb + 16 * (kg + 4 * (r16 >> 3));
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
-  return acc;
-}
-// D += A Y with Y a 16 x 16 block held in accumulator layout (lane (r16, kg) holds rows
-// 4 kg + e of column r16): the contraction index is taken in the order the lanes hold it.
-__device__ __forceinline__ f32x4 mm16_acc(const float *A, int lda, const f32x4 &Y, f32x4 acc,
-                                          int r16, int kg) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r16 * lda + 4 * kg);
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], Y[s], acc, 0, 0, 0);
-  return acc;
+    for (int c = 0; c < NKS / 2; ++c) {
+      const u32x4 X = __builtin_amdgcn_raw_buffer_load_b128(r, vrow + 16 * b * rowb + 128 * c, 0, 0);
+      const u32x4 Y =
+          __builtin_amdgcn_raw_buffer_load_b128(r, vrow + (16 * b + 8) * rowb + 128 * c, 0, 0);
+      u32x4 F0, F1;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        F0[d] = (unsigned)__builtin_amdgcn_update_dpp((int)X[d], (int)Y[d], 0x128, 0xF, 0xC, false);
+        F1[d] = (unsigned)__builtin_amdgcn_update_dpp((int)Y[d], (int)X[d], 0x128, 0xF, 0x3, false);
+      }
+      f[b][2 * c] = __builtin_bit_cast(bf16x8, F0);
+      f[b][2 * c + 1] = __builtin_bit_cast(bf16x8, F1);
+    }
 }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename Tin, int DK, typename TOut>
-__global__ __launch_bounds__(256) void kla_prep_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) * DK > 256 ? 1 : 2))) void kla_prep_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ eta, float eps, int32_t *__restrict__ cu,
     int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
     float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out,
     float *__restrict__ GD_out, CoefOpts opts, PlanArgs pa) {
-  __shared__ PrepSmem<Tin, DK> sm;
-  const int c = blockIdx.x, h = blockIdx.y;
-  ChunkLoc loc;
-  const bool write_tables = pa.mode == kPlanDense ? h == 0 : (c == 0 && h == 0);
-  if (!locate_chunk(pa, SeqTables{cu, chunk_off},
-                    n_seq, c, write_tables, loc))
-    return;
-  const int n = loc.n, t0 = loc.t0, len = loc.len;
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  const int r16 = lane & 15, kg = lane >> 4;
-  const int i0 = 16 * wid;  // this wavefront's rows
+  constexpr int kStage = kChunk * kChunk * (int)(sizeof(Tin) > sizeof(TOut) ? sizeof(Tin) : sizeof(TOut));
+  __shared__ PrepSmem<kStage> sm;
+  const Planner pl = make_planner(pa, SeqTables{cu, chunk_off}, n_seq);
+  write_tables(pl);
+  const int task = blockIdx.x;  // chunk * H + head
+  if (task >= pl.n_chunks * H) return;
+  const int c = __builtin_amdgcn_readfirstlane(task / H);
+  const int h = __builtin_amdgcn_readfirstlane(task - c * H);
+  ChunkLoc loc = locate(pl, c);
+  // wave-uniform by construction; said so, so that buffer descriptors stay in SGPRs
+  loc.n = __builtin_amdgcn_readfirstlane(loc.n);
+  loc.ts = __builtin_amdgcn_readfirstlane(loc.ts);
+  loc.t0 = __builtin_amdgcn_readfirstlane(loc.t0);
+  loc.len = __builtin_amdgcn_readfirstlane(loc.len);
+  const int t0 = loc.t0, len = loc.len;
+  const int lane = threadIdx.x, r16 = lane & 15, kg = lane >> 4;
   const bool want_p = (q != nullptr) && (P_out != nullptr);
   constexpr int NKS = DK / 32;
+  constexpr float kLog2e = 1.4426950408889634f;
   using FragT = typename Frag<Tin>::type;
 
-  // ---- loads: own key rows and the query rows of block 3 - w as fragments (zero past the
-  //      chunk end), and the chunk's g and eta one token per lane.  Wavefront w forms the
-  //      Gram tiles of row block w (w + 1 tiles) and the Q K^T tiles of row block 3 - w
-  //      (4 - w tiles), five tiles each.
-  const int my_row = i0 + r16;
-  const bool row_ok = my_row < len;
-  const int p0 = 16 * (3 - wid), p_row = p0 + r16;
-  const bool prow_ok = p_row < len;
-  FragT kf[NKS], qf[NKS];
+  // ---- loads through range-checked buffers (rows past the chunk end read as zeros): key
+  //      (and query) rows 16 b + r16 as fragments, g and eta one token per lane
+  constexpr int ES = sizeof(Tin);
+  const int rowb = H * DK * ES;  // bytes between consecutive tokens
+  const size_t off0 = ((size_t)t0 * H + h) * DK;
+  const uint32_t kq_bytes = (uint32_t)((len - 1) * rowb + DK * ES);
+  FragT kf[4][NKS], qf[4][NKS];
   {
-    const size_t rbase = ((size_t)(t0 + (row_ok ? my_row : 0)) * H + h) * DK + 8 * kg;
-    const size_t qbase = ((size_t)(t0 + (prow_ok ? p_row : 0)) * H + h) * DK + 8 * kg;
+    const Rsrc rk = make_rsrc(k + off0, kq_bytes);
+    if constexpr (ES == 2) {
+      load_rows_bf16<NKS>(kf, rk, rowb, r16, kg);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = row_ok ? load8<Tin>(k + rbase + 32 * ks) : zero8<Tin>();
-      qf[ks] = (want_p && prow_ok) ? load8<Tin>(q + qbase + 32 * ks) : zero8<Tin>();
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          kf[b][ks] = bload8<Tin>(rk, (16 * b + r16) * rowb + (32 * ks + 8 * kg) * ES);
+    }
+    if (want_p) {
+      const Rsrc rq = make_rsrc(q + off0, kq_bytes);
+      if constexpr (ES == 2) {
+        load_rows_bf16<NKS>(qf, rq, rowb, r16, kg);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            qf[b][ks] = bload8<Tin>(rq, (16 * b + r16) * rowb + (32 * ks + 8 * kg) * ES);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[b][ks] = zero8<Tin>();
     }
   }
   const bool tok_ok = lane < len;
   const size_t th = (size_t)(t0 + (tok_ok ? lane : 0)) * H + h;
-  const float g_l = tok_ok ? g[th] : 0.f;
-  const float eta_l = tok_ok ? eta[th] : 0.f;
+  const uint32_t ge_bytes = (uint32_t)(((len - 1) * H + 1) * 4);
+  const float g_l = bload1(make_rsrc(g + (size_t)t0 * H + h, ge_bytes), lane * H * 4);
+  const float eta_l = bload1(make_rsrc(eta + (size_t)t0 * H + h, ge_bytes), lane * H * 4);
 
-  // ---- b for the own rows, G for token `lane` (every wavefront scans all 64)
-  float ss = 0.f;
+  // ---- G (token `lane`; rows past the end carry G_last)
+  const float G_l = wave_inclusive_scan(g_l, lane);
+  const size_t gd0 = (size_t)task * kGDFloats;
+  if (GD_out) {
+    const float Glast = __shfl(G_l, kChunk - 1, kWave);
+    GD_out[gd0 + lane] = __expf(G_l);
+    GD_out[gd0 + kChunk + lane] = __expf(Glast - G_l);
+  }
+  if (tok_ok && G_out) G_out[th] = G_l;
+  sm.G2[lane] = G_l * kLog2e;
+
+  // ---- diagonal Gram tiles K_i K_i^T; their diagonals are the squared key norms (and, under
+  //      the normalised readout, Q_i Q_i^T gives the squared query norms).  Row 16 i + r16's
+  //      diagonal element sits in lane (r16, r16 / 4), entry r16 % 4.
+  f32x4 gd[4];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
+  for (int i = 0; i < 4; ++i) {
+    gd[i] = zero4();
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const float x = to_f32(kf[ks][s]);
-      ss = fmaf(x, x, ss);
+    for (int ks = 0; ks < NKS; ++ks) gd[i] = mma(kf[i][ks], kf[i][ks], gd[i]);
+  }
+  const int dsrc = r16 + 16 * (r16 >> 2);  // the lane holding row r16's diagonal element
+  const bool diag_lane = lane == dsrc;
+  const int de = r16 & 3;
+  const int pos0 = t0 - loc.ts + 1 + (opts.pos_offset ? opts.pos_offset[loc.n] : 0);
+  float rqv[4], bme[4], G2me[4];  // per own row 16 i + r16: 1/||q||, b, G log2(e)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * i + r16;
+    const float ss = de == 0 ? gd[i][0] : de == 1 ? gd[i][1] : de == 2 ? gd[i][2] : gd[i][3];
+    const float eta_r = __shfl(eta_l, row, kWave);
+    const float G_r = __shfl(G_l, row, kWave);
+    float b_r = row < len ? write_coef(opts.beta_mode, eta_r, ss + eps, (float)(pos0 + row)) : 0.f;
+    b_r = __shfl(b_r, dsrc, kWave);  // the diagonal lane's value, on all four lane groups
+    bme[i] = b_r;
+    G2me[i] = G_r * kLog2e;
+    rqv[i] = 1.f;
+    if (opts.normalize_q) {  // 1 / ||q|| (0 for a zero query)
+      f32x4 qd = zero4();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qd = mma(qf[i][ks], qf[i][ks], qd);
+      const float qq = __shfl(de == 0 ? qd[0] : de == 1 ? qd[1] : de == 2 ? qd[2] : qd[3], dsrc,
+                              kWave);
+      rqv[i] = qq > 0.f ? __builtin_amdgcn_rsqf(qq) : 0.f;
     }
-  ss += __shfl_xor(ss, 16, kWave);
-  ss += __shfl_xor(ss, 32, kWave);
-  const float eta_r = __shfl(eta_l, my_row, kWave);
-  const float den = ss + eps;
-  const float t_abs =
-      (float)(t0 - loc.ts + my_row + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
-  const float b_r = row_ok ? write_coef(opts.beta_mode, eta_r, den, t_abs) : 0.f;
-  const float G_l = wave_inclusive_scan(g_l, lane);  // rows past the end carry G_last
-  // 1 / ||q|| of query row p_row under the normalised readout (0 for a zero query), else 1
-  float rq = 1.f;
-  if (opts.normalize_q) {
-    float qq = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float x = to_f32(qf[ks][s]);
-        qq = fmaf(x, x, qq);
-      }
-    qq += __shfl_xor(qq, 16, kWave);
-    qq += __shfl_xor(qq, 32, kWave);
-    rq = qq > 0.f ? 1.f / sqrtf(qq) : 0.f;
-  }
-
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    *reinterpret_cast<FragT *>(sm.KX + kfrag_off<Tin, DK>(my_row, ks, kg)) = kf[ks];
-  if (kg == 0) sm.beta[my_row] = b_r;
-  if (wid == 0) {
-    sm.G[lane] = G_l;
-    if (tok_ok && G_out) G_out[th] = G_l;
-    // per-chunk decays for the scan: exp(G_i) and exp(G_last - G_i)
-    if (GD_out) {
-      const float Glast = __shfl(G_l, kChunk - 1, kWave);
-      float *gd = GD_out + ((size_t)c * H + h) * kGDFloats;
-      gd[lane] = __expf(G_l);
-      gd[kChunk + lane] = __expf(Glast - G_l);
-    }
-  }
-  // the output factor exp(G_i) / ||q_i|| for the query rows this wavefront holds
-  {
-    const float G_p = __shfl(G_l, p_row, kWave);
-    if (GD_out && kg == 0)
-      GD_out[((size_t)c * H + h) * kGDFloats + 2 * kChunk + p_row] = __expf(G_p) * rq;
-  }
-  if (beta_out && kg == 0 && row_ok) beta_out[((size_t)(t0 + my_row)) * H + h] = b_r;
-  __syncthreads();
-
-  // ---- Gram K K^T (row block w, column blocks jt <= w) -> strictly lower L
-  {
-    const f32x4 b_rows = *reinterpret_cast<const f32x4 *>(&sm.beta[i0 + 4 * kg]);
-    const f32x4 G_rows = *reinterpret_cast<const f32x4 *>(&sm.G[i0 + 4 * kg]);
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      if (jt > wid) continue;
-      FragT bk[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        bk[ks] = *reinterpret_cast<const FragT *>(sm.KX + kfrag_off<Tin, DK>(16 * jt + r16, ks, kg));
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc = mma(kf[ks], bk[ks], acc);  // rows i0 + 4 kg + e
-      const int col = 16 * jt + r16;
-      const float G_col = sm.G[col];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = i0 + 4 * kg + e;
-        sm.L[row][col] = (col < row) ? b_rows[e] * __expf(G_rows[e] - G_col) * acc[e] : 0.f;
-      }
+    if (kg == 0) {
+      sm.beta[row] = b_r;
+      if (GD_out) GD_out[gd0 + 2 * kChunk + row] = __expf(G_r) * rqv[i];
+      if (beta_out && row < len) beta_out[(size_t)(t0 + row) * H + h] = b_r;
     }
   }
-  // ---- P^T = K Q^T for row block 3 - w, so each lane holds 4 consecutive columns of P row
-  //      p_row; P = A o Q K^T is written row-major (zero above the diagonal)
+  lds_barrier();
+
+  // ---- P = A o Q K^T from the tiles K_j Q_i^T (row 16 i + r16, columns 16 j + 4 kg + e;
+  //      zero above the diagonal)
   if (want_p) {
-    Tin *Pc = P_out + ((size_t)c * H + h) * (kChunk * kChunk) + (size_t)p_row * kChunk;
-    const float G_me = sm.G[p_row];
-    const int pb = 3 - wid;
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      const int j0 = 16 * jt + 4 * kg;
-      float pv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (jt <= pb) {
+    for (int i = 0; i < 4; ++i) {
+      const int prow = 16 * i + r16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int j0 = 16 * j + 4 * kg;
+        if (j > i) {
+          stage_put<Tin>(sm.stage, prow, j0, 0.f, 0.f, 0.f, 0.f);
+          continue;
+        }
         f32x4 accp = zero4();
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const FragT bk =
-              *reinterpret_cast<const FragT *>(sm.KX + kfrag_off<Tin, DK>(16 * jt + r16, ks, kg));
-          accp = mma(bk, qf[ks], accp);  // (Q K^T)[p_row][j0 + e]
+        for (int ks = 0; ks < NKS; ++ks) accp = mma(kf[j][ks], qf[i][ks], accp);
+        const f32x4 Gc = *reinterpret_cast<const f32x4 *>(&sm.G2[j0]);
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool keep = (j < i) || (4 * kg + e <= r16);
+          pv[e] = exp2_fast(keep ? G2me[i] - Gc[e] : -INFINITY) * accp[e] * rqv[i];
         }
-        const f32x4 G_cols = *reinterpret_cast<const f32x4 *>(&sm.G[j0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pv[e] = (j0 + e <= p_row) ? __expf(G_me - G_cols[e]) * accp[e] * rq : 0.f;
-      }
-      if constexpr (sizeof(Tin) == 2) {
-        bf16x4 x4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x4[e] = from_f32<Tin>(pv[e]);
-        *reinterpret_cast<bf16x4 *>(Pc + j0) = x4;
-      } else {
-        *reinterpret_cast<f32x4 *>(Pc + j0) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+        stage_put<Tin>(sm.stage, prow, j0, pv[0], pv[1], pv[2], pv[3]);
       }
     }
+    lds_barrier();
+    stage_flush<Tin>(sm.stage, P_out + (size_t)task * (kChunk * kChunk), lane);
   }
 
-  // ---- diagonal block: invert I + L_ww by substitution, lane = column r16 (the four lane
-  //      groups compute the same column); L rows are read four values at a time
-  float x[16];
+  // ---- L: diagonal blocks to LDS (row-major), sub-diagonal blocks kept in registers in the
+  //      A-operand layout (row r16, columns 4 kg + e)
+  f32x4 Lr[4][3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j <= i; ++j) {
+      const int j0 = 16 * j + 4 * kg;
+      f32x4 acc = gd[i];
+      if (j < i) {
+        acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = mma(kf[j][ks], kf[i][ks], acc);
+      }
+      const f32x4 Gc = *reinterpret_cast<const f32x4 *>(&sm.G2[j0]);
+      f32x4 lv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool below = (j < i) || (4 * kg + e < r16);  // column < row
+        lv[e] = bme[i] * exp2_fast(below ? G2me[i] - Gc[e] : -INFINITY) * acc[e];
+      }
+      if (j < i) Lr[i][j] = lv;
+      else *reinterpret_cast<f32x4 *>(&sm.Ld[i][bidx(r16, 4 * kg)]) = lv;
+    }
+  }
+  lds_barrier();
+
+  // ---- diagonal blocks: lane group kg inverts I + L_kk by substitution, lane = column r16;
+  //      rows of L_kk are read four values at a time (one address per lane group)
   {
+    const float *Ld = sm.Ld[kg];
+    float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float lr[16];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&sm.L[i0 + i][i0 + 4 * q4]);
-        lr[4 * q4] = v4[0]; lr[4 * q4 + 1] = v4[1]; lr[4 * q4 + 2] = v4[2]; lr[4 * q4 + 3] = v4[3];
+      for (int u = 0; u < 4; ++u) {
+        if (4 * u < i) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4 *>(Ld + bidx(i, 4 * u));
+          lr[4 * u] = v4[0]; lr[4 * u + 1] = v4[1]; lr[4 * u + 2] = v4[2]; lr[4 * u + 3] = v4[3];
+        }
       }
       float a0 = (i == r16) ? 1.f : 0.f, a1 = 0.f;
 #pragma unroll
@@ -408,68 +502,65 @@ __global__ __launch_bounds__(256) void kla_prep_kernel(
       }
       x[i] = a0 + a1;
     }
-  }
-  __syncthreads();  // every key-tile read and every L row is done; X takes the key tile
-  float(*X)[kLDL] = sm.X();
-  if (kg == 0) {
+    // XT(k, k)[r16][i] = X[16 k + i][16 k + r16]
+    float *XTd = sm.XT[xslot(kg, kg)];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) X[i0 + i][i0 + r16] = x[i];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<f32x4 *>(&sm.XT[i0 + r16][i0 + 4 * q4]) =
-          f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<f32x4 *>(XTd + bidx(r16, 4 * u)) =
+          f32x4{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- sub-diagonal blocks, one level (distance) at a time
+  // ---- T = X Diag(b): lane (r16, kg) writes columns 16 j + 4 kg + e of row 16 i + r16.
+  //      Diagonal blocks from LDS, blocks above the diagonal zero, the rest as they form.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int trow = 16 * i + r16;
+    const float *XTi = sm.XT[xslot(i, i)];
+    const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * i + 4 * kg]);
+    float xv[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xv[s] = XTi[bidx(4 * kg + s, r16)];  // X_ii[r16][4 kg + s]
+    stage_put<TOut>(sm.stage, trow, 16 * i + 4 * kg, xv[0] * bv[0], xv[1] * bv[1], xv[2] * bv[2],
+                    xv[3] * bv[3]);
+#pragma unroll
+    for (int j = i + 1; j < 4; ++j) stage_put<TOut>(sm.stage, trow, 16 * j + 4 * kg, 0.f, 0.f, 0.f, 0.f);
+  }
+
+  // ---- sub-diagonal blocks, by distance; the blocks of one distance are independent
 #pragma unroll
   for (int dist = 1; dist < 4; ++dist) {
-    const int jb = wid, ib = wid + dist;  // block (ib, jb)
-    if (ib < 4) {
+#pragma unroll
+    for (int i = dist; i < 4; ++i) {
+      const int j = i - dist;
+      // Y = sum_k L_ik X_kj: A = L_ik (registers), B = X_kj[4 kg + s][r16] from XT(k, j)
       f32x4 Y = zero4();
-      for (int kb = jb; kb < ib; ++kb)
-        Y = mm16t(&sm.L[16 * ib][16 * kb], kLDL, &sm.XT[16 * jb][16 * kb], kLDL, Y, r16, kg);
-      f32x4 Z = mm16_acc(&X[16 * ib][16 * ib], kLDL, Y, zero4(), r16, kg);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X[16 * ib + 4 * kg + e][16 * jb + r16] = -Z[e];
-      *reinterpret_cast<f32x4 *>(&sm.XT[16 * jb + r16][16 * ib + 4 * kg]) =
-          f32x4{-Z[0], -Z[1], -Z[2], -Z[3]};
-    }
-    __syncthreads();
-  }
-
-  // ---- T = X Diag(b), zero above the diagonal: thread tid writes 16 consecutive entries of
-  //      row tid / 4 (blocks above the diagonal of X were never written)
-  {
-    TOut *Tc = T_out + ((size_t)c * H + h) * (kChunk * kChunk);
-    const int row = tid >> 2, j0 = 16 * (tid & 3);
-    float tv[16];
+      for (int kb = j; kb < i; ++kb) {
+        const f32x4 bx = *reinterpret_cast<const f32x4 *>(&sm.XT[xslot(kb, j)][bidx(r16, 4 * kg)]);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 xv = *reinterpret_cast<const f32x4 *>(&X[row][j0 + 4 * q4]);
-      const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[j0 + 4 * q4]);
+        for (int s = 0; s < 4; ++s)
+          Y = __builtin_amdgcn_mfma_f32_16x16x4f32(Lr[i][kb][s], bx[s], Y, 0, 0, 0);
+      }
+      // X_ij^T = -(Y^T X_ii^T): A = Y^T (Y's accumulator layout), B = X_ii[r16][4 kg + s]
+      const float *XTi = sm.XT[xslot(i, i)];
+      f32x4 Zt = zero4();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 4 * q4 + e;
-        tv[4 * q4 + e] = (j <= row) ? xv[e] * bv[e] : 0.f;
+      for (int s = 0; s < 4; ++s)
+        Zt = __builtin_amdgcn_mfma_f32_16x16x4f32(Y[s], XTi[bidx(4 * kg + s, r16)], Zt, 0, 0, 0);
+      // lane (r16, kg) now holds X_ij[r16][4 kg + e] = -Zt[e]
+      const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * j + 4 * kg]);
+      stage_put<TOut>(sm.stage, 16 * i + r16, 16 * j + 4 * kg, -Zt[0] * bv[0], -Zt[1] * bv[1],
+                      -Zt[2] * bv[2], -Zt[3] * bv[3]);
+      if (i < 3) {  // read again by the next distances
+        float *XTo = sm.XT[xslot(i, j)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) XTo[bidx(4 * kg + e, r16)] = -Zt[e];
       }
     }
-    TOut *dst = Tc + (size_t)row * kChunk + j0;
-    if constexpr (sizeof(TOut) == 2) {
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        bf16x8 o8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] = from_f32<TOut>(tv[8 * h8 + e]);
-        *reinterpret_cast<bf16x8 *>(dst + 8 * h8) = o8;
-      }
-    } else {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<f32x4 *>(dst + 4 * q4) =
-            f32x4{tv[4 * q4], tv[4 * q4 + 1], tv[4 * q4 + 2], tv[4 * q4 + 3]};
-    }
+    lds_barrier();
   }
+  stage_flush<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane);
 }
 
 template <typename Tin, int DK>
@@ -478,16 +569,18 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
                                 int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out,
                                 void *T_out, bool t_fp32, void *P_out, float *GD_out,
                                 const PlanArgs &pa, hipStream_t stream) {
-  if (n_chunks_ub <= 0) return hipSuccess;
-  const dim3 grid((unsigned)n_chunks_ub, H);
+  if (n_chunks_ub <= 0 || H <= 0) return hipSuccess;
+  const int64_t tasks = n_chunks_ub * H;
+  if (tasks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tasks);
   const Tin *qq = static_cast<const Tin *>(q);
   Tin *pp = static_cast<Tin *>(P_out);
   if (t_fp32 || sizeof(Tin) == 4)
-    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(256), 0, stream, qq,
+    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(64), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
                        G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts, pa);
   else
-    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(256), 0, stream, qq,
+    hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(64), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
                        G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out, opts, pa);
   return hipGetLastError();

@@ -45,16 +45,7 @@ constexpr int kBV = 32;            // state columns per workgroup
 constexpr int kScanThreads = 256;  // 2 consumer + 2 producer wavefronts
 constexpr int kLdsBytes = 160 * 1024;
 
-typedef __amdgpu_buffer_rsrc_t Rsrc;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor (stride 0, byte-addressed, range checked against `bytes`).
-__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
 
 // 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.
 __device__ __forceinline__ void dma16(Rsrc r, const void *lds, int voff) {
@@ -66,14 +57,6 @@ __device__ __forceinline__ void store8(u32x2 x, Rsrc r, int voff, int soff) {
 }
 __device__ __forceinline__ void store16(u32x4 x, Rsrc r, int voff, int soff) {
   __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
-}
-
-// LDS-only workgroup barrier: orders LDS traffic without waiting for the global
-// loads that are deliberately left in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Barrier for the producer waves.  They touch LDS only through buffer-to-LDS loads, whose
