@@ -258,13 +258,17 @@ __device__ __forceinline__ void stage_put(unsigned char *st, int row, int col, f
   }
 }
 // The staged tile to dst (row-major, 64 x 64): every store instruction writes whole rows.
+// With skip_upper the block of rows 0..31, columns 32..63 (zero, and never read by the
+// scan, whose operand reads of those rows stop at column 31) is left unwritten.
 template <typename T>
-__device__ __forceinline__ void stage_flush(const unsigned char *st, T *dst, int lane) {
+__device__ __forceinline__ void stage_flush(const unsigned char *st, T *dst, int lane,
+                                            bool skip_upper) {
   constexpr int UPR = kChunk * (int)sizeof(T) / 16;  // 16-byte units per row: 8 or 16
   constexpr int RPI = kWave / UPR;                   // rows per instruction
 #pragma unroll
   for (int m = 0; m < kChunk / RPI; ++m) {
     const int row = RPI * m + lane / UPR, u = lane % UPR;
+    if (skip_upper && row < kChunk / 2 && u >= UPR / 2) continue;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(st + stage_off<T>(row, u * 16 / (int)sizeof(T)));
     *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(dst) + row * UPR * 16 + u * 16) = v;
   }
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
       }
     }
     lds_barrier();
-    stage_flush<Tin>(sm.stage, P_out + (size_t)task * (kChunk * kChunk), lane);
+    stage_flush<Tin>(sm.stage, P_out + (size_t)task * (kChunk * kChunk), lane, true);
   }
 
   // ---- L: diagonal blocks to LDS (row-major), sub-diagonal blocks kept in registers in the
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     }
     lds_barrier();
   }
-  stage_flush<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane);
+  stage_flush<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane, GD_out != nullptr);
 }
 
 template <typename Tin, int DK>
