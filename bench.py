@@ -144,7 +144,8 @@ def main():
     ms_per_step = total_ms / K
     tok_per_s = n_tok / (ms_per_step * 1e-3)
     th = n_tok * H
-    scan_bytes = th * (2 * dk * 2 + dv * 2 + dv * 2 + 2 * CHUNK * 2 + 8) + 2 * n_seq * H * dk * dv * 4
+    # per token-head: q, k, v rows, o row, one row each of T and P, three decay factors
+    scan_bytes = th * (2 * dk * 2 + dv * 2 + dv * 2 + 2 * CHUNK * 2 + 12) + 2 * n_seq * H * dk * dv * 4
     scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     flops_prefill = th * (6 * dk * dv + (CHUNK - 1) * dk + (CHUNK + 1) * (2 * dk + 2 * dv))
     mfma_frac = flops_prefill / (ms_per_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
