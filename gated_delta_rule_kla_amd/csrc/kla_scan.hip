@@ -9,10 +9,12 @@
 //   S_out = exp(G_last) S + K^T Diag(dec) U              Eq. (9)
 // and S_out is the next chunk's S.  The chunks of one sequence are processed in order
 // by one workgroup; the d_v columns of S are independent given K, T, P and the decays,
-// so a (sequence, head) is split over d_v / 32 workgroups.
+// so a (sequence, head) is split over d_v / 64 workgroups.  Each workgroup stages K, Q, T
+// and P once for its 64 columns: the staging traffic from L2 into LDS, summed over the
+// chip, is what limits the scan when more workgroups share it.
 //
-// Workgroup = 4 wavefronts with two roles:
-//   consumers (waves 0, 1) each own 16 state columns and keep them in registers for the
+// Workgroup = 8 wavefronts with two roles:
+//   consumers (waves 0-3) each own 16 state columns and keep them in registers for the
 //     whole sequence.  Every product is a 16 x 16 x 32 MFMA whose register operand is an
 //     accumulator of the previous product: a D fragment holds rows 4 kg .. 4 kg + 3 of a
 //     16-row tile, so two tiles together hold 8 contraction indices per lane, and the
@@ -22,11 +24,11 @@
 //     The LDS operand of every product is then one 16-byte row piece of K, Q, T or P
 //     (or, for K^T, two gfx950 LDS transpose reads).  The output is formed transposed
 //     (O^T = S^T Q^T + U^T P^T, the same registers in the other operand slot), so each
-//     lane ends with 4 consecutive output columns of one token and stores them directly.
-//   producers (waves 2, 3) stream the tiles of later chunks into a ring of LDS slots
-//     with buffer loads that write LDS directly (no register staging).  Each chunk's
-//     buffer descriptors end at the sequence's last token, so rows past a ragged end
-//     read as zero, and output stores past it are dropped.
+//     lane ends with 4 consecutive output columns of one token.
+//   producers (waves 4-7) stream the tiles of later chunks into a ring of LDS slots
+//     with buffer loads that write LDS directly (no register staging), and write the
+//     outputs back.  Each chunk's buffer descriptors end at the sequence's last token, so
+//     rows past a ragged end read as zero, and output stores past it are dropped.
 // One workgroup barrier per chunk hands a slot from producers to consumers.
 //
 // LDS tiles are stored in 16-byte units, unit u of row r at u ^ sw(r) (twice sw for fp32
@@ -41,8 +43,16 @@
 
 namespace kla {
 
-constexpr int kBV = 32;            // state columns per workgroup
-constexpr int kScanThreads = 256;  // 2 consumer + 2 producer wavefronts
+// Workgroup shape: NC consumer wavefronts (16 state columns each) and NP producers.
+template <int NC_, int NP_>
+struct ScanShape {
+  static constexpr int NC = NC_;
+  static constexpr int NP = NP_;
+  static constexpr int BV = 16 * NC;              // state columns per workgroup
+  static constexpr int THREADS = 64 * (NC + NP);  // consumers first
+};
+using ScanNarrow = ScanShape<2, 2>;  // 32 columns: the grid fills the chip
+using ScanWide = ScanShape<4, 4>;    // 64 columns: K, Q, T, P staged once for twice the columns
 constexpr int kLdsBytes = 160 * 1024;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -93,6 +103,36 @@ __device__ __forceinline__ int tile_off(int r, int e) {
   return r * ROWB + (u << 4) + (byte & 15);
 }
 
+// The T and P tiles in LDS without their never-read block (rows 0-31, columns 32-63, zero):
+// region A holds rows 0-31, columns 0-31, in tile order (row slot 4 a + i of tile t at LDS
+// row 16 t + 4 a + i, t = 0, 1), so that the 16 rows of one tile are consecutive; region B
+// holds rows 32-63, all 64 columns, in token order.  Byte offset of element e of row r:
+template <typename T>
+__device__ __forceinline__ int tpc_off(int r, int e) {
+  constexpr int ES = sizeof(T);
+  const int byte = e * ES;
+  if (r < 32) {
+    const int rho = 16 * ((r >> 2) & 1) + 4 * ((r >> 3) & 3) + (r & 3);
+    const int u = (byte >> 4) ^ ((((rho >> 3) & 1) << 1) * (ES / 2));
+    return rho * 32 * ES + (u << 4) + (byte & 15);
+  }
+  const int u = (byte >> 4) ^ (sw_rows<kChunk>(r) * (ES / 2));
+  return 32 * 32 * ES + (r - 32) * kChunk * ES + (u << 4) + (byte & 15);
+}
+// Byte offset, in a row-major 64 x 64 tile in memory, of the 16 bytes that belong at byte pb
+// of the compact LDS tile.
+template <typename T>
+__device__ __forceinline__ int tpc_src(int pb) {
+  constexpr int ES = sizeof(T), RA = 32 * ES, RB = kChunk * ES;
+  if (pb < 32 * RA) {
+    const int rho = pb / RA, pu = (pb % RA) >> 4;
+    const int row = 8 * ((rho >> 2) & 3) + 4 * (rho >> 4) + (rho & 3);
+    return row * RB + ((pu ^ ((((rho >> 3) & 1) << 1) * (ES / 2))) << 4);
+  }
+  const int qb = pb - 32 * RA, row = 32 + qb / RB;
+  return row * RB + ((((qb % RB) >> 4) ^ (sw_rows<kChunk>(row) * (ES / 2))) << 4);
+}
+
 // LDS transpose read of 4 x 16-bit values (gfx950 ds_read_b64_tr_b16).  Within each group
 // of 16 lanes, destination lane d receives element (d & 3) of the 8-byte chunks addressed
 // by source lanes (d >> 2) + 4 i, i = 0..3.
@@ -109,57 +149,59 @@ __device__ __forceinline__ int tmap(int t, int a, int i) {
 }
 
 // ---- LDS layout
-template <typename Tin, int DK>
+template <typename Tin, int DK, int BV>
 struct ScanSlot {
   alignas(16) unsigned char K[kChunk * DK * sizeof(Tin)];
   alignas(16) unsigned char Q[kChunk * DK * sizeof(Tin)];
-  alignas(16) unsigned char T[kChunk * kChunk * sizeof(Tin)];
-  alignas(16) unsigned char P[kChunk * kChunk * sizeof(Tin)];
-  alignas(16) unsigned char V[kChunk * kBV * sizeof(Tin)];
+  alignas(16) unsigned char T[(32 * 32 + 32 * kChunk) * sizeof(Tin)];  // compact (tpc_off)
+  alignas(16) unsigned char P[(32 * 32 + 32 * kChunk) * sizeof(Tin)];
+  alignas(16) unsigned char V[kChunk * BV * sizeof(Tin)];
   alignas(16) float gam[kChunk];   // exp(G_i)
   alignas(16) float dec[kChunk];   // exp(G_last - G_i)
   alignas(16) float gamO[kChunk];  // output factor: exp(G_i), over ||q_i|| when normalised
 };
 
-template <typename Tin, int DK>
+template <typename Tin, int DK, int BV>
 constexpr int scan_nslot() {
-  constexpr int n = kLdsBytes / (int)sizeof(ScanSlot<Tin, DK>);
+  constexpr int n = kLdsBytes / (int)sizeof(ScanSlot<Tin, DK, BV>);
   return n >= 3 ? 3 : n;
 }
 
-template <typename Tin, int DK>
+template <typename Tin, int DK, int BV>
 struct ScanSmem {
-  static constexpr int NSLOT = scan_nslot<Tin, DK>();
-  ScanSlot<Tin, DK> slot[NSLOT];
+  static constexpr int NSLOT = scan_nslot<Tin, DK, BV>();
+  ScanSlot<Tin, DK, BV> slot[NSLOT];
 };
 
 // Buffer-load-to-LDS instructions per chunk (each moves 64 lanes x 16 bytes).
-template <typename Tin, int DK>
+template <typename Tin, int DK, typename SHP>
 struct DmaPlan {
   static constexpr int ES = sizeof(Tin);
-  static constexpr int NK = kChunk * DK * ES / 1024;      // per K (and per Q) tile
-  static constexpr int NT = kChunk * kChunk * ES / 1024;  // per T (and per P) tile
-  static constexpr int NV = kChunk * kBV * ES / 1024;     // value slice
-  // per producer wave: half of every tile and one piece of the 768-byte decay block
-  static constexpr int PER_WAVE = NK + NT + NV / 2 + 1;
-  static_assert(NK % 2 == 0 && NT % 2 == 0 && NV % 2 == 0, "tiles split over two waves");
+  static constexpr int NK = kChunk * DK * ES / 1024;                 // per K (and per Q) tile
+  static constexpr int NTC = (32 * 32 + 32 * kChunk) * ES / 1024;    // per compact T or P tile
+  static constexpr int NV = kChunk * SHP::BV * ES / 1024;            // value slice
+  // per producer wave: an equal share of every tile and of the 768-byte decay block
+  static constexpr int PER_WAVE = (2 * NK + 2 * NTC + NV) / SHP::NP + 1;
+  static_assert(NK % SHP::NP == 0 && (2 * NTC) % SHP::NP == 0 && NV % SHP::NP == 0 &&
+                    768 % (16 * SHP::NP) == 0,
+                "tiles split over the producer waves");
 };
 
-// One workgroup fills a CU's LDS, so each SIMD runs a single wave: let the compiler use
-// the registers that frees to issue LDS reads well ahead of the MFMAs that consume them.
-template <typename Tin, int DK>
-__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// One workgroup fills a CU's LDS; its waves run at most two to a SIMD.
+template <typename Tin, int DK, typename SHP>
+__global__ __launch_bounds__(SHP::THREADS)
+__attribute__((amdgpu_waves_per_eu(SHP::THREADS > 256 ? 2 : 1, SHP::THREADS > 256 ? 2 : 1)))
 void kla_scan_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ GD, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
     const float *S0, Tin *__restrict__ o, float *S_T, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int n_seq, int H, int DV) {
-  using SM = ScanSmem<Tin, DK>;
-  using SL = ScanSlot<Tin, DK>;
-  using DP = DmaPlan<Tin, DK>;
+  constexpr int kBV = SHP::BV, kConsumers = SHP::NC, kScanThreads = SHP::THREADS;
+  using SM = ScanSmem<Tin, DK, kBV>;
+  using SL = ScanSlot<Tin, DK, kBV>;
+  using DP = DmaPlan<Tin, DK, SHP>;
   using FragT = typename Frag<Tin>::type;
   using KQ = std::integral_constant<int, DK>;
-  using TP = std::integral_constant<int, kChunk>;
   constexpr bool B16 = sizeof(Tin) == 2;
   constexpr int ES = sizeof(Tin);
   constexpr int NSLOT = SM::NSLOT;
@@ -176,7 +218,7 @@ void kla_scan_kernel(
   const int h = sh % H, n = sh / H;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kg = lane >> 4;
-  const bool consumer = wid < 2;
+  const bool consumer = wid < kConsumers;
   const int v0 = slice * kBV;
   const int tb = cu[n], te = cu[n + 1];
   const int cbase = chunk_off[n];
@@ -189,11 +231,12 @@ void kla_scan_kernel(
   __syncthreads();
 
   // =========================== producer side ===========================
-  // Producer wave pw issues instructions J = 2 j + pw of every tile; lane l of instruction
+  // Producer wave pw issues instructions J = NP j + pw of every tile; lane l of instruction
   // J writes tile bytes 1024 J + 16 l, i.e. physical unit pu of row r, which holds logical
   // unit pu ^ sw(r) of that row.
-  const int pw = wid - 2;
-  int offK[DP::NK / 2], offT[DP::NT / 2], offV[DP::NV / 2];
+  const int pw = wid - kConsumers;
+  constexpr int NP = SHP::NP;
+  int offK[DP::NK / NP], offTP[2 * DP::NTC / NP], offV[DP::NV / NP];
   auto dma_off = [&](int J, int row_elems, int gstride_bytes, int sw_of_row) {
     const int pbyte = 1024 * J + 16 * lane, rowb = row_elems * ES;
     const int row = pbyte / rowb, pu = (pbyte % rowb) >> 4;
@@ -201,18 +244,19 @@ void kla_scan_kernel(
   };
   if (!consumer) {
 #pragma unroll
-    for (int j = 0; j < DP::NK / 2; ++j) {
-      const int J = 2 * j + pw, row = (1024 * J + 16 * lane) / (DK * ES);
+    for (int j = 0; j < DP::NK / NP; ++j) {
+      const int J = NP * j + pw, row = (1024 * J + 16 * lane) / (DK * ES);
       offK[j] = dma_off(J, DK, H * DK * ES, sw_rows<DK>(row) * (ES / 2));
     }
+    // T then P, compact: item m = NP j + pw is instruction m % NTC of T (m < NTC) or P
 #pragma unroll
-    for (int j = 0; j < DP::NT / 2; ++j) {
-      const int J = 2 * j + pw, row = (1024 * J + 16 * lane) / (kChunk * ES);
-      offT[j] = dma_off(J, kChunk, kChunk * ES, sw_rows<kChunk>(row) * (ES / 2));
+    for (int j = 0; j < 2 * DP::NTC / NP; ++j) {
+      const int m = NP * j + pw;
+      offTP[j] = tpc_src<Tin>(1024 * (m % DP::NTC) + 16 * lane);
     }
 #pragma unroll
-    for (int j = 0; j < DP::NV / 2; ++j) {
-      const int J = 2 * j + pw, row = (1024 * J + 16 * lane) / (kBV * ES);
+    for (int j = 0; j < DP::NV / NP; ++j) {
+      const int J = NP * j + pw, row = (1024 * J + 16 * lane) / (kBV * ES);
       offV[j] = dma_off(J, kBV, H * DV * ES, sw_rows<kBV>(row) * (ES / 2));
     }
   }
@@ -231,32 +275,34 @@ void kla_scan_kernel(
     const Rsrc rp = make_rsrc(Pm + ch * (kChunk * kChunk), kChunk * kChunk * ES);
     const Rsrc rg = make_rsrc(GD + ch * kGDFloats, kGDFloats * sizeof(float));
 #pragma unroll
-    for (int j = 0; j < DP::NK / 2; ++j) {
-      const int J = 2 * j + pw;
+    for (int j = 0; j < DP::NK / NP; ++j) {
+      const int J = NP * j + pw;
       dma16(rk, s.K + 1024 * J, offK[j]);
       dma16(rq, s.Q + 1024 * J, offK[j]);
     }
 #pragma unroll
-    for (int j = 0; j < DP::NT / 2; ++j) {
-      const int J = 2 * j + pw;
-      dma16(rt, s.T + 1024 * J, offT[j]);
-      dma16(rp, s.P + 1024 * J, offT[j]);
+    for (int j = 0; j < 2 * DP::NTC / NP; ++j) {
+      const int m = NP * j + pw;
+      if (m < DP::NTC) dma16(rt, s.T + 1024 * m, offTP[j]);
+      else dma16(rp, s.P + 1024 * (m - DP::NTC), offTP[j]);
     }
 #pragma unroll
-    for (int j = 0; j < DP::NV / 2; ++j) {
-      const int J = 2 * j + pw;
+    for (int j = 0; j < DP::NV / NP; ++j) {
+      const int J = NP * j + pw;
       dma16(rv, s.V + 1024 * J, offV[j]);
     }
-    // decays (gam, dec, gamO are consecutive in the slot): wave 0 fetches gam and dec
-    // (bytes 0..511, 32 lanes), wave 1 gamO (512..767, 16 lanes)
-    if (lane < 32 - 16 * pw)
-      dma16(rg, reinterpret_cast<unsigned char *>(s.gam) + 512 * pw, 512 * pw + 16 * lane);
+    // decays (gam, dec, gamO are consecutive in the slot, 768 bytes): producer pw fetches
+    // its 768 / NP bytes
+    constexpr int GDB = 768 / NP;
+    if (lane < GDB / 16)
+      dma16(rg, reinterpret_cast<unsigned char *>(s.gam) + GDB * pw, GDB * pw + 16 * lane);
   };
 
   // chunk c's outputs, parked in slot s's value tile, back to HBM: 16 bytes per lane per
-  // piece, whole 64-byte value-tile rows per four lanes; rows past a ragged end are dropped
+  // piece, whole value-tile rows; rows past a ragged end are dropped.  Producer pw writes
+  // back exactly the value-tile bytes its own loads fill (instructions J = NP j + pw).
   constexpr int PPR = kBV * ES / 16;                     // 16-byte pieces per value-tile row
-  constexpr int NST = kChunk * PPR / 128;                // store instructions per producer wave
+  constexpr int NST = kChunk * PPR / (64 * NP);          // store instructions per producer wave
   auto p_flush = [&](int c, const SL &s) {
     const int t0 = tb + c * kChunk;
     const int len = min(kChunk, te - t0);
@@ -265,18 +311,18 @@ void kla_scan_kernel(
     u32x4 x[NST];
 #pragma unroll
     for (int j = 0; j < NST; ++j) {
-      const int e = (tid - 128) + 128 * j, row = e / PPR, pc = e % PPR;
+      const int e = (tid - 64 * kConsumers) + 64 * NP * j, row = e / PPR, pc = e % PPR;
       x[j] = *reinterpret_cast<const u32x4 *>(s.V + tile_off<Tin, kBV>(row, pc * (16 / ES)));
     }
 #pragma unroll
     for (int j = 0; j < NST; ++j) {
-      const int e = (tid - 128) + 128 * j, row = e / PPR, pc = e % PPR;
+      const int e = (tid - 64 * kConsumers) + 64 * NP * j, row = e / PPR, pc = e % PPR;
       store16(x[j], ro, (row * H * DV) * ES + pc * 16, 0);
     }
   };
 
   // =========================== consumer side ===========================
-  const int cw = wid & 1;
+  const int cw = wid;  // consumer wave (producers never use it)
   const int col = 16 * cw + r16;  // this lane's state column within the slice
   constexpr int NM = DK / 16;     // 16-row state tiles
   constexpr int NKS = DK / 32;    // k-steps over d_k
@@ -301,6 +347,17 @@ void kla_scan_kernel(
           *reinterpret_cast<const f32x4 *>(tile + tile_off<Tin, RE>(r, 32 * ks + 8 * kg));
       const f32x4 hi =
           *reinterpret_cast<const f32x4 *>(tile + tile_off<Tin, RE>(r, 32 * ks + 8 * kg + 4));
+      return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  // elements 32 ks + 8 kg .. + 7 of row r of a compact T or P tile
+  auto rd_tp = [&](const unsigned char *tile, int r, int ks) {
+    if constexpr (B16) {
+      return *reinterpret_cast<const bf16x8 *>(tile + tpc_off<Tin>(r, 32 * ks + 8 * kg));
+    } else {
+      const f32x4 lo = *reinterpret_cast<const f32x4 *>(tile + tpc_off<Tin>(r, 32 * ks + 8 * kg));
+      const f32x4 hi =
+          *reinterpret_cast<const f32x4 *>(tile + tpc_off<Tin>(r, 32 * ks + 8 * kg + 4));
       return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
@@ -330,12 +387,12 @@ void kla_scan_kernel(
       }
     // ---- reads for R = V - Diag(gam) Y and U = T R
     FragT ft[6];
-    ft[0] = rd_frag(s.T, TP{}, frow(0), 0);
-    ft[1] = rd_frag(s.T, TP{}, frow(1), 0);
-    ft[2] = rd_frag(s.T, TP{}, frow(2), 0);
-    ft[3] = rd_frag(s.T, TP{}, frow(2), 1);
-    ft[4] = rd_frag(s.T, TP{}, frow(3), 0);
-    ft[5] = rd_frag(s.T, TP{}, frow(3), 1);
+    ft[0] = rd_tp(s.T, frow(0), 0);
+    ft[1] = rd_tp(s.T, frow(1), 0);
+    ft[2] = rd_tp(s.T, frow(2), 0);
+    ft[3] = rd_tp(s.T, frow(2), 1);
+    ft[4] = rd_tp(s.T, frow(3), 0);
+    ft[5] = rd_tp(s.T, frow(3), 1);
     f32x4 g4[4], d4[4];
     float vv[4][4];
 #pragma unroll
@@ -418,12 +475,12 @@ void kla_scan_kernel(
     }
     // ---- reads for the output: P fragments and this lane's token decays
     FragT fp[6];
-    fp[0] = rd_frag(s.P, TP{}, frow(0), 0);
-    fp[1] = rd_frag(s.P, TP{}, frow(1), 0);
-    fp[2] = rd_frag(s.P, TP{}, frow(2), 0);
-    fp[3] = rd_frag(s.P, TP{}, frow(2), 1);
-    fp[4] = rd_frag(s.P, TP{}, frow(3), 0);
-    fp[5] = rd_frag(s.P, TP{}, frow(3), 1);
+    fp[0] = rd_tp(s.P, frow(0), 0);
+    fp[1] = rd_tp(s.P, frow(1), 0);
+    fp[2] = rd_tp(s.P, frow(2), 0);
+    fp[3] = rd_tp(s.P, frow(2), 1);
+    fp[4] = rd_tp(s.P, frow(3), 0);
+    fp[5] = rd_tp(s.P, frow(3), 1);
     float gt[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) gt[t] = s.gamO[frow(t)];
@@ -529,32 +586,65 @@ void kla_scan_kernel(
   }
 }
 
+template <typename Tin, int DK, typename SHP>
+static hipError_t launch_scan_s(int d_v, const void *q, const void *k, const void *v,
+                                const float *GD, const void *T, const void *P, const float *S0,
+                                void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
+                                hipStream_t stream) {
+  using SMT = ScanSmem<Tin, DK, SHP::BV>;
+  using SLT = ScanSlot<Tin, DK, SHP::BV>;
+  static_assert(sizeof(SMT) <= kLdsBytes, "LDS budget");
+  static_assert(offsetof(SLT, dec) == offsetof(SLT, gam) + 256 &&
+                    offsetof(SLT, gamO) == offsetof(SLT, gam) + 512,
+                "the decay block is fetched as one contiguous 768-byte piece");
+  const size_t smem = sizeof(SMT);
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t blocks = (int64_t)n_seq * H * (d_v / SHP::BV);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK, SHP>), dim3((unsigned)blocks), dim3(SHP::THREADS),
+                     smem, stream, static_cast<const Tin *>(q), static_cast<const Tin *>(k),
+                     static_cast<const Tin *>(v), GD, static_cast<const Tin *>(T),
+                     static_cast<const Tin *>(P), S0, static_cast<Tin *>(o), S_T, t.cu,
+                     t.chunk_off, n_seq, H, d_v);
+  return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device), 0 if unknown.
+static int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// The narrow shape while its grid fits the chip in one wave of workgroups (more of them
+// would only queue behind each other while their staging traffic adds up); the wide shape,
+// which stages each tile once for 64 columns, beyond that.
 template <typename Tin, int DK>
 static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const void *v,
                                 const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
                                 hipStream_t stream) {
-  static_assert(sizeof(ScanSmem<Tin, DK>) <= kLdsBytes, "LDS budget");
-  using SLT = ScanSlot<Tin, DK>;
-  static_assert(offsetof(SLT, dec) == offsetof(SLT, gam) + 256 &&
-                    offsetof(SLT, gamO) == offsetof(SLT, gam) + 512,
-                "the decay block is fetched as one contiguous 768-byte piece");
-  const size_t smem = sizeof(ScanSmem<Tin, DK>);
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int64_t blocks = (int64_t)n_seq * H * (d_v / kBV);
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK>), dim3((unsigned)blocks), dim3(kScanThreads), smem,
-                     stream, static_cast<const Tin *>(q), static_cast<const Tin *>(k),
-                     static_cast<const Tin *>(v), GD, static_cast<const Tin *>(T),
-                     static_cast<const Tin *>(P), S0, static_cast<Tin *>(o), S_T, t.cu,
-                     t.chunk_off, n_seq, H, d_v);
-  return hipGetLastError();
+  const int64_t narrow_blocks = (int64_t)n_seq * H * (d_v / ScanNarrow::BV);
+  const int cus = device_cus();
+  if (cus > 0 && narrow_blocks > cus)
+    return launch_scan_s<Tin, DK, ScanWide>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
+                                            stream);
+  return launch_scan_s<Tin, DK, ScanNarrow>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
+                                            stream);
 }
 
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,

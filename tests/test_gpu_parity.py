@@ -154,6 +154,19 @@ def test_prefill_fp32_shapes(kla, n_seq, T, H, dk, dv):
     check(ST, So, 1e-4, "ST")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_prefill_wide_workgroups(kla, dtype, dk):
+    """Enough (sequence, head, 32-column) blocks to exceed the chip's compute units, so the
+    scan runs its 64-column workgroup shape; ragged tail, random S0."""
+    w = ki.Workload(99, "unit", 3, 24, dk, 128, dtype, T=130, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    o, ST = run_prefill(kla, d)
+    oo, So = oracle_prefill(d)
+    check(o, oo, TOL[dtype], "o")
+    check(ST, So, TOL[dtype], "ST")
+
+
 def test_prefill_packed_ragged(kla):
     """Packed sequences with empty, one-token, chunk-edge and multi-chunk members, strong
     decay and 5% near-zero keys (the eps guard)."""
