@@ -7,35 +7,41 @@
 //   e = v - a r,  b = eta / (||k||^2 + eps)
 //   S' = a S + b k^T e,   o = a p + b (q . k) e
 // the state is streamed through registers exactly once.  The coefficient variants and the
-// readout divided by ||q|| (see write_coef) only change b and scale o.  One workgroup
-// (256 lanes) per (sequence, head); each lane owns float4 column groups of a
-// few state rows, so every load and store is a coalesced 16-byte access.
+// readout divided by ||q|| (see write_coef) only change b and scale o.  The columns of S are
+// independent given k, q and the scalars, so a (sequence, head) is split over NS workgroups of
+// NT lanes, each taking d_v / NS columns; each lane owns float4 column groups of a few state
+// rows, so every load and store is a coalesced 16-byte access.
 #include "kla_device.h"
 #include "kla_launch.h"
 
 namespace kla {
 
-template <typename Tin, int DK, int DV>
-__global__ __launch_bounds__(256) void kla_decode_kernel(
+template <typename Tin, int DK, int DV, int NS, int NT>
+__global__ __launch_bounds__(NT) void kla_decode_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ eta, float eps, CoefOpts opts,
     int H, const float *S, Tin *__restrict__ o, float *S_new) {
-  constexpr int NC4 = DV / 4;      // float4 column groups per state row
-  constexpr int RPP = 256 / NC4;   // state rows per pass
-  constexpr int NP = DK / RPP;     // passes (float4 registers per lane)
+  constexpr int NC4 = DV / NS / 4;  // float4 column groups of this workgroup per state row
+  constexpr int RS4 = DV / 4;       // float4 column groups per state row
+  constexpr int RPP = NT / NC4;     // state rows per pass
+  constexpr int NP = DK / RPP;      // passes (float4 registers per lane)
+  constexpr int NW = NT / 64;       // wavefronts
+  static_assert(NC4 >= 1 && RPP * NC4 == NT && NP * RPP == DK && NT >= DK, "decode tiling");
   __shared__ float sk[DK], sq[DK];
   __shared__ f32x4 red_r[RPP][NC4], red_p[RPP][NC4];
-  __shared__ float sred[3][4];
+  __shared__ float sred[3][NW];
 
-  const size_t bh = blockIdx.x;
+  const size_t bh = blockIdx.x / NS;
+  const int col0 = (blockIdx.x % NS) * NC4;  // first float4 column group of this workgroup
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int c4 = tid % NC4, rg = tid / NC4;
 
   // issue the state loads first: they are the only large traffic
-  const f32x4 *Sp = reinterpret_cast<const f32x4 *>(S + bh * DK * DV);
+  const f32x4 *Sp = reinterpret_cast<const f32x4 *>(S + bh * DK * DV) + col0;
   f32x4 s[NP];
 #pragma unroll
-  for (int pp = 0; pp < NP; ++pp) s[pp] = __builtin_nontemporal_load(&Sp[(pp * RPP + rg) * NC4 + c4]);
+  for (int pp = 0; pp < NP; ++pp)
+    s[pp] = __builtin_nontemporal_load(&Sp[(pp * RPP + rg) * RS4 + c4]);
 
   float kf = 0.f, qf = 0.f;
   if (tid < DK) {
@@ -63,9 +69,13 @@ __global__ __launch_bounds__(256) void kla_decode_kernel(
 #pragma unroll
   for (int gg = 0; gg < RPP; ++gg) { rt += red_r[gg][c4]; pt += red_p[gg][c4]; }
 
-  const float kk_all = sred[0][0] + sred[0][1] + sred[0][2] + sred[0][3];
-  const float qk_all = sred[1][0] + sred[1][1] + sred[1][2] + sred[1][3];
-  const float qq_all = sred[2][0] + sred[2][1] + sred[2][2] + sred[2][3];
+  float kk_all = 0.f, qk_all = 0.f, qq_all = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    kk_all += sred[0][w];
+    qk_all += sred[1][w];
+    qq_all += sred[2][w];
+  }
   const float a = __expf(g[bh]);
   const float den = kk_all + eps;
   const int brow = (int)(bh / H);
@@ -74,33 +84,46 @@ __global__ __launch_bounds__(256) void kla_decode_kernel(
   // readout factor: 1 / ||q|| under the normalised readout (0 for a zero query), else 1
   const float rq = opts.normalize_q ? (qq_all > 0.f ? 1.f / sqrtf(qq_all) : 0.f) : 1.f;
   f32x4 e;
+  const int vc = 4 * (col0 + c4);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) e[j] = to_f32(v[bh * DV + 4 * c4 + j]) - a * rt[j];
+  for (int j = 0; j < 4; ++j) e[j] = to_f32(v[bh * DV + vc + j]) - a * rt[j];
   if (rg == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      o[bh * DV + 4 * c4 + j] = from_f32<Tin>((a * pt[j] + beta * qk_all * e[j]) * rq);
+      o[bh * DV + vc + j] = from_f32<Tin>((a * pt[j] + beta * qk_all * e[j]) * rq);
   }
-  f32x4 *Sn = reinterpret_cast<f32x4 *>(S_new + bh * DK * DV);
+  f32x4 *Sn = reinterpret_cast<f32x4 *>(S_new + bh * DK * DV) + col0;
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp) {
     const int row = pp * RPP + rg;
     const float bk = beta * sk[row];
-    __builtin_nontemporal_store(a * s[pp] + bk * e, &Sn[row * NC4 + c4]);
+    __builtin_nontemporal_store(a * s[pp] + bk * e, &Sn[row * RS4 + c4]);
   }
 }
+
+// Launch shape by the number of (sequence, head) items: below kDecodeSplitBelow, two 128-lane
+// workgroups per item, so that there are enough workgroups to keep HBM busy; from there on, one
+// 512-lane workgroup per item.  Both measured best on their side of the threshold
+// (256 x 16 items: 5.64 TB/s; 512 x 16 items: 5.79 TB/s).
+constexpr int64_t kDecodeSplitBelow = 5120;
 
 template <typename Tin, int DK, int DV>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
                                   const float *eta, float eps, const CoefOpts &opts,
                                   const float *S, void *o, float *S_new, int32_t batch,
                                   int32_t H, hipStream_t stream) {
-  const int64_t blocks = (int64_t)batch * H;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     static_cast<const Tin *>(q), static_cast<const Tin *>(k),
-                     static_cast<const Tin *>(v), g, eta, eps, opts, H, S, static_cast<Tin *>(o),
-                     S_new);
+  const int64_t items = (int64_t)batch * H;
+  if (items <= 0) return hipSuccess;
+  if (2 * items > 0x7fffffff) return hipErrorInvalidValue;  // grid size
+  const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
+  const Tin *vt = static_cast<const Tin *>(v);
+  Tin *ot = static_cast<Tin *>(o);
+  if (items < kDecodeSplitBelow)
+    hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 2, 128>), dim3((unsigned)(2 * items)),
+                       dim3(128), 0, stream, qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
+  else
+    hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 1, 512>), dim3((unsigned)items),
+                       dim3(512), 0, stream, qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
   return hipGetLastError();
 }
 

@@ -106,6 +106,26 @@ def test_decode_full_batch(kla):
         check(S, So, 2e-2, "S")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_many_items(kla, dtype):
+    """6144 (sequence, head) items: the launch shape with one 512-lane workgroup per item (the
+    smaller cases above take two 128-lane workgroups per item).  Every item runs on the GPU;
+    the oracle checks a sample of 24 sequences, which are independent of the rest."""
+    w = ki.Workload(91, "decode-many", 64, 96, 64, 128, dtype, T=1, s0_var=0.05, decode_steps=2)
+    d = to_dev(ki.decode_inputs(w))
+    S = d["S"].clone()
+    pick = np.arange(0, 64, 8).tolist() + [1, 2, 3, 61, 62, 63] + list(range(20, 30))
+    So = d["S"][pick].double().cpu().numpy()
+    for t in range(2):
+        o, S = kla.kla_decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t],
+                                   d["eps"], S, inplace=(t == 1))
+        oo, So = oracle.decode(d["q"][t][pick], d["k"][t][pick], d["v"][t][pick],
+                               d["g"][t][pick], d["eta"][t][pick], d["eps"], So)
+        torch.cuda.synchronize()
+        check(o[pick], oo, TOL[dtype], "o t")
+        check(S[pick], So, TOL[dtype], "S t")
+
+
 # ------------------------------------------------------------------------------------ prefill
 def test_prefill_tiny_fp32(kla):
     """Workload 0 (fp32, T=256, d=64) at the 1e-4 bar."""
