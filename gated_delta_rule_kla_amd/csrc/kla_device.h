@@ -26,6 +26,48 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 constexpr int kChunk = 64;
 constexpr int kWave = 64;
 
+// ---------------------------------------------------------------- compact T and P tiles
+// The per-chunk matrices T and P (64 x 64, lower triangular) in the form the scan stages them,
+// which the prep writes to the workspace and the scan copies into LDS byte for byte.  It leaves
+// out the block of rows 0-31 x columns 32-63 (zero, and outside every operand read):
+//   region A  rows 0-31, columns 0-31, in tile order: row slot 4 a + i of 16-row tile t
+//             (token 8 a + 4 t + i) at row 16 t + 4 a + i, so that a tile's rows are adjacent;
+//   region B  rows 32-63, all 64 columns, in token order.
+// 16-byte units of a row are XOR-swizzled (twice the amount for fp32 rows) so that the scan's
+// 16-byte fragment reads of a tile's rows hit distinct LDS banks.
+template <typename T> constexpr int tpc_bytes() { return (32 * 32 + 32 * kChunk) * (int)sizeof(T); }
+__device__ __forceinline__ int tpc_sw_a(int rho) { return ((rho >> 3) & 1) << 1; }
+__device__ __forceinline__ int tpc_sw_b(int r) {
+  return (((r >> 1) & 1) << 2) ^ (((r >> 3) & 1) * 3) ^ (((r >> 4) & 1) << 1);
+}
+// Byte offset of element e of row r (row < 32 requires e < 32).
+template <typename T>
+__device__ __forceinline__ int tpc_off(int r, int e) {
+  constexpr int ES = sizeof(T);
+  const int byte = e * ES;
+  if (r < 32) {
+    const int rho = 16 * ((r >> 2) & 1) + 4 * ((r >> 3) & 3) + (r & 3);
+    const int u = (byte >> 4) ^ (tpc_sw_a(rho) * (ES / 2));
+    return rho * 32 * ES + (u << 4) + (byte & 15);
+  }
+  const int u = (byte >> 4) ^ (tpc_sw_b(r) * (ES / 2));
+  return 32 * 32 * ES + (r - 32) * kChunk * ES + (u << 4) + (byte & 15);
+}
+// The row and first column of the 16 bytes at byte offset pb (a multiple of 16).
+template <typename T>
+__device__ __forceinline__ void tpc_piece(int pb, int &row, int &col) {
+  constexpr int ES = sizeof(T), RA = 32 * ES, RB = kChunk * ES;
+  if (pb < 32 * RA) {
+    const int rho = pb / RA;
+    row = 8 * ((rho >> 2) & 3) + 4 * (rho >> 4) + (rho & 3);
+    col = ((((pb % RA) >> 4) ^ (tpc_sw_a(rho) * (ES / 2))) << 4) / ES;
+  } else {
+    const int qb = pb - 32 * RA;
+    row = 32 + qb / RB;
+    col = ((((qb % RB) >> 4) ^ (tpc_sw_b(row) * (ES / 2))) << 4) / ES;
+  }
+}
+
 // ---------------------------------------------------------------- element types
 template <typename T> struct Frag;
 template <> struct Frag<__bf16> { typedef bf16x8 type; };

@@ -258,19 +258,29 @@ __device__ __forceinline__ void stage_put(unsigned char *st, int row, int col, f
   }
 }
 // The staged tile to dst (row-major, 64 x 64): every store instruction writes whole rows.
-// With skip_upper the block of rows 0..31, columns 32..63 (zero, and never read by the
-// scan, whose operand reads of those rows stop at column 31) is left unwritten.
 template <typename T>
-__device__ __forceinline__ void stage_flush(const unsigned char *st, T *dst, int lane,
-                                            bool skip_upper) {
+__device__ __forceinline__ void stage_flush(const unsigned char *st, T *dst, int lane) {
   constexpr int UPR = kChunk * (int)sizeof(T) / 16;  // 16-byte units per row: 8 or 16
   constexpr int RPI = kWave / UPR;                   // rows per instruction
 #pragma unroll
   for (int m = 0; m < kChunk / RPI; ++m) {
     const int row = RPI * m + lane / UPR, u = lane % UPR;
-    if (skip_upper && row < kChunk / 2 && u >= UPR / 2) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(st + stage_off<T>(row, u * 16 / (int)sizeof(T)));
-    *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(dst) + row * UPR * 16 + u * 16) = v;
+    const u32x4 v =
+        *reinterpret_cast<const u32x4 *>(st + stage_off<T>(row, u * 16 / (int)sizeof(T)));
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(dst) + row * UPR * 16 + u * 16) =
+        v;
+  }
+}
+// The staged tile to dst as a compact tile (tpc_off): whole 1 KB store instructions.
+template <typename T>
+__device__ __forceinline__ void stage_flush_compact(const unsigned char *st, T *dst, int lane) {
+#pragma unroll
+  for (int m = 0; m < tpc_bytes<T>() / 1024; ++m) {
+    const int pb = 1024 * m + 16 * lane;
+    int row, col;
+    tpc_piece<T>(pb, row, col);
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(st + stage_off<T>(row, col));
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(dst) + pb) = v;
   }
 }
 
@@ -453,7 +463,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
       }
     }
     lds_barrier();
-    stage_flush<Tin>(sm.stage, P_out + (size_t)task * (kChunk * kChunk), lane, true);
+    stage_flush_compact<Tin>(sm.stage, P_out + (size_t)task * (kChunk * kChunk), lane);
   }
 
   // ---- L: diagonal blocks to LDS (row-major), sub-diagonal blocks kept in registers in the
@@ -564,7 +574,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     }
     lds_barrier();
   }
-  stage_flush<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane, GD_out != nullptr);
+  // the scan's T (written with the decays) as a compact tile, the unit-check stage's in full
+  if (GD_out)
+    stage_flush_compact<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane);
+  else
+    stage_flush<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane);
 }
 
 template <typename Tin, int DK>

@@ -118,36 +118,6 @@ __device__ __forceinline__ int tile_off(int r, int e) {
   return r * ROWB + (u << 4) + (byte & 15);
 }
 
-// The T and P tiles in LDS without their never-read block (rows 0-31, columns 32-63, zero):
-// region A holds rows 0-31, columns 0-31, in tile order (row slot 4 a + i of tile t at LDS
-// row 16 t + 4 a + i, t = 0, 1), so that the 16 rows of one tile are consecutive; region B
-// holds rows 32-63, all 64 columns, in token order.  Byte offset of element e of row r:
-template <typename T>
-__device__ __forceinline__ int tpc_off(int r, int e) {
-  constexpr int ES = sizeof(T);
-  const int byte = e * ES;
-  if (r < 32) {
-    const int rho = 16 * ((r >> 2) & 1) + 4 * ((r >> 3) & 3) + (r & 3);
-    const int u = (byte >> 4) ^ ((((rho >> 3) & 1) << 1) * (ES / 2));
-    return rho * 32 * ES + (u << 4) + (byte & 15);
-  }
-  const int u = (byte >> 4) ^ (sw_rows<kChunk>(r) * (ES / 2));
-  return 32 * 32 * ES + (r - 32) * kChunk * ES + (u << 4) + (byte & 15);
-}
-// Byte offset, in a row-major 64 x 64 tile in memory, of the 16 bytes that belong at byte pb
-// of the compact LDS tile.
-template <typename T>
-__device__ __forceinline__ int tpc_src(int pb) {
-  constexpr int ES = sizeof(T), RA = 32 * ES, RB = kChunk * ES;
-  if (pb < 32 * RA) {
-    const int rho = pb / RA, pu = (pb % RA) >> 4;
-    const int row = 8 * ((rho >> 2) & 3) + 4 * (rho >> 4) + (rho & 3);
-    return row * RB + ((pu ^ ((((rho >> 3) & 1) << 1) * (ES / 2))) << 4);
-  }
-  const int qb = pb - 32 * RA, row = 32 + qb / RB;
-  return row * RB + ((((qb % RB) >> 4) ^ (sw_rows<kChunk>(row) * (ES / 2))) << 4);
-}
-
 // LDS transpose read of 4 x 16-bit values (gfx950 ds_read_b64_tr_b16).  Within each group
 // of 16 lanes, destination lane d receives element (d & 3) of the 8-byte chunks addressed
 // by source lanes (d >> 2) + 4 i, i = 0..3.
@@ -168,8 +138,8 @@ template <typename Tin, int DK, int BV>
 struct ScanSlot {
   alignas(16) unsigned char K[kChunk * DK * sizeof(Tin)];
   alignas(16) unsigned char Q[kChunk * DK * sizeof(Tin)];
-  alignas(16) unsigned char T[(32 * 32 + 32 * kChunk) * sizeof(Tin)];  // compact (tpc_off)
-  alignas(16) unsigned char P[(32 * 32 + 32 * kChunk) * sizeof(Tin)];
+  alignas(16) unsigned char T[tpc_bytes<Tin>()];  // compact tiles (tpc_off)
+  alignas(16) unsigned char P[tpc_bytes<Tin>()];
   alignas(16) unsigned char V[kChunk * BV * sizeof(Tin)];
   alignas(16) float gam[kChunk];   // exp(G_i)
   alignas(16) float dec[kChunk];   // exp(G_last - G_i)
@@ -193,7 +163,7 @@ template <typename Tin, int DK, typename SHP>
 struct DmaPlan {
   static constexpr int ES = sizeof(Tin);
   static constexpr int NK = kChunk * DK * ES / 1024;                 // per K (and per Q) tile
-  static constexpr int NTC = (32 * 32 + 32 * kChunk) * ES / 1024;    // per compact T or P tile
+  static constexpr int NTC = tpc_bytes<Tin>() / 1024;               // per compact T or P tile
   static constexpr int NV = kChunk * SHP::BV * ES / 1024;            // value slice
   // per producer wave: an equal share of every tile and of the 768-byte decay block
   static constexpr int PER_WAVE = (2 * NK + 2 * NTC + NV) / SHP::NP + 1;
@@ -263,11 +233,12 @@ void kla_scan_kernel(
       const int J = NP * j + pw, row = (1024 * J + 16 * lane) / (DK * ES);
       offK[j] = dma_off(J, DK, H * DK * ES, sw_rows<DK>(row) * (ES / 2));
     }
-    // T then P, compact: item m = NP j + pw is instruction m % NTC of T (m < NTC) or P
+    // T then P, stored as compact tiles and copied unchanged: item m = NP j + pw is
+    // instruction m % NTC of T (m < NTC) or P
 #pragma unroll
     for (int j = 0; j < 2 * DP::NTC / NP; ++j) {
       const int m = NP * j + pw;
-      offTP[j] = tpc_src<Tin>(1024 * (m % DP::NTC) + 16 * lane);
+      offTP[j] = 1024 * (m % DP::NTC) + 16 * lane;
     }
 #pragma unroll
     for (int j = 0; j < DP::NV / NP; ++j) {
@@ -286,8 +257,8 @@ void kla_scan_kernel(
     const Rsrc rv =
         make_rsrc(v + tok * DV + v0, (uint32_t)(((size_t)(len - 1) * H * DV + kBV) * ES));
     const size_t ch = (size_t)(cbase + c) * H + h;
-    const Rsrc rt = make_rsrc(Tm + ch * (kChunk * kChunk), kChunk * kChunk * ES);
-    const Rsrc rp = make_rsrc(Pm + ch * (kChunk * kChunk), kChunk * kChunk * ES);
+    const Rsrc rt = make_rsrc(Tm + ch * (kChunk * kChunk), tpc_bytes<Tin>());
+    const Rsrc rp = make_rsrc(Pm + ch * (kChunk * kChunk), tpc_bytes<Tin>());
     const Rsrc rg = make_rsrc(GD + ch * kGDFloats, kGDFloats * sizeof(float));
 #pragma unroll
     for (int j = 0; j < DP::NK / NP; ++j) {
