@@ -27,9 +27,9 @@ constexpr int kChunk = 64;
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------- compact T and P tiles
-// The per-chunk matrices T and P (64 x 64, lower triangular) in the form the scan stages them,
-// which the prep writes to the workspace and the scan copies into LDS byte for byte.  It leaves
-// out the block of rows 0-31 x columns 32-63 (zero, and outside every operand read):
+// The per-chunk matrices T and P (64 x 64, lower triangular) in the form the scan stages them
+// in LDS.  It leaves out the block of rows 0-31 x columns 32-63 (zero, and outside every
+// operand read):
 //   region A  rows 0-31, columns 0-31, in tile order: row slot 4 a + i of 16-row tile t
 //             (token 8 a + 4 t + i) at row 16 t + 4 a + i, so that a tile's rows are adjacent;
 //   region B  rows 32-63, all 64 columns, in token order.
@@ -53,7 +53,31 @@ __device__ __forceinline__ int tpc_off(int r, int e) {
   const int u = (byte >> 4) ^ (tpc_sw_b(r) * (ES / 2));
   return 32 * 32 * ES + (r - 32) * kChunk * ES + (u << 4) + (byte & 15);
 }
-// The row and first column of the 16 bytes at byte offset pb (a multiple of 16).
+// In the workspace the tiles keep only their ten 16 x 16 blocks on and below the diagonal,
+// each row-major, in the order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) .. (3,3); the scan
+// reads zeros for the two upper blocks the compact tile still holds.
+constexpr int kTpbZero = 0x7ffffff0;  // out of range for any tile: a buffer load reads zeros
+template <typename T> constexpr int tpb_bytes() { return 10 * 256 * (int)sizeof(T); }
+// Byte offset of the 16 bytes at (row, col), col a multiple of 16 / sizeof(T); kTpbZero above
+// the diagonal blocks.
+template <typename T>
+__device__ __forceinline__ int tpb_off(int row, int col) {
+  constexpr int ES = sizeof(T);
+  const int I = row >> 4, J = col >> 4;
+  if (J > I) return kTpbZero;
+  return ((I * (I + 1) / 2 + J) * 256 + (row & 15) * 16 + (col & 15)) * ES;
+}
+// The row and column of the 16 bytes at byte offset pb of the packed blocks.
+template <typename T>
+__device__ __forceinline__ void tpb_piece(int pb, int &row, int &col) {
+  constexpr int ES = sizeof(T);
+  const int b = pb / (256 * ES), w = (pb % (256 * ES)) / ES;
+  const int I = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0, J = b - I * (I + 1) / 2;
+  row = 16 * I + w / 16;
+  col = 16 * J + w % 16;
+}
+// The row and first column of the 16 bytes at byte offset pb (a multiple of 16) of a compact
+// tile.
 template <typename T>
 __device__ __forceinline__ void tpc_piece(int pb, int &row, int &col) {
   constexpr int ES = sizeof(T), RA = 32 * ES, RB = kChunk * ES;

@@ -271,14 +271,15 @@ __device__ __forceinline__ void stage_flush(const unsigned char *st, T *dst, int
         v;
   }
 }
-// The staged tile to dst as a compact tile (tpc_off): whole 1 KB store instructions.
+// The staged tile's blocks on and below the diagonal to dst, packed (tpb_off): whole 1 KB
+// store instructions.
 template <typename T>
-__device__ __forceinline__ void stage_flush_compact(const unsigned char *st, T *dst, int lane) {
+__device__ __forceinline__ void stage_flush_packed(const unsigned char *st, T *dst, int lane) {
 #pragma unroll
-  for (int m = 0; m < tpc_bytes<T>() / 1024; ++m) {
+  for (int m = 0; m < tpb_bytes<T>() / 1024; ++m) {
     const int pb = 1024 * m + 16 * lane;
     int row, col;
-    tpc_piece<T>(pb, row, col);
+    tpb_piece<T>(pb, row, col);
     const u32x4 v = *reinterpret_cast<const u32x4 *>(st + stage_off<T>(row, col));
     *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(dst) + pb) = v;
   }
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
       }
     }
     lds_barrier();
-    stage_flush_compact<Tin>(sm.stage, P_out + (size_t)task * (kChunk * kChunk), lane);
+    stage_flush_packed<Tin>(sm.stage, P_out + (size_t)task * (kChunk * kChunk), lane);
   }
 
   // ---- L: diagonal blocks to LDS (row-major), sub-diagonal blocks kept in registers in the
@@ -574,9 +575,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     }
     lds_barrier();
   }
-  // the scan's T (written with the decays) as a compact tile, the unit-check stage's in full
+  // the scan's T (written with the decays) as packed blocks, the unit-check stage's in full
   if (GD_out)
-    stage_flush_compact<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane);
+    stage_flush_packed<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane);
   else
     stage_flush<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane);
 }

@@ -233,12 +233,14 @@ void kla_scan_kernel(
       const int J = NP * j + pw, row = (1024 * J + 16 * lane) / (DK * ES);
       offK[j] = dma_off(J, DK, H * DK * ES, sw_rows<DK>(row) * (ES / 2));
     }
-    // T then P, stored as compact tiles and copied unchanged: item m = NP j + pw is
+    // T then P, compact tiles in LDS from packed blocks in memory: item m = NP j + pw is
     // instruction m % NTC of T (m < NTC) or P
 #pragma unroll
     for (int j = 0; j < 2 * DP::NTC / NP; ++j) {
       const int m = NP * j + pw;
-      offTP[j] = 1024 * (m % DP::NTC) + 16 * lane;
+      int row, col;
+      tpc_piece<Tin>(1024 * (m % DP::NTC) + 16 * lane, row, col);
+      offTP[j] = tpb_off<Tin>(row, col);
     }
 #pragma unroll
     for (int j = 0; j < DP::NV / NP; ++j) {
@@ -257,8 +259,8 @@ void kla_scan_kernel(
     const Rsrc rv =
         make_rsrc(v + tok * DV + v0, (uint32_t)(((size_t)(len - 1) * H * DV + kBV) * ES));
     const size_t ch = (size_t)(cbase + c) * H + h;
-    const Rsrc rt = make_rsrc(Tm + ch * (kChunk * kChunk), tpc_bytes<Tin>());
-    const Rsrc rp = make_rsrc(Pm + ch * (kChunk * kChunk), tpc_bytes<Tin>());
+    const Rsrc rt = make_rsrc(Tm + ch * (kChunk * kChunk), tpb_bytes<Tin>());
+    const Rsrc rp = make_rsrc(Pm + ch * (kChunk * kChunk), tpb_bytes<Tin>());
     const Rsrc rg = make_rsrc(GD + ch * kGDFloats, kGDFloats * sizeof(float));
 #pragma unroll
     for (int j = 0; j < DP::NK / NP; ++j) {
