@@ -18,8 +18,10 @@ timed loop: the prefill is issued as its two halves (kla_prefill_prepare, then
 kla_prefill_scan), which is exactly what kla_prefill_chunked enqueues.
 
 Algorithmic work (per token-head, C = 64, d = d_k = d_v):
-  scan kernel bytes  = 2 d_k e (q, k) + d_v e (v) + d_v e (o) + 2 C e (a row of T and of P)
-                       + 8 (the two decay factors)
+  scan kernel bytes  = 2 d_k e (q, k) + d_v e (v) + d_v e (o)
+                       + 2 x 40 e (T and P: the ten 16 x 16 blocks on and below the diagonal
+                         of each 64 x 64 matrix, 2560 entries per 64 tokens)
+                       + 12 (three fp32 decay factors)
                        + 8 d_k d_v per (sequence, head) for S0 in / S_T out,  e = 2 (bf16)
   prefill MFMA flops = 6 d_k d_v + (C-1) d_k + (C+1)(2 d_k + 2 d_v)
   decode bytes       = 8 d_k d_v + 2 (2 d_k + d_v) + 2 d_v + 8
@@ -154,7 +156,9 @@ def main():
     tok_per_s = n_tok / (ms_per_step * 1e-3)
     th = n_tok * H
     # per token-head: q, k, v rows, o row, one row each of T and P, three decay factors
-    scan_bytes = th * (2 * dk * 2 + dv * 2 + dv * 2 + 2 * CHUNK * 2 + 12) + 2 * n_seq * H * dk * dv * 4
+    tp_per_token = 10 * 256 // CHUNK  # lower 16 x 16 blocks of T (and of P) per token
+    scan_bytes = (th * (2 * dk * 2 + dv * 2 + dv * 2 + 2 * tp_per_token * 2 + 12)
+                  + 2 * n_seq * H * dk * dv * 4)
     scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     flops_prefill = th * (6 * dk * dv + (CHUNK - 1) * dk + (CHUNK + 1) * (2 * dk + 2 * dv))
     mfma_frac = flops_prefill / (ms_per_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
