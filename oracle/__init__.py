@@ -58,10 +58,10 @@ def _load():
         lib.kla_oracle_decode.restype = ctypes.c_int
         i64p = ctypes.POINTER(ctypes.c_int64)
         lib.kla_oracle_prefill_v.argtypes = lib.kla_oracle_prefill.argtypes + [
-            ctypes.c_int, ctypes.c_int, i64p]
+            ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int]
         lib.kla_oracle_prefill_v.restype = ctypes.c_int
         lib.kla_oracle_decode_v.argtypes = lib.kla_oracle_decode.argtypes + [
-            ctypes.c_int, ctypes.c_int, i64p]
+            ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int]
         lib.kla_oracle_decode_v.restype = ctypes.c_int
         lib.kla_oracle_max_threads.argtypes = []
         lib.kla_oracle_max_threads.restype = ctypes.c_int
@@ -112,6 +112,8 @@ def prefill(q, k, v, g, eta, eps, S0=None, cu_seqlens=None, n_seq=None, nthreads
     """Tokenwise fp64 prefill.
 
     q, k: [n_tok, H, d_k]; v: [n_tok, H, d_v]; g, eta: [n_tok, H];
+    g: [n_tok, H, d_k] instead for diagonal gating (one log-decay per key channel, paper
+    Appendix B.5; shaped like k);
     S0: [n_seq, H, d_k, d_v] or None (zeros); cu_seqlens: [n_seq+1] token offsets,
     or None for one sequence per leading batch row when q is [B, T, H, d_k].
     beta_mode / normalize_q / pos_offset ([n_seq]: the first token of sequence n is at
@@ -120,6 +122,7 @@ def prefill(q, k, v, g, eta, eps, S0=None, cu_seqlens=None, n_seq=None, nthreads
     with o shaped like v.
     """
     q, k, v, g, eta = (_f64(x) for x in (q, k, v, g, eta))
+    gdiag = g.shape == q.shape
     out_shape = v.shape
     if cu_seqlens is None and q.ndim == 4:  # dense [B, T, H, d]
         B, T = q.shape[0], q.shape[1]
@@ -135,7 +138,7 @@ def prefill(q, k, v, g, eta, eps, S0=None, cu_seqlens=None, n_seq=None, nthreads
     q = q.reshape(-1, H, dk)
     k = k.reshape(-1, H, dk)
     v = v.reshape(-1, H, dv)
-    g = g.reshape(-1, H)
+    g = g.reshape(-1, H, dk) if gdiag else g.reshape(-1, H)
     eta = eta.reshape(-1, H)
     ns = len(cu) - 1
     if n_seq is not None and n_seq != ns:
@@ -151,7 +154,8 @@ def prefill(q, k, v, g, eta, eps, S0=None, cu_seqlens=None, n_seq=None, nthreads
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S0a),
         cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ns, H, dk, dv, _ptr(o), _ptr(ST),
         int(nthreads), _mode(beta_mode), 1 if normalize_q else 0,
-        None if po is None else po.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        None if po is None else po.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        1 if gdiag else 0)
     if rc != 0:
         raise RuntimeError("kla_oracle_prefill failed")
     return o.reshape(out_shape), ST
@@ -162,10 +166,12 @@ def decode(q, k, v, g, eta, eps, S, nthreads=0, beta_mode="kaczmarz", normalize_
     """One tokenwise fp64 step per sequence.
 
     q, k: [B, H, d_k]; v: [B, H, d_v]; g, eta: [B, H]; S: [B, H, d_k, d_v].
+    g: [B, H, d_k] instead for diagonal gating (shaped like k).
     Variants as in prefill (pos_offset [B]: this token is at position pos_offset + 1).
     Returns (o [B, H, d_v], S_new [B, H, d_k, d_v]) as float64 numpy arrays.
     """
     q, k, v, g, eta, S = (_f64(x) for x in (q, k, v, g, eta, S))
+    gdiag = g.shape == q.shape
     B, H, dk = q.shape
     dv = v.shape[-1]
     o = np.empty((B, H, dv), dtype=np.float64)
@@ -174,7 +180,8 @@ def decode(q, k, v, g, eta, eps, S, nthreads=0, beta_mode="kaczmarz", normalize_
     rc = _load().kla_oracle_decode_v(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S), B, H, dk, dv,
         _ptr(o), _ptr(Sn), int(nthreads), _mode(beta_mode), 1 if normalize_q else 0,
-        None if po is None else po.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        None if po is None else po.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        1 if gdiag else 0)
     if rc != 0:
         raise RuntimeError("kla_oracle_decode failed")
     return o, Sn

@@ -94,3 +94,61 @@ def prefill(q, k, v, g, eta, eps, S0=None, cu_seqlens=None, chunk=64):
                 inter[(n, h, c)] = dict(b=b, G=G, T=T)
             ST[n, h] = S
     return o, ST, inter
+
+
+# ------------------------------------------------------------------ diagonal gating
+# Appendix B.5 ("Extension to diagonal gating"): with D_t = Diag(alpha_t), the scalar gamma
+# of Propositions 3-4 becomes a vector per token and every decay product acts per key
+# channel.  Working the chunk through the same way (row-vector convention, G the per-channel
+# chunk-local cumulative log-decay, C x d_k):
+#     A_ij  = sum_c k_i[c] k_j[c] exp(G_i[c] - G_j[c])      (j < i)
+#     L     = Diag(b) A                                      strictly lower triangular
+#     (I + L) U = Diag(b) (V - (K o exp(G)) S0)
+#     P_ij  = sum_c q_i[c] k_j[c] exp(G_i[c] - G_j[c])      (j <= i)
+#     O     = (Q o exp(G)) S0 + P U
+#     S_out = Diag(exp(G_C)) S0 + (K o exp(G_C - G))^T U
+# Every exponent is a difference G_i - G_j with j <= i, or G_C - G_j, so none is positive.
+
+
+def chunk_step_diag(S0, q, k, v, g, eta, eps):
+    """One chunk of one head under diagonal gating: returns (O, S_out, b, G, T) in fp64.
+
+    S0 [d_k, d_v]; q, k [C, d_k]; v [C, d_v]; g [C, d_k]; eta [C].
+    """
+    C = k.shape[0]
+    b = _beta(k, eta, eps)
+    G = np.cumsum(g, axis=0)                                  # [C, d_k]
+    D = G[:, None, :] - G[None, :, :]                         # D[i, j, c] = G_i[c] - G_j[c]
+    lower = np.tril(np.ones((C, C), dtype=bool))
+    E = np.where(lower[:, :, None], np.exp(np.where(lower[:, :, None], D, 0.0)), 0.0)
+    A = np.einsum("ic,jc,ijc->ij", k, k, E)
+    L = b[:, None] * np.tril(A, -1)
+    rhs = b[:, None] * (v - (k * np.exp(G)) @ S0)
+    U = _forward_substitution(L, rhs)
+    P = np.einsum("ic,jc,ijc->ij", q, k, E)
+    O = (q * np.exp(G)) @ S0 + P @ U
+    S_out = np.exp(G[-1])[:, None] * S0 + (k * np.exp(G[-1][None, :] - G)).T @ U
+    T = _forward_substitution(L, np.diag(b))
+    return O, S_out, b, G, T
+
+
+def prefill_diag(q, k, v, g, eta, eps, S0=None, cu_seqlens=None, chunk=64):
+    """Chunkwise fp64 prefill under diagonal gating (g [n_tok, H, d_k]); as prefill."""
+    q, k, v, g, eta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, eta))
+    n_tok, H, dk = q.shape
+    dv = v.shape[-1]
+    cu = np.array([0, n_tok]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    ns = len(cu) - 1
+    S0 = np.zeros((ns, H, dk, dv)) if S0 is None else np.asarray(S0, dtype=np.float64)
+    o = np.zeros((n_tok, H, dv))
+    ST = np.zeros((ns, H, dk, dv))
+    for n in range(ns):
+        for h in range(H):
+            S = S0[n, h].copy()
+            for t0 in range(int(cu[n]), int(cu[n + 1]), chunk):
+                t1 = min(t0 + chunk, int(cu[n + 1]))
+                O, S, _, _, _ = chunk_step_diag(S, q[t0:t1, h], k[t0:t1, h], v[t0:t1, h],
+                                                g[t0:t1, h], eta[t0:t1, h], eps)
+                o[t0:t1, h] = O
+            ST[n, h] = S
+    return o, ST

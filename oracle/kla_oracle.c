@@ -31,6 +31,10 @@
  *                 "sequence factor"; the second factor is printed without its
  *                 root in the extracted text and read as 1/sqrt(t))
  *   normq   o_t = q_t S_t / ||q_t||_2 (s.3.3, Algorithm 1 step 6), 0 for q_t = 0
+ *   gdiag   diagonal gating (Appendix B.5, "Extension to diagonal gating"): the decay is
+ *           Diag(alpha_t) with one log-decay g_t[i] per key channel i, so the forget step
+ *           scales row i of the state by exp(g_t[i]); everything else, the coefficient
+ *           included, is unchanged (the appendix keeps the Kaczmarz coefficient as is)
  *
  * Readings of points the pages leave open:
  *   - if ||k_t||^2 + eps == 0 the step is b_t = 0 (no write): the constraint
@@ -51,16 +55,18 @@
 #endif
 
 /* One tokenwise step on one head's state S (dk x dv, row-major, d_v fastest) at
- * absolute position t (1-based).  r is caller scratch of length dv.  Writes o
+ * absolute position t (1-based).  g points to the token's log-decay: one value, or dk
+ * values (one per state row) when gdiag.  r is caller scratch of length dv.  Writes o
  * (length dv) if o != NULL. */
 static void kla_oracle_token(double *S, const double *q, const double *k,
-                             const double *v, double g, double eta, double eps,
+                             const double *v, const double *g, double eta, double eps,
                              int dk, int dv, double *r, double *o, int mode,
-                             int normq, double t) {
-  const double a = exp(g);
-  /* S~ = a S */
-  for (int i = 0; i < dk; ++i)
+                             int normq, double t, int gdiag) {
+  /* S~ = a S, or Diag(a) S */
+  for (int i = 0; i < dk; ++i) {
+    const double a = exp(gdiag ? g[i] : g[0]);
     for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;
+  }
   /* e = v - k S~ */
   for (int j = 0; j < dv; ++j) {
     double acc = 0.0;
@@ -106,6 +112,7 @@ static void kla_oracle_token(double *S, const double *q, const double *k,
 /*
  * Prefill: run the recurrence over every token of every sequence.
  *   q, k   [n_tok, H, dk]      v, o [n_tok, H, dv]      g, eta [n_tok, H]
+ *          (g [n_tok, H, dk] when gdiag)
  *   S0     [n_seq, H, dk, dv]  (NULL = zeros)          S_T   [n_seq, H, dk, dv]
  *   cu     [n_seq + 1] token offsets of the packed sequences (cu[0] = 0).
  *   nthreads <= 0 uses the OpenMP default.
@@ -115,7 +122,7 @@ int kla_oracle_prefill_v(const double *q, const double *k, const double *v,
                          const double *g, const double *eta, double eps,
                          const double *S0, const int64_t *cu, int n_seq, int H,
                          int dk, int dv, double *o, double *S_T, int nthreads,
-                         int mode, int normq, const int64_t *pos_offset) {
+                         int mode, int normq, const int64_t *pos_offset, int gdiag) {
   if (!q || !k || !v || !g || !eta || !cu || !o || !S_T) return -1;
   if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   const long pairs = (long)n_seq * H;
@@ -138,9 +145,10 @@ int kla_oracle_prefill_v(const double *q, const double *k, const double *v,
     const int64_t base = pos_offset ? pos_offset[n] : 0;
     for (int64_t t = cu[n]; t < cu[n + 1]; ++t) {
       const size_t th = (size_t)t * H + h;
-      kla_oracle_token(S, q + th * dk, k + th * dk, v + th * dv, g[th], eta[th],
-                       eps, dk, dv, r, o + th * dv, mode, normq,
-                       (double)(base + (t - cu[n]) + 1));
+      kla_oracle_token(S, q + th * dk, k + th * dk, v + th * dv,
+                       gdiag ? g + th * dk : g + th, eta[th], eps, dk, dv, r,
+                       o + th * dv, mode, normq, (double)(base + (t - cu[n]) + 1),
+                       gdiag);
     }
     free(r);
   }
@@ -153,19 +161,20 @@ int kla_oracle_prefill(const double *q, const double *k, const double *v,
                        const double *S0, const int64_t *cu, int n_seq, int H,
                        int dk, int dv, double *o, double *S_T, int nthreads) {
   return kla_oracle_prefill_v(q, k, v, g, eta, eps, S0, cu, n_seq, H, dk, dv, o,
-                              S_T, nthreads, 0, 0, NULL);
+                              S_T, nthreads, 0, 0, NULL, 0);
 }
 
 /*
  * Decode: one token per sequence, B sequences, state updated in S_new.
  *   q, k [B, H, dk]   v, o [B, H, dv]   g, eta [B, H]   S, S_new [B, H, dk, dv]
+ *   (g [B, H, dk] when gdiag)
  * S_new may equal S.
  */
 int kla_oracle_decode_v(const double *q, const double *k, const double *v,
                         const double *g, const double *eta, double eps,
                         const double *S, int B, int H, int dk, int dv, double *o,
                         double *S_new, int nthreads, int mode, int normq,
-                        const int64_t *pos_offset) {
+                        const int64_t *pos_offset, int gdiag) {
   if (!q || !k || !v || !g || !eta || !S || !o || !S_new) return -1;
   if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   const long pairs = (long)B * H;
@@ -184,8 +193,8 @@ int kla_oracle_decode_v(const double *q, const double *k, const double *v,
       memcpy(Sp, S + (size_t)p * dk * dv, sizeof(double) * (size_t)dk * dv);
     const double t = (double)((pos_offset ? pos_offset[p / H] : 0) + 1);
     kla_oracle_token(Sp, q + (size_t)p * dk, k + (size_t)p * dk,
-                     v + (size_t)p * dv, g[p], eta[p], eps, dk, dv, r,
-                     o + (size_t)p * dv, mode, normq, t);
+                     v + (size_t)p * dv, gdiag ? g + (size_t)p * dk : g + p, eta[p],
+                     eps, dk, dv, r, o + (size_t)p * dv, mode, normq, t, gdiag);
     free(r);
   }
   return failed ? -1 : 0;
@@ -197,7 +206,7 @@ int kla_oracle_decode(const double *q, const double *k, const double *v,
                       const double *S, int B, int H, int dk, int dv, double *o,
                       double *S_new, int nthreads) {
   return kla_oracle_decode_v(q, k, v, g, eta, eps, S, B, H, dk, dv, o, S_new,
-                             nthreads, 0, 0, NULL);
+                             nthreads, 0, 0, NULL, 0);
 }
 
 /* Threads the OpenMP runtime would use (for reporting the CPU baseline). */
