@@ -75,6 +75,8 @@ def load_library():
                                     ctypes.c_int, vp]
     lib.kla_decode_step.restype = ctypes.c_int
     opt_p = ctypes.POINTER(KlaOptions)
+    lib.kla_prefill_workspace_bytes_ex.argtypes = [i32, i32, i32, i32, i32, opt_p]
+    lib.kla_prefill_workspace_bytes_ex.restype = sz
     lib.kla_prefill_chunked_ex.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i32,
                                            i32, i32, i32, ctypes.c_int, vp, sz, opt_p, vp]
     lib.kla_prefill_chunked_ex.restype = ctypes.c_int
@@ -100,24 +102,26 @@ BETA_MODES = {"kaczmarz": 0, "gated": 1, "key_norm": 2, "inv_t": 3, "inv_sqrt_t"
 
 
 class KlaOptions(ctypes.Structure):
-    """Mirror of ``kla_options``: the write-coefficient mode, the normalised readout and the
-    per-sequence position offsets (device int32 or NULL)."""
+    """Mirror of ``kla_options``: the write-coefficient mode, the normalised readout, the
+    per-sequence position offsets (device int32 or NULL) and the diagonal gate."""
     _fields_ = [("beta_mode", ctypes.c_int32), ("normalize_q", ctypes.c_int32),
-                ("pos_offset", ctypes.c_void_p)]
+                ("pos_offset", ctypes.c_void_p), ("diagonal_gate", ctypes.c_int32)]
 
 
-def _options(beta_mode, normalize_q, pos_offset, n_rows, dev):
+def _options(beta_mode, normalize_q, pos_offset, n_rows, dev, diagonal_gate=False):
     """ctypes pointer to a KlaOptions (None = the defaults).  beta_mode is a name from
-    BETA_MODES or its integer code; pos_offset an int32 device tensor of n_rows entries."""
+    BETA_MODES or its integer code; pos_offset an int32 device tensor of n_rows entries;
+    diagonal_gate: g holds one log-decay per key channel."""
     mode = BETA_MODES[beta_mode] if isinstance(beta_mode, str) else int(beta_mode)
-    if mode == 0 and not normalize_q and pos_offset is None:
+    if mode == 0 and not normalize_q and pos_offset is None and not diagonal_gate:
         return None
     if pos_offset is not None:
         _need(pos_offset, "pos_offset", torch.int32, dev)
         if pos_offset.numel() != n_rows:
             raise ValueError(f"pos_offset must have {n_rows} entries")
     return ctypes.pointer(KlaOptions(mode, 1 if normalize_q else 0,
-                                     None if pos_offset is None else pos_offset.data_ptr()))
+                                     None if pos_offset is None else pos_offset.data_ptr(),
+                                     1 if diagonal_gate else 0))
 
 
 def _check(status: int):
@@ -149,8 +153,12 @@ def _need(t, name, dtype=None, device=None):
 
 
 def kla_prefill_workspace_bytes(n_seq: int, total_tokens: int, n_heads: int, d_k: int,
-                                d_v: int) -> int:
-    return int(load_library().kla_prefill_workspace_bytes(n_seq, total_tokens, n_heads, d_k, d_v))
+                                d_v: int, diagonal_gate: bool = False) -> int:
+    """Workspace bytes a prefill of this size needs (0 for unsupported sizes); diagonal_gate
+    sizes it for the diagonal-gated variant."""
+    opts = ctypes.pointer(KlaOptions(0, 0, None, 1)) if diagonal_gate else None
+    return int(load_library().kla_prefill_workspace_bytes_ex(n_seq, total_tokens, n_heads, d_k,
+                                                             d_v, opts))
 
 
 def _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq):
@@ -161,7 +169,8 @@ def _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq):
         B, T = q.shape[:2]
         n_seq = B
         q, k, v = (x.reshape(B * T, *x.shape[2:]) for x in (q, k, v))
-        g, eta = (x.reshape(B * T, x.shape[-1]) for x in (g, eta))
+        g = g.reshape(B * T, *g.shape[2:])
+        eta = eta.reshape(B * T, eta.shape[-1])
     elif q.dim() != 3:
         raise ValueError("q must be [n_tok, H, d_k] or [B, T, H, d_k]")
     if n_seq is None:
@@ -176,7 +185,8 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
     """Chunkwise KLA prefill (paper section 4, Eq. (7)-(9); chunk = 64 tokens).
 
     q, k: [n_tok, H, d_k] or [B, T, H, d_k] (fp32 or bf16); v like q with d_v;
-    g, eta: [n_tok, H] / [B, T, H] fp32; S0: [n_seq, H, d_k, d_v] fp32 or None;
+    g, eta: [n_tok, H] / [B, T, H] fp32 (a g shaped like k selects diagonal gating: one
+    log-decay per key channel, paper Appendix B.5); S0: [n_seq, H, d_k, d_v] fp32 or None;
     cu_seqlens: int32 device [n_seq + 1] for packed sequences, or None (dense;
     n_seq sequences of equal length).  Returns (o, S_T); S_T is None when
     output_final_state is False.  Pass S_T=S0 to update the state in place.
@@ -195,7 +205,9 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
     _need(eta, "eta", torch.float32, dev)
     n_tok, H, d_k = q.shape
     d_v = v.shape[-1]
-    if k.shape != q.shape or v.shape[:2] != (n_tok, H) or g.shape != (n_tok, H) or eta.shape != (n_tok, H):
+    diag = tuple(g.shape) == (n_tok, H, d_k)
+    if (k.shape != q.shape or v.shape[:2] != (n_tok, H) or (g.shape != (n_tok, H) and not diag)
+            or eta.shape != (n_tok, H)):
         raise ValueError("inconsistent q/k/v/g/eta shapes")
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
@@ -217,11 +229,11 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
     if S_T is not None:
         _need(S_T, "S_T", torch.float32, dev)
     lib = load_library()
-    ws_bytes = int(lib.kla_prefill_workspace_bytes(n_seq, n_tok, H, d_k, d_v))
+    opts = _options(beta_mode, normalize_q, pos_offset, n_seq, dev, diagonal_gate=diag)
+    ws_bytes = int(lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, d_k, d_v, opts))
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     host_ptr = None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr())
-    opts = _options(beta_mode, normalize_q, pos_offset, n_seq, dev)
     _check(lib.kla_prefill_chunked_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S0), _ptr(o), _ptr(S_T),
         _ptr(cu_seqlens), host_ptr, n_seq, n_tok, H, d_k, d_v, _DTYPES[dt], _ptr(workspace),
@@ -279,6 +291,7 @@ def kla_decode_step(q, k, v, g, eta, eps: float, S, *, o=None, S_new=None, inpla
 
     q, k: [B, H, d_k]; v: [B, H, d_v] (fp32 or bf16); g, eta: [B, H] fp32;
     S: [B, H, d_k, d_v] fp32.  Returns (o, S_new); inplace=True writes S' into S.
+    A g shaped like k ([B, H, d_k]) selects diagonal gating (one log-decay per key channel).
     Variants as in kla_prefill_chunked (pos_offset: int32 [B], this token is at
     position pos_offset + 1).
     """
@@ -294,7 +307,8 @@ def kla_decode_step(q, k, v, g, eta, eps: float, S, *, o=None, S_new=None, inpla
     _need(S, "S", torch.float32, dev)
     B, H, d_k = q.shape
     d_v = v.shape[-1]
-    if S.shape != (B, H, d_k, d_v) or g.shape != (B, H) or eta.shape != (B, H):
+    diag = tuple(g.shape) == (B, H, d_k)
+    if S.shape != (B, H, d_k, d_v) or (g.shape != (B, H) and not diag) or eta.shape != (B, H):
         raise ValueError("inconsistent decode shapes")
     if o is None:
         o = torch.empty((B, H, d_v), dtype=dt, device=dev)
@@ -303,7 +317,7 @@ def kla_decode_step(q, k, v, g, eta, eps: float, S, *, o=None, S_new=None, inpla
     elif S_new is None:
         S_new = torch.empty_like(S)
     _need(S_new, "S_new", torch.float32, dev)
-    opts = _options(beta_mode, normalize_q, pos_offset, B, dev)
+    opts = _options(beta_mode, normalize_q, pos_offset, B, dev, diagonal_gate=diag)
     _check(load_library().kla_decode_step_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S), _ptr(o), _ptr(S_new),
         B, H, d_k, d_v, _DTYPES[dt], opts, _stream(dev)))

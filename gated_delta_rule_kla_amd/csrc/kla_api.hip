@@ -49,10 +49,15 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 // each part 256-byte aligned and T, P sized for fp32 (the scan reads them in the operand
 // type).
 struct WsLayout {
-  size_t off_cu, off_co, off_G, off_GD, off_T, off_P, total;
+  size_t off_cu, off_co, off_G, off_GD, off_T, off_P;
+  // diagonal gating only: per chunk-head the decayed key and query tiles K o exp(G),
+  // Q o exp(G), K o exp(G_last - G) ([64][d_k] each, operand type) and exp(G_last) ([d_k])
+  size_t off_KG = 0, off_QG = 0, off_KD = 0, off_GC = 0;
+  size_t total;
 };
 
-WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H) {
+WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k = 0,
+                   bool diag = false) {
   WsLayout w;
   w.off_cu = 0;
   w.off_co = align256(w.off_cu + sizeof(int32_t) * (size_t)(n_seq + 1));
@@ -63,6 +68,14 @@ WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H) {
   const size_t tile_bytes = sizeof(float) * (size_t)nch * (size_t)H * KLA_CHUNK * KLA_CHUNK;
   w.off_P = align256(w.off_T + tile_bytes);
   w.total = align256(w.off_P + tile_bytes);
+  if (diag) {
+    const size_t kt = sizeof(float) * (size_t)nch * (size_t)H * KLA_CHUNK * (size_t)d_k;
+    w.off_KG = w.total;
+    w.off_QG = align256(w.off_KG + kt);
+    w.off_KD = align256(w.off_QG + kt);
+    w.off_GC = align256(w.off_KD + kt);
+    w.total = align256(w.off_GC + sizeof(float) * (size_t)nch * (size_t)H * (size_t)d_k);
+  }
   return w;
 }
 
@@ -119,7 +132,8 @@ kla_status to_coef(const kla_options *opts, kla::CoefOpts *out) {
     return fail(KLA_ERR_UNSUPPORTED, "unknown beta_mode %d", (int)opts->beta_mode);
   if (opts->pos_offset && !aligned_to(opts->pos_offset, 4))
     return fail(KLA_ERR_INVALID_ARGUMENT, "pos_offset must be 4-byte aligned");
-  *out = kla::CoefOpts{opts->beta_mode, opts->normalize_q != 0 ? 1 : 0, opts->pos_offset};
+  *out = kla::CoefOpts{opts->beta_mode, opts->normalize_q != 0 ? 1 : 0, opts->pos_offset,
+                       opts->diagonal_gate != 0 ? 1 : 0};
   return KLA_OK;
 }
 
@@ -139,6 +153,13 @@ size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t 
   return ws_layout(n_seq, total_tokens, n_heads).total;
 }
 
+size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                                      int32_t d_k, int32_t d_v, const kla_options *opts) {
+  if (n_seq <= 0 || total_tokens < 0 || n_heads <= 0 || !supported_dk(d_k) || !supported_dv(d_v))
+    return 0;
+  return ws_layout(n_seq, total_tokens, n_heads, d_k, opts && opts->diagonal_gate != 0).total;
+}
+
 }  // extern "C"
 
 namespace {
@@ -151,7 +172,7 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
                               const int32_t *cu_seqlens_host, int32_t n_seq, int32_t total_tokens,
                               int32_t n_heads, int32_t d_k, int32_t d_v, kla_dtype dtype,
                               const void *workspace, size_t workspace_bytes, bool need_prep,
-                              bool need_scan, bool check_tables = true) {
+                              bool need_scan, bool check_tables = true, bool diag = false) {
   kla_status st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v,
                                       dtype, eps);
   if (st != KLA_OK) return st;
@@ -174,7 +195,7 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
   const size_t nS = (size_t)n_seq * n_heads * d_k * d_v * sizeof(float);
   if (S_T && S_T != S0 && overlap(S_T, nS, S0, nS))
     return fail(KLA_ERR_INVALID_ARGUMENT, "S_T may equal S0 but must not partially overlap it");
-  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads);
+  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads, d_k, diag);
   if (!workspace || workspace_bytes < w.total)
     return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -187,15 +208,36 @@ struct WsViews {
   kla::SeqTables tabs;
   float *G, *GD;
   void *T, *P;
+  kla::DiagTiles diag;  // diagonal gating only
 };
 
-WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n_heads) {
-  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads);
+WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                 int32_t d_k = 0, bool diag = false) {
+  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads, d_k, diag);
   char *ws = static_cast<char *>(workspace);
-  return WsViews{{reinterpret_cast<int32_t *>(ws + w.off_cu),
-                  reinterpret_cast<int32_t *>(ws + w.off_co)},
-                 reinterpret_cast<float *>(ws + w.off_G), reinterpret_cast<float *>(ws + w.off_GD),
-                 ws + w.off_T, ws + w.off_P};
+  WsViews v{{reinterpret_cast<int32_t *>(ws + w.off_cu),
+             reinterpret_cast<int32_t *>(ws + w.off_co)},
+            reinterpret_cast<float *>(ws + w.off_G), reinterpret_cast<float *>(ws + w.off_GD),
+            ws + w.off_T, ws + w.off_P, {nullptr, nullptr, nullptr, nullptr}};
+  if (diag)
+    v.diag = kla::DiagTiles{ws + w.off_KG, ws + w.off_QG, ws + w.off_KD,
+                            reinterpret_cast<float *>(ws + w.off_GC)};
+  return v;
+}
+
+// Diagonal gating: the plan kernel writes the sequence tables, then the per-chunk stage.
+kla_status enqueue_prepare_diag(const void *q, const void *k, const float *g, const float *eta,
+                                float eps, const kla::CoefOpts &opts, const int32_t *cu_seqlens,
+                                int32_t n_seq, int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                                kla_dtype dtype, void *workspace, hipStream_t s) {
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, true);
+  const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
+  kla_status st =
+      hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan");
+  if (st != KLA_OK) return st;
+  return hip_status(kla::launch_prep_diag(to_dt(dtype), d_k, q, k, g, eta, eps, opts, wv.tabs,
+                                          n_seq, nch_ub, n_heads, wv.diag, wv.T, wv.P, wv.GD, s),
+                    "prep (diagonal gate)");
 }
 
 kla_status enqueue_prepare(const void *q, const void *k, const float *g, const float *eta, float eps,
@@ -222,10 +264,13 @@ kla_status enqueue_prepare(const void *q, const void *k, const float *g, const f
 
 kla_status enqueue_scan(const void *q, const void *k, const void *v, const float *S0, void *o,
                         float *S_T, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
-                        int32_t d_k, int32_t d_v, kla_dtype dtype, void *workspace, hipStream_t s) {
-  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
+                        int32_t d_k, int32_t d_v, kla_dtype dtype, void *workspace, hipStream_t s,
+                        bool diag = false) {
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, diag);
   return hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0, o,
-                                     S_T, wv.tabs, n_seq, n_heads, s), "scan");
+                                     S_T, wv.tabs, n_seq, n_heads, s,
+                                     diag ? &wv.diag : nullptr),
+                    "scan");
 }
 
 }  // namespace
@@ -239,19 +284,25 @@ kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, c
                                   int32_t total_tokens, int32_t n_heads, int32_t d_k,
                                   int32_t d_v, kla_dtype dtype, void *workspace,
                                   size_t workspace_bytes, const kla_options *opts, void *stream) {
-  kla_status st = check_prefill_args(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
-                                     n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
-                                     workspace_bytes, true, true);
-  if (st != KLA_OK) return st;
   kla::CoefOpts co;
-  if ((st = to_coef(opts, &co)) != KLA_OK) return st;
+  kla_status st = to_coef(opts, &co);
+  if (st != KLA_OK) return st;
+  const bool diag = co.diag_gate != 0;
+  if ((st = check_prefill_args(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
+                               n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
+                               workspace_bytes, true, true, true, diag)) != KLA_OK)
+    return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear any stale error from unrelated work
-  if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
-                            dtype, workspace, s)) != KLA_OK)
-    return st;
+  if (diag)
+    st = enqueue_prepare_diag(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads,
+                              d_k, dtype, workspace, s);
+  else
+    st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
+                         dtype, workspace, s);
+  if (st != KLA_OK) return st;
   if ((st = enqueue_scan(q, k, v, S0, o, S_T, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
-                         workspace, s)) != KLA_OK)
+                         workspace, s, diag)) != KLA_OK)
     return st;
   return ok();
 }
@@ -282,6 +333,9 @@ kla_status kla_prefill_prepare_ex(const void *q, const void *k, const float *g,
     return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, g and eta are required");
   kla::CoefOpts co;
   if ((st = to_coef(opts, &co)) != KLA_OK) return st;
+  if (co.diag_gate)
+    return fail(KLA_ERR_UNSUPPORTED,
+                "a diagonal-gated prefill runs through kla_prefill_chunked_ex only");
   (void)hipGetLastError();
   if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
                             dtype, workspace, static_cast<hipStream_t>(stream))) != KLA_OK)

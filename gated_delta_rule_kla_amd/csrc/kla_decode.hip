@@ -11,12 +11,16 @@
 // independent given k, q and the scalars, so a (sequence, head) is split over NS workgroups of
 // NT lanes, each taking d_v / NS columns; each lane owns float4 column groups of a few state
 // rows, so every load and store is a coalesced 16-byte access.
+//
+// Diagonal gating (GDIAG; paper Appendix B.5): the decay is Diag(a) with a_i = exp(g_i) per
+// key channel, so the forgotten state is Diag(a) S and, with the same substitution,
+//   r = (k o a) S,  p = (q o a) S,  e = v - r,  S' = Diag(a) S + b k^T e,  o = p + b (q . k) e.
 #include "kla_device.h"
 #include "kla_launch.h"
 
 namespace kla {
 
-template <typename Tin, int DK, int DV, int NS, int NT>
+template <typename Tin, int DK, int DV, int NS, int NT, bool GDIAG>
 __global__ __launch_bounds__(NT) void kla_decode_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ eta, float eps, CoefOpts opts,
@@ -28,6 +32,7 @@ __global__ __launch_bounds__(NT) void kla_decode_kernel(
   constexpr int NW = NT / 64;       // wavefronts
   static_assert(NC4 >= 1 && RPP * NC4 == NT && NP * RPP == DK && NT >= DK, "decode tiling");
   __shared__ float sk[DK], sq[DK];
+  __shared__ float sa[GDIAG ? DK : 1], ska[GDIAG ? DK : 1], sqa[GDIAG ? DK : 1];
   __shared__ f32x4 red_r[RPP][NC4], red_p[RPP][NC4];
   __shared__ float sred[3][NW];
 
@@ -49,6 +54,12 @@ __global__ __launch_bounds__(NT) void kla_decode_kernel(
     qf = to_f32(q[bh * DK + tid]);
     sk[tid] = kf;
     sq[tid] = qf;
+    if constexpr (GDIAG) {
+      const float ai = __expf(g[bh * DK + tid]);
+      sa[tid] = ai;
+      ska[tid] = kf * ai;
+      sqa[tid] = qf * ai;
+    }
   }
   const float kk = wave_sum(kf * kf), qk = wave_sum(qf * kf);
   const float qq = opts.normalize_q ? wave_sum(qf * qf) : 0.f;
@@ -59,8 +70,13 @@ __global__ __launch_bounds__(NT) void kla_decode_kernel(
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp) {
     const int row = pp * RPP + rg;
-    r += sk[row] * s[pp];
-    p += sq[row] * s[pp];
+    if constexpr (GDIAG) {
+      r += ska[row] * s[pp];
+      p += sqa[row] * s[pp];
+    } else {
+      r += sk[row] * s[pp];
+      p += sq[row] * s[pp];
+    }
   }
   red_r[rg][c4] = r;
   red_p[rg][c4] = p;
@@ -76,7 +92,7 @@ __global__ __launch_bounds__(NT) void kla_decode_kernel(
     qk_all += sred[1][w];
     qq_all += sred[2][w];
   }
-  const float a = __expf(g[bh]);
+  const float a = GDIAG ? 1.f : __expf(g[bh]);  // the diagonal decay is inside r, p and sa
   const float den = kk_all + eps;
   const int brow = (int)(bh / H);
   const float t_abs = (float)(1 + (opts.pos_offset ? opts.pos_offset[brow] : 0));
@@ -97,7 +113,8 @@ __global__ __launch_bounds__(NT) void kla_decode_kernel(
   for (int pp = 0; pp < NP; ++pp) {
     const int row = pp * RPP + rg;
     const float bk = beta * sk[row];
-    __builtin_nontemporal_store(a * s[pp] + bk * e, &Sn[row * RS4 + c4]);
+    const float ar = GDIAG ? sa[row] : a;
+    __builtin_nontemporal_store(ar * s[pp] + bk * e, &Sn[row * RS4 + c4]);
   }
 }
 
@@ -118,12 +135,23 @@ static hipError_t launch_decode_t(const void *q, const void *k, const void *v, c
   const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
   const Tin *vt = static_cast<const Tin *>(v);
   Tin *ot = static_cast<Tin *>(o);
-  if (items < kDecodeSplitBelow)
-    hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 2, 128>), dim3((unsigned)(2 * items)),
-                       dim3(128), 0, stream, qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
-  else
-    hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 1, 512>), dim3((unsigned)items),
-                       dim3(512), 0, stream, qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
+  const bool small = items < kDecodeSplitBelow;
+  const dim3 grid((unsigned)(small ? 2 * items : items)), block(small ? 128 : 512);
+  if (opts.diag_gate) {
+    if (small)
+      hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 2, 128, true>), grid, block, 0, stream,
+                         qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
+    else
+      hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 1, 512, true>), grid, block, 0, stream,
+                         qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
+  } else {
+    if (small)
+      hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 2, 128, false>), grid, block, 0, stream,
+                         qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
+    else
+      hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 1, 512, false>), grid, block, 0, stream,
+                         qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
+  }
   return hipGetLastError();
 }
 

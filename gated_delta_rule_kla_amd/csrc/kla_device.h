@@ -202,6 +202,7 @@ struct CoefOpts {
   int beta_mode;            // BetaMode
   int normalize_q;          // nonzero: o_t = q_t S_t / ||q_t||
   const int32_t *pos_offset;  // per sequence (prefill) or batch row (decode); may be null
+  int diag_gate = 0;        // nonzero: g holds one log-decay per key channel
 };
 
 // b_t from eta_t, den = ||k_t||^2 + eps and the absolute position t >= 1; a zero

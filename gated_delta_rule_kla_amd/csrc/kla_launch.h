@@ -54,16 +54,33 @@ hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const fl
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
                        const PlanArgs &pa, hipStream_t stream);
 
+// Diagonal gating: the decayed key and query tiles per chunk-head ([64][d_k] each, operand
+// type) K o exp(G), Q o exp(G), K o exp(G_last - G), and exp(G_last) ([d_k] fp32).
+struct DiagTiles {
+  const void *kg, *qg, *kd;
+  const float *gc;
+};
+
+// a1 + a2 under diagonal gating (g [n_tok, H, d_k]): b, T and P (packed blocks), unit decays
+// with the readout factor in GD, and the decayed tiles.  Reads the tables launch_plan wrote.
+hipError_t launch_prep_diag(Dtype dt, int d_k, const void *q, const void *k, const float *g,
+                            const float *eta, float eps, const CoefOpts &opts, SeqTables t,
+                            int32_t n_seq, int64_t n_chunks_ub, int32_t H, const DiagTiles &tiles,
+                            void *T_out, void *P_out, float *GD_out, hipStream_t stream);
+
 // Optional WY factors W = T Diag(exp G) K and U~ = T V (unit-check path).
 hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, const float *G,
                      const float *T, SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                      float *W, float *Ut, hipStream_t stream);
 
 // a3 + a4: sequential chunk scan with the output fused in; reads T, P and the per-chunk
-// decays GD that launch_prep wrote.
+// decays GD that launch_prep wrote.  With diag (non-null), the diagonal-gated scan: K and Q
+// come from the decayed tiles, the state update uses K o exp(G_last - G) and the state decays
+// by exp(G_last) per key channel.
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                        const float *GD, const void *T, const void *P, const float *S0, void *o,
-                       float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream);
+                       float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream,
+                       const DiagTiles *diag = nullptr);
 
 // a5: one decode step.
 hipError_t launch_decode(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,

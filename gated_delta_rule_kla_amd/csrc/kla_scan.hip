@@ -134,57 +134,63 @@ __device__ __forceinline__ int tmap(int t, int a, int i) {
 }
 
 // ---- LDS layout
-template <typename Tin, int DK, int BV>
+template <typename Tin, int DK, int BV, bool DIAG>
 struct ScanSlot {
-  alignas(16) unsigned char K[kChunk * DK * sizeof(Tin)];
-  alignas(16) unsigned char Q[kChunk * DK * sizeof(Tin)];
+  alignas(16) unsigned char K[kChunk * DK * sizeof(Tin)];  // K, or K o exp(G) (DIAG)
+  alignas(16) unsigned char Q[kChunk * DK * sizeof(Tin)];  // Q, or Q o exp(G) (DIAG)
   alignas(16) unsigned char T[tpc_bytes<Tin>()];  // compact tiles (tpc_off)
   alignas(16) unsigned char P[tpc_bytes<Tin>()];
   alignas(16) unsigned char V[kChunk * BV * sizeof(Tin)];
   alignas(16) float gam[kChunk];   // exp(G_i)
   alignas(16) float dec[kChunk];   // exp(G_last - G_i)
   alignas(16) float gamO[kChunk];  // output factor: exp(G_i), over ||q_i|| when normalised
+  // diagonal gating: K o exp(G_last - G) for the state update, exp(G_last) per key channel
+  alignas(16) unsigned char Kd[DIAG ? kChunk * DK * sizeof(Tin) : 16];
+  alignas(16) float gC[DIAG ? DK : 4];
 };
 
-template <typename Tin, int DK, int BV>
+template <typename Tin, int DK, int BV, bool DIAG>
 constexpr int scan_nslot() {
-  constexpr int n = kLdsBytes / (int)sizeof(ScanSlot<Tin, DK, BV>);
+  constexpr int n = kLdsBytes / (int)sizeof(ScanSlot<Tin, DK, BV, DIAG>);
   return n >= 3 ? 3 : n;
 }
 
-template <typename Tin, int DK, int BV>
+template <typename Tin, int DK, int BV, bool DIAG>
 struct ScanSmem {
-  static constexpr int NSLOT = scan_nslot<Tin, DK, BV>();
-  ScanSlot<Tin, DK, BV> slot[NSLOT];
+  static constexpr int NSLOT = scan_nslot<Tin, DK, BV, DIAG>();
+  ScanSlot<Tin, DK, BV, DIAG> slot[NSLOT];
 };
 
 // Buffer-load-to-LDS instructions per chunk (each moves 64 lanes x 16 bytes).
-template <typename Tin, int DK, typename SHP>
+template <typename Tin, int DK, typename SHP, bool DIAG>
 struct DmaPlan {
   static constexpr int ES = sizeof(Tin);
   static constexpr int NK = kChunk * DK * ES / 1024;                 // per K (and per Q) tile
   static constexpr int NTC = tpc_bytes<Tin>() / 1024;               // per compact T or P tile
   static constexpr int NV = kChunk * SHP::BV * ES / 1024;            // value slice
-  // per producer wave: an equal share of every tile and of the 768-byte decay block
-  static constexpr int PER_WAVE = (2 * NK + 2 * NTC + NV) / SHP::NP + 1;
+  // per producer wave: an equal share of every tile and of the 768-byte decay block, and
+  // under diagonal gating of the K o exp(G_last - G) tile and of exp(G_last)
+  static constexpr int PER_WAVE =
+      (2 * NK + 2 * NTC + NV) / SHP::NP + 1 + (DIAG ? NK / SHP::NP + 1 : 0);
   static_assert(NK % SHP::NP == 0 && (2 * NTC) % SHP::NP == 0 && NV % SHP::NP == 0 &&
-                    768 % (16 * SHP::NP) == 0,
+                    768 % (16 * SHP::NP) == 0 && (DK * 4) % (16 * SHP::NP) == 0,
                 "tiles split over the producer waves");
 };
 
 // One workgroup fills a CU's LDS; its waves run at most two to a SIMD.
-template <typename Tin, int DK, typename SHP>
+template <typename Tin, int DK, typename SHP, bool DIAG>
 __global__ __launch_bounds__(SHP::THREADS)
 __attribute__((amdgpu_waves_per_eu(SHP::THREADS > 256 ? 2 : 1, SHP::THREADS > 256 ? 2 : 1)))
 void kla_scan_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ GD, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
     const float *S0, Tin *__restrict__ o, float *S_T, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_off, int n_seq, int H, int DV) {
+    const int32_t *__restrict__ chunk_off, int n_seq, int H, int DV, const Tin *__restrict__ KG,
+    const Tin *__restrict__ QG, const Tin *__restrict__ KD, const float *__restrict__ GC) {
   constexpr int kBV = SHP::BV, kConsumers = SHP::NC, kScanThreads = SHP::THREADS;
-  using SM = ScanSmem<Tin, DK, kBV>;
-  using SL = ScanSlot<Tin, DK, kBV>;
-  using DP = DmaPlan<Tin, DK, SHP>;
+  using SM = ScanSmem<Tin, DK, kBV, DIAG>;
+  using SL = ScanSlot<Tin, DK, kBV, DIAG>;
+  using DP = DmaPlan<Tin, DK, SHP, DIAG>;
   using FragT = typename Frag<Tin>::type;
   using KQ = std::integral_constant<int, DK>;
   constexpr bool B16 = sizeof(Tin) == 2;
@@ -231,7 +237,8 @@ void kla_scan_kernel(
 #pragma unroll
     for (int j = 0; j < DP::NK / NP; ++j) {
       const int J = NP * j + pw, row = (1024 * J + 16 * lane) / (DK * ES);
-      offK[j] = dma_off(J, DK, H * DK * ES, sw_rows<DK>(row) * (ES / 2));
+      // K and Q rows: token rows of the inputs, or rows of a chunk's decayed tile (DIAG)
+      offK[j] = dma_off(J, DK, (DIAG ? 1 : H) * DK * ES, sw_rows<DK>(row) * (ES / 2));
     }
     // T then P, compact tiles in LDS from packed blocks in memory: item m = NP j + pw is
     // instruction m % NTC of T (m < NTC) or P
@@ -254,11 +261,14 @@ void kla_scan_kernel(
     const int len = min(kChunk, te - t0);
     const size_t tok = (size_t)t0 * H + h;
     const uint32_t kq_bytes = (uint32_t)(((size_t)(len - 1) * H + 1) * DK * ES);
-    const Rsrc rk = make_rsrc(k + tok * DK, kq_bytes);
-    const Rsrc rq = make_rsrc(q + tok * DK, kq_bytes);
+    const size_t ch = (size_t)(cbase + c) * H + h;
+    // the decayed tiles hold all 64 rows, zero past a ragged end
+    const Rsrc rk = DIAG ? make_rsrc(KG + ch * (kChunk * DK), kChunk * DK * ES)
+                         : make_rsrc(k + tok * DK, kq_bytes);
+    const Rsrc rq = DIAG ? make_rsrc(QG + ch * (kChunk * DK), kChunk * DK * ES)
+                         : make_rsrc(q + tok * DK, kq_bytes);
     const Rsrc rv =
         make_rsrc(v + tok * DV + v0, (uint32_t)(((size_t)(len - 1) * H * DV + kBV) * ES));
-    const size_t ch = (size_t)(cbase + c) * H + h;
     const Rsrc rt = make_rsrc(Tm + ch * (kChunk * kChunk), tpb_bytes<Tin>());
     const Rsrc rp = make_rsrc(Pm + ch * (kChunk * kChunk), tpb_bytes<Tin>());
     const Rsrc rg = make_rsrc(GD + ch * kGDFloats, kGDFloats * sizeof(float));
@@ -284,6 +294,15 @@ void kla_scan_kernel(
     constexpr int GDB = 768 / NP;
     if (lane < GDB / 16)
       dma16(rg, reinterpret_cast<unsigned char *>(s.gam) + GDB * pw, GDB * pw + 16 * lane);
+    if constexpr (DIAG) {
+      const Rsrc rkd = make_rsrc(KD + ch * (kChunk * DK), kChunk * DK * ES);
+#pragma unroll
+      for (int j = 0; j < DP::NK / NP; ++j) dma16(rkd, s.Kd + 1024 * (NP * j + pw), offK[j]);
+      constexpr int GCB = DK * 4 / NP;  // this wave's bytes of exp(G_last)
+      const Rsrc rgc = make_rsrc(GC + ch * DK, DK * sizeof(float));
+      if (lane < GCB / 16)
+        dma16(rgc, reinterpret_cast<unsigned char *>(s.gC) + GCB * pw, GCB * pw + 16 * lane);
+    }
   };
 
   // chunk c's outputs, parked in slot s's value tile, back to HBM: 16 bytes per lane per
@@ -409,6 +428,8 @@ void kla_scan_kernel(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) Y[t] = mma(fk[t][ks], Sop[ks], Y[t]);
     }
+    // the state update's K^T: K, or K o exp(G_last - G) under diagonal gating
+    const unsigned char *kt_tile = DIAG ? s.Kd : s.K;
     // ---- reads for the state update: K^T rows = key dims of state tile m, by transpose
     //      reads (source lane r16 of group kg: token 32 ks + 8 kg + (r16 >> 2), + 4 for the
     //      second read; key dims 32 (m >> 1) + 8 (r16 & 3) + 4 (m & 1) .. + 3)
@@ -420,8 +441,8 @@ void kla_scan_kernel(
         if constexpr (B16) {
           const int dk0 = 32 * (m >> 1) + 8 * (r16 & 3) + 4 * (m & 1);
           const int tk = 32 * ks + 8 * kg + (r16 >> 2);
-          const bf16x4 lo = lds_read_tr(s.K + tile_off<Tin, DK>(tk, dk0));
-          const bf16x4 hi = lds_read_tr(s.K + tile_off<Tin, DK>(tk + 4, dk0));
+          const bf16x4 lo = lds_read_tr(kt_tile + tile_off<Tin, DK>(tk, dk0));
+          const bf16x4 hi = lds_read_tr(kt_tile + tile_off<Tin, DK>(tk + 4, dk0));
 #pragma unroll
           for (int i = 0; i < 4; ++i) { fkt[m][ks][i] = lo[i]; fkt[m][ks][i + 4] = hi[i]; }
         } else {
@@ -429,7 +450,7 @@ void kla_scan_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             fkt[m][ks][e] = *reinterpret_cast<const float *>(
-                s.K + tile_off<Tin, DK>(32 * ks + 8 * kg + e, dkr));
+                kt_tile + tile_off<Tin, DK>(32 * ks + 8 * kg + e, dkr));
         }
       }
     // ---- R = V - Diag(gam) Y, U = T R (row tile t needs k-steps ks <= t / 2); (Q S)^T,
@@ -475,7 +496,10 @@ void kla_scan_kernel(
     // ---- S = exp(G_last) S + K^T Diag(dec) U
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      Sacc[m] *= dl;
+      if constexpr (DIAG)  // per key channel: rows tmap(m, kg, 0..3) are consecutive
+        Sacc[m] *= *reinterpret_cast<const f32x4 *>(&s.gC[tmap(m, kg, 0)]);
+      else
+        Sacc[m] *= dl;
       Sacc[m] = mma(fkt[m][0], Udop[0], Sacc[m]);
       Sacc[m] = mma(fkt[m][1], Udop[1], Sacc[m]);
     }
@@ -574,13 +598,13 @@ void kla_scan_kernel(
   }
 }
 
-template <typename Tin, int DK, typename SHP>
+template <typename Tin, int DK, typename SHP, bool DIAG>
 static hipError_t launch_scan_s(int d_v, const void *q, const void *k, const void *v,
                                 const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream) {
-  using SMT = ScanSmem<Tin, DK, SHP::BV>;
-  using SLT = ScanSlot<Tin, DK, SHP::BV>;
+                                hipStream_t stream, const DiagTiles *dg) {
+  using SMT = ScanSmem<Tin, DK, SHP::BV, DIAG>;
+  using SLT = ScanSlot<Tin, DK, SHP::BV, DIAG>;
   static_assert(sizeof(SMT) <= kLdsBytes, "LDS budget");
   static_assert(offsetof(SLT, dec) == offsetof(SLT, gam) + 256 &&
                     offsetof(SLT, gamO) == offsetof(SLT, gam) + 512,
@@ -589,18 +613,21 @@ static hipError_t launch_scan_s(int d_v, const void *q, const void *k, const voi
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP, DIAG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t blocks = (int64_t)n_seq * H * (d_v / SHP::BV);
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK, SHP>), dim3((unsigned)blocks), dim3(SHP::THREADS),
-                     smem, stream, static_cast<const Tin *>(q), static_cast<const Tin *>(k),
-                     static_cast<const Tin *>(v), GD, static_cast<const Tin *>(T),
-                     static_cast<const Tin *>(P), S0, static_cast<Tin *>(o), S_T, t.cu,
-                     t.chunk_off, n_seq, H, d_v);
+  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK, SHP, DIAG>), dim3((unsigned)blocks),
+                     dim3(SHP::THREADS), smem, stream, static_cast<const Tin *>(q),
+                     static_cast<const Tin *>(k), static_cast<const Tin *>(v), GD,
+                     static_cast<const Tin *>(T), static_cast<const Tin *>(P), S0,
+                     static_cast<Tin *>(o), S_T, t.cu, t.chunk_off, n_seq, H, d_v,
+                     static_cast<const Tin *>(dg ? dg->kg : nullptr),
+                     static_cast<const Tin *>(dg ? dg->qg : nullptr),
+                     static_cast<const Tin *>(dg ? dg->kd : nullptr), dg ? dg->gc : nullptr);
   return hipGetLastError();
 }
 
@@ -621,31 +648,47 @@ static int device_cus() {
 // The narrow shape while its grid fits the chip in one wave of workgroups (more of them
 // would only queue behind each other while their staging traffic adds up); the wide shape,
 // which stages each tile once for 64 columns, beyond that.
-template <typename Tin, int DK>
+template <typename Tin, int DK, bool DIAG>
 static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const void *v,
                                 const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream) {
+                                hipStream_t stream, const DiagTiles *dg) {
   const int64_t narrow_blocks = (int64_t)n_seq * H * (d_v / ScanNarrow::BV);
   const int cus = device_cus();
   if (cus > 0 && narrow_blocks > cus)
-    return launch_scan_s<Tin, DK, ScanWide>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
-                                            stream);
-  return launch_scan_s<Tin, DK, ScanNarrow>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
-                                            stream);
+    return launch_scan_s<Tin, DK, ScanWide, DIAG>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq,
+                                                  H, stream, dg);
+  return launch_scan_s<Tin, DK, ScanNarrow, DIAG>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq,
+                                                  H, stream, dg);
+}
+
+template <typename Tin, int DK>
+static hipError_t launch_scan_g(int d_v, const void *q, const void *k, const void *v,
+                                const float *GD, const void *T, const void *P, const float *S0,
+                                void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
+                                hipStream_t stream, const DiagTiles *dg) {
+  if (dg)
+    return launch_scan_t<Tin, DK, true>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
+                                        dg);
+  return launch_scan_t<Tin, DK, false>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
+                                       dg);
 }
 
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                        const float *GD, const void *T, const void *P, const float *S0, void *o,
-                       float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream) {
+                       float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream,
+                       const DiagTiles *dg) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
-      return launch_scan_t<__bf16, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream);
-    return launch_scan_t<__bf16, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream);
+      return launch_scan_g<__bf16, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
+                                        dg);
+    return launch_scan_g<__bf16, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
+                                     dg);
   }
   if (d_k == 128)
-    return launch_scan_t<float, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream);
-  return launch_scan_t<float, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream);
+    return launch_scan_g<float, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
+                                     dg);
+  return launch_scan_g<float, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream, dg);
 }
 
 }  // namespace kla

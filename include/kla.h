@@ -200,8 +200,16 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
  * all zeros) places a call's tokens in their sequences: the first token of
  * sequence n in a prefill call is at position pos_offset[n] + 1, a decode step
  * of batch row b is at position pos_offset[b] + 1.  Only the sequence-factor
- * modes read it.  A NULL kla_options pointer means the defaults (Kaczmarz
- * coefficient, o_t = q_t S_t).  An unknown mode gives KLA_ERR_UNSUPPORTED.
+ * modes read it.  diagonal_gate != 0 selects diagonal gating (paper Appendix
+ * B.5, "Extension to diagonal gating"): the decay is Diag(alpha_t) with one
+ * log-decay per key channel, so g holds d_k values per token-head, laid out
+ * like k ([n_tok, n_heads, d_k] for prefill, [batch, n_heads, d_k] for decode),
+ * and the forget step scales row i of the state by exp(g_t[i]); the coefficient
+ * b_t is unchanged.  A diagonal-gated prefill needs a larger workspace
+ * (kla_prefill_workspace_bytes_ex) and runs through kla_prefill_chunked_ex only
+ * (kla_prefill_prepare_ex returns KLA_ERR_UNSUPPORTED for it).  A NULL
+ * kla_options pointer means the defaults (Kaczmarz coefficient, o_t = q_t S_t,
+ * scalar gate).  An unknown mode gives KLA_ERR_UNSUPPORTED.
  */
 typedef enum kla_beta_mode {
   KLA_BETA_KACZMARZ = 0,
@@ -216,7 +224,14 @@ typedef struct kla_options {
   int32_t beta_mode;          /* a kla_beta_mode value */
   int32_t normalize_q;        /* nonzero: divide each readout by ||q_t||_2 */
   const int32_t *pos_offset;  /* device, 4-byte aligned, or NULL */
+  int32_t diagonal_gate;      /* nonzero: g is per key channel, shaped like k */
 } kla_options;
+
+/* kla_prefill_workspace_bytes for the variant that opts selects (NULL = the
+ * defaults, the same value as kla_prefill_workspace_bytes); 0 for unsupported
+ * sizes. */
+size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                                      int32_t d_k, int32_t d_v, const kla_options *opts);
 
 /* kla_prefill_chunked, kla_prefill_prepare and kla_decode_step with options
  * (NULL = the defaults, which is what the calls without _ex use).  The scan

@@ -90,13 +90,16 @@ def _keys(n_tok, H, dk, w: Workload, gen, device):
     return k
 
 
-def prefill_inputs(w, device="cpu", seed=None, T=None, lens=None, n_seq=None, H=None):
+def prefill_inputs(w, device="cpu", seed=None, T=None, lens=None, n_seq=None, H=None,
+                   diag=False):
     """Draw one prefill problem for workload ``w`` (a Workload or its index).
 
     Optional overrides shrink the problem (T for dense, lens for packed, n_seq, H)
     while keeping the workload's distributions.  Returns a dict with q, k, v
     ([n_tok, H, d]), g, eta ([n_tok, H] fp32), S0 ([n_seq, H, d_k, d_v] fp32 or
     None), cu_seqlens (int32 [n_seq+1] or None for dense), n_seq, eps, dtype.
+    diag=True draws g per key channel ([n_tok, H, d_k], each entry from the workload's
+    log-decay range) for the diagonal-gated variant.
     """
     if not isinstance(w, Workload):
         w = WORKLOADS[int(w)]
@@ -121,6 +124,8 @@ def prefill_inputs(w, device="cpu", seed=None, T=None, lens=None, n_seq=None, H=
     v = torch.randn(n_tok, Hh, w.d_v, generator=gen, device=device)
     eta = torch.sigmoid(torch.randn(n_tok, Hh, generator=gen, device=device))
     g = w.g_low * torch.rand(n_tok, Hh, generator=gen, device=device)
+    if diag:
+        g = w.g_low * torch.rand(n_tok, Hh, w.d_k, generator=gen, device=device)
     S0 = None
     if w.s0_var > 0:
         S0 = math.sqrt(w.s0_var) * torch.randn(ns, Hh, w.d_k, w.d_v, generator=gen, device=device)
@@ -140,12 +145,12 @@ def hard_variant(inp: dict) -> dict:
     return out
 
 
-def decode_inputs(w, steps=None, device="cpu", seed=None, B=None, H=None, S=None):
+def decode_inputs(w, steps=None, device="cpu", seed=None, B=None, H=None, S=None, diag=False):
     """Draw ``steps`` decode tokens per sequence plus a start state.
 
     Returns dict with q, k ([steps, B, H, d_k]), v ([steps, B, H, d_v]),
     g, eta ([steps, B, H] fp32), S ([B, H, d_k, d_v] fp32, drawn with the
-    workload's state variance unless given), eps, dtype.
+    workload's state variance unless given), eps, dtype.  diag=True: g is [steps, B, H, d_k].
     """
     if not isinstance(w, Workload):
         w = WORKLOADS[int(w)]
@@ -160,10 +165,13 @@ def decode_inputs(w, steps=None, device="cpu", seed=None, B=None, H=None, S=None
     v = torch.randn(n, Hh, w.d_v, generator=gen, device=device)
     eta = torch.sigmoid(torch.randn(n, Hh, generator=gen, device=device))
     g = w.g_low * torch.rand(n, Hh, generator=gen, device=device)
+    if diag:
+        g = w.g_low * torch.rand(n, Hh, w.d_k, generator=gen, device=device)
     if S is None:
         var = w.s0_var if w.s0_var > 0 else 0.05
         S = math.sqrt(var) * torch.randn(Bb, Hh, w.d_k, w.d_v, generator=gen, device=device)
     shp = lambda x, d: x.reshape(steps, Bb, Hh, d) if d else x.reshape(steps, Bb, Hh)
     return dict(q=shp(q.to(w.dtype), w.d_k).contiguous(), k=shp(k.to(w.dtype), w.d_k).contiguous(),
-                v=shp(v.to(w.dtype), w.d_v).contiguous(), g=shp(g, 0).contiguous(),
+                v=shp(v.to(w.dtype), w.d_v).contiguous(),
+                g=(shp(g, w.d_k) if diag else shp(g, 0)).contiguous(),
                 eta=shp(eta, 0).contiguous(), S=S.contiguous(), eps=w.eps, dtype=w.dtype)

@@ -140,8 +140,8 @@ def test_last_error_is_thread_local_text(lib):
     assert "d_k" in lib.kla_last_error().decode()
 
 
-def _opts(mode=0, normq=0, pos=None):
-    return ctypes.pointer(kla.KlaOptions(mode, normq, pos))
+def _opts(mode=0, normq=0, pos=None, diag=0):
+    return ctypes.pointer(kla.KlaOptions(mode, normq, pos, diag))
 
 
 @pytest.mark.parametrize("opts,status", [
@@ -172,3 +172,28 @@ def test_options_default_pointer_is_accepted_up_to_the_workspace_check(lib):
                                     FAKE * 6, None, None, None, 2, 256, 4, 128, 128, BF16, None, 0,
                                     None, None)
     assert st == WORKSPACE
+
+
+def test_diagonal_gate_workspace_and_entry_points(lib):
+    # the diagonal-gated variant needs the decayed key and query tiles: three [64, d_k] fp32
+    # tiles and d_k decays per chunk-head on top of the default workspace
+    n_seq, n_tok, H, dk, dv = 4, 16384, 16, 128, 128
+    base = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv)
+    diag = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, diagonal_gate=True)
+    nch = (n_tok + 63) // 64 + n_seq
+    assert diag >= base + 4 * nch * H * (3 * 64 * dk + dk) and diag % 256 == 0
+    # NULL options give the default size
+    assert lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, dk, dv, None) == base
+    # the default-size workspace is too small for the diagonal-gated prefill
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, eta=FAKE * 5, o=FAKE * 6)
+    st = lib.kla_prefill_chunked_ex(a["q"], a["k"], a["v"], a["g"], a["eta"], 1e-6, None,
+                                    a["o"], None, None, None, 2, 256, 4, 128, 128, BF16, FAKE * 64,
+                                    kla.kla_prefill_workspace_bytes(2, 256, 4, 128, 128),
+                                    _opts(diag=1), None)
+    assert st == WORKSPACE
+    # the two-call prefill does not take the diagonal gate
+    nb = kla.kla_prefill_workspace_bytes(2, 256, 4, 128, 128, diagonal_gate=True)
+    st = lib.kla_prefill_prepare_ex(a["q"], a["k"], a["g"], a["eta"], 1e-6, None, None, 2, 256,
+                                    4, 128, 128, BF16, FAKE * 64, nb, _opts(diag=1), None)
+    assert st == UNSUPPORTED
+    assert "chunked_ex" in lib.kla_last_error().decode()

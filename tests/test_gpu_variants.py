@@ -44,6 +44,10 @@ def kla():
     return m
 
 
+def to_dev(d):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
 def unit_keys(d):
     d = dict(d)
     d["k"] = (d["k"].float() / d["k"].float().norm(dim=-1, keepdim=True)).to(d["k"].dtype)
@@ -102,3 +106,92 @@ def test_decode_variant_parity(kla, dtype, mode):
         check(Sd, Sref, TOL[dtype], f"S step {i}")
         S = torch.from_numpy(Sref).float()
         Sd = S.cuda()
+
+
+# ------------------------------------------------------------------ diagonal gating (decode)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv,B,H", [(64, 64, 6, 3), (128, 128, 4, 5), (128, 256, 3, 2),
+                                       (64, 128, 64, 96)])
+def test_decode_diagonal_gate(kla, dtype, dk, dv, B, H):
+    """Diagonal gating (paper Appendix B.5): g holds one log-decay per key channel.  The last
+    case has 6144 (sequence, head) items, the launch shape with one 512-lane workgroup each."""
+    w = ki.Workload(92, "decode-diag", B, H, dk, dv, dtype, T=1, s0_var=0.05, decode_steps=3,
+                    g_low=-1.0)
+    d = to_dev(ki.decode_inputs(w, diag=True))
+    pick = list(range(B)) if B <= 8 else [0, 1, 7, 31, 62, 63]
+    S = d["S"].clone()
+    So = d["S"][pick].double().cpu().numpy()
+    for t in range(3):
+        o, S = kla.kla_decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t],
+                                   d["eps"], S, inplace=(t == 1))
+        oo, So = oracle.decode(d["q"][t][pick], d["k"][t][pick], d["v"][t][pick],
+                               d["g"][t][pick], d["eta"][t][pick], d["eps"], So)
+        torch.cuda.synchronize()
+        check(o[pick], oo, TOL[dtype], "o t")
+        check(S[pick], So, TOL[dtype], "S t")
+
+
+# ------------------------------------------------------------------ diagonal gating (prefill)
+def run_prefill_diag(kla, d, **kw):
+    o, ST = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                    S0=d["S0"], cu_seqlens=d["cu_seqlens"], n_seq=d["n_seq"], **kw)
+    torch.cuda.synchronize()
+    return o, ST
+
+
+def oracle_prefill_diag(d, **kw):
+    cu = d["cu_seqlens"]
+    if cu is None:
+        T = d["q"].shape[0] // d["n_seq"]
+        cu = np.arange(d["n_seq"] + 1) * T
+    else:
+        cu = cu.cpu().numpy()
+    return oracle.prefill(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"], S0=d["S0"],
+                          cu_seqlens=cu, **kw)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", ["tiny", "ragged128", "dk64_dv256", "strong_decay", "wide"])
+def test_prefill_diagonal_gate(kla, dtype, case):
+    """Diagonal gating (paper Appendix B.5): g [n_tok, H, d_k], one log-decay per key channel,
+    through kla_prefill_chunked_ex, against the fp64 tokenwise oracle.  'wide' has 3 x 24 x 4
+    column slices, more than the compute units, so the 64-column workgroups run."""
+    spec = {
+        "tiny": dict(H=1, dk=64, dv=64, lens=None, T=256, n_seq=1, g_low=-0.5),
+        "ragged128": dict(H=3, dk=128, dv=128, lens=(70, 1, 129, 200), g_low=-0.5),
+        "dk64_dv256": dict(H=2, dk=64, dv=256, lens=(64, 190, 5), g_low=-0.5),
+        "strong_decay": dict(H=2, dk=128, dv=128, lens=(300, 77), g_low=-2.0),
+        "wide": dict(H=24, dk=128, dv=128, lens=None, T=130, n_seq=3, g_low=-0.5),
+    }[case]
+    w = ki.Workload(93, "prefill-diag", spec.get("n_seq", len(spec["lens"] or ())), spec["H"],
+                    spec["dk"], spec["dv"], dtype, T=spec.get("T", 0), lens=spec["lens"] or (),
+                    g_low=spec["g_low"], s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w, diag=True))
+    assert d["g"].shape == d["k"].shape
+    o, ST = run_prefill_diag(kla, d)
+    oo, So = oracle_prefill_diag(d)
+    check(o, oo, TOL[dtype], "o")
+    check(ST, So, TOL[dtype], "S_T")
+
+
+def test_prefill_diagonal_gate_normalised_readout(kla):
+    """Diagonal gating together with the readout divided by ||q_t|| and the GDN coefficient
+    (on unit keys, where that coefficient keeps the recurrence bounded)."""
+    w = ki.Workload(94, "prefill-diag-nq", 2, 2, 128, 128, torch.float32, T=150, s0_var=0.01)
+    d = unit_keys(to_dev(ki.prefill_inputs(w, diag=True)))
+    o, ST = run_prefill_diag(kla, d, normalize_q=True, beta_mode="gated")
+    oo, So = oracle_prefill_diag(d, normalize_q=True, beta_mode="gated")
+    check(o, oo, 1e-4, "o")
+    check(ST, So, 1e-4, "S_T")
+
+
+def test_prefill_diagonal_equal_channels_match_scalar_gate(kla):
+    """A per-channel g that is the same on every channel gives the scalar-gated result."""
+    w = ki.Workload(95, "prefill-diag-eq", 2, 3, 128, 128, torch.float32, T=200, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    o1, S1 = run_prefill_diag(kla, d)
+    dd = dict(d)
+    dd["g"] = d["g"][:, :, None].expand(-1, -1, 128).contiguous()
+    o2, S2 = run_prefill_diag(kla, dd)
+    check(o2, o1.double().cpu().numpy(), 1e-5, "o")
+    check(S2, S1.double().cpu().numpy(), 1e-5, "S_T")
