@@ -14,7 +14,7 @@
 // chunk scan then runs as for the scalar gate on Kg, Qg, Kd in place of K, Q (see
 // kla_scan.hip), with unit decays and the per-channel state decay exp(G_last).
 //
-// One 256-lane workgroup per (chunk, head), everything staged in LDS in fp32.  Every decay
+// One 1024-lane workgroup per (chunk, head), everything staged in LDS in fp32.  Every decay
 // factor is an exponential of a difference G_i - G_j with j <= i (or G_last - G_j), never
 // positive, so nothing overflows whatever the decay.
 #include "kla_device.h"
@@ -24,7 +24,7 @@ namespace kla {
 
 namespace {
 
-constexpr int kDiagThreads = 256;
+constexpr int kDiagThreads = 1024;
 
 __device__ __forceinline__ int find_seq(const int32_t *__restrict__ chunk_off, int n_seq, int c) {
   int lo = 0, hi = n_seq - 1;
@@ -37,11 +37,21 @@ __device__ __forceinline__ int find_seq(const int32_t *__restrict__ chunk_off, i
 
 template <int DK>
 struct DiagSmem {
-  // rows of DK + 1 floats: the pair loops read a column of several rows at once
-  float K[kChunk][DK + 1], Q[kChunk][DK + 1], G[kChunk][DK + 1];
+  // rows of DK + 4 floats: 16-byte aligned for the pair loops' float4 reads, and offset by
+  // one bank group from row to row
+  alignas(16) float K[kChunk][DK + 4];
+  alignas(16) float Q[kChunk][DK + 4];
+  alignas(16) float G[kChunk][DK + 4];
   float A[kChunk][kChunk + 1], P[kChunk][kChunk + 1], X[kChunk][kChunk + 1];
   float b[kChunk], rq[kChunk];
 };
+
+// x from lane `ctrl` of this lane's DPP row (a DPP move with the given control).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               CTRL, 0xF, 0xF, false));
+}
 
 template <typename T>
 __device__ __forceinline__ void put(T *dst, size_t i, float x) {
@@ -69,40 +79,72 @@ __global__ __launch_bounds__(kDiagThreads) void kla_prep_diag_kernel(
   const int len = min(kChunk, tabs.cu[n + 1] - t0);
   const int tid = threadIdx.x;
 
-  // ---- the chunk's rows; rows past its end are zero (and add no decay)
-  for (int e = tid; e < kChunk * DK; e += kDiagThreads) {
-    const int i = e / DK, ch = e % DK;
-    const bool in = i < len;
-    const size_t idx = ((size_t)(t0 + i) * H + h) * DK + ch;
-    sm.K[i][ch] = in ? to_f32(k[idx]) : 0.f;
-    sm.Q[i][ch] = in ? to_f32(q[idx]) : 0.f;
-    sm.G[i][ch] = in ? g[idx] : 0.f;
+  // ---- the chunk's rows; rows past its end are zero (and add no decay).  Lane tid takes 8
+  //      consecutive channels of one row: one 16-byte load of k and of q (bf16), 32 bytes of g
+  {
+    const int e0 = tid * 8, i = e0 / DK, ch = e0 % DK;
+    if (i < kChunk) {
+      float kv[8], qv[8], gv[8];
+      if (i < len) {
+        const size_t idx = ((size_t)(t0 + i) * H + h) * DK + ch;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kv[e] = to_f32(k[idx + e]);
+          qv[e] = to_f32(q[idx + e]);
+          gv[e] = g[idx + e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kv[e] = qv[e] = gv[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sm.K[i][ch + e] = kv[e];
+        sm.Q[i][ch + e] = qv[e];
+        sm.G[i][ch + e] = gv[e];
+      }
+    }
   }
   __syncthreads();
-  // ---- G: inclusive prefix over the chunk's tokens, per channel
+  // ---- G: inclusive prefix over the chunk's tokens, per channel (the column in registers)
   if (tid < DK) {
-    float acc = 0.f;
-    for (int i = 0; i < kChunk; ++i) {
-      acc += sm.G[i][tid];
-      sm.G[i][tid] = acc;
-    }
+    float col[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) col[i] = sm.G[i][tid];
+#pragma unroll
+    for (int i = 1; i < kChunk; ++i) col[i] += col[i - 1];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) sm.G[i][tid] = col[i];
   }
-  // ---- b and the readout factor per token
-  if (tid < kChunk) {
-    const int i = tid;
+  // ---- b and the readout factor per token: 16 lanes a row, 8 channels at a time
+  {
+    const int i = tid >> 4, part = tid & 15;
     float kk = 0.f, qq = 0.f;
-    for (int ch = 0; ch < DK; ++ch) {
-      kk += sm.K[i][ch] * sm.K[i][ch];
-      qq += sm.Q[i][ch] * sm.Q[i][ch];
+    if (i < kChunk) {
+      for (int ch = 8 * part; ch < DK; ch += 128) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kk += sm.K[i][ch + e] * sm.K[i][ch + e];
+          qq += sm.Q[i][ch + e] * sm.Q[i][ch + e];
+        }
+      }
     }
-    float bi = 0.f;
-    if (i < len) {
-      const size_t th = (size_t)(t0 + i) * H + h;
-      const float t_abs = (float)(t0 + i - ts + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
-      bi = write_coef(opts.beta_mode, eta[th], kk + eps, t_abs);
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+      kk += __shfl_xor(kk, off, 16);
+      qq += __shfl_xor(qq, off, 16);
     }
-    sm.b[i] = bi;
-    sm.rq[i] = opts.normalize_q ? (qq > 0.f ? 1.f / sqrtf(qq) : 0.f) : 1.f;
+    if (i < kChunk && part == 0) {
+      float bi = 0.f;
+      if (i < len) {
+        const size_t th = (size_t)(t0 + i) * H + h;
+        const float t_abs =
+            (float)(t0 + i - ts + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
+        bi = write_coef(opts.beta_mode, eta[th], kk + eps, t_abs);
+      }
+      sm.b[i] = bi;
+      sm.rq[i] = opts.normalize_q ? (qq > 0.f ? 1.f / sqrtf(qq) : 0.f) : 1.f;
+    }
   }
   __syncthreads();
 
@@ -119,21 +161,24 @@ __global__ __launch_bounds__(kDiagThreads) void kla_prep_diag_kernel(
   for (int ch = tid; ch < DK; ch += kDiagThreads)
     GC_out[(size_t)task * DK + ch] = __expf(sm.G[kChunk - 1][ch]);
 
-  // ---- A (strictly lower) and P (lower): lane tid owns rows 4 bi .. + 3, columns
-  //      4 bj .. + 3 of both
+  // ---- A (strictly lower) and P (lower): four consecutive lanes share rows 4 bi .. + 3 and
+  //      columns 4 bj .. + 3, each summing a quarter of the channels, four at a time
   {
-    const int bi = tid >> 4, bj = tid & 15;
+    const int tile = tid >> 2, cg = tid & 3;
+    const int bi = tile >> 4, bj = tile & 15;
+    constexpr int CPG = DK / 4;  // channels per lane
     float a[4][4] = {}, p[4][4] = {};
     if (bj <= bi) {
-      for (int ch = 0; ch < DK; ++ch) {
-        float gi[4], ki[4], qi[4], gj[4], kj[4];
+#pragma unroll 1
+      for (int c4 = cg * CPG; c4 < (cg + 1) * CPG; c4 += 4) {
+        f32x4 gi[4], ki[4], qi[4], gj[4], kj[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          gi[r] = sm.G[4 * bi + r][ch];
-          ki[r] = sm.K[4 * bi + r][ch];
-          qi[r] = sm.Q[4 * bi + r][ch];
-          gj[r] = sm.G[4 * bj + r][ch];
-          kj[r] = sm.K[4 * bj + r][ch];
+          gi[r] = *reinterpret_cast<const f32x4 *>(&sm.G[4 * bi + r][c4]);
+          ki[r] = *reinterpret_cast<const f32x4 *>(&sm.K[4 * bi + r][c4]);
+          qi[r] = *reinterpret_cast<const f32x4 *>(&sm.Q[4 * bi + r][c4]);
+          gj[r] = *reinterpret_cast<const f32x4 *>(&sm.G[4 * bj + r][c4]);
+          kj[r] = *reinterpret_cast<const f32x4 *>(&sm.K[4 * bj + r][c4]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -141,34 +186,61 @@ __global__ __launch_bounds__(kDiagThreads) void kla_prep_diag_kernel(
           for (int s = 0; s < 4; ++s) {
             const int i = 4 * bi + r, j = 4 * bj + s;
             if (j <= i) {
-              const float e = __expf(gi[r] - gj[s]) * kj[s];
-              p[r][s] += qi[r] * e;
-              if (j < i) a[r][s] += ki[r] * e;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x = __expf(gi[r][e] - gj[s][e]) * kj[s][e];
+                p[r][s] += qi[r][e] * x;
+                if (j < i) a[r][s] += ki[r][e] * x;
+              }
             }
           }
       }
     }
+    // sum the four channel quarters (lanes 4 tile .. 4 tile + 3)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sm.A[4 * bi + r][4 * bj + s] = a[r][s];
-        sm.P[4 * bi + r][4 * bj + s] = p[r][s] * sm.rq[4 * bi + r];
+        a[r][s] += __shfl_xor(a[r][s], 1, 4);
+        a[r][s] += __shfl_xor(a[r][s], 2, 4);
+        p[r][s] += __shfl_xor(p[r][s], 1, 4);
+        p[r][s] += __shfl_xor(p[r][s], 2, 4);
       }
+    if (cg == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          sm.A[4 * bi + r][4 * bj + s] = a[r][s];
+          sm.P[4 * bi + r][4 * bj + s] = p[r][s] * sm.rq[4 * bi + r];
+        }
+    }
   }
   __syncthreads();
 
-  // ---- X = (I + Diag(b) A)^{-1}, one column per lane, by forward substitution
-  if (tid < kChunk) {
-    const int j = tid;
+  // ---- X = (I + Diag(b) A)^{-1} by forward substitution, row by row: wavefront w takes
+  //      columns 4 w .. 4 w + 3, 16 lanes (one DPP row) a column.  Lane `part` keeps X[l][j]
+  //      for l = part, part + 16, part + 32, part + 48 in registers and sums those terms of
+  //      each dot product; a DPP reduction over the 16 lanes gives every lane the row's value.
+  {
+    const int j = 4 * (tid >> 6) + ((tid & 63) >> 4), part = tid & 15;
+    float xr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-      float x = (i == j) ? 1.f : 0.f;
-      if (i > j) {
-        float acc = 0.f;
-        for (int l = j; l < i; ++l) acc += sm.A[i][l] * sm.X[l][j];
-        x = -sm.b[i] * acc;
+      float acc = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int l = part + 16 * q4;
+        if (16 * q4 < i)  // l < i is checked per lane below; rows l >= i hold 0 in xr
+          acc += (l < i ? sm.A[i][l] : 0.f) * xr[q4];
       }
-      sm.X[i][j] = x;
+      acc += dpp_f32<0xB1>(acc);   // quad_perm [1,0,3,2]
+      acc += dpp_f32<0x4E>(acc);   // quad_perm [2,3,0,1]
+      acc += dpp_f32<0x141>(acc);  // row_half_mirror
+      acc += dpp_f32<0x140>(acc);  // row_mirror
+      const float x = i == j ? 1.f : (i > j ? -sm.b[i] * acc : 0.f);
+      if (part == (i & 15)) xr[i >> 4] = x;
+      if (part == 0) sm.X[i][j] = x;
     }
   }
   __syncthreads();
