@@ -49,11 +49,16 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# what the chunk-scan kernel is compiled from (its sources and the compiler flags): a change to
+# any of them voids its counters
+SCAN_SOURCES = ("csrc/kla_scan.hip", "csrc/kla_device.h", "csrc/kla_launch.h", "build.py")
+
+
 def csrc_digest() -> str:
     h = hashlib.sha256()
-    cdir = os.path.join(ROOT, "gated_delta_rule_kla_amd", "csrc")
-    for name in sorted(os.listdir(cdir)):
-        with open(os.path.join(cdir, name), "rb") as f:
+    pdir = os.path.join(ROOT, "gated_delta_rule_kla_amd")
+    for name in SCAN_SOURCES:
+        with open(os.path.join(pdir, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
