@@ -12,7 +12,8 @@ Functions mirror the C entry points:
 * :func:`kla_prefill_prepare` / :func:`kla_prefill_scan` -- its two halves
 * :func:`kla_decode_step`     -- one decode step (q, k, v, g, eta, eps, S) -> (o, S')
 * :func:`kla_prefill_chunk_stage` -- per-chunk b, G, T (and W, U~) for unit checks
-* :func:`kla_prefill_workspace_bytes`
+* :func:`kla_prefill_backward` -- gradients (dq, dk, dv, dg, deta, dS0) of the prefill
+* :func:`kla_prefill_workspace_bytes`, :func:`kla_prefill_backward_workspace_bytes`
 """
 from __future__ import annotations
 
@@ -22,7 +23,8 @@ import os
 import torch
 
 __all__ = ["kla_prefill_chunked", "kla_prefill_prepare", "kla_prefill_scan", "kla_decode_step",
-           "kla_prefill_chunk_stage", "kla_prefill_workspace_bytes", "library_path",
+           "kla_prefill_chunk_stage", "kla_prefill_workspace_bytes", "kla_prefill_backward",
+           "kla_prefill_backward_workspace_bytes", "library_path",
            "load_library", "CHUNK", "KlaError"]
 
 CHUNK = 64
@@ -86,6 +88,12 @@ def load_library():
     lib.kla_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32,
                                        ctypes.c_int, opt_p, vp]
     lib.kla_decode_step_ex.restype = ctypes.c_int
+    lib.kla_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.kla_prefill_backward_workspace_bytes.restype = sz
+    lib.kla_prefill_backward.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp,
+                                         sz, vp]
+    lib.kla_prefill_backward.restype = ctypes.c_int
     lib.kla_status_string.argtypes = [ctypes.c_int]
     lib.kla_status_string.restype = ctypes.c_char_p
     lib.kla_last_error.argtypes = []
@@ -239,6 +247,73 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
         _ptr(cu_seqlens), host_ptr, n_seq, n_tok, H, d_k, d_v, _DTYPES[dt], _ptr(workspace),
         workspace.numel(), opts, _stream(dev)))
     return o.reshape(shape_v), S_T
+
+
+def kla_prefill_backward_workspace_bytes(n_seq: int, total_tokens: int, n_heads: int, d_k: int,
+                                         d_v: int, dtype=torch.bfloat16) -> int:
+    """Workspace bytes kla_prefill_backward needs (0 for unsupported sizes)."""
+    return int(load_library().kla_prefill_backward_workspace_bytes(
+        n_seq, total_tokens, n_heads, d_k, d_v, _DTYPES[dtype]))
+
+
+def kla_prefill_backward(q, k, v, g, eta, eps: float, dO, S0=None, dS_T=None, cu_seqlens=None,
+                         n_seq=None, *, cu_seqlens_host=None, workspace=None,
+                         need_dS0=True):
+    """Gradients of the prefill for the cotangents dO (like o) and dS_T (like S_T, or None).
+
+    Inputs as for :func:`kla_prefill_chunked` (default variant only: Kaczmarz coefficient,
+    scalar gate, o = q S).  Returns (dq, dk, dv, dg, deta, dS0), shaped like q, k, v, g, eta
+    and S0 ([n_seq, H, d_k, d_v]; None when need_dS0 is False).
+    """
+    shape_q, shape_v, shape_g = q.shape, v.shape, g.shape
+    q, k, v, g, eta, n_seq = _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq)
+    dev = q.device
+    _need(q, "q", device=dev)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    _need(k, "k", dt, dev)
+    _need(v, "v", dt, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(eta, "eta", torch.float32, dev)
+    n_tok, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if (k.shape != q.shape or v.shape[:2] != (n_tok, H) or g.shape != (n_tok, H)
+            or eta.shape != (n_tok, H)):
+        raise ValueError("inconsistent q/k/v/g/eta shapes (the backward takes a scalar gate)")
+    dO = dO.reshape(n_tok, H, d_v)
+    _need(dO, "dO", dt, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        if cu_seqlens.numel() != n_seq + 1:
+            raise ValueError("cu_seqlens must have n_seq + 1 entries")
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous().cpu()
+    for t, name in ((S0, "S0"), (dS_T, "dS_T")):
+        if t is not None:
+            _need(t, name, torch.float32, dev)
+            if t.shape != (n_seq, H, d_k, d_v):
+                raise ValueError(f"{name} must be [{n_seq}, {H}, {d_k}, {d_v}]")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dg = torch.empty_like(g)
+    deta = torch.empty_like(eta)
+    dS0 = torch.empty((n_seq, H, d_k, d_v), dtype=torch.float32, device=dev) if need_dS0 else None
+    lib = load_library()
+    ws_bytes = int(lib.kla_prefill_backward_workspace_bytes(n_seq, n_tok, H, d_k, d_v,
+                                                            _DTYPES[dt]))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    host_ptr = None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr())
+    _check(lib.kla_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S0), _ptr(dO),
+        _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(deta), _ptr(dS0),
+        _ptr(cu_seqlens), host_ptr, n_seq, n_tok, H, d_k, d_v, _DTYPES[dt], _ptr(workspace),
+        workspace.numel(), _stream(dev)))
+    return (dq.reshape(shape_q), dk.reshape(shape_q), dv.reshape(shape_v), dg.reshape(shape_g),
+            deta.reshape(shape_g), dS0)
 
 
 def kla_prefill_prepare(q, k, g, eta, eps, workspace, *, n_seq, d_v, cu_seqlens=None,

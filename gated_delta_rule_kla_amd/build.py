@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkla.so")
-SOURCES = ["kla_api.hip", "kla_prep.hip", "kla_scan.hip", "kla_decode.hip", "kla_diag.hip"]
+SOURCES = ["kla_api.hip", "kla_prep.hip", "kla_scan.hip", "kla_decode.hip", "kla_diag.hip",
+           "kla_bwd.hip"]
 ARCH = "gfx950"
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

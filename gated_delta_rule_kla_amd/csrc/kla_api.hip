@@ -164,6 +164,47 @@ size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32
 
 namespace {
 
+// Backward workspace: the forward layout, then per chunk-head the incoming states S and the
+// cotangents dS' of the outgoing ones ([d_k][d_v] fp32 each), dU and dR ([64][d_v] fp32
+// each), and the forward output the scan writes again ([tokens][H][d_v], operand type).
+struct BwdLayout {
+  WsLayout fw;
+  size_t off_SN, off_dSo, off_dU, off_dR, off_O, total;
+};
+
+BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, int64_t d_v,
+                     size_t es) {
+  BwdLayout b;
+  b.fw = ws_layout(n_seq, total_tokens, H);
+  const size_t nch = (size_t)kla::chunk_upper_bound(n_seq, total_tokens);
+  const size_t st = sizeof(float) * nch * (size_t)H * (size_t)d_k * (size_t)d_v;
+  const size_t ut = sizeof(float) * nch * (size_t)H * KLA_CHUNK * (size_t)d_v;
+  b.off_SN = b.fw.total;
+  b.off_dSo = align256(b.off_SN + st);
+  b.off_dU = align256(b.off_dSo + st);
+  b.off_dR = align256(b.off_dU + ut);
+  b.off_O = align256(b.off_dR + ut);
+  b.total = align256(b.off_O + es * (size_t)total_tokens * (size_t)H * (size_t)d_v);
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kla_prefill_backward_workspace_bytes(int32_t n_seq, int32_t total_tokens,
+                                            int32_t n_heads, int32_t d_k, int32_t d_v,
+                                            kla_dtype dtype) {
+  if (n_seq <= 0 || total_tokens < 0 || n_heads <= 0 || !supported_dk(d_k) ||
+      !supported_dv(d_v) || (dtype != KLA_DTYPE_F32 && dtype != KLA_DTYPE_BF16))
+    return 0;
+  return bwd_layout(n_seq, total_tokens, n_heads, d_k, d_v, elem_size(dtype)).total;
+}
+
+}  // extern "C"
+
+namespace {
+
 // Validation of the prefill arguments shared by the three prefill entry points.  Token
 // buffers that a given entry point does not use are passed as nullptr with need_* = false.
 kla_status check_prefill_args(const void *q, const void *k, const void *v, const float *g,
@@ -317,6 +358,85 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
   return kla_prefill_chunked_ex(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
                                 n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
                                 workspace_bytes, nullptr, stream);
+}
+
+kla_status kla_prefill_backward(const void *q, const void *k, const void *v, const float *g,
+                                const float *eta, float eps, const float *S0, const void *dO,
+                                const float *dS_T, void *dq, void *dk, void *dv, float *dg,
+                                float *deta, float *dS0, const int32_t *cu_seqlens,
+                                const int32_t *cu_seqlens_host, int32_t n_seq,
+                                int32_t total_tokens, int32_t n_heads, int32_t d_k, int32_t d_v,
+                                kla_dtype dtype, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  kla_status st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v,
+                                      dtype, eps);
+  if (st != KLA_OK) return st;
+  if (total_tokens > 0 && (!q || !k || !v || !g || !eta || !dO || !dq || !dk || !dv || !dg || !deta))
+    return fail(KLA_ERR_INVALID_ARGUMENT,
+                "q, k, v, g, eta, dO, dq, dk, dv, dg and deta are required");
+  if ((st = check_dense(cu_seqlens, n_seq, total_tokens)) != KLA_OK) return st;
+  for (const void *p : {q, k, v, dO, static_cast<const void *>(dq),
+                        static_cast<const void *>(dk), static_cast<const void *>(dv)})
+    if (p && !aligned16(p))
+      return fail(KLA_ERR_INVALID_ARGUMENT, "q, k, v, dO, dq, dk, dv must be 16-byte aligned");
+  for (const void *p : {static_cast<const void *>(g), static_cast<const void *>(eta),
+                        static_cast<const void *>(S0), static_cast<const void *>(dS_T),
+                        static_cast<const void *>(dg), static_cast<const void *>(deta),
+                        static_cast<const void *>(dS0)})
+    if (p && !aligned16(p))
+      return fail(KLA_ERR_INVALID_ARGUMENT,
+                  "g, eta, S0, dS_T, dg, deta, dS0 must be 16-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)total_tokens * n_heads * d_k * es;
+  const size_t nv = (size_t)total_tokens * n_heads * d_v * es;
+  const size_t ns = (size_t)total_tokens * n_heads * sizeof(float);
+  const size_t nS = (size_t)n_seq * n_heads * d_k * d_v * sizeof(float);
+  const void *outs[] = {dq, dk, dv, dg, deta, dS0};
+  const size_t nouts[] = {nq, nq, nv, ns, ns, nS};
+  const void *ins[] = {q, k, v, g, eta, S0, dO, dS_T};
+  const size_t nins[] = {nq, nq, nv, ns, ns, nS, nv, nS};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlap(outs[i], nouts[i], ins[j], nins[j]))
+        return fail(KLA_ERR_INVALID_ARGUMENT, "gradient buffers must not overlap the inputs");
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], nouts[i], outs[j], nouts[j]))
+        return fail(KLA_ERR_INVALID_ARGUMENT, "gradient buffers must not overlap each other");
+  }
+  const BwdLayout bl = bwd_layout(n_seq, total_tokens, n_heads, d_k, d_v, es);
+  if (!workspace || workspace_bytes < bl.total)
+    return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", bl.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  for (int i = 0; i < 6; ++i)
+    if (overlap(outs[i], nouts[i], workspace, bl.total))
+      return fail(KLA_ERR_INVALID_ARGUMENT, "gradient buffers must not overlap the workspace");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear any stale error from unrelated work
+  const kla::CoefOpts co{kla::kBetaKaczmarz, 0, nullptr};
+  if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
+                            dtype, workspace, s)) != KLA_OK)
+    return st;
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
+  char *ws = static_cast<char *>(workspace);
+  float *SN = reinterpret_cast<float *>(ws + bl.off_SN);
+  if ((st = hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0,
+                                        ws + bl.off_O, nullptr, wv.tabs, n_seq, n_heads, s,
+                                        nullptr, SN),
+                       "scan (stored states)")) != KLA_OK)
+    return st;
+  if ((st = hip_status(
+           kla::launch_bwd(to_dt(dtype), d_k, d_v, q, k, v, dO, g, eta, eps, wv.GD, wv.T, wv.P,
+                           dS_T, SN, reinterpret_cast<float *>(ws + bl.off_dSo),
+                           reinterpret_cast<float *>(ws + bl.off_dU),
+                           reinterpret_cast<float *>(ws + bl.off_dR), dq, dk, dv, dg, deta, dS0,
+                           wv.tabs, n_seq, kla::chunk_upper_bound(n_seq, total_tokens), n_heads,
+                           s),
+           "backward")) != KLA_OK)
+    return st;
+  return ok();
 }
 
 kla_status kla_prefill_prepare_ex(const void *q, const void *k, const float *g,

@@ -1,0 +1,713 @@
+// kla_bwd.hip -- the backward pass of the chunkwise prefill: gradients of q, k, v, g, eta and
+// of the incoming state S0 for the cotangents dO of the outputs and dS_T of the final state.
+//
+// Paper "Kaczmarz Linear Attention" (arXiv 2605.08587) trains with the chunkwise algorithm of
+// Propositions 3-4 (Eq. (7)-(9)) but derives no backward pass.  What follows is the
+// reverse-mode derivative of that chunk solve, for the default variant (Kaczmarz coefficient
+// of Eq. (3), one scalar gate per token-head, o_t = q_t S_t).  Per chunk of one
+// (sequence, head), with S the chunk's incoming state, G the chunk-local inclusive prefix of
+// g, Gamma_ij = exp(G_i - G_j), gam_i = exp(G_i), dec_i = exp(G_last - G_i),
+// A = strict_lower(Gamma o K K^T), P = lower(Gamma o Q K^T), X = (I + Diag(b) A)^{-1},
+// T = X Diag(b) and den_i = ||k_i||^2 + eps:
+//   forward   R = V - Diag(gam) K S,  U = T R,  O = Diag(gam) Q S + P U,
+//             S' = exp(G_last) S + K^T Diag(dec) U
+//   backward, given dO and dS' (the next chunk's dS, or dS_T):
+//     dU = P^T dO + Diag(dec) K dS',   dR = T^T dU = dV,
+//     dS = exp(G_last) dS' + Q^T Diag(gam) dO - K^T Diag(gam) dR    (the previous chunk's dS')
+//     dP = lower(dO U^T),  dT = lower(dU R^T),  dX = dT Diag(b),
+//     dL = -strict_lower(X^T dX X^T),  dA = Diag(b) dL,
+//     db = colsum(dT o X) + rowsum(dL o A),  deta = db / den,
+//     dQ = Diag(gam) dO S^T + (dP o Gamma) K,
+//     dK = Diag(dec) U dS'^T - Diag(gam) dR S^T + (dP o Gamma)^T Q + (dA o Gamma) K
+//          + (dA o Gamma)^T K - Diag(2 b db / den) K,
+//     dG_i = gam_i q_i.(dO S^T)_i - gam_i k_i.(dR S^T)_i - dec_i k_i.(U dS'^T)_i
+//            + rowsum_i(Z) - colsum_i(Z),   Z = dP o P + dA o A,
+//     dG_last += exp(G_last) <dS', S> + sum_j dec_j k_j.(U dS'^T)_j,
+//     dg_t = sum of dG_i over the chunk's positions i >= t.
+// After the forward kernels have run again (the prep, then the chunk scan storing every
+// chunk's incoming state S), two kernels finish the job:
+//   kla_bwd_scan_kernel  the adjoint scan: sequential over the chunks in reverse, parallel over
+//                        (sequence, head, 32-column slice) since the columns of dS are
+//                        independent given the tiles; stores dS', dU and dR per chunk, writes
+//                        dV and dS0.
+//   kla_bwd_grad_kernel  one workgroup per (chunk, head): the contractions over d_v with the
+//                        stored S and dS', then the chunk-local algebra, dq, dk, dg, deta.
+// Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) from fp32 LDS tiles, whatever the
+// operand type of q, k, v.
+#include "kla_device.h"
+#include "kla_launch.h"
+
+namespace kla {
+
+namespace {
+
+constexpr int kAdjBV = 32;          // state columns per adjoint-scan workgroup
+constexpr int kAdjThreads = 256;    // four wavefronts
+constexpr int kGradThreads = 512;   // eight wavefronts
+constexpr int LDB = kAdjBV + 4;     // row stride of a 32-column fp32 block in LDS
+constexpr int LDC = kChunk + 4;     // row stride of a 64 x 64 fp32 tile in LDS
+
+// acc[i][j] += sum_{k < KD} A(i, k) B(k, j) over one 16 x 16 tile: lane (r, kq) = (l % 16,
+// l / 16) supplies A(r, k0 + kq) and B(k0 + kq, r) and holds D[4 kq + e][r] of the result.
+template <int KD, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int lane, FA fa, FB fb) {
+  const int r = lane & 15, kq = lane >> 4;
+#pragma unroll 4
+  for (int k0 = 0; k0 < KD; k0 += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa(r, k0 + kq), fb(k0 + kq, r), acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 ld4(const __bf16 *p) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+  return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
+}
+
+// Rows [0, len) of a row-strided tensor, columns 0 .. NC - 1 from src, into an fp32 LDS tile
+// with row stride LD; rows past len are zero.
+template <int NC, int LD, int NT, typename Src>
+__device__ __forceinline__ void stage_rows(float *dst, const Src *src, size_t row_stride, int len,
+                                           int tid) {
+  constexpr int N4 = NC / 4;
+  for (int e = tid; e < kChunk * N4; e += NT) {
+    const int r = e / N4, c = 4 * (e % N4);
+    const f32x4 x = r < len ? ld4(src + (size_t)r * row_stride + c) : zero4();
+    *reinterpret_cast<f32x4 *>(dst + r * LD + c) = x;
+  }
+}
+
+// A 64 x 64 matrix stored as its ten lower 16 x 16 blocks (the prep kernel's packed T and P),
+// unpacked into an fp32 LDS tile with zeros above the diagonal blocks.
+template <int NT, typename Tin>
+__device__ __forceinline__ void stage_packed(float (*dst)[LDC], const Tin *src, int tid) {
+  for (int e = tid; e < kChunk * kChunk; e += NT) {
+    const int r = e >> 6, c = e & 63, I = r >> 4, J = c >> 4;
+    dst[r][c] =
+        J > I ? 0.f : to_f32(src[(I * (I + 1) / 2 + J) * 256 + (r & 15) * 16 + (c & 15)]);
+  }
+}
+
+// x from the lane that the DPP control selects within this lane's row of 16
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               CTRL, 0xF, 0xF, false));
+}
+
+// sum over the 16 lanes of a DPP row (lanes with the same l / 16)
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __shfl_xor(x, 1, 16);
+  x += __shfl_xor(x, 2, 16);
+  x += __shfl_xor(x, 4, 16);
+  x += __shfl_xor(x, 8, 16);
+  return x;
+}
+
+template <int DK>
+struct AdjSmem {
+  float K[kChunk][DK + 4];
+  float Q[kChunk][DK + 4];
+  float T[kChunk][LDC];
+  float P[kChunk][LDC];
+  float dO[kChunk][LDB];
+  float dU[kChunk][LDB];
+  float dR[kChunk][LDB];
+  float dS[DK][LDB];
+  float gam[kChunk], dec[kChunk];
+};
+
+}  // namespace
+
+// The adjoint scan.  Workgroup (sequence n, head h, slice) owns state columns
+// 32 slice .. + 31 of dS for the whole sequence, in LDS.
+template <typename Tin, int DK>
+__global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ dO,
+    const float *__restrict__ GD, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
+    const float *__restrict__ dST, float *__restrict__ dS0, float *__restrict__ dSo,
+    float *__restrict__ dUo, float *__restrict__ dRo, Tin *__restrict__ dv,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  AdjSmem<DK> &sm = *reinterpret_cast<AdjSmem<DK> *>(smem_raw);
+  const int nsl = DV / kAdjBV;
+  const int slice = blockIdx.x % nsl, sh = blockIdx.x / nsl;
+  const int h = sh % H, n = sh / H;
+  const int v0 = slice * kAdjBV;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int tb = cu[n], te = cu[n + 1], cbase = chunk_off[n];
+  const int nchunks = (te - tb + kChunk - 1) / kChunk;
+  const size_t sbase = ((size_t)n * H + h) * DK * (size_t)DV + v0;
+
+  // the last chunk's dS' is the cotangent of S_T
+  for (int e = tid; e < DK * kAdjBV; e += kAdjThreads) {
+    const int r = e / kAdjBV, c = e % kAdjBV;
+    sm.dS[r][c] = dST ? dST[sbase + (size_t)r * DV + c] : 0.f;
+  }
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const int t0 = tb + c * kChunk, len = min(kChunk, te - t0);
+    const size_t ch = (size_t)(cbase + c) * H + h;
+    const size_t tok = (size_t)t0 * H + h;
+    stage_rows<DK, DK + 4, kAdjThreads>(&sm.K[0][0], k + tok * DK, (size_t)H * DK, len, tid);
+    stage_rows<DK, DK + 4, kAdjThreads>(&sm.Q[0][0], q + tok * DK, (size_t)H * DK, len, tid);
+    stage_rows<kAdjBV, LDB, kAdjThreads>(&sm.dO[0][0], dO + tok * DV + v0, (size_t)H * DV, len,
+                                         tid);
+    stage_packed<kAdjThreads>(sm.T, Tm + ch * (kChunk * kChunk), tid);
+    stage_packed<kAdjThreads>(sm.P, Pm + ch * (kChunk * kChunk), tid);
+    if (tid < kChunk) {
+      sm.gam[tid] = GD[ch * kGDFloats + tid];
+      sm.dec[tid] = GD[ch * kGDFloats + kChunk + tid];
+    }
+    __syncthreads();
+
+    // this chunk's dS' for the gradient kernel
+    {
+      float *dst = dSo + ch * DK * (size_t)DV + v0;
+      for (int e = tid; e < DK * kAdjBV / 4; e += kAdjThreads) {
+        const int r = e / (kAdjBV / 4), c4 = 4 * (e % (kAdjBV / 4));
+        *reinterpret_cast<f32x4 *>(dst + (size_t)r * DV + c4) =
+            *reinterpret_cast<const f32x4 *>(&sm.dS[r][c4]);
+      }
+    }
+    // dU = P^T dO + Diag(dec) K dS': 4 x 2 tiles, two per wavefront
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int t = 2 * wid + x, ti = t >> 1, tj = t & 1;
+      const f32x4 a = mm_tile<kChunk>(
+          zero4(), lane, [&](int i, int kk) { return sm.P[kk][16 * ti + i]; },
+          [&](int kk, int j) { return sm.dO[kk][16 * tj + j]; });
+      const f32x4 y = mm_tile<DK>(
+          zero4(), lane, [&](int i, int kk) { return sm.K[16 * ti + i][kk]; },
+          [&](int kk, int j) { return sm.dS[kk][16 * tj + j]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * ti + 4 * kq + e;
+        sm.dU[row][16 * tj + r16] = a[e] + sm.dec[row] * y[e];
+      }
+    }
+    __syncthreads();
+    // dR = T^T dU
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int t = 2 * wid + x, ti = t >> 1, tj = t & 1;
+      const f32x4 rr = mm_tile<kChunk>(
+          zero4(), lane, [&](int i, int kk) { return sm.T[kk][16 * ti + i]; },
+          [&](int kk, int j) { return sm.dU[kk][16 * tj + j]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.dR[16 * ti + 4 * kq + e][16 * tj + r16] = rr[e];
+    }
+    __syncthreads();
+    // dU and dR to the workspace; dV = dR on the chunk's tokens
+    {
+      float *du = dUo + ch * kChunk * (size_t)DV + v0, *dr = dRo + ch * kChunk * (size_t)DV + v0;
+      for (int e = tid; e < kChunk * kAdjBV / 4; e += kAdjThreads) {
+        const int r = e / (kAdjBV / 4), c4 = 4 * (e % (kAdjBV / 4));
+        const f32x4 u = *reinterpret_cast<const f32x4 *>(&sm.dU[r][c4]);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.dR[r][c4]);
+        *reinterpret_cast<f32x4 *>(du + (size_t)r * DV + c4) = u;
+        *reinterpret_cast<f32x4 *>(dr + (size_t)r * DV + c4) = x;
+        if (r < len) {
+          Tin *o = dv + (tok + (size_t)r * H) * DV + v0 + c4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = from_f32<Tin>(x[i]);
+        }
+      }
+    }
+    // dS = exp(G_last) dS' + Q^T Diag(gam) dO - K^T Diag(gam) dR: (DK / 16) x 2 tiles
+    const float gl = sm.gam[kChunk - 1];  // rows past a ragged end repeat G_last
+    constexpr int NX = DK / 32;           // tiles per wavefront
+    f32x4 nd[NX];
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      const int t = wid + 4 * x, mi = t >> 1, tj = t & 1;
+      f32x4 acc = mm_tile<kChunk>(
+          zero4(), lane, [&](int i, int kk) { return sm.Q[kk][16 * mi + i]; },
+          [&](int kk, int j) { return sm.gam[kk] * sm.dO[kk][16 * tj + j]; });
+      acc = mm_tile<kChunk>(
+          acc, lane, [&](int i, int kk) { return -sm.K[kk][16 * mi + i]; },
+          [&](int kk, int j) { return sm.gam[kk] * sm.dR[kk][16 * tj + j]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += gl * sm.dS[16 * mi + 4 * kq + e][16 * tj + r16];
+      nd[x] = acc;
+    }
+    __syncthreads();  // every read of this chunk's tiles and of dS' is done
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      const int t = wid + 4 * x, mi = t >> 1, tj = t & 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.dS[16 * mi + 4 * kq + e][16 * tj + r16] = nd[x][e];
+    }
+  }
+  __syncthreads();
+  if (dS0) {
+    for (int e = tid; e < DK * kAdjBV; e += kAdjThreads) {
+      const int r = e / kAdjBV, c = e % kAdjBV;
+      dS0[sbase + (size_t)r * DV + c] = sm.dS[r][c];
+    }
+  }
+}
+
+namespace {
+
+template <int DK>
+struct GradSmem {
+  float K[kChunk][DK + 4];
+  float X[kChunk][LDC];
+  float A[kChunk][LDC];
+  union {
+    struct {  // the loop over 32-column blocks of d_v
+      float S[DK][LDB], So[DK][LDB];
+      float R[kChunk][LDB], U[kChunk][LDB], dO[kChunk][LDB], dU[kChunk][LDB], dR[kChunk][LDB];
+    } lp;
+    struct {  // the chunk-local algebra after it
+      float Q[kChunk][DK + 4];
+      float P[kChunk][LDC];   // P, then W = dT Diag(b) X^T
+      float dP[kChunk][LDC];  // dP, then dP o Gamma
+      float dT[kChunk][LDC];  // dT, then dL, then dA o Gamma
+    } pa;
+  } u;
+  float gam[kChunk], dec[kChunk], G[kChunk], b[kChunk], den[kChunk], db[kChunk];
+  float rz[kChunk], cz[kChunk];
+  float dots[3][2][kChunk];  // row dots of the three d_v contractions, two partial sums each
+  float red[kGradThreads / 64];
+};
+
+// the (I, J) block of the ten blocks on and below the diagonal, in the order (0,0) (1,0) (1,1)
+// (2,0) (2,1) (2,2) (3,0) .. (3,3)
+__device__ __forceinline__ void lower_block(int b, int &I, int &J) {
+  I = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0;
+  J = b - I * (I + 1) / 2;
+}
+
+}  // namespace
+
+template <typename Tin, int DK>
+__global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
+    const Tin *__restrict__ dO, const float *__restrict__ g, const float *__restrict__ eta,
+    float eps, const float *__restrict__ SN, const float *__restrict__ dSo,
+    const float *__restrict__ dUo, const float *__restrict__ dRo, Tin *__restrict__ dq,
+    Tin *__restrict__ dk, float *__restrict__ dg, float *__restrict__ deta,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq, int H,
+    int DV) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  GradSmem<DK> &sm = *reinterpret_cast<GradSmem<DK> *>(smem_raw);
+  const int n_chunks = chunk_off[n_seq];
+  const int task = blockIdx.x;  // chunk * H + head
+  if (task >= n_chunks * H) return;
+  const int c = task / H, h = task - c * H;
+  int n = 0;
+  {
+    int lo = 0, hi = n_seq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+  }
+  const int t0 = cu[n] + (c - chunk_off[n]) * kChunk;
+  const int len = min(kChunk, cu[n + 1] - t0);
+  const size_t tok = (size_t)t0 * H + h;
+  const size_t ch = (size_t)task;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+
+  // ---- K rows; G, b, the decays
+  stage_rows<DK, DK + 4, kGradThreads>(&sm.K[0][0], k + tok * DK, (size_t)H * DK, len, tid);
+  if (wid == 0) {
+    const float gi = lane < len ? g[tok + (size_t)lane * H] : 0.f;
+    const float G = wave_inclusive_scan(gi, lane);  // rows past the end repeat G_last
+    const float Gl = __shfl(G, kChunk - 1, kWave);
+    sm.G[lane] = G;
+    sm.gam[lane] = __expf(G);
+    sm.dec[lane] = __expf(Gl - G);
+  }
+  __syncthreads();
+  {
+    const int i = tid >> 3, part = tid & 7;  // 8 lanes a row
+    float kk = 0.f;
+    for (int cc = part; cc < DK; cc += 8) kk += sm.K[i][cc] * sm.K[i][cc];
+    kk += __shfl_xor(kk, 1, 8);
+    kk += __shfl_xor(kk, 2, 8);
+    kk += __shfl_xor(kk, 4, 8);
+    if (part == 0) {
+      const float den = kk + eps;
+      sm.den[i] = den;
+      sm.b[i] = i < len ? write_coef(kBetaKaczmarz, eta[tok + (size_t)i * H], den, 1.f) : 0.f;
+    }
+  }
+  // ---- A = strict_lower(Gamma o K K^T): all 16 tiles, two per wavefront (zeros above)
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int t = wid + 8 * x, I = t >> 2, J = t & 3;
+    f32x4 acc = zero4();
+    if (J <= I)
+      acc = mm_tile<DK>(
+          acc, lane, [&](int i, int kk) { return sm.K[16 * I + i][kk]; },
+          [&](int kk, int j) { return sm.K[16 * J + j][kk]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
+      sm.A[row][col] = row > col ? __expf(sm.G[row] - sm.G[col]) * acc[e] : 0.f;
+    }
+  }
+  __syncthreads();
+  // ---- X = (I + Diag(b) A)^{-1} by forward substitution: wavefront w takes columns
+  //      8 w .. 8 w + 7, 8 lanes a column; lane `part` keeps X[l][j] for l = part + 8 m in
+  //      registers and sums those terms of each row's dot product, and three DPP steps sum
+  //      the 8 partial sums
+  {
+    const int j = 8 * wid + (lane >> 3), part = lane & 7;
+    float xr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int l = part + 8 * m;
+        if (8 * m < i) acc += (l < i ? sm.A[i][l] : 0.f) * xr[m];
+      }
+      acc += dpp_f32<0xB1>(acc);   // quad_perm [1,0,3,2]
+      acc += dpp_f32<0x4E>(acc);   // quad_perm [2,3,0,1]
+      acc += dpp_f32<0x141>(acc);  // row_half_mirror
+      const float xv = i == j ? 1.f : (i > j ? -sm.b[i] * acc : 0.f);
+      if (part == (i & 7)) xr[i >> 3] = xv;
+      if (part == 0) sm.X[i][j] = xv;
+    }
+  }
+
+  // ---- the contractions over d_v, 32 columns at a time:
+  //      Y = K S -> R = V - Diag(gam) Y, U = T R; then accumulated in registers
+  //      qa = Diag(gam) dO S^T, ka = -Diag(gam) dR S^T, kb = Diag(dec) U dS'^T (64 x DK),
+  //      dP = dO U^T, dT = dU R^T (their lower blocks) and <dS', S>
+  constexpr int NM = DK / 32;  // 64 x DK tiles per wavefront: t = wid + 8 m, rows 16 (wid & 3)
+  const int mti = wid & 3;
+  f32x4 qa[NM], ka[NM], kb[NM], pt[3];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) qa[m] = ka[m] = kb[m] = zero4();
+#pragma unroll
+  for (int x = 0; x < 3; ++x) pt[x] = zero4();
+  float sc = 0.f;
+  const float *Sb = SN + ch * DK * (size_t)DV, *Sob = dSo + ch * DK * (size_t)DV;
+  const float *dUb = dUo + ch * kChunk * (size_t)DV, *dRb = dRo + ch * kChunk * (size_t)DV;
+  for (int v0 = 0; v0 < DV; v0 += kAdjBV) {
+    __syncthreads();  // the previous block's reads (and X's writes) are done
+    for (int e = tid; e < DK * kAdjBV / 4; e += kGradThreads) {
+      const int r = e / (kAdjBV / 4), c4 = 4 * (e % (kAdjBV / 4));
+      const f32x4 s = ld4(Sb + (size_t)r * DV + v0 + c4), so = ld4(Sob + (size_t)r * DV + v0 + c4);
+      *reinterpret_cast<f32x4 *>(&sm.u.lp.S[r][c4]) = s;
+      *reinterpret_cast<f32x4 *>(&sm.u.lp.So[r][c4]) = so;
+      sc += s[0] * so[0] + s[1] * so[1] + s[2] * so[2] + s[3] * so[3];
+    }
+    stage_rows<kAdjBV, LDB, kGradThreads>(&sm.u.lp.R[0][0], v + tok * DV + v0, (size_t)H * DV,
+                                          len, tid);
+    stage_rows<kAdjBV, LDB, kGradThreads>(&sm.u.lp.dO[0][0], dO + tok * DV + v0, (size_t)H * DV,
+                                          len, tid);
+    stage_rows<kAdjBV, LDB, kGradThreads>(&sm.u.lp.dU[0][0], dUb + v0, (size_t)DV, kChunk, tid);
+    stage_rows<kAdjBV, LDB, kGradThreads>(&sm.u.lp.dR[0][0], dRb + v0, (size_t)DV, kChunk, tid);
+    __syncthreads();
+    const int yi = wid >> 1, yj = wid & 1;  // this wavefront's 16 x 16 tile of R and U
+    {
+      const f32x4 y = mm_tile<DK>(
+          zero4(), lane, [&](int i, int kk) { return sm.K[16 * yi + i][kk]; },
+          [&](int kk, int j) { return sm.u.lp.S[kk][16 * yj + j]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * yi + 4 * kq + e;
+        sm.u.lp.R[row][16 * yj + r16] -= sm.gam[row] * y[e];
+      }
+    }
+    __syncthreads();
+    {
+      const f32x4 uu = mm_tile<kChunk>(
+          zero4(), lane, [&](int i, int kk) { return sm.X[16 * yi + i][kk]; },
+          [&](int kk, int j) { return sm.b[kk] * sm.u.lp.R[kk][16 * yj + j]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.u.lp.U[16 * yi + 4 * kq + e][16 * yj + r16] = uu[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int tj = (wid >> 2) + 2 * m;  // column tile of 16 key dims
+      qa[m] = mm_tile<kAdjBV>(
+          qa[m], lane, [&](int i, int kk) { return sm.gam[16 * mti + i] * sm.u.lp.dO[16 * mti + i][kk]; },
+          [&](int kk, int j) { return sm.u.lp.S[16 * tj + j][kk]; });
+      ka[m] = mm_tile<kAdjBV>(
+          ka[m], lane, [&](int i, int kk) { return -sm.gam[16 * mti + i] * sm.u.lp.dR[16 * mti + i][kk]; },
+          [&](int kk, int j) { return sm.u.lp.S[16 * tj + j][kk]; });
+      kb[m] = mm_tile<kAdjBV>(
+          kb[m], lane, [&](int i, int kk) { return sm.dec[16 * mti + i] * sm.u.lp.U[16 * mti + i][kk]; },
+          [&](int kk, int j) { return sm.u.lp.So[16 * tj + j][kk]; });
+    }
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      const int jb = wid + 8 * x;  // jobs 0..9: blocks of dP; 10..19: blocks of dT
+      if (jb < 20) {
+        int I, J;
+        lower_block(jb % 10, I, J);
+        if (jb < 10)
+          pt[x] = mm_tile<kAdjBV>(
+              pt[x], lane, [&](int i, int kk) { return sm.u.lp.dO[16 * I + i][kk]; },
+              [&](int kk, int j) { return sm.u.lp.U[16 * J + j][kk]; });
+        else
+          pt[x] = mm_tile<kAdjBV>(
+              pt[x], lane, [&](int i, int kk) { return sm.u.lp.dU[16 * I + i][kk]; },
+              [&](int kk, int j) { return sm.u.lp.R[16 * J + j][kk]; });
+      }
+    }
+  }
+  sc = wave_sum(sc);
+  if (lane == 0) sm.red[wid] = sc;
+  __syncthreads();  // the loop's LDS is free
+
+  // ---- Q rows, P = lower(Gamma o Q K^T), dP and dT (lower, zeros above)
+  stage_rows<DK, DK + 4, kGradThreads>(&sm.u.pa.Q[0][0], q + tok * DK, (size_t)H * DK, len, tid);
+  for (int e = tid; e < kChunk * kChunk; e += kGradThreads) {
+    const int r = e >> 6, cc = e & 63;
+    if ((cc >> 4) > (r >> 4)) { sm.u.pa.dP[r][cc] = 0.f; sm.u.pa.dT[r][cc] = 0.f; }
+  }
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    const int jb = wid + 8 * x;
+    if (jb < 20) {
+      int I, J;
+      lower_block(jb % 10, I, J);
+      float (*dst)[LDC] = jb < 10 ? sm.u.pa.dP : sm.u.pa.dT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
+        dst[row][col] = col <= row ? pt[x][e] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    // P's lower blocks, two jobs per wavefront (10 blocks; zeros above the diagonal blocks)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int t = wid + 8 * x, I = t >> 2, J = t & 3;
+      f32x4 acc = zero4();
+      if (J <= I)
+        acc = mm_tile<DK>(
+            acc, lane, [&](int i, int kk) { return sm.u.pa.Q[16 * I + i][kk]; },
+            [&](int kk, int j) { return sm.K[16 * J + j][kk]; });
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
+        sm.u.pa.P[row][col] = col <= row ? __expf(sm.G[row] - sm.G[col]) * acc[e] : 0.f;
+      }
+    }
+    // row dots q_i . qa_i, k_i . ka_i, k_i . kb_i: this wavefront's partial over its column
+    // tiles, then its 16-lane row sums
+    float dq4[4] = {0.f, 0.f, 0.f, 0.f}, da4[4] = {0.f, 0.f, 0.f, 0.f}, db4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int col = 16 * ((wid >> 2) + 2 * m) + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * mti + 4 * kq + e;
+        dq4[e] += qa[m][e] * sm.u.pa.Q[row][col];
+        da4[e] += ka[m][e] * sm.K[row][col];
+        db4[e] += kb[m][e] * sm.K[row][col];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dq4[e] = row16_sum(dq4[e]);
+      da4[e] = row16_sum(da4[e]);
+      db4[e] = row16_sum(db4[e]);
+      if (r16 == 0) {
+        const int row = 16 * mti + 4 * kq + e;
+        sm.dots[0][wid >> 2][row] = dq4[e];
+        sm.dots[1][wid >> 2][row] = da4[e];
+        sm.dots[2][wid >> 2][row] = db4[e];
+      }
+    }
+  }
+  __syncthreads();
+  // ---- db from T: column sums of dT o X; the dP o P part of Z's row and column sums;
+  //      W = dT Diag(b) X^T into registers
+  if (tid < kChunk) {
+    float s = 0.f;
+    for (int i = 0; i < kChunk; ++i) s += sm.u.pa.dT[i][tid] * sm.X[i][tid];
+    sm.db[tid] = s;
+  } else if (tid < 2 * kChunk) {
+    const int i = tid - kChunk;
+    float s = 0.f;
+    for (int j = 0; j < kChunk; ++j) s += sm.u.pa.dP[i][j] * sm.u.pa.P[i][j];
+    sm.rz[i] = s;
+  } else if (tid < 3 * kChunk) {
+    const int j = tid - 2 * kChunk;
+    float s = 0.f;
+    for (int i = 0; i < kChunk; ++i) s += sm.u.pa.dP[i][j] * sm.u.pa.P[i][j];
+    sm.cz[j] = s;
+  }
+  f32x4 w[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int t = wid + 8 * x, I = t >> 2, J = t & 3;
+    w[x] = mm_tile<kChunk>(
+        zero4(), lane, [&](int i, int kk) { return sm.u.pa.dT[16 * I + i][kk] * sm.b[kk]; },
+        [&](int kk, int j) { return sm.X[16 * J + j][kk]; });
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int t = wid + 8 * x, I = t >> 2, J = t & 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.u.pa.P[16 * I + 4 * kq + e][16 * J + r16] = w[x][e];
+  }
+  __syncthreads();
+  // ---- dL = -strict_lower(X^T W) into dT's place
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int t = wid + 8 * x, I = t >> 2, J = t & 3;
+    f32x4 acc = zero4();
+    if (J <= I)
+      acc = mm_tile<kChunk>(
+          acc, lane, [&](int i, int kk) { return sm.X[kk][16 * I + i]; },
+          [&](int kk, int j) { return sm.u.pa.P[kk][16 * J + j]; });
+    w[x] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int t = wid + 8 * x, I = t >> 2, J = t & 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
+      sm.u.pa.dT[row][col] = col < row ? -w[x][e] : 0.f;
+    }
+  }
+  __syncthreads();
+  // ---- db += row sums of dL o A; the dA o A part of Z (dA = Diag(b) dL)
+  if (tid < kChunk) {
+    float s = 0.f;
+    for (int j = 0; j < kChunk; ++j) s += sm.u.pa.dT[tid][j] * sm.A[tid][j];
+    sm.db[tid] += s;
+    sm.rz[tid] += sm.b[tid] * s;
+  } else if (tid < 2 * kChunk) {
+    const int j = tid - kChunk;
+    float s = 0.f;
+    for (int i = 0; i < kChunk; ++i) s += sm.b[i] * sm.u.pa.dT[i][j] * sm.A[i][j];
+    sm.cz[j] += s;
+  }
+  __syncthreads();
+  // ---- dP o Gamma and dA o Gamma in place
+  for (int e = tid; e < kChunk * kChunk; e += kGradThreads) {
+    const int r = e >> 6, cc = e & 63;
+    const float gm = cc <= r ? __expf(sm.G[r] - sm.G[cc]) : 0.f;
+    sm.u.pa.dP[r][cc] *= gm;
+    sm.u.pa.dT[r][cc] *= sm.b[r] * gm;
+  }
+  __syncthreads();
+  // ---- dq = qa + (dP o Gamma) K;  dk = ka + kb + (dP o Gamma)^T Q + (dA o Gamma) K
+  //      + (dA o Gamma)^T K - Diag(2 b db / den) K
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int tj = (wid >> 2) + 2 * m;
+    f32x4 aq = mm_tile<kChunk>(
+        qa[m], lane, [&](int i, int kk) { return sm.u.pa.dP[16 * mti + i][kk]; },
+        [&](int kk, int j) { return sm.K[kk][16 * tj + j]; });
+    f32x4 ak = ka[m] + kb[m];
+    ak = mm_tile<kChunk>(
+        ak, lane, [&](int i, int kk) { return sm.u.pa.dP[kk][16 * mti + i]; },
+        [&](int kk, int j) { return sm.u.pa.Q[kk][16 * tj + j]; });
+    ak = mm_tile<kChunk>(
+        ak, lane,
+        [&](int i, int kk) { return sm.u.pa.dT[16 * mti + i][kk] + sm.u.pa.dT[kk][16 * mti + i]; },
+        [&](int kk, int j) { return sm.K[kk][16 * tj + j]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * mti + 4 * kq + e, col = 16 * tj + r16;
+      const float den = sm.den[row];
+      const float cb = den != 0.f ? -2.f * sm.b[row] * sm.db[row] * __builtin_amdgcn_rcpf(den) : 0.f;
+      ak[e] += cb * sm.K[row][col];
+      if (row < len) {
+        const size_t o = (tok + (size_t)row * H) * DK + col;
+        dq[o] = from_f32<Tin>(aq[e]);
+        dk[o] = from_f32<Tin>(ak[e]);
+      }
+    }
+  }
+  // ---- dG, its reverse prefix sum dg, and deta (one wavefront, lane = position)
+  if (wid == 0) {
+    const int i = lane;
+    float dGi = sm.dots[0][0][i] + sm.dots[0][1][i] + sm.dots[1][0][i] + sm.dots[1][1][i] -
+                sm.dots[2][0][i] - sm.dots[2][1][i] + sm.rz[i] - sm.cz[i];
+    const float kb_i = i < len ? sm.dots[2][0][i] + sm.dots[2][1][i] : 0.f;
+    const float kb_all = wave_sum(kb_i);
+    float scs = 0.f;
+#pragma unroll
+    for (int x = 0; x < kGradThreads / 64; ++x) scs += sm.red[x];
+    if (i == len - 1) dGi += sm.gam[kChunk - 1] * scs + kb_all;
+    if (i >= len) dGi = 0.f;
+    // reverse inclusive prefix: scan over the reversed lane order
+    const float rev = wave_inclusive_scan(__shfl(dGi, kChunk - 1 - i, kWave), lane);
+    const float dgi = __shfl(rev, kChunk - 1 - i, kWave);
+    if (i < len) {
+      dg[tok + (size_t)i * H] = dgi;
+      const float den = sm.den[i];
+      deta[tok + (size_t)i * H] = den != 0.f ? sm.db[i] * __builtin_amdgcn_rcpf(den) : 0.f;
+    }
+  }
+}
+
+template <typename Tin, int DK>
+static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void *v,
+                               const void *dO, const float *g, const float *eta, float eps,
+                               const float *GD, const void *T, const void *P, const float *dST,
+                               const float *SN, float *dSo, float *dU, float *dR, void *dq,
+                               void *dk, void *dv, float *dg, float *deta, float *dS0,
+                               SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
+                               hipStream_t stream) {
+  const size_t smA = sizeof(AdjSmem<DK>), smG = sizeof(GradSmem<DK>);
+  static_assert(sizeof(AdjSmem<DK>) <= 160 * 1024 && sizeof(GradSmem<DK>) <= 160 * 1024,
+                "LDS budget");
+  static bool attr_set = false;  // benign race: every thread sets the same values
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_bwd_scan_kernel<Tin, DK>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smA);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_bwd_grad_kernel<Tin, DK>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smG);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
+  const int64_t scan_blocks = (int64_t)n_seq * H * (d_v / kAdjBV);
+  if (scan_blocks > 0)
+    hipLaunchKernelGGL((kla_bwd_scan_kernel<Tin, DK>), dim3((unsigned)scan_blocks),
+                       dim3(kAdjThreads), smA, stream, qt, kt, static_cast<const Tin *>(dO), GD,
+                       static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0, dSo,
+                       dU, dR, static_cast<Tin *>(dv), t.cu, t.chunk_off, H, d_v);
+  const int64_t grad_blocks = n_chunks_ub * H;
+  if (grad_blocks > 0)
+    hipLaunchKernelGGL((kla_bwd_grad_kernel<Tin, DK>), dim3((unsigned)grad_blocks),
+                       dim3(kGradThreads), smG, stream, qt, kt, static_cast<const Tin *>(v),
+                       static_cast<const Tin *>(dO), g, eta, eps, SN, dSo, dU, dR,
+                       static_cast<Tin *>(dq), static_cast<Tin *>(dk), dg, deta, t.cu,
+                       t.chunk_off, n_seq, H, d_v);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
+                      const void *dO, const float *g, const float *eta, float eps,
+                      const float *GD, const void *T, const void *P, const float *dST,
+                      const float *SN, float *dSo, float *dU, float *dR, void *dq, void *dk,
+                      void *dv, float *dg, float *deta, float *dS0, SeqTables t, int32_t n_seq,
+                      int64_t n_chunks_ub, int32_t H, hipStream_t stream) {
+#define KLA_BWD(TIN, DK_)                                                                     \
+  return launch_bwd_t<TIN, DK_>(d_v, q, k, v, dO, g, eta, eps, GD, T, P, dST, SN, dSo, dU, dR, \
+                                dq, dk, dv, dg, deta, dS0, t, n_seq, n_chunks_ub, H, stream);
+  if (dt == Dtype::BF16) {
+    if (d_k == 128) { KLA_BWD(__bf16, 128) }
+    KLA_BWD(__bf16, 64)
+  }
+  if (d_k == 128) { KLA_BWD(float, 128) }
+  KLA_BWD(float, 64)
+#undef KLA_BWD
+}
+
+}  // namespace kla

@@ -178,7 +178,7 @@ struct DmaPlan {
 };
 
 // One workgroup fills a CU's LDS; its waves run at most two to a SIMD.
-template <typename Tin, int DK, typename SHP, bool DIAG>
+template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES>
 __global__ __launch_bounds__(SHP::THREADS)
 __attribute__((amdgpu_waves_per_eu(SHP::THREADS > 256 ? 2 : 1, SHP::THREADS > 256 ? 2 : 1)))
 void kla_scan_kernel(
@@ -186,7 +186,8 @@ void kla_scan_kernel(
     const float *__restrict__ GD, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
     const float *S0, Tin *__restrict__ o, float *S_T, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int n_seq, int H, int DV, const Tin *__restrict__ KG,
-    const Tin *__restrict__ QG, const Tin *__restrict__ KD, const float *__restrict__ GC) {
+    const Tin *__restrict__ QG, const Tin *__restrict__ KD, const float *__restrict__ GC,
+    float *__restrict__ SN) {
   constexpr int kBV = SHP::BV, kConsumers = SHP::NC, kScanThreads = SHP::THREADS;
   using SM = ScanSmem<Tin, DK, kBV, DIAG>;
   using SL = ScanSlot<Tin, DK, kBV, DIAG>;
@@ -379,6 +380,13 @@ void kla_scan_kernel(
   // One chunk.  All LDS operands of a phase are read into registers before the phase's
   // MFMAs, and the next phase's reads are issued while those MFMAs run.
   auto c_step = [&](int c, const SL &s) {
+    if constexpr (STATES) {  // the chunk's incoming state, for the backward pass
+      float *dst = SN + ((size_t)(cbase + c) * H + h) * DK * (size_t)DV + v0 + col;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)tmap(m, kg, i) * DV] = Sacc[m][i];
+    }
     FragT Sop[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) Sop[ks] = accB(Sacc[2 * ks], Sacc[2 * ks + 1]);
@@ -598,11 +606,11 @@ void kla_scan_kernel(
   }
 }
 
-template <typename Tin, int DK, typename SHP, bool DIAG>
+template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES>
 static hipError_t launch_scan_s(int d_v, const void *q, const void *k, const void *v,
                                 const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream, const DiagTiles *dg) {
+                                hipStream_t stream, const DiagTiles *dg, float *SN) {
   using SMT = ScanSmem<Tin, DK, SHP::BV, DIAG>;
   using SLT = ScanSlot<Tin, DK, SHP::BV, DIAG>;
   static_assert(sizeof(SMT) <= kLdsBytes, "LDS budget");
@@ -613,21 +621,21 @@ static hipError_t launch_scan_s(int d_v, const void *q, const void *k, const voi
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP, DIAG>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP, DIAG, STATES>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t blocks = (int64_t)n_seq * H * (d_v / SHP::BV);
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK, SHP, DIAG>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK, SHP, DIAG, STATES>), dim3((unsigned)blocks),
                      dim3(SHP::THREADS), smem, stream, static_cast<const Tin *>(q),
                      static_cast<const Tin *>(k), static_cast<const Tin *>(v), GD,
                      static_cast<const Tin *>(T), static_cast<const Tin *>(P), S0,
                      static_cast<Tin *>(o), S_T, t.cu, t.chunk_off, n_seq, H, d_v,
                      static_cast<const Tin *>(dg ? dg->kg : nullptr),
                      static_cast<const Tin *>(dg ? dg->qg : nullptr),
-                     static_cast<const Tin *>(dg ? dg->kd : nullptr), dg ? dg->gc : nullptr);
+                     static_cast<const Tin *>(dg ? dg->kd : nullptr), dg ? dg->gc : nullptr, SN);
   return hipGetLastError();
 }
 
@@ -648,47 +656,53 @@ static int device_cus() {
 // The narrow shape while its grid fits the chip in one wave of workgroups (more of them
 // would only queue behind each other while their staging traffic adds up); the wide shape,
 // which stages each tile once for 64 columns, beyond that.
-template <typename Tin, int DK, bool DIAG>
+template <typename Tin, int DK, bool DIAG, bool STATES>
 static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const void *v,
                                 const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream, const DiagTiles *dg) {
+                                hipStream_t stream, const DiagTiles *dg, float *SN) {
   const int64_t narrow_blocks = (int64_t)n_seq * H * (d_v / ScanNarrow::BV);
   const int cus = device_cus();
   if (cus > 0 && narrow_blocks > cus)
-    return launch_scan_s<Tin, DK, ScanWide, DIAG>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq,
-                                                  H, stream, dg);
-  return launch_scan_s<Tin, DK, ScanNarrow, DIAG>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq,
-                                                  H, stream, dg);
+    return launch_scan_s<Tin, DK, ScanWide, DIAG, STATES>(d_v, q, k, v, GD, T, P, S0, o, S_T, t,
+                                                          n_seq, H, stream, dg, SN);
+  return launch_scan_s<Tin, DK, ScanNarrow, DIAG, STATES>(d_v, q, k, v, GD, T, P, S0, o, S_T, t,
+                                                          n_seq, H, stream, dg, SN);
 }
 
 template <typename Tin, int DK>
 static hipError_t launch_scan_g(int d_v, const void *q, const void *k, const void *v,
                                 const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream, const DiagTiles *dg) {
-  if (dg)
-    return launch_scan_t<Tin, DK, true>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
-                                        dg);
-  return launch_scan_t<Tin, DK, false>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
-                                       dg);
+                                hipStream_t stream, const DiagTiles *dg, float *SN) {
+  if (dg) {
+    if (SN) return hipErrorInvalidValue;  // no stored states under diagonal gating
+    return launch_scan_t<Tin, DK, true, false>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
+                                               stream, dg, nullptr);
+  }
+  if (SN)
+    return launch_scan_t<Tin, DK, false, true>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
+                                               stream, nullptr, SN);
+  return launch_scan_t<Tin, DK, false, false>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
+                                              stream, nullptr, nullptr);
 }
 
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                        const float *GD, const void *T, const void *P, const float *S0, void *o,
                        float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream,
-                       const DiagTiles *dg) {
+                       const DiagTiles *dg, float *SN) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
       return launch_scan_g<__bf16, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
-                                        dg);
+                                        dg, SN);
     return launch_scan_g<__bf16, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
-                                     dg);
+                                     dg, SN);
   }
   if (d_k == 128)
     return launch_scan_g<float, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
-                                     dg);
-  return launch_scan_g<float, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream, dg);
+                                     dg, SN);
+  return launch_scan_g<float, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream, dg,
+                                  SN);
 }
 
 }  // namespace kla

@@ -259,6 +259,44 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const
                               int32_t d_v, kla_dtype dtype, const kla_options *opts,
                               void *stream);
 
+/*
+ * Backward pass of the chunkwise prefill: the gradients (dq, dk, dv, dg, deta,
+ * dS0) of the scalar loss <dO, o> + <dS_T, S_T> for the default variant
+ * (Kaczmarz coefficient of Eq. (3), one scalar gate per token-head,
+ * o_t = q_t S_t).  The paper trains with the chunkwise algorithm (section 4,
+ * Propositions 3-4, Eq. (7)-(9)) but derives no backward pass; these are the
+ * exact derivatives of that chunk solve, so of the tokenwise recurrence
+ * (Algorithm 1), up to rounding.
+ *
+ *   q, k, v, g, eta, eps, S0, cu_seqlens, cu_seqlens_host, sizes, dtype:
+ *               the forward call's arguments, as for kla_prefill_chunked
+ *   dO          [total_tokens, n_heads, d_v]   dtype (cotangent of o)
+ *   dS_T        [n_seq, n_heads, d_k, d_v] fp32, or NULL for zeros
+ *   dq, dk      [total_tokens, n_heads, d_k]   dtype (written)
+ *   dv          [total_tokens, n_heads, d_v]   dtype (written)
+ *   dg, deta    [total_tokens, n_heads]        fp32 (written)
+ *   dS0         [n_seq, n_heads, d_k, d_v] fp32 (written), or NULL
+ *   workspace   device buffer of at least kla_prefill_backward_workspace_bytes
+ *               bytes, 256-byte aligned; contents are scratch.  It holds the
+ *               forward pass run again with every chunk's incoming state
+ *               stored, the cotangent of every chunk's outgoing state and the
+ *               per-chunk dU and dR, all fp32.
+ * The gradient buffers must not overlap each other, the inputs or the
+ * workspace.  Alignment, size limits and errors as for kla_prefill_chunked;
+ * zero-length sequences get dS0 = dS_T.
+ */
+size_t kla_prefill_backward_workspace_bytes(int32_t n_seq, int32_t total_tokens,
+                                            int32_t n_heads, int32_t d_k, int32_t d_v,
+                                            kla_dtype dtype);
+kla_status kla_prefill_backward(const void *q, const void *k, const void *v, const float *g,
+                                const float *eta, float eps, const float *S0, const void *dO,
+                                const float *dS_T, void *dq, void *dk, void *dv, float *dg,
+                                float *deta, float *dS0, const int32_t *cu_seqlens,
+                                const int32_t *cu_seqlens_host, int32_t n_seq,
+                                int32_t total_tokens, int32_t n_heads, int32_t d_k, int32_t d_v,
+                                kla_dtype dtype, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* Static description of a status code. */
 const char *kla_status_string(kla_status status);
 

@@ -135,6 +135,18 @@ def prefill_inputs(w, device="cpu", seed=None, T=None, lens=None, n_seq=None, H=
                 dtype=w.dtype)
 
 
+def cotangents(inp: dict, seed: int, device="cpu") -> dict:
+    """Seeded cotangents for a backward call on the inputs `inp`: dO ~ N(0, 1) shaped like
+    the output o (in the inputs' dtype) and dS_T ~ N(0, 1) shaped like the final state
+    (fp32)."""
+    n_tok, H, _ = inp["q"].shape
+    d_k, d_v = inp["k"].shape[-1], inp["v"].shape[-1]
+    gen = _gen(device, seed)
+    dO = torch.randn(n_tok, H, d_v, generator=gen, device=device)
+    dST = torch.randn(inp["n_seq"], H, d_k, d_v, generator=gen, device=device)
+    return dict(dO=dO.to(inp["q"].dtype).contiguous(), dS_T=dST.contiguous())
+
+
 def hard_variant(inp: dict) -> dict:
     """Hard-projection variant: eta = 1, g = 0, eps = 0, and q := k (so o_t must equal v_t)."""
     out = dict(inp)

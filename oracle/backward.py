@@ -47,18 +47,21 @@ def _sequence(q, k, v, g, eta, eps, S0):
     return O, S
 
 
-def prefill_backward(q, k, v, g, eta, eps, dO, S0=None, dS_T=None, cu_seqlens=None):
+def prefill_backward(q, k, v, g, eta, eps, dO, S0=None, dS_T=None, cu_seqlens=None, n_seq=1):
     """Gradients of the prefill for the cotangents dO [n_tok, H, dv] and dS_T [n_seq, H, dk, dv].
 
     Inputs as for :func:`oracle.prefill` (q, k [n_tok, H, dk]; v [n_tok, H, dv];
-    g, eta [n_tok, H]; S0 [n_seq, H, dk, dv] or None = zeros; dS_T None = zeros).
+    g, eta [n_tok, H]; S0 [n_seq, H, dk, dv] or None = zeros; dS_T None = zeros);
+    without cu_seqlens the tokens are n_seq sequences of equal length.
     Returns numpy float64 arrays (dq, dk, dv, dg, deta, dS0), shaped like the inputs.
     """
     q, k, v, g, eta, dO = (_t(x) for x in (q, k, v, g, eta, dO))
     n_tok, H, dk = q.shape
     dv_ = v.shape[-1]
     if cu_seqlens is None:
-        cu = np.array([0, n_tok], dtype=np.int64)
+        if n_tok % n_seq:
+            raise ValueError("dense input needs n_tok divisible by n_seq")
+        cu = np.arange(n_seq + 1, dtype=np.int64) * (n_tok // n_seq)
     else:
         cu = np.asarray(cu_seqlens, dtype=np.int64)
     n_seq = len(cu) - 1

@@ -197,3 +197,45 @@ def test_diagonal_gate_workspace_and_entry_points(lib):
                                     4, 128, 128, BF16, FAKE * 64, nb, _opts(diag=1), None)
     assert st == UNSUPPORTED
     assert "chunked_ex" in lib.kla_last_error().decode()
+
+
+def _bwd_call(lib, **over):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, eta=FAKE * 5, eps=1e-6, S0=None,
+             dO=FAKE * 6, dST=None, dq=FAKE * 7, dk=FAKE * 8, dv=FAKE * 9, dg=FAKE * 10,
+             deta=FAKE * 11, dS0=FAKE * 12, cu=None, cu_host=None, n_seq=2, n_tok=256, H=4,
+             dk_=128, dv_=128, dtype=BF16, ws=FAKE * 64, ws_bytes=None)
+    a.update(over)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.kla_prefill_backward_workspace_bytes(a["n_seq"], a["n_tok"], a["H"],
+                                                                 128, 128, BF16)
+    return lib.kla_prefill_backward(
+        a["q"], a["k"], a["v"], a["g"], a["eta"], a["eps"], a["S0"], a["dO"], a["dST"], a["dq"],
+        a["dk"], a["dv"], a["dg"], a["deta"], a["dS0"], a["cu"], a["cu_host"], a["n_seq"],
+        a["n_tok"], a["H"], a["dk_"], a["dv_"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+def test_backward_workspace_and_errors(lib):
+    # the backward workspace holds the forward one plus, per chunk-head, the incoming state
+    # and the outgoing state's cotangent (d_k x d_v fp32 each), dU and dR (64 x d_v fp32
+    # each), and the forward output once more
+    n_seq, n_tok, H, dk, dv = 4, 16384, 16, 128, 128
+    nch = (n_tok + 63) // 64 + n_seq
+    nb = kla.kla_prefill_backward_workspace_bytes(n_seq, n_tok, H, dk, dv)
+    base = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv)
+    assert nb >= base + 4 * nch * H * (2 * dk * dv + 2 * 64 * dv) + 2 * n_tok * H * dv
+    assert nb % 256 == 0
+    assert kla.kla_prefill_backward_workspace_bytes(n_seq, n_tok, H, 96, dv) == 0
+    cases = [
+        (dict(ws_bytes=1024), WORKSPACE),
+        (dict(dk_=96), UNSUPPORTED),
+        (dict(dO=None), INVALID),
+        (dict(dq=None), INVALID),
+        (dict(dk=FAKE + 4), INVALID),                 # misaligned
+        (dict(dg=FAKE * 5), INVALID),                 # dg overlaps eta
+        (dict(dv=FAKE * 7), INVALID),                 # two gradients in one buffer
+        (dict(n_tok=255), INVALID),                   # dense: 255 tokens over 2 sequences
+        (dict(eps=-1.0), INVALID),
+        (dict(dtype=7), UNSUPPORTED),
+    ]
+    for over, want in cases:
+        assert _bwd_call(lib, **over) == want, (over, lib.kla_last_error())

@@ -1,0 +1,123 @@
+"""Parity of the backward pass (kla_prefill_backward, through the C ABI) with the fp64
+oracle's reverse-mode gradients of the tokenwise recurrence (oracle/backward.py), on seeded
+inputs and cotangents.
+
+Bars (per tensor, err = max|x - y| / max|y| with y the oracle), for each of dq, dk, dv, dg,
+deta and dS0, the forward's bars: fp32 inputs 1e-4; bf16 inputs 2e-2 (dq, dk, dv are rounded
+to bf16 on output, and the stored forward tiles T and P are bf16).  The last test runs the
+full prefill workload (4 sequences x 4096 tokens x 16 heads, d = 128, bf16) in the launch
+configuration bench.py times and checks two sampled (sequence, head) pairs: sequences and
+heads are independent, so the oracle runs on those alone.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kla_inputs as ki
+from oracle import backward as ob
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+DEV = "cuda"
+NAMES = ("dq", "dk", "dv", "dg", "deta", "dS0")
+
+
+def err(x, y):
+    x = x.detach().double().cpu().numpy()
+    y = np.asarray(y, np.float64)
+    assert x.shape == y.shape, (x.shape, y.shape)
+    assert np.all(np.isfinite(x)), "non-finite values in device output"
+    return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
+
+
+@pytest.fixture(scope="module")
+def kla():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import gated_delta_rule_kla_amd as m
+    m.load_library()
+    return m
+
+
+def run_case(kla, inp, ct, tol, with_state=True, with_dst=True):
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    S0 = d["S0"] if with_state else None
+    dST = ct["dS_T"].to(DEV) if with_dst else None
+    grads = kla.kla_prefill_backward(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                     ct["dO"].to(DEV), S0=S0, dS_T=dST,
+                                     cu_seqlens=d["cu_seqlens"], n_seq=d["n_seq"])
+    torch.cuda.synchronize()
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy()
+    f64 = lambda t: None if t is None else t.double().numpy()
+    ref = ob.prefill_backward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["g"]),
+                              f64(inp["eta"]), inp["eps"], f64(ct["dO"]),
+                              S0=f64(inp["S0"]) if with_state else None,
+                              dS_T=f64(ct["dS_T"]) if with_dst else None, cu_seqlens=cu,
+                              n_seq=inp["n_seq"])
+    for name, x, y in zip(NAMES, grads, ref):
+        e = err(x, y)
+        print(f"  {name}: err {e:.3e} (bar {tol:g})", flush=True)
+        assert e < tol, f"{name}: err {e:.3e} >= {tol:g}"
+
+
+CASES = {
+    # name: (workload, overrides)
+    "tiny_fp32_T256_d64": (0, dict()),
+    "fp32_ragged_packed": (0, dict(lens=(150, 64, 5, 0, 1, 70), H=2)),
+    "bf16_d128_T300": (1, dict(T=300, n_seq=2, H=3)),
+    "bf16_packed_dv256": (4, dict(lens=(100, 0, 200, 33), H=2)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_backward_matches_oracle(kla, case):
+    w, over = CASES[case]
+    inp = ki.prefill_inputs(w, **over)
+    if inp["S0"] is None:  # give every case a nonzero incoming state
+        gen = torch.Generator().manual_seed(7)
+        inp["S0"] = 0.3 * torch.randn(inp["n_seq"], inp["q"].shape[1], inp["k"].shape[-1],
+                                      inp["v"].shape[-1], generator=gen)
+    ct = ki.cotangents(inp, seed=1000 + len(case))
+    print(f"case {case}", flush=True)
+    run_case(kla, inp, ct, TOL[inp["dtype"]])
+
+
+def test_backward_without_state_or_final_cotangent(kla):
+    inp = ki.prefill_inputs(0, T=200)
+    ct = ki.cotangents(inp, seed=5)
+    run_case(kla, inp, ct, TOL[torch.float32], with_state=False, with_dst=False)
+
+
+def test_backward_strong_decay(kla):
+    # log-decays down to -8 per token: exp(G) spans many decades inside one chunk
+    inp = ki.prefill_inputs(0, T=192)
+    gen = torch.Generator().manual_seed(9)
+    inp["g"] = (-8.0 * torch.rand(inp["g"].shape, generator=gen)).contiguous()
+    ct = ki.cotangents(inp, seed=6)
+    run_case(kla, inp, ct, TOL[torch.float32])
+
+
+def test_backward_full_workload_sampled(kla):
+    inp = ki.prefill_inputs(1)
+    ct = ki.cotangents(inp, seed=2024)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    grads = kla.kla_prefill_backward(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                     ct["dO"].to(DEV), S0=d["S0"], dS_T=ct["dS_T"].to(DEV),
+                                     n_seq=d["n_seq"])
+    torch.cuda.synchronize()
+    T = inp["q"].shape[0] // inp["n_seq"]
+    f64 = lambda t: t.double().numpy()
+    for n, h in ((0, 0), (3, 15)):
+        sl = slice(n * T, (n + 1) * T)
+        pick = lambda t: f64(t[sl, h:h + 1])
+        ref = ob.prefill_backward(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]),
+                                  pick(inp["g"]), pick(inp["eta"]), inp["eps"], pick(ct["dO"]),
+                                  S0=f64(inp["S0"][n:n + 1, h:h + 1]),
+                                  dS_T=f64(ct["dS_T"][n:n + 1, h:h + 1]))
+        got = [x[sl, h:h + 1] for x in grads[:5]] + [grads[5][n:n + 1, h:h + 1]]
+        print(f"sequence {n}, head {h}", flush=True)
+        for name, x, y in zip(NAMES, got, ref):
+            e = err(x, y)
+            print(f"  {name}: err {e:.3e} (bar {TOL[torch.bfloat16]:g})", flush=True)
+            assert e < TOL[torch.bfloat16], f"{name}: err {e:.3e}"

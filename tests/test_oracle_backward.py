@@ -128,3 +128,12 @@ def test_packed_equals_per_sequence():
         for a, b in zip(packed[:5], one[:5]):
             assert np.allclose(a[s:e], b, rtol=1e-13, atol=1e-15)
         assert np.allclose(packed[5][n], one[5][0], rtol=1e-13)
+
+
+def test_dense_sequences_equal_packed():
+    q, k, v, g, eta, S0, dO, dST = draw(6, 24, H=2, dk=3, dv=2, n_seq=3)
+    dense = ob.prefill_backward(q, k, v, g, eta, 1e-6, dO, S0=S0, dS_T=dST, n_seq=3)
+    packed = ob.prefill_backward(q, k, v, g, eta, 1e-6, dO, S0=S0, dS_T=dST,
+                                 cu_seqlens=np.array([0, 8, 16, 24]))
+    for a, b in zip(dense, packed):
+        assert np.array_equal(a, b)
