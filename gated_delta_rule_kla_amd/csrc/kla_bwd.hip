@@ -42,7 +42,7 @@ namespace kla {
 namespace {
 
 constexpr int kAdjBV = 32;          // state columns per adjoint-scan workgroup
-constexpr int kAdjThreads = 256;    // four wavefronts
+constexpr int kAdjThreads = 512;    // eight wavefronts, two to a SIMD
 constexpr int kGradThreads = 512;   // eight wavefronts
 constexpr int LDB = kAdjBV + 4;     // row stride of a 32-column fp32 block in LDS
 constexpr int LDC = kChunk + 4;     // row stride of a 64 x 64 fp32 tile in LDS
@@ -52,7 +52,7 @@ constexpr int LDC = kChunk + 4;     // row stride of a 64 x 64 fp32 tile in LDS
 template <int KD, typename FA, typename FB>
 __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int lane, FA fa, FB fb) {
   const int r = lane & 15, kq = lane >> 4;
-#pragma unroll 4
+#pragma unroll
   for (int k0 = 0; k0 < KD; k0 += 4)
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa(r, k0 + kq), fb(k0 + kq, r), acc, 0, 0, 0);
   return acc;
@@ -77,16 +77,78 @@ __device__ __forceinline__ void stage_rows(float *dst, const Src *src, size_t ro
   }
 }
 
-// A 64 x 64 matrix stored as its ten lower 16 x 16 blocks (the prep kernel's packed T and P),
-// unpacked into an fp32 LDS tile with zeros above the diagonal blocks.
-template <int NT, typename Tin>
-__device__ __forceinline__ void stage_packed(float (*dst)[LDC], const Tin *src, int tid) {
-  for (int e = tid; e < kChunk * kChunk; e += NT) {
-    const int r = e >> 6, c = e & 63, I = r >> 4, J = c >> 4;
-    dst[r][c] =
-        J > I ? 0.f : to_f32(src[(I * (I + 1) / 2 + J) * 256 + (r & 15) * 16 + (c & 15)]);
-  }
+// the (I, J) block of the ten blocks on and below the diagonal, in the order (0,0) (1,0) (1,1)
+// (2,0) (2,1) (2,2) (3,0) .. (3,3)
+__device__ __forceinline__ void lower_block(int b, int &I, int &J) {
+  I = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0;
+  J = b - I * (I + 1) / 2;
 }
+
+// Four consecutive elements as loaded (raw), and as fp32.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> { typedef f32x4 type; };
+template <> struct Raw4<__bf16> { typedef bf16x4 type; };
+__device__ __forceinline__ f32x4 cvt4(const f32x4 &x) { return x; }
+__device__ __forceinline__ f32x4 cvt4(const bf16x4 &x) {
+  return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
+}
+
+// A tile of NR rows x NC columns of a row-strided tensor, held in registers between its
+// load (all of a thread's loads issued back to back) and its store into an fp32 LDS tile;
+// rows at or past `len` read as zeros.
+template <typename T, int NR, int NC, int NT>
+struct RegTile {
+  static constexpr int NQ = NR * NC / 4, J = (NQ + NT - 1) / NT;
+  typename Raw4<T>::type x[J];
+  __device__ __forceinline__ void load(const T *src, size_t row_stride, int len, int tid) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = tid + NT * j, r = e / (NC / 4), c = 4 * (e % (NC / 4));
+      typename Raw4<T>::type z = {};
+      if ((NQ % NT == 0 || e < NQ) && r < len)
+        z = *reinterpret_cast<const typename Raw4<T>::type *>(src + (size_t)r * row_stride + c);
+      x[j] = z;
+    }
+  }
+  template <int LD>
+  __device__ __forceinline__ void store(float *dst, int tid) const {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = tid + NT * j, r = e / (NC / 4), c = 4 * (e % (NC / 4));
+      if (NQ % NT == 0 || e < NQ) *reinterpret_cast<f32x4 *>(dst + r * LD + c) = cvt4(x[j]);
+    }
+  }
+};
+
+// A 64 x 64 matrix stored as its ten lower 16 x 16 blocks (the prep kernel's packed T and P),
+// in registers; stored into the lower blocks of an fp32 LDS tile (the upper blocks are left
+// as they are: zero).
+template <typename T, int NT>
+struct PackedTile {
+  static constexpr int NQ = 10 * 256 / 4, J = (NQ + NT - 1) / NT;
+  typename Raw4<T>::type x[J];
+  __device__ __forceinline__ void load(const T *src, int tid) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int pq = tid + NT * j;
+      typename Raw4<T>::type z = {};
+      if (pq < NQ) z = *reinterpret_cast<const typename Raw4<T>::type *>(src + 4 * pq);
+      x[j] = z;
+    }
+  }
+  __device__ __forceinline__ void store(float (*dst)[LDC], int tid) const {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int pq = tid + NT * j;
+      if (pq < NQ) {
+        const int e0 = 4 * pq, w = e0 & 255;
+        int I, Jb;
+        lower_block(e0 >> 8, I, Jb);
+        *reinterpret_cast<f32x4 *>(&dst[16 * I + (w >> 4)][16 * Jb + (w & 15)]) = cvt4(x[j]);
+      }
+    }
+  }
+};
 
 // x from the lane that the DPP control selects within this lane's row of 16
 template <int CTRL>
@@ -140,26 +202,46 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
   const int nchunks = (te - tb + kChunk - 1) / kChunk;
   const size_t sbase = ((size_t)n * H + h) * DK * (size_t)DV + v0;
 
-  // the last chunk's dS' is the cotangent of S_T
+  // the last chunk's dS' is the cotangent of S_T; T and P keep zeros above their lower blocks
   for (int e = tid; e < DK * kAdjBV; e += kAdjThreads) {
     const int r = e / kAdjBV, c = e % kAdjBV;
     sm.dS[r][c] = dST ? dST[sbase + (size_t)r * DV + c] : 0.f;
   }
+  for (int e = tid; e < kChunk * LDC; e += kAdjThreads) {
+    (&sm.T[0][0])[e] = 0.f;
+    (&sm.P[0][0])[e] = 0.f;
+  }
+  // a chunk's tiles are loaded into registers while the chunk before it (in this reverse
+  // order) is computed, and written to LDS when its turn comes
+  RegTile<Tin, kChunk, DK, kAdjThreads> rk, rq;
+  RegTile<Tin, kChunk, kAdjBV, kAdjThreads> rdo;
+  PackedTile<Tin, kAdjThreads> rt, rp;
+  float rgd = 0.f;
+  auto issue = [&](int c) {
+    const int t0 = tb + c * kChunk, len = min(kChunk, te - t0);
+    const size_t ch = (size_t)(cbase + c) * H + h;
+    const size_t tok = (size_t)t0 * H + h;
+    rk.load(k + tok * DK, (size_t)H * DK, len, tid);
+    rq.load(q + tok * DK, (size_t)H * DK, len, tid);
+    rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
+    rt.load(Tm + ch * (kChunk * kChunk), tid);
+    rp.load(Pm + ch * (kChunk * kChunk), tid);
+    if (tid < 2 * kChunk) rgd = GD[ch * kGDFloats + tid];  // gam then dec
+  };
+  if (nchunks > 0) issue(nchunks - 1);
   for (int c = nchunks - 1; c >= 0; --c) {
     const int t0 = tb + c * kChunk, len = min(kChunk, te - t0);
     const size_t ch = (size_t)(cbase + c) * H + h;
     const size_t tok = (size_t)t0 * H + h;
-    stage_rows<DK, DK + 4, kAdjThreads>(&sm.K[0][0], k + tok * DK, (size_t)H * DK, len, tid);
-    stage_rows<DK, DK + 4, kAdjThreads>(&sm.Q[0][0], q + tok * DK, (size_t)H * DK, len, tid);
-    stage_rows<kAdjBV, LDB, kAdjThreads>(&sm.dO[0][0], dO + tok * DV + v0, (size_t)H * DV, len,
-                                         tid);
-    stage_packed<kAdjThreads>(sm.T, Tm + ch * (kChunk * kChunk), tid);
-    stage_packed<kAdjThreads>(sm.P, Pm + ch * (kChunk * kChunk), tid);
-    if (tid < kChunk) {
-      sm.gam[tid] = GD[ch * kGDFloats + tid];
-      sm.dec[tid] = GD[ch * kGDFloats + kChunk + tid];
-    }
+    rk.template store<DK + 4>(&sm.K[0][0], tid);
+    rq.template store<DK + 4>(&sm.Q[0][0], tid);
+    rdo.template store<LDB>(&sm.dO[0][0], tid);
+    rt.store(sm.T, tid);
+    rp.store(sm.P, tid);
+    if (tid < kChunk) sm.gam[tid] = rgd;
+    else if (tid < 2 * kChunk) sm.dec[tid - kChunk] = rgd;
     __syncthreads();
+    if (c > 0) issue(c - 1);
 
     // this chunk's dS' for the gradient kernel
     {
@@ -170,10 +252,11 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
             *reinterpret_cast<const f32x4 *>(&sm.dS[r][c4]);
       }
     }
-    // dU = P^T dO + Diag(dec) K dS': 4 x 2 tiles, two per wavefront
+    // dU = P^T dO + Diag(dec) K dS': 4 x 2 tiles, 8 / NW per wavefront
+    constexpr int NW = kAdjThreads / 64, NU = 8 / NW;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int t = 2 * wid + x, ti = t >> 1, tj = t & 1;
+    for (int x = 0; x < NU; ++x) {
+      const int t = NU * wid + x, ti = t >> 1, tj = t & 1;
       const f32x4 a = mm_tile<kChunk>(
           zero4(), lane, [&](int i, int kk) { return sm.P[kk][16 * ti + i]; },
           [&](int kk, int j) { return sm.dO[kk][16 * tj + j]; });
@@ -189,8 +272,8 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     __syncthreads();
     // dR = T^T dU
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int t = 2 * wid + x, ti = t >> 1, tj = t & 1;
+    for (int x = 0; x < NU; ++x) {
+      const int t = NU * wid + x, ti = t >> 1, tj = t & 1;
       const f32x4 rr = mm_tile<kChunk>(
           zero4(), lane, [&](int i, int kk) { return sm.T[kk][16 * ti + i]; },
           [&](int kk, int j) { return sm.dU[kk][16 * tj + j]; });
@@ -216,11 +299,11 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     }
     // dS = exp(G_last) dS' + Q^T Diag(gam) dO - K^T Diag(gam) dR: (DK / 16) x 2 tiles
     const float gl = sm.gam[kChunk - 1];  // rows past a ragged end repeat G_last
-    constexpr int NX = DK / 32;           // tiles per wavefront
+    constexpr int NX = DK / 8 / NW;       // tiles per wavefront
     f32x4 nd[NX];
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-      const int t = wid + 4 * x, mi = t >> 1, tj = t & 1;
+      const int t = wid + NW * x, mi = t >> 1, tj = t & 1;
       f32x4 acc = mm_tile<kChunk>(
           zero4(), lane, [&](int i, int kk) { return sm.Q[kk][16 * mi + i]; },
           [&](int kk, int j) { return sm.gam[kk] * sm.dO[kk][16 * tj + j]; });
@@ -234,7 +317,7 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     __syncthreads();  // every read of this chunk's tiles and of dS' is done
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-      const int t = wid + 4 * x, mi = t >> 1, tj = t & 1;
+      const int t = wid + NW * x, mi = t >> 1, tj = t & 1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm.dS[16 * mi + 4 * kq + e][16 * tj + r16] = nd[x][e];
     }
@@ -272,13 +355,6 @@ struct GradSmem {
   float dots[3][2][kChunk];  // row dots of the three d_v contractions, two partial sums each
   float red[kGradThreads / 64];
 };
-
-// the (I, J) block of the ten blocks on and below the diagonal, in the order (0,0) (1,0) (1,1)
-// (2,0) (2,1) (2,2) (3,0) .. (3,3)
-__device__ __forceinline__ void lower_block(int b, int &I, int &J) {
-  I = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0;
-  J = b - I * (I + 1) / 2;
-}
 
 }  // namespace
 
@@ -391,22 +467,33 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   float sc = 0.f;
   const float *Sb = SN + ch * DK * (size_t)DV, *Sob = dSo + ch * DK * (size_t)DV;
   const float *dUb = dUo + ch * kChunk * (size_t)DV, *dRb = dRo + ch * kChunk * (size_t)DV;
+  // each 32-column block is loaded into registers while the one before it is computed
+  RegTile<float, DK, kAdjBV, kGradThreads> rs, rso;
+  RegTile<Tin, kChunk, kAdjBV, kGradThreads> rv, rdo;
+  RegTile<float, kChunk, kAdjBV, kGradThreads> rdu, rdr;
+  auto issue = [&](int v0) {
+    rs.load(Sb + v0, (size_t)DV, DK, tid);
+    rso.load(Sob + v0, (size_t)DV, DK, tid);
+    rv.load(v + tok * DV + v0, (size_t)H * DV, len, tid);
+    rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
+    rdu.load(dUb + v0, (size_t)DV, kChunk, tid);
+    rdr.load(dRb + v0, (size_t)DV, kChunk, tid);
+  };
+  issue(0);
   for (int v0 = 0; v0 < DV; v0 += kAdjBV) {
     __syncthreads();  // the previous block's reads (and X's writes) are done
-    for (int e = tid; e < DK * kAdjBV / 4; e += kGradThreads) {
-      const int r = e / (kAdjBV / 4), c4 = 4 * (e % (kAdjBV / 4));
-      const f32x4 s = ld4(Sb + (size_t)r * DV + v0 + c4), so = ld4(Sob + (size_t)r * DV + v0 + c4);
-      *reinterpret_cast<f32x4 *>(&sm.u.lp.S[r][c4]) = s;
-      *reinterpret_cast<f32x4 *>(&sm.u.lp.So[r][c4]) = so;
-      sc += s[0] * so[0] + s[1] * so[1] + s[2] * so[2] + s[3] * so[3];
-    }
-    stage_rows<kAdjBV, LDB, kGradThreads>(&sm.u.lp.R[0][0], v + tok * DV + v0, (size_t)H * DV,
-                                          len, tid);
-    stage_rows<kAdjBV, LDB, kGradThreads>(&sm.u.lp.dO[0][0], dO + tok * DV + v0, (size_t)H * DV,
-                                          len, tid);
-    stage_rows<kAdjBV, LDB, kGradThreads>(&sm.u.lp.dU[0][0], dUb + v0, (size_t)DV, kChunk, tid);
-    stage_rows<kAdjBV, LDB, kGradThreads>(&sm.u.lp.dR[0][0], dRb + v0, (size_t)DV, kChunk, tid);
+    rs.template store<LDB>(&sm.u.lp.S[0][0], tid);
+    rso.template store<LDB>(&sm.u.lp.So[0][0], tid);
+#pragma unroll
+    for (int j = 0; j < rs.J; ++j)
+      sc += rs.x[j][0] * rso.x[j][0] + rs.x[j][1] * rso.x[j][1] + rs.x[j][2] * rso.x[j][2] +
+            rs.x[j][3] * rso.x[j][3];
+    rv.template store<LDB>(&sm.u.lp.R[0][0], tid);
+    rdo.template store<LDB>(&sm.u.lp.dO[0][0], tid);
+    rdu.template store<LDB>(&sm.u.lp.dU[0][0], tid);
+    rdr.template store<LDB>(&sm.u.lp.dR[0][0], tid);
     __syncthreads();
+    if (v0 + kAdjBV < DV) issue(v0 + kAdjBV);
     const int yi = wid >> 1, yj = wid & 1;  // this wavefront's 16 x 16 tile of R and U
     {
       const f32x4 y = mm_tile<DK>(
