@@ -83,6 +83,8 @@ def measured_traffic():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--backward-steps", type=int, default=10,
+                    help="timed steps of the backward pass (0 = skip)")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=512)
@@ -220,6 +222,38 @@ def main():
                             "unit-norm keys; one kla_prefill_chunked call per step; "
                             "diagonal_gate: g per key channel [n_tok, H, d_k]")
         log(f"variants: {variants}")
+
+    # backward pass on the same workload: gradients for seeded cotangents dO, dS_T
+    backward = None
+    if args.backward_steps > 0:
+        s0 = sets[0]
+        ct = ki.cotangents({"q": s0["q"], "k": s0["k"], "v": s0["v"], "n_seq": n_seq},
+                           seed=ki.BASE_SEED + 99, device=dev)
+        wsb = torch.empty(kla.kla_prefill_backward_workspace_bytes(n_seq, n_tok, H, dk, dv,
+                                                                   s0["q"].dtype),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return kla.kla_prefill_backward(s0["q"], s0["k"], s0["v"], s0["g"], s0["eta"],
+                                            base["eps"], ct["dO"], S0=s0["S0"],
+                                            dS_T=ct["dS_T"], n_seq=n_seq, workspace=wsb)
+        for _ in range(2):
+            bstep()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.backward_steps):
+            bstep()
+        e1.record()
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / args.backward_steps
+        backward = {"ms_per_step": bwd_ms, "tokens_per_s": n_tok / (bwd_ms * 1e-3),
+                    "steps": args.backward_steps, "workspace_bytes": wsb.numel(),
+                    "note": "kla_prefill_backward (dq, dk, dv, dg, deta, dS0) on the prefill "
+                            "workload, one input set; each step runs the prep, the chunk scan "
+                            "storing every chunk's state, the adjoint scan and the per-chunk "
+                            "gradients"}
+        log(f"backward: {bwd_ms:.3f} ms/step")
+        del wsb, ct
     del sets
 
     # ---------------------------------------------------------------- decode
@@ -327,6 +361,7 @@ def main():
                                      "achieved_GBs": dec_diag_gbs,
                                      "frac": dec_diag_gbs / PEAK_HBM_GBS}},
         "variants": variants,
+        "backward": backward,
         "cpu_baseline": cpu,
         "context": "the pages report 3.54 vs 1.65 tok/s decode at 32K context (2.1x KLA/GDN) for "
                    "a whole 0.4B model at batch 1 on NVIDIA A100 80GB (FLA library); not this "
