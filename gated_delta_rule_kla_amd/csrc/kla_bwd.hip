@@ -32,8 +32,9 @@
 //                        dV and dS0.
 //   kla_bwd_grad_kernel  one workgroup per (chunk, head): the contractions over d_v with the
 //                        stored S and dS', then the chunk-local algebra, dq, dk, dg, deta.
-// Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) from fp32 LDS tiles, whatever the
-// operand type of q, k, v.
+// Tiles sit in LDS in fp32.  Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) for fp32
+// inputs, and on bf16 MFMA (v_mfma_f32_16x16x32_bf16, operands rounded to bf16 as they are
+// read, fp32 accumulation) for bf16 inputs.
 #include "kla_device.h"
 #include "kla_launch.h"
 
@@ -56,6 +57,30 @@ __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int lane, FA fa, FB fb) {
   for (int k0 = 0; k0 < KD; k0 += 4)
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa(r, k0 + kq), fb(k0 + kq, r), acc, 0, 0, 0);
   return acc;
+}
+
+// The same tile product in the operand precision of the inputs: fp32 inputs keep the fp32
+// MFMA; bf16 inputs round both operands to bf16 and contract 32 at a time on
+// v_mfma_f32_16x16x32_bf16 (lane (r, kq) supplies A(r, k0 + 8 kq + s) and B(k0 + 8 kq + s, r),
+// s = 0..7), accumulating in fp32.  KD is a multiple of 32.
+template <typename Tin, int KD, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mmt(f32x4 acc, int lane, FA fa, FB fb) {
+  if constexpr (sizeof(Tin) == 2) {
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int k0 = 0; k0 < KD; k0 += 32) {
+      bf16x8 a, b;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        a[s] = from_f32<__bf16>(fa(r, k0 + 8 * kq + s));
+        b[s] = from_f32<__bf16>(fb(k0 + 8 * kq + s, r));
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+  } else {
+    return mm_tile<KD>(acc, lane, fa, fb);
+  }
 }
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
@@ -257,10 +282,10 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
 #pragma unroll
     for (int x = 0; x < NU; ++x) {
       const int t = NU * wid + x, ti = t >> 1, tj = t & 1;
-      const f32x4 a = mm_tile<kChunk>(
+      const f32x4 a = mmt<Tin, kChunk>(
           zero4(), lane, [&](int i, int kk) { return sm.P[kk][16 * ti + i]; },
           [&](int kk, int j) { return sm.dO[kk][16 * tj + j]; });
-      const f32x4 y = mm_tile<DK>(
+      const f32x4 y = mmt<Tin, DK>(
           zero4(), lane, [&](int i, int kk) { return sm.K[16 * ti + i][kk]; },
           [&](int kk, int j) { return sm.dS[kk][16 * tj + j]; });
 #pragma unroll
@@ -274,7 +299,7 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
 #pragma unroll
     for (int x = 0; x < NU; ++x) {
       const int t = NU * wid + x, ti = t >> 1, tj = t & 1;
-      const f32x4 rr = mm_tile<kChunk>(
+      const f32x4 rr = mmt<Tin, kChunk>(
           zero4(), lane, [&](int i, int kk) { return sm.T[kk][16 * ti + i]; },
           [&](int kk, int j) { return sm.dU[kk][16 * tj + j]; });
 #pragma unroll
@@ -304,10 +329,10 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
       const int t = wid + NW * x, mi = t >> 1, tj = t & 1;
-      f32x4 acc = mm_tile<kChunk>(
+      f32x4 acc = mmt<Tin, kChunk>(
           zero4(), lane, [&](int i, int kk) { return sm.Q[kk][16 * mi + i]; },
           [&](int kk, int j) { return sm.gam[kk] * sm.dO[kk][16 * tj + j]; });
-      acc = mm_tile<kChunk>(
+      acc = mmt<Tin, kChunk>(
           acc, lane, [&](int i, int kk) { return -sm.K[kk][16 * mi + i]; },
           [&](int kk, int j) { return sm.gam[kk] * sm.dR[kk][16 * tj + j]; });
 #pragma unroll
@@ -419,7 +444,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const int t = wid + 8 * x, I = t >> 2, J = t & 3;
     f32x4 acc = zero4();
     if (J <= I)
-      acc = mm_tile<DK>(
+      acc = mmt<Tin, DK>(
           acc, lane, [&](int i, int kk) { return sm.K[16 * I + i][kk]; },
           [&](int kk, int j) { return sm.K[16 * J + j][kk]; });
 #pragma unroll
@@ -496,7 +521,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     if (v0 + kAdjBV < DV) issue(v0 + kAdjBV);
     const int yi = wid >> 1, yj = wid & 1;  // this wavefront's 16 x 16 tile of R and U
     {
-      const f32x4 y = mm_tile<DK>(
+      const f32x4 y = mmt<Tin, DK>(
           zero4(), lane, [&](int i, int kk) { return sm.K[16 * yi + i][kk]; },
           [&](int kk, int j) { return sm.u.lp.S[kk][16 * yj + j]; });
 #pragma unroll
@@ -507,7 +532,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     }
     __syncthreads();
     {
-      const f32x4 uu = mm_tile<kChunk>(
+      const f32x4 uu = mmt<Tin, kChunk>(
           zero4(), lane, [&](int i, int kk) { return sm.X[16 * yi + i][kk]; },
           [&](int kk, int j) { return sm.b[kk] * sm.u.lp.R[kk][16 * yj + j]; });
 #pragma unroll
@@ -517,13 +542,13 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int tj = (wid >> 2) + 2 * m;  // column tile of 16 key dims
-      qa[m] = mm_tile<kAdjBV>(
+      qa[m] = mmt<Tin, kAdjBV>(
           qa[m], lane, [&](int i, int kk) { return sm.gam[16 * mti + i] * sm.u.lp.dO[16 * mti + i][kk]; },
           [&](int kk, int j) { return sm.u.lp.S[16 * tj + j][kk]; });
-      ka[m] = mm_tile<kAdjBV>(
+      ka[m] = mmt<Tin, kAdjBV>(
           ka[m], lane, [&](int i, int kk) { return -sm.gam[16 * mti + i] * sm.u.lp.dR[16 * mti + i][kk]; },
           [&](int kk, int j) { return sm.u.lp.S[16 * tj + j][kk]; });
-      kb[m] = mm_tile<kAdjBV>(
+      kb[m] = mmt<Tin, kAdjBV>(
           kb[m], lane, [&](int i, int kk) { return sm.dec[16 * mti + i] * sm.u.lp.U[16 * mti + i][kk]; },
           [&](int kk, int j) { return sm.u.lp.So[16 * tj + j][kk]; });
     }
@@ -534,11 +559,11 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
         int I, J;
         lower_block(jb % 10, I, J);
         if (jb < 10)
-          pt[x] = mm_tile<kAdjBV>(
+          pt[x] = mmt<Tin, kAdjBV>(
               pt[x], lane, [&](int i, int kk) { return sm.u.lp.dO[16 * I + i][kk]; },
               [&](int kk, int j) { return sm.u.lp.U[16 * J + j][kk]; });
         else
-          pt[x] = mm_tile<kAdjBV>(
+          pt[x] = mmt<Tin, kAdjBV>(
               pt[x], lane, [&](int i, int kk) { return sm.u.lp.dU[16 * I + i][kk]; },
               [&](int kk, int j) { return sm.u.lp.R[16 * J + j][kk]; });
       }
@@ -576,7 +601,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       const int t = wid + 8 * x, I = t >> 2, J = t & 3;
       f32x4 acc = zero4();
       if (J <= I)
-        acc = mm_tile<DK>(
+        acc = mmt<Tin, DK>(
             acc, lane, [&](int i, int kk) { return sm.u.pa.Q[16 * I + i][kk]; },
             [&](int kk, int j) { return sm.K[16 * J + j][kk]; });
 #pragma unroll
@@ -634,7 +659,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int t = wid + 8 * x, I = t >> 2, J = t & 3;
-    w[x] = mm_tile<kChunk>(
+    w[x] = mmt<Tin, kChunk>(
         zero4(), lane, [&](int i, int kk) { return sm.u.pa.dT[16 * I + i][kk] * sm.b[kk]; },
         [&](int kk, int j) { return sm.X[16 * J + j][kk]; });
   }
@@ -652,7 +677,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const int t = wid + 8 * x, I = t >> 2, J = t & 3;
     f32x4 acc = zero4();
     if (J <= I)
-      acc = mm_tile<kChunk>(
+      acc = mmt<Tin, kChunk>(
           acc, lane, [&](int i, int kk) { return sm.X[kk][16 * I + i]; },
           [&](int kk, int j) { return sm.u.pa.P[kk][16 * J + j]; });
     w[x] = acc;
@@ -694,14 +719,14 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const int tj = (wid >> 2) + 2 * m;
-    f32x4 aq = mm_tile<kChunk>(
+    f32x4 aq = mmt<Tin, kChunk>(
         qa[m], lane, [&](int i, int kk) { return sm.u.pa.dP[16 * mti + i][kk]; },
         [&](int kk, int j) { return sm.K[kk][16 * tj + j]; });
     f32x4 ak = ka[m] + kb[m];
-    ak = mm_tile<kChunk>(
+    ak = mmt<Tin, kChunk>(
         ak, lane, [&](int i, int kk) { return sm.u.pa.dP[kk][16 * mti + i]; },
         [&](int kk, int j) { return sm.u.pa.Q[kk][16 * tj + j]; });
-    ak = mm_tile<kChunk>(
+    ak = mmt<Tin, kChunk>(
         ak, lane,
         [&](int i, int kk) { return sm.u.pa.dT[16 * mti + i][kk] + sm.u.pa.dT[kk][16 * mti + i]; },
         [&](int kk, int j) { return sm.K[kk][16 * tj + j]; });
