@@ -216,7 +216,15 @@ def main():
             dstep()
         e1.record()
         torch.cuda.synchronize()
-        variants["diagonal_gate_ms_per_step"] = e0.elapsed_time(e1) / args.variant_steps
+        variants["diagonal_gate_ms_per_step"] = dg_ms = e0.elapsed_time(e1) / args.variant_steps
+        # algorithmic HBM bytes of the diagonal-gated prefill: q, k, v read, o written, g read
+        # per key channel, eta read; S0 read and S_T written
+        es = s0["q"].element_size()
+        dg_bytes = n_tok * H * (es * (2 * dk + 2 * dv) + 4 * dk + 4) + 2 * n_seq * H * dk * dv * 4
+        dg_gbs = dg_bytes / (dg_ms * 1e-3) / 1e9
+        variants["diagonal_gate_roofline"] = {
+            "bound": "hbm", "achieved": dg_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": dg_gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_step": dg_bytes}
         del wsd, gd
         variants["note"] = ("same workload, one input set (cache-warm, unlike the headline), "
                             "unit-norm keys; one kla_prefill_chunked call per step; "
@@ -246,7 +254,16 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         bwd_ms = e0.elapsed_time(e1) / args.backward_steps
+        # algorithmic HBM bytes: q, k, v, dO, g, eta read and dq, dk, dv, dg, deta written once
+        # per token-head, S0 and dS_T read and dS0 written once per (sequence, head)
+        es = s0["q"].element_size()
+        bwd_bytes = (n_tok * H * (es * (4 * dk + 3 * dv) + 16)
+                     + 3 * n_seq * H * dk * dv * 4)
+        bwd_gbs = bwd_bytes / (bwd_ms * 1e-3) / 1e9
         backward = {"ms_per_step": bwd_ms, "tokens_per_s": n_tok / (bwd_ms * 1e-3),
+                    "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": PEAK_HBM_GBS,
+                                 "unit": "GB/s", "frac": bwd_gbs / PEAK_HBM_GBS,
+                                 "algorithmic_bytes_per_step": bwd_bytes},
                     "steps": args.backward_steps, "workspace_bytes": wsb.numel(),
                     "note": "kla_prefill_backward (dq, dk, dv, dg, deta, dS0) on the prefill "
                             "workload, one input set; each step runs the prep, the chunk scan "
