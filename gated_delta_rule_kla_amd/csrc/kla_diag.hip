@@ -161,58 +161,142 @@ __global__ __launch_bounds__(kDiagThreads) void kla_prep_diag_kernel(
   for (int ch = tid; ch < DK; ch += kDiagThreads)
     GC_out[(size_t)task * DK + ch] = __expf(sm.G[kChunk - 1][ch]);
 
-  // ---- A (strictly lower) and P (lower): four consecutive lanes share rows 4 bi .. + 3 and
-  //      columns 4 bj .. + 3, each summing a quarter of the channels, four at a time
+  // ---- A (strictly lower) and P (lower) in 4 x 4 tiles of (row, column) pairs.  With
+  //      l_i = G_i - G_{4 floor(i/4)} (the log-decay since the first row of row i's tile),
+  //      a pair in tiles bi > bj factors through the tiles' anchor rows,
+  //        exp(G_i - G_j) = exp(l_i) exp(G_{4 bi} - G_{4 bj + 3}) exp(l_{4 bj + 3} - l_j),
+  //      three factors that are each at most 1, so the off-diagonal tiles need one exponential
+  //      per channel instead of sixteen: with K o exp(l), Q o exp(l) and K o exp(l_last - l)
+  //      staged, they are plain sums of products.  The diagonal tiles take exp(l_i - l_j)
+  //      directly.
+  constexpr int EPL = kChunk * DK / kDiagThreads;  // elements per lane in the elementwise steps
+  float *GA = &sm.X[0][0], *GB = GA + 16 * DK;     // G of each tile's first and last row (X is
+                                                   // free until the substitution)
+  for (int e = tid; e < 16 * DK; e += kDiagThreads) {
+    const int t = e / DK, ch = e % DK;
+    GA[e] = sm.G[4 * t][ch];
+    GB[e] = sm.G[4 * t + 3][ch];
+  }
   {
-    const int tile = tid >> 2, cg = tid & 3;
-    const int bi = tile >> 4, bj = tile & 15;
-    constexpr int CPG = DK / 4;  // channels per lane
-    float a[4][4] = {}, p[4][4] = {};
-    if (bj <= bi) {
-#pragma unroll 1
-      for (int c4 = cg * CPG; c4 < (cg + 1) * CPG; c4 += 4) {
-        f32x4 gi[4], ki[4], qi[4], gj[4], kj[4];
+    const int e0 = tid * EPL, i = e0 / DK, ch = e0 % DK;
+    float l[EPL];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          gi[r] = *reinterpret_cast<const f32x4 *>(&sm.G[4 * bi + r][c4]);
-          ki[r] = *reinterpret_cast<const f32x4 *>(&sm.K[4 * bi + r][c4]);
-          qi[r] = *reinterpret_cast<const f32x4 *>(&sm.Q[4 * bi + r][c4]);
-          gj[r] = *reinterpret_cast<const f32x4 *>(&sm.G[4 * bj + r][c4]);
-          kj[r] = *reinterpret_cast<const f32x4 *>(&sm.K[4 * bj + r][c4]);
-        }
+    for (int e = 0; e < EPL; ++e) l[e] = sm.G[i][ch + e] - sm.G[i & ~3][ch + e];
+    __syncthreads();  // every read of G (the decayed tiles, the anchors) is done
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+    for (int e = 0; e < EPL; ++e) sm.G[i][ch + e] = l[e];
+  }
+  __syncthreads();
+  // diagonal tiles: wavefront w takes tile w, each lane DK / 64 channels, then wavefront sums
+  {
+    const int wid = tid >> 6, lane = tid & 63;
+    constexpr int CPL = DK / kWave;
+    const int t = wid;
+    float ad[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, pd[10] = {};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int i = 4 * bi + r, j = 4 * bj + s;
-            if (j <= i) {
+    for (int cc = 0; cc < CPL; ++cc) {
+      const int ch = lane * CPL + cc;
+      float lg[4], kv[4], qv[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float x = __expf(gi[r][e] - gj[s][e]) * kj[s][e];
-                p[r][s] += qi[r][e] * x;
-                if (j < i) a[r][s] += ki[r][e] * x;
-              }
-            }
-          }
+      for (int r = 0; r < 4; ++r) {
+        lg[r] = sm.G[4 * t + r][ch];
+        kv[r] = sm.K[4 * t + r][ch];
+        qv[r] = sm.Q[4 * t + r][ch];
       }
-    }
-    // sum the four channel quarters (lanes 4 tile .. 4 tile + 3)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        a[r][s] += __shfl_xor(a[r][s], 1, 4);
-        a[r][s] += __shfl_xor(a[r][s], 2, 4);
-        p[r][s] += __shfl_xor(p[r][s], 1, 4);
-        p[r][s] += __shfl_xor(p[r][s], 2, 4);
-      }
-    if (cg == 0) {
+      int ia = 0, ip = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          sm.A[4 * bi + r][4 * bj + s] = a[r][s];
-          sm.P[4 * bi + r][4 * bj + s] = p[r][s] * sm.rq[4 * bi + r];
+        for (int c2 = 0; c2 <= r; ++c2) {
+          const float x = __expf(lg[r] - lg[c2]) * kv[c2];
+          pd[ip++] += qv[r] * x;
+          if (c2 < r) ad[ia++] += kv[r] * x;
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < 10; ++x) pd[x] = wave_sum(pd[x]);
+#pragma unroll
+    for (int x = 0; x < 6; ++x) ad[x] = wave_sum(ad[x]);
+    if (lane < 16) {
+      const int r = lane >> 2, c2 = lane & 3;
+      const int ip = r * (r + 1) / 2 + c2, ia = r * (r - 1) / 2 + c2;
+      float pv = 0.f, av = 0.f;
+#pragma unroll
+      for (int x = 0; x < 10; ++x) pv = x == ip && c2 <= r ? pd[x] : pv;
+#pragma unroll
+      for (int x = 0; x < 6; ++x) av = x == ia && c2 < r ? ad[x] : av;
+      sm.P[4 * t + r][4 * t + c2] = pv * sm.rq[4 * t + r];
+      sm.A[4 * t + r][4 * t + c2] = av;
+    }
+  }
+  // K -> K o exp(l), Q -> Q o exp(l), l -> K o exp(l_last - l) (l_last: the tile's last row)
+  {
+    const int e0 = tid * EPL, i = e0 / DK, ch = e0 % DK;
+    float kl[EPL], ql[EPL], kr[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float lv = sm.G[i][ch + e], k0 = sm.K[i][ch + e];
+      const float el = __expf(lv);
+      kl[e] = k0 * el;
+      ql[e] = sm.Q[i][ch + e] * el;
+      kr[e] = k0 * __expf(sm.G[i | 3][ch + e] - lv);
+    }
+    __syncthreads();  // the diagonal tiles' reads are done
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      sm.K[i][ch + e] = kl[e];
+      sm.Q[i][ch + e] = ql[e];
+      sm.G[i][ch + e] = kr[e];
+    }
+  }
+  __syncthreads();
+  // off-diagonal tiles (bj < bi): 120 tiles x 8 channel groups on lanes 0..959
+  if (tid < 120 * 8) {
+    const int t = tid >> 3, g8 = tid & 7;
+    const int bi = (int)((1.f + sqrtf(1.f + 8.f * (float)t)) * 0.5f);  // t = bi (bi - 1) / 2 + bj
+    const int bj = t - bi * (bi - 1) / 2;
+    constexpr int CPG = DK / 8;
+    float a[4][4] = {}, p[4][4] = {};
+#pragma unroll 1
+    for (int c4 = g8 * CPG; c4 < (g8 + 1) * CPG; c4 += 4) {
+      const f32x4 ga = *reinterpret_cast<const f32x4 *>(GA + bi * DK + c4);
+      const f32x4 gb = *reinterpret_cast<const f32x4 *>(GB + bj * DK + c4);
+      f32x4 d;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[e] = __expf(ga[e] - gb[e]);
+      f32x4 kl[4], ql[4], kr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kl[r] = *reinterpret_cast<const f32x4 *>(&sm.K[4 * bi + r][c4]);
+        ql[r] = *reinterpret_cast<const f32x4 *>(&sm.Q[4 * bi + r][c4]);
+        kr[r] = *reinterpret_cast<const f32x4 *>(&sm.G[4 * bj + r][c4]) * d;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c2 = 0; c2 < 4; ++c2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[r][c2] += kl[r][e] * kr[c2][e];
+            p[r][c2] += ql[r][e] * kr[c2][e];
+          }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2)
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {
+          a[r][c2] += __shfl_xor(a[r][c2], off, 8);
+          p[r][c2] += __shfl_xor(p[r][c2], off, 8);
+        }
+    if (g8 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c2 = 0; c2 < 4; ++c2) {
+          sm.A[4 * bi + r][4 * bj + c2] = a[r][c2];
+          sm.P[4 * bi + r][4 * bj + c2] = p[r][c2] * sm.rq[4 * bi + r];
         }
     }
   }
