@@ -135,12 +135,22 @@ struct RegTile {
       x[j] = z;
     }
   }
-  template <int LD>
-  __device__ __forceinline__ void store(float *dst, int tid) const {
+  template <int LD, typename D>
+  __device__ __forceinline__ void store(D *dst, int tid) const {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int e = tid + NT * j, r = e / (NC / 4), c = 4 * (e % (NC / 4));
-      if (NQ % NT == 0 || e < NQ) *reinterpret_cast<f32x4 *>(dst + r * LD + c) = cvt4(x[j]);
+      if (NQ % NT == 0 || e < NQ) {
+        const f32x4 v = cvt4(x[j]);
+        if constexpr (sizeof(D) == 2) {
+          bf16x4 b;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) b[i] = from_f32<__bf16>(v[i]);
+          *reinterpret_cast<bf16x4 *>(dst + r * LD + c) = b;
+        } else {
+          *reinterpret_cast<f32x4 *>(dst + r * LD + c) = v;
+        }
+      }
     }
   }
 };
@@ -358,15 +368,18 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
 
 namespace {
 
-template <int DK>
+// LT: the element type of the d_v-loop tiles: the operand type of the inputs.  Every read of
+// them feeds a product in that precision, so bf16 storage loses nothing and halves the LDS
+// traffic of those products.
+template <typename LT, int DK>
 struct GradSmem {
   float K[kChunk][DK + 4];
   float X[kChunk][LDC];
   float A[kChunk][LDC];
   union {
     struct {  // the loop over 32-column blocks of d_v
-      float S[DK][LDB], So[DK][LDB];
-      float R[kChunk][LDB], U[kChunk][LDB], dO[kChunk][LDB], dU[kChunk][LDB], dR[kChunk][LDB];
+      LT S[DK][LDB], So[DK][LDB];
+      LT R[kChunk][LDB], U[kChunk][LDB], dO[kChunk][LDB], dU[kChunk][LDB], dR[kChunk][LDB];
     } lp;
     struct {  // the chunk-local algebra after it
       float Q[kChunk][DK + 4];
@@ -393,7 +406,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq, int H,
     int DV) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  GradSmem<DK> &sm = *reinterpret_cast<GradSmem<DK> *>(smem_raw);
+  GradSmem<Tin, DK> &sm = *reinterpret_cast<GradSmem<Tin, DK> *>(smem_raw);
   const int n_chunks = chunk_off[n_seq];
   const int task = blockIdx.x;  // chunk * H + head
   if (task >= n_chunks * H) return;
@@ -523,34 +536,35 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     {
       const f32x4 y = mmt<Tin, DK>(
           zero4(), lane, [&](int i, int kk) { return sm.K[16 * yi + i][kk]; },
-          [&](int kk, int j) { return sm.u.lp.S[kk][16 * yj + j]; });
+          [&](int kk, int j) { return to_f32(sm.u.lp.S[kk][16 * yj + j]); });
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * yi + 4 * kq + e;
-        sm.u.lp.R[row][16 * yj + r16] -= sm.gam[row] * y[e];
+        Tin &rv_ = sm.u.lp.R[row][16 * yj + r16];
+        rv_ = from_f32<Tin>(to_f32(rv_) - sm.gam[row] * y[e]);
       }
     }
     __syncthreads();
     {
       const f32x4 uu = mmt<Tin, kChunk>(
           zero4(), lane, [&](int i, int kk) { return sm.X[16 * yi + i][kk]; },
-          [&](int kk, int j) { return sm.b[kk] * sm.u.lp.R[kk][16 * yj + j]; });
+          [&](int kk, int j) { return sm.b[kk] * to_f32(sm.u.lp.R[kk][16 * yj + j]); });
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.u.lp.U[16 * yi + 4 * kq + e][16 * yj + r16] = uu[e];
+      for (int e = 0; e < 4; ++e) sm.u.lp.U[16 * yi + 4 * kq + e][16 * yj + r16] = from_f32<Tin>(uu[e]);
     }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int tj = (wid >> 2) + 2 * m;  // column tile of 16 key dims
       qa[m] = mmt<Tin, kAdjBV>(
-          qa[m], lane, [&](int i, int kk) { return sm.gam[16 * mti + i] * sm.u.lp.dO[16 * mti + i][kk]; },
-          [&](int kk, int j) { return sm.u.lp.S[16 * tj + j][kk]; });
+          qa[m], lane, [&](int i, int kk) { return sm.gam[16 * mti + i] * to_f32(sm.u.lp.dO[16 * mti + i][kk]); },
+          [&](int kk, int j) { return to_f32(sm.u.lp.S[16 * tj + j][kk]); });
       ka[m] = mmt<Tin, kAdjBV>(
-          ka[m], lane, [&](int i, int kk) { return -sm.gam[16 * mti + i] * sm.u.lp.dR[16 * mti + i][kk]; },
-          [&](int kk, int j) { return sm.u.lp.S[16 * tj + j][kk]; });
+          ka[m], lane, [&](int i, int kk) { return -sm.gam[16 * mti + i] * to_f32(sm.u.lp.dR[16 * mti + i][kk]); },
+          [&](int kk, int j) { return to_f32(sm.u.lp.S[16 * tj + j][kk]); });
       kb[m] = mmt<Tin, kAdjBV>(
-          kb[m], lane, [&](int i, int kk) { return sm.dec[16 * mti + i] * sm.u.lp.U[16 * mti + i][kk]; },
-          [&](int kk, int j) { return sm.u.lp.So[16 * tj + j][kk]; });
+          kb[m], lane, [&](int i, int kk) { return sm.dec[16 * mti + i] * to_f32(sm.u.lp.U[16 * mti + i][kk]); },
+          [&](int kk, int j) { return to_f32(sm.u.lp.So[16 * tj + j][kk]); });
     }
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
@@ -560,12 +574,12 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
         lower_block(jb % 10, I, J);
         if (jb < 10)
           pt[x] = mmt<Tin, kAdjBV>(
-              pt[x], lane, [&](int i, int kk) { return sm.u.lp.dO[16 * I + i][kk]; },
-              [&](int kk, int j) { return sm.u.lp.U[16 * J + j][kk]; });
+              pt[x], lane, [&](int i, int kk) { return to_f32(sm.u.lp.dO[16 * I + i][kk]); },
+              [&](int kk, int j) { return to_f32(sm.u.lp.U[16 * J + j][kk]); });
         else
           pt[x] = mmt<Tin, kAdjBV>(
-              pt[x], lane, [&](int i, int kk) { return sm.u.lp.dU[16 * I + i][kk]; },
-              [&](int kk, int j) { return sm.u.lp.R[16 * J + j][kk]; });
+              pt[x], lane, [&](int i, int kk) { return to_f32(sm.u.lp.dU[16 * I + i][kk]); },
+              [&](int kk, int j) { return to_f32(sm.u.lp.R[16 * J + j][kk]); });
       }
     }
   }
@@ -638,22 +652,29 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     }
   }
   __syncthreads();
-  // ---- db from T: column sums of dT o X; the dP o P part of Z's row and column sums;
-  //      W = dT Diag(b) X^T into registers
-  if (tid < kChunk) {
-    float s = 0.f;
-    for (int i = 0; i < kChunk; ++i) s += sm.u.pa.dT[i][tid] * sm.X[i][tid];
-    sm.db[tid] = s;
-  } else if (tid < 2 * kChunk) {
-    const int i = tid - kChunk;
-    float s = 0.f;
-    for (int j = 0; j < kChunk; ++j) s += sm.u.pa.dP[i][j] * sm.u.pa.P[i][j];
-    sm.rz[i] = s;
-  } else if (tid < 3 * kChunk) {
-    const int j = tid - 2 * kChunk;
-    float s = 0.f;
-    for (int i = 0; i < kChunk; ++i) s += sm.u.pa.dP[i][j] * sm.u.pa.P[i][j];
-    sm.cz[j] = s;
+  // ---- db from T: column sums of dT o X; the dP o P part of Z's row and column sums
+  //      (8 lanes a row or column, 8 entries each); W = dT Diag(b) X^T into registers
+  const int rc = tid >> 3, part = tid & 7;  // row / column rc, entries part + 8 m
+  {
+    float s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int x = part + 8 * m;
+      s1 += sm.u.pa.dT[x][rc] * sm.X[x][rc];
+      s2 += sm.u.pa.dP[rc][x] * sm.u.pa.P[rc][x];
+      s3 += sm.u.pa.dP[x][rc] * sm.u.pa.P[x][rc];
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      s1 += __shfl_xor(s1, off, 8);
+      s2 += __shfl_xor(s2, off, 8);
+      s3 += __shfl_xor(s3, off, 8);
+    }
+    if (part == 0) {
+      sm.db[rc] = s1;
+      sm.rz[rc] = s2;
+      sm.cz[rc] = s3;
+    }
   }
   f32x4 w[2];
 #pragma unroll
@@ -694,16 +715,24 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   }
   __syncthreads();
   // ---- db += row sums of dL o A; the dA o A part of Z (dA = Diag(b) dL)
-  if (tid < kChunk) {
-    float s = 0.f;
-    for (int j = 0; j < kChunk; ++j) s += sm.u.pa.dT[tid][j] * sm.A[tid][j];
-    sm.db[tid] += s;
-    sm.rz[tid] += sm.b[tid] * s;
-  } else if (tid < 2 * kChunk) {
-    const int j = tid - kChunk;
-    float s = 0.f;
-    for (int i = 0; i < kChunk; ++i) s += sm.b[i] * sm.u.pa.dT[i][j] * sm.A[i][j];
-    sm.cz[j] += s;
+  {
+    float s4 = 0.f, s5 = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int x = part + 8 * m;
+      s4 += sm.u.pa.dT[rc][x] * sm.A[rc][x];
+      s5 += sm.b[x] * sm.u.pa.dT[x][rc] * sm.A[x][rc];
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      s4 += __shfl_xor(s4, off, 8);
+      s5 += __shfl_xor(s5, off, 8);
+    }
+    if (part == 0) {
+      sm.db[rc] += s4;
+      sm.rz[rc] += sm.b[rc] * s4;
+      sm.cz[rc] += s5;
+    }
   }
   __syncthreads();
   // ---- dP o Gamma and dA o Gamma in place
@@ -774,8 +803,8 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
                                void *dk, void *dv, float *dg, float *deta, float *dS0,
                                SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                                hipStream_t stream) {
-  const size_t smA = sizeof(AdjSmem<DK>), smG = sizeof(GradSmem<DK>);
-  static_assert(sizeof(AdjSmem<DK>) <= 160 * 1024 && sizeof(GradSmem<DK>) <= 160 * 1024,
+  const size_t smA = sizeof(AdjSmem<DK>), smG = sizeof(GradSmem<Tin, DK>);
+  static_assert(sizeof(AdjSmem<DK>) <= 160 * 1024 && sizeof(GradSmem<Tin, DK>) <= 160 * 1024,
                 "LDS budget");
   static bool attr_set = false;  // benign race: every thread sets the same values
   if (!attr_set) {
