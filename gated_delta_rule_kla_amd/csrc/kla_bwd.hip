@@ -227,8 +227,12 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AdjSmem<DK> &sm = *reinterpret_cast<AdjSmem<DK> *>(smem_raw);
+  // the d_v slices of one (sequence, head) read the same K, Q, T and P: give them
+  // consecutive logical ids on one XCD (workgroup b runs on XCD b % 8) to share its L2
   const int nsl = DV / kAdjBV;
-  const int slice = blockIdx.x % nsl, sh = blockIdx.x / nsl;
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int pidx = (nblk % 8 == 0) ? (b % 8) * (nblk / 8) + b / 8 : b;
+  const int slice = pidx % nsl, sh = pidx / nsl;
   const int h = sh % H, n = sh / H;
   const int v0 = slice * kAdjBV;
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
