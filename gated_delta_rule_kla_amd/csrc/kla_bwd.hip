@@ -36,6 +36,7 @@
 // inputs, and on bf16 MFMA (v_mfma_f32_16x16x32_bf16, operands rounded to bf16 as they are
 // read, fp32 accumulation) for bf16 inputs.
 #include "kla_device.h"
+#include "kla_inverse.h"
 #include "kla_launch.h"
 
 namespace kla {
@@ -184,13 +185,6 @@ struct PackedTile {
     }
   }
 };
-
-// x from the lane that the DPP control selects within this lane's row of 16
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               CTRL, 0xF, 0xF, false));
-}
 
 // sum over the 16 lanes of a DPP row (lanes with the same l / 16)
 __device__ __forceinline__ float row16_sum(float x) {
@@ -471,29 +465,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     }
   }
   __syncthreads();
-  // ---- X = (I + Diag(b) A)^{-1} by forward substitution: wavefront w takes columns
-  //      8 w .. 8 w + 7, 8 lanes a column; lane `part` keeps X[l][j] for l = part + 8 m in
-  //      registers and sums those terms of each row's dot product, and three DPP steps sum
-  //      the 8 partial sums
-  {
-    const int j = 8 * wid + (lane >> 3), part = lane & 7;
-    float xr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      float acc = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int l = part + 8 * m;
-        if (8 * m < i) acc += (l < i ? sm.A[i][l] : 0.f) * xr[m];
-      }
-      acc += dpp_f32<0xB1>(acc);   // quad_perm [1,0,3,2]
-      acc += dpp_f32<0x4E>(acc);   // quad_perm [2,3,0,1]
-      acc += dpp_f32<0x141>(acc);  // row_half_mirror
-      const float xv = i == j ? 1.f : (i > j ? -sm.b[i] * acc : 0.f);
-      if (part == (i & 7)) xr[i >> 3] = xv;
-      if (part == 0) sm.X[i][j] = xv;
-    }
-  }
+  // ---- X = (I + Diag(b) A)^{-1} by 16 x 16 blocks (the loop's LDS is free scratch now)
+  blocked_inverse<kGradThreads, LDC, LDC>(&sm.A[0][0], sm.b, &sm.X[0][0], &sm.u.pa.P[0][0],
+                                          tid);
 
   // ---- the contractions over d_v, 32 columns at a time:
   //      Y = K S -> R = V - Diag(gam) Y, U = T R; then accumulated in registers

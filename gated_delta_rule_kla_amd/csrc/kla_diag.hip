@@ -18,6 +18,7 @@
 // factor is an exponential of a difference G_i - G_j with j <= i (or G_last - G_j), never
 // positive, so nothing overflows whatever the decay.
 #include "kla_device.h"
+#include "kla_inverse.h"
 #include "kla_launch.h"
 
 namespace kla {
@@ -45,13 +46,6 @@ struct DiagSmem {
   float A[kChunk][kChunk + 1], P[kChunk][kChunk + 1], X[kChunk][kChunk + 1];
   float b[kChunk], rq[kChunk];
 };
-
-// x from lane `ctrl` of this lane's DPP row (a DPP move with the given control).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               CTRL, 0xF, 0xF, false));
-}
 
 template <typename T>
 __device__ __forceinline__ void put(T *dst, size_t i, float x) {
@@ -302,32 +296,9 @@ __global__ __launch_bounds__(kDiagThreads) void kla_prep_diag_kernel(
   }
   __syncthreads();
 
-  // ---- X = (I + Diag(b) A)^{-1} by forward substitution, row by row: wavefront w takes
-  //      columns 4 w .. 4 w + 3, 16 lanes (one DPP row) a column.  Lane `part` keeps X[l][j]
-  //      for l = part, part + 16, part + 32, part + 48 in registers and sums those terms of
-  //      each dot product; a DPP reduction over the 16 lanes gives every lane the row's value.
-  {
-    const int j = 4 * (tid >> 6) + ((tid & 63) >> 4), part = tid & 15;
-    float xr[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      float acc = 0.f;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int l = part + 16 * q4;
-        if (16 * q4 < i)  // l < i is checked per lane below; rows l >= i hold 0 in xr
-          acc += (l < i ? sm.A[i][l] : 0.f) * xr[q4];
-      }
-      acc += dpp_f32<0xB1>(acc);   // quad_perm [1,0,3,2]
-      acc += dpp_f32<0x4E>(acc);   // quad_perm [2,3,0,1]
-      acc += dpp_f32<0x141>(acc);  // row_half_mirror
-      acc += dpp_f32<0x140>(acc);  // row_mirror
-      const float x = i == j ? 1.f : (i > j ? -sm.b[i] * acc : 0.f);
-      if (part == (i & 15)) xr[i >> 4] = x;
-      if (part == 0) sm.X[i][j] = x;
-    }
-  }
-  __syncthreads();
+  // ---- X = (I + Diag(b) A)^{-1} by 16 x 16 blocks (the staged key tile is free scratch now)
+  blocked_inverse<kDiagThreads, kChunk + 1, kChunk + 1>(&sm.A[0][0], sm.b, &sm.X[0][0],
+                                                        &sm.K[0][0], tid);
 
   // ---- T = X Diag(b) and P, as their ten 16 x 16 blocks on and below the diagonal (tpb_off
   //      layout), in element order of the packed blocks
