@@ -150,3 +150,22 @@ def test_backward_all_sequences_empty(kla):
     torch.cuda.synchronize()
     assert torch.equal(grads[5], dST)
     assert all(x.numel() == 0 for x in grads[:5])
+
+
+def test_backward_zero_keys_at_zero_eps(kla):
+    # eps = 0 and some keys exactly zero: b = 0 there (no write), and the gradients through
+    # the coefficient vanish at those tokens (deta = 0)
+    inp = ki.prefill_inputs(0, T=160)
+    inp["eps"] = 0.0
+    k = inp["k"].clone()
+    k[::7] = 0.0
+    inp["k"] = k.contiguous()
+    ct = ki.cotangents(inp, seed=12)
+    run_case(kla, inp, ct, TOL[torch.float32])
+
+
+def test_backward_hard_projection(kla):
+    # eta = 1, g = 0, eps = 0, q := k: every write is an exact projection (Theorem 1)
+    inp = ki.hard_variant(ki.prefill_inputs(0, T=128))
+    ct = ki.cotangents(inp, seed=13)
+    run_case(kla, inp, ct, TOL[torch.float32])
