@@ -32,9 +32,10 @@
 //                        dV and dS0.
 //   kla_bwd_grad_kernel  one workgroup per (chunk, head): the contractions over d_v with the
 //                        stored S and dS', then the chunk-local algebra, dq, dk, dg, deta.
-// Tiles sit in LDS in fp32.  Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) for fp32
-// inputs, and on bf16 MFMA (v_mfma_f32_16x16x32_bf16, operands rounded to bf16 as they are
-// read, fp32 accumulation) for bf16 inputs.
+// Tiles sit in LDS in fp32 (the gradient kernel's d_v-loop tiles in the operand type).
+// Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) for fp32 inputs, and on bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16, operands rounded to bf16 as they are read, fp32 accumulation)
+// for bf16 inputs.  The block inverse X comes from kla_inverse.h.
 #include "kla_device.h"
 #include "kla_inverse.h"
 #include "kla_launch.h"
@@ -46,7 +47,7 @@ namespace {
 constexpr int kAdjBV = 32;          // state columns per adjoint-scan workgroup
 constexpr int kAdjThreads = 512;    // eight wavefronts, two to a SIMD
 constexpr int kGradThreads = 512;   // eight wavefronts
-constexpr int LDB = kAdjBV + 4;     // row stride of a 32-column fp32 block in LDS
+constexpr int LDB = kAdjBV + 4;     // row stride (elements) of a 32-column block in LDS
 constexpr int LDC = kChunk + 4;     // row stride of a 64 x 64 fp32 tile in LDS
 
 // acc[i][j] += sum_{k < KD} A(i, k) B(k, j) over one 16 x 16 tile: lane (r, kq) = (l % 16,

@@ -15,8 +15,9 @@
 // kla_scan.hip), with unit decays and the per-channel state decay exp(G_last).
 //
 // One 1024-lane workgroup per (chunk, head), everything staged in LDS in fp32.  Every decay
-// factor is an exponential of a difference G_i - G_j with j <= i (or G_last - G_j), never
-// positive, so nothing overflows whatever the decay.
+// factor is an exponential of a non-positive difference of log-decays (G_i - G_j with j <= i,
+// G_last - G_j, or the tile-anchored pieces of the A and P sums), so nothing overflows
+// whatever the decay.  X = (I + Diag(b) A)^{-1} comes from kla_inverse.h.
 #include "kla_device.h"
 #include "kla_inverse.h"
 #include "kla_launch.h"
