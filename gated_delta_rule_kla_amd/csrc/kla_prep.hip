@@ -225,63 +225,34 @@ __host__ __device__ constexpr int xslot(int i, int j) {
   return i == j ? i : (i == 1 ? 4 : (j == 0 ? 5 : 6));
 }
 
-template <int STAGE_BYTES>
 struct PrepSmem {
   alignas(16) float Ld[4][256];  // diagonal blocks of L, row-major
   alignas(16) float XT[7][256];  // X blocks transposed: XT(i, j)[c][r] = X[16 i + r][16 j + c]
   alignas(16) float G2[kChunk];  // G * log2(e)
   alignas(16) float beta[kChunk];
-  alignas(16) unsigned char stage[STAGE_BYTES];  // P, then T, on their way out
 };
 
-// 64 x 64 output tile of element type T staged in LDS: rows of 64 sizeof(T) bytes, 16-byte
-// units XOR-swizzled by row / 2 so that the fragment writes (16 rows x 4 lane groups) and
-// the whole-row reads are both free of bank conflicts.
+// Entries (row, col .. col + 3) of a chunk's 64 x 64 output, col a multiple of 4, straight
+// from registers: in the packed layout (tpb_off; entries of the blocks above the diagonal are
+// not stored) or row-major.  A lane group (r16, kg) covering one 16 x 16 block writes its
+// 256 contiguous packed elements, so a store instruction writes whole lines.
 template <typename T>
-__device__ __forceinline__ int stage_off(int row, int col) {
-  constexpr int RB = kChunk * (int)sizeof(T);
-  const int byte = col * (int)sizeof(T);
-  const int sw = sizeof(T) == 2 ? ((row >> 1) & 7) : (((row >> 1) & 7) << 1);
-  return row * RB + ((((byte >> 4) ^ sw)) << 4) + (byte & 15);
-}
-// Entries (row, col .. col + 3), col a multiple of 4.
-template <typename T>
-__device__ __forceinline__ void stage_put(unsigned char *st, int row, int col, float a, float b,
-                                          float c, float d) {
-  T *p = reinterpret_cast<T *>(st + stage_off<T>(row, col));
+__device__ __forceinline__ void out_put(T *dst, bool packed, int row, int col, float a, float b,
+                                        float c, float d) {
+  int off;
+  if (packed) {
+    const int I = row >> 4, J = col >> 4;
+    if (J > I) return;
+    off = (I * (I + 1) / 2 + J) * 256 + (row & 15) * 16 + (col & 15);
+  } else {
+    off = row * kChunk + col;
+  }
   if constexpr (sizeof(T) == 2) {
     bf16x4 x4;
     x4[0] = from_f32<T>(a); x4[1] = from_f32<T>(b); x4[2] = from_f32<T>(c); x4[3] = from_f32<T>(d);
-    *reinterpret_cast<bf16x4 *>(p) = x4;
+    *reinterpret_cast<bf16x4 *>(dst + off) = x4;
   } else {
-    *reinterpret_cast<f32x4 *>(p) = f32x4{a, b, c, d};
-  }
-}
-// The staged tile to dst (row-major, 64 x 64): every store instruction writes whole rows.
-template <typename T>
-__device__ __forceinline__ void stage_flush(const unsigned char *st, T *dst, int lane) {
-  constexpr int UPR = kChunk * (int)sizeof(T) / 16;  // 16-byte units per row: 8 or 16
-  constexpr int RPI = kWave / UPR;                   // rows per instruction
-#pragma unroll
-  for (int m = 0; m < kChunk / RPI; ++m) {
-    const int row = RPI * m + lane / UPR, u = lane % UPR;
-    const u32x4 v =
-        *reinterpret_cast<const u32x4 *>(st + stage_off<T>(row, u * 16 / (int)sizeof(T)));
-    *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(dst) + row * UPR * 16 + u * 16) =
-        v;
-  }
-}
-// The staged tile's blocks on and below the diagonal to dst, packed (tpb_off): whole 1 KB
-// store instructions.
-template <typename T>
-__device__ __forceinline__ void stage_flush_packed(const unsigned char *st, T *dst, int lane) {
-#pragma unroll
-  for (int m = 0; m < tpb_bytes<T>() / 1024; ++m) {
-    const int pb = 1024 * m + 16 * lane;
-    int row, col;
-    tpb_piece<T>(pb, row, col);
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(st + stage_off<T>(row, col));
-    *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(dst) + pb) = v;
+    *reinterpret_cast<f32x4 *>(dst + off) = f32x4{a, b, c, d};
   }
 }
 
@@ -321,8 +292,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
     float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out,
     float *__restrict__ GD_out, CoefOpts opts, PlanArgs pa) {
-  constexpr int kStage = kChunk * kChunk * (int)(sizeof(Tin) > sizeof(TOut) ? sizeof(Tin) : sizeof(TOut));
-  __shared__ PrepSmem<kStage> sm;
+  __shared__ PrepSmem sm;
   const Planner pl = make_planner(pa, SeqTables{cu, chunk_off}, n_seq);
   write_tables(pl);
   const int task = blockIdx.x;  // chunk * H + head
@@ -440,16 +410,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
   // ---- P = A o Q K^T from the tiles K_j Q_i^T (row 16 i + r16, columns 16 j + 4 kg + e;
   //      zero above the diagonal)
   if (want_p) {
+    Tin *P_task = P_out + (size_t)task * (kChunk * kChunk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int prow = 16 * i + r16;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j <= i; ++j) {
         const int j0 = 16 * j + 4 * kg;
-        if (j > i) {
-          stage_put<Tin>(sm.stage, prow, j0, 0.f, 0.f, 0.f, 0.f);
-          continue;
-        }
         f32x4 accp = zero4();
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) accp = mma(kf[j][ks], qf[i][ks], accp);
@@ -460,11 +427,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
           const bool keep = (j < i) || (4 * kg + e <= r16);
           pv[e] = exp2_fast(keep ? G2me[i] - Gc[e] : -INFINITY) * accp[e] * rqv[i];
         }
-        stage_put<Tin>(sm.stage, prow, j0, pv[0], pv[1], pv[2], pv[3]);
+        out_put<Tin>(P_task, true, prow, j0, pv[0], pv[1], pv[2], pv[3]);
       }
     }
-    lds_barrier();
-    stage_flush_packed<Tin>(sm.stage, P_out + (size_t)task * (kChunk * kChunk), lane);
   }
 
   // ---- L: diagonal blocks to LDS (row-major), sub-diagonal blocks kept in registers in the
@@ -527,7 +492,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
   lds_barrier();
 
   // ---- T = X Diag(b): lane (r16, kg) writes columns 16 j + 4 kg + e of row 16 i + r16.
-  //      Diagonal blocks from LDS, blocks above the diagonal zero, the rest as they form.
+  //      Diagonal blocks from LDS, blocks above the diagonal zero, the rest as they form.  The
+  //      scan's T (written with the decays) goes out as packed blocks, the unit-check stage's
+  //      in full.
+  const bool t_packed = GD_out != nullptr;
+  TOut *T_task = T_out + (size_t)task * (kChunk * kChunk);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int trow = 16 * i + r16;
@@ -536,10 +505,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     float xv[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) xv[s] = XTi[bidx(4 * kg + s, r16)];  // X_ii[r16][4 kg + s]
-    stage_put<TOut>(sm.stage, trow, 16 * i + 4 * kg, xv[0] * bv[0], xv[1] * bv[1], xv[2] * bv[2],
-                    xv[3] * bv[3]);
+    out_put<TOut>(T_task, t_packed, trow, 16 * i + 4 * kg, xv[0] * bv[0], xv[1] * bv[1],
+                  xv[2] * bv[2], xv[3] * bv[3]);
+    if (!t_packed) {
 #pragma unroll
-    for (int j = i + 1; j < 4; ++j) stage_put<TOut>(sm.stage, trow, 16 * j + 4 * kg, 0.f, 0.f, 0.f, 0.f);
+      for (int j = i + 1; j < 4; ++j) out_put<TOut>(T_task, false, trow, 16 * j + 4 * kg, 0.f, 0.f, 0.f, 0.f);
+    }
   }
 
   // ---- sub-diagonal blocks, by distance; the blocks of one distance are independent
@@ -565,8 +536,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
         Zt = __builtin_amdgcn_mfma_f32_16x16x4f32(Y[s], XTi[bidx(4 * kg + s, r16)], Zt, 0, 0, 0);
       // lane (r16, kg) now holds X_ij[r16][4 kg + e] = -Zt[e]
       const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * j + 4 * kg]);
-      stage_put<TOut>(sm.stage, 16 * i + r16, 16 * j + 4 * kg, -Zt[0] * bv[0], -Zt[1] * bv[1],
-                      -Zt[2] * bv[2], -Zt[3] * bv[3]);
+      out_put<TOut>(T_task, t_packed, 16 * i + r16, 16 * j + 4 * kg, -Zt[0] * bv[0],
+                    -Zt[1] * bv[1], -Zt[2] * bv[2], -Zt[3] * bv[3]);
       if (i < 3) {  // read again by the next distances
         float *XTo = sm.XT[xslot(i, j)];
 #pragma unroll
@@ -575,11 +546,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     }
     lds_barrier();
   }
-  // the scan's T (written with the decays) as packed blocks, the unit-check stage's in full
-  if (GD_out)
-    stage_flush_packed<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane);
-  else
-    stage_flush<TOut>(sm.stage, T_out + (size_t)task * (kChunk * kChunk), lane);
 }
 
 template <typename Tin, int DK>
