@@ -383,9 +383,9 @@ kla_status kla_prefill_backward(const void *q, const void *k, const void *v, con
                         static_cast<const void *>(S0), static_cast<const void *>(dS_T),
                         static_cast<const void *>(dg), static_cast<const void *>(deta),
                         static_cast<const void *>(dS0)})
-    if (p && !aligned16(p))
+    if (p && !aligned_to(p, 4))
       return fail(KLA_ERR_INVALID_ARGUMENT,
-                  "g, eta, S0, dS_T, dg, deta, dS0 must be 16-byte aligned");
+                  "g, eta, S0, dS_T, dg, deta, dS0 must be 4-byte aligned");
   const size_t es = elem_size(dtype);
   const size_t nq = (size_t)total_tokens * n_heads * d_k * es;
   const size_t nv = (size_t)total_tokens * n_heads * d_v * es;

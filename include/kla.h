@@ -282,8 +282,9 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const
  *               stored, the cotangent of every chunk's outgoing state and the
  *               per-chunk dU and dR, all fp32.
  * The gradient buffers must not overlap each other, the inputs or the
- * workspace.  Alignment, size limits and errors as for kla_prefill_chunked;
- * zero-length sequences get dS0 = dS_T.
+ * workspace.  q, k, v, dO, dq, dk and dv must be 16-byte aligned; g, eta, S0,
+ * dS_T, dg, deta and dS0 4-byte aligned.  Size limits and errors as for
+ * kla_prefill_chunked; zero-length sequences get dS0 = dS_T.
  */
 size_t kla_prefill_backward_workspace_bytes(int32_t n_seq, int32_t total_tokens,
                                             int32_t n_heads, int32_t d_k, int32_t d_v,

@@ -230,7 +230,8 @@ def test_backward_workspace_and_errors(lib):
         (dict(dk_=96), UNSUPPORTED),
         (dict(dO=None), INVALID),
         (dict(dq=None), INVALID),
-        (dict(dk=FAKE + 4), INVALID),                 # misaligned
+        (dict(dk=FAKE + 4), INVALID),                 # misaligned (16-byte vector access)
+        (dict(dg=FAKE * 10 + 2), INVALID),            # misaligned (4-byte scalars)
         (dict(dg=FAKE * 5), INVALID),                 # dg overlaps eta
         (dict(dv=FAKE * 7), INVALID),                 # two gradients in one buffer
         (dict(n_tok=255), INVALID),                   # dense: 255 tokens over 2 sequences
