@@ -97,9 +97,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); the sharding design is described in DESIGN.md",
-              file=sys.stderr, flush=True)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); sequences and heads shard across GPUs with no exchange, "
+              f"so the path is timed on one GPU's share", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import torch
