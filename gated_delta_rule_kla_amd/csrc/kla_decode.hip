@@ -1,8 +1,8 @@
 // kla_decode.hip -- single-token decode step, one HBM read and one HBM write of the state.
 //
 // Paper "Kaczmarz Linear Attention" (arXiv 2605.08587), Algorithm 1 tokenwise
-// panel (steps 2-6) with the coefficient of Eq. (3).  Substituting step 5 into
-// step 6 gives o = a q S + b (q . k) e, so with
+// panel with the coefficient of Eq. (3).  Substituting the write into the readout
+// gives o = a q S + b (q . k) e, so with
 //   r = k S,  p = q S  (column reductions over d_k of the OLD state)
 //   e = v - a r,  b = eta / (||k||^2 + eps)
 //   S' = a S + b k^T e,   o = a p + b (q . k) e

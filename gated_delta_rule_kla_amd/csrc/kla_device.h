@@ -195,7 +195,7 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // the default; section 2 for the gated delta rule's b_t = eta_t; Appendix D and Table 5 for
 // the key-norm-only coefficient and the sequence factors 1/t, 1/sqrt(t), 1/log(t + 1) on
 // the Kaczmarz coefficient, t the absolute 1-based position in the sequence; section 3.3
-// and Algorithm 1 step 6 for the readout divided by ||q_t||).
+// and Algorithm 1's readout for the readout divided by ||q_t||).
 enum BetaMode { kBetaKaczmarz = 0, kBetaGated = 1, kBetaKeyNorm = 2, kBetaInvT = 3,
                 kBetaInvSqrtT = 4, kBetaInvLogT = 5 };
 struct CoefOpts {

@@ -120,7 +120,7 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
  * kla_prefill_prepare(...) followed by kla_prefill_scan(...) on one stream.
  *
  * kla_prefill_prepare: per-chunk stage (paper section 4, Algorithm 1 chunkwise
- *   panel steps 2-6 up to the triangular solve): sequence tables, the chunk-local
+ *   panel up to the triangular solve): sequence tables, the chunk-local
  *   decays exp(G_i) and exp(G_last - G_i), T = (I + L)^{-1} Diag(b) and the
  *   intra-chunk matrix P = A o Q K^T of Eq. (8) for every chunk, written into
  *   `workspace`.
@@ -145,7 +145,7 @@ kla_status kla_prefill_scan(const void *q, const void *k, const void *v, const f
 
 /*
  * One decode step per sequence: (q, k, v, g, eta, eps, S) -> (o, S').
- * Paper Algorithm 1 tokenwise panel steps 2-6 (with Eq. (3)), evaluated with
+ * Paper Algorithm 1 tokenwise panel (with Eq. (3)), evaluated with
  * a single read and a single write of S:  r = k S, p = q S,
  * e = v - a r, S' = a S + b k^T e, o = a p + b (q . k) e.
  *
@@ -195,7 +195,7 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
  *   KLA_BETA_INV_LOG_T    Kaczmarz coefficient x 1 / log(t + 1) the absolute 1-based position
  * Wherever b_t divides by ||k_t||^2 + eps, a zero denominator gives b_t = 0.
  * normalize_q != 0 gives the readout o_t = q_t S_t / ||q_t||_2 of section 3.3 and
- * Algorithm 1 step 6 (o_t = 0 for a zero query); 0 gives o_t = q_t S_t.
+ * Algorithm 1's readout (o_t = 0 for a zero query); 0 gives o_t = q_t S_t.
  * pos_offset (device int32, [n_seq] for prefill, [batch] for decode, or NULL for
  * all zeros) places a call's tokens in their sequences: the first token of
  * sequence n in a prefill call is at position pos_offset[n] + 1, a decode step

@@ -13,10 +13,10 @@
  *
  *     a_t  = exp(g_t)                       decay; the blog "From Gated DeltaNet
  *                                            to Kaczmarz" s.2 writes alpha_t = exp(g_t)
- *     S~   = a_t S_{t-1}                    forget first               (Alg. 1 step 2)
- *     e_t  = v_t - k_t S~                   residual                   (Alg. 1 step 3)
- *     b_t  = eta_t / (||k_t||^2 + eps)      Kaczmarz step, Eq. (3)     (Alg. 1 step 4)
- *     S_t  = S~ + b_t k_t^T e_t             rank-one projection write  (Alg. 1 step 5)
+ *     S~   = a_t S_{t-1}                    forget first               (Alg. 1, forget)
+ *     e_t  = v_t - k_t S~                   residual                   (Alg. 1, residual)
+ *     b_t  = eta_t / (||k_t||^2 + eps)      Kaczmarz step, Eq. (3)     (Alg. 1, step size)
+ *     S_t  = S~ + b_t k_t^T e_t             rank-one projection write  (Alg. 1, write)
  *     o_t  = q_t S_t                        readout on the q given (no 1/||q||;
  *                                            normalising q is the caller's job)
  *
@@ -30,7 +30,7 @@
  *                 t the absolute 1-based position in the sequence (Appendix D,
  *                 "sequence factor"; the second factor is printed without its
  *                 root in the extracted text and read as 1/sqrt(t))
- *   normq   o_t = q_t S_t / ||q_t||_2 (s.3.3, Algorithm 1 step 6), 0 for q_t = 0
+ *   normq   o_t = q_t S_t / ||q_t||_2 (s.3.3, Algorithm 1 readout), 0 for q_t = 0
  *   gdiag   diagonal gating (Appendix B.5, "Extension to diagonal gating"): the decay is
  *           Diag(alpha_t) with one log-decay g_t[i] per key channel i, so the forget step
  *           scales row i of the state by exp(g_t[i]); everything else, the coefficient

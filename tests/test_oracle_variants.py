@@ -3,7 +3,7 @@
 The variants are the pages' ablations of the coefficient (paper section 2 for the gated
 delta rule's b_t = eta_t; Table 5 and Appendix D for key-norm only and the sequence
 factors on the Kaczmarz coefficient, t the absolute position) and the readout divided by
-||q_t|| (section 3.3, Algorithm 1 step 6).  Each test ties a variant either to a closed
+||q_t|| (section 3.3, Algorithm 1's readout).  Each test ties a variant either to a closed
 form or to the pinned default method under the substitution the variant's definition
 implies, so that a wrong position base, a dropped eta or a misplaced norm fails.
 """
