@@ -15,8 +15,12 @@ automatic differentiation in plain PyTorch CPU ops in float64:
 for the scalar loss  L = <dO, O> + <dS_T, S_T>, so that the returned tensors are the
 vector-Jacobian products (dq, dk, dv, dg, deta, dS0) of the forward map
 (q, k, v, g, eta, S0) -> (O, S_T) with the cotangents (dO, dS_T).  Sequences are independent;
-packed input follows ``cu_seqlens`` as in the forward oracle.  Only the default variant
-(Kaczmarz coefficient, one scalar gate per token-head, o_t = q_t S_t) is covered.
+packed input follows ``cu_seqlens`` as in the forward oracle.  The coefficient variants of
+the forward oracle are covered (``beta_mode``: the gated delta rule's b_t = eta_t, section 2;
+key-norm only b_t = 1/(||k_t||^2 + eps) and the sequence factors 1/t, 1/sqrt(t),
+1/log(t + 1) on the Kaczmarz coefficient, Appendix D and Table 5; t the absolute 1-based
+position, sequence n starting at pos_offset[n] + 1), with one scalar gate per token-head and
+o_t = q_t S_t.
 """
 from __future__ import annotations
 
@@ -28,17 +32,39 @@ def _t(x):
     return torch.as_tensor(np.asarray(x, dtype=np.float64))
 
 
-def _sequence(q, k, v, g, eta, eps, S0):
-    """The tokenwise recurrence over one sequence, all heads at once: (O [T, H, dv], S_T)."""
+MODES = ("kaczmarz", "gated", "key_norm", "inv_t", "inv_sqrt_t", "inv_log_t")
+
+
+def _coef(mode, eta_t, den, pos):
+    """b_t for one token of every head; a zero denominator gives 0 wherever b_t divides by it."""
+    if mode == "gated":
+        return eta_t
+    nz = den != 0
+    rden = torch.where(nz, 1.0 / torch.where(nz, den, torch.ones_like(den)), torch.zeros_like(den))
+    if mode == "key_norm":
+        return rden
+    b = eta_t * rden
+    if mode == "inv_t":
+        b = b / pos
+    elif mode == "inv_sqrt_t":
+        b = b / np.sqrt(pos)
+    elif mode == "inv_log_t":
+        b = b / np.log(pos + 1.0)
+    elif mode != "kaczmarz":
+        raise ValueError(f"unknown beta_mode {mode}")
+    return b
+
+
+def _sequence(q, k, v, g, eta, eps, S0, mode="kaczmarz", pos0=0):
+    """The tokenwise recurrence over one sequence, all heads at once: (O [T, H, dv], S_T).
+    Token t of the sequence is at absolute position pos0 + t + 1."""
     S = S0
     outs = []
     for t in range(q.shape[0]):
         kt, qt = k[t], q[t]                                   # [H, dk]
         a = torch.exp(g[t])                                   # [H]
         den = (kt * kt).sum(-1) + eps                         # [H]
-        nz = den != 0
-        b = torch.where(nz, eta[t] / torch.where(nz, den, torch.ones_like(den)),
-                        torch.zeros_like(den))
+        b = _coef(mode, eta[t], den, float(pos0 + t + 1))
         St = a[:, None, None] * S                             # forget
         e = v[t] - torch.einsum("hi,hij->hj", kt, St)         # residual
         S = St + b[:, None, None] * kt[:, :, None] * e[:, None, :]   # Kaczmarz write
@@ -47,12 +73,14 @@ def _sequence(q, k, v, g, eta, eps, S0):
     return O, S
 
 
-def prefill_backward(q, k, v, g, eta, eps, dO, S0=None, dS_T=None, cu_seqlens=None, n_seq=1):
+def prefill_backward(q, k, v, g, eta, eps, dO, S0=None, dS_T=None, cu_seqlens=None, n_seq=1,
+                     beta_mode="kaczmarz", pos_offset=None):
     """Gradients of the prefill for the cotangents dO [n_tok, H, dv] and dS_T [n_seq, H, dk, dv].
 
     Inputs as for :func:`oracle.prefill` (q, k [n_tok, H, dk]; v [n_tok, H, dv];
     g, eta [n_tok, H]; S0 [n_seq, H, dk, dv] or None = zeros; dS_T None = zeros);
-    without cu_seqlens the tokens are n_seq sequences of equal length.
+    without cu_seqlens the tokens are n_seq sequences of equal length.  beta_mode and
+    pos_offset ([n_seq] or None) select the coefficient variant as in the forward oracle.
     Returns numpy float64 arrays (dq, dk, dv, dg, deta, dS0), shaped like the inputs.
     """
     q, k, v, g, eta, dO = (_t(x) for x in (q, k, v, g, eta, dO))
@@ -72,7 +100,9 @@ def prefill_backward(q, k, v, g, eta, eps, dO, S0=None, dS_T=None, cu_seqlens=No
     loss = q.new_zeros(())
     for n in range(n_seq):
         s, e = int(cu[n]), int(cu[n + 1])
-        O, ST = _sequence(q[s:e], k[s:e], v[s:e], g[s:e], eta[s:e], float(eps), S0[n])
+        pos0 = 0 if pos_offset is None else int(pos_offset[n])
+        O, ST = _sequence(q[s:e], k[s:e], v[s:e], g[s:e], eta[s:e], float(eps), S0[n],
+                          beta_mode, pos0)
         loss = loss + (O * dO[s:e]).sum() + (ST * dS_T[n]).sum()
     grads = torch.autograd.grad(loss, (q, k, v, g, eta, S0), allow_unused=True)
     out = []

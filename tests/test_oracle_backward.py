@@ -137,3 +137,34 @@ def test_dense_sequences_equal_packed():
                                  cu_seqlens=np.array([0, 8, 16, 24]))
     for a, b in zip(dense, packed):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("mode", ["gated", "key_norm", "inv_t", "inv_sqrt_t", "inv_log_t"])
+def test_variant_gradients_match_central_differences(mode):
+    # the coefficient variants, each against central differences of the C oracle run in the
+    # same mode (packed, with position offsets for the sequence factors)
+    q, k, v, g, eta, S0, dO, dST = draw(7, 5, H=2, dk=3, dv=2, n_seq=2)
+    cu = np.array([0, 3, 5])
+    pos = np.array([4, 0], dtype=np.int32)
+    eps = 0.1
+    grads = ob.prefill_backward(q, k, v, g, eta, eps, dO, S0=S0, dS_T=dST, cu_seqlens=cu,
+                                beta_mode=mode, pos_offset=pos)
+
+    def loss(xs):
+        O, ST = oracle.prefill(*xs[:5], eps, S0=xs[5], cu_seqlens=cu, beta_mode=mode,
+                               pos_offset=pos)
+        return float((O * dO).sum() + (ST * dST).sum())
+    inputs = [q, k, v, g, eta, S0]
+    h = 1e-6
+    for which, (x, gx) in enumerate(zip(inputs, grads)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = [a.copy() for a in inputs]
+            xm = [a.copy() for a in inputs]
+            xp[which][idx] += h
+            xm[which][idx] -= h
+            num[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        err = np.abs(num - gx).max() / max(np.abs(num).max(), 1e-300)
+        assert err < 1e-6, (mode, which, err)
+    if mode == "key_norm":
+        assert np.abs(grads[4]).max() == 0.0  # b does not depend on eta
