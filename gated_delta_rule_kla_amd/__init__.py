@@ -94,6 +94,8 @@ def load_library():
                                          vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp,
                                          sz, vp]
     lib.kla_prefill_backward.restype = ctypes.c_int
+    lib.kla_prefill_backward_ex.argtypes = lib.kla_prefill_backward.argtypes[:-1] + [opt_p, vp]
+    lib.kla_prefill_backward_ex.restype = ctypes.c_int
     lib.kla_status_string.argtypes = [ctypes.c_int]
     lib.kla_status_string.restype = ctypes.c_char_p
     lib.kla_last_error.argtypes = []
@@ -258,12 +260,13 @@ def kla_prefill_backward_workspace_bytes(n_seq: int, total_tokens: int, n_heads:
 
 def kla_prefill_backward(q, k, v, g, eta, eps: float, dO, S0=None, dS_T=None, cu_seqlens=None,
                          n_seq=None, *, cu_seqlens_host=None, workspace=None,
-                         need_dS0=True):
+                         need_dS0=True, beta_mode="kaczmarz", pos_offset=None):
     """Gradients of the prefill for the cotangents dO (like o) and dS_T (like S_T, or None).
 
-    Inputs as for :func:`kla_prefill_chunked` (default variant only: Kaczmarz coefficient,
-    scalar gate, o = q S).  Returns (dq, dk, dv, dg, deta, dS0), shaped like q, k, v, g, eta
-    and S0 ([n_seq, H, d_k, d_v]; None when need_dS0 is False).
+    Inputs as for :func:`kla_prefill_chunked`, with a scalar gate and o = q S; beta_mode /
+    pos_offset select the coefficient variant of the forward call.  Returns
+    (dq, dk, dv, dg, deta, dS0), shaped like q, k, v, g, eta and S0 ([n_seq, H, d_k, d_v];
+    None when need_dS0 is False).
     """
     shape_q, shape_v, shape_g = q.shape, v.shape, g.shape
     q, k, v, g, eta, n_seq = _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq)
@@ -307,11 +310,12 @@ def kla_prefill_backward(q, k, v, g, eta, eps: float, dO, S0=None, dS_T=None, cu
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     host_ptr = None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr())
-    _check(lib.kla_prefill_backward(
+    opts = _options(beta_mode, False, pos_offset, n_seq, dev)
+    _check(lib.kla_prefill_backward_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S0), _ptr(dO),
         _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(deta), _ptr(dS0),
         _ptr(cu_seqlens), host_ptr, n_seq, n_tok, H, d_k, d_v, _DTYPES[dt], _ptr(workspace),
-        workspace.numel(), _stream(dev)))
+        workspace.numel(), opts, _stream(dev)))
     return (dq.reshape(shape_q), dk.reshape(shape_q), dv.reshape(shape_v), dg.reshape(shape_g),
             deta.reshape(shape_g), dS0)
 

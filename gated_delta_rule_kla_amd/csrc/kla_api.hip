@@ -360,17 +360,24 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
                                 workspace_bytes, nullptr, stream);
 }
 
-kla_status kla_prefill_backward(const void *q, const void *k, const void *v, const float *g,
-                                const float *eta, float eps, const float *S0, const void *dO,
-                                const float *dS_T, void *dq, void *dk, void *dv, float *dg,
-                                float *deta, float *dS0, const int32_t *cu_seqlens,
-                                const int32_t *cu_seqlens_host, int32_t n_seq,
-                                int32_t total_tokens, int32_t n_heads, int32_t d_k, int32_t d_v,
-                                kla_dtype dtype, void *workspace, size_t workspace_bytes,
-                                void *stream) {
-  kla_status st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v,
-                                      dtype, eps);
+kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, const float *g,
+                                   const float *eta, float eps, const float *S0, const void *dO,
+                                   const float *dS_T, void *dq, void *dk, void *dv, float *dg,
+                                   float *deta, float *dS0, const int32_t *cu_seqlens,
+                                   const int32_t *cu_seqlens_host, int32_t n_seq,
+                                   int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                                   int32_t d_v, kla_dtype dtype, void *workspace,
+                                   size_t workspace_bytes, const kla_options *opts, void *stream) {
+  kla::CoefOpts co;
+  kla_status st = to_coef(opts, &co);
   if (st != KLA_OK) return st;
+  if (co.normalize_q || co.diag_gate)
+    return fail(KLA_ERR_UNSUPPORTED,
+                "the backward pass takes the coefficient modes only (no normalised readout, "
+                "no diagonal gate)");
+  if ((st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
+                                eps)) != KLA_OK)
+    return st;
   if (total_tokens > 0 && (!q || !k || !v || !g || !eta || !dO || !dq || !dk || !dv || !dg || !deta))
     return fail(KLA_ERR_INVALID_ARGUMENT,
                 "q, k, v, g, eta, dO, dq, dk, dv, dg and deta are required");
@@ -415,7 +422,6 @@ kla_status kla_prefill_backward(const void *q, const void *k, const void *v, con
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear any stale error from unrelated work
-  const kla::CoefOpts co{kla::kBetaKaczmarz, 0, nullptr};
   if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
                             dtype, workspace, s)) != KLA_OK)
     return st;
@@ -428,7 +434,7 @@ kla_status kla_prefill_backward(const void *q, const void *k, const void *v, con
                        "scan (stored states)")) != KLA_OK)
     return st;
   if ((st = hip_status(
-           kla::launch_bwd(to_dt(dtype), d_k, d_v, q, k, v, dO, g, eta, eps, wv.GD, wv.T, wv.P,
+           kla::launch_bwd(to_dt(dtype), d_k, d_v, q, k, v, dO, g, eta, eps, co, wv.GD, wv.T, wv.P,
                            dS_T, SN, reinterpret_cast<float *>(ws + bl.off_dSo),
                            reinterpret_cast<float *>(ws + bl.off_dU),
                            reinterpret_cast<float *>(ws + bl.off_dR), dq, dk, dv, dg, deta, dS0,
@@ -437,6 +443,19 @@ kla_status kla_prefill_backward(const void *q, const void *k, const void *v, con
            "backward")) != KLA_OK)
     return st;
   return ok();
+}
+
+kla_status kla_prefill_backward(const void *q, const void *k, const void *v, const float *g,
+                                const float *eta, float eps, const float *S0, const void *dO,
+                                const float *dS_T, void *dq, void *dk, void *dv, float *dg,
+                                float *deta, float *dS0, const int32_t *cu_seqlens,
+                                const int32_t *cu_seqlens_host, int32_t n_seq,
+                                int32_t total_tokens, int32_t n_heads, int32_t d_k, int32_t d_v,
+                                kla_dtype dtype, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  return kla_prefill_backward_ex(q, k, v, g, eta, eps, S0, dO, dS_T, dq, dk, dv, dg, deta, dS0,
+                                 cu_seqlens, cu_seqlens_host, n_seq, total_tokens, n_heads, d_k,
+                                 d_v, dtype, workspace, workspace_bytes, nullptr, stream);
 }
 
 kla_status kla_prefill_prepare_ex(const void *q, const void *k, const float *g,

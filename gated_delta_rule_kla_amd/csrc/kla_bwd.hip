@@ -3,8 +3,9 @@
 //
 // Paper "Kaczmarz Linear Attention" (arXiv 2605.08587) trains with the chunkwise algorithm of
 // Propositions 3-4 (Eq. (7)-(9)) but derives no backward pass.  What follows is the
-// reverse-mode derivative of that chunk solve, for the default variant (Kaczmarz coefficient
-// of Eq. (3), one scalar gate per token-head, o_t = q_t S_t).  Per chunk of one
+// reverse-mode derivative of that chunk solve, with one scalar gate per token-head and
+// o_t = q_t S_t, for the Kaczmarz coefficient of Eq. (3) and its variants (the gated rule's
+// b = eta, key-norm only, the sequence factors; b enters only through db below).  Per chunk of one
 // (sequence, head), with S the chunk's incoming state, G the chunk-local inclusive prefix of
 // g, Gamma_ij = exp(G_i - G_j), gam_i = exp(G_i), dec_i = exp(G_last - G_i),
 // A = strict_lower(Gamma o K K^T), P = lower(Gamma o Q K^T), X = (I + Diag(b) A)^{-1},
@@ -16,10 +17,11 @@
 //     dS = exp(G_last) dS' + Q^T Diag(gam) dO - K^T Diag(gam) dR    (the previous chunk's dS')
 //     dP = lower(dO U^T),  dT = lower(dU R^T),  dX = dT Diag(b),
 //     dL = -strict_lower(X^T dX X^T),  dA = Diag(b) dL,
-//     db = colsum(dT o X) + rowsum(dL o A),  deta = db / den,
+//     db = colsum(dT o X) + rowsum(dL o A),  deta = db (d b / d eta),
 //     dQ = Diag(gam) dO S^T + (dP o Gamma) K,
 //     dK = Diag(dec) U dS'^T - Diag(gam) dR S^T + (dP o Gamma)^T Q + (dA o Gamma) K
-//          + (dA o Gamma)^T K - Diag(2 b db / den) K,
+//          + (dA o Gamma)^T K - Diag(2 b db / den) K   (that last term where b depends on
+//          ||k||^2: every mode but the gated rule's),
 //     dG_i = gam_i q_i.(dO S^T)_i - gam_i k_i.(dR S^T)_i - dec_i k_i.(U dS'^T)_i
 //            + rowsum_i(Z) - colsum_i(Z),   Z = dP o P + dA o A,
 //     dG_last += exp(G_last) <dS', S> + sum_j dec_j k_j.(U dS'^T)_j,
@@ -388,6 +390,7 @@ struct GradSmem {
     } pa;
   } u;
   float gam[kChunk], dec[kChunk], G[kChunk], b[kChunk], den[kChunk], db[kChunk];
+  float db_deta[kChunk];  // the derivative of b in eta
   float rz[kChunk], cz[kChunk];
   float dots[3][2][kChunk];  // row dots of the three d_v contractions, two partial sums each
   float red[kGradThreads / 64];
@@ -399,7 +402,7 @@ template <typename Tin, int DK>
 __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ dO, const float *__restrict__ g, const float *__restrict__ eta,
-    float eps, const float *__restrict__ SN, const float *__restrict__ dSo,
+    float eps, CoefOpts opts, const float *__restrict__ SN, const float *__restrict__ dSo,
     const float *__restrict__ dUo, const float *__restrict__ dRo, Tin *__restrict__ dq,
     Tin *__restrict__ dk, float *__restrict__ dg, float *__restrict__ deta,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq, int H,
@@ -447,7 +450,16 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     if (part == 0) {
       const float den = kk + eps;
       sm.den[i] = den;
-      sm.b[i] = i < len ? write_coef(kBetaKaczmarz, eta[tok + (size_t)i * H], den, 1.f) : 0.f;
+      float bi = 0.f, ci = 0.f;  // b and its derivative in eta
+      if (i < len) {
+        const float t_abs =
+            (float)(t0 + i - cu[n] + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
+        bi = write_coef(opts.beta_mode, eta[tok + (size_t)i * H], den, t_abs);
+        // every mode but key-norm only is linear in eta: db/deta is the coefficient at eta = 1
+        ci = opts.beta_mode == kBetaKeyNorm ? 0.f : write_coef(opts.beta_mode, 1.f, den, t_abs);
+      }
+      sm.b[i] = bi;
+      sm.db_deta[i] = ci;
     }
   }
   // ---- A = strict_lower(Gamma o K K^T): all 16 tiles, two per wavefront (zeros above)
@@ -741,8 +753,11 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * mti + 4 * kq + e, col = 16 * tj + r16;
+      // b depends on k through den = ||k||^2 + eps (all modes but the gated rule's b = eta)
       const float den = sm.den[row];
-      const float cb = den != 0.f ? -2.f * sm.b[row] * sm.db[row] * __builtin_amdgcn_rcpf(den) : 0.f;
+      const float cb = opts.beta_mode != kBetaGated && den != 0.f
+                           ? -2.f * sm.b[row] * sm.db[row] * __builtin_amdgcn_rcpf(den)
+                           : 0.f;
       ak[e] += cb * sm.K[row][col];
       if (row < len) {
         const size_t o = (tok + (size_t)row * H) * DK + col;
@@ -768,8 +783,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const float dgi = __shfl(rev, kChunk - 1 - i, kWave);
     if (i < len) {
       dg[tok + (size_t)i * H] = dgi;
-      const float den = sm.den[i];
-      deta[tok + (size_t)i * H] = den != 0.f ? sm.db[i] * __builtin_amdgcn_rcpf(den) : 0.f;
+      deta[tok + (size_t)i * H] = sm.db[i] * sm.db_deta[i];
     }
   }
 }
@@ -777,7 +791,8 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 template <typename Tin, int DK>
 static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void *v,
                                const void *dO, const float *g, const float *eta, float eps,
-                               const float *GD, const void *T, const void *P, const float *dST,
+                               const CoefOpts &opts, const float *GD, const void *T,
+                               const void *P, const float *dST,
                                const float *SN, float *dSo, float *dU, float *dR, void *dq,
                                void *dk, void *dv, float *dg, float *deta, float *dS0,
                                SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
@@ -806,7 +821,7 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
   if (grad_blocks > 0)
     hipLaunchKernelGGL((kla_bwd_grad_kernel<Tin, DK>), dim3((unsigned)grad_blocks),
                        dim3(kGradThreads), smG, stream, qt, kt, static_cast<const Tin *>(v),
-                       static_cast<const Tin *>(dO), g, eta, eps, SN, dSo, dU, dR,
+                       static_cast<const Tin *>(dO), g, eta, eps, opts, SN, dSo, dU, dR,
                        static_cast<Tin *>(dq), static_cast<Tin *>(dk), dg, deta, t.cu,
                        t.chunk_off, n_seq, H, d_v);
   return hipGetLastError();
@@ -814,12 +829,12 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
 
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
-                      const float *GD, const void *T, const void *P, const float *dST,
+                      const CoefOpts &opts, const float *GD, const void *T, const void *P, const float *dST,
                       const float *SN, float *dSo, float *dU, float *dR, void *dq, void *dk,
                       void *dv, float *dg, float *deta, float *dS0, SeqTables t, int32_t n_seq,
                       int64_t n_chunks_ub, int32_t H, hipStream_t stream) {
 #define KLA_BWD(TIN, DK_)                                                                     \
-  return launch_bwd_t<TIN, DK_>(d_v, q, k, v, dO, g, eta, eps, GD, T, P, dST, SN, dSo, dU, dR, \
+  return launch_bwd_t<TIN, DK_>(d_v, q, k, v, dO, g, eta, eps, opts, GD, T, P, dST, SN, dSo, dU, dR, \
                                 dq, dk, dv, dg, deta, dS0, t, n_seq, n_chunks_ub, H, stream);
   if (dt == Dtype::BF16) {
     if (d_k == 128) { KLA_BWD(__bf16, 128) }

@@ -83,13 +83,13 @@ hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k,
                        float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream,
                        const DiagTiles *diag = nullptr, float *SN = nullptr);
 
-// The backward pass after launch_prep and launch_scan with SN: the adjoint scan (dS' per
+// The backward pass after launch_prep (with the same opts) and launch_scan with SN: the adjoint scan (dS' per
 // chunk into dSo, dU and dR into their [chunk][H][64][d_v] fp32 buffers, dv, and dS0 if
 // non-null), then the per-chunk gradients dq, dk (operand type) and dg, deta (fp32).  dST
 // may be null (a zero cotangent of the final state).
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
-                      const float *GD, const void *T, const void *P, const float *dST,
+                      const CoefOpts &opts, const float *GD, const void *T, const void *P, const float *dST,
                       const float *SN, float *dSo, float *dU, float *dR, void *dq, void *dk,
                       void *dv, float *dg, float *deta, float *dS0, SeqTables t, int32_t n_seq,
                       int64_t n_chunks_ub, int32_t H, hipStream_t stream);

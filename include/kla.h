@@ -263,7 +263,7 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const
  * Backward pass of the chunkwise prefill: the gradients (dq, dk, dv, dg, deta,
  * dS0) of the scalar loss <dO, o> + <dS_T, S_T> for the default variant
  * (Kaczmarz coefficient of Eq. (3), one scalar gate per token-head,
- * o_t = q_t S_t).  The paper trains with the chunkwise algorithm (section 4,
+ * o_t = q_t S_t; kla_prefill_backward_ex below adds the coefficient modes).  The paper trains with the chunkwise algorithm (section 4,
  * Propositions 3-4, Eq. (7)-(9)) but derives no backward pass; these are the
  * exact derivatives of that chunk solve, so of the tokenwise recurrence
  * (Algorithm 1), up to rounding.
@@ -297,6 +297,19 @@ kla_status kla_prefill_backward(const void *q, const void *k, const void *v, con
                                 int32_t total_tokens, int32_t n_heads, int32_t d_k, int32_t d_v,
                                 kla_dtype dtype, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/* kla_prefill_backward with options (NULL = the defaults): the coefficient
+ * modes (beta_mode, pos_offset) are supported; normalize_q or diagonal_gate
+ * give KLA_ERR_UNSUPPORTED.  The forward arguments and options must be those
+ * of the forward call whose gradients are wanted. */
+kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, const float *g,
+                                   const float *eta, float eps, const float *S0, const void *dO,
+                                   const float *dS_T, void *dq, void *dk, void *dv, float *dg,
+                                   float *deta, float *dS0, const int32_t *cu_seqlens,
+                                   const int32_t *cu_seqlens_host, int32_t n_seq,
+                                   int32_t total_tokens, int32_t n_heads, int32_t d_k,
+                                   int32_t d_v, kla_dtype dtype, void *workspace,
+                                   size_t workspace_bytes, const kla_options *opts, void *stream);
 
 /* Static description of a status code. */
 const char *kla_status_string(kla_status status);

@@ -169,3 +169,38 @@ def test_backward_hard_projection(kla):
     inp = ki.hard_variant(ki.prefill_inputs(0, T=128))
     ct = ki.cotangents(inp, seed=13)
     run_case(kla, inp, ct, TOL[torch.float32])
+
+
+@pytest.mark.parametrize("mode", ["gated", "key_norm", "inv_t", "inv_sqrt_t", "inv_log_t"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_coefficient_modes(kla, mode, dtype):
+    # packed sequences with position offsets; unit-norm keys keep the gated rule bounded
+    # (b ||k||^2 = eta < 2)
+    inp = ki.prefill_inputs(0, lens=(150, 40, 77), H=2)
+    kf = inp["k"].float()
+    inp["k"] = (kf / kf.norm(dim=-1, keepdim=True)).to(dtype).contiguous()
+    inp["q"], inp["v"] = inp["q"].to(dtype).contiguous(), inp["v"].to(dtype).contiguous()
+    inp["dtype"] = dtype
+    gen = torch.Generator().manual_seed(21)
+    inp["S0"] = 0.3 * torch.randn(3, 2, 64, 64, generator=gen)
+    pos = torch.tensor([5, 0, 300], dtype=torch.int32)
+    ct = ki.cotangents(inp, seed=22)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    grads = kla.kla_prefill_backward(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                     ct["dO"].to(DEV), S0=d["S0"], dS_T=ct["dS_T"].to(DEV),
+                                     cu_seqlens=d["cu_seqlens"], n_seq=d["n_seq"],
+                                     beta_mode=mode, pos_offset=pos.to(DEV))
+    torch.cuda.synchronize()
+    f64 = lambda t: t.double().numpy()
+    ref = ob.prefill_backward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["g"]),
+                              f64(inp["eta"]), inp["eps"], f64(ct["dO"]), S0=f64(inp["S0"]),
+                              dS_T=f64(ct["dS_T"]), cu_seqlens=inp["cu_seqlens"].numpy(),
+                              beta_mode=mode, pos_offset=pos.numpy())
+    print(f"mode {mode} {dtype}", flush=True)
+    for name, x, y in zip(NAMES, grads, ref):
+        if name == "deta" and mode == "key_norm":
+            assert torch.count_nonzero(x) == 0, "deta must vanish: b does not depend on eta"
+            continue
+        e = err(x, y)
+        print(f"  {name}: err {e:.3e} (bar {TOL[dtype]:g})", flush=True)
+        assert e < TOL[dtype], f"{name}: err {e:.3e} >= {TOL[dtype]:g}"
