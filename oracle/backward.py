@@ -19,8 +19,8 @@ packed input follows ``cu_seqlens`` as in the forward oracle.  The coefficient v
 the forward oracle are covered (``beta_mode``: the gated delta rule's b_t = eta_t, section 2;
 key-norm only b_t = 1/(||k_t||^2 + eps) and the sequence factors 1/t, 1/sqrt(t),
 1/log(t + 1) on the Kaczmarz coefficient, Appendix D and Table 5; t the absolute 1-based
-position, sequence n starting at pos_offset[n] + 1), with one scalar gate per token-head and
-o_t = q_t S_t.
+position, sequence n starting at pos_offset[n] + 1) and the readout divided by ||q_t||
+(section 3.3; 0 for a zero query), with one scalar gate per token-head.
 """
 from __future__ import annotations
 
@@ -55,7 +55,7 @@ def _coef(mode, eta_t, den, pos):
     return b
 
 
-def _sequence(q, k, v, g, eta, eps, S0, mode="kaczmarz", pos0=0):
+def _sequence(q, k, v, g, eta, eps, S0, mode="kaczmarz", pos0=0, normalize_q=False):
     """The tokenwise recurrence over one sequence, all heads at once: (O [T, H, dv], S_T).
     Token t of the sequence is at absolute position pos0 + t + 1."""
     S = S0
@@ -68,19 +68,23 @@ def _sequence(q, k, v, g, eta, eps, S0, mode="kaczmarz", pos0=0):
         St = a[:, None, None] * S                             # forget
         e = v[t] - torch.einsum("hi,hij->hj", kt, St)         # residual
         S = St + b[:, None, None] * kt[:, :, None] * e[:, None, :]   # Kaczmarz write
+        if normalize_q:                                       # readout q_t / ||q_t||
+            qn = (qt * qt).sum(-1).sqrt()
+            nzq = qn > 0
+            qt = qt / torch.where(nzq, qn, torch.ones_like(qn))[:, None]
         outs.append(torch.einsum("hi,hij->hj", qt, S))        # readout
     O = torch.stack(outs) if outs else q.new_zeros((0,) + v.shape[1:])
     return O, S
 
 
 def prefill_backward(q, k, v, g, eta, eps, dO, S0=None, dS_T=None, cu_seqlens=None, n_seq=1,
-                     beta_mode="kaczmarz", pos_offset=None):
+                     beta_mode="kaczmarz", pos_offset=None, normalize_q=False):
     """Gradients of the prefill for the cotangents dO [n_tok, H, dv] and dS_T [n_seq, H, dk, dv].
 
     Inputs as for :func:`oracle.prefill` (q, k [n_tok, H, dk]; v [n_tok, H, dv];
     g, eta [n_tok, H]; S0 [n_seq, H, dk, dv] or None = zeros; dS_T None = zeros);
-    without cu_seqlens the tokens are n_seq sequences of equal length.  beta_mode and
-    pos_offset ([n_seq] or None) select the coefficient variant as in the forward oracle.
+    without cu_seqlens the tokens are n_seq sequences of equal length.  beta_mode,
+    pos_offset ([n_seq] or None) and normalize_q select the variant as in the forward oracle.
     Returns numpy float64 arrays (dq, dk, dv, dg, deta, dS0), shaped like the inputs.
     """
     q, k, v, g, eta, dO = (_t(x) for x in (q, k, v, g, eta, dO))
@@ -102,7 +106,7 @@ def prefill_backward(q, k, v, g, eta, eps, dO, S0=None, dS_T=None, cu_seqlens=No
         s, e = int(cu[n]), int(cu[n + 1])
         pos0 = 0 if pos_offset is None else int(pos_offset[n])
         O, ST = _sequence(q[s:e], k[s:e], v[s:e], g[s:e], eta[s:e], float(eps), S0[n],
-                          beta_mode, pos0)
+                          beta_mode, pos0, normalize_q)
         loss = loss + (O * dO[s:e]).sum() + (ST * dS_T[n]).sum()
     grads = torch.autograd.grad(loss, (q, k, v, g, eta, S0), allow_unused=True)
     out = []

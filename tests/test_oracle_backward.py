@@ -168,3 +168,29 @@ def test_variant_gradients_match_central_differences(mode):
         assert err < 1e-6, (mode, which, err)
     if mode == "key_norm":
         assert np.abs(grads[4]).max() == 0.0  # b does not depend on eta
+
+
+def test_normalised_readout_gradients_match_central_differences():
+    # o_t = q_t S_t / ||q_t|| against central differences of the C oracle's normalised readout
+    q, k, v, g, eta, S0, dO, dST = draw(8, 6, H=2, dk=3, dv=2, n_seq=2)
+    cu = np.array([0, 4, 6])
+    grads = ob.prefill_backward(q, k, v, g, eta, 0.2, dO, S0=S0, dS_T=dST, cu_seqlens=cu,
+                                normalize_q=True)
+
+    def loss(xs):
+        O, ST = oracle.prefill(*xs[:5], 0.2, S0=xs[5], cu_seqlens=cu, normalize_q=True)
+        return float((O * dO).sum() + (ST * dST).sum())
+    inputs = [q, k, v, g, eta, S0]
+    h = 1e-6
+    for which, (x, gx) in enumerate(zip(inputs, grads)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = [a.copy() for a in inputs]
+            xm = [a.copy() for a in inputs]
+            xp[which][idx] += h
+            xm[which][idx] -= h
+            num[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        err = np.abs(num - gx).max() / max(np.abs(num).max(), 1e-300)
+        assert err < 1e-6, (which, err)
+    # the readout depends on q_t only through its direction: q_t . dq_t = 0
+    assert np.abs(np.einsum("thi,thi->th", q, grads[0])).max() < 1e-12 * np.abs(grads[0]).max()
