@@ -69,9 +69,11 @@ def _sequence(q, k, v, g, eta, eps, S0, mode="kaczmarz", pos0=0, normalize_q=Fal
         e = v[t] - torch.einsum("hi,hij->hj", kt, St)         # residual
         S = St + b[:, None, None] * kt[:, :, None] * e[:, None, :]   # Kaczmarz write
         if normalize_q:                                       # readout q_t / ||q_t||
-            qn = (qt * qt).sum(-1).sqrt()
-            nzq = qn > 0
-            qt = qt / torch.where(nzq, qn, torch.ones_like(qn))[:, None]
+            qq = (qt * qt).sum(-1)                            # a zero query reads out 0, with
+            nzq = qq > 0                                      # a zero gradient
+            r = torch.where(nzq, 1.0 / torch.where(nzq, qq, torch.ones_like(qq)).sqrt(),
+                            torch.zeros_like(qq))
+            qt = qt * r[:, None]
         outs.append(torch.einsum("hi,hij->hj", qt, S))        # readout
     O = torch.stack(outs) if outs else q.new_zeros((0,) + v.shape[1:])
     return O, S

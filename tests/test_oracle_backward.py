@@ -194,3 +194,12 @@ def test_normalised_readout_gradients_match_central_differences():
         assert err < 1e-6, (which, err)
     # the readout depends on q_t only through its direction: q_t . dq_t = 0
     assert np.abs(np.einsum("thi,thi->th", q, grads[0])).max() < 1e-12 * np.abs(grads[0]).max()
+
+
+def test_normalised_readout_zero_query():
+    # a zero query reads out 0; its gradient is taken as 0 (the direction is undefined there)
+    q, k, v, g, eta, S0, dO, dST = draw(9, 5, H=1, dk=3, dv=2)
+    q[2] = 0.0
+    dq = ob.prefill_backward(q, k, v, g, eta, 1e-6, dO, S0=S0, dS_T=dST, normalize_q=True)[0]
+    assert np.all(np.isfinite(dq)) and np.abs(dq[2]).max() == 0.0
+    assert np.abs(dq[1]).max() > 0
