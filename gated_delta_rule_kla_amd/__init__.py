@@ -260,11 +260,12 @@ def kla_prefill_backward_workspace_bytes(n_seq: int, total_tokens: int, n_heads:
 
 def kla_prefill_backward(q, k, v, g, eta, eps: float, dO, S0=None, dS_T=None, cu_seqlens=None,
                          n_seq=None, *, cu_seqlens_host=None, workspace=None,
-                         need_dS0=True, beta_mode="kaczmarz", pos_offset=None):
+                         need_dS0=True, beta_mode="kaczmarz", normalize_q=False,
+                         pos_offset=None):
     """Gradients of the prefill for the cotangents dO (like o) and dS_T (like S_T, or None).
 
-    Inputs as for :func:`kla_prefill_chunked`, with a scalar gate and o = q S; beta_mode /
-    pos_offset select the coefficient variant of the forward call.  Returns
+    Inputs as for :func:`kla_prefill_chunked`, with a scalar gate; beta_mode / normalize_q /
+    pos_offset select the variant of the forward call.  Returns
     (dq, dk, dv, dg, deta, dS0), shaped like q, k, v, g, eta and S0 ([n_seq, H, d_k, d_v];
     None when need_dS0 is False).
     """
@@ -310,7 +311,7 @@ def kla_prefill_backward(q, k, v, g, eta, eps: float, dO, S0=None, dS_T=None, cu
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     host_ptr = None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr())
-    opts = _options(beta_mode, False, pos_offset, n_seq, dev)
+    opts = _options(beta_mode, normalize_q, pos_offset, n_seq, dev)
     _check(lib.kla_prefill_backward_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S0), _ptr(dO),
         _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(deta), _ptr(dS0),

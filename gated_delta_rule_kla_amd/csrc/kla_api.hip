@@ -371,10 +371,8 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
   kla::CoefOpts co;
   kla_status st = to_coef(opts, &co);
   if (st != KLA_OK) return st;
-  if (co.normalize_q || co.diag_gate)
-    return fail(KLA_ERR_UNSUPPORTED,
-                "the backward pass takes the coefficient modes only (no normalised readout, "
-                "no diagonal gate)");
+  if (co.diag_gate)
+    return fail(KLA_ERR_UNSUPPORTED, "the backward pass takes no diagonal gate");
   if ((st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
                                 eps)) != KLA_OK)
     return st;

@@ -208,7 +208,7 @@ struct AdjSmem {
   float dU[kChunk][LDB];
   float dR[kChunk][LDB];
   float dS[DK][LDB];
-  float gam[kChunk], dec[kChunk];
+  float gam[kChunk], dec[kChunk], gamO[kChunk];
 };
 
 }  // namespace
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
     rt.load(Tm + ch * (kChunk * kChunk), tid);
     rp.load(Pm + ch * (kChunk * kChunk), tid);
-    if (tid < 2 * kChunk) rgd = GD[ch * kGDFloats + tid];  // gam then dec
+    if (tid < 3 * kChunk) rgd = GD[ch * kGDFloats + tid];  // gam, dec, gamO
   };
   if (nchunks > 0) issue(nchunks - 1);
   for (int c = nchunks - 1; c >= 0; --c) {
@@ -276,6 +276,7 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     rp.store(sm.P, tid);
     if (tid < kChunk) sm.gam[tid] = rgd;
     else if (tid < 2 * kChunk) sm.dec[tid - kChunk] = rgd;
+    else if (tid < 3 * kChunk) sm.gamO[tid - 2 * kChunk] = rgd;
     __syncthreads();
     if (c > 0) issue(c - 1);
 
@@ -333,7 +334,8 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
         }
       }
     }
-    // dS = exp(G_last) dS' + Q^T Diag(gam) dO - K^T Diag(gam) dR: (DK / 16) x 2 tiles
+    // dS = exp(G_last) dS' + Q^T Diag(gamO) dO - K^T Diag(gam) dR: (DK / 16) x 2 tiles
+    //      (gamO = gam, over ||q_i|| under the normalised readout)
     const float gl = sm.gam[kChunk - 1];  // rows past a ragged end repeat G_last
     constexpr int NX = DK / 8 / NW;       // tiles per wavefront
     f32x4 nd[NX];
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
       const int t = wid + NW * x, mi = t >> 1, tj = t & 1;
       f32x4 acc = mmt<Tin, kChunk>(
           zero4(), lane, [&](int i, int kk) { return sm.Q[kk][16 * mi + i]; },
-          [&](int kk, int j) { return sm.gam[kk] * sm.dO[kk][16 * tj + j]; });
+          [&](int kk, int j) { return sm.gamO[kk] * sm.dO[kk][16 * tj + j]; });
       acc = mmt<Tin, kChunk>(
           acc, lane, [&](int i, int kk) { return -sm.K[kk][16 * mi + i]; },
           [&](int kk, int j) { return sm.gam[kk] * sm.dR[kk][16 * tj + j]; });
@@ -391,6 +393,8 @@ struct GradSmem {
   } u;
   float gam[kChunk], dec[kChunk], G[kChunk], b[kChunk], den[kChunk], db[kChunk];
   float db_deta[kChunk];  // the derivative of b in eta
+  float rqn[kChunk];      // 1 / ||q_i|| (normalised readout)
+  float qdot[2][kChunk];  // q^_i . dq^_i, two partial sums
   float rz[kChunk], cz[kChunk];
   float dots[3][2][kChunk];  // row dots of the three d_v contractions, two partial sums each
   float red[kGradThreads / 64];
@@ -599,6 +603,20 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     }
   }
   __syncthreads();
+  // normalised readout: the chunk solve sees q^ = q / ||q|| (0 for a zero query); each
+  // 8-lane group scales its own row in place
+  if (opts.normalize_q) {
+    const int i = tid >> 3, part = tid & 7;
+    float qq = 0.f;
+    for (int cc = part; cc < DK; cc += 8) qq += sm.u.pa.Q[i][cc] * sm.u.pa.Q[i][cc];
+    qq += __shfl_xor(qq, 1, 8);
+    qq += __shfl_xor(qq, 2, 8);
+    qq += __shfl_xor(qq, 4, 8);
+    const float r = qq > 0.f ? 1.f / sqrtf(qq) : 0.f;
+    for (int cc = part; cc < DK; cc += 8) sm.u.pa.Q[i][cc] *= r;
+    if (part == 0) sm.rqn[i] = r;
+    __syncthreads();
+  }
   {
     // P's lower blocks, two jobs per wavefront (10 blocks; zeros above the diagonal blocks)
 #pragma unroll
@@ -736,6 +754,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   __syncthreads();
   // ---- dq = qa + (dP o Gamma) K;  dk = ka + kb + (dP o Gamma)^T Q + (dA o Gamma) K
   //      + (dA o Gamma)^T K - Diag(2 b db / den) K
+  f32x4 aqs[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const int tj = (wid >> 2) + 2 * m;
@@ -761,8 +780,37 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       ak[e] += cb * sm.K[row][col];
       if (row < len) {
         const size_t o = (tok + (size_t)row * H) * DK + col;
-        dq[o] = from_f32<Tin>(aq[e]);
+        if (!opts.normalize_q) dq[o] = from_f32<Tin>(aq[e]);
         dk[o] = from_f32<Tin>(ak[e]);
+      }
+    }
+    aqs[m] = aq;
+  }
+  // normalised readout: dq = (dq^ - (q^ . dq^) q^) / ||q||
+  if (opts.normalize_q) {
+    float pd[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int col = 16 * ((wid >> 2) + 2 * m) + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pd[e] += aqs[m][e] * sm.u.pa.Q[16 * mti + 4 * kq + e][col];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pd[e] = row16_sum(pd[e]);
+      if (r16 == 0) sm.qdot[wid >> 2][16 * mti + 4 * kq + e] = pd[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int col = 16 * ((wid >> 2) + 2 * m) + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * mti + 4 * kq + e;
+        const float d = sm.qdot[0][row] + sm.qdot[1][row];
+        if (row < len)
+          dq[(tok + (size_t)row * H) * DK + col] =
+              from_f32<Tin>(sm.rqn[row] * (aqs[m][e] - d * sm.u.pa.Q[row][col]));
       }
     }
   }

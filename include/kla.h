@@ -263,7 +263,8 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const
  * Backward pass of the chunkwise prefill: the gradients (dq, dk, dv, dg, deta,
  * dS0) of the scalar loss <dO, o> + <dS_T, S_T> for the default variant
  * (Kaczmarz coefficient of Eq. (3), one scalar gate per token-head,
- * o_t = q_t S_t; kla_prefill_backward_ex below adds the coefficient modes).  The paper trains with the chunkwise algorithm (section 4,
+ * o_t = q_t S_t; kla_prefill_backward_ex below adds the coefficient modes and
+ * the normalised readout).  The paper trains with the chunkwise algorithm (section 4,
  * Propositions 3-4, Eq. (7)-(9)) but derives no backward pass; these are the
  * exact derivatives of that chunk solve, so of the tokenwise recurrence
  * (Algorithm 1), up to rounding.
@@ -299,9 +300,10 @@ kla_status kla_prefill_backward(const void *q, const void *k, const void *v, con
                                 void *stream);
 
 /* kla_prefill_backward with options (NULL = the defaults): the coefficient
- * modes (beta_mode, pos_offset) are supported; normalize_q or diagonal_gate
- * give KLA_ERR_UNSUPPORTED.  The forward arguments and options must be those
- * of the forward call whose gradients are wanted. */
+ * modes (beta_mode, pos_offset) and the normalised readout (normalize_q; the
+ * gradient of a zero query is 0) are supported; diagonal_gate gives
+ * KLA_ERR_UNSUPPORTED.  The forward arguments and options must be those of the
+ * forward call whose gradients are wanted. */
 kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, const float *g,
                                    const float *eta, float eps, const float *S0, const void *dO,
                                    const float *dS_T, void *dq, void *dk, void *dv, float *dg,

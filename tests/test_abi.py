@@ -242,8 +242,8 @@ def test_backward_workspace_and_errors(lib):
         assert _bwd_call(lib, **over) == want, (over, lib.kla_last_error())
 
 
-def test_backward_ex_rejects_readout_and_diagonal_variants(lib):
-    for opts in (kla.KlaOptions(0, 1, None, 0), kla.KlaOptions(0, 0, None, 1)):
+def test_backward_ex_rejects_the_diagonal_gate(lib):
+    for opts in (kla.KlaOptions(0, 0, None, 1), kla.KlaOptions(0, 1, None, 1)):
         st = lib.kla_prefill_backward_ex(
             FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1e-6, None, FAKE * 6, None, FAKE * 7,
             FAKE * 8, FAKE * 9, FAKE * 10, FAKE * 11, FAKE * 12, None, None, 2, 256, 4, 128, 128,

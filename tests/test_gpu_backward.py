@@ -204,3 +204,34 @@ def test_backward_coefficient_modes(kla, mode, dtype):
         e = err(x, y)
         print(f"  {name}: err {e:.3e} (bar {TOL[dtype]:g})", flush=True)
         assert e < TOL[dtype], f"{name}: err {e:.3e} >= {TOL[dtype]:g}"
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_normalised_readout(kla, dtype):
+    # o = q S / ||q||, with one query row exactly zero (its output and gradient are 0)
+    inp = ki.prefill_inputs(0, lens=(130, 61), H=2)
+    q = inp["q"].clone()
+    q[7] = 0.0
+    inp["q"] = q.to(dtype).contiguous()
+    inp["k"], inp["v"] = inp["k"].to(dtype).contiguous(), inp["v"].to(dtype).contiguous()
+    inp["dtype"] = dtype
+    gen = torch.Generator().manual_seed(31)
+    inp["S0"] = 0.3 * torch.randn(2, 2, 64, 64, generator=gen)
+    ct = ki.cotangents(inp, seed=32)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    grads = kla.kla_prefill_backward(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                     ct["dO"].to(DEV), S0=d["S0"], dS_T=ct["dS_T"].to(DEV),
+                                     cu_seqlens=d["cu_seqlens"], n_seq=d["n_seq"],
+                                     normalize_q=True)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.double().numpy()
+    ref = ob.prefill_backward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["g"]),
+                              f64(inp["eta"]), inp["eps"], f64(ct["dO"]), S0=f64(inp["S0"]),
+                              dS_T=f64(ct["dS_T"]), cu_seqlens=inp["cu_seqlens"].numpy(),
+                              normalize_q=True)
+    print(f"normalised readout {dtype}", flush=True)
+    for name, x, y in zip(NAMES, grads, ref):
+        e = err(x, y)
+        print(f"  {name}: err {e:.3e} (bar {TOL[dtype]:g})", flush=True)
+        assert e < TOL[dtype], f"{name}: err {e:.3e} >= {TOL[dtype]:g}"
+    assert torch.count_nonzero(grads[0][7]) == 0
