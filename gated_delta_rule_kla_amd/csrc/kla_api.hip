@@ -164,9 +164,10 @@ size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32
 
 namespace {
 
-// Backward workspace: the forward layout, then per chunk-head the incoming states S and the
-// cotangents dS' of the outgoing ones ([d_k][d_v] fp32 each), dU and dR ([64][d_v] fp32
-// each), and the forward output the scan writes again ([tokens][H][d_v], operand type).
+// Backward workspace: the forward layout, then per chunk-head the incoming states S (operand
+// type; sized for fp32) and the cotangents dS' of the outgoing ones ([d_k][d_v] fp32), dU and
+// dR ([64][d_v] fp32 each), and the forward output the scan writes again ([tokens][H][d_v],
+// operand type).
 struct BwdLayout {
   WsLayout fw;
   size_t off_SN, off_dSo, off_dU, off_dR, off_O, total;
@@ -425,7 +426,7 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
     return st;
   const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
   char *ws = static_cast<char *>(workspace);
-  float *SN = reinterpret_cast<float *>(ws + bl.off_SN);
+  void *SN = ws + bl.off_SN;  // incoming states in the operand type
   if ((st = hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0,
                                         ws + bl.off_O, nullptr, wv.tabs, n_seq, n_heads, s,
                                         nullptr, SN),

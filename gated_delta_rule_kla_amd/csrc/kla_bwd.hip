@@ -406,7 +406,7 @@ template <typename Tin, int DK>
 __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ dO, const float *__restrict__ g, const float *__restrict__ eta,
-    float eps, CoefOpts opts, const float *__restrict__ SN, const float *__restrict__ dSo,
+    float eps, CoefOpts opts, const Tin *__restrict__ SN, const float *__restrict__ dSo,
     const float *__restrict__ dUo, const float *__restrict__ dRo, Tin *__restrict__ dq,
     Tin *__restrict__ dk, float *__restrict__ dg, float *__restrict__ deta,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq, int H,
@@ -498,10 +498,12 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 #pragma unroll
   for (int x = 0; x < 3; ++x) pt[x] = zero4();
   float sc = 0.f;
-  const float *Sb = SN + ch * DK * (size_t)DV, *Sob = dSo + ch * DK * (size_t)DV;
+  const Tin *Sb = SN + ch * DK * (size_t)DV;
+  const float *Sob = dSo + ch * DK * (size_t)DV;
   const float *dUb = dUo + ch * kChunk * (size_t)DV, *dRb = dRo + ch * kChunk * (size_t)DV;
   // each 32-column block is loaded into registers while the one before it is computed
-  RegTile<float, DK, kAdjBV, kGradThreads> rs, rso;
+  RegTile<Tin, DK, kAdjBV, kGradThreads> rs;
+  RegTile<float, DK, kAdjBV, kGradThreads> rso;
   RegTile<Tin, kChunk, kAdjBV, kGradThreads> rv, rdo;
   RegTile<float, kChunk, kAdjBV, kGradThreads> rdu, rdr;
   auto issue = [&](int v0) {
@@ -518,9 +520,10 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     rs.template store<LDB>(&sm.u.lp.S[0][0], tid);
     rso.template store<LDB>(&sm.u.lp.So[0][0], tid);
 #pragma unroll
-    for (int j = 0; j < rs.J; ++j)
-      sc += rs.x[j][0] * rso.x[j][0] + rs.x[j][1] * rso.x[j][1] + rs.x[j][2] * rso.x[j][2] +
-            rs.x[j][3] * rso.x[j][3];
+    for (int j = 0; j < rs.J; ++j) {
+      const f32x4 sv = cvt4(rs.x[j]);
+      sc += sv[0] * rso.x[j][0] + sv[1] * rso.x[j][1] + sv[2] * rso.x[j][2] + sv[3] * rso.x[j][3];
+    }
     rv.template store<LDB>(&sm.u.lp.R[0][0], tid);
     rdo.template store<LDB>(&sm.u.lp.dO[0][0], tid);
     rdu.template store<LDB>(&sm.u.lp.dU[0][0], tid);
@@ -841,7 +844,7 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
                                const void *dO, const float *g, const float *eta, float eps,
                                const CoefOpts &opts, const float *GD, const void *T,
                                const void *P, const float *dST,
-                               const float *SN, float *dSo, float *dU, float *dR, void *dq,
+                               const void *SN, float *dSo, float *dU, float *dR, void *dq,
                                void *dk, void *dv, float *dg, float *deta, float *dS0,
                                SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                                hipStream_t stream) {
@@ -869,7 +872,8 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
   if (grad_blocks > 0)
     hipLaunchKernelGGL((kla_bwd_grad_kernel<Tin, DK>), dim3((unsigned)grad_blocks),
                        dim3(kGradThreads), smG, stream, qt, kt, static_cast<const Tin *>(v),
-                       static_cast<const Tin *>(dO), g, eta, eps, opts, SN, dSo, dU, dR,
+                       static_cast<const Tin *>(dO), g, eta, eps, opts,
+                       static_cast<const Tin *>(SN), dSo, dU, dR,
                        static_cast<Tin *>(dq), static_cast<Tin *>(dk), dg, deta, t.cu,
                        t.chunk_off, n_seq, H, d_v);
   return hipGetLastError();
@@ -878,7 +882,7 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
                       const CoefOpts &opts, const float *GD, const void *T, const void *P, const float *dST,
-                      const float *SN, float *dSo, float *dU, float *dR, void *dq, void *dk,
+                      const void *SN, float *dSo, float *dU, float *dR, void *dq, void *dk,
                       void *dv, float *dg, float *deta, float *dS0, SeqTables t, int32_t n_seq,
                       int64_t n_chunks_ub, int32_t H, hipStream_t stream) {
 #define KLA_BWD(TIN, DK_)                                                                     \

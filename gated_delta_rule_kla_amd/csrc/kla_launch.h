@@ -77,11 +77,12 @@ hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, c
 // decays GD that launch_prep wrote.  With diag (non-null), the diagonal-gated scan: K and Q
 // come from the decayed tiles, the state update uses K o exp(G_last - G) and the state decays
 // by exp(G_last) per key channel.  With SN (non-null; scalar gate only), also every chunk's
-// incoming state, [chunk][H][d_k][d_v] fp32 by global chunk number, for the backward pass.
+// incoming state, [chunk][H][d_k][d_v] in the operand type by global chunk number, for the
+// backward pass.
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                        const float *GD, const void *T, const void *P, const float *S0, void *o,
                        float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream,
-                       const DiagTiles *diag = nullptr, float *SN = nullptr);
+                       const DiagTiles *diag = nullptr, void *SN = nullptr);
 
 // The backward pass after launch_prep (with the same opts) and launch_scan with SN: the adjoint scan (dS' per
 // chunk into dSo, dU and dR into their [chunk][H][64][d_v] fp32 buffers, dv, and dS0 if
@@ -90,7 +91,7 @@ hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k,
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
                       const CoefOpts &opts, const float *GD, const void *T, const void *P, const float *dST,
-                      const float *SN, float *dSo, float *dU, float *dR, void *dq, void *dk,
+                      const void *SN, float *dSo, float *dU, float *dR, void *dq, void *dk,
                       void *dv, float *dg, float *deta, float *dS0, SeqTables t, int32_t n_seq,
                       int64_t n_chunks_ub, int32_t H, hipStream_t stream);
 

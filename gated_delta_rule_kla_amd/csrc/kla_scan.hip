@@ -187,7 +187,7 @@ void kla_scan_kernel(
     const float *S0, Tin *__restrict__ o, float *S_T, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int n_seq, int H, int DV, const Tin *__restrict__ KG,
     const Tin *__restrict__ QG, const Tin *__restrict__ KD, const float *__restrict__ GC,
-    float *__restrict__ SN) {
+    Tin *__restrict__ SN) {
   constexpr int kBV = SHP::BV, kConsumers = SHP::NC, kScanThreads = SHP::THREADS;
   using SM = ScanSmem<Tin, DK, kBV, DIAG>;
   using SL = ScanSlot<Tin, DK, kBV, DIAG>;
@@ -380,12 +380,13 @@ void kla_scan_kernel(
   // One chunk.  All LDS operands of a phase are read into registers before the phase's
   // MFMAs, and the next phase's reads are issued while those MFMAs run.
   auto c_step = [&](int c, const SL &s) {
-    if constexpr (STATES) {  // the chunk's incoming state, for the backward pass
-      float *dst = SN + ((size_t)(cbase + c) * H + h) * DK * (size_t)DV + v0 + col;
+    if constexpr (STATES) {  // the chunk's incoming state in the operand type, for the
+                             // backward pass (whose products read it in that precision)
+      Tin *dst = SN + ((size_t)(cbase + c) * H + h) * DK * (size_t)DV + v0 + col;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(size_t)tmap(m, kg, i) * DV] = Sacc[m][i];
+        for (int i = 0; i < 4; ++i) dst[(size_t)tmap(m, kg, i) * DV] = from_f32<Tin>(Sacc[m][i]);
     }
     FragT Sop[NKS];
 #pragma unroll
@@ -610,7 +611,7 @@ template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES>
 static hipError_t launch_scan_s(int d_v, const void *q, const void *k, const void *v,
                                 const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream, const DiagTiles *dg, float *SN) {
+                                hipStream_t stream, const DiagTiles *dg, void *SN) {
   using SMT = ScanSmem<Tin, DK, SHP::BV, DIAG>;
   using SLT = ScanSlot<Tin, DK, SHP::BV, DIAG>;
   static_assert(sizeof(SMT) <= kLdsBytes, "LDS budget");
@@ -635,7 +636,8 @@ static hipError_t launch_scan_s(int d_v, const void *q, const void *k, const voi
                      static_cast<Tin *>(o), S_T, t.cu, t.chunk_off, n_seq, H, d_v,
                      static_cast<const Tin *>(dg ? dg->kg : nullptr),
                      static_cast<const Tin *>(dg ? dg->qg : nullptr),
-                     static_cast<const Tin *>(dg ? dg->kd : nullptr), dg ? dg->gc : nullptr, SN);
+                     static_cast<const Tin *>(dg ? dg->kd : nullptr), dg ? dg->gc : nullptr,
+                     static_cast<Tin *>(SN));
   return hipGetLastError();
 }
 
@@ -660,7 +662,7 @@ template <typename Tin, int DK, bool DIAG, bool STATES>
 static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const void *v,
                                 const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream, const DiagTiles *dg, float *SN) {
+                                hipStream_t stream, const DiagTiles *dg, void *SN) {
   const int64_t narrow_blocks = (int64_t)n_seq * H * (d_v / ScanNarrow::BV);
   const int cus = device_cus();
   if (cus > 0 && narrow_blocks > cus)
@@ -674,7 +676,7 @@ template <typename Tin, int DK>
 static hipError_t launch_scan_g(int d_v, const void *q, const void *k, const void *v,
                                 const float *GD, const void *T, const void *P, const float *S0,
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream, const DiagTiles *dg, float *SN) {
+                                hipStream_t stream, const DiagTiles *dg, void *SN) {
   if (dg) {
     if (SN) return hipErrorInvalidValue;  // no stored states under diagonal gating
     return launch_scan_t<Tin, DK, true, false>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
@@ -690,7 +692,7 @@ static hipError_t launch_scan_g(int d_v, const void *q, const void *k, const voi
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                        const float *GD, const void *T, const void *P, const float *S0, void *o,
                        float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream,
-                       const DiagTiles *dg, float *SN) {
+                       const DiagTiles *dg, void *SN) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
       return launch_scan_g<__bf16, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream,
