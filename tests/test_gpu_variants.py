@@ -195,3 +195,40 @@ def test_prefill_diagonal_equal_channels_match_scalar_gate(kla):
     o2, S2 = run_prefill_diag(kla, dd)
     check(o2, o1.double().cpu().numpy(), 1e-5, "o")
     check(S2, S1.double().cpu().numpy(), 1e-5, "S_T")
+
+
+# ------------------------------------------------------------- variants at the full layer size
+@pytest.mark.parametrize("variant", ["diagonal_gate", "gated_unit_keys", "normalised_inv_sqrt_t"])
+def test_variants_full_workload_sampled(kla, variant):
+    """The prefill workload at full size (4 sequences x 4096 tokens x 16 heads, d = 128, bf16,
+    random S0) in the bench launch configuration, once per variant: the diagonal gate (g per
+    key channel), the gated delta rule on unit-norm keys, and the readout divided by ||q_t||
+    with the 1/sqrt(t) coefficient and position offsets.  The oracle checks two sampled
+    (sequence, head) pairs, every token and the final state of each."""
+    d = ki.prefill_inputs(1, diag=(variant == "diagonal_gate"))
+    kw = {}
+    if variant == "gated_unit_keys":
+        d = unit_keys(d)
+        kw = dict(beta_mode="gated")
+    elif variant == "normalised_inv_sqrt_t":
+        kw = dict(beta_mode="inv_sqrt_t", normalize_q=True)
+    pos = torch.tensor([0, 4096, 100000, 7], dtype=torch.int32)
+    if kw:
+        kw["pos_offset"] = pos
+    dev = to_dev(d)
+    print(f"full-size variant {variant}", flush=True)
+    o, ST = run_prefill_diag(kla, dev, **{key: (val.cuda() if isinstance(val, torch.Tensor)
+                                                else val) for key, val in kw.items()})
+    T = d["q"].shape[0] // d["n_seq"]
+    for n, h in ((1, 3), (3, 15)):
+        sl = slice(n * T, (n + 1) * T)
+        pk = lambda t: t[sl, h:h + 1]
+        okw = dict(kw)
+        if "pos_offset" in okw:
+            okw["pos_offset"] = pos[n:n + 1].numpy()
+        oo, So = oracle.prefill(pk(d["q"]), pk(d["k"]), pk(d["v"]), pk(d["g"]), pk(d["eta"]),
+                                d["eps"], S0=d["S0"][n:n + 1, h:h + 1],
+                                cu_seqlens=np.array([0, T]), **okw)
+        print(f"sequence {n}, head {h}", flush=True)
+        check(o[sl, h:h + 1], oo, TOL[torch.bfloat16], "o")
+        check(ST[n:n + 1, h:h + 1], So, TOL[torch.bfloat16], "S_T")
