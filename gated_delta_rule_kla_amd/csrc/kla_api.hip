@@ -165,7 +165,7 @@ size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32
 namespace {
 
 // Backward workspace: the forward layout, then per chunk-head the incoming states S (operand
-// type; sized for fp32) and the cotangents dS' of the outgoing ones ([d_k][d_v] fp32), dU and
+// type) and the cotangents dS' of the outgoing ones ([d_k][d_v] fp32), dU and
 // dR ([64][d_v] fp32 each), and the forward output the scan writes again ([tokens][H][d_v],
 // operand type).
 struct BwdLayout {
@@ -181,7 +181,7 @@ BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k
   const size_t st = sizeof(float) * nch * (size_t)H * (size_t)d_k * (size_t)d_v;
   const size_t ut = sizeof(float) * nch * (size_t)H * KLA_CHUNK * (size_t)d_v;
   b.off_SN = b.fw.total;
-  b.off_dSo = align256(b.off_SN + st);
+  b.off_dSo = align256(b.off_SN + es * nch * (size_t)H * (size_t)d_k * (size_t)d_v);
   b.off_dU = align256(b.off_dSo + st);
   b.off_dR = align256(b.off_dU + ut);
   b.off_O = align256(b.off_dR + ut);
