@@ -235,3 +235,33 @@ def test_backward_normalised_readout(kla, dtype):
         print(f"  {name}: err {e:.3e} (bar {TOL[dtype]:g})", flush=True)
         assert e < TOL[dtype], f"{name}: err {e:.3e} >= {TOL[dtype]:g}"
     assert torch.count_nonzero(grads[0][7]) == 0
+
+
+def test_backward_variant_full_workload_sampled(kla):
+    # the 1/sqrt(t) coefficient with position offsets and the readout divided by ||q_t||, on
+    # the full prefill workload; one sampled (sequence, head) pair against the oracle
+    inp = ki.prefill_inputs(1)
+    ct = ki.cotangents(inp, seed=2025)
+    pos = torch.tensor([0, 4096, 100000, 7], dtype=torch.int32)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    grads = kla.kla_prefill_backward(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                     ct["dO"].to(DEV), S0=d["S0"], dS_T=ct["dS_T"].to(DEV),
+                                     n_seq=d["n_seq"], beta_mode="inv_sqrt_t", normalize_q=True,
+                                     pos_offset=pos.to(DEV))
+    torch.cuda.synchronize()
+    T = inp["q"].shape[0] // inp["n_seq"]
+    f64 = lambda t: t.double().numpy()
+    n, h = 2, 9
+    sl = slice(n * T, (n + 1) * T)
+    pick = lambda t: f64(t[sl, h:h + 1])
+    ref = ob.prefill_backward(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), pick(inp["g"]),
+                              pick(inp["eta"]), inp["eps"], pick(ct["dO"]),
+                              S0=f64(inp["S0"][n:n + 1, h:h + 1]),
+                              dS_T=f64(ct["dS_T"][n:n + 1, h:h + 1]), beta_mode="inv_sqrt_t",
+                              pos_offset=pos[n:n + 1].numpy(), normalize_q=True)
+    got = [x[sl, h:h + 1] for x in grads[:5]] + [grads[5][n:n + 1, h:h + 1]]
+    print(f"sequence {n}, head {h}", flush=True)
+    for name, x, y in zip(NAMES, got, ref):
+        e = err(x, y)
+        print(f"  {name}: err {e:.3e} (bar {TOL[torch.bfloat16]:g})", flush=True)
+        assert e < TOL[torch.bfloat16], f"{name}: err {e:.3e}"
