@@ -17,14 +17,17 @@ Per-kernel durations come from HIP events recorded on the launch stream inside t
 timed loop: the prefill is issued as its two halves (kla_prefill_prepare, then
 kla_prefill_scan), which is exactly what kla_prefill_chunked enqueues.
 
-Algorithmic work (per token-head, C = 64, d = d_k = d_v):
-  scan kernel bytes  = 2 d_k e (q, k) + d_v e (v) + d_v e (o)
-                       + 2 x 40 e (T and P: the ten 16 x 16 blocks on and below the diagonal
-                         of each 64 x 64 matrix, 2560 entries per 64 tokens)
-                       + 12 (three fp32 decay factors)
-                       + 8 d_k d_v per (sequence, head) for S0 in / S_T out,  e = 2 (bf16)
+Algorithmic work (per token-head, C = 64; the survey's minimum for the chunkwise method):
+  prefill bytes      = 2 (2 d_k + d_v) e + 8 + 2 d_v e        (q, k, v, g, eta read; o written)
+                       + 8 d_k d_v per (sequence, head)        (S0 read, S_T written), e = 2 (bf16)
+                     = 1064 B per token-head on the layer workload (d = 128, T = 4096)
   prefill MFMA flops = 6 d_k d_v + (C-1) d_k + (C+1)(2 d_k + 2 d_v)
   decode bytes       = 8 d_k d_v + 2 (2 d_k + d_v) + 2 d_v + 8
+The roofline object is for the dominant kernel (the chunk scan): the prefill's algorithmic
+bytes per launch over the scan's mean event-timed duration.  ``step`` gives the same bytes
+and flops over the whole step (prep + scan).  The long-context (T = 65536) and packed
+wide-head workloads are timed the same way on one input set each (their inputs exceed the
+256 MB last-level cache), the packed one followed by 128 decode steps from its state.
 """
 from __future__ import annotations
 
@@ -43,6 +46,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
 CHUNK = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_prefill_B4_H16_T4096_d128.txt")
+TRAFFIC_NOTE = ("rocprofv3 read-request and WRITE_SIZE counters of this scan kernel build, "
+                "committed under profiles/ (not measured in this run)")
 
 
 def log(msg):
@@ -91,6 +96,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant-steps", type=int, default=10,
                     help="steps timed for each coefficient / readout variant (0 = skip)")
+    ap.add_argument("--workload-steps", type=int, default=5,
+                    help="timed calls of the long-context and packed workloads (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finally copy this many MiB device to device once: a kernel of known "
                          "traffic for scaling hardware byte counters")
@@ -109,69 +116,125 @@ def main():
     kla.load_library()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    def prefill_bytes_flops(n_tok, n_seq, H, dk, dv, es):
+        """The survey's algorithmic bytes and MFMA flops of one prefill call."""
+        th = n_tok * H
+        nb = th * (es * (2 * dk + dv) + 8 + es * dv) + 2 * n_seq * H * dk * dv * 4
+        nf = th * (6 * dk * dv + (CHUNK - 1) * dk + (CHUNK + 1) * (2 * dk + 2 * dv))
+        return nb, nf
+
+    def time_prefill(sets, meta, steps, warmup):
+        """Time `steps` prefill calls (prepare then scan, what kla_prefill_chunked enqueues)
+        rotating over `sets`: one event pair around the back-to-back calls, then a second
+        pass with events between the two halves for the per-kernel split."""
+        n_seq, dv, eps = meta["n_seq"], meta["d_v"], meta["eps"]
+
+        def step(s, ev_mid=None):
+            kla.kla_prefill_prepare(s["q"], s["k"], s["g"], s["eta"], eps, s["ws"], n_seq=n_seq,
+                                    d_v=dv, cu_seqlens=s.get("cu"))
+            if ev_mid is not None:
+                ev_mid.record()
+            kla.kla_prefill_scan(s["q"], s["k"], s["v"], s["ws"], n_seq=n_seq, S0=s.get("S0"),
+                                 o=s["o"], S_T=s["S_T"])
+        for i in range(warmup):
+            step(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_start.record()
+        for i in range(steps):
+            step(sets[i % len(sets)])
+        e_end.record()
+        torch.cuda.synchronize()
+        ms = e_start.elapsed_time(e_end) / steps
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            step(sets[i % len(sets)], ev[i][1])
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+        scan = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+        return ms, prep, scan
+
+    def make_set(inp, dev, ws_bytes, dtype):
+        n_tok, H, dk = inp["q"].shape
+        dv = inp["v"].shape[-1]
+        return dict(q=inp["q"], k=inp["k"], v=inp["v"], g=inp["g"], eta=inp["eta"],
+                    S0=inp["S0"], cu=inp["cu_seqlens"],
+                    o=torch.empty(n_tok, H, dv, dtype=dtype, device=dev),
+                    S_T=torch.empty(inp["n_seq"], H, dk, dv, dtype=torch.float32, device=dev),
+                    ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev))
+
+    def workload_leg(widx, steps, warmup):
+        """One of the long-context or packed workloads: timing and roofline fractions."""
+        wl = ki.WORKLOADS[widx]
+        inp = ki.prefill_inputs(wl, device=dev)
+        n_tok, H_, dk_, dv_ = inp["q"].shape[0], wl.H, wl.d_k, wl.d_v
+        es = inp["q"].element_size()
+        s = make_set(inp, dev, kla.kla_prefill_workspace_bytes(inp["n_seq"], n_tok, H_, dk_, dv_,
+                                                               wl.dtype), wl.dtype)
+        meta = {"n_seq": inp["n_seq"], "d_v": dv_, "eps": inp["eps"]}
+        ms, prep, scan = time_prefill([s], meta, steps, warmup)
+        nb, nf = prefill_bytes_flops(n_tok, inp["n_seq"], H_, dk_, dv_, es)
+        out = {"workload": wl.name, "tokens": n_tok, "ms_per_call": ms, "prep_ms": prep,
+               "scan_ms": scan, "tokens_per_s": n_tok / (ms * 1e-3),
+               "mfma_frac": nf / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+               "hbm_frac": nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               "scan_hbm_frac": nb / (scan * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               "algorithmic_bytes": nb, "algorithmic_flops": nf, "steps": steps}
+        if wl.decode_steps:
+            nd = wl.decode_steps
+            dd = ki.decode_inputs(wl, steps=nd, device=dev, S=s["S_T"])
+            S = s["S_T"].clone()
+            od = torch.empty(inp["n_seq"], H_, dv_, dtype=wl.dtype, device=dev)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(nd):
+                kla.kla_decode_step(dd["q"][i], dd["k"][i], dd["v"][i], dd["g"][i], dd["eta"][i],
+                                    dd["eps"], S, o=od, inplace=True)
+            e1.record()
+            torch.cuda.synchronize()
+            dms = e0.elapsed_time(e1) / nd
+            dbytes = inp["n_seq"] * H_ * (8 * dk_ * dv_ + es * (2 * dk_ + dv_) + es * dv_ + 8)
+            out["decode"] = {"steps": nd, "ms_per_step": dms,
+                             "tokens_per_s": inp["n_seq"] / (dms * 1e-3),
+                             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "note": "state of 16.8 MB stays in the last-level cache"}
+            del dd, S
+        log(f"{wl.name}: {ms:.3f} ms/call (prep {prep:.3f}, scan {scan:.3f}), "
+            f"{n_tok / (ms * 1e-3):.3e} tok/s")
+        del inp, s
+        return out
+
     w = ki.WORKLOADS[1]
     log(f"prefill workload {w.name}: generating inputs")
     base = ki.prefill_inputs(w, device=dev)
     n_seq, H, dk, dv = base["n_seq"], w.H, w.d_k, w.d_v
     n_tok = base["q"].shape[0]
-    ws_bytes = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv)
+    ws_bytes = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, w.dtype)
     sets = []
     for _ in range(4):
-        sets.append(dict(q=base["q"].clone(), k=base["k"].clone(), v=base["v"].clone(),
-                         g=base["g"].clone(), eta=base["eta"].clone(), S0=base["S0"].clone(),
-                         o=torch.empty(n_tok, H, dv, dtype=w.dtype, device=dev),
-                         S_T=torch.empty(n_seq, H, dk, dv, dtype=torch.float32, device=dev),
-                         ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
-
-    def step(s, ev_mid=None):
-        kla.kla_prefill_prepare(s["q"], s["k"], s["g"], s["eta"], base["eps"], s["ws"], n_seq=n_seq, d_v=dv)
-        if ev_mid is not None:
-            ev_mid.record()
-        kla.kla_prefill_scan(s["q"], s["k"], s["v"], s["ws"], n_seq=n_seq, S0=s["S0"], o=s["o"],
-                             S_T=s["S_T"])
-
-    for i in range(args.warmup):
-        step(sets[i % 4])
-    torch.cuda.synchronize()
+        cp = {key: (val.clone() if isinstance(val, torch.Tensor) else val)
+              for key, val in base.items()}
+        sets.append(make_set(cp, dev, ws_bytes, w.dtype))
     K = args.steps
-    # the timed region: K back-to-back steps between one pair of events
     log(f"timing {K} prefill steps")
-    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e_start.record()
-    for i in range(K):
-        step(sets[i % 4])
-    e_end.record()
-    torch.cuda.synchronize()
+    ms_per_step, prep_ms, scan_ms = time_prefill(sets, {"n_seq": n_seq, "d_v": dv,
+                                                        "eps": base["eps"]}, K, args.warmup)
     wall = time.perf_counter() - t0
-    total_ms = e_start.elapsed_time(e_end)
-    ms_per_step = total_ms / K
-    # a second pass with events around each kernel, for the prep / scan split and the scan's
-    # launch duration (the extra event records make it slightly slower than the pass above)
-    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        ev_start[i].record()
-        step(sets[i % 4], ev_mid[i])
-        ev_end[i].record()
-    torch.cuda.synchronize()
-    prep_ms = sum(ev_start[i].elapsed_time(ev_mid[i]) for i in range(K)) / K
-    scan_ms = sum(ev_mid[i].elapsed_time(ev_end[i]) for i in range(K)) / K
     tok_per_s = n_tok / (ms_per_step * 1e-3)
-    th = n_tok * H
-    # per token-head: q, k, v rows, o row, one row each of T and P, three decay factors
-    tp_per_token = 10 * 256 // CHUNK  # lower 16 x 16 blocks of T (and of P) per token
-    scan_bytes = (th * (2 * dk * 2 + dv * 2 + dv * 2 + 2 * tp_per_token * 2 + 12)
-                  + 2 * n_seq * H * dk * dv * 4)
-    scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
-    flops_prefill = th * (6 * dk * dv + (CHUNK - 1) * dk + (CHUNK + 1) * (2 * dk + 2 * dv))
+    prefill_bytes, flops_prefill = prefill_bytes_flops(n_tok, n_seq, H, dk, dv, 2)
+    scan_gbs = prefill_bytes / (scan_ms * 1e-3) / 1e9
+    step_gbs = prefill_bytes / (ms_per_step * 1e-3) / 1e9
     mfma_frac = flops_prefill / (ms_per_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
-    prefill_bytes_min = th * (2 * (2 * dk + dv) + 8 + 2 * dv) + 2 * n_seq * H * dk * dv * 4
     log(f"prefill {ms_per_step:.3f} ms/step (prep {prep_ms:.3f}, scan {scan_ms:.3f}); "
         f"{tok_per_s:.3e} tok/s; wall {wall:.2f}s")
+    others = {}
+    if args.workload_steps > 0:
+        for widx, key in ((2, "long_context"), (4, "packed")):
+            others[key] = workload_leg(widx, args.workload_steps, 1)
 
     # ---------------------------------------------------------------- coefficient / readout
     # variants on the same kernels: the gated delta rule's b = eta against the Kaczmarz
@@ -362,12 +425,13 @@ def main():
                    "d_k": dk, "d_v": dv, "chunk": CHUNK, "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "kla_scan_kernel", "bound": "hbm", "achieved": scan_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": scan_gbs / PEAK_HBM_GBS,
-                     "traffic": traffic, "avg_launch_ms": scan_ms,
-                     "algorithmic_bytes_per_launch": scan_bytes},
-        "prefill": {"mfma_frac": mfma_frac, "algorithmic_flops_per_step": flops_prefill,
-                    "hbm_frac_at_min_bytes": prefill_bytes_min / (ms_per_step * 1e-3) / 1e9
-                    / PEAK_HBM_GBS,
-                    "prep_ms": prep_ms, "scan_ms": scan_ms},
+                     "traffic": traffic, "traffic_source": TRAFFIC_NOTE if traffic else None,
+                     "avg_launch_ms": scan_ms, "algorithmic_bytes_per_launch": prefill_bytes},
+        "step": {"hbm_frac": step_gbs / PEAK_HBM_GBS, "mfma_frac": mfma_frac,
+                 "algorithmic_bytes": prefill_bytes, "algorithmic_flops": flops_prefill,
+                 "note": "prep + scan, the same algorithmic bytes and flops over the step time"},
+        "prefill": {"mfma_frac": mfma_frac, "prep_ms": prep_ms, "scan_ms": scan_ms},
+        "workloads": others,
         "decode": {"workload": wd.name, "tokens_per_s": wd.n_seq / (dec_ms * 1e-3),
                    "ms_per_step": dec_ms, "steps": nd,
                    "roofline": {"kernel": "kla_decode_kernel", "bound": "hbm",

@@ -59,7 +59,7 @@ def load_library():
             "python gated_delta_rule_kla_amd/build.py)")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
-    lib.kla_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.kla_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     lib.kla_prefill_workspace_bytes.restype = sz
     lib.kla_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i32, i32,
                                         i32, i32, ctypes.c_int, vp, sz, vp]
@@ -77,7 +77,7 @@ def load_library():
                                     ctypes.c_int, vp]
     lib.kla_decode_step.restype = ctypes.c_int
     opt_p = ctypes.POINTER(KlaOptions)
-    lib.kla_prefill_workspace_bytes_ex.argtypes = [i32, i32, i32, i32, i32, opt_p]
+    lib.kla_prefill_workspace_bytes_ex.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, opt_p]
     lib.kla_prefill_workspace_bytes_ex.restype = sz
     lib.kla_prefill_chunked_ex.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i32,
                                            i32, i32, i32, ctypes.c_int, vp, sz, opt_p, vp]
@@ -163,12 +163,12 @@ def _need(t, name, dtype=None, device=None):
 
 
 def kla_prefill_workspace_bytes(n_seq: int, total_tokens: int, n_heads: int, d_k: int,
-                                d_v: int, diagonal_gate: bool = False) -> int:
-    """Workspace bytes a prefill of this size needs (0 for unsupported sizes); diagonal_gate
-    sizes it for the diagonal-gated variant."""
+                                d_v: int, dtype=torch.bfloat16, diagonal_gate: bool = False) -> int:
+    """Workspace bytes a prefill of this size and element type needs (0 for unsupported
+    sizes); diagonal_gate sizes it for the diagonal-gated variant."""
     opts = ctypes.pointer(KlaOptions(0, 0, None, 1)) if diagonal_gate else None
     return int(load_library().kla_prefill_workspace_bytes_ex(n_seq, total_tokens, n_heads, d_k,
-                                                             d_v, opts))
+                                                             d_v, _DTYPES[dtype], opts))
 
 
 def _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq):
@@ -240,7 +240,8 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
         _need(S_T, "S_T", torch.float32, dev)
     lib = load_library()
     opts = _options(beta_mode, normalize_q, pos_offset, n_seq, dev, diagonal_gate=diag)
-    ws_bytes = int(lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, d_k, d_v, opts))
+    ws_bytes = int(lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, d_k, d_v, _DTYPES[dt],
+                                                      opts))
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     host_ptr = None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr())
@@ -437,7 +438,7 @@ def kla_prefill_chunk_stage(k, v, g, eta, eps: float = 1e-6, cu_seqlens=None, n_
     T = torch.zeros((max(n_chunks, 1), H, CHUNK, CHUNK), dtype=torch.float32, device=dev)
     W = torch.zeros((n_tok, H, d_k), dtype=torch.float32, device=dev) if want_wy else None
     Ut = torch.zeros((n_tok, H, d_v), dtype=torch.float32, device=dev) if want_wy else None
-    ws_bytes = int(lib.kla_prefill_workspace_bytes(n_seq, n_tok, H, d_k, d_v))
+    ws_bytes = int(lib.kla_prefill_workspace_bytes(n_seq, n_tok, H, d_k, d_v, _DTYPES[dt]))
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     # chunk indices written by the kernel are below the true chunk count, which sizes T
     _check(lib.kla_prefill_chunk_stage(

@@ -44,10 +44,11 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Workspace layout: [cu: n_seq+1 int32][chunk_off: n_seq+1 int32][G: total*H fp32]
-//                   [GD: n_chunks_ub * H * 192 fp32][T: n_chunks_ub * H * 64 * 64][P: same],
-// each part 256-byte aligned and T, P sized for fp32 (the scan reads them in the operand
-// type).
+// Workspace layout, each part 256-byte aligned:
+//   [cu: n_seq+1 int32][chunk_off: n_seq+1 int32][G: total*H fp32]
+//   [GD: n_chunks_ub * H * 192 fp32][T: n_chunks_ub * H * 10 * 256][P: same]
+// T and P are stored by the prep kernel as their ten 16 x 16 blocks on and below the
+// diagonal, in the operand type (es bytes per element).
 struct WsLayout {
   size_t off_cu, off_co, off_G, off_GD, off_T, off_P;
   // diagonal gating only: per chunk-head the decayed key and query tiles K o exp(G),
@@ -56,7 +57,7 @@ struct WsLayout {
   size_t total;
 };
 
-WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k = 0,
+WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, size_t es,
                    bool diag = false) {
   WsLayout w;
   w.off_cu = 0;
@@ -65,11 +66,11 @@ WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k =
   const int64_t nch = kla::chunk_upper_bound(n_seq, total_tokens);
   w.off_GD = align256(w.off_G + sizeof(float) * (size_t)total_tokens * (size_t)H);
   w.off_T = align256(w.off_GD + sizeof(float) * (size_t)nch * (size_t)H * kla::kGDFloats);
-  const size_t tile_bytes = sizeof(float) * (size_t)nch * (size_t)H * KLA_CHUNK * KLA_CHUNK;
+  const size_t tile_bytes = es * (size_t)nch * (size_t)H * kla::kTpbElems;
   w.off_P = align256(w.off_T + tile_bytes);
   w.total = align256(w.off_P + tile_bytes);
   if (diag) {
-    const size_t kt = sizeof(float) * (size_t)nch * (size_t)H * KLA_CHUNK * (size_t)d_k;
+    const size_t kt = es * (size_t)nch * (size_t)H * KLA_CHUNK * (size_t)d_k;
     w.off_KG = w.total;
     w.off_QG = align256(w.off_KG + kt);
     w.off_KD = align256(w.off_QG + kt);
@@ -146,18 +147,19 @@ kla_status hip_status(hipError_t e, const char *what) {
 
 extern "C" {
 
-size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
-                                   int32_t d_k, int32_t d_v) {
-  if (n_seq <= 0 || total_tokens < 0 || n_heads <= 0 || !supported_dk(d_k) || !supported_dv(d_v))
+size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                                      int32_t d_k, int32_t d_v, kla_dtype dtype,
+                                      const kla_options *opts) {
+  if (n_seq <= 0 || total_tokens < 0 || n_heads <= 0 || !supported_dk(d_k) ||
+      !supported_dv(d_v) || (dtype != KLA_DTYPE_F32 && dtype != KLA_DTYPE_BF16))
     return 0;
-  return ws_layout(n_seq, total_tokens, n_heads).total;
+  return ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype),
+                   opts && opts->diagonal_gate != 0).total;
 }
 
-size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
-                                      int32_t d_k, int32_t d_v, const kla_options *opts) {
-  if (n_seq <= 0 || total_tokens < 0 || n_heads <= 0 || !supported_dk(d_k) || !supported_dv(d_v))
-    return 0;
-  return ws_layout(n_seq, total_tokens, n_heads, d_k, opts && opts->diagonal_gate != 0).total;
+size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                                   int32_t d_k, int32_t d_v, kla_dtype dtype) {
+  return kla_prefill_workspace_bytes_ex(n_seq, total_tokens, n_heads, d_k, d_v, dtype, nullptr);
 }
 
 }  // extern "C"
@@ -176,7 +178,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, int64_t d_v,
                      size_t es) {
   BwdLayout b;
-  b.fw = ws_layout(n_seq, total_tokens, H);
+  b.fw = ws_layout(n_seq, total_tokens, H, d_k, es);
   const size_t nch = (size_t)kla::chunk_upper_bound(n_seq, total_tokens);
   const size_t st = sizeof(float) * nch * (size_t)H * (size_t)d_k * (size_t)d_v;
   const size_t ut = sizeof(float) * nch * (size_t)H * KLA_CHUNK * (size_t)d_v;
@@ -237,7 +239,7 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
   const size_t nS = (size_t)n_seq * n_heads * d_k * d_v * sizeof(float);
   if (S_T && S_T != S0 && overlap(S_T, nS, S0, nS))
     return fail(KLA_ERR_INVALID_ARGUMENT, "S_T may equal S0 but must not partially overlap it");
-  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads, d_k, diag);
+  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads, d_k, es, diag);
   if (!workspace || workspace_bytes < w.total)
     return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -254,8 +256,8 @@ struct WsViews {
 };
 
 WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
-                 int32_t d_k = 0, bool diag = false) {
-  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads, d_k, diag);
+                 int32_t d_k, kla_dtype dtype, bool diag = false) {
+  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype), diag);
   char *ws = static_cast<char *>(workspace);
   WsViews v{{reinterpret_cast<int32_t *>(ws + w.off_cu),
              reinterpret_cast<int32_t *>(ws + w.off_co)},
@@ -272,7 +274,7 @@ kla_status enqueue_prepare_diag(const void *q, const void *k, const float *g, co
                                 float eps, const kla::CoefOpts &opts, const int32_t *cu_seqlens,
                                 int32_t n_seq, int32_t total_tokens, int32_t n_heads, int32_t d_k,
                                 kla_dtype dtype, void *workspace, hipStream_t s) {
-  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, true);
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, true);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
   kla_status st =
       hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan");
@@ -286,7 +288,7 @@ kla_status enqueue_prepare(const void *q, const void *k, const float *g, const f
                            const kla::CoefOpts &opts, const int32_t *cu_seqlens, int32_t n_seq,
                            int32_t total_tokens, int32_t n_heads, int32_t d_k, kla_dtype dtype,
                            void *workspace, hipStream_t s) {
-  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
   kla::PlanArgs pa{kla::kPlanTables, cu_seqlens, total_tokens};
   if (!cu_seqlens)
@@ -308,7 +310,7 @@ kla_status enqueue_scan(const void *q, const void *k, const void *v, const float
                         float *S_T, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
                         int32_t d_k, int32_t d_v, kla_dtype dtype, void *workspace, hipStream_t s,
                         bool diag = false) {
-  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, diag);
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, diag);
   return hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0, o,
                                      S_T, wv.tabs, n_seq, n_heads, s,
                                      diag ? &wv.diag : nullptr),
@@ -424,7 +426,7 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
   if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
                             dtype, workspace, s)) != KLA_OK)
     return st;
-  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads);
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype);
   char *ws = static_cast<char *>(workspace);
   void *SN = ws + bl.off_SN;  // incoming states in the operand type
   if ((st = hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0,
@@ -530,7 +532,7 @@ kla_status kla_prefill_chunk_stage(const void *k, const void *v, const float *g,
     if (p && !aligned_to(p, 4)) return fail(KLA_ERR_INVALID_ARGUMENT, "fp32 buffers must be 4-byte aligned");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(KLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads);
+  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype));
   // this entry point writes G into the caller's buffer when given, else into the workspace
   if (!workspace || workspace_bytes < w.total)
     return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
@@ -617,6 +619,6 @@ const char *kla_status_string(kla_status status) {
 
 const char *kla_last_error(void) { return g_last_error; }
 
-int32_t kla_version(void) { return 200; }
+int32_t kla_version(void) { return 30000; }
 
 }  // extern "C"

@@ -247,6 +247,8 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     (&sm.T[0][0])[e] = 0.f;
     (&sm.P[0][0])[e] = 0.f;
   }
+  // every zero is in place before any thread stores a chunk's lower blocks over them
+  __syncthreads();
   // a chunk's tiles are loaded into registers while the chunk before it (in this reverse
   // order) is computed, and written to LDS when its turn comes
   RegTile<Tin, kChunk, DK, kAdjThreads> rk, rq;
@@ -260,8 +262,8 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     rk.load(k + tok * DK, (size_t)H * DK, len, tid);
     rq.load(q + tok * DK, (size_t)H * DK, len, tid);
     rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
-    rt.load(Tm + ch * (kChunk * kChunk), tid);
-    rp.load(Pm + ch * (kChunk * kChunk), tid);
+    rt.load(Tm + ch * kTpbElems, tid);
+    rp.load(Pm + ch * kTpbElems, tid);
     if (tid < 3 * kChunk) rgd = GD[ch * kGDFloats + tid];  // gam, dec, gamO
   };
   if (nchunks > 0) issue(nchunks - 1);

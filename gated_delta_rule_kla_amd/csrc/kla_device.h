@@ -57,7 +57,8 @@ __device__ __forceinline__ int tpc_off(int r, int e) {
 // each row-major, in the order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) .. (3,3); the scan
 // reads zeros for the two upper blocks the compact tile still holds.
 constexpr int kTpbZero = 0x7ffffff0;  // out of range for any tile: a buffer load reads zeros
-template <typename T> constexpr int tpb_bytes() { return 10 * 256 * (int)sizeof(T); }
+constexpr int kTpbElems = 10 * 256;  // elements of one packed tile
+template <typename T> constexpr int tpb_bytes() { return kTpbElems * (int)sizeof(T); }
 // Byte offset of the 16 bytes at (row, col), col a multiple of 16 / sizeof(T); kTpbZero above
 // the diagonal blocks.
 template <typename T>

@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kDiagThreads) void kla_prep_diag_kernel(
 
   // ---- T = X Diag(b) and P, as their ten 16 x 16 blocks on and below the diagonal (tpb_off
   //      layout), in element order of the packed blocks
-  const size_t tp0 = (size_t)task * (kChunk * kChunk);
+  const size_t tp0 = (size_t)task * kTpbElems;
   for (int e = 4 * tid; e < 10 * 256; e += 4 * kDiagThreads) {  // 4 columns of a row per lane
     const int blk = e >> 8, w = e & 255;
     const int I = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0, J = blk - I * (I + 1) / 2;

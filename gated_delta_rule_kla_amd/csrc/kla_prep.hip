@@ -410,7 +410,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
   // ---- P = A o Q K^T from the tiles K_j Q_i^T (row 16 i + r16, columns 16 j + 4 kg + e;
   //      zero above the diagonal)
   if (want_p) {
-    Tin *P_task = P_out + (size_t)task * (kChunk * kChunk);
+    Tin *P_task = P_out + (size_t)task * kTpbElems;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int prow = 16 * i + r16;
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
   //      scan's T (written with the decays) goes out as packed blocks, the unit-check stage's
   //      in full.
   const bool t_packed = GD_out != nullptr;
-  TOut *T_task = T_out + (size_t)task * (kChunk * kChunk);
+  TOut *T_task = T_out + (size_t)task * (t_packed ? kTpbElems : kChunk * kChunk);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int trow = 16 * i + r16;

@@ -270,8 +270,8 @@ void kla_scan_kernel(
                          : make_rsrc(q + tok * DK, kq_bytes);
     const Rsrc rv =
         make_rsrc(v + tok * DV + v0, (uint32_t)(((size_t)(len - 1) * H * DV + kBV) * ES));
-    const Rsrc rt = make_rsrc(Tm + ch * (kChunk * kChunk), tpb_bytes<Tin>());
-    const Rsrc rp = make_rsrc(Pm + ch * (kChunk * kChunk), tpb_bytes<Tin>());
+    const Rsrc rt = make_rsrc(Tm + ch * kTpbElems, tpb_bytes<Tin>());
+    const Rsrc rp = make_rsrc(Pm + ch * kTpbElems, tpb_bytes<Tin>());
     const Rsrc rg = make_rsrc(GD + ch * kGDFloats, kGDFloats * sizeof(float));
 #pragma unroll
     for (int j = 0; j < DP::NK / NP; ++j) {

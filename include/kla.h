@@ -67,11 +67,13 @@ typedef enum kla_dtype {
   KLA_DTYPE_BF16 = 1  /* bfloat16; outputs rounded to nearest even */
 } kla_dtype;
 
-/* Bytes of device workspace kla_prefill_chunked needs for this problem size
- * (an upper bound valid for any cu_seqlens with these totals).  Returns 0 for
- * an unsupported or invalid size. */
+/* Bytes of device workspace kla_prefill_chunked needs for this problem size and
+ * element type (an upper bound valid for any cu_seqlens with these totals).  Per
+ * 64-token chunk and head it holds the chunk's T and P (Eq. (7)-(8)) as their ten
+ * 16 x 16 blocks on and below the diagonal in the element type, and 768 bytes of
+ * decay factors.  Returns 0 for an unsupported or invalid size or dtype. */
 size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
-                                   int32_t d_k, int32_t d_v);
+                                   int32_t d_k, int32_t d_v, kla_dtype dtype);
 
 /*
  * Chunkwise prefill: (q, k, v, g, eta, eps, S0) -> (o, S_T).
@@ -231,7 +233,8 @@ typedef struct kla_options {
  * defaults, the same value as kla_prefill_workspace_bytes); 0 for unsupported
  * sizes. */
 size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
-                                      int32_t d_k, int32_t d_v, const kla_options *opts);
+                                      int32_t d_k, int32_t d_v, kla_dtype dtype,
+                                      const kla_options *opts);
 
 /* kla_prefill_chunked, kla_prefill_prepare and kla_decode_step with options
  * (NULL = the defaults, which is what the calls without _ex use).  The scan
@@ -280,8 +283,9 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const
  *   workspace   device buffer of at least kla_prefill_backward_workspace_bytes
  *               bytes, 256-byte aligned; contents are scratch.  It holds the
  *               forward pass run again with every chunk's incoming state
- *               stored, the cotangent of every chunk's outgoing state and the
- *               per-chunk dU and dR, all fp32.
+ *               stored in the element type `dtype` (bf16 for bf16 inputs), and
+ *               in fp32 the cotangent of every chunk's outgoing state and the
+ *               per-chunk dU and dR.
  * The gradient buffers must not overlap each other, the inputs or the
  * workspace.  q, k, v, dO, dq, dk and dv must be 16-byte aligned; g, eta, S0,
  * dS_T, dg, deta and dS0 4-byte aligned.  Size limits and errors as for

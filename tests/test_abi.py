@@ -49,15 +49,23 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes_formula(lib):
-    # cu + chunk offsets + G (fp32 per token-head) + decays (2 x 64 fp32 per chunk-head)
-    # + T and P (64x64 fp32 each per chunk-head), chunk count bounded by ceil(n/64) + n_seq
+    # cu + chunk offsets + G (fp32 per token-head) + decays (3 x 64 fp32 per chunk-head)
+    # + T and P as ten 16 x 16 blocks each per chunk-head in the element type; the chunk
+    # count is bounded by ceil(n/64) + n_seq, and each part is padded to 256 bytes
     n_seq, n_tok, H = 4, 16384, 16
-    nb = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, 128, 128)
     nch = (n_tok + 63) // 64 + n_seq
-    assert nb >= 4 * n_tok * H + 4 * nch * H * 128 + 2 * 4 * nch * H * 64 * 64
-    assert nb % 256 == 0
+    pad = lambda x: (x + 255) // 256 * 256
+    for torch_dt, es in ((kla.torch.bfloat16, 2), (kla.torch.float32, 4)):
+        nb = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, 128, 128, torch_dt)
+        want = (2 * pad(4 * (n_seq + 1)) + pad(4 * n_tok * H) + pad(4 * nch * H * 192)
+                + 2 * pad(es * nch * H * 2560))
+        assert nb == want, (torch_dt, nb, want)
+    # bf16 halves the tiles against fp32
+    assert (kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, 128, 128, kla.torch.float32)
+            - kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, 128, 128)) == 2 * 2 * nch * H * 2560
     assert kla.kla_prefill_workspace_bytes(4, 100, 16, 96, 128) == 0
     assert kla.kla_prefill_workspace_bytes(0, 100, 16, 128, 128) == 0
+    assert lib.kla_prefill_workspace_bytes(4, 100, 16, 128, 128, 7) == 0  # unknown dtype
 
 
 FAKE = 1 << 32  # 16-byte aligned non-NULL addresses 4 GiB apart; never dereferenced on error paths
@@ -175,15 +183,16 @@ def test_options_default_pointer_is_accepted_up_to_the_workspace_check(lib):
 
 
 def test_diagonal_gate_workspace_and_entry_points(lib):
-    # the diagonal-gated variant needs the decayed key and query tiles: three [64, d_k] fp32
-    # tiles and d_k decays per chunk-head on top of the default workspace
+    # the diagonal-gated variant needs the decayed key and query tiles: three [64, d_k]
+    # tiles in the element type and d_k fp32 decays per chunk-head on top of the default
+    # workspace
     n_seq, n_tok, H, dk, dv = 4, 16384, 16, 128, 128
     base = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv)
     diag = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, diagonal_gate=True)
     nch = (n_tok + 63) // 64 + n_seq
-    assert diag >= base + 4 * nch * H * (3 * 64 * dk + dk) and diag % 256 == 0
+    assert diag >= base + nch * H * (2 * 3 * 64 * dk + 4 * dk) and diag % 256 == 0
     # NULL options give the default size
-    assert lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, dk, dv, None) == base
+    assert lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, dk, dv, BF16, None) == base
     # the default-size workspace is too small for the diagonal-gated prefill
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, eta=FAKE * 5, o=FAKE * 6)
     st = lib.kla_prefill_chunked_ex(a["q"], a["k"], a["v"], a["g"], a["eta"], 1e-6, None,
