@@ -88,6 +88,9 @@ def load_library():
     lib.kla_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i32, i32, i32,
                                        ctypes.c_int, opt_p, vp]
     lib.kla_decode_step_ex.restype = ctypes.c_int
+    lib.kla_prefill_chunked_noalloc.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32,
+                                                i32, i32, i32, i32, ctypes.c_int, opt_p, vp]
+    lib.kla_prefill_chunked_noalloc.restype = ctypes.c_int
     lib.kla_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     lib.kla_prefill_backward_workspace_bytes.restype = sz
     lib.kla_prefill_backward.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp,

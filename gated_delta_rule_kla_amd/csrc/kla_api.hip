@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kla.h"
 #include "kla_launch.h"
 
@@ -361,6 +363,65 @@ kla_status kla_prefill_chunked(const void *q, const void *k, const void *v, cons
   return kla_prefill_chunked_ex(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
                                 n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
                                 workspace_bytes, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free prefill: one array per device, held until the process ends.
+// Host code never uses the name itself as an address (on the host it is a stand-in, not the
+// device array): scratch_ptr() looks the device address up once per device, with that device
+// current, and every launch takes that pointer.
+static __device__ __align__(256) unsigned char scratch[KLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+kla_status scratch_ptr(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KLA_ERR_UNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kla_status kla_prefill_chunked_noalloc(const void *q, const void *k, const void *v,
+                                       const float *g, const float *eta, float eps,
+                                       const float *S0, void *o, float *S_T,
+                                       const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                       int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                                       int32_t d_k, int32_t d_v, kla_dtype dtype,
+                                       const kla_options *opts, void *stream) {
+  const size_t need =
+      kla_prefill_workspace_bytes_ex(n_seq, total_tokens, n_heads, d_k, d_v, dtype, opts);
+  if (need > (size_t)KLA_NOALLOC_SCRATCH_BYTES)
+    return fail(KLA_ERR_WORKSPACE,
+                "this prefill needs %zu bytes of scratch, more than the %zu-byte static "
+                "scratch of kla_prefill_chunked_noalloc; use kla_prefill_chunked_ex with a "
+                "workspace",
+                need, (size_t)KLA_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  kla_status st = scratch_ptr(&ws);
+  if (st != KLA_OK) return st;
+  // (an unsupported size gives need == 0 and is reported by the shared checks below)
+  return kla_prefill_chunked_ex(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
+                                n_seq, total_tokens, n_heads, d_k, d_v, dtype, ws,
+                                (size_t)KLA_NOALLOC_SCRATCH_BYTES, opts, stream);
 }
 
 kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, const float *g,

@@ -317,6 +317,28 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
                                    int32_t d_v, kla_dtype dtype, void *workspace,
                                    size_t workspace_bytes, const kla_options *opts, void *stream);
 
+/*
+ * kla_prefill_chunked_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Its scratch is a static device array of
+ * KLA_NOALLOC_SCRATCH_BYTES bytes in libkla.so, one per device the library runs
+ * on, held until the process ends; the call allocates nothing.  A problem whose
+ * kla_prefill_workspace_bytes_ex exceeds that size returns KLA_ERR_WORKSPACE with
+ * nothing enqueued.  Every call on one device shares that device's array, and the
+ * scratch keeps the last call's contents (each call writes all it reads, so
+ * nothing needs clearing): calls that overlap in time on one device (other
+ * streams, other threads) race on it and give wrong results; serialise them.
+ * Other arguments, results and errors as for kla_prefill_chunked_ex.
+ */
+#define KLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+kla_status kla_prefill_chunked_noalloc(const void *q, const void *k, const void *v,
+                                       const float *g, const float *eta, float eps,
+                                       const float *S0, void *o, float *S_T,
+                                       const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                       int32_t n_seq, int32_t total_tokens, int32_t n_heads,
+                                       int32_t d_k, int32_t d_v, kla_dtype dtype,
+                                       const kla_options *opts, void *stream);
+
 /* Static description of a status code. */
 const char *kla_status_string(kla_status status);
 

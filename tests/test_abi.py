@@ -266,3 +266,14 @@ def test_backward_ex_rejects_the_diagonal_gate(lib):
         BF16, FAKE * 64, lib.kla_prefill_backward_workspace_bytes(2, 256, 4, 128, 128, BF16),
         ctypes.pointer(bad), None)
     assert st == UNSUPPORTED
+
+
+def test_noalloc_rejects_a_problem_beyond_its_static_scratch(lib):
+    # the size check runs on the host before any HIP call
+    n_seq, n_tok, H = 1, 1 << 20, 64
+    assert lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, 128, 128, BF16, None) > (64 << 20)
+    st = lib.kla_prefill_chunked_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1e-6, None,
+                                         FAKE * 6, None, None, None, n_seq, n_tok, H, 128, 128,
+                                         BF16, None, None)
+    assert st == WORKSPACE
+    assert "static scratch" in lib.kla_last_error().decode()
