@@ -241,9 +241,9 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
   const size_t nS = (size_t)n_seq * n_heads * d_k * d_v * sizeof(float);
   if (S_T && S_T != S0 && overlap(S_T, nS, S0, nS))
     return fail(KLA_ERR_INVALID_ARGUMENT, "S_T may equal S0 but must not partially overlap it");
-  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads, d_k, es, diag);
-  if (!workspace || workspace_bytes < w.total)
-    return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+  const size_t need = ws_layout(n_seq, total_tokens, n_heads, d_k, es, diag).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(KLA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");

@@ -10,6 +10,7 @@
 //                                                        U = T (V - Diag(gamma) K S0)
 // The Gram matrix runs on the matrix cores; (I + L)^{-1} is formed by forward
 // substitution out of LDS, one column per lane of a wavefront.
+#include "kla_chunk.h"
 #include "kla_device.h"
 #include "kla_launch.h"
 
@@ -213,25 +214,6 @@ __device__ __forceinline__ ChunkLoc locate(const Planner &p, int c) {
 // A_ij = exp(G_i - G_j) for j <= i, zero above the diagonal) for the scan.
 // ---------------------------------------------------------------------------------------------
 
-// Element (r, c) of a 16 x 16 fp32 block in LDS: rows of 64 bytes, the 16-byte units of
-// rows 8..15 XOR-swizzled by 2 so that a half-wavefront reading (row r16, unit kg) hits 32
-// distinct 16-byte positions.
-__device__ __forceinline__ int bidx(int r, int c) {
-  return r * 16 + ((((c >> 2) ^ (((r >> 3) & 1) << 1))) << 2) + (c & 3);
-}
-// LDS slot of the X block (i, j) that later products read: the diagonal blocks and the
-// sub-diagonal blocks of rows 1 and 2.
-__host__ __device__ constexpr int xslot(int i, int j) {
-  return i == j ? i : (i == 1 ? 4 : (j == 0 ? 5 : 6));
-}
-
-struct PrepSmem {
-  alignas(16) float Ld[4][256];  // diagonal blocks of L, row-major
-  alignas(16) float XT[7][256];  // X blocks transposed: XT(i, j)[c][r] = X[16 i + r][16 j + c]
-  alignas(16) float G2[kChunk];  // G * log2(e)
-  alignas(16) float beta[kChunk];
-};
-
 // Entries (row, col .. col + 3) of a chunk's 64 x 64 output, col a multiple of 4, straight
 // from registers: in the packed layout (tpb_off; entries of the blocks above the diagonal are
 // not stored) or row-major.  A lane group (r16, kg) covering one 16 x 16 block writes its
@@ -282,8 +264,6 @@ __device__ __forceinline__ void load_rows_bf16(bf16x8 (&f)[4][NKS], Rsrc r, int 
       f[b][2 * c + 1] = __builtin_bit_cast(bf16x8, F1);
     }
 }
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename Tin, int DK, typename TOut>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) * DK > 256 ? 1 : 2))) void kla_prep_kernel(
@@ -376,7 +356,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     for (int ks = 0; ks < NKS; ++ks) gd[i] = mma(kf[i][ks], kf[i][ks], gd[i]);
   }
   const int dsrc = r16 + 16 * (r16 >> 2);  // the lane holding row r16's diagonal element
-  const bool diag_lane = lane == dsrc;
   const int de = r16 & 3;
   const int pos0 = t0 - loc.ts + 1 + (opts.pos_offset ? opts.pos_offset[loc.n] : 0);
   float rqv[4], bme[4], G2me[4];  // per own row 16 i + r16: 1/||q||, b, G log2(e)
@@ -432,120 +411,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     }
   }
 
-  // ---- L: diagonal blocks to LDS (row-major), sub-diagonal blocks kept in registers in the
-  //      A-operand layout (row r16, columns 4 kg + e)
-  f32x4 Lr[4][3];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j <= i; ++j) {
-      const int j0 = 16 * j + 4 * kg;
-      f32x4 acc = gd[i];
-      if (j < i) {
-        acc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) acc = mma(kf[j][ks], kf[i][ks], acc);
-      }
-      const f32x4 Gc = *reinterpret_cast<const f32x4 *>(&sm.G2[j0]);
-      f32x4 lv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool below = (j < i) || (4 * kg + e < r16);  // column < row
-        lv[e] = bme[i] * exp2_fast(below ? G2me[i] - Gc[e] : -INFINITY) * acc[e];
-      }
-      if (j < i) Lr[i][j] = lv;
-      else *reinterpret_cast<f32x4 *>(&sm.Ld[i][bidx(r16, 4 * kg)]) = lv;
-    }
-  }
-  lds_barrier();
-
-  // ---- diagonal blocks: lane group kg inverts I + L_kk by substitution, lane = column r16;
-  //      rows of L_kk are read four values at a time (one address per lane group)
-  {
-    const float *Ld = sm.Ld[kg];
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float lr[16];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (4 * u < i) {
-          const f32x4 v4 = *reinterpret_cast<const f32x4 *>(Ld + bidx(i, 4 * u));
-          lr[4 * u] = v4[0]; lr[4 * u + 1] = v4[1]; lr[4 * u + 2] = v4[2]; lr[4 * u + 3] = v4[3];
-        }
-      }
-      float a0 = (i == r16) ? 1.f : 0.f, a1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < i; j += 2) {
-        a0 = fmaf(-lr[j], x[j], a0);
-        if (j + 1 < i) a1 = fmaf(-lr[j + 1], x[j + 1], a1);
-      }
-      x[i] = a0 + a1;
-    }
-    // XT(k, k)[r16][i] = X[16 k + i][16 k + r16]
-    float *XTd = sm.XT[xslot(kg, kg)];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<f32x4 *>(XTd + bidx(r16, 4 * u)) =
-          f32x4{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
-  }
-  lds_barrier();
-
-  // ---- T = X Diag(b): lane (r16, kg) writes columns 16 j + 4 kg + e of row 16 i + r16.
-  //      Diagonal blocks from LDS, blocks above the diagonal zero, the rest as they form.  The
-  //      scan's T (written with the decays) goes out as packed blocks, the unit-check stage's
-  //      in full.
+  // ---- T = (I + L)^{-1} Diag(b), written as the scan's packed blocks (with the decays) or
+  //      in full (the unit-check stage, blocks above the diagonal zero)
   const bool t_packed = GD_out != nullptr;
   TOut *T_task = T_out + (size_t)task * (t_packed ? kTpbElems : kChunk * kChunk);
+  if (!t_packed) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int trow = 16 * i + r16;
-    const float *XTi = sm.XT[xslot(i, i)];
-    const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * i + 4 * kg]);
-    float xv[4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xv[s] = XTi[bidx(4 * kg + s, r16)];  // X_ii[r16][4 kg + s]
-    out_put<TOut>(T_task, t_packed, trow, 16 * i + 4 * kg, xv[0] * bv[0], xv[1] * bv[1],
-                  xv[2] * bv[2], xv[3] * bv[3]);
-    if (!t_packed) {
-#pragma unroll
-      for (int j = i + 1; j < 4; ++j) out_put<TOut>(T_task, false, trow, 16 * j + 4 * kg, 0.f, 0.f, 0.f, 0.f);
-    }
+      for (int j = i + 1; j < 4; ++j)
+        out_put<TOut>(T_task, false, 16 * i + r16, 16 * j + 4 * kg, 0.f, 0.f, 0.f, 0.f);
   }
-
-  // ---- sub-diagonal blocks, by distance; the blocks of one distance are independent
-#pragma unroll
-  for (int dist = 1; dist < 4; ++dist) {
-#pragma unroll
-    for (int i = dist; i < 4; ++i) {
-      const int j = i - dist;
-      // Y = sum_k L_ik X_kj: A = L_ik (registers), B = X_kj[4 kg + s][r16] from XT(k, j)
-      f32x4 Y = zero4();
-#pragma unroll
-      for (int kb = j; kb < i; ++kb) {
-        const f32x4 bx = *reinterpret_cast<const f32x4 *>(&sm.XT[xslot(kb, j)][bidx(r16, 4 * kg)]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          Y = __builtin_amdgcn_mfma_f32_16x16x4f32(Lr[i][kb][s], bx[s], Y, 0, 0, 0);
-      }
-      // X_ij^T = -(Y^T X_ii^T): A = Y^T (Y's accumulator layout), B = X_ii[r16][4 kg + s]
-      const float *XTi = sm.XT[xslot(i, i)];
-      f32x4 Zt = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        Zt = __builtin_amdgcn_mfma_f32_16x16x4f32(Y[s], XTi[bidx(4 * kg + s, r16)], Zt, 0, 0, 0);
-      // lane (r16, kg) now holds X_ij[r16][4 kg + e] = -Zt[e]
-      const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * j + 4 * kg]);
-      out_put<TOut>(T_task, t_packed, 16 * i + r16, 16 * j + 4 * kg, -Zt[0] * bv[0],
-                    -Zt[1] * bv[1], -Zt[2] * bv[2], -Zt[3] * bv[3]);
-      if (i < 3) {  // read again by the next distances
-        float *XTo = sm.XT[xslot(i, j)];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) XTo[bidx(4 * kg + e, r16)] = -Zt[e];
-      }
-    }
-    lds_barrier();
-  }
+  chunk_T<Tin, NKS, false>(
+      kf, gd, bme, G2me, sm, [] { lds_barrier(); },
+      [&](int row, int col, float a, float b, float c, float d) {
+        out_put<TOut>(T_task, t_packed, row, col, a, b, c, d);
+      });
 }
 
 template <typename Tin, int DK>

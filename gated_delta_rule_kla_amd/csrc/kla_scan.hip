@@ -44,6 +44,7 @@
 
 #include "kla_device.h"
 #include "kla_launch.h"
+#include "kla_tile.h"
 
 namespace kla {
 
@@ -58,80 +59,6 @@ struct ScanShape {
 using ScanNarrow = ScanShape<2, 2>;  // 32 columns: the grid fills the chip
 using ScanWide = ScanShape<4, 4>;    // 64 columns: K, Q, T, P staged once for twice the columns
 constexpr int kLdsBytes = 160 * 1024;
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.
-__device__ __forceinline__ void dma16(Rsrc r, const void *lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lds), 16, voff, 0, 0, 0);
-}
-// Buffer stores of 8 and 16 bytes (dropped beyond the descriptor's range).
-__device__ __forceinline__ void store8(u32x2 x, Rsrc r, int voff, int soff) {
-  __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, 0);
-}
-__device__ __forceinline__ void store16(u32x4 x, Rsrc r, int voff, int soff) {
-  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
-}
-
-// Barrier for the producer waves.  They touch LDS only through buffer-to-LDS loads, whose
-// completion they establish themselves with wait_vmcnt before arriving; the bare s_barrier
-// (a compiler barrier for memory operations) avoids the release fence, which would wait
-// for the later chunks' loads as well.
-__device__ __forceinline__ void producer_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima, i.e. not waited on).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// ---- swizzles, in 16-byte units of a bf16 row (fp32 rows use twice the value).  Each is
-// linear over GF(2): row bits 0, 1, 3 and 4 each flip a fixed set of unit bits.
-template <int ROW_ELEMS>
-__device__ __forceinline__ int sw_rows(int r) {
-  const int b0 = r & 1, b1 = (r >> 1) & 1, b3 = (r >> 3) & 1, b4 = (r >> 4) & 1;
-  if constexpr (ROW_ELEMS >= 128)  // 16 units: K, Q with d_k = 128
-    return b0 ^ (b1 << 2) ^ (b3 << 3) ^ (b4 << 1);
-  else  // 8 units: rows 32-63 of T and P, and K, Q with d_k = 64
-    return (b1 << 2) ^ (b3 * 3) ^ (b4 << 1);
-}
-// value tiles (32 or 64 columns): read by transpose reads, written by the output parking
-template <int BV>
-__device__ __forceinline__ int sw_val(int r) {
-  const int b1 = (r >> 1) & 1, b3 = (r >> 3) & 1, b4 = (r >> 4) & 1;
-  if constexpr (BV >= 64)  // 8 units
-    return (b1 << 1) ^ (b3 * 3) ^ (b4 << 2);
-  else  // 4 units
-    return (b3 << 1) ^ (b4 * 3);
-}
-
-// Byte offset of element e of row r in a swizzled tile of ROW_ELEMS elements of type T
-// (a value tile when VAL).
-template <typename T, int ROW_ELEMS, bool VAL = false>
-__device__ __forceinline__ int tile_off(int r, int e) {
-  constexpr int ES = sizeof(T), ROWB = ROW_ELEMS * ES;
-  const int byte = e * ES;
-  const int sw = VAL ? sw_val<ROW_ELEMS>(r) : sw_rows<ROW_ELEMS>(r);
-  const int u = (byte >> 4) ^ (sw * (ES / 2));
-  return r * ROWB + (u << 4) + (byte & 15);
-}
-
-// LDS transpose read of 4 x 16-bit values (gfx950 ds_read_b64_tr_b16).  Within each group
-// of 16 lanes, destination lane d receives element (d & 3) of the 8-byte chunks addressed
-// by source lanes (d >> 2) + 4 i, i = 0..3.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-__device__ __forceinline__ bf16x4 lds_read_tr(const void *p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-  return __builtin_bit_cast(bf16x4, r);
-}
-
-// Token (or key dim) of row slot 4 a + i of 16-row tile t.
-__device__ __forceinline__ int tmap(int t, int a, int i) {
-  return 32 * (t >> 1) + 8 * a + 4 * (t & 1) + i;
-}
 
 // ---- LDS layout
 template <typename Tin, int DK, int BV, bool DIAG>

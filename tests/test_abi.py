@@ -269,11 +269,12 @@ def test_backward_ex_rejects_the_diagonal_gate(lib):
 
 
 def test_noalloc_rejects_a_problem_beyond_its_static_scratch(lib):
-    # the size check runs on the host before any HIP call
+    # the size check runs on the host before any HIP call; fp32 inputs take the staged path,
+    # whose workspace holds every chunk's T and P
     n_seq, n_tok, H = 1, 1 << 20, 64
-    assert lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, 128, 128, BF16, None) > (64 << 20)
+    assert lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, 128, 128, F32, None) > (64 << 20)
     st = lib.kla_prefill_chunked_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1e-6, None,
                                          FAKE * 6, None, None, None, n_seq, n_tok, H, 128, 128,
-                                         BF16, None, None)
+                                         F32, None, None)
     assert st == WORKSPACE
     assert "static scratch" in lib.kla_last_error().decode()

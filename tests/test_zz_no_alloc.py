@@ -60,12 +60,12 @@ def test_noalloc_matches_workspace_entry_point_twice(lib):
 
 def test_noalloc_rejects_a_problem_beyond_its_scratch(lib):
     kla, L = lib
-    n_seq, n_tok, H = 1, 1 << 20, 64  # ~1 GB of per-chunk tiles
-    need = L.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, 128, 128, BF16, None)
+    n_seq, n_tok, H = 1, 1 << 20, 64  # fp32 inputs: ~1 GB of per-chunk tiles
+    need = L.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, 128, 128, 0, None)
     assert need > (64 << 20)
     FAKE = 1 << 32
     st = L.kla_prefill_chunked_noalloc(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1e-6, None,
                                        FAKE * 6, None, None, None, n_seq, n_tok, H, 128, 128,
-                                       BF16, None, None)
+                                       0, None, None)
     assert st == 3  # KLA_ERR_WORKSPACE, nothing enqueued
     assert "static scratch" in L.kla_last_error().decode()
