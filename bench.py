@@ -124,37 +124,50 @@ def main():
         return nb, nf
 
     def time_prefill(sets, meta, steps, warmup):
-        """Time `steps` prefill calls (prepare then scan, what kla_prefill_chunked enqueues)
-        rotating over `sets`: one event pair around the back-to-back calls, then a second
-        pass with events between the two halves for the per-kernel split."""
+        """Time `steps` kla_prefill_chunked calls rotating over `sets` (one event pair around
+        the back-to-back calls), then split them into the prep kernel and the scan: with
+        the sequential scan by a pass of prepare + scan calls (what kla_prefill_chunked
+        enqueues) with an event between the halves; with the two-level scan (reachable
+        through kla_prefill_chunked only) by a pass of prepare calls alone, the scan phases
+        taking the rest."""
         n_seq, dv, eps = meta["n_seq"], meta["d_v"], meta["eps"]
 
-        def step(s, ev_mid=None):
+        def whole(s):
+            kla.kla_prefill_chunked(s["q"], s["k"], s["v"], s["g"], s["eta"], eps,
+                                    S0=s.get("S0"), cu_seqlens=s.get("cu"), n_seq=n_seq,
+                                    o=s["o"], S_T=s["S_T"], workspace=s["ws"])
+
+        def prepare(s):
             kla.kla_prefill_prepare(s["q"], s["k"], s["g"], s["eta"], eps, s["ws"], n_seq=n_seq,
                                     d_v=dv, cu_seqlens=s.get("cu"))
-            if ev_mid is not None:
-                ev_mid.record()
+
+        def scan(s):
             kla.kla_prefill_scan(s["q"], s["k"], s["v"], s["ws"], n_seq=n_seq, S0=s.get("S0"),
                                  o=s["o"], S_T=s["S_T"])
         for i in range(warmup):
-            step(sets[i % len(sets)])
+            whole(sets[i % len(sets)])
         torch.cuda.synchronize()
         e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e_start.record()
         for i in range(steps):
-            step(sets[i % len(sets)])
+            whole(sets[i % len(sets)])
         e_end.record()
         torch.cuda.synchronize()
         ms = e_start.elapsed_time(e_end) / steps
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         for i in range(steps):
+            s = sets[i % len(sets)]
             ev[i][0].record()
-            step(sets[i % len(sets)], ev[i][1])
+            prepare(s)
+            ev[i][1].record()
+            if not meta.get("two_level"):
+                scan(s)
             ev[i][2].record()
         torch.cuda.synchronize()
         prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-        scan = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-        return ms, prep, scan
+        if meta.get("two_level"):
+            return ms, prep, ms - prep
+        return ms, prep, sum(e[1].elapsed_time(e[2]) for e in ev) / steps
 
     def make_set(inp, dev, ws_bytes, dtype):
         n_tok, H, dk = inp["q"].shape
@@ -171,13 +184,17 @@ def main():
         inp = ki.prefill_inputs(wl, device=dev)
         n_tok, H_, dk_, dv_ = inp["q"].shape[0], wl.H, wl.d_k, wl.d_v
         es = inp["q"].element_size()
-        s = make_set(inp, dev, kla.kla_prefill_workspace_bytes(inp["n_seq"], n_tok, H_, dk_, dv_,
-                                                               wl.dtype), wl.dtype)
-        meta = {"n_seq": inp["n_seq"], "d_v": dv_, "eps": inp["eps"]}
+        ws_b = kla.kla_prefill_workspace_bytes(inp["n_seq"], n_tok, H_, dk_, dv_, wl.dtype)
+        s = make_set(inp, dev, ws_b, wl.dtype)
+        # dense input whose workspace holds the two-level scan's scratch runs that scan
+        two_level = inp["cu_seqlens"] is None and ws_b != kla.kla_prefill_workspace_bytes(
+            inp["n_seq"], n_tok, H_, dk_, dv_, wl.dtype, scan_segments=1)
+        meta = {"n_seq": inp["n_seq"], "d_v": dv_, "eps": inp["eps"], "two_level": two_level}
         ms, prep, scan = time_prefill([s], meta, steps, warmup)
         nb, nf = prefill_bytes_flops(n_tok, inp["n_seq"], H_, dk_, dv_, es)
         out = {"workload": wl.name, "tokens": n_tok, "ms_per_call": ms, "prep_ms": prep,
-               "scan_ms": scan, "tokens_per_s": n_tok / (ms * 1e-3),
+               "scan_ms": scan, "scan": "two-level" if two_level else "sequential",
+               "tokens_per_s": n_tok / (ms * 1e-3),
                "mfma_frac": nf / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                "hbm_frac": nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                "scan_hbm_frac": nb / (scan * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kla.h"
@@ -56,11 +57,43 @@ struct WsLayout {
   // diagonal gating only: per chunk-head the decayed key and query tiles K o exp(G),
   // Q o exp(G), K o exp(G_last - G) ([64][d_k] each, operand type) and exp(G_last) ([d_k])
   size_t off_KG = 0, off_QG = 0, off_KD = 0, off_GC = 0;
+  // two-level scan only (G >= 2 segments): [N_g | M_g] per (sequence, segment < G-1, head),
+  // [d_k][d_v + d_k] fp32, and the chained incoming states, [d_k][d_v] fp32
+  size_t off_NM = 0, off_Sin = 0;
   size_t total;
 };
 
+// The two-level scan's segmentation of a dense problem: G segments of Ls tokens (G = 0: the
+// sequential scan).  A function of the shape and the option only, so that the workspace
+// size does not depend on the device.  segs_opt: 0 automatic, 1 sequential, >= 2 requested.
+struct SegPlan {
+  int G = 0, Ls = 0;
+};
+SegPlan seg_plan(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_v, bool diag,
+                 int32_t segs_opt) {
+  SegPlan p;
+  if (diag || segs_opt == 1 || segs_opt < 0 || n_seq <= 0 || H <= 0 || d_v < 32 ||
+      total_tokens <= 0 || total_tokens % n_seq != 0)
+    return p;
+  const int64_t L = total_tokens / n_seq, cpl = (L + KLA_CHUNK - 1) / KLA_CHUNK;
+  int64_t G = segs_opt;
+  if (G == 0) {
+    const int64_t blocks = n_seq * H * (d_v / 32);  // workgroups of the sequential scan
+    if (2 * blocks > 256) return p;
+    G = std::min<int64_t>(512 / blocks, cpl / 32);
+  }
+  G = std::min<int64_t>(G, cpl);
+  if (G < 2) return p;
+  const int64_t per = (cpl + G - 1) / G;  // chunks per segment
+  G = (cpl + per - 1) / per;              // segments that hold tokens
+  if (G < 2) return p;
+  p.G = (int)G;
+  p.Ls = (int)(per * KLA_CHUNK);
+  return p;
+}
+
 WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, size_t es,
-                   bool diag = false) {
+                   bool diag = false, int64_t d_v = 0, int segs = 0) {
   WsLayout w;
   w.off_cu = 0;
   w.off_co = align256(w.off_cu + sizeof(int32_t) * (size_t)(n_seq + 1));
@@ -78,6 +111,12 @@ WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, 
     w.off_KD = align256(w.off_QG + kt);
     w.off_GC = align256(w.off_KD + kt);
     w.total = align256(w.off_GC + sizeof(float) * (size_t)nch * (size_t)H * (size_t)d_k);
+  }
+  if (segs >= 2) {
+    const size_t units = (size_t)n_seq * (size_t)(segs - 1) * (size_t)H * (size_t)d_k;
+    w.off_NM = w.total;
+    w.off_Sin = align256(w.off_NM + sizeof(float) * units * (size_t)(d_v + d_k));
+    w.total = align256(w.off_Sin + sizeof(float) * units * (size_t)d_v);
   }
   return w;
 }
@@ -155,8 +194,10 @@ size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32
   if (n_seq <= 0 || total_tokens < 0 || n_heads <= 0 || !supported_dk(d_k) ||
       !supported_dv(d_v) || (dtype != KLA_DTYPE_F32 && dtype != KLA_DTYPE_BF16))
     return 0;
-  return ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype),
-                   opts && opts->diagonal_gate != 0).total;
+  const bool diag = opts && opts->diagonal_gate != 0;
+  const SegPlan sp =
+      seg_plan(n_seq, total_tokens, n_heads, d_v, diag, opts ? opts->scan_segments : 0);
+  return ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype), diag, d_v, sp.G).total;
 }
 
 size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
@@ -218,7 +259,8 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
                               const int32_t *cu_seqlens_host, int32_t n_seq, int32_t total_tokens,
                               int32_t n_heads, int32_t d_k, int32_t d_v, kla_dtype dtype,
                               const void *workspace, size_t workspace_bytes, bool need_prep,
-                              bool need_scan, bool check_tables = true, bool diag = false) {
+                              bool need_scan, bool check_tables = true, bool diag = false,
+                              int segs = 0) {
   kla_status st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v,
                                       dtype, eps);
   if (st != KLA_OK) return st;
@@ -241,7 +283,7 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
   const size_t nS = (size_t)n_seq * n_heads * d_k * d_v * sizeof(float);
   if (S_T && S_T != S0 && overlap(S_T, nS, S0, nS))
     return fail(KLA_ERR_INVALID_ARGUMENT, "S_T may equal S0 but must not partially overlap it");
-  const size_t need = ws_layout(n_seq, total_tokens, n_heads, d_k, es, diag).total;
+  const size_t need = ws_layout(n_seq, total_tokens, n_heads, d_k, es, diag, d_v, segs).total;
   if (!workspace || workspace_bytes < need)
     return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -255,16 +297,23 @@ struct WsViews {
   float *G, *GD;
   void *T, *P;
   kla::DiagTiles diag;  // diagonal gating only
+  float *NM, *Sin;      // two-level scan only
 };
 
 WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
-                 int32_t d_k, kla_dtype dtype, bool diag = false) {
-  const WsLayout w = ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype), diag);
+                 int32_t d_k, kla_dtype dtype, bool diag = false, int32_t d_v = 0,
+                 int segs = 0) {
+  const WsLayout w =
+      ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype), diag, d_v, segs);
   char *ws = static_cast<char *>(workspace);
   WsViews v{{reinterpret_cast<int32_t *>(ws + w.off_cu),
              reinterpret_cast<int32_t *>(ws + w.off_co)},
             reinterpret_cast<float *>(ws + w.off_G), reinterpret_cast<float *>(ws + w.off_GD),
-            ws + w.off_T, ws + w.off_P, {nullptr, nullptr, nullptr, nullptr}};
+            ws + w.off_T, ws + w.off_P, {nullptr, nullptr, nullptr, nullptr}, nullptr, nullptr};
+  if (segs >= 2) {
+    v.NM = reinterpret_cast<float *>(ws + w.off_NM);
+    v.Sin = reinterpret_cast<float *>(ws + w.off_Sin);
+  }
   if (diag)
     v.diag = kla::DiagTiles{ws + w.off_KG, ws + w.off_QG, ws + w.off_KD,
                             reinterpret_cast<float *>(ws + w.off_GC)};
@@ -334,9 +383,15 @@ kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, c
   kla_status st = to_coef(opts, &co);
   if (st != KLA_OK) return st;
   const bool diag = co.diag_gate != 0;
+  if (opts && opts->scan_segments < 0)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "scan_segments must be >= 0");
+  // the workspace is sized for the shape's segmentation whatever cu_seqlens is; the
+  // two-level scan itself runs on dense input only
+  const SegPlan sp = seg_plan(n_seq, total_tokens, n_heads, d_v, diag,
+                              opts ? opts->scan_segments : 0);
   if ((st = check_prefill_args(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
                                n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
-                               workspace_bytes, true, true, true, diag)) != KLA_OK)
+                               workspace_bytes, true, true, true, diag, sp.G)) != KLA_OK)
     return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear any stale error from unrelated work
@@ -347,9 +402,22 @@ kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, c
     st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
                          dtype, workspace, s);
   if (st != KLA_OK) return st;
-  if ((st = enqueue_scan(q, k, v, S0, o, S_T, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
-                         workspace, s, diag)) != KLA_OK)
-    return st;
+  if (sp.G >= 2 && !cu_seqlens && total_tokens > 0) {
+    const WsViews wv =
+        ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, false, d_v, sp.G);
+    kla::SegArgs sa;
+    sa.G = sp.G;
+    sa.L = total_tokens / n_seq;
+    sa.Ls = sp.Ls;
+    sa.dv = d_v;
+    st = hip_status(kla::launch_scan_two_level(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P,
+                                               S0, o, S_T, n_seq, n_heads, sa, wv.NM, wv.Sin, s),
+                    "two-level scan");
+  } else {
+    st = enqueue_scan(q, k, v, S0, o, S_T, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
+                      workspace, s, diag);
+  }
+  if (st != KLA_OK) return st;
   return ok();
 }
 

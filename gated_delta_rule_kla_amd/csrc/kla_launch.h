@@ -84,6 +84,24 @@ hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k,
                        float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream,
                        const DiagTiles *diag = nullptr, void *SN = nullptr);
 
+// The two-level scan of equal-length sequences (the chunk scan's map, combine and segment
+// phases), for few long sequences: each sequence of L tokens is cut into G segments of Ls
+// tokens (a multiple of 64; the last one may be shorter).  NM holds [n_seq][G-1][H][d_k]
+// [d_v + d_k] fp32 and Sin [n_seq][G-1][H][d_k][d_v] fp32 (scratch).  Same inputs and
+// outputs as launch_scan with equal-length sequence tables.
+enum ScanMode { kScanSeq = 0, kScanMap = 1, kScanSeg = 2 };
+struct SegArgs {
+  int G = 0;                   // segments per sequence
+  int L = 0;                   // tokens per sequence
+  int Ls = 0;                  // tokens per segment
+  int dv = 0;                  // value columns d_v
+  const float *Sin = nullptr;  // incoming states of segments 1 .. G-1 (set by the launcher)
+};
+hipError_t launch_scan_two_level(Dtype dt, int d_k, int d_v, const void *q, const void *k,
+                                 const void *v, const float *GD, const void *T, const void *P,
+                                 const float *S0, void *o, float *S_T, int32_t n_seq, int32_t H,
+                                 const SegArgs &sa, float *NM, float *Sin, hipStream_t stream);
+
 // The backward pass after launch_prep (with the same opts) and launch_scan with SN: the adjoint scan (dS' per
 // chunk into dSo, dU and dR into their [chunk][H][64][d_v] fp32 buffers, dv, and dS0 if
 // non-null), then the per-chunk gradients dq, dk (operand type) and dg, deta (fp32).  dST

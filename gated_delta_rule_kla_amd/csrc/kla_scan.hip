@@ -61,64 +61,83 @@ using ScanWide = ScanShape<4, 4>;    // 64 columns: K, Q, T, P staged once for t
 constexpr int kLdsBytes = 160 * 1024;
 
 // ---- LDS layout
-template <typename Tin, int DK, int BV, bool DIAG>
+template <typename Tin, int DK, int BV, bool DIAG, bool NOQP = false>
 struct ScanSlot {
   alignas(16) unsigned char K[kChunk * DK * sizeof(Tin)];  // K, or K o exp(G) (DIAG)
-  alignas(16) unsigned char Q[kChunk * DK * sizeof(Tin)];  // Q, or Q o exp(G) (DIAG)
+  // Q, or Q o exp(G) (DIAG); not staged by the map mode, which forms no outputs
+  alignas(16) unsigned char Q[NOQP ? 16 : kChunk * DK * sizeof(Tin)];
   alignas(16) unsigned char T[tpc_bytes<Tin>()];  // compact tiles (tpc_off)
-  alignas(16) unsigned char P[tpc_bytes<Tin>()];
+  alignas(16) unsigned char P[NOQP ? 16 : tpc_bytes<Tin>()];
   alignas(16) unsigned char V[kChunk * BV * sizeof(Tin)];
   alignas(16) float gam[kChunk];   // exp(G_i)
   alignas(16) float dec[kChunk];   // exp(G_last - G_i)
-  alignas(16) float gamO[kChunk];  // output factor: exp(G_i), over ||q_i|| when normalised
+  // output factor: exp(G_i), over ||q_i|| when normalised (not staged by the map mode, which
+  // then fits three slots in half of a CU's LDS, two workgroups to a CU)
+  alignas(16) float gamO[NOQP ? 4 : kChunk];
   // diagonal gating: K o exp(G_last - G) for the state update, exp(G_last) per key channel
   alignas(16) unsigned char Kd[DIAG ? kChunk * DK * sizeof(Tin) : 16];
   alignas(16) float gC[DIAG ? DK : 4];
 };
 
-template <typename Tin, int DK, int BV, bool DIAG>
+template <typename Tin, int DK, int BV, bool DIAG, bool NOQP>
 constexpr int scan_nslot() {
-  constexpr int n = kLdsBytes / (int)sizeof(ScanSlot<Tin, DK, BV, DIAG>);
+  constexpr int n = kLdsBytes / (int)sizeof(ScanSlot<Tin, DK, BV, DIAG, NOQP>);
   return n >= 3 ? 3 : n;
 }
 
-template <typename Tin, int DK, int BV, bool DIAG>
+template <typename Tin, int DK, int BV, bool DIAG, bool NOQP = false>
 struct ScanSmem {
-  static constexpr int NSLOT = scan_nslot<Tin, DK, BV, DIAG>();
-  ScanSlot<Tin, DK, BV, DIAG> slot[NSLOT];
+  static constexpr int NSLOT = scan_nslot<Tin, DK, BV, DIAG, NOQP>();
+  ScanSlot<Tin, DK, BV, DIAG, NOQP> slot[NSLOT];
 };
 
 // Buffer-load-to-LDS instructions per chunk (each moves 64 lanes x 16 bytes).
-template <typename Tin, int DK, typename SHP, bool DIAG>
+template <typename Tin, int DK, typename SHP, bool DIAG, bool NOQP>
 struct DmaPlan {
   static constexpr int ES = sizeof(Tin);
   static constexpr int NK = kChunk * DK * ES / 1024;                 // per K (and per Q) tile
   static constexpr int NTC = tpc_bytes<Tin>() / 1024;               // per compact T or P tile
   static constexpr int NV = kChunk * SHP::BV * ES / 1024;            // value slice
   // per producer wave: an equal share of every tile and of the 768-byte decay block, and
-  // under diagonal gating of the K o exp(G_last - G) tile and of exp(G_last)
+  // under diagonal gating of the K o exp(G_last - G) tile and of exp(G_last); the map mode
+  // stages no Q and no P
+  // T pieces per wave: the map mode stages T alone, NTC pieces over the producer waves, the
+  // last round repeating earlier pieces so that every wave issues the same count
+  static constexpr int NTW = NOQP ? (NTC + SHP::NP - 1) / SHP::NP : 2 * NTC / SHP::NP;
   static constexpr int PER_WAVE =
-      (2 * NK + 2 * NTC + NV) / SHP::NP + 1 + (DIAG ? NK / SHP::NP + 1 : 0);
+      ((NOQP ? 1 : 2) * NK + NV) / SHP::NP + NTW + 1 + (DIAG ? NK / SHP::NP + 1 : 0);
   static_assert(NK % SHP::NP == 0 && (2 * NTC) % SHP::NP == 0 && NV % SHP::NP == 0 &&
                     768 % (16 * SHP::NP) == 0 && (DK * 4) % (16 * SHP::NP) == 0,
                 "tiles split over the producer waves");
 };
 
 // One workgroup fills a CU's LDS; its waves run at most two to a SIMD.
-template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES>
+//
+// MODE kScanSeq: a workgroup per (sequence, head, column slice), sequences from the tables.
+// MODE kScanMap / kScanSeg: the two phases of the two-level scan of equal-length sequences
+// (SegArgs): a workgroup per (segment, head, column slice).  kScanMap runs segments
+// 0 .. G-2 of each sequence with no outputs on a state of dv + d_k columns: the first dv
+// start from zero (segment 0: from S0) and take the values, so they end as the segment's
+// N_g = S_out(S_in = 0); the last d_k start from the identity and take zero values, so they
+// end as the segment's transition M_g (Eq. (9) makes S_out affine in S_in:
+// S_out = M_g S_in + N_g).  kScanSeg runs every segment from its true incoming state (S0
+// for segment 0, sa.Sin for the others) with the outputs, and stores S_T from the last one.
+template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES, int MODE>
 __global__ __launch_bounds__(SHP::THREADS)
-__attribute__((amdgpu_waves_per_eu(SHP::THREADS > 256 ? 2 : 1, SHP::THREADS > 256 ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu(SHP::THREADS > 256 || MODE == kScanMap ? 2 : 1,
+                                    SHP::THREADS > 256 || MODE == kScanMap ? 2 : 1)))
 void kla_scan_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ GD, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
     const float *S0, Tin *__restrict__ o, float *S_T, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int n_seq, int H, int DV, const Tin *__restrict__ KG,
     const Tin *__restrict__ QG, const Tin *__restrict__ KD, const float *__restrict__ GC,
-    Tin *__restrict__ SN) {
+    Tin *__restrict__ SN, SegArgs sa) {
   constexpr int kBV = SHP::BV, kConsumers = SHP::NC, kScanThreads = SHP::THREADS;
-  using SM = ScanSmem<Tin, DK, kBV, DIAG>;
-  using SL = ScanSlot<Tin, DK, kBV, DIAG>;
-  using DP = DmaPlan<Tin, DK, SHP, DIAG>;
+  constexpr bool MAP = MODE == kScanMap;
+  using SM = ScanSmem<Tin, DK, kBV, DIAG, MAP>;
+  using SL = ScanSlot<Tin, DK, kBV, DIAG, MAP>;
+  using DP = DmaPlan<Tin, DK, SHP, DIAG, MAP>;
   using FragT = typename Frag<Tin>::type;
   using KQ = std::integral_constant<int, DK>;
   constexpr bool B16 = sizeof(Tin) == 2;
@@ -134,13 +153,30 @@ void kla_scan_kernel(
   const int nblk = gridDim.x, b = blockIdx.x;
   const int pidx = (nblk % 8 == 0) ? (b % 8) * (nblk / 8) + b / 8 : b;
   const int slice = pidx % nsl, sh = pidx / nsl;
-  const int h = sh % H, n = sh / H;
+  const int h = sh % H, n = sh / H;  // n: the sequence, or the unit of the two-level scan
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kg = lane >> 4;
   const bool consumer = wid < kConsumers;
   const int v0 = slice * kBV;
-  const int tb = cu[n], te = cu[n + 1];
-  const int cbase = chunk_off[n];
+  // the token range and first global chunk of this workgroup's sequence or segment; VR is the
+  // row length of the values and outputs (the state may be wider in the map mode)
+  int tb, te, cbase, VR = DV;
+  [[maybe_unused]] int seq = n, seg = 0;
+  if constexpr (MODE == kScanSeq) {
+    tb = cu[n];
+    te = cu[n + 1];
+    cbase = chunk_off[n];
+  } else {
+    const int per = MODE == kScanMap ? sa.G - 1 : sa.G;
+    seq = n / per;
+    seg = n % per;
+    tb = seq * sa.L + seg * sa.Ls;
+    te = min(tb + sa.Ls, (seq + 1) * sa.L);
+    cbase = seq * ((sa.L + kChunk - 1) / kChunk) + seg * (sa.Ls / kChunk);
+    VR = sa.dv;
+    // segment 0 starts from S0 and needs no transition: its identity columns have no work
+    if (MAP && seg == 0 && v0 >= sa.dv) return;
+  }
   const int nchunks = (te - tb + kChunk - 1) / kChunk;
 
   // Zero the slots once, so a tile row that the range check drops holds zeros or an
@@ -180,7 +216,7 @@ void kla_scan_kernel(
 #pragma unroll
     for (int j = 0; j < DP::NV / NP; ++j) {
       const int J = NP * j + pw, row = (1024 * J + 16 * lane) / (kBV * ES);
-      offV[j] = dma_off(J, kBV, H * DV * ES, sw_val<kBV>(row) * (ES / 2));
+      offV[j] = dma_off(J, kBV, H * VR * ES, sw_val<kBV>(row) * (ES / 2));
     }
   }
   // issue this wave's half of every load of chunk c into slot s
@@ -195,8 +231,10 @@ void kla_scan_kernel(
                          : make_rsrc(k + tok * DK, kq_bytes);
     const Rsrc rq = DIAG ? make_rsrc(QG + ch * (kChunk * DK), kChunk * DK * ES)
                          : make_rsrc(q + tok * DK, kq_bytes);
-    const Rsrc rv =
-        make_rsrc(v + tok * DV + v0, (uint32_t)(((size_t)(len - 1) * H * DV + kBV) * ES));
+    // value slice (the identity columns of the map mode take zero values: an empty range)
+    const bool vcols = !MAP || v0 < VR;
+    const Rsrc rv = make_rsrc(v + tok * VR + (vcols ? v0 : 0),
+                              vcols ? (uint32_t)(((size_t)(len - 1) * H * VR + kBV) * ES) : 0u);
     const Rsrc rt = make_rsrc(Tm + ch * kTpbElems, tpb_bytes<Tin>());
     const Rsrc rp = make_rsrc(Pm + ch * kTpbElems, tpb_bytes<Tin>());
     const Rsrc rg = make_rsrc(GD + ch * kGDFloats, kGDFloats * sizeof(float));
@@ -204,12 +242,12 @@ void kla_scan_kernel(
     for (int j = 0; j < DP::NK / NP; ++j) {
       const int J = NP * j + pw;
       dma16(rk, s.K + 1024 * J, offK[j]);
-      dma16(rq, s.Q + 1024 * J, offK[j]);
+      if constexpr (!MAP) dma16(rq, s.Q + 1024 * J, offK[j]);
     }
 #pragma unroll
-    for (int j = 0; j < 2 * DP::NTC / NP; ++j) {
+    for (int j = 0; j < DP::NTW; ++j) {
       const int m = NP * j + pw;
-      if (m < DP::NTC) dma16(rt, s.T + 1024 * m, offTP[j]);
+      if (MAP || m < DP::NTC) dma16(rt, s.T + 1024 * (m % DP::NTC), offTP[j]);
       else dma16(rp, s.P + 1024 * (m - DP::NTC), offTP[j]);
     }
 #pragma unroll
@@ -217,9 +255,9 @@ void kla_scan_kernel(
       const int J = NP * j + pw;
       dma16(rv, s.V + 1024 * J, offV[j]);
     }
-    // decays (gam, dec, gamO are consecutive in the slot, 768 bytes): producer pw fetches
-    // its 768 / NP bytes
-    constexpr int GDB = 768 / NP;
+    // decays (gam, dec, gamO are consecutive in the slot, 768 bytes; the map mode takes the
+    // first 512): producer pw fetches its share
+    constexpr int GDB = (MAP ? 512 : 768) / NP;
     if (lane < GDB / 16)
       dma16(rg, reinterpret_cast<unsigned char *>(s.gam) + GDB * pw, GDB * pw + 16 * lane);
     if constexpr (DIAG) {
@@ -239,6 +277,7 @@ void kla_scan_kernel(
   constexpr int PPR = kBV * ES / 16;                     // 16-byte pieces per value-tile row
   constexpr int NST = kChunk * PPR / (64 * NP);          // store instructions per producer wave
   auto p_flush = [&](int c, const SL &s) {
+    if constexpr (MAP) return;  // no outputs
     const int t0 = tb + c * kChunk;
     const int len = min(kChunk, te - t0);
     const Rsrc ro = make_rsrc(o + ((size_t)t0 * H + h) * DV + v0,
@@ -261,14 +300,27 @@ void kla_scan_kernel(
   const int col = 16 * cw + r16;  // this lane's state column within the slice
   constexpr int NM = DK / 16;     // 16-row state tiles
   constexpr int NKS = DK / 32;    // k-steps over d_k
-  const size_t sbase = ((size_t)n * H + h) * DK * (size_t)DV;
+  const size_t sbase = ((size_t)n * H + h) * DK * (size_t)DV;  // this unit's state (S_T)
+  // element (r, cc) of this workgroup's incoming state
+  auto initial_state = [&](int r, int cc) -> float {
+    if constexpr (MODE == kScanSeq) {
+      return S0 ? S0[sbase + (size_t)r * DV + cc] : 0.f;
+    } else {
+      const size_t seq_base = ((size_t)seq * H + h) * DK * (size_t)VR;
+      if (MODE == kScanMap && cc >= VR) return r == cc - VR ? 1.f : 0.f;  // identity columns
+      if (seg == 0) return S0 ? S0[seq_base + (size_t)r * VR + cc] : 0.f;
+      if (MODE == kScanMap) return 0.f;  // N_g starts from zero
+      return sa.Sin[(((size_t)seq * (sa.G - 1) + seg - 1) * H + h) * DK * (size_t)VR +
+                    (size_t)r * VR + cc];
+    }
+  };
   f32x4 Sacc[NM];
   if (consumer) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        Sacc[m][i] = S0 ? S0[sbase + (size_t)tmap(m, kg, i) * DV + v0 + col] : 0.f;
+        Sacc[m][i] = initial_state(tmap(m, kg, i), v0 + col);
   }
   // row of this lane's A/B operand fragments in 16-row tile t
   auto frow = [&](int t) { return tmap(t, r16 >> 2, r16 & 3); };
@@ -326,7 +378,7 @@ void kla_scan_kernel(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         fk[t][ks] = rd_frag(s.K, KQ{}, frow(t), ks);
-        fq[t][ks] = rd_frag(s.Q, KQ{}, frow(t), ks);
+        if constexpr (!MAP) fq[t][ks] = rd_frag(s.Q, KQ{}, frow(t), ks);
       }
     // ---- reads for R = V - Diag(gam) Y and U = T R
     FragT ft[6];
@@ -397,8 +449,10 @@ void kla_scan_kernel(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         OT[t] = zero4();
+        if constexpr (!MAP) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) OT[t] = mma(Sop[ks], fq[t][ks], OT[t]);
+          for (int ks = 0; ks < NKS; ++ks) OT[t] = mma(Sop[ks], fq[t][ks], OT[t]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) R[t][i] = vv[t][i] - g4[t][i] * Y[t][i];
       }
@@ -418,17 +472,20 @@ void kla_scan_kernel(
       Udop[0] = accB(Ud[0], Ud[1]);
       Udop[1] = accB(Ud[2], Ud[3]);
     }
-    // ---- reads for the output: P fragments and this lane's token decays
+    // ---- reads for the output: P fragments and this lane's token decays (none in the map
+    //      mode)
     FragT fp[6];
-    fp[0] = rd_tp(s.P, frow(0), 0);
-    fp[1] = rd_tp(s.P, frow(1), 0);
-    fp[2] = rd_tp(s.P, frow(2), 0);
-    fp[3] = rd_tp(s.P, frow(2), 1);
-    fp[4] = rd_tp(s.P, frow(3), 0);
-    fp[5] = rd_tp(s.P, frow(3), 1);
     float gt[4];
+    if constexpr (!MAP) {
+      fp[0] = rd_tp(s.P, frow(0), 0);
+      fp[1] = rd_tp(s.P, frow(1), 0);
+      fp[2] = rd_tp(s.P, frow(2), 0);
+      fp[3] = rd_tp(s.P, frow(2), 1);
+      fp[4] = rd_tp(s.P, frow(3), 0);
+      fp[5] = rd_tp(s.P, frow(3), 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) gt[t] = s.gamO[frow(t)];
+      for (int t = 0; t < 4; ++t) gt[t] = s.gamO[frow(t)];
+    }
     // ---- S = exp(G_last) S + K^T Diag(dec) U
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
@@ -439,6 +496,7 @@ void kla_scan_kernel(
       Sacc[m] = mma(fkt[m][0], Udop[0], Sacc[m]);
       Sacc[m] = mma(fkt[m][1], Udop[1], Sacc[m]);
     }
+    if constexpr (!MAP) {
     // ---- O^T = Diag(gam) (Q S)^T + U^T P^T: lane (r16, kg) holds token frow(t), columns
     //      16 cw + 4 kg .. + 3 of this slice.  The block is parked in this wavefront's own
     //      columns of the value tile (read above, and read by no other wavefront); the
@@ -464,6 +522,7 @@ void kla_scan_kernel(
           *reinterpret_cast<f32x4 *>(dst) = O;
         }
       }
+    }
     }
   };
 
@@ -525,22 +584,34 @@ void kla_scan_kernel(
     }
   }
 
-  if (consumer && S_T) {
+  // the final state: of the sequence, of the map mode's segment ([N_g | M_g]), or of the
+  // segment mode's last segment of each sequence
+  bool store_st = consumer && S_T;
+  size_t st_base = sbase;
+  if constexpr (MODE == kScanSeg) {
+    store_st = store_st && seg == sa.G - 1;
+    st_base = ((size_t)seq * H + h) * DK * (size_t)DV;
+  }
+  if (store_st) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S_T[sbase + (size_t)tmap(m, kg, i) * DV + v0 + col] = Sacc[m][i];
+        S_T[st_base + (size_t)tmap(m, kg, i) * DV + v0 + col] = Sacc[m][i];
   }
 }
 
-template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES>
-static hipError_t launch_scan_s(int d_v, const void *q, const void *k, const void *v,
-                                const float *GD, const void *T, const void *P, const float *S0,
-                                void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream, const DiagTiles *dg, void *SN) {
-  using SMT = ScanSmem<Tin, DK, SHP::BV, DIAG>;
-  using SLT = ScanSlot<Tin, DK, SHP::BV, DIAG>;
+// units: sequences (kScanSeq) or segments; DVs: the state's column count (d_v, or
+// d_v + d_k in the map mode).
+template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES, int MODE>
+static hipError_t launch_scan_s(int DVs, int64_t units, const void *q, const void *k,
+                                const void *v, const float *GD, const void *T, const void *P,
+                                const float *S0, void *o, float *S_T, SeqTables t, int32_t H,
+                                hipStream_t stream, const DiagTiles *dg, void *SN,
+                                const SegArgs &sa) {
+  constexpr bool MAP = MODE == kScanMap;
+  using SMT = ScanSmem<Tin, DK, SHP::BV, DIAG, MAP>;
+  using SLT = ScanSlot<Tin, DK, SHP::BV, DIAG, MAP>;
   static_assert(sizeof(SMT) <= kLdsBytes, "LDS budget");
   static_assert(offsetof(SLT, dec) == offsetof(SLT, gam) + 256 &&
                     offsetof(SLT, gamO) == offsetof(SLT, gam) + 512,
@@ -548,23 +619,24 @@ static hipError_t launch_scan_s(int d_v, const void *q, const void *k, const voi
   const size_t smem = sizeof(SMT);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP, DIAG, STATES>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP, DIAG, STATES, MODE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t blocks = (int64_t)n_seq * H * (d_v / SHP::BV);
+  const int64_t blocks = units * H * (DVs / SHP::BV);
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK, SHP, DIAG, STATES>), dim3((unsigned)blocks),
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK, SHP, DIAG, STATES, MODE>), dim3((unsigned)blocks),
                      dim3(SHP::THREADS), smem, stream, static_cast<const Tin *>(q),
                      static_cast<const Tin *>(k), static_cast<const Tin *>(v), GD,
                      static_cast<const Tin *>(T), static_cast<const Tin *>(P), S0,
-                     static_cast<Tin *>(o), S_T, t.cu, t.chunk_off, n_seq, H, d_v,
+                     static_cast<Tin *>(o), S_T, t.cu, t.chunk_off, (int)units, H, DVs,
                      static_cast<const Tin *>(dg ? dg->kg : nullptr),
                      static_cast<const Tin *>(dg ? dg->qg : nullptr),
                      static_cast<const Tin *>(dg ? dg->kd : nullptr), dg ? dg->gc : nullptr,
-                     static_cast<Tin *>(SN));
+                     static_cast<Tin *>(SN), sa);
   return hipGetLastError();
 }
 
@@ -585,18 +657,24 @@ static int device_cus() {
 // The narrow shape while its grid fits the chip in one wave of workgroups (more of them
 // would only queue behind each other while their staging traffic adds up); the wide shape,
 // which stages each tile once for 64 columns, beyond that.
-template <typename Tin, int DK, bool DIAG, bool STATES>
-static hipError_t launch_scan_t(int d_v, const void *q, const void *k, const void *v,
-                                const float *GD, const void *T, const void *P, const float *S0,
-                                void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
-                                hipStream_t stream, const DiagTiles *dg, void *SN) {
-  const int64_t narrow_blocks = (int64_t)n_seq * H * (d_v / ScanNarrow::BV);
-  const int cus = device_cus();
-  if (cus > 0 && narrow_blocks > cus)
-    return launch_scan_s<Tin, DK, ScanWide, DIAG, STATES>(d_v, q, k, v, GD, T, P, S0, o, S_T, t,
-                                                          n_seq, H, stream, dg, SN);
-  return launch_scan_s<Tin, DK, ScanNarrow, DIAG, STATES>(d_v, q, k, v, GD, T, P, S0, o, S_T, t,
-                                                          n_seq, H, stream, dg, SN);
+template <typename Tin, int DK, bool DIAG, bool STATES, int MODE = kScanSeq>
+static hipError_t launch_scan_t(int DVs, int64_t units, const void *q, const void *k,
+                                const void *v, const float *GD, const void *T, const void *P,
+                                const float *S0, void *o, float *S_T, SeqTables t, int32_t H,
+                                hipStream_t stream, const DiagTiles *dg, void *SN,
+                                const SegArgs &sa = SegArgs{}) {
+  const int64_t narrow_blocks = units * H * (DVs / ScanNarrow::BV);
+  // workgroups of the narrow shape per CU: one, or in the map mode (two waves per SIMD) as
+  // many as the LDS holds, at most two
+  constexpr int lds_fit =
+      kLdsBytes / (int)sizeof(ScanSmem<Tin, DK, ScanNarrow::BV, DIAG, MODE == kScanMap>);
+  constexpr int per_cu = MODE == kScanMap ? (lds_fit >= 2 ? 2 : 1) : 1;
+  const int64_t fit = (int64_t)device_cus() * per_cu;
+  if (fit > 0 && narrow_blocks > fit)
+    return launch_scan_s<Tin, DK, ScanWide, DIAG, STATES, MODE>(DVs, units, q, k, v, GD, T, P, S0,
+                                                                o, S_T, t, H, stream, dg, SN, sa);
+  return launch_scan_s<Tin, DK, ScanNarrow, DIAG, STATES, MODE>(DVs, units, q, k, v, GD, T, P, S0,
+                                                                o, S_T, t, H, stream, dg, SN, sa);
 }
 
 template <typename Tin, int DK>
@@ -606,13 +684,13 @@ static hipError_t launch_scan_g(int d_v, const void *q, const void *k, const voi
                                 hipStream_t stream, const DiagTiles *dg, void *SN) {
   if (dg) {
     if (SN) return hipErrorInvalidValue;  // no stored states under diagonal gating
-    return launch_scan_t<Tin, DK, true, false>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
+    return launch_scan_t<Tin, DK, true, false>(d_v, n_seq, q, k, v, GD, T, P, S0, o, S_T, t, H,
                                                stream, dg, nullptr);
   }
   if (SN)
-    return launch_scan_t<Tin, DK, false, true>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
+    return launch_scan_t<Tin, DK, false, true>(d_v, n_seq, q, k, v, GD, T, P, S0, o, S_T, t, H,
                                                stream, nullptr, SN);
-  return launch_scan_t<Tin, DK, false, false>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H,
+  return launch_scan_t<Tin, DK, false, false>(d_v, n_seq, q, k, v, GD, T, P, S0, o, S_T, t, H,
                                               stream, nullptr, nullptr);
 }
 
@@ -632,6 +710,131 @@ hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k,
                                      dg, SN);
   return launch_scan_g<float, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream, dg,
                                   SN);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The two-level scan's middle phase, sequential over the segments of each sequence: the map
+// mode left, per (sequence, segment g < G - 1, head), [N_g | M_g] (d_k x (d_v + d_k)) with
+// N_0 = S_out of segment 0 from S0; so the incoming states are S_in(1) = N_0 and
+// S_in(g + 1) = M_g S_in(g) + N_g (Eq. (9): S_out is affine in S_in), in fp32 on the matrix
+// cores (fp32 16x16x4 steps: exact products).  One workgroup of four wavefronts per
+// (sequence, head, 16 state columns); wavefront w forms rows [d_k/4 w, d_k/4 (w + 1)).  The
+// contraction over the d_k rows of S_in is ordered so that lane group kg takes the rows
+// [d_k/4 kg, d_k/4 (kg + 1)): each lane then reads a contiguous run of M_g's row from memory,
+// and S_in sits in LDS with row k at position 4 (k mod d_k/4) + k div d_k/4, so that the
+// four lane groups of one step read four consecutive rows.
+// ---------------------------------------------------------------------------------------------
+template <int DK>
+__global__ __launch_bounds__(256) void kla_seg_combine_kernel(const float *__restrict__ NM,
+                                                              float *__restrict__ Sin, int G,
+                                                              int H, int dv) {
+  constexpr int KS = DK / 4;   // contraction steps; also rows per wavefront
+  constexpr int TW = KS / 16;  // 16-row output tiles per wavefront
+  constexpr int NF = KS / 4;   // float4 pieces of a lane's run of M_g's row
+  __shared__ __align__(16) float Ss[DK * 16];
+  const int nsl = dv / 16;
+  const int slice = blockIdx.x % nsl, sh = blockIdx.x / nsl;
+  const int h = sh % H, n = sh / H;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
+  const int W = dv + DK, c0 = 16 * slice;
+  auto nm = [&](int g) { return NM + (((size_t)n * (G - 1) + g) * H + h) * DK * (size_t)W; };
+  auto sin_ = [&](int g) { return Sin + (((size_t)n * (G - 1) + g) * H + h) * DK * (size_t)dv; };
+  auto pos = [](int k) { return 16 * (4 * (k % KS) + k / KS); };
+  {
+    const float *N0 = nm(0);
+    float *S1 = sin_(0);
+    for (int e = tid; e < DK * 16; e += 256) {
+      const int r = e >> 4, cc = e & 15;
+      const float x = N0[(size_t)r * W + c0 + cc];
+      Ss[pos(r) + cc] = x;
+      S1[(size_t)r * dv + c0 + cc] = x;
+    }
+  }
+  // this lane's operands of step g: M_g[row][KS kg .. + KS) for the rows of its tiles, and
+  // the N_g entries its accumulators start from
+  f32x4 A[TW][NF], Nv[TW];
+  auto load = [&](int g) {
+    const float *b = nm(g);
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      const int row = KS * w + 16 * t + r16;
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        A[t][j] = *reinterpret_cast<const f32x4 *>(b + (size_t)row * W + dv + KS * kg + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Nv[t][e] = b[(size_t)(KS * w + 16 * t + 4 * kg + e) * W + c0 + r16];
+    }
+  };
+  if (G > 2) load(1);
+  for (int g = 1; g + 1 < G; ++g) {
+    f32x4 Ac[TW][NF], acc[TW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      acc[t] = Nv[t];
+#pragma unroll
+      for (int j = 0; j < NF; ++j) Ac[t][j] = A[t][j];
+    }
+    if (g + 2 < G) load(g + 1);  // the next step's operands load while this one runs
+    __syncthreads();              // Ss holds S_in(g)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float bv = Ss[16 * (4 * s + kg) + r16];
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ac[t][s >> 2][s & 3], bv, acc[t], 0, 0, 0);
+    }
+    __syncthreads();  // every read of S_in(g) is done
+    float *So = sin_(g);
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = KS * w + 16 * t + 4 * kg + e;
+        Ss[pos(row) + r16] = acc[t][e];
+        So[(size_t)row * dv + c0 + r16] = acc[t][e];
+      }
+  }
+}
+
+template <typename Tin, int DK>
+static hipError_t launch_two_level_t(int d_v, const void *q, const void *k, const void *v,
+                                     const float *GD, const void *T, const void *P,
+                                     const float *S0, void *o, float *S_T, int32_t n_seq,
+                                     int32_t H, const SegArgs &sa0, float *NM, float *Sin,
+                                     hipStream_t stream) {
+  const SeqTables none{nullptr, nullptr};
+  SegArgs sa = sa0;
+  sa.Sin = Sin;
+  hipError_t e = launch_scan_t<Tin, DK, false, false, kScanMap>(
+      d_v + DK, (int64_t)n_seq * (sa.G - 1), q, k, v, GD, T, P, S0, nullptr, NM, none, H, stream,
+      nullptr, nullptr, sa);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kla_seg_combine_kernel<DK>, dim3((unsigned)(n_seq * H * (d_v / 16))),
+                     dim3(256), 0, stream, NM, Sin, sa.G, H, d_v);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_scan_t<Tin, DK, false, false, kScanSeg>(d_v, (int64_t)n_seq * sa.G, q, k, v, GD,
+                                                        T, P, S0, o, S_T, none, H, stream, nullptr,
+                                                        nullptr, sa);
+}
+
+hipError_t launch_scan_two_level(Dtype dt, int d_k, int d_v, const void *q, const void *k,
+                                 const void *v, const float *GD, const void *T, const void *P,
+                                 const float *S0, void *o, float *S_T, int32_t n_seq, int32_t H,
+                                 const SegArgs &sa, float *NM, float *Sin, hipStream_t stream) {
+  if (sa.G < 2 || sa.Ls <= 0 || sa.Ls % kChunk != 0 || sa.dv != d_v) return hipErrorInvalidValue;
+  if (dt == Dtype::BF16) {
+    if (d_k == 128)
+      return launch_two_level_t<__bf16, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, n_seq, H, sa, NM,
+                                             Sin, stream);
+    return launch_two_level_t<__bf16, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, n_seq, H, sa, NM,
+                                          Sin, stream);
+  }
+  if (d_k == 128)
+    return launch_two_level_t<float, 128>(d_v, q, k, v, GD, T, P, S0, o, S_T, n_seq, H, sa, NM,
+                                          Sin, stream);
+  return launch_two_level_t<float, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, n_seq, H, sa, NM, Sin,
+                                       stream);
 }
 
 }  // namespace kla

@@ -71,7 +71,9 @@ typedef enum kla_dtype {
  * element type (an upper bound valid for any cu_seqlens with these totals).  Per
  * 64-token chunk and head it holds the chunk's T and P (Eq. (7)-(8)) as their ten
  * 16 x 16 blocks on and below the diagonal in the element type, and 768 bytes of
- * decay factors.  Returns 0 for an unsupported or invalid size or dtype. */
+ * decay factors; for dense input of few long sequences, also the scratch of the
+ * two-level scan (kla_options.scan_segments).  Returns 0 for an unsupported or
+ * invalid size or dtype. */
 size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
                                    int32_t d_k, int32_t d_v, kla_dtype dtype);
 
@@ -227,11 +229,26 @@ typedef struct kla_options {
   int32_t normalize_q;        /* nonzero: divide each readout by ||q_t||_2 */
   const int32_t *pos_offset;  /* device, 4-byte aligned, or NULL */
   int32_t diagonal_gate;      /* nonzero: g is per key channel, shaped like k */
+  /* kla_prefill_chunked_ex's chunk scan over dense input (cu_seqlens NULL) with a
+   * scalar gate: 0 picks by shape, 1 forces the sequential scan, G >= 2 the
+   * two-level scan with (at most) G segments per sequence.  The two-level scan
+   * runs segments 1..G-1 of every sequence from a zero state and from the
+   * identity (their outputs unused; only their final states [N_g | M_g], with
+   * S_out = M_g S_in + N_g since the chunk update is affine in the state,
+   * Eq. (9)), chains the incoming states of the segments in fp32, then runs every
+   * segment again from its true incoming state.  It does three times the
+   * arithmetic for G-fold parallelism; the shape rule takes it when
+   * n_seq * n_heads * d_v / 32 <= 128 (at most half of 256 compute units busy)
+   * and each sequence has at least 64 chunks: G = min(512 / (n_seq * n_heads *
+   * d_v / 32), chunks per sequence / 32).  Ignored elsewhere. */
+  int32_t scan_segments;
 } kla_options;
 
 /* kla_prefill_workspace_bytes for the variant that opts selects (NULL = the
  * defaults, the same value as kla_prefill_workspace_bytes); 0 for unsupported
- * sizes. */
+ * sizes.  Where total_tokens is a multiple of n_seq and the shape (or
+ * scan_segments) selects the two-level scan, the size includes its fp32 scratch:
+ * n_seq (G - 1) n_heads d_k (2 d_v + d_k) floats. */
 size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
                                       int32_t d_k, int32_t d_v, kla_dtype dtype,
                                       const kla_options *opts);

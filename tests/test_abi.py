@@ -68,6 +68,39 @@ def test_workspace_bytes_formula(lib):
     assert lib.kla_prefill_workspace_bytes(4, 100, 16, 128, 128, 7) == 0  # unknown dtype
 
 
+def test_workspace_two_level_scratch(lib):
+    """Dense input of few long sequences adds the two-level scan's fp32 scratch: per
+    (sequence, segment but the last, head) [N_g | M_g] ([d_k][d_v + d_k]) and the chained
+    incoming state ([d_k][d_v]).  The shape rule: n_seq H d_v / 32 workgroups of the
+    sequential scan below 128 and G = min(512 / that, chunks per sequence / 32)."""
+    pad = lambda x: (x + 255) // 256 * 256
+    n_seq, n_tok, H, dk, dv = 1, 65536, 16, 128, 128
+    seq = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, scan_segments=1)
+    G = min(512 // (n_seq * H * dv // 32), (n_tok // 64) // 32)
+    assert G == 8
+    units = n_seq * (G - 1) * H * dk
+    want = seq + pad(4 * units * (dv + dk)) + pad(4 * units * dv)
+    assert kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv) == want
+    assert kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, scan_segments=8) == want
+    # an explicit count: segments of ceil(chunks / G) chunks, G recounted over what holds tokens
+    units7 = n_seq * 6 * H * dk
+    assert (kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, scan_segments=7)
+            == seq + pad(4 * units7 * (dv + dk)) + pad(4 * units7 * dv))
+    # 5 chunks in 4 requested segments: 2 chunks each, so 3 segments
+    units3 = 1 * 2 * H * dk
+    assert (kla.kla_prefill_workspace_bytes(1, 300, H, dk, dv, scan_segments=4)
+            == kla.kla_prefill_workspace_bytes(1, 300, H, dk, dv, scan_segments=1)
+            + pad(4 * units3 * (dv + dk)) + pad(4 * units3 * dv))
+    # no scratch: enough sequences to fill the chip, short sequences, uneven totals (packed
+    # input only), the diagonal gate
+    for args in ((4, n_tok, H, dk, dv), (1, 64 * 63, H, dk, dv), (3, 3 * 4096 + 1, 2, dk, dv)):
+        assert (kla.kla_prefill_workspace_bytes(*args)
+                == kla.kla_prefill_workspace_bytes(*args, scan_segments=1)), args
+    assert (kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, diagonal_gate=True)
+            == kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, diagonal_gate=True,
+                                               scan_segments=1))
+
+
 FAKE = 1 << 32  # 16-byte aligned non-NULL addresses 4 GiB apart; never dereferenced on error paths
 
 

@@ -264,6 +264,44 @@ def test_prefill_long_context_full(kla):
     check(ST, So, 2e-2, "ST")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n_seq,T,H,dk,dv,G,S0,weak", [
+    (1, 64 * 9 + 13, 2, 128, 128, 3, True, False),   # ragged last segment
+    (2, 64 * 8, 1, 64, 256, 2, True, False),
+    (1, 64 * 7, 2, 128, 64, 7, False, False),        # one chunk per segment, zero S0
+    (3, 64 * 5 + 1, 2, 64, 64, 4, True, False),      # 3 segments of 2 chunks, one-token tail
+    (1, 64 * 6, 40, 128, 128, 3, True, False),       # enough workgroups for the 64-column shape
+    (1, 64 * 9 + 13, 2, 128, 128, 3, True, True),    # the same without decay and with weak
+    (3, 64 * 5 + 1, 2, 64, 64, 4, True, True),       # writes: the transitions M_g matter
+    (1, 64 * 6, 40, 128, 128, 6, True, True),
+])
+def test_prefill_two_level_scan(kla, dtype, n_seq, T, H, dk, dv, G, S0, weak):
+    """The two-level scan (segments' transitions, chained incoming states, segments rerun)
+    against the oracle and against the sequential scan on the same inputs.  With the
+    workloads' gates a state fades within a few chunks, so the segments' transitions
+    M_g are near zero; weak=True sets g = 0 and eta to 5% of its draw, so that a state
+    carries across whole segments and the chained states depend on M_g."""
+    w = ki.Workload(97, "unit", n_seq, H, dk, dv, dtype, T=T, s0_var=0.01)
+    inp = ki.prefill_inputs(w)
+    if weak:
+        inp["g"] = torch.zeros_like(inp["g"])
+        inp["eta"] = inp["eta"] * 0.05
+    d = to_dev(inp)
+    outs = []
+    for segs in (G, 1):
+        o, ST = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                        S0=d["S0"] if S0 else None, n_seq=n_seq,
+                                        scan_segments=segs)
+        torch.cuda.synchronize()
+        outs.append((o, ST))
+    oo, So = oracle_prefill(d, S0=S0)
+    for (o, ST), name in zip(outs, ("two-level", "sequential")):
+        check(o, oo, TOL[dtype], f"o {name}")
+        check(ST, So, TOL[dtype], f"ST {name}")
+    check(outs[0][0], outs[1][0], TOL[dtype], "o two-level vs sequential")
+    check(outs[0][1], outs[1][1], TOL[dtype], "ST two-level vs sequential")
+
+
 def test_packed_workload_sampled_with_decode(kla):
     """Workload 4 (16 packed sequences of 1024..16384 tokens, H=8, d_v=256, g ~ U(-2,0),
     tiny keys) on the device in full; the oracle checks three sampled sequences, then 8 of
