@@ -306,9 +306,30 @@ def main():
             "bound": "hbm", "achieved": dg_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": dg_gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_step": dg_bytes}
         del wsd, gd
+        # split operand precision (T R, P U and the state update on hi/lo bf16 pairs) on the
+        # headline's keys, with its own larger workspace
+        wss = torch.empty(kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv,
+                                                          precision="split"),
+                          dtype=torch.uint8, device=dev)
+
+        def sstep():
+            kla.kla_prefill_chunked(s0["q"], s0["k"], s0["v"], s0["g"], s0["eta"], base["eps"],
+                                    S0=s0["S0"], n_seq=n_seq, o=s0["o"], S_T=s0["S_T"],
+                                    workspace=wss, precision="split")
+        for _ in range(2):
+            sstep()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.variant_steps):
+            sstep()
+        e1.record()
+        torch.cuda.synchronize()
+        variants["split_precision_ms_per_step"] = e0.elapsed_time(e1) / args.variant_steps
+        del wss
         variants["note"] = ("same workload, one input set (cache-warm, unlike the headline), "
-                            "unit-norm keys; one kla_prefill_chunked call per step; "
-                            "diagonal_gate: g per key channel [n_tok, H, d_k]")
+                            "unit-norm keys (split precision: the headline's keys); one "
+                            "kla_prefill_chunked call per step; diagonal_gate: g per key "
+                            "channel [n_tok, H, d_k]")
         log(f"variants: {variants}")
 
     # backward pass on the same workload: gradients for seeded cotangents dO, dS_T

@@ -117,20 +117,27 @@ BETA_MODES = {"kaczmarz": 0, "gated": 1, "key_norm": 2, "inv_t": 3, "inv_sqrt_t"
 class KlaOptions(ctypes.Structure):
     """Mirror of ``kla_options``: the write-coefficient mode, the normalised readout, the
     per-sequence position offsets (device int32 or NULL), the diagonal gate and the
-    segment count of the two-level scan (0 = by shape, 1 = sequential scan)."""
+    segment count of the two-level scan (0 = by shape, 1 = sequential scan) and the operand
+    precision (PRECISIONS)."""
     _fields_ = [("beta_mode", ctypes.c_int32), ("normalize_q", ctypes.c_int32),
                 ("pos_offset", ctypes.c_void_p), ("diagonal_gate", ctypes.c_int32),
-                ("scan_segments", ctypes.c_int32)]
+                ("scan_segments", ctypes.c_int32), ("precision", ctypes.c_int32)]
+
+
+# Operand precision of the bf16 prefill's products (kla_precision in include/kla.h).
+PRECISIONS = {"bf16": 0, "split": 1}
 
 
 def _options(beta_mode, normalize_q, pos_offset, n_rows, dev, diagonal_gate=False,
-             scan_segments=0):
+             scan_segments=0, precision="bf16"):
     """ctypes pointer to a KlaOptions (None = the defaults).  beta_mode is a name from
     BETA_MODES or its integer code; pos_offset an int32 device tensor of n_rows entries;
-    diagonal_gate: g holds one log-decay per key channel; scan_segments as in kla_options."""
+    diagonal_gate: g holds one log-decay per key channel; scan_segments as in kla_options;
+    precision a name from PRECISIONS or its code."""
     mode = BETA_MODES[beta_mode] if isinstance(beta_mode, str) else int(beta_mode)
+    prec = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
     if (mode == 0 and not normalize_q and pos_offset is None and not diagonal_gate
-            and not scan_segments):
+            and not scan_segments and prec == 0):
         return None
     if pos_offset is not None:
         _need(pos_offset, "pos_offset", torch.int32, dev)
@@ -138,7 +145,7 @@ def _options(beta_mode, normalize_q, pos_offset, n_rows, dev, diagonal_gate=Fals
             raise ValueError(f"pos_offset must have {n_rows} entries")
     return ctypes.pointer(KlaOptions(mode, 1 if normalize_q else 0,
                                      None if pos_offset is None else pos_offset.data_ptr(),
-                                     1 if diagonal_gate else 0, int(scan_segments)))
+                                     1 if diagonal_gate else 0, int(scan_segments), prec))
 
 
 def _check(status: int):
@@ -171,12 +178,14 @@ def _need(t, name, dtype=None, device=None):
 
 def kla_prefill_workspace_bytes(n_seq: int, total_tokens: int, n_heads: int, d_k: int,
                                 d_v: int, dtype=torch.bfloat16, diagonal_gate: bool = False,
-                                scan_segments: int = 0) -> int:
+                                scan_segments: int = 0, precision="bf16") -> int:
     """Workspace bytes a prefill of this size and element type needs (0 for unsupported
-    sizes); diagonal_gate sizes it for the diagonal-gated variant, scan_segments for that
-    choice of the chunk scan (kla_options)."""
-    opts = (ctypes.pointer(KlaOptions(0, 0, None, 1 if diagonal_gate else 0, int(scan_segments)))
-            if diagonal_gate or scan_segments else None)
+    sizes); diagonal_gate sizes it for the diagonal-gated variant, scan_segments and
+    precision for those choices (kla_options)."""
+    prec = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
+    opts = (ctypes.pointer(KlaOptions(0, 0, None, 1 if diagonal_gate else 0, int(scan_segments),
+                                      prec))
+            if diagonal_gate or scan_segments or prec else None)
     return int(load_library().kla_prefill_workspace_bytes_ex(n_seq, total_tokens, n_heads, d_k,
                                                              d_v, _DTYPES[dtype], opts))
 
@@ -201,7 +210,7 @@ def _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq):
 def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=None,
                         n_seq=None, *, cu_seqlens_host=None, output_final_state=True, o=None,
                         S_T=None, workspace=None, beta_mode="kaczmarz", normalize_q=False,
-                        pos_offset=None, scan_segments=0):
+                        pos_offset=None, scan_segments=0, precision="bf16"):
     """Chunkwise KLA prefill (paper section 4, Eq. (7)-(9); chunk = 64 tokens).
 
     q, k: [n_tok, H, d_k] or [B, T, H, d_k] (fp32 or bf16); v like q with d_v;
@@ -212,7 +221,8 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
     output_final_state is False.  Pass S_T=S0 to update the state in place.
     beta_mode / normalize_q / pos_offset select the variants of kla_options; scan_segments
     the chunk scan of dense input (0: by shape, 1: sequential, G >= 2: two-level with G
-    segments per sequence).
+    segments per sequence); precision the operand precision of bf16 products ("bf16" or
+    "split", kla_precision).
     """
     shape_v = v.shape
     q, k, v, g, eta, n_seq = _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq)
@@ -252,7 +262,7 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
         _need(S_T, "S_T", torch.float32, dev)
     lib = load_library()
     opts = _options(beta_mode, normalize_q, pos_offset, n_seq, dev, diagonal_gate=diag,
-                    scan_segments=scan_segments)
+                    scan_segments=scan_segments, precision=precision)
     ws_bytes = int(lib.kla_prefill_workspace_bytes_ex(n_seq, n_tok, H, d_k, d_v, _DTYPES[dt],
                                                       opts))
     if workspace is None or workspace.numel() < ws_bytes:

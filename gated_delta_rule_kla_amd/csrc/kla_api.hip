@@ -70,9 +70,9 @@ struct SegPlan {
   int G = 0, Ls = 0;
 };
 SegPlan seg_plan(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_v, bool diag,
-                 int32_t segs_opt) {
+                 int32_t segs_opt, bool split = false) {
   SegPlan p;
-  if (diag || segs_opt == 1 || segs_opt < 0 || n_seq <= 0 || H <= 0 || d_v < 32 ||
+  if (diag || split || segs_opt == 1 || segs_opt < 0 || n_seq <= 0 || H <= 0 || d_v < 32 ||
       total_tokens <= 0 || total_tokens % n_seq != 0)
     return p;
   const int64_t L = total_tokens / n_seq, cpl = (L + KLA_CHUNK - 1) / KLA_CHUNK;
@@ -93,7 +93,7 @@ SegPlan seg_plan(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_v, bo
 }
 
 WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, size_t es,
-                   bool diag = false, int64_t d_v = 0, int segs = 0) {
+                   bool diag = false, int64_t d_v = 0, int segs = 0, bool split = false) {
   WsLayout w;
   w.off_cu = 0;
   w.off_co = align256(w.off_cu + sizeof(int32_t) * (size_t)(n_seq + 1));
@@ -101,7 +101,8 @@ WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, 
   const int64_t nch = kla::chunk_upper_bound(n_seq, total_tokens);
   w.off_GD = align256(w.off_G + sizeof(float) * (size_t)total_tokens * (size_t)H);
   w.off_T = align256(w.off_GD + sizeof(float) * (size_t)nch * (size_t)H * kla::kGDFloats);
-  const size_t tile_bytes = es * (size_t)nch * (size_t)H * kla::kTpbElems;
+  // split precision: hi and lo blocks per chunk-head
+  const size_t tile_bytes = es * (size_t)nch * (size_t)H * kla::kTpbElems * (split ? 2 : 1);
   w.off_P = align256(w.off_T + tile_bytes);
   w.total = align256(w.off_P + tile_bytes);
   if (diag) {
@@ -172,6 +173,8 @@ kla_status to_coef(const kla_options *opts, kla::CoefOpts *out) {
   if (!opts) return KLA_OK;
   if (opts->beta_mode < KLA_BETA_KACZMARZ || opts->beta_mode > KLA_BETA_INV_LOG_T)
     return fail(KLA_ERR_UNSUPPORTED, "unknown beta_mode %d", (int)opts->beta_mode);
+  if (opts->precision != KLA_PRECISION_BF16 && opts->precision != KLA_PRECISION_SPLIT)
+    return fail(KLA_ERR_UNSUPPORTED, "unknown precision %d", (int)opts->precision);
   if (opts->pos_offset && !aligned_to(opts->pos_offset, 4))
     return fail(KLA_ERR_INVALID_ARGUMENT, "pos_offset must be 4-byte aligned");
   *out = kla::CoefOpts{opts->beta_mode, opts->normalize_q != 0 ? 1 : 0, opts->pos_offset,
@@ -195,9 +198,11 @@ size_t kla_prefill_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens, int32
       !supported_dv(d_v) || (dtype != KLA_DTYPE_F32 && dtype != KLA_DTYPE_BF16))
     return 0;
   const bool diag = opts && opts->diagonal_gate != 0;
+  const bool split = opts && opts->precision == KLA_PRECISION_SPLIT && dtype == KLA_DTYPE_BF16;
   const SegPlan sp =
-      seg_plan(n_seq, total_tokens, n_heads, d_v, diag, opts ? opts->scan_segments : 0);
-  return ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype), diag, d_v, sp.G).total;
+      seg_plan(n_seq, total_tokens, n_heads, d_v, diag, opts ? opts->scan_segments : 0, split);
+  return ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype), diag, d_v, sp.G, split)
+      .total;
 }
 
 size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t n_heads,
@@ -260,7 +265,7 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
                               int32_t n_heads, int32_t d_k, int32_t d_v, kla_dtype dtype,
                               const void *workspace, size_t workspace_bytes, bool need_prep,
                               bool need_scan, bool check_tables = true, bool diag = false,
-                              int segs = 0) {
+                              int segs = 0, bool split = false) {
   kla_status st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v,
                                       dtype, eps);
   if (st != KLA_OK) return st;
@@ -283,7 +288,8 @@ kla_status check_prefill_args(const void *q, const void *k, const void *v, const
   const size_t nS = (size_t)n_seq * n_heads * d_k * d_v * sizeof(float);
   if (S_T && S_T != S0 && overlap(S_T, nS, S0, nS))
     return fail(KLA_ERR_INVALID_ARGUMENT, "S_T may equal S0 but must not partially overlap it");
-  const size_t need = ws_layout(n_seq, total_tokens, n_heads, d_k, es, diag, d_v, segs).total;
+  const size_t need =
+      ws_layout(n_seq, total_tokens, n_heads, d_k, es, diag, d_v, segs, split).total;
   if (!workspace || workspace_bytes < need)
     return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -302,9 +308,9 @@ struct WsViews {
 
 WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
                  int32_t d_k, kla_dtype dtype, bool diag = false, int32_t d_v = 0,
-                 int segs = 0) {
+                 int segs = 0, bool split = false) {
   const WsLayout w =
-      ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype), diag, d_v, segs);
+      ws_layout(n_seq, total_tokens, n_heads, d_k, elem_size(dtype), diag, d_v, segs, split);
   char *ws = static_cast<char *>(workspace);
   WsViews v{{reinterpret_cast<int32_t *>(ws + w.off_cu),
              reinterpret_cast<int32_t *>(ws + w.off_co)},
@@ -338,8 +344,9 @@ kla_status enqueue_prepare_diag(const void *q, const void *k, const float *g, co
 kla_status enqueue_prepare(const void *q, const void *k, const float *g, const float *eta, float eps,
                            const kla::CoefOpts &opts, const int32_t *cu_seqlens, int32_t n_seq,
                            int32_t total_tokens, int32_t n_heads, int32_t d_k, kla_dtype dtype,
-                           void *workspace, hipStream_t s) {
-  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype);
+                           void *workspace, hipStream_t s, bool split = false) {
+  const WsViews wv =
+      ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, false, 0, 0, split);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
   kla::PlanArgs pa{kla::kPlanTables, cu_seqlens, total_tokens};
   if (!cu_seqlens)
@@ -353,7 +360,7 @@ kla_status enqueue_prepare(const void *q, const void *k, const float *g, const f
     return st;
   return hip_status(kla::launch_prep(to_dt(dtype), d_k, q, k, g, eta, eps, opts, wv.tabs, n_seq,
                                      nch_ub, n_heads, nullptr, nullptr, wv.T, false, wv.P, wv.GD,
-                                     pa, s),
+                                     pa, s, split),
                     "prep");
 }
 
@@ -385,13 +392,17 @@ kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, c
   const bool diag = co.diag_gate != 0;
   if (opts && opts->scan_segments < 0)
     return fail(KLA_ERR_INVALID_ARGUMENT, "scan_segments must be >= 0");
+  // split precision matters for bf16 operands only (fp32 ones take exact products)
+  const bool split = opts && opts->precision == KLA_PRECISION_SPLIT && dtype == KLA_DTYPE_BF16;
+  if (split && diag)
+    return fail(KLA_ERR_UNSUPPORTED, "split precision takes the scalar gate only");
   // the workspace is sized for the shape's segmentation whatever cu_seqlens is; the
   // two-level scan itself runs on dense input only
   const SegPlan sp = seg_plan(n_seq, total_tokens, n_heads, d_v, diag,
-                              opts ? opts->scan_segments : 0);
+                              opts ? opts->scan_segments : 0, split);
   if ((st = check_prefill_args(q, k, v, g, eta, eps, S0, o, S_T, cu_seqlens, cu_seqlens_host,
                                n_seq, total_tokens, n_heads, d_k, d_v, dtype, workspace,
-                               workspace_bytes, true, true, true, diag, sp.G)) != KLA_OK)
+                               workspace_bytes, true, true, true, diag, sp.G, split)) != KLA_OK)
     return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear any stale error from unrelated work
@@ -400,9 +411,15 @@ kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, c
                               d_k, dtype, workspace, s);
   else
     st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
-                         dtype, workspace, s);
+                         dtype, workspace, s, split);
   if (st != KLA_OK) return st;
-  if (sp.G >= 2 && !cu_seqlens && total_tokens > 0) {
+  if (split) {
+    const WsViews wv =
+        ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, false, 0, 0, true);
+    st = hip_status(kla::launch_scan_split(d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0, o, S_T,
+                                           wv.tabs, n_seq, n_heads, s),
+                    "scan (split precision)");
+  } else if (sp.G >= 2 && !cu_seqlens && total_tokens > 0) {
     const WsViews wv =
         ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, false, d_v, sp.G);
     kla::SegArgs sa;
@@ -505,6 +522,8 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
   if (st != KLA_OK) return st;
   if (co.diag_gate)
     return fail(KLA_ERR_UNSUPPORTED, "the backward pass takes no diagonal gate");
+  if (opts && opts->precision != KLA_PRECISION_BF16)
+    return fail(KLA_ERR_UNSUPPORTED, "the backward pass takes the bf16 operand precision only");
   if ((st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
                                 eps)) != KLA_OK)
     return st;
@@ -605,6 +624,9 @@ kla_status kla_prefill_prepare_ex(const void *q, const void *k, const float *g,
   if (co.diag_gate)
     return fail(KLA_ERR_UNSUPPORTED,
                 "a diagonal-gated prefill runs through kla_prefill_chunked_ex only");
+  if (opts && opts->precision != KLA_PRECISION_BF16)
+    return fail(KLA_ERR_UNSUPPORTED,
+                "a split-precision prefill runs through kla_prefill_chunked_ex only");
   (void)hipGetLastError();
   if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
                             dtype, workspace, static_cast<hipStream_t>(stream))) != KLA_OK)

@@ -47,12 +47,14 @@ constexpr int kGDFloats = 3 * 64;
 // when t_fp32 is set, else in the operand type (what the scan kernel reads).  With q and
 // P_out given, also P = A o Q K^T per chunk-head (operand type, zero above the diagonal;
 // rows divided by ||q_i|| under the normalised readout).  G_out / beta_out (per token) and
-// GD_out (per chunk-head decay factors) are each optional.
+// GD_out (per chunk-head decay factors) are each optional.  tp_split (bf16, packed): T and
+// P as hi = bf16(x) and lo = bf16(x - hi) blocks, the lo blocks after the hi ones of each
+// chunk-head (twice the packed size).
 hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const float *g,
                        const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                        int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
-                       const PlanArgs &pa, hipStream_t stream);
+                       const PlanArgs &pa, hipStream_t stream, bool tp_split = false);
 
 // Diagonal gating: the decayed key and query tiles per chunk-head ([64][d_k] each, operand
 // type) K o exp(G), Q o exp(G), K o exp(G_last - G), and exp(G_last) ([d_k] fp32).
@@ -83,6 +85,13 @@ hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k,
                        const float *GD, const void *T, const void *P, const float *S0, void *o,
                        float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream,
                        const DiagTiles *diag = nullptr, void *SN = nullptr);
+
+// launch_scan for bf16 operands at split precision (scalar gate): T and P as hi/lo pairs
+// (launch_prep with tp_split), and T R, P U, K^T Diag(dec) U on hi/lo operand pairs.
+hipError_t launch_scan_split(int d_k, int d_v, const void *q, const void *k, const void *v,
+                             const float *GD, const void *T, const void *P, const float *S0,
+                             void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
+                             hipStream_t stream);
 
 // The two-level scan of equal-length sequences (the chunk scan's map, combine and segment
 // phases), for few long sequences: each sequence of L tokens is cut into G segments of Ls

@@ -220,7 +220,7 @@ __device__ __forceinline__ ChunkLoc locate(const Planner &p, int c) {
 // 256 contiguous packed elements, so a store instruction writes whole lines.
 template <typename T>
 __device__ __forceinline__ void out_put(T *dst, bool packed, int row, int col, float a, float b,
-                                        float c, float d) {
+                                        float c, float d, bool split = false) {
   int off;
   if (packed) {
     const int I = row >> 4, J = col >> 4;
@@ -233,6 +233,14 @@ __device__ __forceinline__ void out_put(T *dst, bool packed, int row, int col, f
     bf16x4 x4;
     x4[0] = from_f32<T>(a); x4[1] = from_f32<T>(b); x4[2] = from_f32<T>(c); x4[3] = from_f32<T>(d);
     *reinterpret_cast<bf16x4 *>(dst + off) = x4;
+    if (split) {  // the rounding residuals, one packed tile further on
+      bf16x4 l4;
+      l4[0] = from_f32<T>(a - to_f32(x4[0]));
+      l4[1] = from_f32<T>(b - to_f32(x4[1]));
+      l4[2] = from_f32<T>(c - to_f32(x4[2]));
+      l4[3] = from_f32<T>(d - to_f32(x4[3]));
+      *reinterpret_cast<bf16x4 *>(dst + kTpbElems + off) = l4;
+    }
   } else {
     *reinterpret_cast<f32x4 *>(dst + off) = f32x4{a, b, c, d};
   }
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     const float *__restrict__ eta, float eps, int32_t *__restrict__ cu,
     int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
     float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out,
-    float *__restrict__ GD_out, CoefOpts opts, PlanArgs pa) {
+    float *__restrict__ GD_out, CoefOpts opts, PlanArgs pa, int tp_split) {
   __shared__ PrepSmem sm;
   const Planner pl = make_planner(pa, SeqTables{cu, chunk_off}, n_seq);
   write_tables(pl);
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
   // ---- P = A o Q K^T from the tiles K_j Q_i^T (row 16 i + r16, columns 16 j + 4 kg + e;
   //      zero above the diagonal)
   if (want_p) {
-    Tin *P_task = P_out + (size_t)task * kTpbElems;
+    Tin *P_task = P_out + (size_t)task * (tp_split ? 2 * kTpbElems : kTpbElems);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int prow = 16 * i + r16;
@@ -406,7 +414,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
           const bool keep = (j < i) || (4 * kg + e <= r16);
           pv[e] = exp2_fast(keep ? G2me[i] - Gc[e] : -INFINITY) * accp[e] * rqv[i];
         }
-        out_put<Tin>(P_task, true, prow, j0, pv[0], pv[1], pv[2], pv[3]);
+        out_put<Tin>(P_task, true, prow, j0, pv[0], pv[1], pv[2], pv[3], tp_split != 0);
       }
     }
   }
@@ -414,7 +422,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
   // ---- T = (I + L)^{-1} Diag(b), written as the scan's packed blocks (with the decays) or
   //      in full (the unit-check stage, blocks above the diagonal zero)
   const bool t_packed = GD_out != nullptr;
-  TOut *T_task = T_out + (size_t)task * (t_packed ? kTpbElems : kChunk * kChunk);
+  TOut *T_task =
+      T_out + (size_t)task * (t_packed ? (tp_split ? 2 : 1) * kTpbElems : kChunk * kChunk);
   if (!t_packed) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
   chunk_T<Tin, NKS, false>(
       kf, gd, bme, G2me, sm, [] { lds_barrier(); },
       [&](int row, int col, float a, float b, float c, float d) {
-        out_put<TOut>(T_task, t_packed, row, col, a, b, c, d);
+        out_put<TOut>(T_task, t_packed, row, col, a, b, c, d, tp_split != 0);
       });
 }
 
@@ -434,8 +443,9 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
                                 float eps, const CoefOpts &opts, SeqTables t, int32_t n_seq,
                                 int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out,
                                 void *T_out, bool t_fp32, void *P_out, float *GD_out,
-                                const PlanArgs &pa, hipStream_t stream) {
+                                const PlanArgs &pa, hipStream_t stream, bool tp_split) {
   if (n_chunks_ub <= 0 || H <= 0) return hipSuccess;
+  if (tp_split && (sizeof(Tin) != 2 || t_fp32 || !GD_out)) return hipErrorInvalidValue;
   const int64_t tasks = n_chunks_ub * H;
   if (tasks > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)tasks);
@@ -444,11 +454,12 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
   if (t_fp32 || sizeof(Tin) == 4)
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(64), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts, pa);
+                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts, pa, 0);
   else
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(64), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out, opts, pa);
+                       G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out, opts, pa,
+                       tp_split ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -456,19 +467,19 @@ hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const fl
                        const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                        int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
-                       const PlanArgs &pa, hipStream_t stream) {
+                       const PlanArgs &pa, hipStream_t stream, bool tp_split) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
       return launch_prep_t<__bf16, 128>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
-                                        beta_out, T_out, t_fp32, P_out, GD_out, pa, stream);
+                                        beta_out, T_out, t_fp32, P_out, GD_out, pa, stream, tp_split);
     return launch_prep_t<__bf16, 64>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
-                                     beta_out, T_out, t_fp32, P_out, GD_out, pa, stream);
+                                     beta_out, T_out, t_fp32, P_out, GD_out, pa, stream, tp_split);
   }
   if (d_k == 128)
     return launch_prep_t<float, 128>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
-                                     beta_out, T_out, t_fp32, P_out, GD_out, pa, stream);
+                                     beta_out, T_out, t_fp32, P_out, GD_out, pa, stream, tp_split);
   return launch_prep_t<float, 64>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
-                                  beta_out, T_out, t_fp32, P_out, GD_out, pa, stream);
+                                  beta_out, T_out, t_fp32, P_out, GD_out, pa, stream, tp_split);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -61,7 +61,7 @@ using ScanWide = ScanShape<4, 4>;    // 64 columns: K, Q, T, P staged once for t
 constexpr int kLdsBytes = 160 * 1024;
 
 // ---- LDS layout
-template <typename Tin, int DK, int BV, bool DIAG, bool NOQP = false>
+template <typename Tin, int DK, int BV, bool DIAG, bool NOQP = false, bool SPLIT = false>
 struct ScanSlot {
   alignas(16) unsigned char K[kChunk * DK * sizeof(Tin)];  // K, or K o exp(G) (DIAG)
   // Q, or Q o exp(G) (DIAG); not staged by the map mode, which forms no outputs
@@ -77,22 +77,25 @@ struct ScanSlot {
   // diagonal gating: K o exp(G_last - G) for the state update, exp(G_last) per key channel
   alignas(16) unsigned char Kd[DIAG ? kChunk * DK * sizeof(Tin) : 16];
   alignas(16) float gC[DIAG ? DK : 4];
+  // split precision: the low parts of T and P (x - bf16(x), in bf16)
+  alignas(16) unsigned char Tl[SPLIT ? tpc_bytes<Tin>() : 16];
+  alignas(16) unsigned char Pl[SPLIT ? tpc_bytes<Tin>() : 16];
 };
 
-template <typename Tin, int DK, int BV, bool DIAG, bool NOQP>
+template <typename Tin, int DK, int BV, bool DIAG, bool NOQP, bool SPLIT>
 constexpr int scan_nslot() {
-  constexpr int n = kLdsBytes / (int)sizeof(ScanSlot<Tin, DK, BV, DIAG, NOQP>);
+  constexpr int n = kLdsBytes / (int)sizeof(ScanSlot<Tin, DK, BV, DIAG, NOQP, SPLIT>);
   return n >= 3 ? 3 : n;
 }
 
-template <typename Tin, int DK, int BV, bool DIAG, bool NOQP = false>
+template <typename Tin, int DK, int BV, bool DIAG, bool NOQP = false, bool SPLIT = false>
 struct ScanSmem {
-  static constexpr int NSLOT = scan_nslot<Tin, DK, BV, DIAG, NOQP>();
-  ScanSlot<Tin, DK, BV, DIAG, NOQP> slot[NSLOT];
+  static constexpr int NSLOT = scan_nslot<Tin, DK, BV, DIAG, NOQP, SPLIT>();
+  ScanSlot<Tin, DK, BV, DIAG, NOQP, SPLIT> slot[NSLOT];
 };
 
 // Buffer-load-to-LDS instructions per chunk (each moves 64 lanes x 16 bytes).
-template <typename Tin, int DK, typename SHP, bool DIAG, bool NOQP>
+template <typename Tin, int DK, typename SHP, bool DIAG, bool NOQP, bool SPLIT = false>
 struct DmaPlan {
   static constexpr int ES = sizeof(Tin);
   static constexpr int NK = kChunk * DK * ES / 1024;                 // per K (and per Q) tile
@@ -102,8 +105,10 @@ struct DmaPlan {
   // under diagonal gating of the K o exp(G_last - G) tile and of exp(G_last); the map mode
   // stages no Q and no P
   // T pieces per wave: the map mode stages T alone, NTC pieces over the producer waves, the
-  // last round repeating earlier pieces so that every wave issues the same count
-  static constexpr int NTW = NOQP ? (NTC + SHP::NP - 1) / SHP::NP : 2 * NTC / SHP::NP;
+  // last round repeating earlier pieces so that every wave issues the same count; split
+  // precision stages T, P and their low parts
+  static constexpr int NTW =
+      NOQP ? (NTC + SHP::NP - 1) / SHP::NP : (SPLIT ? 4 : 2) * NTC / SHP::NP;
   static constexpr int PER_WAVE =
       ((NOQP ? 1 : 2) * NK + NV) / SHP::NP + NTW + 1 + (DIAG ? NK / SHP::NP + 1 : 0);
   static_assert(NK % SHP::NP == 0 && (2 * NTC) % SHP::NP == 0 && NV % SHP::NP == 0 &&
@@ -122,7 +127,13 @@ struct DmaPlan {
 // end as the segment's transition M_g (Eq. (9) makes S_out affine in S_in:
 // S_out = M_g S_in + N_g).  kScanSeg runs every segment from its true incoming state (S0
 // for segment 0, sa.Sin for the others) with the outputs, and stores S_T from the last one.
-template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES, int MODE>
+//
+// SPLIT (bf16, kScanSeq, scalar gate): the products T R, P U and K^T Diag(dec) U take each
+// rounded operand other than K as a pair of bf16 values, hi = bf16(x) and lo = bf16(x - hi),
+// and sum hi*hi + hi*lo + lo*hi (K is exact in bf16: two terms).  The prep kernel stores T
+// and P as such pairs.  S stays one bf16 operand in K S and Q S.
+template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES, int MODE,
+          bool SPLIT = false>
 __global__ __launch_bounds__(SHP::THREADS)
 __attribute__((amdgpu_waves_per_eu(SHP::THREADS > 256 || MODE == kScanMap ? 2 : 1,
                                     SHP::THREADS > 256 || MODE == kScanMap ? 2 : 1)))
@@ -135,9 +146,11 @@ void kla_scan_kernel(
     Tin *__restrict__ SN, SegArgs sa) {
   constexpr int kBV = SHP::BV, kConsumers = SHP::NC, kScanThreads = SHP::THREADS;
   constexpr bool MAP = MODE == kScanMap;
-  using SM = ScanSmem<Tin, DK, kBV, DIAG, MAP>;
-  using SL = ScanSlot<Tin, DK, kBV, DIAG, MAP>;
-  using DP = DmaPlan<Tin, DK, SHP, DIAG, MAP>;
+  static_assert(!SPLIT || (sizeof(Tin) == 2 && !DIAG && !STATES && MODE == kScanSeq),
+                "split precision: bf16 operands, sequential scalar-gate scan");
+  using SM = ScanSmem<Tin, DK, kBV, DIAG, MAP, SPLIT>;
+  using SL = ScanSlot<Tin, DK, kBV, DIAG, MAP, SPLIT>;
+  using DP = DmaPlan<Tin, DK, SHP, DIAG, MAP, SPLIT>;
   using FragT = typename Frag<Tin>::type;
   using KQ = std::integral_constant<int, DK>;
   constexpr bool B16 = sizeof(Tin) == 2;
@@ -191,7 +204,7 @@ void kla_scan_kernel(
   // unit pu ^ sw(r) of that row.
   const int pw = wid - kConsumers;
   constexpr int NP = SHP::NP;
-  int offK[DP::NK / NP], offTP[2 * DP::NTC / NP], offV[DP::NV / NP];
+  int offK[DP::NK / NP], offTP[DP::NTW], offV[DP::NV / NP];
   auto dma_off = [&](int J, int row_elems, int gstride_bytes, int sw_of_row) {
     const int pbyte = 1024 * J + 16 * lane, rowb = row_elems * ES;
     const int row = pbyte / rowb, pu = (pbyte % rowb) >> 4;
@@ -204,10 +217,10 @@ void kla_scan_kernel(
       // K and Q rows: token rows of the inputs, or rows of a chunk's decayed tile (DIAG)
       offK[j] = dma_off(J, DK, (DIAG ? 1 : H) * DK * ES, sw_rows<DK>(row) * (ES / 2));
     }
-    // T then P, compact tiles in LDS from packed blocks in memory: item m = NP j + pw is
-    // instruction m % NTC of T (m < NTC) or P
+    // T then P (then their low parts), compact tiles in LDS from packed blocks in memory:
+    // item m = NP j + pw is instruction m % NTC of tile m / NTC
 #pragma unroll
-    for (int j = 0; j < 2 * DP::NTC / NP; ++j) {
+    for (int j = 0; j < DP::NTW; ++j) {
       const int m = NP * j + pw;
       int row, col;
       tpc_piece<Tin>(1024 * (m % DP::NTC) + 16 * lane, row, col);
@@ -235,8 +248,10 @@ void kla_scan_kernel(
     const bool vcols = !MAP || v0 < VR;
     const Rsrc rv = make_rsrc(v + tok * VR + (vcols ? v0 : 0),
                               vcols ? (uint32_t)(((size_t)(len - 1) * H * VR + kBV) * ES) : 0u);
-    const Rsrc rt = make_rsrc(Tm + ch * kTpbElems, tpb_bytes<Tin>());
-    const Rsrc rp = make_rsrc(Pm + ch * kTpbElems, tpb_bytes<Tin>());
+    // split precision: per chunk-head the hi blocks, then the lo blocks
+    constexpr int TS = SPLIT ? 2 : 1;
+    const Rsrc rt = make_rsrc(Tm + ch * (TS * kTpbElems), tpb_bytes<Tin>());
+    const Rsrc rp = make_rsrc(Pm + ch * (TS * kTpbElems), tpb_bytes<Tin>());
     const Rsrc rg = make_rsrc(GD + ch * kGDFloats, kGDFloats * sizeof(float));
 #pragma unroll
     for (int j = 0; j < DP::NK / NP; ++j) {
@@ -247,8 +262,16 @@ void kla_scan_kernel(
 #pragma unroll
     for (int j = 0; j < DP::NTW; ++j) {
       const int m = NP * j + pw;
-      if (MAP || m < DP::NTC) dma16(rt, s.T + 1024 * (m % DP::NTC), offTP[j]);
-      else dma16(rp, s.P + 1024 * (m - DP::NTC), offTP[j]);
+      if (MAP || m < DP::NTC) {
+        dma16(rt, s.T + 1024 * (m % DP::NTC), offTP[j]);
+      } else if (m < 2 * DP::NTC) {
+        dma16(rp, s.P + 1024 * (m - DP::NTC), offTP[j]);
+      } else if constexpr (SPLIT) {
+        const Rsrc rtl = make_rsrc(Tm + ch * (2 * kTpbElems) + kTpbElems, tpb_bytes<Tin>());
+        const Rsrc rpl = make_rsrc(Pm + ch * (2 * kTpbElems) + kTpbElems, tpb_bytes<Tin>());
+        if (m < 3 * DP::NTC) dma16(rtl, s.Tl + 1024 * (m - 2 * DP::NTC), offTP[j]);
+        else dma16(rpl, s.Pl + 1024 * (m - 3 * DP::NTC), offTP[j]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < DP::NV / NP; ++j) {
@@ -355,6 +378,16 @@ void kla_scan_kernel(
     for (int i = 0; i < 4; ++i) { r[i] = from_f32<Tin>(lo[i]); r[i + 4] = from_f32<Tin>(hi[i]); }
     return r;
   };
+  // the rounding residuals x - bf16(x) of the same operand (split precision)
+  auto accB_res = [&](const f32x4 &lo, const f32x4 &hi) {
+    FragT r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = from_f32<Tin>(lo[i] - to_f32(from_f32<Tin>(lo[i])));
+      r[i + 4] = from_f32<Tin>(hi[i] - to_f32(from_f32<Tin>(hi[i])));
+    }
+    return r;
+  };
 
   // One chunk.  All LDS operands of a phase are read into registers before the phase's
   // MFMAs, and the next phase's reads are issued while those MFMAs run.
@@ -381,13 +414,21 @@ void kla_scan_kernel(
         if constexpr (!MAP) fq[t][ks] = rd_frag(s.Q, KQ{}, frow(t), ks);
       }
     // ---- reads for R = V - Diag(gam) Y and U = T R
-    FragT ft[6];
+    FragT ft[6], ftl[SPLIT ? 6 : 1];
     ft[0] = rd_tp(s.T, frow(0), 0);
     ft[1] = rd_tp(s.T, frow(1), 0);
     ft[2] = rd_tp(s.T, frow(2), 0);
     ft[3] = rd_tp(s.T, frow(2), 1);
     ft[4] = rd_tp(s.T, frow(3), 0);
     ft[5] = rd_tp(s.T, frow(3), 1);
+    if constexpr (SPLIT) {
+      ftl[0] = rd_tp(s.Tl, frow(0), 0);
+      ftl[1] = rd_tp(s.Tl, frow(1), 0);
+      ftl[2] = rd_tp(s.Tl, frow(2), 0);
+      ftl[3] = rd_tp(s.Tl, frow(2), 1);
+      ftl[4] = rd_tp(s.Tl, frow(3), 0);
+      ftl[5] = rd_tp(s.Tl, frow(3), 1);
+    }
     f32x4 g4[4], d4[4];
     float vv[4][4];
 #pragma unroll
@@ -444,6 +485,7 @@ void kla_scan_kernel(
     // ---- R = V - Diag(gam) Y, U = T R (row tile t needs k-steps ks <= t / 2); (Q S)^T,
     //      which is off the chain, fills the matrix core while R is formed
     FragT Uop[2], Udop[2];
+    [[maybe_unused]] FragT Uopl[2], Udopl[2];
     {
       f32x4 R[4];
 #pragma unroll
@@ -462,6 +504,13 @@ void kla_scan_kernel(
       U[1] = mma(ft[1], Rop0, zero4());
       U[2] = mma(ft[3], Rop1, mma(ft[2], Rop0, zero4()));
       U[3] = mma(ft[5], Rop1, mma(ft[4], Rop0, zero4()));
+      if constexpr (SPLIT) {  // + T_hi R_lo + T_lo R_hi
+        const FragT Rl0 = accB_res(R[0], R[1]), Rl1 = accB_res(R[2], R[3]);
+        U[0] = mma(ftl[0], Rop0, mma(ft[0], Rl0, U[0]));
+        U[1] = mma(ftl[1], Rop0, mma(ft[1], Rl0, U[1]));
+        U[2] = mma(ftl[3], Rop1, mma(ft[3], Rl1, mma(ftl[2], Rop0, mma(ft[2], Rl0, U[2]))));
+        U[3] = mma(ftl[5], Rop1, mma(ft[5], Rl1, mma(ftl[4], Rop0, mma(ft[4], Rl0, U[3]))));
+      }
       f32x4 Ud[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -471,10 +520,16 @@ void kla_scan_kernel(
       Uop[1] = accB(U[2], U[3]);
       Udop[0] = accB(Ud[0], Ud[1]);
       Udop[1] = accB(Ud[2], Ud[3]);
+      if constexpr (SPLIT) {
+        Uopl[0] = accB_res(U[0], U[1]);
+        Uopl[1] = accB_res(U[2], U[3]);
+        Udopl[0] = accB_res(Ud[0], Ud[1]);
+        Udopl[1] = accB_res(Ud[2], Ud[3]);
+      }
     }
     // ---- reads for the output: P fragments and this lane's token decays (none in the map
     //      mode)
-    FragT fp[6];
+    FragT fp[6], fpl[SPLIT ? 6 : 1];
     float gt[4];
     if constexpr (!MAP) {
       fp[0] = rd_tp(s.P, frow(0), 0);
@@ -483,6 +538,14 @@ void kla_scan_kernel(
       fp[3] = rd_tp(s.P, frow(2), 1);
       fp[4] = rd_tp(s.P, frow(3), 0);
       fp[5] = rd_tp(s.P, frow(3), 1);
+      if constexpr (SPLIT) {
+        fpl[0] = rd_tp(s.Pl, frow(0), 0);
+        fpl[1] = rd_tp(s.Pl, frow(1), 0);
+        fpl[2] = rd_tp(s.Pl, frow(2), 0);
+        fpl[3] = rd_tp(s.Pl, frow(2), 1);
+        fpl[4] = rd_tp(s.Pl, frow(3), 0);
+        fpl[5] = rd_tp(s.Pl, frow(3), 1);
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t) gt[t] = s.gamO[frow(t)];
     }
@@ -495,6 +558,10 @@ void kla_scan_kernel(
         Sacc[m] *= dl;
       Sacc[m] = mma(fkt[m][0], Udop[0], Sacc[m]);
       Sacc[m] = mma(fkt[m][1], Udop[1], Sacc[m]);
+      if constexpr (SPLIT) {
+        Sacc[m] = mma(fkt[m][0], Udopl[0], Sacc[m]);
+        Sacc[m] = mma(fkt[m][1], Udopl[1], Sacc[m]);
+      }
     }
     if constexpr (!MAP) {
     // ---- O^T = Diag(gam) (Q S)^T + U^T P^T: lane (r16, kg) holds token frow(t), columns
@@ -508,9 +575,14 @@ void kla_scan_kernel(
         f32x4 O = OT[t] * gt[t];
         if (t < 2) {
           O = mma(Uop[0], fp[t], O);
+          if constexpr (SPLIT) O = mma(Uop[0], fpl[t], mma(Uopl[0], fp[t], O));
         } else {
           O = mma(Uop[0], fp[2 * t - 2], O);
           O = mma(Uop[1], fp[2 * t - 1], O);
+          if constexpr (SPLIT) {
+            O = mma(Uop[0], fpl[2 * t - 2], mma(Uopl[0], fp[2 * t - 2], O));
+            O = mma(Uop[1], fpl[2 * t - 1], mma(Uopl[1], fp[2 * t - 1], O));
+          }
         }
         unsigned char *dst = vt + tile_off<Tin, kBV, true>(frow(t), 16 * cw + 4 * kg);
         if constexpr (B16) {
@@ -603,15 +675,16 @@ void kla_scan_kernel(
 
 // units: sequences (kScanSeq) or segments; DVs: the state's column count (d_v, or
 // d_v + d_k in the map mode).
-template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES, int MODE>
+template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES, int MODE,
+          bool SPLIT = false>
 static hipError_t launch_scan_s(int DVs, int64_t units, const void *q, const void *k,
                                 const void *v, const float *GD, const void *T, const void *P,
                                 const float *S0, void *o, float *S_T, SeqTables t, int32_t H,
                                 hipStream_t stream, const DiagTiles *dg, void *SN,
                                 const SegArgs &sa) {
   constexpr bool MAP = MODE == kScanMap;
-  using SMT = ScanSmem<Tin, DK, SHP::BV, DIAG, MAP>;
-  using SLT = ScanSlot<Tin, DK, SHP::BV, DIAG, MAP>;
+  using SMT = ScanSmem<Tin, DK, SHP::BV, DIAG, MAP, SPLIT>;
+  using SLT = ScanSlot<Tin, DK, SHP::BV, DIAG, MAP, SPLIT>;
   static_assert(sizeof(SMT) <= kLdsBytes, "LDS budget");
   static_assert(offsetof(SLT, dec) == offsetof(SLT, gam) + 256 &&
                     offsetof(SLT, gamO) == offsetof(SLT, gam) + 512,
@@ -620,7 +693,7 @@ static hipError_t launch_scan_s(int DVs, int64_t units, const void *q, const voi
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP, DIAG, STATES, MODE>),
+        reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP, DIAG, STATES, MODE, SPLIT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -628,7 +701,7 @@ static hipError_t launch_scan_s(int DVs, int64_t units, const void *q, const voi
   const int64_t blocks = units * H * (DVs / SHP::BV);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK, SHP, DIAG, STATES, MODE>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((kla_scan_kernel<Tin, DK, SHP, DIAG, STATES, MODE, SPLIT>), dim3((unsigned)blocks),
                      dim3(SHP::THREADS), smem, stream, static_cast<const Tin *>(q),
                      static_cast<const Tin *>(k), static_cast<const Tin *>(v), GD,
                      static_cast<const Tin *>(T), static_cast<const Tin *>(P), S0,
@@ -657,7 +730,7 @@ static int device_cus() {
 // The narrow shape while its grid fits the chip in one wave of workgroups (more of them
 // would only queue behind each other while their staging traffic adds up); the wide shape,
 // which stages each tile once for 64 columns, beyond that.
-template <typename Tin, int DK, bool DIAG, bool STATES, int MODE = kScanSeq>
+template <typename Tin, int DK, bool DIAG, bool STATES, int MODE = kScanSeq, bool SPLIT = false>
 static hipError_t launch_scan_t(int DVs, int64_t units, const void *q, const void *k,
                                 const void *v, const float *GD, const void *T, const void *P,
                                 const float *S0, void *o, float *S_T, SeqTables t, int32_t H,
@@ -667,14 +740,14 @@ static hipError_t launch_scan_t(int DVs, int64_t units, const void *q, const voi
   // workgroups of the narrow shape per CU: one, or in the map mode (two waves per SIMD) as
   // many as the LDS holds, at most two
   constexpr int lds_fit =
-      kLdsBytes / (int)sizeof(ScanSmem<Tin, DK, ScanNarrow::BV, DIAG, MODE == kScanMap>);
+      kLdsBytes / (int)sizeof(ScanSmem<Tin, DK, ScanNarrow::BV, DIAG, MODE == kScanMap, SPLIT>);
   constexpr int per_cu = MODE == kScanMap ? (lds_fit >= 2 ? 2 : 1) : 1;
   const int64_t fit = (int64_t)device_cus() * per_cu;
   if (fit > 0 && narrow_blocks > fit)
-    return launch_scan_s<Tin, DK, ScanWide, DIAG, STATES, MODE>(DVs, units, q, k, v, GD, T, P, S0,
-                                                                o, S_T, t, H, stream, dg, SN, sa);
-  return launch_scan_s<Tin, DK, ScanNarrow, DIAG, STATES, MODE>(DVs, units, q, k, v, GD, T, P, S0,
-                                                                o, S_T, t, H, stream, dg, SN, sa);
+    return launch_scan_s<Tin, DK, ScanWide, DIAG, STATES, MODE, SPLIT>(
+        DVs, units, q, k, v, GD, T, P, S0, o, S_T, t, H, stream, dg, SN, sa);
+  return launch_scan_s<Tin, DK, ScanNarrow, DIAG, STATES, MODE, SPLIT>(
+      DVs, units, q, k, v, GD, T, P, S0, o, S_T, t, H, stream, dg, SN, sa);
 }
 
 template <typename Tin, int DK>
@@ -710,6 +783,17 @@ hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k,
                                      dg, SN);
   return launch_scan_g<float, 64>(d_v, q, k, v, GD, T, P, S0, o, S_T, t, n_seq, H, stream, dg,
                                   SN);
+}
+
+hipError_t launch_scan_split(int d_k, int d_v, const void *q, const void *k, const void *v,
+                             const float *GD, const void *T, const void *P, const float *S0,
+                             void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
+                             hipStream_t stream) {
+  if (d_k == 128)
+    return launch_scan_t<__bf16, 128, false, false, kScanSeq, true>(
+        d_v, n_seq, q, k, v, GD, T, P, S0, o, S_T, t, H, stream, nullptr, nullptr);
+  return launch_scan_t<__bf16, 64, false, false, kScanSeq, true>(
+      d_v, n_seq, q, k, v, GD, T, P, S0, o, S_T, t, H, stream, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -751,38 +835,41 @@ __global__ __launch_bounds__(256) void kla_seg_combine_kernel(const float *__res
     }
   }
   // this lane's operands of step g: M_g[row][KS kg .. + KS) for the rows of its tiles, and
-  // the N_g entries its accumulators start from
-  f32x4 A[TW][NF], Nv[TW];
-  auto load = [&](int g) {
+  // the N_g entries its accumulators start from.  Three register buffers in rotation keep
+  // the loads of the next two steps in flight while one step runs.
+  struct Ops {
+    f32x4 A[TW][NF], N[TW];
+  };
+  auto load = [&](Ops &o, int g) {
+    if (g + 1 >= G) return;  // no such step
     const float *b = nm(g);
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
       const int row = KS * w + 16 * t + r16;
 #pragma unroll
       for (int j = 0; j < NF; ++j)
-        A[t][j] = *reinterpret_cast<const f32x4 *>(b + (size_t)row * W + dv + KS * kg + 4 * j);
+        o.A[t][j] = *reinterpret_cast<const f32x4 *>(b + (size_t)row * W + dv + KS * kg + 4 * j);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        Nv[t][e] = b[(size_t)(KS * w + 16 * t + 4 * kg + e) * W + c0 + r16];
+        o.N[t][e] = b[(size_t)(KS * w + 16 * t + 4 * kg + e) * W + c0 + r16];
     }
   };
-  if (G > 2) load(1);
-  for (int g = 1; g + 1 < G; ++g) {
-    f32x4 Ac[TW][NF], acc[TW];
+  auto step = [&](const Ops &o, int g) {
+    // two accumulators per tile (even and odd contraction steps) halve the dependent chain
+    f32x4 acc[TW][2];
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
-      acc[t] = Nv[t];
-#pragma unroll
-      for (int j = 0; j < NF; ++j) Ac[t][j] = A[t][j];
+      acc[t][0] = o.N[t];
+      acc[t][1] = zero4();
     }
-    if (g + 2 < G) load(g + 1);  // the next step's operands load while this one runs
-    __syncthreads();              // Ss holds S_in(g)
+    __syncthreads();  // Ss holds S_in(g)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const float bv = Ss[16 * (4 * s + kg) + r16];
 #pragma unroll
       for (int t = 0; t < TW; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ac[t][s >> 2][s & 3], bv, acc[t], 0, 0, 0);
+        acc[t][s & 1] =
+            __builtin_amdgcn_mfma_f32_16x16x4f32(o.A[t][s >> 2][s & 3], bv, acc[t][s & 1], 0, 0, 0);
     }
     __syncthreads();  // every read of S_in(g) is done
     float *So = sin_(g);
@@ -791,9 +878,23 @@ __global__ __launch_bounds__(256) void kla_seg_combine_kernel(const float *__res
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = KS * w + 16 * t + 4 * kg + e;
-        Ss[pos(row) + r16] = acc[t][e];
-        So[(size_t)row * dv + c0 + r16] = acc[t][e];
+        const float x = acc[t][0][e] + acc[t][1][e];
+        Ss[pos(row) + r16] = x;
+        So[(size_t)row * dv + c0 + r16] = x;
       }
+  };
+  Ops o0, o1, o2;
+  load(o0, 1);
+  load(o1, 2);
+  for (int g = 1; g + 1 < G; g += 3) {
+    load(o2, g + 2);
+    step(o0, g);
+    if (g + 2 >= G) break;
+    load(o0, g + 3);
+    step(o1, g + 1);
+    if (g + 3 >= G) break;
+    load(o1, g + 4);
+    step(o2, g + 2);
   }
 }
 

@@ -224,6 +224,24 @@ typedef enum kla_beta_mode {
   KLA_BETA_INV_LOG_T = 5
 } kla_beta_mode;
 
+/* Operand precision of the bf16 prefill's matrix-core products (fp32 state and
+ * accumulation either way; fp32 inputs always take exact fp32 products).
+ *   KLA_PRECISION_BF16   S, the residual R = V - Diag(gamma) K S, U = T R,
+ *                        Diag(dec) U, T and P enter their products rounded to
+ *                        bf16 (relative error 2^-9 each).
+ *   KLA_PRECISION_SPLIT  T R, P U and K^T Diag(dec) U take R, U, Diag(dec) U, T
+ *                        and P as pairs hi = bf16(x), lo = bf16(x - hi) and sum
+ *                        hi*hi + hi*lo + lo*hi (K is exact in bf16); T and P are
+ *                        stored as such pairs (twice their workspace).  It holds
+ *                        o = v of the hard projection (Theorem 1) for keys whose
+ *                        norms span 100x, where the bf16 mode's cancellation of
+ *                        ||k|| |S|-sized terms loses ~0.1 relative.  Scalar gate,
+ *                        kla_prefill_chunked_ex only (sequential chunk scan). */
+typedef enum kla_precision {
+  KLA_PRECISION_BF16 = 0,
+  KLA_PRECISION_SPLIT = 1
+} kla_precision;
+
 typedef struct kla_options {
   int32_t beta_mode;          /* a kla_beta_mode value */
   int32_t normalize_q;        /* nonzero: divide each readout by ||q_t||_2 */
@@ -242,6 +260,7 @@ typedef struct kla_options {
    * and each sequence has at least 64 chunks: G = min(512 / (n_seq * n_heads *
    * d_v / 32), chunks per sequence / 32).  Ignored elsewhere. */
   int32_t scan_segments;
+  int32_t precision;          /* a kla_precision value */
 } kla_options;
 
 /* kla_prefill_workspace_bytes for the variant that opts selects (NULL = the

@@ -181,14 +181,16 @@ def test_last_error_is_thread_local_text(lib):
     assert "d_k" in lib.kla_last_error().decode()
 
 
-def _opts(mode=0, normq=0, pos=None, diag=0):
-    return ctypes.pointer(kla.KlaOptions(mode, normq, pos, diag))
+def _opts(mode=0, normq=0, pos=None, diag=0, prec=0):
+    return ctypes.pointer(kla.KlaOptions(mode, normq, pos, diag, 0, prec))
 
 
 @pytest.mark.parametrize("opts,status", [
     (lambda: _opts(mode=6), UNSUPPORTED),       # unknown coefficient mode
     (lambda: _opts(mode=-1), UNSUPPORTED),
     (lambda: _opts(mode=3, pos=FAKE + 2), INVALID),   # int32 offsets need 4-byte alignment
+    (lambda: _opts(prec=2), UNSUPPORTED),       # unknown precision
+    (lambda: _opts(prec=-1), UNSUPPORTED),
 ])
 def test_options_errors(lib, opts, status):
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, eta=FAKE * 5, o=FAKE * 6)
@@ -205,6 +207,49 @@ def test_options_errors(lib, opts, status):
                                 FAKE * 7, 4, 2, 128, 128, BF16, opts(), None)
     assert st == status
     assert lib.kla_last_error().decode() != ""
+
+
+def test_split_precision_workspace_and_entry_points(lib):
+    """Split precision stores T and P as hi and lo bf16 blocks: twice their region for bf16
+    inputs, nothing for fp32 ones (exact fp32 products already).  It runs through
+    kla_prefill_chunked_ex with the scalar gate only."""
+    pad = lambda x: (x + 255) // 256 * 256
+    n_seq, n_tok, H, dk, dv = 4, 16384, 16, 128, 128
+    nch = (n_tok + 63) // 64 + n_seq
+    base = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv)
+    split = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, precision="split")
+    assert split - base == 2 * pad(2 * nch * H * 2560)
+    assert (kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, kla.torch.float32,
+                                            precision="split")
+            == kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, kla.torch.float32))
+    # split precision takes no two-level scan: no segment scratch for a long sequence
+    assert (kla.kla_prefill_workspace_bytes(1, 65536, 16, dk, dv, precision="split")
+            - kla.kla_prefill_workspace_bytes(1, 65536, 16, dk, dv, scan_segments=1)
+            == 2 * pad(2 * ((65536 + 63) // 64 + 1) * 16 * 2560))
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, eta=FAKE * 5, o=FAKE * 6)
+    ws = FAKE * 64
+    nb = kla.kla_prefill_workspace_bytes(2, 256, 4, 128, 128, precision="split")
+    # the staged entry point and the backward refuse it
+    st = lib.kla_prefill_prepare_ex(a["q"], a["k"], a["g"], a["eta"], 1e-6, None, None, 2, 256, 4,
+                                    128, 128, BF16, ws, nb, _opts(prec=1), None)
+    assert st == UNSUPPORTED
+    st = lib.kla_prefill_backward_ex(
+        FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1e-6, None, FAKE * 6, None, FAKE * 7,
+        FAKE * 8, FAKE * 9, FAKE * 10, FAKE * 11, FAKE * 12, None, None, 2, 256, 4, 128, 128,
+        BF16, FAKE * 64, lib.kla_prefill_backward_workspace_bytes(2, 256, 4, 128, 128, BF16),
+        _opts(prec=1), None)
+    assert st == UNSUPPORTED
+    # with the diagonal gate
+    st = lib.kla_prefill_chunked_ex(a["q"], a["k"], a["v"], a["g"], a["eta"], 1e-6, None, a["o"],
+                                    None, None, None, 2, 256, 4, 128, 128, BF16, ws, nb,
+                                    _opts(diag=1, prec=1), None)
+    assert st == UNSUPPORTED
+    # a workspace sized for the bf16 mode is too small for it
+    st = lib.kla_prefill_chunked_ex(a["q"], a["k"], a["v"], a["g"], a["eta"], 1e-6, None, a["o"],
+                                    None, None, None, 2, 256, 4, 128, 128, BF16, ws,
+                                    kla.kla_prefill_workspace_bytes(2, 256, 4, 128, 128),
+                                    _opts(prec=1), None)
+    assert st == WORKSPACE
 
 
 def test_options_default_pointer_is_accepted_up_to_the_workspace_check(lib):

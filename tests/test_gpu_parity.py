@@ -372,6 +372,61 @@ def test_hard_projection_bf16_reads_back_values(kla):
     check(o, d["v"].double().cpu().numpy(), 2e-2, "o")
 
 
+def _config0_keys_hard_bf16(T, H, dk, dv):
+    """Config 0's draws (keys with norms 10^U(-1, 1)) in bf16, hard variant."""
+    w = ki.Workload(0, "c0-bf16", 1, H, dk, dv, torch.bfloat16, T=T)
+    return to_dev(ki.hard_variant(ki.prefill_inputs(w)))
+
+
+@pytest.mark.parametrize("T,H,dk,dv", [(256, 1, 64, 64), (300, 2, 128, 128)])
+def test_hard_projection_bf16_config0_keys_split_precision(kla, T, H, dk, dv):
+    """Theorem 1 on bf16 inputs with keys whose norms span 100x: with split precision (T R,
+    P U and the state update on hi/lo bf16 operand pairs) o_t = v_t, and o matches the
+    oracle."""
+    d = _config0_keys_hard_bf16(T, H, dk, dv)
+    o, _ = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                   n_seq=1, precision="split")
+    torch.cuda.synchronize()
+    check(o, d["v"].double().cpu().numpy(), 2e-2, "o vs v")
+    oo, _ = oracle_prefill(d, S0=False)
+    check(o, oo, 2e-2, "o vs oracle")
+
+
+@pytest.mark.xfail(strict=True, reason="bf16 operand mode on keys whose norms span 100x: o = "
+                   "k S~ + e cancels terms of size ||k|| |S| down to |v|, and bf16 operands "
+                   "(2^-9) leave a measured error of 0.10-0.20 against the 2e-2 bar; the split "
+                   "precision mode holds it")
+def test_hard_projection_bf16_config0_keys_bf16_operands(kla):
+    d = _config0_keys_hard_bf16(300, 2, 128, 128)
+    o, _ = run_prefill(kla, d, S0=False)
+    check(o, d["v"].double().cpu().numpy(), 2e-2, "o vs v")
+
+
+@pytest.mark.parametrize("n_seq,T,H,dk,dv,S0", [
+    (2, 200, 3, 128, 128, True),   # ragged tail
+    (3, 130, 2, 128, 256, True),
+    (1, 1, 1, 128, 128, False),    # a single token
+    (2, 127, 2, 64, 128, True),
+    (3, 130, 24, 128, 128, True),  # the 64-column workgroup shape
+])
+def test_prefill_split_precision_shapes(kla, n_seq, T, H, dk, dv, S0):
+    """Split precision against the oracle on the workloads' draws; never worse than the
+    bf16 operand mode beyond rounding."""
+    w = ki.Workload(96, "unit", n_seq, H, dk, dv, torch.bfloat16, T=T, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w))
+    outs = {}
+    for prec in ("split", "bf16"):
+        o, ST = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                        S0=d["S0"] if S0 else None, n_seq=n_seq, precision=prec)
+        torch.cuda.synchronize()
+        outs[prec] = (o, ST)
+    oo, So = oracle_prefill(d, S0=S0)
+    check(outs["split"][0], oo, 2e-2, "o split")
+    check(outs["split"][1], So, 2e-2, "ST split")
+    assert err(outs["split"][0], oo) <= err(outs["bf16"][0], oo) + 4e-3
+    assert err(outs["split"][1], So) <= err(outs["bf16"][1], So) + 4e-3
+
+
 def test_split_resume_and_prefill_decode_chain(kla):
     """prefill(T) == prefill(T1) + prefill(rest, S0 = S_T1) for a split inside a chunk, and
     prefill(T) + m decode steps == prefill(T + m)."""
