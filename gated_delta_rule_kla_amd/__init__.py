@@ -29,7 +29,9 @@ __all__ = ["kla_prefill_chunked", "kla_prefill_prepare", "kla_prefill_scan", "kl
 
 CHUNK = 64
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libkla.so")
+# KLA_LIBRARY names another build of the same C ABI (the sanitized host build of the CPU
+# tests); the default is the in-tree libkla.so
+_LIB_PATH = os.environ.get("KLA_LIBRARY") or os.path.join(_PKG, "libkla.so")
 _lib = None
 
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}

@@ -764,12 +764,13 @@ const char *kla_status_string(kla_status status) {
     case KLA_ERR_UNSUPPORTED: return "KLA_ERR_UNSUPPORTED: unsupported size or dtype";
     case KLA_ERR_WORKSPACE: return "KLA_ERR_WORKSPACE: workspace missing or too small";
     case KLA_ERR_HIP: return "KLA_ERR_HIP: HIP launch failed";
+    default: break;
   }
   return "unknown kla_status";
 }
 
 const char *kla_last_error(void) { return g_last_error; }
 
-int32_t kla_version(void) { return 30000; }
+int32_t kla_version(void) { return 30100; }
 
 }  // extern "C"

@@ -59,12 +59,18 @@ typedef enum kla_status {
   KLA_ERR_UNSUPPORTED = 2,      /* d_k not in {64, 128}, d_v not in {64, 128, 256},
                                    or an unknown dtype */
   KLA_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than required */
-  KLA_ERR_HIP = 4               /* a kernel launch failed */
+  KLA_ERR_HIP = 4,              /* a kernel launch failed */
+  /* not a status: makes every int32 value a valid kla_status, so that a caller's
+   * unknown value is an ordinary input (kla_status_string says "unknown status") */
+  KLA_STATUS_RANGE_ = 0x7fffffff
 } kla_status;
 
 typedef enum kla_dtype {
   KLA_DTYPE_F32 = 0,  /* IEEE fp32 */
-  KLA_DTYPE_BF16 = 1  /* bfloat16; outputs rounded to nearest even */
+  KLA_DTYPE_BF16 = 1, /* bfloat16; outputs rounded to nearest even */
+  /* not a dtype: makes every int32 value a valid kla_dtype, so that an unknown one is
+   * an ordinary input rejected with KLA_ERR_UNSUPPORTED (or a workspace size of 0) */
+  KLA_DTYPE_RANGE_ = 0x7fffffff
 } kla_dtype;
 
 /* Bytes of device workspace kla_prefill_chunked needs for this problem size and

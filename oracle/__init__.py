@@ -24,7 +24,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kla_oracle.c")
-_LIB = os.path.join(_HERE, "libkla_oracle.so")
+# KLA_ORACLE_LIBRARY names another build of kla_oracle.c (the sanitized build of the CPU
+# tests); the default is the one build() writes next to the source
+_LIB = os.environ.get("KLA_ORACLE_LIBRARY") or os.path.join(_HERE, "libkla_oracle.so")
 _lib = None
 
 
@@ -38,6 +40,16 @@ def build(force: bool = True) -> str:
         os.replace(tmp, _LIB)
         _lib = None
     return _LIB
+
+
+def build_sanitized(path: str) -> str:
+    """Compile ``kla_oracle.c`` with gcc under AddressSanitizer and UndefinedBehaviorSanitizer
+    into ``path`` (loading it needs gcc's libasan preloaded)."""
+    subprocess.check_call(
+        ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-std=c99", "-fopenmp", "-fPIC",
+         "-shared", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", _SRC,
+         "-o", path, "-lm"])
+    return path
 
 
 def _load():
