@@ -106,6 +106,31 @@ def test_decode_full_batch(kla):
         check(S, So, 2e-2, "S")
 
 
+def test_decode_from_prefill_built_32k_state(kla):
+    """Workload 3 with its state built by the prefill over 32768 tokens of workload 1's
+    distributions (from a zero state), on a 2-sequence subset: the device prefill's state
+    and last-chunk outputs against the oracle's, then 8 decode steps of workload 3's draws
+    from each state."""
+    B, T = 2, 32768
+    pre = to_dev(ki.prefill_inputs(1, T=T, n_seq=B))
+    o, ST = run_prefill(kla, pre, S0=False)
+    oo, So = oracle_prefill(pre, S0=False)
+    check(ST, So, 2e-2, "S after 32768 tokens")
+    for n in range(B):
+        check(o[(n + 1) * T - 64:(n + 1) * T], oo[(n + 1) * T - 64:(n + 1) * T], 2e-2,
+              "o, last chunk")
+    dd = to_dev(ki.decode_inputs(3, steps=8, B=B, S=ST))
+    S, Sd = ST.clone(), So
+    for t in range(8):
+        od, S = kla.kla_decode_step(dd["q"][t], dd["k"][t], dd["v"][t], dd["g"][t], dd["eta"][t],
+                                    dd["eps"], S, inplace=True)
+        ood, Sd = oracle.decode(dd["q"][t], dd["k"][t], dd["v"][t], dd["g"][t], dd["eta"][t],
+                                dd["eps"], Sd)
+        torch.cuda.synchronize()
+        check(od, ood, 2e-2, "decode o")
+    check(S, Sd, 2e-2, "decode S")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_decode_many_items(kla, dtype):
     """6144 (sequence, head) items: the launch shape with one 512-lane workgroup per item (the
