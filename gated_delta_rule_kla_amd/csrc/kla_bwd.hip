@@ -87,6 +87,48 @@ __device__ __forceinline__ f32x4 mmt(f32x4 acc, int lane, FA fa, FB fb) {
   }
 }
 
+// The same tile product with each lane's operands read as contiguous runs: pa(r, k) points at
+// A(r, k .. k + 7) and pb(r, k) at B(k .. k + 7, r) (a row of B^T), for k = k0 + 8 kq; the
+// pointees are float or __bf16 (16-byte aligned).  bf16 inputs: one v_mfma_f32_16x16x32_bf16
+// per 32 contraction indices (fp32 pointees rounded to bf16 as read); fp32 inputs: eight
+// exact v_mfma_f32_16x16x4_f32 steps, step s contracting the indices k0 + 8 kq + s.
+__device__ __forceinline__ void rd8(const float *p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3]; x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+__device__ __forceinline__ void rd8(const __bf16 *p, float (&x)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) x[s] = to_f32(v[s]);
+}
+__device__ __forceinline__ bf16x8 rd8b(const float *p) {
+  float x[8];
+  rd8(p, x);
+  bf16x8 r;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) r[s] = from_f32<__bf16>(x[s]);
+  return r;
+}
+__device__ __forceinline__ bf16x8 rd8b(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+template <typename Tin, int KD, typename PA, typename PB>
+__device__ __forceinline__ f32x4 mmr(f32x4 acc, int lane, PA pa, PB pb) {
+  const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < KD; k0 += 32) {
+    if constexpr (sizeof(Tin) == 2) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rd8b(pa(r, k0 + 8 * kq)), rd8b(pb(r, k0 + 8 * kq)),
+                                                    acc, 0, 0, 0);
+    } else {
+      float a[8], b[8];
+      rd8(pa(r, k0 + 8 * kq), a);
+      rd8(pb(r, k0 + 8 * kq), b);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ f32x4 ld4(const __bf16 *p) {
   const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
@@ -376,15 +418,26 @@ namespace {
 // LT: the element type of the d_v-loop tiles: the operand type of the inputs.  Every read of
 // them feeds a product in that precision, so bf16 storage loses nothing and halves the LDS
 // traffic of those products.
+// Row strides of the d_v-loop tiles, whole 16-byte units: 32 columns (40 bf16 or 36 fp32),
+// and the transposed copies' rows of d_k and of 64 tokens.
+template <typename LT> constexpr int ldl() { return sizeof(LT) == 2 ? 40 : 36; }
+template <typename LT, int N> constexpr int ldt() { return sizeof(LT) == 2 ? N + 8 : N + 4; }
+
 template <typename LT, int DK>
 struct GradSmem {
+  static constexpr int LDL = ldl<LT>();
+  static constexpr bool TR = sizeof(LT) == 2;
   float K[kChunk][DK + 4];
   float X[kChunk][LDC];
   float A[kChunk][LDC];
   union {
     struct {  // the loop over 32-column blocks of d_v
-      LT S[DK][LDB], So[DK][LDB];
-      LT R[kChunk][LDB], U[kChunk][LDB], dO[kChunk][LDB], dU[kChunk][LDB], dR[kChunk][LDB];
+      LT S[DK][LDL], So[DK][LDL];
+      LT R[kChunk][LDL], U[kChunk][LDL], dO[kChunk][LDL], dU[kChunk][LDL], dR[kChunk][LDL];
+      // bf16: transposed copies S^T (d_v x d_k) and (Diag(b) R)^T (d_v x tokens), the B
+      // operands of K S and X Diag(b) R read as rows (fp32 tiles have no room for them: those
+      // two products read columns)
+      LT ST[TR ? kAdjBV : 1][TR ? ldt<LT, DK>() : 4], RbT[TR ? kAdjBV : 1][TR ? ldt<LT, kChunk>() : 4];
     } lp;
     struct {  // the chunk-local algebra after it
       float Q[kChunk][DK + 4];
@@ -517,54 +570,81 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     rdr.load(dRb + v0, (size_t)DV, kChunk, tid);
   };
   issue(0);
+  constexpr int LDL = GradSmem<Tin, DK>::LDL;
+  constexpr bool TR = GradSmem<Tin, DK>::TR;
   for (int v0 = 0; v0 < DV; v0 += kAdjBV) {
     __syncthreads();  // the previous block's reads (and X's writes) are done
-    rs.template store<LDB>(&sm.u.lp.S[0][0], tid);
-    rso.template store<LDB>(&sm.u.lp.So[0][0], tid);
+    rs.template store<LDL>(&sm.u.lp.S[0][0], tid);
+    // S^T: thread quad (row r, columns c .. c + 3) into column r of rows c .. c + 3
+#pragma unroll
+    for (int j = 0; j < (TR ? rs.J : 0); ++j) {
+      const int e = tid + kGradThreads * j, r = e / (kAdjBV / 4), c = 4 * (e % (kAdjBV / 4));
+      if (rs.NQ % kGradThreads == 0 || e < rs.NQ) {
+        const f32x4 sv = cvt4(rs.x[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.u.lp.ST[c + i][r] = from_f32<Tin>(sv[i]);
+      }
+    }
+    rso.template store<LDL>(&sm.u.lp.So[0][0], tid);
 #pragma unroll
     for (int j = 0; j < rs.J; ++j) {
       const f32x4 sv = cvt4(rs.x[j]);
       sc += sv[0] * rso.x[j][0] + sv[1] * rso.x[j][1] + sv[2] * rso.x[j][2] + sv[3] * rso.x[j][3];
     }
-    rv.template store<LDB>(&sm.u.lp.R[0][0], tid);
-    rdo.template store<LDB>(&sm.u.lp.dO[0][0], tid);
-    rdu.template store<LDB>(&sm.u.lp.dU[0][0], tid);
-    rdr.template store<LDB>(&sm.u.lp.dR[0][0], tid);
+    rv.template store<LDL>(&sm.u.lp.R[0][0], tid);
+    rdo.template store<LDL>(&sm.u.lp.dO[0][0], tid);
+    rdu.template store<LDL>(&sm.u.lp.dU[0][0], tid);
+    rdr.template store<LDL>(&sm.u.lp.dR[0][0], tid);
     __syncthreads();
     if (v0 + kAdjBV < DV) issue(v0 + kAdjBV);
     const int yi = wid >> 1, yj = wid & 1;  // this wavefront's 16 x 16 tile of R and U
     {
-      const f32x4 y = mmt<Tin, DK>(
-          zero4(), lane, [&](int i, int kk) { return sm.K[16 * yi + i][kk]; },
-          [&](int kk, int j) { return to_f32(sm.u.lp.S[kk][16 * yj + j]); });
+      f32x4 y;
+      if constexpr (TR)
+        y = mmr<Tin, DK>(
+            zero4(), lane, [&](int i, int kk) { return &sm.K[16 * yi + i][kk]; },
+            [&](int j, int kk) { return &sm.u.lp.ST[16 * yj + j][kk]; });
+      else
+        y = mmt<Tin, DK>(
+            zero4(), lane, [&](int i, int kk) { return sm.K[16 * yi + i][kk]; },
+            [&](int kk, int j) { return to_f32(sm.u.lp.S[kk][16 * yj + j]); });
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * yi + 4 * kq + e;
         Tin &rv_ = sm.u.lp.R[row][16 * yj + r16];
-        rv_ = from_f32<Tin>(to_f32(rv_) - sm.gam[row] * y[e]);
+        const Tin rn = from_f32<Tin>(to_f32(rv_) - sm.gam[row] * y[e]);
+        rv_ = rn;
+        if constexpr (TR) sm.u.lp.RbT[16 * yj + r16][row] = from_f32<Tin>(sm.b[row] * to_f32(rn));
       }
     }
     __syncthreads();
     {
-      const f32x4 uu = mmt<Tin, kChunk>(
-          zero4(), lane, [&](int i, int kk) { return sm.X[16 * yi + i][kk]; },
-          [&](int kk, int j) { return sm.b[kk] * to_f32(sm.u.lp.R[kk][16 * yj + j]); });
+      f32x4 uu;
+      if constexpr (TR)
+        uu = mmr<Tin, kChunk>(
+            zero4(), lane, [&](int i, int kk) { return &sm.X[16 * yi + i][kk]; },
+            [&](int j, int kk) { return &sm.u.lp.RbT[16 * yj + j][kk]; });
+      else
+        uu = mmt<Tin, kChunk>(
+            zero4(), lane, [&](int i, int kk) { return sm.X[16 * yi + i][kk]; },
+            [&](int kk, int j) { return sm.b[kk] * to_f32(sm.u.lp.R[kk][16 * yj + j]); });
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm.u.lp.U[16 * yi + 4 * kq + e][16 * yj + r16] = from_f32<Tin>(uu[e]);
     }
     __syncthreads();
+    // qa, ka, kb without their row factors gam, -gam and dec (applied after the loop)
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int tj = (wid >> 2) + 2 * m;  // column tile of 16 key dims
-      qa[m] = mmt<Tin, kAdjBV>(
-          qa[m], lane, [&](int i, int kk) { return sm.gam[16 * mti + i] * to_f32(sm.u.lp.dO[16 * mti + i][kk]); },
-          [&](int kk, int j) { return to_f32(sm.u.lp.S[16 * tj + j][kk]); });
-      ka[m] = mmt<Tin, kAdjBV>(
-          ka[m], lane, [&](int i, int kk) { return -sm.gam[16 * mti + i] * to_f32(sm.u.lp.dR[16 * mti + i][kk]); },
-          [&](int kk, int j) { return to_f32(sm.u.lp.S[16 * tj + j][kk]); });
-      kb[m] = mmt<Tin, kAdjBV>(
-          kb[m], lane, [&](int i, int kk) { return sm.dec[16 * mti + i] * to_f32(sm.u.lp.U[16 * mti + i][kk]); },
-          [&](int kk, int j) { return to_f32(sm.u.lp.So[16 * tj + j][kk]); });
+      qa[m] = mmr<Tin, kAdjBV>(
+          qa[m], lane, [&](int i, int kk) { return &sm.u.lp.dO[16 * mti + i][kk]; },
+          [&](int j, int kk) { return &sm.u.lp.S[16 * tj + j][kk]; });
+      ka[m] = mmr<Tin, kAdjBV>(
+          ka[m], lane, [&](int i, int kk) { return &sm.u.lp.dR[16 * mti + i][kk]; },
+          [&](int j, int kk) { return &sm.u.lp.S[16 * tj + j][kk]; });
+      kb[m] = mmr<Tin, kAdjBV>(
+          kb[m], lane, [&](int i, int kk) { return &sm.u.lp.U[16 * mti + i][kk]; },
+          [&](int j, int kk) { return &sm.u.lp.So[16 * tj + j][kk]; });
     }
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
@@ -573,16 +653,25 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
         int I, J;
         lower_block(jb % 10, I, J);
         if (jb < 10)
-          pt[x] = mmt<Tin, kAdjBV>(
-              pt[x], lane, [&](int i, int kk) { return to_f32(sm.u.lp.dO[16 * I + i][kk]); },
-              [&](int kk, int j) { return to_f32(sm.u.lp.U[16 * J + j][kk]); });
+          pt[x] = mmr<Tin, kAdjBV>(
+              pt[x], lane, [&](int i, int kk) { return &sm.u.lp.dO[16 * I + i][kk]; },
+              [&](int j, int kk) { return &sm.u.lp.U[16 * J + j][kk]; });
         else
-          pt[x] = mmt<Tin, kAdjBV>(
-              pt[x], lane, [&](int i, int kk) { return to_f32(sm.u.lp.dU[16 * I + i][kk]); },
-              [&](int kk, int j) { return to_f32(sm.u.lp.R[16 * J + j][kk]); });
+          pt[x] = mmr<Tin, kAdjBV>(
+              pt[x], lane, [&](int i, int kk) { return &sm.u.lp.dU[16 * I + i][kk]; },
+              [&](int j, int kk) { return &sm.u.lp.R[16 * J + j][kk]; });
       }
     }
   }
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * mti + 4 * kq + e;
+      qa[m][e] *= sm.gam[row];
+      ka[m][e] *= -sm.gam[row];
+      kb[m][e] *= sm.dec[row];
+    }
   sc = wave_sum(sc);
   if (lane == 0) sm.red[wid] = sc;
   __syncthreads();  // the loop's LDS is free
