@@ -415,6 +415,236 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
 
 namespace {
 
+// The adjoint scan for bf16 inputs.  The tiles sit in LDS in bf16 rows (K, Q, P, T, dO and
+// Diag(gamO) dO as staged, dS', dU and Diag(gam) dR transposed, as their producers hold them);
+// each product takes each lane's 8 contraction indices either as one 16-byte row read or,
+// where it contracts down a column, as two gfx950 transpose reads, and the workgroup's
+// 128 x 32 (or 64 x 32) block of dS stays in the registers of the wavefronts that update it,
+// as fp32 accumulators.
+template <int DK>
+struct AdjSmem16 {
+  static constexpr int LK = DK + 8, LC = kChunk + 8, LV = kAdjBV + 8;  // bf16 row strides
+  __bf16 K[kChunk][LK], Q[kChunk][LK];
+  __bf16 P[kChunk][LC], T[kChunk][LC];       // lower blocks; zero above them
+  __bf16 dO[kChunk][LV], dOg[kChunk][LV];    // dO and Diag(gamO) dO
+  __bf16 dST[kAdjBV][LK];                    // dS'^T
+  __bf16 dUT[kAdjBV][LC], dRgT[kAdjBV][LC];  // dU^T, (Diag(gam) dR)^T
+  float gam[kChunk], dec[kChunk];
+};
+
+// gfx950 ds_read_b64_tr_b16: within each group of 16 lanes, lane d receives element d & 3 of
+// the 8-byte pieces addressed by lanes (d >> 2) + 4 i, i = 0..3.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+__device__ __forceinline__ bf16x4 tr_read(const __bf16 *p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(p)));
+}
+// Rows k .. k + 7 of column c0 + (lane & 15) of a row-major bf16 tile with row stride LD:
+// lane s of each 16-lane group addresses row k + (s >> 2) (+ 4), columns c0 + 4 (s & 3) .. + 3.
+template <int LD>
+__device__ __forceinline__ bf16x8 col8(const __bf16 *M, int c0, int k, int lane) {
+  const int s = lane & 15;
+  const __bf16 *p = M + (k + (s >> 2)) * LD + c0 + 4 * (s & 3);
+  const bf16x4 lo = tr_read(p), hi = tr_read(p + 4 * LD);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// Row c0 + (lane & 15), elements k .. k + 7, of a row-major bf16 tile.
+template <int LD>
+__device__ __forceinline__ bf16x8 row8(const __bf16 *M, int c0, int k, int lane) {
+  return *reinterpret_cast<const bf16x8 *>(M + (c0 + (lane & 15)) * LD + k);
+}
+// acc += the 16 x 16 product with operand fragments fa(k), fb(k) for k = k0 + 8 kq.
+template <int KD, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mmf(f32x4 acc, int lane, FA fa, FB fb) {
+  const int kq = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < KD; k0 += 32)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa(k0 + 8 * kq), fb(k0 + 8 * kq), acc, 0, 0, 0);
+  return acc;
+}
+
+}  // namespace
+
+template <int DK>
+__global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ dO,
+    const float *__restrict__ GD, const __bf16 *__restrict__ Tm, const __bf16 *__restrict__ Pm,
+    const float *__restrict__ dST, float *__restrict__ dS0, float *__restrict__ dSo,
+    float *__restrict__ dUo, float *__restrict__ dRo, __bf16 *__restrict__ dv,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV) {
+  using SM = AdjSmem16<DK>;
+  constexpr int LK = SM::LK, LC = SM::LC, LV = SM::LV;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  SM &sm = *reinterpret_cast<SM *>(smem_raw);
+  // the d_v slices of one (sequence, head) read the same K, Q, T and P: give them
+  // consecutive logical ids on one XCD (workgroup b runs on XCD b % 8) to share its L2
+  const int nsl = DV / kAdjBV;
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int pidx = (nblk % 8 == 0) ? (b % 8) * (nblk / 8) + b / 8 : b;
+  const int slice = pidx % nsl, sh = pidx / nsl;
+  const int h = sh % H, n = sh / H;
+  const int v0 = slice * kAdjBV;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int tb = cu[n], te = cu[n + 1], cbase = chunk_off[n];
+  const int nchunks = (te - tb + kChunk - 1) / kChunk;
+  const size_t sbase = ((size_t)n * H + h) * DK * (size_t)DV + v0;
+  constexpr int NW = kAdjThreads / 64;
+  constexpr int NX = DK / 64;  // dS tiles per wavefront: t = wid + NW x, rows 16 (t >> 1)
+
+  // P and T: zero the blocks above the diagonal blocks, which the packed tiles never write,
+  // before any staging
+  for (int e = tid; e < kChunk * LC; e += kAdjThreads) {
+    (&sm.P[0][0])[e] = from_f32<__bf16>(0.f);
+    (&sm.T[0][0])[e] = from_f32<__bf16>(0.f);
+  }
+  // this wavefront's tiles of dS (initially dS_T): lane (r16, kq) holds rows
+  // 16 mi + 4 kq + e, column 16 tj + r16
+  f32x4 dS[NX];
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    const int t = wid + NW * x, mi = t >> 1, tj = t & 1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dS[x][e] = dST ? dST[sbase + (size_t)(16 * mi + 4 * kq + e) * DV + 16 * tj + r16] : 0.f;
+  }
+  __syncthreads();
+
+  // a chunk's inputs are loaded into registers while the chunk before it (in this reverse
+  // order) is computed, and staged when its turn comes
+  RegTile<__bf16, kChunk, DK, kAdjThreads> rk, rq;
+  RegTile<__bf16, kChunk, kAdjBV, kAdjThreads> rdo;
+  PackedTile<__bf16, kAdjThreads> rt, rp;
+  static_assert(RegTile<__bf16, kChunk, kAdjBV, kAdjThreads>::J == 1, "one dO quad per thread");
+  float rgo = 0.f, rgd = 0.f;  // gamO of this thread's dO row; gam or dec of token tid
+  auto issue = [&](int c) {
+    const int t0 = tb + c * kChunk, len = min(kChunk, te - t0);
+    const size_t ch = (size_t)(cbase + c) * H + h;
+    const size_t tok = (size_t)t0 * H + h;
+    rk.load(k + tok * DK, (size_t)H * DK, len, tid);
+    rq.load(q + tok * DK, (size_t)H * DK, len, tid);
+    rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
+    rt.load(Tm + ch * kTpbElems, tid);
+    rp.load(Pm + ch * kTpbElems, tid);
+    rgo = GD[ch * kGDFloats + 2 * kChunk + tid / (kAdjBV / 4)];
+    if (tid < 2 * kChunk) rgd = GD[ch * kGDFloats + tid];  // gam, dec
+  };
+  if (nchunks > 0) issue(nchunks - 1);
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const int t0 = tb + c * kChunk, len = min(kChunk, te - t0);
+    const size_t ch = (size_t)(cbase + c) * H + h;
+    const size_t tok = (size_t)t0 * H + h;
+    __syncthreads();  // every read of the previous chunk's tiles is done
+    // ---- stage K, Q, P, T, dO and Diag(gamO) dO as rows
+    rk.template store<LK>(&sm.K[0][0], tid);
+    rq.template store<LK>(&sm.Q[0][0], tid);
+#pragma unroll
+    for (int j = 0; j < rt.J; ++j) {
+      const int pq = tid + kAdjThreads * j;
+      if (pq < rt.NQ) {
+        const int e0 = 4 * pq, w = e0 & 255;
+        int I, Jb;
+        lower_block(e0 >> 8, I, Jb);
+        const int row = 16 * I + (w >> 4), col = 16 * Jb + (w & 15);
+        *reinterpret_cast<bf16x4 *>(&sm.T[row][col]) = rt.x[j];
+        *reinterpret_cast<bf16x4 *>(&sm.P[row][col]) = rp.x[j];
+      }
+    }
+    {
+      const int r = tid / (kAdjBV / 4), c4 = 4 * (tid % (kAdjBV / 4));
+      *reinterpret_cast<bf16x4 *>(&sm.dO[r][c4]) = rdo.x[0];
+      bf16x4 g4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g4[i] = from_f32<__bf16>(rgo * to_f32(rdo.x[0][i]));
+      *reinterpret_cast<bf16x4 *>(&sm.dOg[r][c4]) = g4;
+    }
+    if (tid < kChunk) sm.gam[tid] = rgd;
+    else if (tid < 2 * kChunk) sm.dec[tid - kChunk] = rgd;
+    // dS' (the state in registers) as dS'^T for K dS', and to the workspace for the gradients
+    {
+      float *dst = dSo + ch * DK * (size_t)DV + v0;
+#pragma unroll
+      for (int x = 0; x < NX; ++x) {
+        const int t = wid + NW * x, mi = t >> 1, tj = t & 1;
+        bf16x4 b4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          b4[e] = from_f32<__bf16>(dS[x][e]);
+          dst[(size_t)(16 * mi + 4 * kq + e) * DV + 16 * tj + r16] = dS[x][e];
+        }
+        *reinterpret_cast<bf16x4 *>(&sm.dST[16 * tj + r16][16 * mi + 4 * kq]) = b4;
+      }
+    }
+    __syncthreads();
+    if (c > 0) issue(c - 1);
+
+    // ---- dU = P^T dO + Diag(dec) K dS': tile (ti, tj) = (wid >> 1, wid & 1)
+    const int ti = wid >> 1, tj = wid & 1;
+    {
+      const f32x4 a = mmf<kChunk>(
+          zero4(), lane, [&](int kk) { return col8<LC>(&sm.P[0][0], 16 * ti, kk, lane); },
+          [&](int kk) { return col8<LV>(&sm.dO[0][0], 16 * tj, kk, lane); });
+      const f32x4 y = mmf<DK>(
+          zero4(), lane, [&](int kk) { return row8<LK>(&sm.K[0][0], 16 * ti, kk, lane); },
+          [&](int kk) { return row8<LK>(&sm.dST[0][0], 16 * tj, kk, lane); });
+      float *du = dUo + ch * kChunk * (size_t)DV + v0;
+      bf16x4 b4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * ti + 4 * kq + e;
+        const float u = a[e] + sm.dec[row] * y[e];
+        du[(size_t)row * DV + 16 * tj + r16] = u;
+        b4[e] = from_f32<__bf16>(u);
+      }
+      *reinterpret_cast<bf16x4 *>(&sm.dUT[16 * tj + r16][16 * ti + 4 * kq]) = b4;
+    }
+    __syncthreads();
+    // ---- dR = T^T dU (the same tile); dV = dR on the chunk's tokens
+    {
+      const f32x4 rr = mmf<kChunk>(
+          zero4(), lane, [&](int kk) { return col8<LC>(&sm.T[0][0], 16 * ti, kk, lane); },
+          [&](int kk) { return row8<LC>(&sm.dUT[0][0], 16 * tj, kk, lane); });
+      float *dr = dRo + ch * kChunk * (size_t)DV + v0;
+      bf16x4 b4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * ti + 4 * kq + e, col = 16 * tj + r16;
+        dr[(size_t)row * DV + col] = rr[e];
+        if (row < len) dv[(tok + (size_t)row * H) * DV + v0 + col] = from_f32<__bf16>(rr[e]);
+        b4[e] = from_f32<__bf16>(sm.gam[row] * rr[e]);
+      }
+      *reinterpret_cast<bf16x4 *>(&sm.dRgT[16 * tj + r16][16 * ti + 4 * kq]) = b4;
+    }
+    __syncthreads();
+    // ---- dS = exp(G_last) dS' + Q^T Diag(gamO) dO - K^T Diag(gam) dR, on this wavefront's
+    //      tiles (gamO = gam, over ||q_i|| under the normalised readout)
+    const float gl = sm.gam[kChunk - 1];  // rows past a ragged end repeat G_last
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      const int t = wid + NW * x, mi = t >> 1, sj = t & 1;
+      f32x4 acc = dS[x] * gl;
+      acc = mmf<kChunk>(
+          acc, lane, [&](int kk) { return col8<LK>(&sm.Q[0][0], 16 * mi, kk, lane); },
+          [&](int kk) { return col8<LV>(&sm.dOg[0][0], 16 * sj, kk, lane); });
+      const f32x4 kr = mmf<kChunk>(
+          zero4(), lane, [&](int kk) { return col8<LK>(&sm.K[0][0], 16 * mi, kk, lane); },
+          [&](int kk) { return row8<LC>(&sm.dRgT[0][0], 16 * sj, kk, lane); });
+      dS[x] = acc - kr;
+    }
+  }
+  if (dS0) {
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      const int t = wid + NW * x, mi = t >> 1, tj = t & 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dS0[sbase + (size_t)(16 * mi + 4 * kq + e) * DV + 16 * tj + r16] = dS[x][e];
+    }
+  }
+}
+
+namespace {
+
 // LT: the element type of the d_v-loop tiles: the operand type of the inputs.  Every read of
 // them feeds a product in that precision, so bf16 storage loses nothing and halves the LDS
 // traffic of those products.
@@ -527,9 +757,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const int t = wid + 8 * x, I = t >> 2, J = t & 3;
     f32x4 acc = zero4();
     if (J <= I)
-      acc = mmt<Tin, DK>(
-          acc, lane, [&](int i, int kk) { return sm.K[16 * I + i][kk]; },
-          [&](int kk, int j) { return sm.K[16 * J + j][kk]; });
+      acc = mmr<Tin, DK>(
+          acc, lane, [&](int i, int kk) { return &sm.K[16 * I + i][kk]; },
+          [&](int j, int kk) { return &sm.K[16 * J + j][kk]; });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
@@ -718,9 +948,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       const int t = wid + 8 * x, I = t >> 2, J = t & 3;
       f32x4 acc = zero4();
       if (J <= I)
-        acc = mmt<Tin, DK>(
-            acc, lane, [&](int i, int kk) { return sm.u.pa.Q[16 * I + i][kk]; },
-            [&](int kk, int j) { return sm.K[16 * J + j][kk]; });
+        acc = mmr<Tin, DK>(
+            acc, lane, [&](int i, int kk) { return &sm.u.pa.Q[16 * I + i][kk]; },
+            [&](int j, int kk) { return &sm.K[16 * J + j][kk]; });
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
@@ -954,11 +1184,28 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
   }
   const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
   const int64_t scan_blocks = (int64_t)n_seq * H * (d_v / kAdjBV);
-  if (scan_blocks > 0)
-    hipLaunchKernelGGL((kla_bwd_scan_kernel<Tin, DK>), dim3((unsigned)scan_blocks),
-                       dim3(kAdjThreads), smA, stream, qt, kt, static_cast<const Tin *>(dO), GD,
-                       static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0, dSo,
-                       dU, dR, static_cast<Tin *>(dv), t.cu, t.chunk_off, H, d_v);
+  if (scan_blocks > 0) {
+    if constexpr (sizeof(Tin) == 2) {
+      const size_t sm16 = sizeof(AdjSmem16<DK>);
+      static bool attr16 = false;  // benign race: every thread sets the same value
+      if (!attr16) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&kla_bwd_scan16_kernel<DK>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm16);
+        if (e != hipSuccess) return e;
+        attr16 = true;
+      }
+      hipLaunchKernelGGL((kla_bwd_scan16_kernel<DK>), dim3((unsigned)scan_blocks),
+                         dim3(kAdjThreads), sm16, stream, qt, kt, static_cast<const Tin *>(dO),
+                         GD, static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
+                         dSo, dU, dR, static_cast<Tin *>(dv), t.cu, t.chunk_off, H, d_v);
+    } else {
+      hipLaunchKernelGGL((kla_bwd_scan_kernel<Tin, DK>), dim3((unsigned)scan_blocks),
+                         dim3(kAdjThreads), smA, stream, qt, kt, static_cast<const Tin *>(dO), GD,
+                         static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0, dSo,
+                         dU, dR, static_cast<Tin *>(dv), t.cu, t.chunk_off, H, d_v);
+    }
+  }
   const int64_t grad_blocks = n_chunks_ub * H;
   if (grad_blocks > 0)
     hipLaunchKernelGGL((kla_bwd_grad_kernel<Tin, DK>), dim3((unsigned)grad_blocks),
