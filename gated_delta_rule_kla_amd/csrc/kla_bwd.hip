@@ -664,10 +664,9 @@ struct GradSmem {
     struct {  // the loop over 32-column blocks of d_v
       LT S[DK][LDL], So[DK][LDL];
       LT R[kChunk][LDL], U[kChunk][LDL], dO[kChunk][LDL], dU[kChunk][LDL], dR[kChunk][LDL];
-      // bf16: transposed copies S^T (d_v x d_k) and (Diag(b) R)^T (d_v x tokens), the B
-      // operands of K S and X Diag(b) R read as rows (fp32 tiles have no room for them: those
-      // two products read columns)
-      LT ST[TR ? kAdjBV : 1][TR ? ldt<LT, DK>() : 4], RbT[TR ? kAdjBV : 1][TR ? ldt<LT, kChunk>() : 4];
+      // bf16: Diag(b) R, whose columns (like those of S) the products K S and X Diag(b) R
+      // read by transpose reads (fp32 tiles read their columns element by element)
+      LT Rb[TR ? kChunk : 1][TR ? LDL : 4];
     } lp;
     struct {  // the chunk-local algebra after it
       float Q[kChunk][DK + 4];
@@ -805,16 +804,6 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   for (int v0 = 0; v0 < DV; v0 += kAdjBV) {
     __syncthreads();  // the previous block's reads (and X's writes) are done
     rs.template store<LDL>(&sm.u.lp.S[0][0], tid);
-    // S^T: thread quad (row r, columns c .. c + 3) into column r of rows c .. c + 3
-#pragma unroll
-    for (int j = 0; j < (TR ? rs.J : 0); ++j) {
-      const int e = tid + kGradThreads * j, r = e / (kAdjBV / 4), c = 4 * (e % (kAdjBV / 4));
-      if (rs.NQ % kGradThreads == 0 || e < rs.NQ) {
-        const f32x4 sv = cvt4(rs.x[j]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.u.lp.ST[c + i][r] = from_f32<Tin>(sv[i]);
-      }
-    }
     rso.template store<LDL>(&sm.u.lp.So[0][0], tid);
 #pragma unroll
     for (int j = 0; j < rs.J; ++j) {
@@ -831,9 +820,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     {
       f32x4 y;
       if constexpr (TR)
-        y = mmr<Tin, DK>(
-            zero4(), lane, [&](int i, int kk) { return &sm.K[16 * yi + i][kk]; },
-            [&](int j, int kk) { return &sm.u.lp.ST[16 * yj + j][kk]; });
+        y = mmf<DK>(
+            zero4(), lane, [&](int kk) { return rd8b(&sm.K[16 * yi + r16][kk]); },
+            [&](int kk) { return col8<LDL>(&sm.u.lp.S[0][0], 16 * yj, kk, lane); });
       else
         y = mmt<Tin, DK>(
             zero4(), lane, [&](int i, int kk) { return sm.K[16 * yi + i][kk]; },
@@ -844,16 +833,16 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
         Tin &rv_ = sm.u.lp.R[row][16 * yj + r16];
         const Tin rn = from_f32<Tin>(to_f32(rv_) - sm.gam[row] * y[e]);
         rv_ = rn;
-        if constexpr (TR) sm.u.lp.RbT[16 * yj + r16][row] = from_f32<Tin>(sm.b[row] * to_f32(rn));
+        if constexpr (TR) sm.u.lp.Rb[row][16 * yj + r16] = from_f32<Tin>(sm.b[row] * to_f32(rn));
       }
     }
     __syncthreads();
     {
       f32x4 uu;
       if constexpr (TR)
-        uu = mmr<Tin, kChunk>(
-            zero4(), lane, [&](int i, int kk) { return &sm.X[16 * yi + i][kk]; },
-            [&](int j, int kk) { return &sm.u.lp.RbT[16 * yj + j][kk]; });
+        uu = mmf<kChunk>(
+            zero4(), lane, [&](int kk) { return rd8b(&sm.X[16 * yi + r16][kk]); },
+            [&](int kk) { return col8<LDL>(&sm.u.lp.Rb[0][0], 16 * yj, kk, lane); });
       else
         uu = mmt<Tin, kChunk>(
             zero4(), lane, [&](int i, int kk) { return sm.X[16 * yi + i][kk]; },
