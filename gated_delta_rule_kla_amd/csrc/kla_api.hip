@@ -216,11 +216,11 @@ namespace {
 
 // Backward workspace: the forward layout, then per chunk-head the incoming states S (operand
 // type) and the cotangents dS' of the outgoing ones ([d_k][d_v] fp32), dU and
-// dR ([64][d_v] fp32 each), and the forward output the scan writes again ([tokens][H][d_v],
-// operand type).
+// dR ([64][d_v] fp32 each), the forward output the scan writes again ([tokens][H][d_v],
+// operand type), and X = (I + L)^{-1} (fp32 packed blocks, kTpbElems floats).
 struct BwdLayout {
   WsLayout fw;
-  size_t off_SN, off_dSo, off_dU, off_dR, off_O, total;
+  size_t off_SN, off_dSo, off_dU, off_dR, off_O, off_X, total;
 };
 
 BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, int64_t d_v,
@@ -235,7 +235,8 @@ BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k
   b.off_dU = align256(b.off_dSo + st);
   b.off_dR = align256(b.off_dU + ut);
   b.off_O = align256(b.off_dR + ut);
-  b.total = align256(b.off_O + es * (size_t)total_tokens * (size_t)H * (size_t)d_v);
+  b.off_X = align256(b.off_O + es * (size_t)total_tokens * (size_t)H * (size_t)d_v);
+  b.total = align256(b.off_X + sizeof(float) * nch * (size_t)H * kla::kTpbElems);
   return b;
 }
 
@@ -344,7 +345,8 @@ kla_status enqueue_prepare_diag(const void *q, const void *k, const float *g, co
 kla_status enqueue_prepare(const void *q, const void *k, const float *g, const float *eta, float eps,
                            const kla::CoefOpts &opts, const int32_t *cu_seqlens, int32_t n_seq,
                            int32_t total_tokens, int32_t n_heads, int32_t d_k, kla_dtype dtype,
-                           void *workspace, hipStream_t s, bool split = false) {
+                           void *workspace, hipStream_t s, bool split = false,
+                           float *X_out = nullptr) {
   const WsViews wv =
       ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, false, 0, 0, split);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
@@ -360,7 +362,7 @@ kla_status enqueue_prepare(const void *q, const void *k, const float *g, const f
     return st;
   return hip_status(kla::launch_prep(to_dt(dtype), d_k, q, k, g, eta, eps, opts, wv.tabs, n_seq,
                                      nch_ub, n_heads, nullptr, nullptr, wv.T, false, wv.P, wv.GD,
-                                     pa, s, split),
+                                     pa, s, split, X_out),
                     "prep");
 }
 
@@ -571,11 +573,12 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear any stale error from unrelated work
+  char *ws = static_cast<char *>(workspace);
+  float *Xbuf = reinterpret_cast<float *>(ws + bl.off_X);
   if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
-                            dtype, workspace, s)) != KLA_OK)
+                            dtype, workspace, s, false, Xbuf)) != KLA_OK)
     return st;
   const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype);
-  char *ws = static_cast<char *>(workspace);
   void *SN = ws + bl.off_SN;  // incoming states in the operand type
   if ((st = hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0,
                                         ws + bl.off_O, nullptr, wv.tabs, n_seq, n_heads, s,
@@ -584,7 +587,7 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
     return st;
   if ((st = hip_status(
            kla::launch_bwd(to_dt(dtype), d_k, d_v, q, k, v, dO, g, eta, eps, co, wv.GD, wv.T, wv.P,
-                           dS_T, SN, reinterpret_cast<float *>(ws + bl.off_dSo),
+                           Xbuf, dS_T, SN, reinterpret_cast<float *>(ws + bl.off_dSo),
                            reinterpret_cast<float *>(ws + bl.off_dU),
                            reinterpret_cast<float *>(ws + bl.off_dR), dq, dk, dv, dg, deta, dS0,
                            wv.tabs, n_seq, kla::chunk_upper_bound(n_seq, total_tokens), n_heads,

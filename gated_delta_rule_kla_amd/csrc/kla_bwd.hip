@@ -26,8 +26,9 @@
 //            + rowsum_i(Z) - colsum_i(Z),   Z = dP o P + dA o A,
 //     dG_last += exp(G_last) <dS', S> + sum_j dec_j k_j.(U dS'^T)_j,
 //     dg_t = sum of dG_i over the chunk's positions i >= t.
-// After the forward kernels have run again (the prep, then the chunk scan storing every
-// chunk's incoming state S), two kernels finish the job:
+// After the forward kernels have run again (the prep, which also stores every chunk's
+// X = (I + Diag(b) A)^{-1} in fp32, then the chunk scan storing every chunk's incoming state
+// S), two kernels finish the job:
 //   kla_bwd_scan_kernel  the adjoint scan: sequential over the chunks in reverse, parallel over
 //                        (sequence, head, 32-column slice) since the columns of dS are
 //                        independent given the tiles; stores dS', dU and dR per chunk, writes
@@ -37,9 +38,8 @@
 // Tiles sit in LDS in fp32 (the gradient kernel's d_v-loop tiles in the operand type).
 // Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) for fp32 inputs, and on bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16, operands rounded to bf16 as they are read, fp32 accumulation)
-// for bf16 inputs.  The block inverse X comes from kla_inverse.h.
+// for bf16 inputs.
 #include "kla_device.h"
-#include "kla_inverse.h"
 #include "kla_launch.h"
 
 namespace kla {
@@ -137,14 +137,23 @@ __device__ __forceinline__ f32x4 ld4(const __bf16 *p) {
 
 // Rows [0, len) of a row-strided tensor, columns 0 .. NC - 1 from src, into an fp32 LDS tile
 // with row stride LD; rows past len are zero.
+// Every load of the thread is issued before the first store.
 template <int NC, int LD, int NT, typename Src>
 __device__ __forceinline__ void stage_rows(float *dst, const Src *src, size_t row_stride, int len,
                                            int tid) {
   constexpr int N4 = NC / 4;
-  for (int e = tid; e < kChunk * N4; e += NT) {
-    const int r = e / N4, c = 4 * (e % N4);
-    const f32x4 x = r < len ? ld4(src + (size_t)r * row_stride + c) : zero4();
-    *reinterpret_cast<f32x4 *>(dst + r * LD + c) = x;
+  static_assert((kChunk * N4) % NT == 0, "whole rounds of pieces");
+  constexpr int NPER = kChunk * N4 / NT;
+  f32x4 x[NPER];
+#pragma unroll
+  for (int m = 0; m < NPER; ++m) {
+    const int e = tid + NT * m, r = e / N4, c = 4 * (e % N4);
+    x[m] = r < len ? ld4(src + (size_t)r * row_stride + c) : zero4();
+  }
+#pragma unroll
+  for (int m = 0; m < NPER; ++m) {
+    const int e = tid + NT * m, r = e / N4, c = 4 * (e % N4);
+    *reinterpret_cast<f32x4 *>(dst + r * LD + c) = x[m];
   }
 }
 
@@ -648,10 +657,8 @@ namespace {
 // LT: the element type of the d_v-loop tiles: the operand type of the inputs.  Every read of
 // them feeds a product in that precision, so bf16 storage loses nothing and halves the LDS
 // traffic of those products.
-// Row strides of the d_v-loop tiles, whole 16-byte units: 32 columns (40 bf16 or 36 fp32),
-// and the transposed copies' rows of d_k and of 64 tokens.
+// Row stride of the d_v-loop tiles, whole 16-byte units: 32 columns (40 bf16 or 36 fp32).
 template <typename LT> constexpr int ldl() { return sizeof(LT) == 2 ? 40 : 36; }
-template <typename LT, int N> constexpr int ldt() { return sizeof(LT) == 2 ? N + 8 : N + 4; }
 
 template <typename LT, int DK>
 struct GradSmem {
@@ -691,8 +698,8 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ dO, const float *__restrict__ g, const float *__restrict__ eta,
     float eps, CoefOpts opts, const Tin *__restrict__ SN, const float *__restrict__ dSo,
-    const float *__restrict__ dUo, const float *__restrict__ dRo, Tin *__restrict__ dq,
-    Tin *__restrict__ dk, float *__restrict__ dg, float *__restrict__ deta,
+    const float *__restrict__ dUo, const float *__restrict__ dRo, const float *__restrict__ Xp,
+    Tin *__restrict__ dq, Tin *__restrict__ dk, float *__restrict__ dg, float *__restrict__ deta,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq, int H,
     int DV) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -717,8 +724,32 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
 
+  // ---- X = (I + Diag(b) A)^{-1}: the prep kernel's packed fp32 blocks (ten 16 x 16 blocks on
+  //      and below the diagonal, 640 pieces of four), loaded first, stored after the key rows
+  constexpr int kXPieces = kTpbElems / 4;
+  f32x4 xr[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int e = tid + kGradThreads * x;
+    if (e < kXPieces) xr[x] = *reinterpret_cast<const f32x4 *>(Xp + ch * kTpbElems + 4 * e);
+  }
   // ---- K rows; G, b, the decays
   stage_rows<DK, DK + 4, kGradThreads>(&sm.K[0][0], k + tok * DK, (size_t)H * DK, len, tid);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int e = tid + kGradThreads * x;
+    if (e < kXPieces) {
+      int I, J;
+      lower_block(e >> 6, I, J);
+      const int r = (e >> 2) & 15, c4 = 4 * (e & 3);
+      *reinterpret_cast<f32x4 *>(&sm.X[16 * I + r][16 * J + c4]) = xr[x];
+    }
+  }
+  if (tid < 6 * 64) {  // the six blocks above the diagonal are zero
+    const int ub = tid >> 6, I = ub < 3 ? 0 : ub < 5 ? 1 : 2, J = ub < 3 ? ub + 1 : ub < 5 ? ub - 1 : 3;
+    const int r = (tid >> 2) & 15, c4 = 4 * (tid & 3);
+    *reinterpret_cast<f32x4 *>(&sm.X[16 * I + r][16 * J + c4]) = zero4();
+  }
   if (wid == 0) {
     const float gi = lane < len ? g[tok + (size_t)lane * H] : 0.f;
     const float G = wave_inclusive_scan(gi, lane);  // rows past the end repeat G_last
@@ -765,10 +796,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       sm.A[row][col] = row > col ? __expf(sm.G[row] - sm.G[col]) * acc[e] : 0.f;
     }
   }
-  __syncthreads();
-  // ---- X = (I + Diag(b) A)^{-1} by 16 x 16 blocks (the loop's LDS is free scratch now)
-  blocked_inverse<kGradThreads, LDC, LDC>(&sm.A[0][0], sm.b, &sm.X[0][0], &sm.u.pa.P[0][0],
-                                          tid);
+
 
   // ---- the contractions over d_v, 32 columns at a time:
   //      Y = K S -> R = V - Diag(gam) Y, U = T R; then accumulated in registers
@@ -1153,7 +1181,7 @@ template <typename Tin, int DK>
 static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void *v,
                                const void *dO, const float *g, const float *eta, float eps,
                                const CoefOpts &opts, const float *GD, const void *T,
-                               const void *P, const float *dST,
+                               const void *P, const float *X, const float *dST,
                                const void *SN, float *dSo, float *dU, float *dR, void *dq,
                                void *dk, void *dv, float *dg, float *deta, float *dS0,
                                SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
@@ -1200,7 +1228,7 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
     hipLaunchKernelGGL((kla_bwd_grad_kernel<Tin, DK>), dim3((unsigned)grad_blocks),
                        dim3(kGradThreads), smG, stream, qt, kt, static_cast<const Tin *>(v),
                        static_cast<const Tin *>(dO), g, eta, eps, opts,
-                       static_cast<const Tin *>(SN), dSo, dU, dR,
+                       static_cast<const Tin *>(SN), dSo, dU, dR, X,
                        static_cast<Tin *>(dq), static_cast<Tin *>(dk), dg, deta, t.cu,
                        t.chunk_off, n_seq, H, d_v);
   return hipGetLastError();
@@ -1208,12 +1236,13 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
 
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
-                      const CoefOpts &opts, const float *GD, const void *T, const void *P, const float *dST,
-                      const void *SN, float *dSo, float *dU, float *dR, void *dq, void *dk,
-                      void *dv, float *dg, float *deta, float *dS0, SeqTables t, int32_t n_seq,
-                      int64_t n_chunks_ub, int32_t H, hipStream_t stream) {
+                      const CoefOpts &opts, const float *GD, const void *T, const void *P,
+                      const float *X, const float *dST, const void *SN, float *dSo, float *dU,
+                      float *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
+                      SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
+                      hipStream_t stream) {
 #define KLA_BWD(TIN, DK_)                                                                     \
-  return launch_bwd_t<TIN, DK_>(d_v, q, k, v, dO, g, eta, eps, opts, GD, T, P, dST, SN, dSo, dU, dR, \
+  return launch_bwd_t<TIN, DK_>(d_v, q, k, v, dO, g, eta, eps, opts, GD, T, P, X, dST, SN, dSo, dU, dR, \
                                 dq, dk, dv, dg, deta, dS0, t, n_seq, n_chunks_ub, H, stream);
   if (dt == Dtype::BF16) {
     if (d_k == 128) { KLA_BWD(__bf16, 128) }

@@ -76,8 +76,9 @@ __device__ __forceinline__ f32x4 blk_mma(const f32x4 &a, const f32x4 &b, f32x4 c
 //   sm         the wavefront's scratch, with sm.G2 and sm.beta (per token) already written
 //              and visible to every lane
 //   sync()     makes this wavefront's LDS writes visible to its other lanes
-//   put(row, col, x0, x1, x2, x3)  stores T[row][col .. col + 3]; called for the ten blocks
-//              on and below the diagonal only (blocks above it are zero)
+//   put(row, col, x, bv)  gets X[row][col .. col + 3] = x with bv = b[col .. col + 3], so
+//              that T[row][col + e] = x[e] bv[e]; called for the ten blocks on and below the
+//              diagonal only (blocks above it are zero)
 // SPLIT selects the pair-of-bf16 products for the sub-diagonal blocks (see blk_mma).
 template <typename Tin, int NKS, bool SPLIT, typename Sync, typename Put>
 __device__ __forceinline__ void chunk_T(const typename Frag<Tin>::type (&kf)[4][NKS],
@@ -153,8 +154,7 @@ __device__ __forceinline__ void chunk_T(const typename Frag<Tin>::type (&kf)[4][
     float xv[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) xv[s] = XTi[bidx(4 * kg + s, r16)];  // X_ii[r16][4 kg + s]
-    put(16 * i + r16, 16 * i + 4 * kg, xv[0] * bv[0], xv[1] * bv[1], xv[2] * bv[2],
-        xv[3] * bv[3]);
+    put(16 * i + r16, 16 * i + 4 * kg, f32x4{xv[0], xv[1], xv[2], xv[3]}, bv);
   }
 
   // ---- sub-diagonal blocks, by distance; the blocks of one distance are independent
@@ -178,8 +178,7 @@ __device__ __forceinline__ void chunk_T(const typename Frag<Tin>::type (&kf)[4][
       const f32x4 Zt = blk_mma<SPLIT>(Y, xc, zero4());
       // lane (r16, kg) now holds X_ij[r16][4 kg + e] = -Zt[e]
       const f32x4 bv = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * j + 4 * kg]);
-      put(16 * i + r16, 16 * j + 4 * kg, -Zt[0] * bv[0], -Zt[1] * bv[1], -Zt[2] * bv[2],
-          -Zt[3] * bv[3]);
+      put(16 * i + r16, 16 * j + 4 * kg, f32x4{-Zt[0], -Zt[1], -Zt[2], -Zt[3]}, bv);
       if (i < 3) {  // read again by the next distances
         float *XTo = sm.XT[xslot(i, j)];
 #pragma unroll

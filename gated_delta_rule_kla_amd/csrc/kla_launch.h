@@ -49,12 +49,14 @@ constexpr int kGDFloats = 3 * 64;
 // rows divided by ||q_i|| under the normalised readout).  G_out / beta_out (per token) and
 // GD_out (per chunk-head decay factors) are each optional.  tp_split (bf16, packed): T and
 // P as hi = bf16(x) and lo = bf16(x - hi) blocks, the lo blocks after the hi ones of each
-// chunk-head (twice the packed size).
+// chunk-head (twice the packed size).  X_out (optional): X = (I + L)^{-1} itself in fp32,
+// packed blocks (kTpbElems floats per chunk-head), for the backward pass.
 hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const float *g,
                        const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                        int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
-                       const PlanArgs &pa, hipStream_t stream, bool tp_split = false);
+                       const PlanArgs &pa, hipStream_t stream, bool tp_split = false,
+                       float *X_out = nullptr);
 
 // Diagonal gating: the decayed key and query tiles per chunk-head ([64][d_k] each, operand
 // type) K o exp(G), Q o exp(G), K o exp(G_last - G), and exp(G_last) ([d_k] fp32).
@@ -111,16 +113,17 @@ hipError_t launch_scan_two_level(Dtype dt, int d_k, int d_v, const void *q, cons
                                  const float *S0, void *o, float *S_T, int32_t n_seq, int32_t H,
                                  const SegArgs &sa, float *NM, float *Sin, hipStream_t stream);
 
-// The backward pass after launch_prep (with the same opts) and launch_scan with SN: the adjoint scan (dS' per
-// chunk into dSo, dU and dR into their [chunk][H][64][d_v] fp32 buffers, dv, and dS0 if
-// non-null), then the per-chunk gradients dq, dk (operand type) and dg, deta (fp32).  dST
-// may be null (a zero cotangent of the final state).
+// The backward pass after launch_prep (with the same opts, and X_out = X) and launch_scan
+// with SN: the adjoint scan (dS' per chunk into dSo, dU and dR into their [chunk][H][64][d_v]
+// fp32 buffers, dv, and dS0 if non-null), then the per-chunk gradients dq, dk (operand type)
+// and dg, deta (fp32).  dST may be null (a zero cotangent of the final state).
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
-                      const CoefOpts &opts, const float *GD, const void *T, const void *P, const float *dST,
-                      const void *SN, float *dSo, float *dU, float *dR, void *dq, void *dk,
-                      void *dv, float *dg, float *deta, float *dS0, SeqTables t, int32_t n_seq,
-                      int64_t n_chunks_ub, int32_t H, hipStream_t stream);
+                      const CoefOpts &opts, const float *GD, const void *T, const void *P,
+                      const float *X, const float *dST, const void *SN, float *dSo, float *dU,
+                      float *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
+                      SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
+                      hipStream_t stream);
 
 // a5: one decode step.
 hipError_t launch_decode(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
