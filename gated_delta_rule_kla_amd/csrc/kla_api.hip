@@ -216,11 +216,10 @@ namespace {
 
 // Backward workspace: the forward layout, then per chunk-head the incoming states S (operand
 // type) and the cotangents dS' of the outgoing ones ([d_k][d_v] fp32), dU and
-// dR ([64][d_v] fp32 each), the forward output the scan writes again ([tokens][H][d_v],
-// operand type), and X = (I + L)^{-1} (fp32 packed blocks, kTpbElems floats).
+// dR ([64][d_v] fp32 each), and X = (I + L)^{-1} (fp32 packed blocks, kTpbElems floats).
 struct BwdLayout {
   WsLayout fw;
-  size_t off_SN, off_dSo, off_dU, off_dR, off_O, off_X, total;
+  size_t off_SN, off_dSo, off_dU, off_dR, off_X, total;
 };
 
 BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, int64_t d_v,
@@ -234,8 +233,7 @@ BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k
   b.off_dSo = align256(b.off_SN + es * nch * (size_t)H * (size_t)d_k * (size_t)d_v);
   b.off_dU = align256(b.off_dSo + st);
   b.off_dR = align256(b.off_dU + ut);
-  b.off_O = align256(b.off_dR + ut);
-  b.off_X = align256(b.off_O + es * (size_t)total_tokens * (size_t)H * (size_t)d_v);
+  b.off_X = align256(b.off_dR + ut);
   b.total = align256(b.off_X + sizeof(float) * nch * (size_t)H * kla::kTpbElems);
   return b;
 }
@@ -580,9 +578,9 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
     return st;
   const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype);
   void *SN = ws + bl.off_SN;  // incoming states in the operand type
-  if ((st = hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0,
-                                        ws + bl.off_O, nullptr, wv.tabs, n_seq, n_heads, s,
-                                        nullptr, SN),
+  if ((st = hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, nullptr, k, v, wv.GD, wv.T,
+                                        nullptr, S0, nullptr, nullptr, wv.tabs, n_seq, n_heads,
+                                        s, nullptr, SN),
                        "scan (stored states)")) != KLA_OK)
     return st;
   if ((st = hip_status(

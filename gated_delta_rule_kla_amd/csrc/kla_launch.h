@@ -80,9 +80,9 @@ hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, c
 // a3 + a4: sequential chunk scan with the output fused in; reads T, P and the per-chunk
 // decays GD that launch_prep wrote.  With diag (non-null), the diagonal-gated scan: K and Q
 // come from the decayed tiles, the state update uses K o exp(G_last - G) and the state decays
-// by exp(G_last) per key channel.  With SN (non-null; scalar gate only), also every chunk's
+// by exp(G_last) per key channel.  With SN (non-null; scalar gate only), every chunk's
 // incoming state, [chunk][H][d_k][d_v] in the operand type by global chunk number, for the
-// backward pass.
+// backward pass, and no outputs (q, P and o are not read or written and may be null).
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                        const float *GD, const void *T, const void *P, const float *S0, void *o,
                        float *S_T, SeqTables t, int32_t n_seq, int32_t H, hipStream_t stream,

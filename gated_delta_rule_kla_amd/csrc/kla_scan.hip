@@ -146,11 +146,13 @@ void kla_scan_kernel(
     Tin *__restrict__ SN, SegArgs sa) {
   constexpr int kBV = SHP::BV, kConsumers = SHP::NC, kScanThreads = SHP::THREADS;
   constexpr bool MAP = MODE == kScanMap;
+  // no queries, P or outputs: the map mode, and the states-only pass of the backward
+  constexpr bool NOQP = MAP || STATES;
   static_assert(!SPLIT || (sizeof(Tin) == 2 && !DIAG && !STATES && MODE == kScanSeq),
                 "split precision: bf16 operands, sequential scalar-gate scan");
-  using SM = ScanSmem<Tin, DK, kBV, DIAG, MAP, SPLIT>;
-  using SL = ScanSlot<Tin, DK, kBV, DIAG, MAP, SPLIT>;
-  using DP = DmaPlan<Tin, DK, SHP, DIAG, MAP, SPLIT>;
+  using SM = ScanSmem<Tin, DK, kBV, DIAG, NOQP, SPLIT>;
+  using SL = ScanSlot<Tin, DK, kBV, DIAG, NOQP, SPLIT>;
+  using DP = DmaPlan<Tin, DK, SHP, DIAG, NOQP, SPLIT>;
   using FragT = typename Frag<Tin>::type;
   using KQ = std::integral_constant<int, DK>;
   constexpr bool B16 = sizeof(Tin) == 2;
@@ -257,12 +259,12 @@ void kla_scan_kernel(
     for (int j = 0; j < DP::NK / NP; ++j) {
       const int J = NP * j + pw;
       dma16(rk, s.K + 1024 * J, offK[j]);
-      if constexpr (!MAP) dma16(rq, s.Q + 1024 * J, offK[j]);
+      if constexpr (!NOQP) dma16(rq, s.Q + 1024 * J, offK[j]);
     }
 #pragma unroll
     for (int j = 0; j < DP::NTW; ++j) {
       const int m = NP * j + pw;
-      if (MAP || m < DP::NTC) {
+      if (NOQP || m < DP::NTC) {
         dma16(rt, s.T + 1024 * (m % DP::NTC), offTP[j]);
       } else if (m < 2 * DP::NTC) {
         dma16(rp, s.P + 1024 * (m - DP::NTC), offTP[j]);
@@ -278,9 +280,9 @@ void kla_scan_kernel(
       const int J = NP * j + pw;
       dma16(rv, s.V + 1024 * J, offV[j]);
     }
-    // decays (gam, dec, gamO are consecutive in the slot, 768 bytes; the map mode takes the
+    // decays (gam, dec, gamO are consecutive in the slot, 768 bytes; without outputs the
     // first 512): producer pw fetches its share
-    constexpr int GDB = (MAP ? 512 : 768) / NP;
+    constexpr int GDB = (NOQP ? 512 : 768) / NP;
     if (lane < GDB / 16)
       dma16(rg, reinterpret_cast<unsigned char *>(s.gam) + GDB * pw, GDB * pw + 16 * lane);
     if constexpr (DIAG) {
@@ -300,7 +302,7 @@ void kla_scan_kernel(
   constexpr int PPR = kBV * ES / 16;                     // 16-byte pieces per value-tile row
   constexpr int NST = kChunk * PPR / (64 * NP);          // store instructions per producer wave
   auto p_flush = [&](int c, const SL &s) {
-    if constexpr (MAP) return;  // no outputs
+    if constexpr (NOQP) return;  // no outputs
     const int t0 = tb + c * kChunk;
     const int len = min(kChunk, te - t0);
     const Rsrc ro = make_rsrc(o + ((size_t)t0 * H + h) * DV + v0,
@@ -411,7 +413,7 @@ void kla_scan_kernel(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         fk[t][ks] = rd_frag(s.K, KQ{}, frow(t), ks);
-        if constexpr (!MAP) fq[t][ks] = rd_frag(s.Q, KQ{}, frow(t), ks);
+        if constexpr (!NOQP) fq[t][ks] = rd_frag(s.Q, KQ{}, frow(t), ks);
       }
     // ---- reads for R = V - Diag(gam) Y and U = T R
     FragT ft[6], ftl[SPLIT ? 6 : 1];
@@ -491,7 +493,7 @@ void kla_scan_kernel(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         OT[t] = zero4();
-        if constexpr (!MAP) {
+        if constexpr (!NOQP) {
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) OT[t] = mma(Sop[ks], fq[t][ks], OT[t]);
         }
@@ -527,11 +529,11 @@ void kla_scan_kernel(
         Udopl[1] = accB_res(Ud[2], Ud[3]);
       }
     }
-    // ---- reads for the output: P fragments and this lane's token decays (none in the map
-    //      mode)
+    // ---- reads for the output: P fragments and this lane's token decays (none without
+    //      outputs)
     FragT fp[6], fpl[SPLIT ? 6 : 1];
     float gt[4];
-    if constexpr (!MAP) {
+    if constexpr (!NOQP) {
       fp[0] = rd_tp(s.P, frow(0), 0);
       fp[1] = rd_tp(s.P, frow(1), 0);
       fp[2] = rd_tp(s.P, frow(2), 0);
@@ -563,7 +565,7 @@ void kla_scan_kernel(
         Sacc[m] = mma(fkt[m][1], Udopl[1], Sacc[m]);
       }
     }
-    if constexpr (!MAP) {
+    if constexpr (!NOQP) {
     // ---- O^T = Diag(gam) (Q S)^T + U^T P^T: lane (r16, kg) holds token frow(t), columns
     //      16 cw + 4 kg .. + 3 of this slice.  The block is parked in this wavefront's own
     //      columns of the value tile (read above, and read by no other wavefront); the
@@ -682,9 +684,9 @@ static hipError_t launch_scan_s(int DVs, int64_t units, const void *q, const voi
                                 const float *S0, void *o, float *S_T, SeqTables t, int32_t H,
                                 hipStream_t stream, const DiagTiles *dg, void *SN,
                                 const SegArgs &sa) {
-  constexpr bool MAP = MODE == kScanMap;
-  using SMT = ScanSmem<Tin, DK, SHP::BV, DIAG, MAP, SPLIT>;
-  using SLT = ScanSlot<Tin, DK, SHP::BV, DIAG, MAP, SPLIT>;
+  constexpr bool NOQP = MODE == kScanMap || STATES;
+  using SMT = ScanSmem<Tin, DK, SHP::BV, DIAG, NOQP, SPLIT>;
+  using SLT = ScanSlot<Tin, DK, SHP::BV, DIAG, NOQP, SPLIT>;
   static_assert(sizeof(SMT) <= kLdsBytes, "LDS budget");
   static_assert(offsetof(SLT, dec) == offsetof(SLT, gam) + 256 &&
                     offsetof(SLT, gamO) == offsetof(SLT, gam) + 512,
