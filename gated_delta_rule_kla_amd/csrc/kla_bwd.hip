@@ -129,31 +129,52 @@ __device__ __forceinline__ f32x4 mmr(f32x4 acc, int lane, PA pa, PB pb) {
   return acc;
 }
 
-__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
-__device__ __forceinline__ f32x4 ld4(const __bf16 *p) {
-  const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+// Four consecutive elements as loaded (raw), and as fp32.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> { typedef f32x4 type; };
+template <> struct Raw4<__bf16> { typedef bf16x4 type; };
+__device__ __forceinline__ f32x4 cvt4(const f32x4 &x) { return x; }
+__device__ __forceinline__ f32x4 cvt4(const bf16x4 &x) {
   return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
 }
 
-// Rows [0, len) of a row-strided tensor, columns 0 .. NC - 1 from src, into an fp32 LDS tile
-// with row stride LD; rows past len are zero.
-// Every load of the thread is issued before the first store.
-template <int NC, int LD, int NT, typename Src>
-__device__ __forceinline__ void stage_rows(float *dst, const Src *src, size_t row_stride, int len,
-                                           int tid) {
+// Rows [0, len) of a row-strided tensor, columns 0 .. NC - 1 from src, into an LDS tile with
+// row stride LD (fp32, or bf16 rows copied as they are); rows past len are zero.  Every load
+// of the thread is issued before the first store.  With sq, also each row's squared norm into
+// sq[row] (the NC / 4 consecutive lanes that hold a row reduce it).
+template <int NC, int LD, int NT, typename D, typename Src>
+__device__ __forceinline__ void stage_rows(D *dst, const Src *src, size_t row_stride, int len,
+                                           int tid, float *sq = nullptr) {
   constexpr int N4 = NC / 4;
-  static_assert((kChunk * N4) % NT == 0, "whole rounds of pieces");
+  static_assert((kChunk * N4) % NT == 0 && 64 % N4 == 0, "whole rounds of pieces");
+  static_assert(sizeof(D) == 4 || sizeof(Src) == 2, "bf16 tiles take bf16 rows");
   constexpr int NPER = kChunk * N4 / NT;
-  f32x4 x[NPER];
+  typename Raw4<Src>::type x[NPER];
 #pragma unroll
   for (int m = 0; m < NPER; ++m) {
     const int e = tid + NT * m, r = e / N4, c = 4 * (e % N4);
-    x[m] = r < len ? ld4(src + (size_t)r * row_stride + c) : zero4();
+    typename Raw4<Src>::type z = {};
+    if (r < len) z = *reinterpret_cast<const typename Raw4<Src>::type *>(src + (size_t)r * row_stride + c);
+    x[m] = z;
   }
 #pragma unroll
   for (int m = 0; m < NPER; ++m) {
     const int e = tid + NT * m, r = e / N4, c = 4 * (e % N4);
-    *reinterpret_cast<f32x4 *>(dst + r * LD + c) = x[m];
+    if constexpr (sizeof(D) == 2)
+      *reinterpret_cast<bf16x4 *>(dst + r * LD + c) = x[m];
+    else
+      *reinterpret_cast<f32x4 *>(dst + r * LD + c) = cvt4(x[m]);
+  }
+  if (sq) {
+#pragma unroll
+    for (int m = 0; m < NPER; ++m) {
+      const f32x4 v = cvt4(x[m]);
+      float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+#pragma unroll
+      for (int off = 1; off < N4; off <<= 1) ss += __shfl_xor(ss, off, N4);
+      const int e = tid + NT * m;
+      if (e % N4 == 0) sq[e / N4] = ss;
+    }
   }
 }
 
@@ -162,15 +183,6 @@ __device__ __forceinline__ void stage_rows(float *dst, const Src *src, size_t ro
 __device__ __forceinline__ void lower_block(int b, int &I, int &J) {
   I = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0;
   J = b - I * (I + 1) / 2;
-}
-
-// Four consecutive elements as loaded (raw), and as fp32.
-template <typename T> struct Raw4;
-template <> struct Raw4<float> { typedef f32x4 type; };
-template <> struct Raw4<__bf16> { typedef bf16x4 type; };
-__device__ __forceinline__ f32x4 cvt4(const f32x4 &x) { return x; }
-__device__ __forceinline__ f32x4 cvt4(const bf16x4 &x) {
-  return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
 }
 
 // A tile of NR rows x NC columns of a row-strided tensor, held in registers between its
@@ -664,7 +676,9 @@ template <typename LT, int DK>
 struct GradSmem {
   static constexpr int LDL = ldl<LT>();
   static constexpr bool TR = sizeof(LT) == 2;
-  float K[kChunk][DK + 4];
+  static constexpr int LK = DK + (TR ? 8 : 4);  // row stride of the key and query tiles
+  static constexpr int LG = kChunk + 8;          // row stride of the bf16 64 x 64 tiles
+  LT K[kChunk][LK];  // key rows in the operand type (exact)
   float X[kChunk][LDC];
   float A[kChunk][LDC];
   union {
@@ -676,15 +690,17 @@ struct GradSmem {
       LT Rb[TR ? kChunk : 1][TR ? LDL : 4];
     } lp;
     struct {  // the chunk-local algebra after it
-      float Q[kChunk][DK + 4];
+      LT Q[kChunk][LK];       // query rows in the operand type (not normalised)
       float P[kChunk][LDC];   // P, then W = dT Diag(b) X^T
-      float dP[kChunk][LDC];  // dP, then dP o Gamma
-      float dT[kChunk][LDC];  // dT, then dL, then dA o Gamma
+      float dP[kChunk][LDC];  // dP (fp32: then Diag(rqn) (dP o Gamma))
+      float dT[kChunk][LDC];  // dT, then dL (fp32: then dA o Gamma)
+      // bf16: Diag(rqn) (dP o Gamma) and dA o Gamma + its transpose, for the dq and dk products
+      __bf16 dPq[TR ? kChunk : 1][TR ? LG : 8], dAs[TR ? kChunk : 1][TR ? LG : 8];
     } pa;
   } u;
   float gam[kChunk], dec[kChunk], G[kChunk], b[kChunk], den[kChunk], db[kChunk];
   float db_deta[kChunk];  // the derivative of b in eta
-  float rqn[kChunk];      // 1 / ||q_i|| (normalised readout)
+  float rqn[kChunk];      // the readout's row factor: 1 / ||q_i|| (normalised readout), else 1
   float qdot[2][kChunk];  // q^_i . dq^_i, two partial sums
   float rz[kChunk], cz[kChunk];
   float dots[3][2][kChunk];  // row dots of the three d_v contractions, two partial sums each
@@ -703,7 +719,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq, int H,
     int DV) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  GradSmem<Tin, DK> &sm = *reinterpret_cast<GradSmem<Tin, DK> *>(smem_raw);
+  using SMG = GradSmem<Tin, DK>;
+  SMG &sm = *reinterpret_cast<SMG *>(smem_raw);
+  constexpr int LK = SMG::LK, LG = SMG::LG;
   const int n_chunks = chunk_off[n_seq];
   const int task = blockIdx.x;  // chunk * H + head
   if (task >= n_chunks * H) return;
@@ -727,6 +745,12 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   // ---- X = (I + Diag(b) A)^{-1}: the prep kernel's packed fp32 blocks (ten 16 x 16 blocks on
   //      and below the diagonal, 640 pieces of four), loaded first, stored after the key rows
   constexpr int kXPieces = kTpbElems / 4;
+  // g and eta of token `lane`, for wavefront 0 (the decays and b), loaded first
+  float g_l = 0.f, eta_l = 0.f;
+  if (wid == 0 && lane < len) {
+    g_l = g[tok + (size_t)lane * H];
+    eta_l = eta[tok + (size_t)lane * H];
+  }
   f32x4 xr[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
@@ -734,7 +758,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     if (e < kXPieces) xr[x] = *reinterpret_cast<const f32x4 *>(Xp + ch * kTpbElems + 4 * e);
   }
   // ---- K rows; G, b, the decays
-  stage_rows<DK, DK + 4, kGradThreads>(&sm.K[0][0], k + tok * DK, (size_t)H * DK, len, tid);
+  stage_rows<DK, LK, kGradThreads>(&sm.K[0][0], k + tok * DK, (size_t)H * DK, len, tid, sm.den);
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int e = tid + kGradThreads * x;
@@ -751,29 +775,23 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     *reinterpret_cast<f32x4 *>(&sm.X[16 * I + r][16 * J + c4]) = zero4();
   }
   if (wid == 0) {
-    const float gi = lane < len ? g[tok + (size_t)lane * H] : 0.f;
-    const float G = wave_inclusive_scan(gi, lane);  // rows past the end repeat G_last
+    const float G = wave_inclusive_scan(g_l, lane);  // rows past the end repeat G_last
     const float Gl = __shfl(G, kChunk - 1, kWave);
     sm.G[lane] = G;
     sm.gam[lane] = __expf(G);
     sm.dec[lane] = __expf(Gl - G);
   }
   __syncthreads();
-  {
-    const int i = tid >> 3, part = tid & 7;  // 8 lanes a row
-    float kk = 0.f;
-    for (int cc = part; cc < DK; cc += 8) kk += sm.K[i][cc] * sm.K[i][cc];
-    kk += __shfl_xor(kk, 1, 8);
-    kk += __shfl_xor(kk, 2, 8);
-    kk += __shfl_xor(kk, 4, 8);
-    if (part == 0) {
-      const float den = kk + eps;
+  if (wid == 0) {  // token i = lane; sm.den holds the squared key norms
+    const int i = lane;
+    {
+      const float den = sm.den[i] + eps;
       sm.den[i] = den;
       float bi = 0.f, ci = 0.f;  // b and its derivative in eta
       if (i < len) {
         const float t_abs =
             (float)(t0 + i - cu[n] + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
-        bi = write_coef(opts.beta_mode, eta[tok + (size_t)i * H], den, t_abs);
+        bi = write_coef(opts.beta_mode, eta_l, den, t_abs);
         // every mode but key-norm only is linear in eta: db/deta is the coefficient at eta = 1
         ci = opts.beta_mode == kBetaKeyNorm ? 0.f : write_coef(opts.beta_mode, 1.f, den, t_abs);
       }
@@ -924,7 +942,8 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   __syncthreads();  // the loop's LDS is free
 
   // ---- Q rows, P = lower(Gamma o Q K^T), dP and dT (lower, zeros above)
-  stage_rows<DK, DK + 4, kGradThreads>(&sm.u.pa.Q[0][0], q + tok * DK, (size_t)H * DK, len, tid);
+  stage_rows<DK, LK, kGradThreads>(&sm.u.pa.Q[0][0], q + tok * DK, (size_t)H * DK, len, tid,
+                                   opts.normalize_q ? &sm.qdot[0][0] : nullptr);
   for (int e = tid; e < kChunk * kChunk; e += kGradThreads) {
     const int r = e >> 6, cc = e & 63;
     if ((cc >> 4) > (r >> 4)) { sm.u.pa.dP[r][cc] = 0.f; sm.u.pa.dT[r][cc] = 0.f; }
@@ -944,20 +963,14 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     }
   }
   __syncthreads();
-  // normalised readout: the chunk solve sees q^ = q / ||q|| (0 for a zero query); each
-  // 8-lane group scales its own row in place
-  if (opts.normalize_q) {
-    const int i = tid >> 3, part = tid & 7;
-    float qq = 0.f;
-    for (int cc = part; cc < DK; cc += 8) qq += sm.u.pa.Q[i][cc] * sm.u.pa.Q[i][cc];
-    qq += __shfl_xor(qq, 1, 8);
-    qq += __shfl_xor(qq, 2, 8);
-    qq += __shfl_xor(qq, 4, 8);
-    const float r = qq > 0.f ? 1.f / sqrtf(qq) : 0.f;
-    for (int cc = part; cc < DK; cc += 8) sm.u.pa.Q[i][cc] *= r;
-    if (part == 0) sm.rqn[i] = r;
-    __syncthreads();
-  }
+  // the readout's row factor: the chunk solve sees q^_i = rqn_i q_i, rqn_i = 1 / ||q_i|| under
+  // the normalised readout (0 for a zero query), else 1; Q stays unscaled in LDS
+  auto row_factor = [&](int i) {
+    if (!opts.normalize_q) return 1.f;
+    const float qq = sm.qdot[0][i];
+    return qq > 0.f ? 1.f / sqrtf(qq) : 0.f;
+  };
+  if (tid < kChunk) sm.rqn[tid] = row_factor(tid);
   {
     // P's lower blocks, two jobs per wavefront (10 blocks; zeros above the diagonal blocks)
 #pragma unroll
@@ -971,10 +984,11 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
-        sm.u.pa.P[row][col] = col <= row ? __expf(sm.G[row] - sm.G[col]) * acc[e] : 0.f;
+        sm.u.pa.P[row][col] =
+            col <= row ? row_factor(row) * __expf(sm.G[row] - sm.G[col]) * acc[e] : 0.f;
       }
     }
-    // row dots q_i . qa_i, k_i . ka_i, k_i . kb_i: this wavefront's partial over its column
+    // row dots q^_i . qa_i, k_i . ka_i, k_i . kb_i: this wavefront's partial over its column
     // tiles, then its 16-lane row sums
     float dq4[4] = {0.f, 0.f, 0.f, 0.f}, da4[4] = {0.f, 0.f, 0.f, 0.f}, db4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -983,9 +997,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * mti + 4 * kq + e;
-        dq4[e] += qa[m][e] * sm.u.pa.Q[row][col];
-        da4[e] += ka[m][e] * sm.K[row][col];
-        db4[e] += kb[m][e] * sm.K[row][col];
+        dq4[e] += qa[m][e] * to_f32(sm.u.pa.Q[row][col]);
+        da4[e] += ka[m][e] * to_f32(sm.K[row][col]);
+        db4[e] += kb[m][e] * to_f32(sm.K[row][col]);
       }
     }
 #pragma unroll
@@ -995,7 +1009,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       db4[e] = row16_sum(db4[e]);
       if (r16 == 0) {
         const int row = 16 * mti + 4 * kq + e;
-        sm.dots[0][wid >> 2][row] = dq4[e];
+        sm.dots[0][wid >> 2][row] = row_factor(row) * dq4[e];
         sm.dots[1][wid >> 2][row] = da4[e];
         sm.dots[2][wid >> 2][row] = db4[e];
       }
@@ -1085,31 +1099,69 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     }
   }
   __syncthreads();
-  // ---- dP o Gamma and dA o Gamma in place
+  // ---- Diag(rqn) (dP o Gamma) and dA o Gamma (dA = Diag(b) dL, strictly lower): fp32 in
+  //      place; bf16 as tiles for the products below, the latter with its transpose added
+  //      (off the diagonal one of the two terms is zero)
   for (int e = tid; e < kChunk * kChunk; e += kGradThreads) {
     const int r = e >> 6, cc = e & 63;
     const float gm = cc <= r ? __expf(sm.G[r] - sm.G[cc]) : 0.f;
-    sm.u.pa.dP[r][cc] *= gm;
-    sm.u.pa.dT[r][cc] *= sm.b[r] * gm;
+    const float pq = sm.u.pa.dP[r][cc] * gm * sm.rqn[r];
+    if constexpr (TR) {
+      const int ra = cc < r ? r : cc, ca = cc < r ? cc : r;  // the entry below the diagonal
+      const float as =
+          ra > ca ? sm.u.pa.dT[ra][ca] * sm.b[ra] * __expf(sm.G[ra] - sm.G[ca]) : 0.f;
+      sm.u.pa.dPq[r][cc] = from_f32<__bf16>(pq);
+      sm.u.pa.dAs[r][cc] = from_f32<__bf16>(as);
+    } else {
+      sm.u.pa.dP[r][cc] = pq;
+      sm.u.pa.dT[r][cc] *= sm.b[r] * gm;
+    }
   }
   __syncthreads();
-  // ---- dq = qa + (dP o Gamma) K;  dk = ka + kb + (dP o Gamma)^T Q + (dA o Gamma) K
-  //      + (dA o Gamma)^T K - Diag(2 b db / den) K
+  // ---- Diag(rqn) dq^ = Diag(rqn) qa + Diag(rqn) (dP o Gamma) K (dq^: the gradient in q^);
+  //      dk = ka + kb + (Diag(rqn) (dP o Gamma))^T Q + (dA o Gamma) K + (dA o Gamma)^T K
+  //      - Diag(2 b db / den) K
   f32x4 aqs[NM];
+  // bf16: this wavefront's 16 rows of the 64-wide left operands, as 16-byte runs (rows of
+  // dPq and dAs, columns of dPq by transpose reads), read once for all its column tiles
+  [[maybe_unused]] bf16x8 fP[2], fPt[2], fS[2];
+  if constexpr (TR) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int kk = 32 * x + 8 * kq;
+      fP[x] = row8<LG>(&sm.u.pa.dPq[0][0], 16 * mti, kk, lane);
+      fPt[x] = col8<LG>(&sm.u.pa.dPq[0][0], 16 * mti, kk, lane);
+      fS[x] = row8<LG>(&sm.u.pa.dAs[0][0], 16 * mti, kk, lane);
+    }
+  }
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const int tj = (wid >> 2) + 2 * m;
-    f32x4 aq = mmt<Tin, kChunk>(
-        qa[m], lane, [&](int i, int kk) { return sm.u.pa.dP[16 * mti + i][kk]; },
-        [&](int kk, int j) { return sm.K[kk][16 * tj + j]; });
-    f32x4 ak = ka[m] + kb[m];
-    ak = mmt<Tin, kChunk>(
-        ak, lane, [&](int i, int kk) { return sm.u.pa.dP[kk][16 * mti + i]; },
-        [&](int kk, int j) { return sm.u.pa.Q[kk][16 * tj + j]; });
-    ak = mmt<Tin, kChunk>(
-        ak, lane,
-        [&](int i, int kk) { return sm.u.pa.dT[16 * mti + i][kk] + sm.u.pa.dT[kk][16 * mti + i]; },
-        [&](int kk, int j) { return sm.K[kk][16 * tj + j]; });
+    f32x4 aq = qa[m], ak = ka[m] + kb[m];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) aq[e] *= sm.rqn[16 * mti + 4 * kq + e];
+    if constexpr (TR) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int kk = 32 * x + 8 * kq;
+        const bf16x8 bk = col8<LK>(&sm.K[0][0], 16 * tj, kk, lane);
+        const bf16x8 bq = col8<LK>(&sm.u.pa.Q[0][0], 16 * tj, kk, lane);
+        aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fP[x], bk, aq, 0, 0, 0);
+        ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fPt[x], bq, ak, 0, 0, 0);
+        ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fS[x], bk, ak, 0, 0, 0);
+      }
+    } else {
+      aq = mmt<Tin, kChunk>(
+          aq, lane, [&](int i, int kk) { return sm.u.pa.dP[16 * mti + i][kk]; },
+          [&](int kk, int j) { return sm.K[kk][16 * tj + j]; });
+      ak = mmt<Tin, kChunk>(
+          ak, lane, [&](int i, int kk) { return sm.u.pa.dP[kk][16 * mti + i]; },
+          [&](int kk, int j) { return sm.u.pa.Q[kk][16 * tj + j]; });
+      ak = mmt<Tin, kChunk>(
+          ak, lane,
+          [&](int i, int kk) { return sm.u.pa.dT[16 * mti + i][kk] + sm.u.pa.dT[kk][16 * mti + i]; },
+          [&](int kk, int j) { return sm.K[kk][16 * tj + j]; });
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * mti + 4 * kq + e, col = 16 * tj + r16;
@@ -1118,7 +1170,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       const float cb = opts.beta_mode != kBetaGated && den != 0.f
                            ? -2.f * sm.b[row] * sm.db[row] * __builtin_amdgcn_rcpf(den)
                            : 0.f;
-      ak[e] += cb * sm.K[row][col];
+      ak[e] += cb * to_f32(sm.K[row][col]);
       if (row < len) {
         const size_t o = (tok + (size_t)row * H) * DK + col;
         if (!opts.normalize_q) dq[o] = from_f32<Tin>(aq[e]);
@@ -1127,14 +1179,15 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     }
     aqs[m] = aq;
   }
-  // normalised readout: dq = (dq^ - (q^ . dq^) q^) / ||q||
+  // normalised readout: dq = rqn (dq^ - (q^ . dq^) q^) = aq - rqn^2 (q . aq) q with
+  // aq = Diag(rqn) dq^ as formed above
   if (opts.normalize_q) {
     float pd[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int col = 16 * ((wid >> 2) + 2 * m) + r16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pd[e] += aqs[m][e] * sm.u.pa.Q[16 * mti + 4 * kq + e][col];
+      for (int e = 0; e < 4; ++e) pd[e] += aqs[m][e] * to_f32(sm.u.pa.Q[16 * mti + 4 * kq + e][col]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1151,7 +1204,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
         const float d = sm.qdot[0][row] + sm.qdot[1][row];
         if (row < len)
           dq[(tok + (size_t)row * H) * DK + col] =
-              from_f32<Tin>(sm.rqn[row] * (aqs[m][e] - d * sm.u.pa.Q[row][col]));
+              from_f32<Tin>(aqs[m][e] - sm.rqn[row] * sm.rqn[row] * d * to_f32(sm.u.pa.Q[row][col]));
       }
     }
   }
