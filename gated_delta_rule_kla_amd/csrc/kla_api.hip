@@ -214,9 +214,9 @@ size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t 
 
 namespace {
 
-// Backward workspace: the forward layout, then per chunk-head the incoming states S (operand
-// type) and the cotangents dS' of the outgoing ones ([d_k][d_v] fp32), dU and
-// dR ([64][d_v] fp32 each), and X = (I + L)^{-1} (fp32 packed blocks, kTpbElems floats).
+// Backward workspace: the forward layout, then per chunk-head the incoming states S and the
+// cotangents dS' of the outgoing ones ([d_k][d_v]), dU and dR ([64][d_v] each), all in the
+// operand type, and X = (I + L)^{-1} (fp32 packed blocks, kTpbElems floats).
 struct BwdLayout {
   WsLayout fw;
   size_t off_SN, off_dSo, off_dU, off_dR, off_X, total;
@@ -227,8 +227,8 @@ BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k
   BwdLayout b;
   b.fw = ws_layout(n_seq, total_tokens, H, d_k, es);
   const size_t nch = (size_t)kla::chunk_upper_bound(n_seq, total_tokens);
-  const size_t st = sizeof(float) * nch * (size_t)H * (size_t)d_k * (size_t)d_v;
-  const size_t ut = sizeof(float) * nch * (size_t)H * KLA_CHUNK * (size_t)d_v;
+  const size_t st = es * nch * (size_t)H * (size_t)d_k * (size_t)d_v;
+  const size_t ut = es * nch * (size_t)H * KLA_CHUNK * (size_t)d_v;
   b.off_SN = b.fw.total;
   b.off_dSo = align256(b.off_SN + es * nch * (size_t)H * (size_t)d_k * (size_t)d_v);
   b.off_dU = align256(b.off_dSo + st);
@@ -585,9 +585,8 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
     return st;
   if ((st = hip_status(
            kla::launch_bwd(to_dt(dtype), d_k, d_v, q, k, v, dO, g, eta, eps, co, wv.GD, wv.T, wv.P,
-                           Xbuf, dS_T, SN, reinterpret_cast<float *>(ws + bl.off_dSo),
-                           reinterpret_cast<float *>(ws + bl.off_dU),
-                           reinterpret_cast<float *>(ws + bl.off_dR), dq, dk, dv, dg, deta, dS0,
+                           Xbuf, dS_T, SN, ws + bl.off_dSo, ws + bl.off_dU, ws + bl.off_dR, dq,
+                           dk, dv, dg, deta, dS0,
                            wv.tabs, n_seq, kla::chunk_upper_bound(n_seq, total_tokens), n_heads,
                            s),
            "backward")) != KLA_OK)

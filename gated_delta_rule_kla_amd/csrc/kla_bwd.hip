@@ -220,6 +220,20 @@ struct RegTile {
       }
     }
   }
+  // each row's squared norm into sq[row] (the NC / 4 consecutive lanes holding a row reduce it)
+  __device__ __forceinline__ void sqnorms(float *sq, int tid) const {
+    constexpr int N4 = NC / 4;
+    static_assert(NQ % NT == 0 && 64 % N4 == 0, "whole rows within a wavefront");
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const f32x4 v = cvt4(x[j]);
+      float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+#pragma unroll
+      for (int off = 1; off < N4; off <<= 1) ss += __shfl_xor(ss, off, N4);
+      const int e = tid + NT * j;
+      if (e % N4 == 0) sq[e / N4] = ss;
+    }
+  }
 };
 
 // A 64 x 64 matrix stored as its ten lower 16 x 16 blocks (the prep kernel's packed T and P),
@@ -490,8 +504,8 @@ template <int DK>
 __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ dO,
     const float *__restrict__ GD, const __bf16 *__restrict__ Tm, const __bf16 *__restrict__ Pm,
-    const float *__restrict__ dST, float *__restrict__ dS0, float *__restrict__ dSo,
-    float *__restrict__ dUo, float *__restrict__ dRo, __bf16 *__restrict__ dv,
+    const float *__restrict__ dST, float *__restrict__ dS0, __bf16 *__restrict__ dSo,
+    __bf16 *__restrict__ dUo, __bf16 *__restrict__ dRo, __bf16 *__restrict__ dv,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV) {
   using SM = AdjSmem16<DK>;
   constexpr int LK = SM::LK, LC = SM::LC, LV = SM::LV;
@@ -582,8 +596,9 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
     if (tid < kChunk) sm.gam[tid] = rgd;
     else if (tid < 2 * kChunk) sm.dec[tid - kChunk] = rgd;
     // dS' (the state in registers) as dS'^T for K dS', and to the workspace for the gradients
+    // (bf16, the slice's d_k x 32 block contiguous)
     {
-      float *dst = dSo + ch * DK * (size_t)DV + v0;
+      __bf16 *dst = dSo + ch * DK * (size_t)DV + (size_t)v0 * DK;
 #pragma unroll
       for (int x = 0; x < NX; ++x) {
         const int t = wid + NW * x, mi = t >> 1, tj = t & 1;
@@ -591,7 +606,7 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           b4[e] = from_f32<__bf16>(dS[x][e]);
-          dst[(size_t)(16 * mi + 4 * kq + e) * DV + 16 * tj + r16] = dS[x][e];
+          dst[(16 * mi + 4 * kq + e) * kAdjBV + 16 * tj + r16] = b4[e];
         }
         *reinterpret_cast<bf16x4 *>(&sm.dST[16 * tj + r16][16 * mi + 4 * kq]) = b4;
       }
@@ -608,14 +623,13 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
       const f32x4 y = mmf<DK>(
           zero4(), lane, [&](int kk) { return row8<LK>(&sm.K[0][0], 16 * ti, kk, lane); },
           [&](int kk) { return row8<LK>(&sm.dST[0][0], 16 * tj, kk, lane); });
-      float *du = dUo + ch * kChunk * (size_t)DV + v0;
+      __bf16 *du = dUo + ch * kChunk * (size_t)DV + (size_t)v0 * kChunk;
       bf16x4 b4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * ti + 4 * kq + e;
-        const float u = a[e] + sm.dec[row] * y[e];
-        du[(size_t)row * DV + 16 * tj + r16] = u;
-        b4[e] = from_f32<__bf16>(u);
+        b4[e] = from_f32<__bf16>(a[e] + sm.dec[row] * y[e]);
+        du[row * kAdjBV + 16 * tj + r16] = b4[e];
       }
       *reinterpret_cast<bf16x4 *>(&sm.dUT[16 * tj + r16][16 * ti + 4 * kq]) = b4;
     }
@@ -625,13 +639,14 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
       const f32x4 rr = mmf<kChunk>(
           zero4(), lane, [&](int kk) { return col8<LC>(&sm.T[0][0], 16 * ti, kk, lane); },
           [&](int kk) { return row8<LC>(&sm.dUT[0][0], 16 * tj, kk, lane); });
-      float *dr = dRo + ch * kChunk * (size_t)DV + v0;
+      __bf16 *dr = dRo + ch * kChunk * (size_t)DV + (size_t)v0 * kChunk;
       bf16x4 b4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * ti + 4 * kq + e, col = 16 * tj + r16;
-        dr[(size_t)row * DV + col] = rr[e];
-        if (row < len) dv[(tok + (size_t)row * H) * DV + v0 + col] = from_f32<__bf16>(rr[e]);
+        const __bf16 rb = from_f32<__bf16>(rr[e]);
+        dr[row * kAdjBV + col] = rb;
+        if (row < len) dv[(tok + (size_t)row * H) * DV + v0 + col] = rb;
         b4[e] = from_f32<__bf16>(sm.gam[row] * rr[e]);
       }
       *reinterpret_cast<bf16x4 *>(&sm.dRgT[16 * tj + r16][16 * ti + 4 * kq]) = b4;
@@ -678,9 +693,12 @@ struct GradSmem {
   static constexpr bool TR = sizeof(LT) == 2;
   static constexpr int LK = DK + (TR ? 8 : 4);  // row stride of the key and query tiles
   static constexpr int LG = kChunk + 8;          // row stride of the bf16 64 x 64 tiles
+  // bf16: the query rows and P sit outside the union (staged and formed before the d_v loop)
+  static constexpr bool QO = TR;
   LT K[kChunk][LK];  // key rows in the operand type (exact)
+  LT Qo[QO ? kChunk : 1][QO ? LK : 8];
   float X[kChunk][LDC];
-  float A[kChunk][LDC];
+  float Po[QO ? kChunk : 1][QO ? LDC : 4];
   union {
     struct {  // the loop over 32-column blocks of d_v
       LT S[DK][LDL], So[DK][LDL];
@@ -690,8 +708,8 @@ struct GradSmem {
       LT Rb[TR ? kChunk : 1][TR ? LDL : 4];
     } lp;
     struct {  // the chunk-local algebra after it
-      LT Q[kChunk][LK];       // query rows in the operand type (not normalised)
-      float P[kChunk][LDC];   // P, then W = dT Diag(b) X^T
+      LT Qi[QO ? 1 : kChunk][QO ? 8 : LK];
+      float Pi[QO ? 1 : kChunk][QO ? 4 : LDC];
       float dP[kChunk][LDC];  // dP (fp32: then Diag(rqn) (dP o Gamma))
       float dT[kChunk][LDC];  // dT, then dL (fp32: then dA o Gamma)
       // bf16: Diag(rqn) (dP o Gamma) and dA o Gamma + its transpose, for the dq and dk products
@@ -701,8 +719,18 @@ struct GradSmem {
   float gam[kChunk], dec[kChunk], G[kChunk], b[kChunk], den[kChunk], db[kChunk];
   float db_deta[kChunk];  // the derivative of b in eta
   float rqn[kChunk];      // the readout's row factor: 1 / ||q_i|| (normalised readout), else 1
-  float qdot[2][kChunk];  // q^_i . dq^_i, two partial sums
+  float qdot[2][kChunk];  // squared query norms, then q^_i . dq^_i as two partial sums
   float rz[kChunk], cz[kChunk];
+  float zr[4][kChunk], zc[4][kChunk];  // dL o A row sums and Diag(b) (dL o A) column sums,
+                                       // one partial per 16-column (16-row) tile
+  // query rows in the operand type (not normalised) and P = Diag(rqn) lower(Gamma o Q K^T),
+  // then W = dT Diag(b) X^T in P's place
+  __device__ LT *Q() {
+    if constexpr (QO) return &Qo[0][0]; else return &u.pa.Qi[0][0];
+  }
+  __device__ float *P() {
+    if constexpr (QO) return &Po[0][0]; else return &u.pa.Pi[0][0];
+  }
   float dots[3][2][kChunk];  // row dots of the three d_v contractions, two partial sums each
   float red[kGradThreads / 64];
 };
@@ -713,8 +741,8 @@ template <typename Tin, int DK>
 __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ dO, const float *__restrict__ g, const float *__restrict__ eta,
-    float eps, CoefOpts opts, const Tin *__restrict__ SN, const float *__restrict__ dSo,
-    const float *__restrict__ dUo, const float *__restrict__ dRo, const float *__restrict__ Xp,
+    float eps, CoefOpts opts, const Tin *__restrict__ SN, const Tin *__restrict__ dSo,
+    const Tin *__restrict__ dUo, const Tin *__restrict__ dRo, const float *__restrict__ Xp,
     Tin *__restrict__ dq, Tin *__restrict__ dk, float *__restrict__ dg, float *__restrict__ deta,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq, int H,
     int DV) {
@@ -722,6 +750,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   using SMG = GradSmem<Tin, DK>;
   SMG &sm = *reinterpret_cast<SMG *>(smem_raw);
   constexpr int LK = SMG::LK, LG = SMG::LG;
+  constexpr bool QO = SMG::QO;
   const int n_chunks = chunk_off[n_seq];
   const int task = blockIdx.x;  // chunk * H + head
   if (task >= n_chunks * H) return;
@@ -757,8 +786,17 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const int e = tid + kGradThreads * x;
     if (e < kXPieces) xr[x] = *reinterpret_cast<const f32x4 *>(Xp + ch * kTpbElems + 4 * e);
   }
-  // ---- K rows; G, b, the decays
-  stage_rows<DK, LK, kGradThreads>(&sm.K[0][0], k + tok * DK, (size_t)H * DK, len, tid, sm.den);
+  // ---- K rows (and, bf16, Q rows) with their squared norms; G, b, the decays
+  RegTile<Tin, kChunk, DK, kGradThreads> rk;
+  RegTile<Tin, QO ? kChunk : 4, QO ? DK : 4, kGradThreads> rq;
+  rk.load(k + tok * DK, (size_t)H * DK, len, tid);
+  if constexpr (QO) rq.load(q + tok * DK, (size_t)H * DK, len, tid);
+  rk.template store<LK>(&sm.K[0][0], tid);
+  rk.sqnorms(sm.den, tid);
+  if constexpr (QO) {
+    rq.template store<LK>(sm.Q(), tid);
+    if (opts.normalize_q) rq.sqnorms(&sm.qdot[0][0], tid);
+  }
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int e = tid + kGradThreads * x;
@@ -799,20 +837,35 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       sm.db_deta[i] = ci;
     }
   }
-  // ---- A = strict_lower(Gamma o K K^T): all 16 tiles, two per wavefront (zeros above)
+  // the readout's row factor: the chunk solve sees q^_i = rqn_i q_i, rqn_i = 1 / ||q_i|| under
+  // the normalised readout (0 for a zero query), else 1; Q stays unscaled in LDS
+  auto row_factor = [&](int i) {
+    if (!opts.normalize_q) return 1.f;
+    const float qq = sm.qdot[0][i];
+    return qq > 0.f ? 1.f / sqrtf(qq) : 0.f;
+  };
+  // P = Diag(rqn) lower(Gamma o Q K^T), two 16 x 16 tiles per wavefront (zeros above the
+  // diagonal blocks)
+  auto form_P = [&]() {
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int t = wid + 8 * x, I = t >> 2, J = t & 3;
-    f32x4 acc = zero4();
-    if (J <= I)
-      acc = mmr<Tin, DK>(
-          acc, lane, [&](int i, int kk) { return &sm.K[16 * I + i][kk]; },
-          [&](int j, int kk) { return &sm.K[16 * J + j][kk]; });
+    for (int x = 0; x < 2; ++x) {
+      const int t = wid + 8 * x, I = t >> 2, J = t & 3;
+      f32x4 acc = zero4();
+      if (J <= I)
+        acc = mmr<Tin, DK>(
+            acc, lane, [&](int i, int kk) { return sm.Q() + (16 * I + i) * LK + kk; },
+            [&](int j, int kk) { return &sm.K[16 * J + j][kk]; });
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
-      sm.A[row][col] = row > col ? __expf(sm.G[row] - sm.G[col]) * acc[e] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
+        sm.P()[row * LDC + col] =
+            col <= row ? row_factor(row) * __expf(sm.G[row] - sm.G[col]) * acc[e] : 0.f;
+      }
     }
+  };
+  if constexpr (QO) {
+    if (tid < kChunk) sm.rqn[tid] = row_factor(tid);
+    form_P();
   }
 
 
@@ -829,20 +882,27 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   for (int x = 0; x < 3; ++x) pt[x] = zero4();
   float sc = 0.f;
   const Tin *Sb = SN + ch * DK * (size_t)DV;
-  const float *Sob = dSo + ch * DK * (size_t)DV;
-  const float *dUb = dUo + ch * kChunk * (size_t)DV, *dRb = dRo + ch * kChunk * (size_t)DV;
+  const Tin *Sob = dSo + ch * DK * (size_t)DV;
+  const Tin *dUb = dUo + ch * kChunk * (size_t)DV, *dRb = dRo + ch * kChunk * (size_t)DV;
+  // dS', dU and dR as the adjoint scan left them: bf16, each 32-column slice's block
+  // contiguous; fp32, row-major over all d_v columns
+  constexpr bool SLM = sizeof(Tin) == 2;
   // each 32-column block is loaded into registers while the one before it is computed
-  RegTile<Tin, DK, kAdjBV, kGradThreads> rs;
-  RegTile<float, DK, kAdjBV, kGradThreads> rso;
-  RegTile<Tin, kChunk, kAdjBV, kGradThreads> rv, rdo;
-  RegTile<float, kChunk, kAdjBV, kGradThreads> rdu, rdr;
+  RegTile<Tin, DK, kAdjBV, kGradThreads> rs, rso;
+  RegTile<Tin, kChunk, kAdjBV, kGradThreads> rv, rdo, rdu, rdr;
   auto issue = [&](int v0) {
     rs.load(Sb + v0, (size_t)DV, DK, tid);
-    rso.load(Sob + v0, (size_t)DV, DK, tid);
     rv.load(v + tok * DV + v0, (size_t)H * DV, len, tid);
     rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
-    rdu.load(dUb + v0, (size_t)DV, kChunk, tid);
-    rdr.load(dRb + v0, (size_t)DV, kChunk, tid);
+    if constexpr (SLM) {
+      rso.load(Sob + (size_t)v0 * DK, kAdjBV, DK, tid);
+      rdu.load(dUb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
+      rdr.load(dRb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
+    } else {
+      rso.load(Sob + v0, (size_t)DV, DK, tid);
+      rdu.load(dUb + v0, (size_t)DV, kChunk, tid);
+      rdr.load(dRb + v0, (size_t)DV, kChunk, tid);
+    }
   };
   issue(0);
   constexpr int LDL = GradSmem<Tin, DK>::LDL;
@@ -853,8 +913,8 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     rso.template store<LDL>(&sm.u.lp.So[0][0], tid);
 #pragma unroll
     for (int j = 0; j < rs.J; ++j) {
-      const f32x4 sv = cvt4(rs.x[j]);
-      sc += sv[0] * rso.x[j][0] + sv[1] * rso.x[j][1] + sv[2] * rso.x[j][2] + sv[3] * rso.x[j][3];
+      const f32x4 sv = cvt4(rs.x[j]), so = cvt4(rso.x[j]);
+      sc += sv[0] * so[0] + sv[1] * so[1] + sv[2] * so[2] + sv[3] * so[3];
     }
     rv.template store<LDL>(&sm.u.lp.R[0][0], tid);
     rdo.template store<LDL>(&sm.u.lp.dO[0][0], tid);
@@ -941,12 +1001,18 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   if (lane == 0) sm.red[wid] = sc;
   __syncthreads();  // the loop's LDS is free
 
-  // ---- Q rows, P = lower(Gamma o Q K^T), dP and dT (lower, zeros above)
-  stage_rows<DK, LK, kGradThreads>(&sm.u.pa.Q[0][0], q + tok * DK, (size_t)H * DK, len, tid,
-                                   opts.normalize_q ? &sm.qdot[0][0] : nullptr);
+  // ---- dP and dT (lower, zeros above); bf16: also Diag(rqn) (dP o Gamma) for the dq products.
+  //      fp32: the query rows, then P
+  if constexpr (!QO)
+    stage_rows<DK, LK, kGradThreads>(sm.Q(), q + tok * DK, (size_t)H * DK, len, tid,
+                                     opts.normalize_q ? &sm.qdot[0][0] : nullptr);
   for (int e = tid; e < kChunk * kChunk; e += kGradThreads) {
     const int r = e >> 6, cc = e & 63;
-    if ((cc >> 4) > (r >> 4)) { sm.u.pa.dP[r][cc] = 0.f; sm.u.pa.dT[r][cc] = 0.f; }
+    if ((cc >> 4) > (r >> 4)) {
+      sm.u.pa.dP[r][cc] = 0.f;
+      sm.u.pa.dT[r][cc] = 0.f;
+      if constexpr (TR) sm.u.pa.dPq[r][cc] = from_f32<__bf16>(0.f);
+    }
   }
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
@@ -959,34 +1025,18 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
         dst[row][col] = col <= row ? pt[x][e] : 0.f;
+        if constexpr (TR)
+          if (jb < 10)
+            sm.u.pa.dPq[row][col] = from_f32<__bf16>(
+                col <= row ? sm.rqn[row] * __expf(sm.G[row] - sm.G[col]) * pt[x][e] : 0.f);
       }
     }
   }
   __syncthreads();
-  // the readout's row factor: the chunk solve sees q^_i = rqn_i q_i, rqn_i = 1 / ||q_i|| under
-  // the normalised readout (0 for a zero query), else 1; Q stays unscaled in LDS
-  auto row_factor = [&](int i) {
-    if (!opts.normalize_q) return 1.f;
-    const float qq = sm.qdot[0][i];
-    return qq > 0.f ? 1.f / sqrtf(qq) : 0.f;
-  };
-  if (tid < kChunk) sm.rqn[tid] = row_factor(tid);
   {
-    // P's lower blocks, two jobs per wavefront (10 blocks; zeros above the diagonal blocks)
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int t = wid + 8 * x, I = t >> 2, J = t & 3;
-      f32x4 acc = zero4();
-      if (J <= I)
-        acc = mmr<Tin, DK>(
-            acc, lane, [&](int i, int kk) { return &sm.u.pa.Q[16 * I + i][kk]; },
-            [&](int j, int kk) { return &sm.K[16 * J + j][kk]; });
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
-        sm.u.pa.P[row][col] =
-            col <= row ? row_factor(row) * __expf(sm.G[row] - sm.G[col]) * acc[e] : 0.f;
-      }
+    if constexpr (!QO) {
+      if (tid < kChunk) sm.rqn[tid] = row_factor(tid);
+      form_P();
     }
     // row dots q^_i . qa_i, k_i . ka_i, k_i . kb_i: this wavefront's partial over its column
     // tiles, then its 16-lane row sums
@@ -997,7 +1047,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * mti + 4 * kq + e;
-        dq4[e] += qa[m][e] * to_f32(sm.u.pa.Q[row][col]);
+        dq4[e] += qa[m][e] * to_f32(sm.Q()[row * LK + col]);
         da4[e] += ka[m][e] * to_f32(sm.K[row][col]);
         db4[e] += kb[m][e] * to_f32(sm.K[row][col]);
       }
@@ -1015,7 +1065,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       }
     }
   }
-  __syncthreads();
+  if constexpr (!QO) __syncthreads();  // P formed just above
   // ---- db from T: column sums of dT o X; the dP o P part of Z's row and column sums
   //      (8 lanes a row or column, 8 entries each); W = dT Diag(b) X^T into registers
   const int rc = tid >> 3, part = tid & 7;  // row / column rc, entries part + 8 m
@@ -1025,8 +1075,8 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     for (int m = 0; m < 8; ++m) {
       const int x = part + 8 * m;
       s1 += sm.u.pa.dT[x][rc] * sm.X[x][rc];
-      s2 += sm.u.pa.dP[rc][x] * sm.u.pa.P[rc][x];
-      s3 += sm.u.pa.dP[x][rc] * sm.u.pa.P[x][rc];
+      s2 += sm.u.pa.dP[rc][x] * sm.P()[rc * LDC + x];
+      s3 += sm.u.pa.dP[x][rc] * sm.P()[x * LDC + rc];
     }
 #pragma unroll
     for (int off = 1; off < 8; off <<= 1) {
@@ -1053,71 +1103,76 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   for (int x = 0; x < 2; ++x) {
     const int t = wid + 8 * x, I = t >> 2, J = t & 3;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.u.pa.P[16 * I + 4 * kq + e][16 * J + r16] = w[x][e];
+    for (int e = 0; e < 4; ++e) sm.P()[(16 * I + 4 * kq + e) * LDC + 16 * J + r16] = w[x][e];
   }
   __syncthreads();
-  // ---- dL = -strict_lower(X^T W) into dT's place
+  // ---- dL = -strict_lower(X^T W) into dT's place (dT's last readers are past two barriers);
+  //      bf16: dA o Gamma + its transpose as a tile (dA = Diag(b) dL); with A =
+  //      strict_lower(Gamma o K K^T) formed here tile by tile, the row sums of dL o A and the
+  //      column sums of Diag(b) (dL o A), one partial per tile
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int t = wid + 8 * x, I = t >> 2, J = t & 3;
-    f32x4 acc = zero4();
-    if (J <= I)
+    f32x4 acc = zero4(), kk4 = zero4();
+    if (J <= I) {
       acc = mmt<Tin, kChunk>(
           acc, lane, [&](int i, int kk) { return sm.X[kk][16 * I + i]; },
-          [&](int kk, int j) { return sm.u.pa.P[kk][16 * J + j]; });
-    w[x] = acc;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int t = wid + 8 * x, I = t >> 2, J = t & 3;
+          [&](int kk, int j) { return sm.P()[kk * LDC + 16 * J + j]; });
+      kk4 = mmr<Tin, DK>(
+          kk4, lane, [&](int i, int kk) { return &sm.K[16 * I + i][kk]; },
+          [&](int j, int kk) { return &sm.K[16 * J + j][kk]; });
+    }
+    float zr4[4], zc = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
-      sm.u.pa.dT[row][col] = col < row ? -w[x][e] : 0.f;
+      const bool lower = col < row;
+      const float gm = lower ? __expf(sm.G[row] - sm.G[col]) : 0.f;
+      const float dl = lower ? -acc[e] : 0.f;
+      sm.u.pa.dT[row][col] = dl;
+      const float la = dl * gm * kk4[e];  // (dL o A)[row][col]
+      zr4[e] = la;
+      zc += sm.b[row] * la;
+      if constexpr (TR) {
+        const __bf16 av = from_f32<__bf16>(sm.b[row] * gm * dl);
+        if (lower) {
+          sm.u.pa.dAs[row][col] = av;
+          sm.u.pa.dAs[col][row] = av;
+        } else if (col == row) {
+          sm.u.pa.dAs[row][col] = av;  // zero
+        }
+      }
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      zr4[e] = row16_sum(zr4[e]);
+      if (r16 == 0) sm.zr[J][16 * I + 4 * kq + e] = zr4[e];
+    }
+    zc += __shfl_xor(zc, 16, kWave);
+    zc += __shfl_xor(zc, 32, kWave);
+    if (kq == 0) sm.zc[I][16 * J + r16] = zc;
   }
   __syncthreads();
   // ---- db += row sums of dL o A; the dA o A part of Z (dA = Diag(b) dL)
-  {
-    float s4 = 0.f, s5 = 0.f;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int x = part + 8 * m;
-      s4 += sm.u.pa.dT[rc][x] * sm.A[rc][x];
-      s5 += sm.b[x] * sm.u.pa.dT[x][rc] * sm.A[x][rc];
-    }
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) {
-      s4 += __shfl_xor(s4, off, 8);
-      s5 += __shfl_xor(s5, off, 8);
-    }
-    if (part == 0) {
-      sm.db[rc] += s4;
-      sm.rz[rc] += sm.b[rc] * s4;
-      sm.cz[rc] += s5;
-    }
+  if (tid < kChunk) {
+    const int i = tid;
+    const float s4 = sm.zr[0][i] + sm.zr[1][i] + sm.zr[2][i] + sm.zr[3][i];
+    sm.db[i] += s4;
+    sm.rz[i] += sm.b[i] * s4;
+    sm.cz[i] += sm.zc[0][i] + sm.zc[1][i] + sm.zc[2][i] + sm.zc[3][i];
   }
   __syncthreads();
-  // ---- Diag(rqn) (dP o Gamma) and dA o Gamma (dA = Diag(b) dL, strictly lower): fp32 in
-  //      place; bf16 as tiles for the products below, the latter with its transpose added
-  //      (off the diagonal one of the two terms is zero)
-  for (int e = tid; e < kChunk * kChunk; e += kGradThreads) {
-    const int r = e >> 6, cc = e & 63;
-    const float gm = cc <= r ? __expf(sm.G[r] - sm.G[cc]) : 0.f;
-    const float pq = sm.u.pa.dP[r][cc] * gm * sm.rqn[r];
-    if constexpr (TR) {
-      const int ra = cc < r ? r : cc, ca = cc < r ? cc : r;  // the entry below the diagonal
-      const float as =
-          ra > ca ? sm.u.pa.dT[ra][ca] * sm.b[ra] * __expf(sm.G[ra] - sm.G[ca]) : 0.f;
-      sm.u.pa.dPq[r][cc] = from_f32<__bf16>(pq);
-      sm.u.pa.dAs[r][cc] = from_f32<__bf16>(as);
-    } else {
-      sm.u.pa.dP[r][cc] = pq;
+  // ---- fp32: Diag(rqn) (dP o Gamma) and dA o Gamma (dA = Diag(b) dL) in place (the bf16 path
+  //      formed them as tiles above)
+  if constexpr (!TR) {
+    for (int e = tid; e < kChunk * kChunk; e += kGradThreads) {
+      const int r = e >> 6, cc = e & 63;
+      const float gm = cc <= r ? __expf(sm.G[r] - sm.G[cc]) : 0.f;
+      sm.u.pa.dP[r][cc] *= gm * sm.rqn[r];
       sm.u.pa.dT[r][cc] *= sm.b[r] * gm;
     }
+    __syncthreads();
   }
-  __syncthreads();
   // ---- Diag(rqn) dq^ = Diag(rqn) qa + Diag(rqn) (dP o Gamma) K (dq^: the gradient in q^);
   //      dk = ka + kb + (Diag(rqn) (dP o Gamma))^T Q + (dA o Gamma) K + (dA o Gamma)^T K
   //      - Diag(2 b db / den) K
@@ -1145,7 +1200,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       for (int x = 0; x < 2; ++x) {
         const int kk = 32 * x + 8 * kq;
         const bf16x8 bk = col8<LK>(&sm.K[0][0], 16 * tj, kk, lane);
-        const bf16x8 bq = col8<LK>(&sm.u.pa.Q[0][0], 16 * tj, kk, lane);
+        const bf16x8 bq = col8<LK>(sm.Q(), 16 * tj, kk, lane);
         aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fP[x], bk, aq, 0, 0, 0);
         ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fPt[x], bq, ak, 0, 0, 0);
         ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fS[x], bk, ak, 0, 0, 0);
@@ -1156,7 +1211,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
           [&](int kk, int j) { return sm.K[kk][16 * tj + j]; });
       ak = mmt<Tin, kChunk>(
           ak, lane, [&](int i, int kk) { return sm.u.pa.dP[kk][16 * mti + i]; },
-          [&](int kk, int j) { return sm.u.pa.Q[kk][16 * tj + j]; });
+          [&](int kk, int j) { return sm.Q()[kk * LK + 16 * tj + j]; });
       ak = mmt<Tin, kChunk>(
           ak, lane,
           [&](int i, int kk) { return sm.u.pa.dT[16 * mti + i][kk] + sm.u.pa.dT[kk][16 * mti + i]; },
@@ -1187,7 +1242,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     for (int m = 0; m < NM; ++m) {
       const int col = 16 * ((wid >> 2) + 2 * m) + r16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pd[e] += aqs[m][e] * to_f32(sm.u.pa.Q[16 * mti + 4 * kq + e][col]);
+      for (int e = 0; e < 4; ++e) pd[e] += aqs[m][e] * to_f32(sm.Q()[(16 * mti + 4 * kq + e) * LK + col]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1204,7 +1259,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
         const float d = sm.qdot[0][row] + sm.qdot[1][row];
         if (row < len)
           dq[(tok + (size_t)row * H) * DK + col] =
-              from_f32<Tin>(aqs[m][e] - sm.rqn[row] * sm.rqn[row] * d * to_f32(sm.u.pa.Q[row][col]));
+              from_f32<Tin>(aqs[m][e] - sm.rqn[row] * sm.rqn[row] * d * to_f32(sm.Q()[row * LK + col]));
       }
     }
   }
@@ -1235,7 +1290,7 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
                                const void *dO, const float *g, const float *eta, float eps,
                                const CoefOpts &opts, const float *GD, const void *T,
                                const void *P, const float *X, const float *dST,
-                               const void *SN, float *dSo, float *dU, float *dR, void *dq,
+                               const void *SN, void *dSo, void *dU, void *dR, void *dq,
                                void *dk, void *dv, float *dg, float *deta, float *dS0,
                                SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                                hipStream_t stream) {
@@ -1268,12 +1323,16 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
       hipLaunchKernelGGL((kla_bwd_scan16_kernel<DK>), dim3((unsigned)scan_blocks),
                          dim3(kAdjThreads), sm16, stream, qt, kt, static_cast<const Tin *>(dO),
                          GD, static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
-                         dSo, dU, dR, static_cast<Tin *>(dv), t.cu, t.chunk_off, H, d_v);
+                         static_cast<__bf16 *>(dSo), static_cast<__bf16 *>(dU),
+                         static_cast<__bf16 *>(dR), static_cast<Tin *>(dv), t.cu, t.chunk_off, H,
+                         d_v);
     } else {
       hipLaunchKernelGGL((kla_bwd_scan_kernel<Tin, DK>), dim3((unsigned)scan_blocks),
                          dim3(kAdjThreads), smA, stream, qt, kt, static_cast<const Tin *>(dO), GD,
-                         static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0, dSo,
-                         dU, dR, static_cast<Tin *>(dv), t.cu, t.chunk_off, H, d_v);
+                         static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
+                         static_cast<float *>(dSo), static_cast<float *>(dU),
+                         static_cast<float *>(dR), static_cast<Tin *>(dv), t.cu, t.chunk_off, H,
+                         d_v);
     }
   }
   const int64_t grad_blocks = n_chunks_ub * H;
@@ -1281,7 +1340,8 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
     hipLaunchKernelGGL((kla_bwd_grad_kernel<Tin, DK>), dim3((unsigned)grad_blocks),
                        dim3(kGradThreads), smG, stream, qt, kt, static_cast<const Tin *>(v),
                        static_cast<const Tin *>(dO), g, eta, eps, opts,
-                       static_cast<const Tin *>(SN), dSo, dU, dR, X,
+                       static_cast<const Tin *>(SN), static_cast<const Tin *>(dSo),
+                       static_cast<const Tin *>(dU), static_cast<const Tin *>(dR), X,
                        static_cast<Tin *>(dq), static_cast<Tin *>(dk), dg, deta, t.cu,
                        t.chunk_off, n_seq, H, d_v);
   return hipGetLastError();
@@ -1290,8 +1350,8 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
                       const CoefOpts &opts, const float *GD, const void *T, const void *P,
-                      const float *X, const float *dST, const void *SN, float *dSo, float *dU,
-                      float *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
+                      const float *X, const float *dST, const void *SN, void *dSo, void *dU,
+                      void *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
                       SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                       hipStream_t stream) {
 #define KLA_BWD(TIN, DK_)                                                                     \

@@ -114,14 +114,15 @@ hipError_t launch_scan_two_level(Dtype dt, int d_k, int d_v, const void *q, cons
                                  const SegArgs &sa, float *NM, float *Sin, hipStream_t stream);
 
 // The backward pass after launch_prep (with the same opts, and X_out = X) and launch_scan
-// with SN: the adjoint scan (dS' per chunk into dSo, dU and dR into their [chunk][H][64][d_v]
-// fp32 buffers, dv, and dS0 if non-null), then the per-chunk gradients dq, dk (operand type)
-// and dg, deta (fp32).  dST may be null (a zero cotangent of the final state).
+// with SN: the adjoint scan (per chunk-head dS' ([d_k][d_v]), dU and dR ([64][d_v]) in the
+// operand type into dSo, dU and dR: fp32 row-major, or bf16 with each 32-column slice's block
+// contiguous; dv, and dS0 if non-null), then the per-chunk gradients dq, dk (operand type) and
+// dg, deta (fp32).  dST may be null (a zero cotangent of the final state).
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
                       const CoefOpts &opts, const float *GD, const void *T, const void *P,
-                      const float *X, const float *dST, const void *SN, float *dSo, float *dU,
-                      float *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
+                      const float *X, const float *dST, const void *SN, void *dSo, void *dU,
+                      void *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
                       SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                       hipStream_t stream);
 

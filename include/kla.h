@@ -325,10 +325,9 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const
  *   workspace   device buffer of at least kla_prefill_backward_workspace_bytes
  *               bytes, 256-byte aligned; contents are scratch.  It holds the
  *               forward chunk stage run again (with every chunk's
- *               (I + L)^{-1} in fp32), every chunk's incoming state in the
- *               element type `dtype` (bf16 for bf16 inputs), and in fp32 the
- *               cotangent of every chunk's outgoing state and the per-chunk dU
- *               and dR.
+ *               (I + L)^{-1} in fp32), and in the element type `dtype` (bf16
+ *               for bf16 inputs) every chunk's incoming state, the cotangent
+ *               of its outgoing state and its dU and dR.
  * The gradient buffers must not overlap each other, the inputs or the
  * workspace.  q, k, v, dO, dq, dk and dv must be 16-byte aligned; g, eta, S0,
  * dS_T, dg, deta and dS0 4-byte aligned.  Size limits and errors as for

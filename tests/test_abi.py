@@ -303,14 +303,13 @@ def _bwd_call(lib, **over):
 
 def test_backward_workspace_and_errors(lib):
     # the backward workspace holds the forward one plus, per chunk-head, the incoming state
-    # (d_k x d_v in the operand type, bf16 by default), the outgoing state's cotangent
-    # (d_k x d_v fp32), dU and dR (64 x d_v fp32 each), and (I + L)^{-1} (ten 16 x 16 fp32
-    # blocks)
+    # and the outgoing state's cotangent (d_k x d_v each), dU and dR (64 x d_v each), all in
+    # the operand type (bf16 by default), and (I + L)^{-1} (ten 16 x 16 fp32 blocks)
     n_seq, n_tok, H, dk, dv = 4, 16384, 16, 128, 128
     nch = (n_tok + 63) // 64 + n_seq
     nb = kla.kla_prefill_backward_workspace_bytes(n_seq, n_tok, H, dk, dv)
     base = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv)
-    assert nb >= base + nch * H * (2 * dk * dv + 4 * dk * dv + 4 * 2 * 64 * dv + 4 * 10 * 256)
+    assert nb >= base + nch * H * (2 * (2 * dk * dv + 2 * 64 * dv) + 4 * 10 * 256)
     assert nb % 256 == 0
     assert kla.kla_prefill_backward_workspace_bytes(n_seq, n_tok, H, 96, dv) == 0
     cases = [
