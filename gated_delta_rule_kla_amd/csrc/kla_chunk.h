@@ -30,6 +30,38 @@ __host__ __device__ constexpr int xslot(int i, int j) {
   return i == j ? i : (i == 1 ? 4 : (j == 0 ? 5 : 6));
 }
 
+// Entries (row, col .. col + 3) of a chunk's 64 x 64 output, col a multiple of 4, straight
+// from registers: in the packed layout (tpb_off; entries of the blocks above the diagonal are
+// not stored) or row-major.  A lane group (r16, kg) covering one 16 x 16 block writes its
+// 256 contiguous packed elements, so a store instruction writes whole lines.
+template <typename T>
+__device__ __forceinline__ void out_put(T *dst, bool packed, int row, int col, float a, float b,
+                                        float c, float d, bool split = false) {
+  int off;
+  if (packed) {
+    const int I = row >> 4, J = col >> 4;
+    if (J > I) return;
+    off = (I * (I + 1) / 2 + J) * 256 + (row & 15) * 16 + (col & 15);
+  } else {
+    off = row * kChunk + col;
+  }
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 x4;
+    x4[0] = from_f32<T>(a); x4[1] = from_f32<T>(b); x4[2] = from_f32<T>(c); x4[3] = from_f32<T>(d);
+    *reinterpret_cast<bf16x4 *>(dst + off) = x4;
+    if (split) {  // the rounding residuals, one packed tile further on
+      bf16x4 l4;
+      l4[0] = from_f32<T>(a - to_f32(x4[0]));
+      l4[1] = from_f32<T>(b - to_f32(x4[1]));
+      l4[2] = from_f32<T>(c - to_f32(x4[2]));
+      l4[3] = from_f32<T>(d - to_f32(x4[3]));
+      *reinterpret_cast<bf16x4 *>(dst + kTpbElems + off) = l4;
+    }
+  } else {
+    *reinterpret_cast<f32x4 *>(dst + off) = f32x4{a, b, c, d};
+  }
+}
+
 // Scratch of one wavefront's solve.
 struct PrepSmem {
   alignas(16) float Ld[4][256];  // diagonal blocks of L, row-major
@@ -69,50 +101,14 @@ __device__ __forceinline__ f32x4 blk_mma(const f32x4 &a, const f32x4 &b, f32x4 c
   }
 }
 
-// T = (I + L)^{-1} Diag(b) of one chunk from its key rows, by one wavefront.
-//   kf[b][ks]  key rows 16 b + r16 as A fragments (elements 32 ks + 8 kg .. + 7)
-//   gd[i]      the diagonal Gram tiles K_i K_i^T (fp32 accumulators)
-//   bme[i]     b of row 16 i + r16;  G2me[i] its G * log2(e)
-//   sm         the wavefront's scratch, with sm.G2 and sm.beta (per token) already written
-//              and visible to every lane
-//   sync()     makes this wavefront's LDS writes visible to its other lanes
-//   put(row, col, x, bv)  gets X[row][col .. col + 3] = x with bv = b[col .. col + 3], so
-//              that T[row][col + e] = x[e] bv[e]; called for the ten blocks on and below the
-//              diagonal only (blocks above it are zero)
-// SPLIT selects the pair-of-bf16 products for the sub-diagonal blocks (see blk_mma).
-template <typename Tin, int NKS, bool SPLIT, typename Sync, typename Put>
-__device__ __forceinline__ void chunk_T(const typename Frag<Tin>::type (&kf)[4][NKS],
-                                        const f32x4 (&gd)[4], const float (&bme)[4],
-                                        const float (&G2me)[4], PrepSmem &sm, Sync sync,
-                                        Put put) {
+// The solve proper: X = (I + L)^{-1} and the callbacks put(row, col, x, bv) as for chunk_T,
+// from L's sub-diagonal blocks in registers (Lr[i][j], j < i: lane (r16, kg) holds row
+// 16 i + r16, columns 16 j + 4 kg + e) and its diagonal blocks in sm.Ld (strictly lower,
+// bidx layout), with sm.beta written; both visible to every lane of the wavefront.
+template <bool SPLIT, typename Sync, typename Put>
+__device__ __forceinline__ void chunk_inverse(const f32x4 (&Lr)[4][3], PrepSmem &sm, Sync sync,
+                                              Put put) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, kg = lane >> 4;
-  // ---- L: diagonal blocks to LDS (row-major), sub-diagonal blocks kept in registers in the
-  //      A-operand layout (row r16, columns 4 kg + e); each tile is formed as K_j K_i^T
-  f32x4 Lr[4][3];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j <= i; ++j) {
-      const int j0 = 16 * j + 4 * kg;
-      f32x4 acc = gd[i];
-      if (j < i) {
-        acc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) acc = mma(kf[j][ks], kf[i][ks], acc);
-      }
-      const f32x4 Gc = *reinterpret_cast<const f32x4 *>(&sm.G2[j0]);
-      f32x4 lv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool below = (j < i) || (4 * kg + e < r16);  // column < row
-        lv[e] = bme[i] * exp2_fast(below ? G2me[i] - Gc[e] : -INFINITY) * acc[e];
-      }
-      if (j < i) Lr[i][j] = lv;
-      else *reinterpret_cast<f32x4 *>(&sm.Ld[i][bidx(r16, 4 * kg)]) = lv;
-    }
-  }
-  sync();
-
   // ---- diagonal blocks: lane group kg inverts I + L_kk by substitution, lane = column r16;
   //      rows of L_kk are read four values at a time (one address per lane group)
   {
@@ -187,6 +183,53 @@ __device__ __forceinline__ void chunk_T(const typename Frag<Tin>::type (&kf)[4][
     }
     sync();
   }
+}
+
+
+// T = (I + L)^{-1} Diag(b) of one chunk from its key rows, by one wavefront.
+//   kf[b][ks]  key rows 16 b + r16 as A fragments (elements 32 ks + 8 kg .. + 7)
+//   gd[i]      the diagonal Gram tiles K_i K_i^T (fp32 accumulators)
+//   bme[i]     b of row 16 i + r16;  G2me[i] its G * log2(e)
+//   sm         the wavefront's scratch, with sm.G2 and sm.beta (per token) already written
+//              and visible to every lane
+//   sync()     makes this wavefront's LDS writes visible to its other lanes
+//   put(row, col, x, bv)  gets X[row][col .. col + 3] = x with bv = b[col .. col + 3], so
+//              that T[row][col + e] = x[e] bv[e]; called for the ten blocks on and below the
+//              diagonal only (blocks above it are zero)
+// SPLIT selects the pair-of-bf16 products for the sub-diagonal blocks (see blk_mma).
+template <typename Tin, int NKS, bool SPLIT, typename Sync, typename Put>
+__device__ __forceinline__ void chunk_T(const typename Frag<Tin>::type (&kf)[4][NKS],
+                                        const f32x4 (&gd)[4], const float (&bme)[4],
+                                        const float (&G2me)[4], PrepSmem &sm, Sync sync,
+                                        Put put) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, kg = lane >> 4;
+  // ---- L: diagonal blocks to LDS (row-major), sub-diagonal blocks kept in registers in the
+  //      A-operand layout (row r16, columns 4 kg + e); each tile is formed as K_j K_i^T
+  f32x4 Lr[4][3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j <= i; ++j) {
+      const int j0 = 16 * j + 4 * kg;
+      f32x4 acc = gd[i];
+      if (j < i) {
+        acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = mma(kf[j][ks], kf[i][ks], acc);
+      }
+      const f32x4 Gc = *reinterpret_cast<const f32x4 *>(&sm.G2[j0]);
+      f32x4 lv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool below = (j < i) || (4 * kg + e < r16);  // column < row
+        lv[e] = bme[i] * exp2_fast(below ? G2me[i] - Gc[e] : -INFINITY) * acc[e];
+      }
+      if (j < i) Lr[i][j] = lv;
+      else *reinterpret_cast<f32x4 *>(&sm.Ld[i][bidx(r16, 4 * kg)]) = lv;
+    }
+  }
+  sync();
+  chunk_inverse<SPLIT>(Lr, sm, sync, put);
 }
 
 }  // namespace kla

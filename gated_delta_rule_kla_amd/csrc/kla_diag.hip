@@ -14,19 +14,28 @@
 // chunk scan then runs as for the scalar gate on Kg, Qg, Kd in place of K, Q (see
 // kla_scan.hip), with unit decays and the per-channel state decay exp(G_last).
 //
-// One 1024-lane workgroup per (chunk, head), everything staged in LDS in fp32.  Every decay
-// factor is an exponential of a non-positive difference of log-decays (G_i - G_j with j <= i,
-// G_last - G_j, or the tile-anchored pieces of the A and P sums), so nothing overflows
-// whatever the decay.  X = (I + Diag(b) A)^{-1} comes from kla_inverse.h.
+// One workgroup of d_k / 32 wavefronts per (chunk, head); wavefront w owns the 32 key
+// channels [32 w, 32 w + 32) and lane (r16, kq) the rows 16 I + r16 (I = 0..3) of channels
+// 32 w + 8 kq .. + 7, which is the operand layout of one 16x16x32 matrix-core step.  So the
+// sums over channels of A and P become matrix-core products once the decay is split between
+// the two operands, with an anchor row a between the rows j < a <= i of every pair:
+//   exp(G_i - G_j) = exp(G_i - G_a) exp(G_a - G_j),  both factors at most 1,
+// so nothing overflows whatever the decay.  Off the diagonal 16 x 16 blocks the anchor is the
+// first row of block I; within a diagonal block, the first row of each 4-row group (one
+// product per group, the other rows masked to zero); the pairs within one 4-row group take
+// exp(G_i - G_j) directly.  Each wavefront sums its 32 channels; the partial tiles meet in
+// LDS.  bf16 operands are split into hi = bf16(x) and lo = bf16(x - hi) and multiplied as
+// hi hi + hi lo + lo hi (about 2^-16 relative error, the precision of the fp32 sums they
+// replace); fp32 operands use the fp32 matrix core.  Wavefront 0 then solves
+// X = (I + Diag(b) A)^{-1} (the prep kernel's blocked solve) and writes T; wavefront 1
+// writes P.
+#include "kla_chunk.h"
 #include "kla_device.h"
-#include "kla_inverse.h"
 #include "kla_launch.h"
 
 namespace kla {
 
 namespace {
-
-constexpr int kDiagThreads = 1024;
 
 __device__ __forceinline__ int find_seq(const int32_t *__restrict__ chunk_off, int n_seq, int c) {
   int lo = 0, hi = n_seq - 1;
@@ -39,35 +48,99 @@ __device__ __forceinline__ int find_seq(const int32_t *__restrict__ chunk_off, i
 
 template <int DK>
 struct DiagSmem {
-  // rows of DK + 4 floats: 16-byte aligned for the pair loops' float4 reads, and offset by
-  // one bank group from row to row
-  alignas(16) float K[kChunk][DK + 4];
-  alignas(16) float Q[kChunk][DK + 4];
-  alignas(16) float G[kChunk][DK + 4];
-  float A[kChunk][kChunk + 1], P[kChunk][kChunk + 1], X[kChunk][kChunk + 1];
-  float b[kChunk], rq[kChunk];
+  static constexpr int NW = DK / 32;
+  // partial tiles (ten 16 x 16 blocks each, one 16-byte piece per lane): A from wavefronts
+  // 1 .. NW - 1, P from wavefronts 0, 2 .. NW - 1
+  f32x4 pa[NW - 1][10][64], pp[NW - 1][10][64];
+  float nk[NW][kChunk], nq[NW][kChunk];  // partial squared norms of the key and query rows
+  PrepSmem ps;                           // wavefront 0's solve
 };
 
-// four consecutive values, one 16-byte (fp32) or 8-byte (bf16) store
-__device__ __forceinline__ void put4(float *dst, const f32x4 &x) {
-  *reinterpret_cast<f32x4 *>(dst) = x;
+// one wavefront's LDS writes visible to its other lanes (LDS work of a wavefront is done in
+// order; the fences keep the compiler from moving accesses across)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-__device__ __forceinline__ void put4(__bf16 *dst, const f32x4 &x) {
-  bf16x4 b;
+
+// x from the lane d lanes lower in the same 16-lane row, 0 for the first d lanes
+__device__ __forceinline__ float row_shr(float x, int d) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (d) {
+    case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+// x from lane m of the same group of four lanes
+__device__ __forceinline__ float quad_bcast(float x, int m) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (m) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, v, 0x00, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x55, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0xAA, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, v, 0xFF, 0xF, 0xF, false); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// acc += the 16 x 16 product over 32 channels with lane (r16, kq) supplying row r16 of the
+// left operand a and column r16 of the right one b at channels 8 kq .. + 7: bf16 inputs as
+// hi/lo bf16 pairs on 16x16x32 steps, fp32 inputs as eight exact 16x16x4 steps
+template <typename Tin>
+__device__ __forceinline__ f32x4 dot32(f32x4 acc, const float (&a)[8], const float (&b)[8]) {
+  if constexpr (sizeof(Tin) == 2) {
+    bf16x8 ah, al, bh, bl;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) b[i] = from_f32<__bf16>(x[i]);
-  *reinterpret_cast<bf16x4 *>(dst) = b;
+    for (int s = 0; s < 8; ++s) {
+      ah[s] = from_f32<__bf16>(a[s]);
+      al[s] = from_f32<__bf16>(a[s] - to_f32(ah[s]));
+      bh[s] = from_f32<__bf16>(b[s]);
+      bl[s] = from_f32<__bf16>(b[s] - to_f32(bh[s]));
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    return acc;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_row8(const T *p, float (&x)[8]) {
+  const typename Frag<T>::type v = load8<T>(p);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) x[s] = to_f32(v[s]);
+}
+__device__ __forceinline__ void store_row8(float *p, const float (&x)[8]) {
+  *reinterpret_cast<f32x4 *>(p) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4 *>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+__device__ __forceinline__ void store_row8(__bf16 *p, const float (&x)[8]) {
+  bf16x8 b;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) b[s] = from_f32<__bf16>(x[s]);
+  *reinterpret_cast<bf16x8 *>(p) = b;
 }
 
 }  // namespace
 
 template <typename Tin, int DK>
-__global__ __launch_bounds__(kDiagThreads) void kla_prep_diag_kernel(
+__global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ eta, float eps, CoefOpts opts, SeqTables tabs, int n_seq, int H,
     Tin *__restrict__ T_out, Tin *__restrict__ P_out, float *__restrict__ GD_out,
     Tin *__restrict__ KG_out, Tin *__restrict__ QG_out, Tin *__restrict__ KD_out,
     float *__restrict__ GC_out) {
+  constexpr int NW = DK / 32;
+  static_assert(NW >= 2, "wavefronts 0 and 1 finish the chunk");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DiagSmem<DK> &sm = *reinterpret_cast<DiagSmem<DK> *>(smem_raw);
   const int n_chunks = tabs.chunk_off[n_seq];
@@ -78,271 +151,238 @@ __global__ __launch_bounds__(kDiagThreads) void kla_prep_diag_kernel(
   const int ts = tabs.cu[n];
   const int t0 = ts + (c - tabs.chunk_off[n]) * kChunk;
   const int len = min(kChunk, tabs.cu[n + 1] - t0);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int c0 = 32 * wid + 8 * kq;  // this lane's eight channels
 
-  // ---- the chunk's rows; rows past its end are zero (and add no decay).  Lane tid takes 8
-  //      consecutive channels of one row: one 16-byte load of k and of q (bf16), 32 bytes of g
-  {
-    const int e0 = tid * 8, i = e0 / DK, ch = e0 % DK;
-    if (i < kChunk) {
-      float kv[8], qv[8], gv[8];
-      if (i < len) {
-        const size_t idx = ((size_t)(t0 + i) * H + h) * DK + ch;
+  // ---- rows 16 I + r16 of k, q and g at this lane's channels (zeros past the chunk end)
+  float kv[4][8], qv[4][8], G[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kv[e] = to_f32(k[idx + e]);
-          qv[e] = to_f32(q[idx + e]);
-          gv[e] = g[idx + e];
-        }
-      } else {
+  for (int I = 0; I < 4; ++I) {
+    const int row = 16 * I + r16;
+    if (row < len) {
+      const size_t idx = ((size_t)(t0 + row) * H + h) * DK + c0;
+      load_row8(k + idx, kv[I]);
+      load_row8(q + idx, qv[I]);
+      load_row8(g + idx, G[I]);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kv[e] = qv[e] = gv[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sm.K[i][ch + e] = kv[e];
-        sm.Q[i][ch + e] = qv[e];
-        sm.G[i][ch + e] = gv[e];
-      }
+      for (int s = 0; s < 8; ++s) kv[I][s] = qv[I][s] = G[I][s] = 0.f;
     }
   }
-  __syncthreads();
-  // ---- G: inclusive prefix over the chunk's tokens, per channel (the column in registers)
-  if (tid < DK) {
-    float col[kChunk];
+  // ---- G: inclusive prefix over the tokens per channel, within each 16-row block across the
+  //      16 lanes of a row group, then the blocks' carries; rows past the end repeat G_last
+  float Gl[8];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) col[i] = sm.G[i][tid];
+  for (int s = 0; s < 8; ++s) {
 #pragma unroll
-    for (int i = 1; i < kChunk; ++i) col[i] += col[i - 1];
+    for (int I = 0; I < 4; ++I) {
+      float x = G[I][s];
+      x += row_shr(x, 1);
+      x += row_shr(x, 2);
+      x += row_shr(x, 4);
+      x += row_shr(x, 8);
+      G[I][s] = x;
+    }
+    float carry = 0.f;
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) sm.G[i][tid] = col[i];
+    for (int I = 0; I < 4; ++I) {
+      const float tot = __shfl(G[I][s], (lane & ~15) | 15, kWave);
+      G[I][s] += carry;
+      carry += tot;
+    }
+    Gl[s] = carry;
   }
-  // ---- b and the readout factor per token: 16 lanes a row, 8 channels at a time
-  {
-    const int i = tid >> 4, part = tid & 15;
-    float kk = 0.f, qq = 0.f;
-    if (i < kChunk) {
-      for (int ch = 8 * part; ch < DK; ch += 128) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kk += sm.K[i][ch + e] * sm.K[i][ch + e];
-          qq += sm.Q[i][ch + e] * sm.Q[i][ch + e];
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) {
-      kk += __shfl_xor(kk, off, 16);
-      qq += __shfl_xor(qq, off, 16);
-    }
-    if (i < kChunk && part == 0) {
-      float bi = 0.f;
-      if (i < len) {
-        const size_t th = (size_t)(t0 + i) * H + h;
-        const float t_abs =
-            (float)(t0 + i - ts + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
-        bi = write_coef(opts.beta_mode, eta[th], kk + eps, t_abs);
-      }
-      sm.b[i] = bi;
-      sm.rq[i] = opts.normalize_q ? (qq > 0.f ? 1.f / sqrtf(qq) : 0.f) : 1.f;
-    }
-  }
-  __syncthreads();
-
-  // ---- decayed tiles and the state decay exp(G_last) (row 63 carries G_last)
-  //      four consecutive channels per lane and step: 16-byte LDS reads, 8- or 16-byte stores
+  // ---- decayed tiles (all 64 rows) and exp(G_last)
   const size_t tile0 = (size_t)task * kChunk * DK;
-  for (int e = 4 * tid; e < kChunk * DK; e += 4 * kDiagThreads) {
-    const int i = e / DK, ch = e % DK;
-    const f32x4 Gi = *reinterpret_cast<const f32x4 *>(&sm.G[i][ch]);
-    const f32x4 Gl = *reinterpret_cast<const f32x4 *>(&sm.G[kChunk - 1][ch]);
-    const f32x4 kv = *reinterpret_cast<const f32x4 *>(&sm.K[i][ch]);
-    const f32x4 qv = *reinterpret_cast<const f32x4 *>(&sm.Q[i][ch]);
-    f32x4 kg, qg, kd;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const float ei = __expf(Gi[x]);
-      kg[x] = kv[x] * ei;
-      qg[x] = qv[x] * ei;
-      kd[x] = kv[x] * __expf(Gl[x] - Gi[x]);
+  for (int I = 0; I < 4; ++I) {
+    float kg[8], qg[8], kd[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float e = __expf(G[I][s]);
+      kg[s] = kv[I][s] * e;
+      qg[s] = qv[I][s] * e;
+      kd[s] = kv[I][s] * __expf(Gl[s] - G[I][s]);
     }
-    put4(KG_out + tile0 + e, kg);
-    put4(QG_out + tile0 + e, qg);
-    put4(KD_out + tile0 + e, kd);
+    const size_t off = tile0 + (size_t)(16 * I + r16) * DK + c0;
+    store_row8(KG_out + off, kg);
+    store_row8(QG_out + off, qg);
+    store_row8(KD_out + off, kd);
   }
-  for (int ch = tid; ch < DK; ch += kDiagThreads)
-    GC_out[(size_t)task * DK + ch] = __expf(sm.G[kChunk - 1][ch]);
+  if (r16 == 0) {
+    float gc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) gc[s] = __expf(Gl[s]);
+    store_row8(GC_out + (size_t)task * DK + c0, gc);
+  }
+  // ---- squared norms over this wavefront's channels
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      sk += kv[I][s] * kv[I][s];
+      sq += qv[I][s] * qv[I][s];
+    }
+    sk += __shfl_xor(sk, 16, kWave);
+    sk += __shfl_xor(sk, 32, kWave);
+    sq += __shfl_xor(sq, 16, kWave);
+    sq += __shfl_xor(sq, 32, kWave);
+    if (kq == 0) {
+      sm.nk[wid][16 * I + r16] = sk;
+      sm.nq[wid][16 * I + r16] = sq;
+    }
+  }
 
-  // ---- A (strictly lower) and P (lower) in 4 x 4 tiles of (row, column) pairs.  With
-  //      l_i = G_i - G_{4 floor(i/4)} (the log-decay since the first row of row i's tile),
-  //      a pair in tiles bi > bj factors through the tiles' anchor rows,
-  //        exp(G_i - G_j) = exp(l_i) exp(G_{4 bi} - G_{4 bj + 3}) exp(l_{4 bj + 3} - l_j),
-  //      three factors that are each at most 1, so the off-diagonal tiles need one exponential
-  //      per channel instead of sixteen: with K o exp(l), Q o exp(l) and K o exp(l_last - l)
-  //      staged, they are plain sums of products.  The diagonal tiles take exp(l_i - l_j)
-  //      directly.
-  constexpr int EPL = kChunk * DK / kDiagThreads;  // elements per lane in the elementwise steps
-  float *GA = &sm.X[0][0], *GB = GA + 16 * DK;     // G of each tile's first and last row (X is
-                                                   // free until the substitution)
-  for (int e = tid; e < 16 * DK; e += kDiagThreads) {
-    const int t = e / DK, ch = e % DK;
-    GA[e] = sm.G[4 * t][ch];
-    GB[e] = sm.G[4 * t + 3][ch];
-  }
-  {
-    const int e0 = tid * EPL, i = e0 / DK, ch = e0 % DK;
-    float l[EPL];
+  // ---- A and P over this wavefront's channels, ten 16 x 16 blocks each (lower_block order
+  //      b = I (I + 1) / 2 + J).  Each product is formed transposed (right factor as the left
+  //      operand) so that lane (r16, kq) ends with row 16 I + r16, columns 16 J + 4 kq + e.
+  f32x4 Aa[10], Pa[10];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) l[e] = sm.G[i][ch + e] - sm.G[i & ~3][ch + e];
-    __syncthreads();  // every read of G (the decayed tiles, the anchors) is done
+  for (int b = 0; b < 10; ++b) Aa[b] = Pa[b] = zero4();
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) sm.G[i][ch + e] = l[e];
-  }
-  __syncthreads();
-  // diagonal tiles: wavefront w takes tile w, each lane DK / 64 channels, then wavefront sums
-  {
-    const int wid = tid >> 6, lane = tid & 63;
-    constexpr int CPL = DK / kWave;
-    const int t = wid;
-    float ad[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, pd[10] = {};
+  for (int I = 0; I < 4; ++I) {
+    const int bII = I * (I + 1) / 2 + I;
+    // blocks J < I, anchored at row 16 I
+    if (I > 0) {
+      float Ga[8], L[8], Lq[8];
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) {
-      const int ch = lane * CPL + cc;
-      float lg[4], kv[4], qv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        lg[r] = sm.G[4 * t + r][ch];
-        kv[r] = sm.K[4 * t + r][ch];
-        qv[r] = sm.Q[4 * t + r][ch];
-      }
-      int ia = 0, ip = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c2 = 0; c2 <= r; ++c2) {
-          const float x = __expf(lg[r] - lg[c2]) * kv[c2];
-          pd[ip++] += qv[r] * x;
-          if (c2 < r) ad[ia++] += kv[r] * x;
-        }
-    }
-#pragma unroll
-    for (int x = 0; x < 10; ++x) pd[x] = wave_sum(pd[x]);
-#pragma unroll
-    for (int x = 0; x < 6; ++x) ad[x] = wave_sum(ad[x]);
-    if (lane < 16) {
-      const int r = lane >> 2, c2 = lane & 3;
-      const int ip = r * (r + 1) / 2 + c2, ia = r * (r - 1) / 2 + c2;
-      float pv = 0.f, av = 0.f;
-#pragma unroll
-      for (int x = 0; x < 10; ++x) pv = x == ip && c2 <= r ? pd[x] : pv;
-#pragma unroll
-      for (int x = 0; x < 6; ++x) av = x == ia && c2 < r ? ad[x] : av;
-      sm.P[4 * t + r][4 * t + c2] = pv * sm.rq[4 * t + r];
-      sm.A[4 * t + r][4 * t + c2] = av;
-    }
-  }
-  // K -> K o exp(l), Q -> Q o exp(l), l -> K o exp(l_last - l) (l_last: the tile's last row)
-  {
-    const int e0 = tid * EPL, i = e0 / DK, ch = e0 % DK;
-    float kl[EPL], ql[EPL], kr[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float lv = sm.G[i][ch + e], k0 = sm.K[i][ch + e];
-      const float el = __expf(lv);
-      kl[e] = k0 * el;
-      ql[e] = sm.Q[i][ch + e] * el;
-      kr[e] = k0 * __expf(sm.G[i | 3][ch + e] - lv);
-    }
-    __syncthreads();  // the diagonal tiles' reads are done
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      sm.K[i][ch + e] = kl[e];
-      sm.Q[i][ch + e] = ql[e];
-      sm.G[i][ch + e] = kr[e];
-    }
-  }
-  __syncthreads();
-  // off-diagonal tiles (bj < bi): 120 tiles x 8 channel groups on lanes 0..959
-  if (tid < 120 * 8) {
-    const int t = tid >> 3, g8 = tid & 7;
-    const int bi = (int)((1.f + sqrtf(1.f + 8.f * (float)t)) * 0.5f);  // t = bi (bi - 1) / 2 + bj
-    const int bj = t - bi * (bi - 1) / 2;
-    constexpr int CPG = DK / 8;
-    float a[4][4] = {}, p[4][4] = {};
-#pragma unroll 1
-    for (int c4 = g8 * CPG; c4 < (g8 + 1) * CPG; c4 += 4) {
-      const f32x4 ga = *reinterpret_cast<const f32x4 *>(GA + bi * DK + c4);
-      const f32x4 gb = *reinterpret_cast<const f32x4 *>(GB + bj * DK + c4);
-      f32x4 d;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) d[e] = __expf(ga[e] - gb[e]);
-      f32x4 kl[4], ql[4], kr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        kl[r] = *reinterpret_cast<const f32x4 *>(&sm.K[4 * bi + r][c4]);
-        ql[r] = *reinterpret_cast<const f32x4 *>(&sm.Q[4 * bi + r][c4]);
-        kr[r] = *reinterpret_cast<const f32x4 *>(&sm.G[4 * bj + r][c4]) * d;
+      for (int s = 0; s < 8; ++s) {
+        Ga[s] = __shfl(G[I][s], lane & ~15, kWave);
+        const float e = __expf(G[I][s] - Ga[s]);
+        L[s] = kv[I][s] * e;
+        Lq[s] = qv[I][s] * e;
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int J = 0; J < I; ++J) {
+        float R[8];
 #pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2)
+        for (int s = 0; s < 8; ++s) R[s] = kv[J][s] * __expf(Ga[s] - G[J][s]);
+        const int b = I * (I + 1) / 2 + J;
+        Aa[b] = dot32<Tin>(Aa[b], R, L);
+        Pa[b] = dot32<Tin>(Pa[b], R, Lq);
+      }
+    }
+    // the diagonal block: pairs in different 4-row groups, anchored at the first row of the
+    // later group (rows of other groups masked to zero in each product)
+    const int grp = r16 >> 2;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[r][c2] += kl[r][e] * kr[c2][e];
-            p[r][c2] += ql[r][e] * kr[c2][e];
-          }
+    for (int s4 = 1; s4 < 4; ++s4) {
+      float L[8], Lq[8], R[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float Gs = __shfl(G[I][s], (lane & ~15) | (4 * s4), kWave);
+        const float el = grp == s4 ? __expf(G[I][s] - Gs) : 0.f;
+        L[s] = kv[I][s] * el;
+        Lq[s] = qv[I][s] * el;
+        R[s] = grp < s4 ? kv[I][s] * __expf(Gs - G[I][s]) : 0.f;
+      }
+      Aa[bII] = dot32<Tin>(Aa[bII], R, L);
+      Pa[bII] = dot32<Tin>(Pa[bII], R, Lq);
+    }
+    // pairs within one 4-row group, directly: row i = 16 I + r16 against rows
+    // 16 I + 4 grp + m of its group (m <= r16 % 4), summed over the lane groups
+    float a4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float Gj = quad_bcast(G[I][s], m), kj = quad_bcast(kv[I][s], m);
+        const float t = m <= (r16 & 3) ? kj * __expf(G[I][s] - Gj) : 0.f;
+        if (m < (r16 & 3)) a4[m] += kv[I][s] * t;
+        p4[m] += qv[I][s] * t;
+      }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c2 = 0; c2 < 4; ++c2)
-#pragma unroll
-        for (int off = 1; off < 8; off <<= 1) {
-          a[r][c2] += __shfl_xor(a[r][c2], off, 8);
-          p[r][c2] += __shfl_xor(p[r][c2], off, 8);
-        }
-    if (g8 == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) {
-          sm.A[4 * bi + r][4 * bj + c2] = a[r][c2];
-          sm.P[4 * bi + r][4 * bj + c2] = p[r][c2] * sm.rq[4 * bi + r];
-        }
+    for (int m = 0; m < 4; ++m) {
+      a4[m] += __shfl_xor(a4[m], 16, kWave);
+      a4[m] += __shfl_xor(a4[m], 32, kWave);
+      p4[m] += __shfl_xor(p4[m], 16, kWave);
+      p4[m] += __shfl_xor(p4[m], 32, kWave);
     }
+    if (kq == grp) {  // entry (16 I + r16, 16 I + 4 grp + m) sits in lane (r16, grp), e = m
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        Aa[bII][m] += a4[m];
+        Pa[bII][m] += p4[m];
+      }
+    }
+  }
+
+  // ---- the partial tiles meet: wavefront 0 sums A, wavefront 1 sums P
+  if (wid != 0) {
+#pragma unroll
+    for (int b = 0; b < 10; ++b) sm.pa[wid - 1][b][lane] = Aa[b];
+  }
+  if (wid != 1) {
+#pragma unroll
+    for (int b = 0; b < 10; ++b) sm.pp[wid == 0 ? 0 : wid - 1][b][lane] = Pa[b];
   }
   __syncthreads();
-
-  // ---- X = (I + Diag(b) A)^{-1} by 16 x 16 blocks (the staged key tile is free scratch now)
-  blocked_inverse<kDiagThreads, kChunk + 1, kChunk + 1>(&sm.A[0][0], sm.b, &sm.X[0][0],
-                                                        &sm.K[0][0], tid);
-
-  // ---- T = X Diag(b) and P, as their ten 16 x 16 blocks on and below the diagonal (tpb_off
-  //      layout), in element order of the packed blocks
-  const size_t tp0 = (size_t)task * kTpbElems;
-  for (int e = 4 * tid; e < 10 * 256; e += 4 * kDiagThreads) {  // 4 columns of a row per lane
-    const int blk = e >> 8, w = e & 255;
-    const int I = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0, J = blk - I * (I + 1) / 2;
-    const int i = 16 * I + (w >> 4), j0 = 16 * J + (w & 15);
-    f32x4 tv, pv;
+  if (wid >= 2) return;
+  const int i = lane;  // per-token work: token `lane`
+  if (wid == 1) {
+    // P = Diag(rq) P as ten packed blocks; unit gam and dec for the scan (the decay sits in
+    // the tiles) and the readout factor rq as gamO
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const bool low = j0 + x <= i;
-      tv[x] = low ? sm.X[i][j0 + x] * sm.b[j0 + x] : 0.f;
-      pv[x] = low ? sm.P[i][j0 + x] : 0.f;
-    }
-    put4(T_out + tp0 + e, tv);
-    put4(P_out + tp0 + e, pv);
-  }
-  // ---- decays for the scan: unit gam and dec (the decay sits in Kg, Qg, Kd), the readout
-  //      factor as gamO
-  if (tid < kChunk) {
+    for (int w = 0; w < NW - 1; ++w)
+#pragma unroll
+      for (int b = 0; b < 10; ++b) Pa[b] += sm.pp[w][b][lane];
+    float qq = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) qq += sm.nq[w][i];
+    const float rq_i = opts.normalize_q ? (qq > 0.f ? 1.f / sqrtf(qq) : 0.f) : 1.f;
     const size_t gd0 = (size_t)task * kGDFloats;
-    GD_out[gd0 + tid] = 1.f;
-    GD_out[gd0 + kChunk + tid] = 1.f;
-    GD_out[gd0 + 2 * kChunk + tid] = sm.rq[tid];
+    GD_out[gd0 + i] = 1.f;
+    GD_out[gd0 + kChunk + i] = 1.f;
+    GD_out[gd0 + 2 * kChunk + i] = rq_i;
+    Tin *P_task = P_out + (size_t)task * kTpbElems;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const float rr = __shfl(rq_i, 16 * I + r16, kWave);
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        const f32x4 pv = Pa[I * (I + 1) / 2 + J];
+        out_put<Tin>(P_task, true, 16 * I + r16, 16 * J + 4 * kq, rr * pv[0], rr * pv[1],
+                     rr * pv[2], rr * pv[3]);
+      }
+    }
+    return;
   }
+  // wavefront 0: b, L = Diag(b) A, and the solve
+#pragma unroll
+  for (int w = 0; w < NW - 1; ++w)
+#pragma unroll
+    for (int b = 0; b < 10; ++b) Aa[b] += sm.pa[w][b][lane];
+  {
+    float kk = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) kk += sm.nk[w][i];
+    float bi = 0.f;
+    if (i < len) {
+      const size_t th = (size_t)(t0 + i) * H + h;
+      const float t_abs = (float)(t0 + i - ts + 1 + (opts.pos_offset ? opts.pos_offset[n] : 0));
+      bi = write_coef(opts.beta_mode, eta[th], kk + eps, t_abs);
+    }
+    sm.ps.beta[i] = bi;
+  }
+  wave_lds_sync();
+  f32x4 Lr[4][3];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    const float bme = sm.ps.beta[16 * I + r16];
+#pragma unroll
+    for (int J = 0; J < I; ++J) Lr[I][J] = Aa[I * (I + 1) / 2 + J] * bme;
+    *reinterpret_cast<f32x4 *>(&sm.ps.Ld[I][bidx(r16, 4 * kq)]) = Aa[I * (I + 1) / 2 + I] * bme;
+  }
+  wave_lds_sync();
+  Tin *T_task = T_out + (size_t)task * kTpbElems;
+  chunk_inverse<false>(Lr, sm.ps, [] { wave_lds_sync(); },
+                       [&](int row, int col, const f32x4 &x, const f32x4 &bv) {
+                         out_put<Tin>(T_task, true, row, col, x[0] * bv[0], x[1] * bv[1],
+                                      x[2] * bv[2], x[3] * bv[3]);
+                       });
 }
 
 template <typename Tin, int DK>
@@ -352,6 +392,7 @@ static hipError_t launch_prep_diag_t(const void *q, const void *k, const float *
                                      const DiagTiles &dt, void *T_out, void *P_out,
                                      float *GD_out, hipStream_t stream) {
   const size_t smem = sizeof(DiagSmem<DK>);
+  static_assert(sizeof(DiagSmem<DK>) <= 80 * 1024, "two workgroups to a compute unit");
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     hipError_t e =
@@ -362,7 +403,8 @@ static hipError_t launch_prep_diag_t(const void *q, const void *k, const float *
   }
   const int64_t blocks = n_chunks_ub * H;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((kla_prep_diag_kernel<Tin, DK>), dim3((unsigned)blocks), dim3(kDiagThreads),
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((kla_prep_diag_kernel<Tin, DK>), dim3((unsigned)blocks), dim3(DK * 2),
                      smem, stream, static_cast<const Tin *>(q), static_cast<const Tin *>(k), g,
                      eta, eps, opts, t, n_seq, H, static_cast<Tin *>(T_out),
                      static_cast<Tin *>(P_out), GD_out,

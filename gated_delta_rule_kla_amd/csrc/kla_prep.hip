@@ -214,38 +214,6 @@ __device__ __forceinline__ ChunkLoc locate(const Planner &p, int c) {
 // A_ij = exp(G_i - G_j) for j <= i, zero above the diagonal) for the scan.
 // ---------------------------------------------------------------------------------------------
 
-// Entries (row, col .. col + 3) of a chunk's 64 x 64 output, col a multiple of 4, straight
-// from registers: in the packed layout (tpb_off; entries of the blocks above the diagonal are
-// not stored) or row-major.  A lane group (r16, kg) covering one 16 x 16 block writes its
-// 256 contiguous packed elements, so a store instruction writes whole lines.
-template <typename T>
-__device__ __forceinline__ void out_put(T *dst, bool packed, int row, int col, float a, float b,
-                                        float c, float d, bool split = false) {
-  int off;
-  if (packed) {
-    const int I = row >> 4, J = col >> 4;
-    if (J > I) return;
-    off = (I * (I + 1) / 2 + J) * 256 + (row & 15) * 16 + (col & 15);
-  } else {
-    off = row * kChunk + col;
-  }
-  if constexpr (sizeof(T) == 2) {
-    bf16x4 x4;
-    x4[0] = from_f32<T>(a); x4[1] = from_f32<T>(b); x4[2] = from_f32<T>(c); x4[3] = from_f32<T>(d);
-    *reinterpret_cast<bf16x4 *>(dst + off) = x4;
-    if (split) {  // the rounding residuals, one packed tile further on
-      bf16x4 l4;
-      l4[0] = from_f32<T>(a - to_f32(x4[0]));
-      l4[1] = from_f32<T>(b - to_f32(x4[1]));
-      l4[2] = from_f32<T>(c - to_f32(x4[2]));
-      l4[3] = from_f32<T>(d - to_f32(x4[3]));
-      *reinterpret_cast<bf16x4 *>(dst + kTpbElems + off) = l4;
-    }
-  } else {
-    *reinterpret_cast<f32x4 *>(dst + off) = f32x4{a, b, c, d};
-  }
-}
-
 // bf16 key or query rows of one chunk as MFMA fragments f[b][ks] (rows 16 b + r16, k-step
 // ks), loaded as whole 128-byte lines: for each block and line c, one load covers rows
 // 16 b + 0..7 and one rows 16 b + 8..15, lane (r16, kg) taking row r16 % 8 and 16-byte
