@@ -49,9 +49,16 @@ __device__ __forceinline__ int find_seq(const int32_t *__restrict__ chunk_off, i
 template <int DK>
 struct DiagSmem {
   static constexpr int NW = DK / 32;
-  // partial tiles (ten 16 x 16 blocks each, one 16-byte piece per lane): A from wavefronts
-  // 1 .. NW - 1, P from wavefronts 0, 2 .. NW - 1
-  f32x4 pa[NW - 1][10][64], pp[NW - 1][10][64];
+  union {
+    // G within each 16-row block (prefix over the block's rows only), for the block totals
+    // and the anchor rows; each wavefront reads back its own channels
+    float Gb[kChunk][DK + 4];
+    // partial tiles (ten 16 x 16 blocks each, one 16-byte piece per lane): A from wavefronts
+    // 1 .. NW - 1, P from wavefronts 0, 2 .. NW - 1
+    struct {
+      f32x4 pa[NW - 1][10][64], pp[NW - 1][10][64];
+    } t;
+  } u;
   float nk[NW][kChunk], nq[NW][kChunk];  // partial squared norms of the key and query rows
   PrepSmem ps;                           // wavefront 0's solve
 };
@@ -89,28 +96,68 @@ __device__ __forceinline__ float quad_bcast(float x, int m) {
   return __builtin_bit_cast(float, r);
 }
 
-// acc += the 16 x 16 product over 32 channels with lane (r16, kq) supplying row r16 of the
-// left operand a and column r16 of the right one b at channels 8 kq .. + 7: bf16 inputs as
-// hi/lo bf16 pairs on 16x16x32 steps, fp32 inputs as eight exact 16x16x4 steps
-template <typename Tin>
-__device__ __forceinline__ f32x4 dot32(f32x4 acc, const float (&a)[8], const float (&b)[8]) {
-  if constexpr (sizeof(Tin) == 2) {
-    bf16x8 ah, al, bh, bl;
+// An operand of the 16 x 16 products over 32 channels: lane (r16, kq) holds row r16 at
+// channels 8 kq .. + 7; bf16 inputs keep it as a hi/lo pair of bf16 fragments, fp32 inputs
+// as fp32.
+// masked(keep) is the operand or zero.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <typename Tin> struct Opnd;
+template <> struct Opnd<__bf16> {
+  u32x4 hi, lo;  // bf16 pairs
+  __device__ __forceinline__ Opnd() {}
+  __device__ __forceinline__ explicit Opnd(const float (&x)[8]) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      ah[s] = from_f32<__bf16>(a[s]);
-      al[s] = from_f32<__bf16>(a[s] - to_f32(ah[s]));
-      bh[s] = from_f32<__bf16>(b[s]);
-      bl[s] = from_f32<__bf16>(b[s] - to_f32(bh[s]));
+    for (int p = 0; p < 4; ++p) {
+      const f32x2_t x2 = {x[2 * p], x[2 * p + 1]};
+      const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector(x2, bf16x2_t));
+      const f32x2_t l2 = {x[2 * p] - __builtin_bit_cast(float, h << 16),
+                          x[2 * p + 1] - __builtin_bit_cast(float, h & 0xffff0000u)};
+      hi[p] = h;
+      lo[p] = __builtin_bit_cast(unsigned, __builtin_convertvector(l2, bf16x2_t));
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
-    return acc;
   }
+  __device__ __forceinline__ Opnd masked(bool keep) const {
+    Opnd r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      r.hi[p] = keep ? hi[p] : 0u;
+      r.lo[p] = keep ? lo[p] : 0u;
+    }
+    return r;
+  }
+};
+template <> struct Opnd<float> {
+  float v[8];
+  __device__ __forceinline__ Opnd() {}
+  __device__ __forceinline__ explicit Opnd(const float (&x)[8]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) v[s] = x[s];
+  }
+  __device__ __forceinline__ Opnd masked(bool keep) const {
+    Opnd r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r.v[s] = keep ? v[s] : 0.f;
+    return r;
+  }
+};
+// acc += a^T b in the 16x16 tile sense: D[4 kq + e][r16] = sum_c a[row 4 kq + e][c] b[row r16][c]
+// (bf16: hi hi + hi lo + lo hi on 16x16x32 steps; fp32: eight exact 16x16x4 steps)
+__device__ __forceinline__ f32x4 dot32(f32x4 acc, const Opnd<__bf16> &a, const Opnd<__bf16> &b) {
+  const bf16x8 ah = __builtin_bit_cast(bf16x8, a.hi), al = __builtin_bit_cast(bf16x8, a.lo);
+  const bf16x8 bh = __builtin_bit_cast(bf16x8, b.hi), bl = __builtin_bit_cast(bf16x8, b.lo);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 dot32(f32x4 acc, const Opnd<float> &a, const Opnd<float> &b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3]; x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
 
 template <typename T>
@@ -154,6 +201,7 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
   const int c0 = 32 * wid + 8 * kq;  // this lane's eight channels
+  constexpr float kLog2e = 1.4426950408889634f;
 
   // ---- rows 16 I + r16 of k, q and g at this lane's channels (zeros past the chunk end)
   float kv[4][8], qv[4][8], G[4][8];
@@ -165,18 +213,20 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
       load_row8(k + idx, kv[I]);
       load_row8(q + idx, qv[I]);
       load_row8(g + idx, G[I]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) G[I][s] *= kLog2e;  // G in log2 units: exp(x) = exp2(x log2 e)
     } else {
 #pragma unroll
       for (int s = 0; s < 8; ++s) kv[I][s] = qv[I][s] = G[I][s] = 0.f;
     }
   }
   // ---- G: inclusive prefix over the tokens per channel, within each 16-row block across the
-  //      16 lanes of a row group, then the blocks' carries; rows past the end repeat G_last
-  float Gl[8];
+  //      16 lanes of a row group (parked in LDS: each block's total and anchor rows are read
+  //      back from there), then the blocks' carries; rows past the end repeat G_last
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int I = 0; I < 4; ++I) {
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
+    for (int s = 0; s < 8; ++s) {
       float x = G[I][s];
       x += row_shr(x, 1);
       x += row_shr(x, 2);
@@ -184,15 +234,30 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
       x += row_shr(x, 8);
       G[I][s] = x;
     }
-    float carry = 0.f;
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const float tot = __shfl(G[I][s], (lane & ~15) | 15, kWave);
-      G[I][s] += carry;
-      carry += tot;
-    }
-    Gl[s] = carry;
+    store_row8(&sm.u.Gb[16 * I + r16][c0], G[I]);
   }
+  wave_lds_sync();  // a wavefront reads back only its own channels
+  float carry[4][8];  // G at the row before each block
+  float Gl[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) carry[0][s] = 0.f;
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    float tot[8];
+    ld8(&sm.u.Gb[16 * I + 15][c0], tot);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      G[I][s] += carry[I][s];
+      const float nx = carry[I][s] + tot[s];
+      if (I < 3) carry[I + 1][s] = nx; else Gl[s] = nx;
+    }
+  }
+  // G at row 16 I + a (a within the block) for this lane's channels
+  auto anchor = [&](int I, int a, float (&x)[8]) {
+    ld8(&sm.u.Gb[16 * I + a][c0], x);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) x[s] += carry[I][s];
+  };
   // ---- decayed tiles (all 64 rows) and exp(G_last)
   const size_t tile0 = (size_t)task * kChunk * DK;
 #pragma unroll
@@ -200,10 +265,10 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
     float kg[8], qg[8], kd[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const float e = __expf(G[I][s]);
+      const float e = exp2_fast(G[I][s]);
       kg[s] = kv[I][s] * e;
       qg[s] = qv[I][s] * e;
-      kd[s] = kv[I][s] * __expf(Gl[s] - G[I][s]);
+      kd[s] = kv[I][s] * exp2_fast(Gl[s] - G[I][s]);
     }
     const size_t off = tile0 + (size_t)(16 * I + r16) * DK + c0;
     store_row8(KG_out + off, kg);
@@ -213,7 +278,7 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
   if (r16 == 0) {
     float gc[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) gc[s] = __expf(Gl[s]);
+    for (int s = 0; s < 8; ++s) gc[s] = exp2_fast(Gl[s]);
     store_row8(GC_out + (size_t)task * DK + c0, gc);
   }
   // ---- squared norms over this wavefront's channels
@@ -247,39 +312,49 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
     // blocks J < I, anchored at row 16 I
     if (I > 0) {
       float Ga[8], L[8], Lq[8];
+      anchor(I, 0, Ga);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        Ga[s] = __shfl(G[I][s], lane & ~15, kWave);
-        const float e = __expf(G[I][s] - Ga[s]);
+        const float e = exp2_fast(G[I][s] - Ga[s]);
         L[s] = kv[I][s] * e;
         Lq[s] = qv[I][s] * e;
       }
+      const Opnd<Tin> oL(L), oLq(Lq);
 #pragma unroll
       for (int J = 0; J < I; ++J) {
         float R[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) R[s] = kv[J][s] * __expf(Ga[s] - G[J][s]);
+        for (int s = 0; s < 8; ++s) R[s] = kv[J][s] * exp2_fast(Ga[s] - G[J][s]);
+        const Opnd<Tin> oR(R);
         const int b = I * (I + 1) / 2 + J;
-        Aa[b] = dot32<Tin>(Aa[b], R, L);
-        Pa[b] = dot32<Tin>(Pa[b], R, Lq);
+        Aa[b] = dot32(Aa[b], oR, oL);
+        Pa[b] = dot32(Pa[b], oR, oLq);
       }
     }
     // the diagonal block: pairs in different 4-row groups, anchored at the first row of the
     // later group (rows of other groups masked to zero in each product)
     const int grp = r16 >> 2;
-#pragma unroll
-    for (int s4 = 1; s4 < 4; ++s4) {
-      float L[8], Lq[8], R[8];
+    float Lo[8], Lqo[8];  // k_i and q_i times exp(G_i - G at the first row of their group)
+    {
+      float Go[8];
+      ld8(&sm.u.Gb[16 * I + 4 * grp][c0], Go);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const float Gs = __shfl(G[I][s], (lane & ~15) | (4 * s4), kWave);
-        const float el = grp == s4 ? __expf(G[I][s] - Gs) : 0.f;
-        L[s] = kv[I][s] * el;
-        Lq[s] = qv[I][s] * el;
-        R[s] = grp < s4 ? kv[I][s] * __expf(Gs - G[I][s]) : 0.f;
+        const float e = exp2_fast(G[I][s] - (Go[s] + carry[I][s]));
+        Lo[s] = kv[I][s] * e;
+        Lqo[s] = qv[I][s] * e;
       }
-      Aa[bII] = dot32<Tin>(Aa[bII], R, L);
-      Pa[bII] = dot32<Tin>(Pa[bII], R, Lq);
+    }
+    const Opnd<Tin> oLo(Lo), oLqo(Lqo);
+#pragma unroll
+    for (int s4 = 1; s4 < 4; ++s4) {
+      float Gs[8], R[8];
+      anchor(I, 4 * s4, Gs);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) R[s] = kv[I][s] * exp2_fast(Gs[s] - G[I][s]);
+      const Opnd<Tin> oR = Opnd<Tin>(R).masked(grp < s4);
+      Aa[bII] = dot32(Aa[bII], oR, oLo.masked(grp == s4));
+      Pa[bII] = dot32(Pa[bII], oR, oLqo.masked(grp == s4));
     }
     // pairs within one 4-row group, directly: row i = 16 I + r16 against rows
     // 16 I + 4 grp + m of its group (m <= r16 % 4), summed over the lane groups
@@ -289,7 +364,7 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const float Gj = quad_bcast(G[I][s], m), kj = quad_bcast(kv[I][s], m);
-        const float t = m <= (r16 & 3) ? kj * __expf(G[I][s] - Gj) : 0.f;
+        const float t = m <= (r16 & 3) ? kj * exp2_fast(G[I][s] - Gj) : 0.f;
         if (m < (r16 & 3)) a4[m] += kv[I][s] * t;
         p4[m] += qv[I][s] * t;
       }
@@ -310,14 +385,16 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
     }
   }
 
-  // ---- the partial tiles meet: wavefront 0 sums A, wavefront 1 sums P
+  // ---- the partial tiles meet (in the LDS of the G staging, once every wavefront is past
+  //      it): wavefront 0 sums A, wavefront 1 sums P
+  __syncthreads();
   if (wid != 0) {
 #pragma unroll
-    for (int b = 0; b < 10; ++b) sm.pa[wid - 1][b][lane] = Aa[b];
+    for (int b = 0; b < 10; ++b) sm.u.t.pa[wid - 1][b][lane] = Aa[b];
   }
   if (wid != 1) {
 #pragma unroll
-    for (int b = 0; b < 10; ++b) sm.pp[wid == 0 ? 0 : wid - 1][b][lane] = Pa[b];
+    for (int b = 0; b < 10; ++b) sm.u.t.pp[wid == 0 ? 0 : wid - 1][b][lane] = Pa[b];
   }
   __syncthreads();
   if (wid >= 2) return;
@@ -328,7 +405,7 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
 #pragma unroll
     for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
-      for (int b = 0; b < 10; ++b) Pa[b] += sm.pp[w][b][lane];
+      for (int b = 0; b < 10; ++b) Pa[b] += sm.u.t.pp[w][b][lane];
     float qq = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) qq += sm.nq[w][i];
@@ -354,7 +431,7 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
 #pragma unroll
   for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
-    for (int b = 0; b < 10; ++b) Aa[b] += sm.pa[w][b][lane];
+    for (int b = 0; b < 10; ++b) Aa[b] += sm.u.t.pa[w][b][lane];
   {
     float kk = 0.f;
 #pragma unroll
