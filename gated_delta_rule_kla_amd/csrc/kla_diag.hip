@@ -180,7 +180,7 @@ __device__ __forceinline__ void store_row8(__bf16 *p, const float (&x)[8]) {
 }  // namespace
 
 template <typename Tin, int DK>
-__global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
+__global__ __launch_bounds__(DK * 2) __attribute__((amdgpu_waves_per_eu(2))) void kla_prep_diag_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ eta, float eps, CoefOpts opts, SeqTables tabs, int n_seq, int H,
     Tin *__restrict__ T_out, Tin *__restrict__ P_out, float *__restrict__ GD_out,
@@ -306,6 +306,59 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
   f32x4 Aa[10], Pa[10];
 #pragma unroll
   for (int b = 0; b < 10; ++b) Aa[b] = Pa[b] = zero4();
+  // One anchor for the whole chunk, row 32, when on every channel of this wavefront every row
+  // is within kSpan (log2 units) of row 32: then L_i = k_i 2^(G_i - G_32) and
+  // R_j = k_j 2^(G_32 - G_j) stay within 2^-kSpan .. 2^kSpan times k (normal numbers), each
+  // tile is one product of them, and the entries above the diagonal are dropped.  Otherwise
+  // the blockwise anchors below, whose factors are all at most 1, whatever the decay.
+  constexpr float kSpan = 64.f;
+  float G32[8];
+  bool fast;
+  {
+    anchor(2, 0, G32);
+    float span = 0.f;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) span = fmaxf(span, fabsf(G[I][s] - G32[s]));
+    fast = __all(span <= kSpan);
+  }
+  if (fast) {
+    // every operand first (the rows' k, q and G are dead after), then the products
+    Opnd<Tin> oR[4], oL[4], oLq[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      float L[8], Lq[8], R[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float d = G[I][s] - G32[s];
+        const float e = exp2_fast(d);
+        L[s] = kv[I][s] * e;
+        Lq[s] = qv[I][s] * e;
+        R[s] = kv[I][s] * exp2_fast(-d);
+      }
+      oR[I] = Opnd<Tin>(R);
+      oL[I] = Opnd<Tin>(L);
+      oLq[I] = Opnd<Tin>(Lq);
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        const int b = I * (I + 1) / 2 + J;
+        Aa[b] = dot32(Aa[b], oR[J], oL[I]);
+        Pa[b] = dot32(Pa[b], oR[J], oLq[I]);
+      }
+      // the diagonal block: keep column < row for A, column <= row for P
+      const int bII = I * (I + 1) / 2 + I;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = 4 * kq + e;
+        Aa[bII][e] = col < r16 ? Aa[bII][e] : 0.f;
+        Pa[bII][e] = col <= r16 ? Pa[bII][e] : 0.f;
+      }
+    }
+  } else {
 #pragma unroll
   for (int I = 0; I < 4; ++I) {
     const int bII = I * (I + 1) / 2 + I;
@@ -383,6 +436,7 @@ __global__ __launch_bounds__(DK * 2) void kla_prep_diag_kernel(
         Pa[bII][m] += p4[m];
       }
     }
+  }
   }
 
   // ---- the partial tiles meet (in the LDS of the G staging, once every wavefront is past

@@ -151,16 +151,21 @@ def oracle_prefill_diag(d, **kw):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("case", ["tiny", "ragged128", "dk64_dv256", "strong_decay", "wide"])
+@pytest.mark.parametrize("case", ["tiny", "ragged128", "dk64_dv256", "strong_decay",
+                                  "extreme_decay", "extreme_decay_dk64", "wide"])
 def test_prefill_diagonal_gate(kla, dtype, case):
     """Diagonal gating (paper Appendix B.5): g [n_tok, H, d_k], one log-decay per key channel,
     through kla_prefill_chunked_ex, against the fp64 tokenwise oracle.  'wide' has 3 x 24 x 4
-    column slices, more than the compute units, so the 64-column workgroups run."""
+    column slices, more than the compute units, so the 64-column workgroups run.  With
+    g ~ U(-8, 0) ('extreme_decay') a chunk's channels decay by far more than 2^64 around its
+    middle row, so the prep takes its blockwise-anchored products."""
     spec = {
         "tiny": dict(H=1, dk=64, dv=64, lens=None, T=256, n_seq=1, g_low=-0.5),
         "ragged128": dict(H=3, dk=128, dv=128, lens=(70, 1, 129, 200), g_low=-0.5),
         "dk64_dv256": dict(H=2, dk=64, dv=256, lens=(64, 190, 5), g_low=-0.5),
         "strong_decay": dict(H=2, dk=128, dv=128, lens=(300, 77), g_low=-2.0),
+        "extreme_decay": dict(H=2, dk=128, dv=128, lens=(200, 64, 3), g_low=-8.0),
+        "extreme_decay_dk64": dict(H=2, dk=64, dv=128, lens=(150, 70), g_low=-8.0),
         "wide": dict(H=24, dk=128, dv=128, lens=None, T=130, n_seq=3, g_low=-0.5),
     }[case]
     w = ki.Workload(93, "prefill-diag", spec.get("n_seq", len(spec["lens"] or ())), spec["H"],
@@ -168,6 +173,23 @@ def test_prefill_diagonal_gate(kla, dtype, case):
                     g_low=spec["g_low"], s0_var=0.01)
     d = to_dev(ki.prefill_inputs(w, diag=True))
     assert d["g"].shape == d["k"].shape
+    o, ST = run_prefill_diag(kla, d)
+    oo, So = oracle_prefill_diag(d)
+    check(o, oo, TOL[dtype], "o")
+    check(ST, So, TOL[dtype], "S_T")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_diagonal_gate_mixed_channel_decay(kla, dtype):
+    """Key channels 32..63 decay with g ~ U(-8, 0), the others with g ~ U(-0.5, 0): the prep's
+    wavefront over those 32 channels takes the blockwise-anchored products while the others
+    take the one-anchor products, and their partial A and P sums meet in one chunk solve."""
+    w = ki.Workload(96, "prefill-diag-mixed", 2, 2, 128, 128, dtype, lens=(190, 64),
+                    g_low=-0.5, s0_var=0.01)
+    d = to_dev(ki.prefill_inputs(w, diag=True))
+    g = d["g"].clone()
+    g[:, :, 32:64] *= 16.0
+    d["g"] = g.contiguous()
     o, ST = run_prefill_diag(kla, d)
     oo, So = oracle_prefill_diag(d)
     check(o, oo, TOL[dtype], "o")
