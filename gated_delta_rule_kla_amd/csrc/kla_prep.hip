@@ -252,7 +252,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
   __shared__ PrepSmem sm;
   const Planner pl = make_planner(pa, SeqTables{cu, chunk_off}, n_seq);
   write_tables(pl);
-  const int task = blockIdx.x;  // chunk * H + head
+  // task = chunk * H + head.  Workgroup b runs on XCD b % 8; consecutive tasks (the heads of
+  // a chunk, whose g and eta share cache lines) go to one XCD so that its L2 fetches each
+  // line once.
+  const int nblk = gridDim.x, bid = blockIdx.x;
+  const int task = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
   if (task >= pl.n_chunks * H) return;
   const int c = __builtin_amdgcn_readfirstlane(task / H);
   const int h = __builtin_amdgcn_readfirstlane(task - c * H);
