@@ -58,8 +58,9 @@ struct WsLayout {
   // Q o exp(G), K o exp(G_last - G) ([64][d_k] each, operand type) and exp(G_last) ([d_k])
   size_t off_KG = 0, off_QG = 0, off_KD = 0, off_GC = 0;
   // two-level scan only (G >= 2 segments): [N_g | M_g] per (sequence, segment < G-1, head),
-  // [d_k][d_v + d_k] fp32, and the chained incoming states, [d_k][d_v] fp32
-  size_t off_NM = 0, off_Sin = 0;
+  // [d_k][d_v + d_k] fp32, the chained incoming states, [d_k][d_v] fp32, and per chunk-head
+  // the log contraction bound of the warm-up test (fp32)
+  size_t off_NM = 0, off_Sin = 0, off_LC = 0;
   size_t total;
 };
 
@@ -69,6 +70,8 @@ struct WsLayout {
 struct SegPlan {
   int G = 0, Ls = 0;
 };
+// Warm-up length of the two-level scan's early segment starts, in chunks (512 tokens).
+constexpr int kWarmChunks = 8;
 SegPlan seg_plan(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_v, bool diag,
                  int32_t segs_opt, bool split = false) {
   SegPlan p;
@@ -117,7 +120,8 @@ WsLayout ws_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, 
     const size_t units = (size_t)n_seq * (size_t)(segs - 1) * (size_t)H * (size_t)d_k;
     w.off_NM = w.total;
     w.off_Sin = align256(w.off_NM + sizeof(float) * units * (size_t)(d_v + d_k));
-    w.total = align256(w.off_Sin + sizeof(float) * units * (size_t)d_v);
+    w.off_LC = align256(w.off_Sin + sizeof(float) * units * (size_t)d_v);
+    w.total = align256(w.off_LC + sizeof(float) * (size_t)nch * (size_t)H);
   }
   return w;
 }
@@ -302,7 +306,7 @@ struct WsViews {
   float *G, *GD;
   void *T, *P;
   kla::DiagTiles diag;  // diagonal gating only
-  float *NM, *Sin;      // two-level scan only
+  float *NM, *Sin, *LC;  // two-level scan only
 };
 
 WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n_heads,
@@ -314,10 +318,12 @@ WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n
   WsViews v{{reinterpret_cast<int32_t *>(ws + w.off_cu),
              reinterpret_cast<int32_t *>(ws + w.off_co)},
             reinterpret_cast<float *>(ws + w.off_G), reinterpret_cast<float *>(ws + w.off_GD),
-            ws + w.off_T, ws + w.off_P, {nullptr, nullptr, nullptr, nullptr}, nullptr, nullptr};
+            ws + w.off_T, ws + w.off_P, {nullptr, nullptr, nullptr, nullptr}, nullptr, nullptr,
+            nullptr};
   if (segs >= 2) {
     v.NM = reinterpret_cast<float *>(ws + w.off_NM);
     v.Sin = reinterpret_cast<float *>(ws + w.off_Sin);
+    v.LC = reinterpret_cast<float *>(ws + w.off_LC);
   }
   if (diag)
     v.diag = kla::DiagTiles{ws + w.off_KG, ws + w.off_QG, ws + w.off_KD,
@@ -344,7 +350,7 @@ kla_status enqueue_prepare(const void *q, const void *k, const float *g, const f
                            const kla::CoefOpts &opts, const int32_t *cu_seqlens, int32_t n_seq,
                            int32_t total_tokens, int32_t n_heads, int32_t d_k, kla_dtype dtype,
                            void *workspace, hipStream_t s, bool split = false,
-                           float *X_out = nullptr) {
+                           float *X_out = nullptr, float *LC_out = nullptr) {
   const WsViews wv =
       ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, false, 0, 0, split);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
@@ -360,7 +366,7 @@ kla_status enqueue_prepare(const void *q, const void *k, const float *g, const f
     return st;
   return hip_status(kla::launch_prep(to_dt(dtype), d_k, q, k, g, eta, eps, opts, wv.tabs, n_seq,
                                      nch_ub, n_heads, nullptr, nullptr, wv.T, false, wv.P, wv.GD,
-                                     pa, s, split, X_out),
+                                     pa, s, split, X_out, LC_out),
                     "prep");
 }
 
@@ -406,12 +412,17 @@ kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, c
     return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear any stale error from unrelated work
+  const bool two_level = !split && sp.G >= 2 && !cu_seqlens && total_tokens > 0;
   if (diag)
     st = enqueue_prepare_diag(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads,
                               d_k, dtype, workspace, s);
   else
-    st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
-                         dtype, workspace, s, split);
+    st = enqueue_prepare(
+        q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k, dtype, workspace,
+        s, split, nullptr,
+        two_level ? ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, false, d_v,
+                             sp.G).LC
+                  : nullptr);
   if (st != KLA_OK) return st;
   if (split) {
     const WsViews wv =
@@ -419,7 +430,7 @@ kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, c
     st = hip_status(kla::launch_scan_split(d_k, d_v, q, k, v, wv.GD, wv.T, wv.P, S0, o, S_T,
                                            wv.tabs, n_seq, n_heads, s),
                     "scan (split precision)");
-  } else if (sp.G >= 2 && !cu_seqlens && total_tokens > 0) {
+  } else if (two_level) {
     const WsViews wv =
         ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, false, d_v, sp.G);
     kla::SegArgs sa;
@@ -427,6 +438,8 @@ kla_status kla_prefill_chunked_ex(const void *q, const void *k, const void *v, c
     sa.L = total_tokens / n_seq;
     sa.Ls = sp.Ls;
     sa.dv = d_v;
+    sa.LC = wv.LC;
+    sa.W = kWarmChunks;
     st = hip_status(kla::launch_scan_two_level(to_dt(dtype), d_k, d_v, q, k, v, wv.GD, wv.T, wv.P,
                                                S0, o, S_T, n_seq, n_heads, sa, wv.NM, wv.Sin, s),
                     "two-level scan");

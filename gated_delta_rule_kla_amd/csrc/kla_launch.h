@@ -50,13 +50,15 @@ constexpr int kGDFloats = 3 * 64;
 // GD_out (per chunk-head decay factors) are each optional.  tp_split (bf16, packed): T and
 // P as hi = bf16(x) and lo = bf16(x - hi) blocks, the lo blocks after the hi ones of each
 // chunk-head (twice the packed size).  X_out (optional): X = (I + L)^{-1} itself in fp32,
-// packed blocks (kTpbElems floats per chunk-head), for the backward pass.
+// packed blocks (kTpbElems floats per chunk-head), for the backward pass.  LC_out (optional):
+// per chunk-head the natural log of a bound on the spectral norm of the chunk's homogeneous
+// state map, G_last + sum_t ln max(1, |1 - b_t ||k_t||^2|).
 hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const float *g,
                        const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                        int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
                        const PlanArgs &pa, hipStream_t stream, bool tp_split = false,
-                       float *X_out = nullptr);
+                       float *X_out = nullptr, float *LC_out = nullptr);
 
 // Diagonal gating: the decayed key and query tiles per chunk-head ([64][d_k] each, operand
 // type) K o exp(G), Q o exp(G), K o exp(G_last - G), and exp(G_last) ([d_k] fp32).
@@ -99,7 +101,8 @@ hipError_t launch_scan_split(int d_k, int d_v, const void *q, const void *k, con
 // phases), for few long sequences: each sequence of L tokens is cut into G segments of Ls
 // tokens (a multiple of 64; the last one may be shorter).  NM holds [n_seq][G-1][H][d_k]
 // [d_v + d_k] fp32 and Sin [n_seq][G-1][H][d_k][d_v] fp32 (scratch).  Same inputs and
-// outputs as launch_scan with equal-length sequence tables.
+// outputs as launch_scan with equal-length sequence tables.  With sa.LC and sa.W, the
+// warm-up start above where it holds.
 enum ScanMode { kScanSeq = 0, kScanMap = 1, kScanSeg = 2 };
 struct SegArgs {
   int G = 0;                   // segments per sequence
@@ -107,7 +110,17 @@ struct SegArgs {
   int Ls = 0;                  // tokens per segment
   int dv = 0;                  // value columns d_v
   const float *Sin = nullptr;  // incoming states of segments 1 .. G-1 (set by the launcher)
+  // Warm-up start (optional): per chunk-head the log contraction bound launch_prep writes
+  // (LC_out), and the warm-up length W in chunks.  A (sequence, head) whose every segment
+  // boundary is preceded by W chunks that contract the state by 2^-150 or more (or that reach
+  // back to the sequence start) skips the map and combine phases: each segment starts W
+  // chunks early from a zero state (from S0 at the sequence start) and writes outputs from
+  // its own first chunk on.
+  const float *LC = nullptr;
+  int W = 0;
 };
+// ln(2^-150): the warm-up start's contraction threshold
+constexpr float kWarmLog = -103.97207708399179f;
 hipError_t launch_scan_two_level(Dtype dt, int d_k, int d_v, const void *q, const void *k,
                                  const void *v, const float *GD, const void *T, const void *P,
                                  const float *S0, void *o, float *S_T, int32_t n_seq, int32_t H,

@@ -248,7 +248,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
     float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out,
     float *__restrict__ GD_out, CoefOpts opts, PlanArgs pa, int tp_split,
-    float *__restrict__ X_out) {
+    float *__restrict__ X_out, float *__restrict__ LC_out) {
   __shared__ PrepSmem sm;
   const Planner pl = make_planner(pa, SeqTables{cu, chunk_off}, n_seq);
   write_tables(pl);
@@ -340,6 +340,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
   const int de = r16 & 3;
   const int pos0 = t0 - loc.ts + 1 + (opts.pos_offset ? opts.pos_offset[loc.n] : 0);
   float rqv[4], bme[4], G2me[4];  // per own row 16 i + r16: 1/||q||, b, G log2(e)
+  float lexp = 0.f;  // this lane's rows' ln max(1, |1 - b ||k||^2|) (lane group 0)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 16 * i + r16;
@@ -349,6 +350,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     float b_r = row < len ? write_coef(opts.beta_mode, eta_r, ss + eps, (float)(pos0 + row)) : 0.f;
     b_r = __shfl(b_r, dsrc, kWave);  // the diagonal lane's value, on all four lane groups
     bme[i] = b_r;
+    if (LC_out) {
+      const float bk = b_r * __shfl(ss, dsrc, kWave);  // b ||k||^2 of this row
+      if (kg == 0) lexp += logf(fmaxf(1.f, fabsf(1.f - bk)));
+    }
     G2me[i] = G_r * kLog2e;
     rqv[i] = 1.f;
     if (opts.normalize_q) {  // 1 / ||q|| (0 for a zero query)
@@ -364,6 +369,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
       if (GD_out) GD_out[gd0 + 2 * kChunk + row] = __expf(G_r) * rqv[i];
       if (beta_out && row < len) beta_out[(size_t)(t0 + row) * H + h] = b_r;
     }
+  }
+  // the chunk's contraction bound: the homogeneous map S -> S' of its tokens has spectral norm
+  // at most prod_t a_t max(1, |1 - b_t ||k_t||^2|) (each token's map is a_t (I - b_t k_t^T k_t),
+  // symmetric); its natural log, for the two-level scan's warm-up test
+  if (LC_out) {
+    const float lsum = wave_sum(lexp), glast = __shfl(G_l, kChunk - 1, kWave);
+    if (lane == 0) LC_out[task] = glast + lsum;
   }
   lds_barrier();
 
@@ -420,7 +432,7 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
                                 int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out,
                                 void *T_out, bool t_fp32, void *P_out, float *GD_out,
                                 const PlanArgs &pa, hipStream_t stream, bool tp_split,
-                                float *X_out) {
+                                float *X_out, float *LC_out) {
   if (n_chunks_ub <= 0 || H <= 0) return hipSuccess;
   if (tp_split && (sizeof(Tin) != 2 || t_fp32 || !GD_out)) return hipErrorInvalidValue;
   const int64_t tasks = n_chunks_ub * H;
@@ -431,12 +443,13 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
   if (t_fp32 || sizeof(Tin) == 4)
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(64), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts, pa, 0, X_out);
+                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts, pa, 0, X_out,
+                       LC_out);
   else
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(64), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
                        G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out, opts, pa,
-                       tp_split ? 1 : 0, X_out);
+                       tp_split ? 1 : 0, X_out, LC_out);
   return hipGetLastError();
 }
 
@@ -444,23 +457,24 @@ hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const fl
                        const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                        int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
-                       const PlanArgs &pa, hipStream_t stream, bool tp_split, float *X_out) {
+                       const PlanArgs &pa, hipStream_t stream, bool tp_split, float *X_out,
+                       float *LC_out) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)
       return launch_prep_t<__bf16, 128>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
                                         beta_out, T_out, t_fp32, P_out, GD_out, pa, stream,
-                                        tp_split, X_out);
+                                        tp_split, X_out, LC_out);
     return launch_prep_t<__bf16, 64>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
                                      beta_out, T_out, t_fp32, P_out, GD_out, pa, stream, tp_split,
-                                  X_out);
+                                  X_out, LC_out);
   }
   if (d_k == 128)
     return launch_prep_t<float, 128>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
                                      beta_out, T_out, t_fp32, P_out, GD_out, pa, stream, tp_split,
-                                  X_out);
+                                  X_out, LC_out);
   return launch_prep_t<float, 64>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, G_out,
                                   beta_out, T_out, t_fp32, P_out, GD_out, pa, stream, tp_split,
-                                  X_out);
+                                  X_out, LC_out);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -132,6 +132,30 @@ struct DmaPlan {
 // rounded operand other than K as a pair of bf16 values, hi = bf16(x) and lo = bf16(x - hi),
 // and sum hi*hi + hi*lo + lo*hi (K is exact in bf16: two terms).  The prep kernel stores T
 // and P as such pairs.  S stays one bf16 operand in K S and Q S.
+// Whether sequence seq, head h of the two-level scan takes the warm-up start: at every
+// segment boundary the W chunks before it either reach back to the sequence start or have a
+// contraction bound (the sum of their log bounds) of at most ln 2^-150.  Starting those W
+// chunks from a zero state then changes the segment's incoming state by at most 2^-150 times
+// the norm of the state W chunks back (the homogeneous map of the W chunks has at most that
+// spectral norm).  The same answer in every kernel that asks: it reads only LC.
+// Lane l of each wavefront tests boundary 1 + l (+ 64 i); the wavefront's answer is the AND.
+__device__ __forceinline__ bool warm_start(const SegArgs &sa, int seq, int h, int H) {
+  if (sa.LC == nullptr || sa.W <= 0) return false;
+  const int cps = (sa.L + kChunk - 1) / kChunk, cpg = sa.Ls / kChunk;
+  const int lane = threadIdx.x & 63;
+  bool ok = true;
+  for (int g0 = 1; g0 < sa.G; g0 += kWave) {
+    const int g = g0 + lane;
+    const int c1 = g * cpg, c0 = c1 - sa.W;
+    if (g < sa.G && c0 > 0) {  // else past the last boundary, or from S0 at the start: exact
+      float s = 0.f;
+      for (int c = c0; c < c1; ++c) s += sa.LC[((size_t)seq * cps + c) * H + h];
+      ok = ok && (s <= kWarmLog);  // a NaN bound fails too
+    }
+  }
+  return __all(ok);
+}
+
 template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES, int MODE,
           bool SPLIT = false>
 __global__ __launch_bounds__(SHP::THREADS)
@@ -177,6 +201,10 @@ void kla_scan_kernel(
   // row length of the values and outputs (the state may be wider in the map mode)
   int tb, te, cbase, VR = DV;
   [[maybe_unused]] int seq = n, seg = 0;
+  // the warm-up start (segment mode): chunks [0, nwarm) of this workgroup's run precede its
+  // segment and write nothing; `zero_start` runs them from a zero state
+  int nwarm = 0;
+  [[maybe_unused]] bool zero_start = false;
   if constexpr (MODE == kScanSeq) {
     tb = cu[n];
     te = cu[n + 1];
@@ -191,6 +219,14 @@ void kla_scan_kernel(
     VR = sa.dv;
     // segment 0 starts from S0 and needs no transition: its identity columns have no work
     if (MAP && seg == 0 && v0 >= sa.dv) return;
+    const bool warm = warm_start(sa, seq, h, H);
+    if (MAP && warm) return;  // the segments start early instead: no transitions needed
+    if (MODE == kScanSeg && warm && seg > 0) {
+      nwarm = min(sa.W, seg * (sa.Ls / kChunk));
+      tb -= nwarm * kChunk;
+      cbase -= nwarm;
+      zero_start = tb > seq * sa.L;  // else the run starts at the sequence start, from S0
+    }
   }
   const int nchunks = (te - tb + kChunk - 1) / kChunk;
 
@@ -303,6 +339,7 @@ void kla_scan_kernel(
   constexpr int NST = kChunk * PPR / (64 * NP);          // store instructions per producer wave
   auto p_flush = [&](int c, const SL &s) {
     if constexpr (NOQP) return;  // no outputs
+    if (c < nwarm) return;       // a warm-up chunk before the segment
     const int t0 = tb + c * kChunk;
     const int len = min(kChunk, te - t0);
     const Rsrc ro = make_rsrc(o + ((size_t)t0 * H + h) * DV + v0,
@@ -335,6 +372,7 @@ void kla_scan_kernel(
       if (MODE == kScanMap && cc >= VR) return r == cc - VR ? 1.f : 0.f;  // identity columns
       if (seg == 0) return S0 ? S0[seq_base + (size_t)r * VR + cc] : 0.f;
       if (MODE == kScanMap) return 0.f;  // N_g starts from zero
+      if (nwarm > 0) return zero_start ? 0.f : (S0 ? S0[seq_base + (size_t)r * VR + cc] : 0.f);
       return sa.Sin[(((size_t)seq * (sa.G - 1) + seg - 1) * H + h) * DK * (size_t)VR +
                     (size_t)r * VR + cc];
     }
@@ -813,7 +851,7 @@ hipError_t launch_scan_split(int d_k, int d_v, const void *q, const void *k, con
 template <int DK>
 __global__ __launch_bounds__(256) void kla_seg_combine_kernel(const float *__restrict__ NM,
                                                               float *__restrict__ Sin, int G,
-                                                              int H, int dv) {
+                                                              int H, int dv, SegArgs sa) {
   constexpr int KS = DK / 4;   // contraction steps; also rows per wavefront
   constexpr int TW = KS / 16;  // 16-row output tiles per wavefront
   constexpr int NF = KS / 4;   // float4 pieces of a lane's run of M_g's row
@@ -821,6 +859,7 @@ __global__ __launch_bounds__(256) void kla_seg_combine_kernel(const float *__res
   const int nsl = dv / 16;
   const int slice = blockIdx.x % nsl, sh = blockIdx.x / nsl;
   const int h = sh % H, n = sh / H;
+  if (warm_start(sa, n, h, H)) return;  // the segments start early instead
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kg = lane >> 4;
   const int W = dv + DK, c0 = 16 * slice;
   auto nm = [&](int g) { return NM + (((size_t)n * (G - 1) + g) * H + h) * DK * (size_t)W; };
@@ -914,7 +953,7 @@ static hipError_t launch_two_level_t(int d_v, const void *q, const void *k, cons
       nullptr, nullptr, sa);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kla_seg_combine_kernel<DK>, dim3((unsigned)(n_seq * H * (d_v / 16))),
-                     dim3(256), 0, stream, NM, Sin, sa.G, H, d_v);
+                     dim3(256), 0, stream, NM, Sin, sa.G, H, d_v, sa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return launch_scan_t<Tin, DK, false, false, kScanSeg>(d_v, (int64_t)n_seq * sa.G, q, k, v, GD,
                                                         T, P, S0, o, S_T, none, H, stream, nullptr,

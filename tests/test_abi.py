@@ -71,26 +71,28 @@ def test_workspace_bytes_formula(lib):
 def test_workspace_two_level_scratch(lib):
     """Dense input of few long sequences adds the two-level scan's fp32 scratch: per
     (sequence, segment but the last, head) [N_g | M_g] ([d_k][d_v + d_k]) and the chained
-    incoming state ([d_k][d_v]).  The shape rule: n_seq H d_v / 32 workgroups of the
-    sequential scan below 128 and G = min(512 / that, chunks per sequence / 32)."""
+    incoming state ([d_k][d_v]), and per chunk-head the log contraction bound of the warm-up
+    test.  The shape rule: n_seq H d_v / 32 workgroups of the sequential scan below 128 and
+    G = min(512 / that, chunks per sequence / 32)."""
     pad = lambda x: (x + 255) // 256 * 256
     n_seq, n_tok, H, dk, dv = 1, 65536, 16, 128, 128
+    nch = (n_tok + 63) // 64 + n_seq
     seq = kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, scan_segments=1)
     G = min(512 // (n_seq * H * dv // 32), (n_tok // 64) // 32)
     assert G == 8
     units = n_seq * (G - 1) * H * dk
-    want = seq + pad(4 * units * (dv + dk)) + pad(4 * units * dv)
+    want = seq + pad(4 * units * (dv + dk)) + pad(4 * units * dv) + pad(4 * nch * H)
     assert kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv) == want
     assert kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, scan_segments=8) == want
     # an explicit count: segments of ceil(chunks / G) chunks, G recounted over what holds tokens
     units7 = n_seq * 6 * H * dk
     assert (kla.kla_prefill_workspace_bytes(n_seq, n_tok, H, dk, dv, scan_segments=7)
-            == seq + pad(4 * units7 * (dv + dk)) + pad(4 * units7 * dv))
+            == seq + pad(4 * units7 * (dv + dk)) + pad(4 * units7 * dv) + pad(4 * nch * H))
     # 5 chunks in 4 requested segments: 2 chunks each, so 3 segments
     units3 = 1 * 2 * H * dk
     assert (kla.kla_prefill_workspace_bytes(1, 300, H, dk, dv, scan_segments=4)
             == kla.kla_prefill_workspace_bytes(1, 300, H, dk, dv, scan_segments=1)
-            + pad(4 * units3 * (dv + dk)) + pad(4 * units3 * dv))
+            + pad(4 * units3 * (dv + dk)) + pad(4 * units3 * dv) + pad(4 * (5 + 1) * H))
     # no scratch: enough sequences to fill the chip, short sequences, uneven totals (packed
     # input only), the diagonal gate
     for args in ((4, n_tok, H, dk, dv), (1, 64 * 63, H, dk, dv), (3, 3 * 4096 + 1, 2, dk, dv)):

@@ -299,6 +299,14 @@ def test_prefill_long_context_full(kla):
     (1, 64 * 9 + 13, 2, 128, 128, 3, True, True),    # the same without decay and with weak
     (3, 64 * 5 + 1, 2, 64, 64, 4, True, True),       # writes: the transitions M_g matter
     (1, 64 * 6, 40, 128, 128, 6, True, True),
+    # segments longer than the 8-chunk warm-up: with the workloads' gates every boundary's
+    # warm-up contracts by far more than 2^-150 (segments start early from zero); without
+    # decay none does (map, combine and segment phases); both in one call ('head0': head 0
+    # without decay)
+    (1, 64 * 40 + 7, 2, 128, 128, 4, True, False),
+    (2, 64 * 33, 2, 64, 128, 3, True, False),
+    (1, 64 * 40 + 7, 2, 128, 128, 4, True, True),
+    (1, 64 * 40 + 7, 3, 128, 128, 4, True, "head0"),
 ])
 def test_prefill_two_level_scan(kla, dtype, n_seq, T, H, dk, dv, G, S0, weak):
     """The two-level scan (segments' transitions, chained incoming states, segments rerun)
@@ -308,7 +316,10 @@ def test_prefill_two_level_scan(kla, dtype, n_seq, T, H, dk, dv, G, S0, weak):
     carries across whole segments and the chained states depend on M_g."""
     w = ki.Workload(97, "unit", n_seq, H, dk, dv, dtype, T=T, s0_var=0.01)
     inp = ki.prefill_inputs(w)
-    if weak:
+    if weak == "head0":
+        inp["g"][:, 0] = 0.0
+        inp["eta"][:, 0] = inp["eta"][:, 0] * 0.05
+    elif weak:
         inp["g"] = torch.zeros_like(inp["g"])
         inp["eta"] = inp["eta"] * 0.05
     d = to_dev(inp)
