@@ -20,7 +20,9 @@ the forward oracle are covered (``beta_mode``: the gated delta rule's b_t = eta_
 key-norm only b_t = 1/(||k_t||^2 + eps) and the sequence factors 1/t, 1/sqrt(t),
 1/log(t + 1) on the Kaczmarz coefficient, Appendix D and Table 5; t the absolute 1-based
 position, sequence n starting at pos_offset[n] + 1) and the readout divided by ||q_t||
-(section 3.3; 0 for a zero query), with one scalar gate per token-head.
+(section 3.3; 0 for a zero query), with one scalar gate per token-head, or one gate per key
+channel (Appendix B.5, diagonal gating: g of shape [n_tok, H, d_k], S~ = Diag(exp(g_t)) S_{t-1},
+the rows of S being key channels).
 """
 from __future__ import annotations
 
@@ -62,10 +64,10 @@ def _sequence(q, k, v, g, eta, eps, S0, mode="kaczmarz", pos0=0, normalize_q=Fal
     outs = []
     for t in range(q.shape[0]):
         kt, qt = k[t], q[t]                                   # [H, dk]
-        a = torch.exp(g[t])                                   # [H]
+        a = torch.exp(g[t])                                   # [H], or [H, dk] per key channel
         den = (kt * kt).sum(-1) + eps                         # [H]
         b = _coef(mode, eta[t], den, float(pos0 + t + 1))
-        St = a[:, None, None] * S                             # forget
+        St = (a[:, :, None] if a.dim() == 2 else a[:, None, None]) * S   # forget
         e = v[t] - torch.einsum("hi,hij->hj", kt, St)         # residual
         S = St + b[:, None, None] * kt[:, :, None] * e[:, None, :]   # Kaczmarz write
         if normalize_q:                                       # readout q_t / ||q_t||
@@ -84,7 +86,8 @@ def prefill_backward(q, k, v, g, eta, eps, dO, S0=None, dS_T=None, cu_seqlens=No
     """Gradients of the prefill for the cotangents dO [n_tok, H, dv] and dS_T [n_seq, H, dk, dv].
 
     Inputs as for :func:`oracle.prefill` (q, k [n_tok, H, dk]; v [n_tok, H, dv];
-    g, eta [n_tok, H]; S0 [n_seq, H, dk, dv] or None = zeros; dS_T None = zeros);
+    g, eta [n_tok, H], or g [n_tok, H, dk] for diagonal gating; S0 [n_seq, H, dk, dv] or
+    None = zeros; dS_T None = zeros);
     without cu_seqlens the tokens are n_seq sequences of equal length.  beta_mode,
     pos_offset ([n_seq] or None) and normalize_q select the variant as in the forward oracle.
     Returns numpy float64 arrays (dq, dk, dv, dg, deta, dS0), shaped like the inputs.

@@ -203,3 +203,59 @@ def test_normalised_readout_zero_query():
     dq = ob.prefill_backward(q, k, v, g, eta, 1e-6, dO, S0=S0, dS_T=dST, normalize_q=True)[0]
     assert np.all(np.isfinite(dq)) and np.abs(dq[2]).max() == 0.0
     assert np.abs(dq[1]).max() > 0
+
+
+def draw_diag(seed, n_tok, H=2, dk=3, dv=2, n_seq=1):
+    """draw() with one log-decay per key channel (diagonal gating), channels decaying at
+    rates that differ by an order of magnitude"""
+    q, k, v, _, eta, S0, dO, dST = draw(seed, n_tok, H=H, dk=dk, dv=dv, n_seq=n_seq)
+    rng = np.random.default_rng(seed + 1000)
+    g = rng.uniform(-1.0, 0.0, (n_tok, H, dk)) * 10.0 ** rng.uniform(-1.0, 0.0, (1, 1, dk))
+    return q, k, v, g, eta, S0, dO, dST
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.3])
+def test_diagonal_gate_gradients_match_central_differences(eps):
+    # Appendix B.5: every input element of a small packed case against central differences of
+    # the C oracle's diagonal-gate forward pass (g per key channel)
+    q, k, v, g, eta, S0, dO, dST = draw_diag(11, 7, H=2, dk=3, dv=2, n_seq=2)
+    cu = np.array([0, 5, 7])
+    grads = ob.prefill_backward(q, k, v, g, eta, eps, dO, S0=S0, dS_T=dST, cu_seqlens=cu)
+    assert grads[3].shape == g.shape
+    inputs = [q, k, v, g, eta, S0]
+    h = 1e-6
+    for which, (x, gx) in enumerate(zip(inputs, grads)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = [a.copy() for a in inputs]
+            xm = [a.copy() for a in inputs]
+            xp[which][idx] += h
+            xm[which][idx] -= h
+            num[idx] = (loss_c(*xp[:5], eps, xp[5], dO, dST, cu) -
+                        loss_c(*xm[:5], eps, xm[5], dO, dST, cu)) / (2 * h)
+        err = np.abs(num - gx).max() / max(np.abs(num).max(), 1e-300)
+        assert err < 1e-6, (which, err)
+
+
+def test_diagonal_gate_with_equal_channels_is_the_scalar_gate():
+    # a per-channel gate equal across channels is the scalar gate (Appendix B.5 with
+    # Diag(alpha_t) = alpha_t I): the same gradients of q, k, v, eta and S0, and the scalar
+    # gate's dg_t is the sum of the channels' dg_t (chain rule through g_t -> (g_t, .., g_t))
+    q, k, v, g, eta, S0, dO, dST = draw(12, 9, H=2, dk=4, dv=3, n_seq=1)
+    gd = np.repeat(g[:, :, None], 4, axis=2)
+    gs = ob.prefill_backward(q, k, v, g, eta, 1e-3, dO, S0=S0, dS_T=dST)
+    gdg = ob.prefill_backward(q, k, v, gd, eta, 1e-3, dO, S0=S0, dS_T=dST)
+    for which in (0, 1, 2, 4, 5):
+        assert np.abs(gs[which] - gdg[which]).max() < 1e-12 * np.abs(gs[which]).max()
+    assert np.abs(gdg[3].sum(-1) - gs[3]).max() < 1e-12 * np.abs(gs[3]).max()
+
+
+def test_diagonal_gate_dead_channel_blocks_the_state():
+    # a channel whose gate is -inf at the first token forgets row c of S0 before anything
+    # reads it (Diag(alpha_1) with alpha_{1,c} = 0), so the gradients of that row of S0
+    # vanish, while the other rows keep theirs
+    q, k, v, g, eta, S0, dO, dST = draw_diag(13, 6, H=1, dk=3, dv=2)
+    g[0, 0, 1] = -np.inf
+    dS0 = ob.prefill_backward(q, k, v, g, eta, 1e-3, dO, S0=S0, dS_T=dST)[5]
+    assert np.abs(dS0[0, 0, 1]).max() == 0.0
+    assert np.abs(dS0[0, 0, 0]).max() > 0 and np.abs(dS0[0, 0, 2]).max() > 0
