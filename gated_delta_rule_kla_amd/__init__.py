@@ -95,6 +95,9 @@ def load_library():
     lib.kla_prefill_chunked_noalloc.restype = ctypes.c_int
     lib.kla_prefill_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     lib.kla_prefill_backward_workspace_bytes.restype = sz
+    lib.kla_prefill_backward_workspace_bytes_ex.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int,
+                                                            opt_p]
+    lib.kla_prefill_backward_workspace_bytes_ex.restype = sz
     lib.kla_prefill_backward.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp,
                                          sz, vp]
@@ -278,10 +281,13 @@ def kla_prefill_chunked(q, k, v, g, eta, eps: float = 1e-6, S0=None, cu_seqlens=
 
 
 def kla_prefill_backward_workspace_bytes(n_seq: int, total_tokens: int, n_heads: int, d_k: int,
-                                         d_v: int, dtype=torch.bfloat16) -> int:
-    """Workspace bytes kla_prefill_backward needs (0 for unsupported sizes)."""
-    return int(load_library().kla_prefill_backward_workspace_bytes(
-        n_seq, total_tokens, n_heads, d_k, d_v, _DTYPES[dtype]))
+                                         d_v: int, dtype=torch.bfloat16,
+                                         diagonal_gate: bool = False) -> int:
+    """Workspace bytes kla_prefill_backward needs (0 for unsupported sizes); diagonal_gate
+    sizes it for the diagonal-gated variant."""
+    opts = (ctypes.pointer(KlaOptions(0, 0, None, 1, 0, 0)) if diagonal_gate else None)
+    return int(load_library().kla_prefill_backward_workspace_bytes_ex(
+        n_seq, total_tokens, n_heads, d_k, d_v, _DTYPES[dtype], opts))
 
 
 def kla_prefill_backward(q, k, v, g, eta, eps: float, dO, S0=None, dS_T=None, cu_seqlens=None,
@@ -290,12 +296,12 @@ def kla_prefill_backward(q, k, v, g, eta, eps: float, dO, S0=None, dS_T=None, cu
                          pos_offset=None):
     """Gradients of the prefill for the cotangents dO (like o) and dS_T (like S_T, or None).
 
-    Inputs as for :func:`kla_prefill_chunked`, with a scalar gate; beta_mode / normalize_q /
-    pos_offset select the variant of the forward call.  Returns
-    (dq, dk, dv, dg, deta, dS0), shaped like q, k, v, g, eta and S0 ([n_seq, H, d_k, d_v];
-    None when need_dS0 is False).
+    Inputs as for :func:`kla_prefill_chunked`: a g shaped like k selects diagonal gating (one
+    log-decay per key channel); beta_mode / normalize_q / pos_offset select the variant of the
+    forward call.  Returns (dq, dk, dv, dg, deta, dS0), shaped like q, k, v, g, eta and S0
+    ([n_seq, H, d_k, d_v]; None when need_dS0 is False).
     """
-    shape_q, shape_v, shape_g = q.shape, v.shape, g.shape
+    shape_q, shape_v, shape_g, shape_eta = q.shape, v.shape, g.shape, eta.shape
     q, k, v, g, eta, n_seq = _flatten_tokens(q, k, v, g, eta, cu_seqlens, n_seq)
     dev = q.device
     _need(q, "q", device=dev)
@@ -308,9 +314,10 @@ def kla_prefill_backward(q, k, v, g, eta, eps: float, dO, S0=None, dS_T=None, cu
     _need(eta, "eta", torch.float32, dev)
     n_tok, H, d_k = q.shape
     d_v = v.shape[-1]
-    if (k.shape != q.shape or v.shape[:2] != (n_tok, H) or g.shape != (n_tok, H)
+    diag = tuple(g.shape) == (n_tok, H, d_k)
+    if (k.shape != q.shape or v.shape[:2] != (n_tok, H) or (g.shape != (n_tok, H) and not diag)
             or eta.shape != (n_tok, H)):
-        raise ValueError("inconsistent q/k/v/g/eta shapes (the backward takes a scalar gate)")
+        raise ValueError("inconsistent q/k/v/g/eta shapes")
     dO = dO.reshape(n_tok, H, d_v)
     _need(dO, "dO", dt, dev)
     if cu_seqlens is not None:
@@ -332,19 +339,19 @@ def kla_prefill_backward(q, k, v, g, eta, eps: float, dO, S0=None, dS_T=None, cu
     deta = torch.empty_like(eta)
     dS0 = torch.empty((n_seq, H, d_k, d_v), dtype=torch.float32, device=dev) if need_dS0 else None
     lib = load_library()
-    ws_bytes = int(lib.kla_prefill_backward_workspace_bytes(n_seq, n_tok, H, d_k, d_v,
-                                                            _DTYPES[dt]))
+    opts = _options(beta_mode, normalize_q, pos_offset, n_seq, dev, diagonal_gate=diag)
+    ws_bytes = int(lib.kla_prefill_backward_workspace_bytes_ex(n_seq, n_tok, H, d_k, d_v,
+                                                               _DTYPES[dt], opts))
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     host_ptr = None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr())
-    opts = _options(beta_mode, normalize_q, pos_offset, n_seq, dev)
     _check(lib.kla_prefill_backward_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(eta), float(eps), _ptr(S0), _ptr(dO),
         _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(deta), _ptr(dS0),
         _ptr(cu_seqlens), host_ptr, n_seq, n_tok, H, d_k, d_v, _DTYPES[dt], _ptr(workspace),
         workspace.numel(), opts, _stream(dev)))
     return (dq.reshape(shape_q), dk.reshape(shape_q), dv.reshape(shape_v), dg.reshape(shape_g),
-            deta.reshape(shape_g), dS0)
+            deta.reshape(shape_eta), dS0)
 
 
 def kla_prefill_prepare(q, k, g, eta, eps, workspace, *, n_seq, d_v, cu_seqlens=None,

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkla.so")
 SOURCES = ["kla_api.hip", "kla_prep.hip", "kla_scan.hip", "kla_decode.hip", "kla_diag.hip",
-           "kla_bwd.hip"]
+           "kla_bwd.hip", "kla_bwd_diag.hip"]
 ARCH = "gfx950"
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -221,15 +221,17 @@ namespace {
 // Backward workspace: the forward layout, then per chunk-head the incoming states S and the
 // cotangents dS' of the outgoing ones ([d_k][d_v]), dU and dR ([64][d_v] each), all in the
 // operand type, and X = (I + L)^{-1} (fp32 packed blocks, kTpbElems floats).
+// Diagonal gating adds the forward's decayed tiles (in the forward layout) and A itself
+// (fp32 packed blocks, like X).
 struct BwdLayout {
   WsLayout fw;
-  size_t off_SN, off_dSo, off_dU, off_dR, off_X, total;
+  size_t off_SN, off_dSo, off_dU, off_dR, off_X, off_A = 0, total;
 };
 
 BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, int64_t d_v,
-                     size_t es) {
+                     size_t es, bool diag = false) {
   BwdLayout b;
-  b.fw = ws_layout(n_seq, total_tokens, H, d_k, es);
+  b.fw = ws_layout(n_seq, total_tokens, H, d_k, es, diag);
   const size_t nch = (size_t)kla::chunk_upper_bound(n_seq, total_tokens);
   const size_t st = es * nch * (size_t)H * (size_t)d_k * (size_t)d_v;
   const size_t ut = es * nch * (size_t)H * KLA_CHUNK * (size_t)d_v;
@@ -239,6 +241,10 @@ BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k
   b.off_dR = align256(b.off_dU + ut);
   b.off_X = align256(b.off_dR + ut);
   b.total = align256(b.off_X + sizeof(float) * nch * (size_t)H * kla::kTpbElems);
+  if (diag) {
+    b.off_A = b.total;
+    b.total = align256(b.off_A + sizeof(float) * nch * (size_t)H * kla::kTpbElems);
+  }
   return b;
 }
 
@@ -246,13 +252,22 @@ BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k
 
 extern "C" {
 
-size_t kla_prefill_backward_workspace_bytes(int32_t n_seq, int32_t total_tokens,
-                                            int32_t n_heads, int32_t d_k, int32_t d_v,
-                                            kla_dtype dtype) {
+size_t kla_prefill_backward_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens,
+                                               int32_t n_heads, int32_t d_k, int32_t d_v,
+                                               kla_dtype dtype, const kla_options *opts) {
   if (n_seq <= 0 || total_tokens < 0 || n_heads <= 0 || !supported_dk(d_k) ||
       !supported_dv(d_v) || (dtype != KLA_DTYPE_F32 && dtype != KLA_DTYPE_BF16))
     return 0;
-  return bwd_layout(n_seq, total_tokens, n_heads, d_k, d_v, elem_size(dtype)).total;
+  return bwd_layout(n_seq, total_tokens, n_heads, d_k, d_v, elem_size(dtype),
+                    opts && opts->diagonal_gate != 0)
+      .total;
+}
+
+size_t kla_prefill_backward_workspace_bytes(int32_t n_seq, int32_t total_tokens,
+                                            int32_t n_heads, int32_t d_k, int32_t d_v,
+                                            kla_dtype dtype) {
+  return kla_prefill_backward_workspace_bytes_ex(n_seq, total_tokens, n_heads, d_k, d_v, dtype,
+                                                 nullptr);
 }
 
 }  // extern "C"
@@ -335,14 +350,16 @@ WsViews ws_views(void *workspace, int32_t n_seq, int32_t total_tokens, int32_t n
 kla_status enqueue_prepare_diag(const void *q, const void *k, const float *g, const float *eta,
                                 float eps, const kla::CoefOpts &opts, const int32_t *cu_seqlens,
                                 int32_t n_seq, int32_t total_tokens, int32_t n_heads, int32_t d_k,
-                                kla_dtype dtype, void *workspace, hipStream_t s) {
+                                kla_dtype dtype, void *workspace, hipStream_t s,
+                                float *X_out = nullptr, float *A_out = nullptr) {
   const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, true);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
   kla_status st =
       hip_status(kla::launch_plan(cu_seqlens, n_seq, total_tokens, wv.tabs, s), "plan");
   if (st != KLA_OK) return st;
   return hip_status(kla::launch_prep_diag(to_dt(dtype), d_k, q, k, g, eta, eps, opts, wv.tabs,
-                                          n_seq, nch_ub, n_heads, wv.diag, wv.T, wv.P, wv.GD, s),
+                                          n_seq, nch_ub, n_heads, wv.diag, wv.T, wv.P, wv.GD, s,
+                                          X_out, A_out),
                     "prep (diagonal gate)");
 }
 
@@ -533,8 +550,7 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
   kla::CoefOpts co;
   kla_status st = to_coef(opts, &co);
   if (st != KLA_OK) return st;
-  if (co.diag_gate)
-    return fail(KLA_ERR_UNSUPPORTED, "the backward pass takes no diagonal gate");
+  const bool diag = co.diag_gate != 0;
   if (opts && opts->precision != KLA_PRECISION_BF16)
     return fail(KLA_ERR_UNSUPPORTED, "the backward pass takes the bf16 operand precision only");
   if ((st = check_prefill_shape(cu_seqlens_host, n_seq, total_tokens, n_heads, d_k, d_v, dtype,
@@ -559,11 +575,12 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
   const size_t nq = (size_t)total_tokens * n_heads * d_k * es;
   const size_t nv = (size_t)total_tokens * n_heads * d_v * es;
   const size_t ns = (size_t)total_tokens * n_heads * sizeof(float);
+  const size_t ng = ns * (diag ? (size_t)d_k : 1);  // g and dg: per key channel under diag
   const size_t nS = (size_t)n_seq * n_heads * d_k * d_v * sizeof(float);
   const void *outs[] = {dq, dk, dv, dg, deta, dS0};
-  const size_t nouts[] = {nq, nq, nv, ns, ns, nS};
+  const size_t nouts[] = {nq, nq, nv, ng, ns, nS};
   const void *ins[] = {q, k, v, g, eta, S0, dO, dS_T};
-  const size_t nins[] = {nq, nq, nv, ns, ns, nS, nv, nS};
+  const size_t nins[] = {nq, nq, nv, ng, ns, nS, nv, nS};
   for (int i = 0; i < 6; ++i) {
     for (int j = 0; j < 8; ++j)
       if (overlap(outs[i], nouts[i], ins[j], nins[j]))
@@ -572,7 +589,7 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
       if (overlap(outs[i], nouts[i], outs[j], nouts[j]))
         return fail(KLA_ERR_INVALID_ARGUMENT, "gradient buffers must not overlap each other");
   }
-  const BwdLayout bl = bwd_layout(n_seq, total_tokens, n_heads, d_k, d_v, es);
+  const BwdLayout bl = bwd_layout(n_seq, total_tokens, n_heads, d_k, d_v, es, diag);
   if (!workspace || workspace_bytes < bl.total)
     return fail(KLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", bl.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -586,14 +603,19 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
   (void)hipGetLastError();  // clear any stale error from unrelated work
   char *ws = static_cast<char *>(workspace);
   float *Xbuf = reinterpret_cast<float *>(ws + bl.off_X);
-  if ((st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
-                            dtype, workspace, s, false, Xbuf)) != KLA_OK)
-    return st;
-  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype);
+  float *Abuf = diag ? reinterpret_cast<float *>(ws + bl.off_A) : nullptr;
+  if (diag)
+    st = enqueue_prepare_diag(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads,
+                              d_k, dtype, workspace, s, Xbuf, Abuf);
+  else
+    st = enqueue_prepare(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads, d_k,
+                         dtype, workspace, s, false, Xbuf);
+  if (st != KLA_OK) return st;
+  const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, diag);
   void *SN = ws + bl.off_SN;  // incoming states in the operand type
   if ((st = hip_status(kla::launch_scan(to_dt(dtype), d_k, d_v, nullptr, k, v, wv.GD, wv.T,
                                         nullptr, S0, nullptr, nullptr, wv.tabs, n_seq, n_heads,
-                                        s, nullptr, SN),
+                                        s, diag ? &wv.diag : nullptr, SN),
                        "scan (stored states)")) != KLA_OK)
     return st;
   if ((st = hip_status(
@@ -601,7 +623,7 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
                            Xbuf, dS_T, SN, ws + bl.off_dSo, ws + bl.off_dU, ws + bl.off_dR, dq,
                            dk, dv, dg, deta, dS0,
                            wv.tabs, n_seq, kla::chunk_upper_bound(n_seq, total_tokens), n_heads,
-                           s),
+                           s, diag ? &wv.diag : nullptr, Abuf),
            "backward")) != KLA_OK)
     return st;
   return ok();

@@ -39,241 +39,11 @@
 // Products run on fp32 MFMA (v_mfma_f32_16x16x4_f32) for fp32 inputs, and on bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16, operands rounded to bf16 as they are read, fp32 accumulation)
 // for bf16 inputs.
-#include "kla_device.h"
-#include "kla_launch.h"
+#include "kla_bwd_common.h"
 
 namespace kla {
 
 namespace {
-
-constexpr int kAdjBV = 32;          // state columns per adjoint-scan workgroup
-constexpr int kAdjThreads = 512;    // eight wavefronts, two to a SIMD
-constexpr int kGradThreads = 512;   // eight wavefronts
-constexpr int LDB = kAdjBV + 4;     // row stride (elements) of a 32-column block in LDS
-constexpr int LDC = kChunk + 4;     // row stride of a 64 x 64 fp32 tile in LDS
-
-// acc[i][j] += sum_{k < KD} A(i, k) B(k, j) over one 16 x 16 tile: lane (r, kq) = (l % 16,
-// l / 16) supplies A(r, k0 + kq) and B(k0 + kq, r) and holds D[4 kq + e][r] of the result.
-template <int KD, typename FA, typename FB>
-__device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int lane, FA fa, FB fb) {
-  const int r = lane & 15, kq = lane >> 4;
-#pragma unroll
-  for (int k0 = 0; k0 < KD; k0 += 4)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa(r, k0 + kq), fb(k0 + kq, r), acc, 0, 0, 0);
-  return acc;
-}
-
-// The same tile product in the operand precision of the inputs: fp32 inputs keep the fp32
-// MFMA; bf16 inputs round both operands to bf16 and contract 32 at a time on
-// v_mfma_f32_16x16x32_bf16 (lane (r, kq) supplies A(r, k0 + 8 kq + s) and B(k0 + 8 kq + s, r),
-// s = 0..7), accumulating in fp32.  KD is a multiple of 32.
-template <typename Tin, int KD, typename FA, typename FB>
-__device__ __forceinline__ f32x4 mmt(f32x4 acc, int lane, FA fa, FB fb) {
-  if constexpr (sizeof(Tin) == 2) {
-    const int r = lane & 15, kq = lane >> 4;
-#pragma unroll
-    for (int k0 = 0; k0 < KD; k0 += 32) {
-      bf16x8 a, b;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        a[s] = from_f32<__bf16>(fa(r, k0 + 8 * kq + s));
-        b[s] = from_f32<__bf16>(fb(k0 + 8 * kq + s, r));
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-    }
-    return acc;
-  } else {
-    return mm_tile<KD>(acc, lane, fa, fb);
-  }
-}
-
-// The same tile product with each lane's operands read as contiguous runs: pa(r, k) points at
-// A(r, k .. k + 7) and pb(r, k) at B(k .. k + 7, r) (a row of B^T), for k = k0 + 8 kq; the
-// pointees are float or __bf16 (16-byte aligned).  bf16 inputs: one v_mfma_f32_16x16x32_bf16
-// per 32 contraction indices (fp32 pointees rounded to bf16 as read); fp32 inputs: eight
-// exact v_mfma_f32_16x16x4_f32 steps, step s contracting the indices k0 + 8 kq + s.
-__device__ __forceinline__ void rd8(const float *p, float (&x)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
-  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3]; x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
-}
-__device__ __forceinline__ void rd8(const __bf16 *p, float (&x)[8]) {
-  const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) x[s] = to_f32(v[s]);
-}
-__device__ __forceinline__ bf16x8 rd8b(const float *p) {
-  float x[8];
-  rd8(p, x);
-  bf16x8 r;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) r[s] = from_f32<__bf16>(x[s]);
-  return r;
-}
-__device__ __forceinline__ bf16x8 rd8b(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-template <typename Tin, int KD, typename PA, typename PB>
-__device__ __forceinline__ f32x4 mmr(f32x4 acc, int lane, PA pa, PB pb) {
-  const int r = lane & 15, kq = lane >> 4;
-#pragma unroll
-  for (int k0 = 0; k0 < KD; k0 += 32) {
-    if constexpr (sizeof(Tin) == 2) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rd8b(pa(r, k0 + 8 * kq)), rd8b(pb(r, k0 + 8 * kq)),
-                                                    acc, 0, 0, 0);
-    } else {
-      float a[8], b[8];
-      rd8(pa(r, k0 + 8 * kq), a);
-      rd8(pb(r, k0 + 8 * kq), b);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
-    }
-  }
-  return acc;
-}
-
-// Four consecutive elements as loaded (raw), and as fp32.
-template <typename T> struct Raw4;
-template <> struct Raw4<float> { typedef f32x4 type; };
-template <> struct Raw4<__bf16> { typedef bf16x4 type; };
-__device__ __forceinline__ f32x4 cvt4(const f32x4 &x) { return x; }
-__device__ __forceinline__ f32x4 cvt4(const bf16x4 &x) {
-  return f32x4{to_f32(x[0]), to_f32(x[1]), to_f32(x[2]), to_f32(x[3])};
-}
-
-// Rows [0, len) of a row-strided tensor, columns 0 .. NC - 1 from src, into an LDS tile with
-// row stride LD (fp32, or bf16 rows copied as they are); rows past len are zero.  Every load
-// of the thread is issued before the first store.  With sq, also each row's squared norm into
-// sq[row] (the NC / 4 consecutive lanes that hold a row reduce it).
-template <int NC, int LD, int NT, typename D, typename Src>
-__device__ __forceinline__ void stage_rows(D *dst, const Src *src, size_t row_stride, int len,
-                                           int tid, float *sq = nullptr) {
-  constexpr int N4 = NC / 4;
-  static_assert((kChunk * N4) % NT == 0 && 64 % N4 == 0, "whole rounds of pieces");
-  static_assert(sizeof(D) == 4 || sizeof(Src) == 2, "bf16 tiles take bf16 rows");
-  constexpr int NPER = kChunk * N4 / NT;
-  typename Raw4<Src>::type x[NPER];
-#pragma unroll
-  for (int m = 0; m < NPER; ++m) {
-    const int e = tid + NT * m, r = e / N4, c = 4 * (e % N4);
-    typename Raw4<Src>::type z = {};
-    if (r < len) z = *reinterpret_cast<const typename Raw4<Src>::type *>(src + (size_t)r * row_stride + c);
-    x[m] = z;
-  }
-#pragma unroll
-  for (int m = 0; m < NPER; ++m) {
-    const int e = tid + NT * m, r = e / N4, c = 4 * (e % N4);
-    if constexpr (sizeof(D) == 2)
-      *reinterpret_cast<bf16x4 *>(dst + r * LD + c) = x[m];
-    else
-      *reinterpret_cast<f32x4 *>(dst + r * LD + c) = cvt4(x[m]);
-  }
-  if (sq) {
-#pragma unroll
-    for (int m = 0; m < NPER; ++m) {
-      const f32x4 v = cvt4(x[m]);
-      float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-#pragma unroll
-      for (int off = 1; off < N4; off <<= 1) ss += __shfl_xor(ss, off, N4);
-      const int e = tid + NT * m;
-      if (e % N4 == 0) sq[e / N4] = ss;
-    }
-  }
-}
-
-// the (I, J) block of the ten blocks on and below the diagonal, in the order (0,0) (1,0) (1,1)
-// (2,0) (2,1) (2,2) (3,0) .. (3,3)
-__device__ __forceinline__ void lower_block(int b, int &I, int &J) {
-  I = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0;
-  J = b - I * (I + 1) / 2;
-}
-
-// A tile of NR rows x NC columns of a row-strided tensor, held in registers between its
-// load (all of a thread's loads issued back to back) and its store into an fp32 LDS tile;
-// rows at or past `len` read as zeros.
-template <typename T, int NR, int NC, int NT>
-struct RegTile {
-  static constexpr int NQ = NR * NC / 4, J = (NQ + NT - 1) / NT;
-  typename Raw4<T>::type x[J];
-  __device__ __forceinline__ void load(const T *src, size_t row_stride, int len, int tid) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int e = tid + NT * j, r = e / (NC / 4), c = 4 * (e % (NC / 4));
-      typename Raw4<T>::type z = {};
-      if ((NQ % NT == 0 || e < NQ) && r < len)
-        z = *reinterpret_cast<const typename Raw4<T>::type *>(src + (size_t)r * row_stride + c);
-      x[j] = z;
-    }
-  }
-  template <int LD, typename D>
-  __device__ __forceinline__ void store(D *dst, int tid) const {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int e = tid + NT * j, r = e / (NC / 4), c = 4 * (e % (NC / 4));
-      if (NQ % NT == 0 || e < NQ) {
-        const f32x4 v = cvt4(x[j]);
-        if constexpr (sizeof(D) == 2) {
-          bf16x4 b;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) b[i] = from_f32<__bf16>(v[i]);
-          *reinterpret_cast<bf16x4 *>(dst + r * LD + c) = b;
-        } else {
-          *reinterpret_cast<f32x4 *>(dst + r * LD + c) = v;
-        }
-      }
-    }
-  }
-  // each row's squared norm into sq[row] (the NC / 4 consecutive lanes holding a row reduce it)
-  __device__ __forceinline__ void sqnorms(float *sq, int tid) const {
-    constexpr int N4 = NC / 4;
-    static_assert(NQ % NT == 0 && 64 % N4 == 0, "whole rows within a wavefront");
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const f32x4 v = cvt4(x[j]);
-      float ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-#pragma unroll
-      for (int off = 1; off < N4; off <<= 1) ss += __shfl_xor(ss, off, N4);
-      const int e = tid + NT * j;
-      if (e % N4 == 0) sq[e / N4] = ss;
-    }
-  }
-};
-
-// A 64 x 64 matrix stored as its ten lower 16 x 16 blocks (the prep kernel's packed T and P),
-// in registers; stored into the lower blocks of an fp32 LDS tile (the upper blocks are left
-// as they are: zero).
-template <typename T, int NT>
-struct PackedTile {
-  static constexpr int NQ = 10 * 256 / 4, J = (NQ + NT - 1) / NT;
-  typename Raw4<T>::type x[J];
-  __device__ __forceinline__ void load(const T *src, int tid) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int pq = tid + NT * j;
-      typename Raw4<T>::type z = {};
-      if (pq < NQ) z = *reinterpret_cast<const typename Raw4<T>::type *>(src + 4 * pq);
-      x[j] = z;
-    }
-  }
-  __device__ __forceinline__ void store(float (*dst)[LDC], int tid) const {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int pq = tid + NT * j;
-      if (pq < NQ) {
-        const int e0 = 4 * pq, w = e0 & 255;
-        int I, Jb;
-        lower_block(e0 >> 8, I, Jb);
-        *reinterpret_cast<f32x4 *>(&dst[16 * I + (w >> 4)][16 * Jb + (w & 15)]) = cvt4(x[j]);
-      }
-    }
-  }
-};
-
-// sum over the 16 lanes of a DPP row (lanes with the same l / 16)
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __shfl_xor(x, 1, 16);
-  x += __shfl_xor(x, 2, 16);
-  x += __shfl_xor(x, 4, 16);
-  x += __shfl_xor(x, 8, 16);
-  return x;
-}
 
 template <int DK>
 struct AdjSmem {
@@ -286,19 +56,26 @@ struct AdjSmem {
   float dR[kChunk][LDB];
   float dS[DK][LDB];
   float gam[kChunk], dec[kChunk], gamO[kChunk];
+  float gC[DK];  // diagonal gating: exp(G_last) per key channel
 };
 
 }  // namespace
 
 // The adjoint scan.  Workgroup (sequence n, head h, slice) owns state columns
 // 32 slice .. + 31 of dS for the whole sequence, in LDS.
-template <typename Tin, int DK>
+// DIAG (diagonal gating, Appendix B.5): the prep's decayed tiles replace the key and query
+// rows: dU = P^T dO + Kd dS' with Kd = K o exp(G_last - G), and
+// dS = Diag(exp(G_last)) dS' + Qg^T Diag(gamO) dO - Kg^T dR with Qg = Q o exp(G),
+// Kg = K o exp(G), exp(G_last) per key channel (the prep's gam and dec are then 1).  Kd sits
+// in the key tile for the dU products and Kg replaces it once they are done.
+template <typename Tin, int DK, bool DIAG>
 __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ dO,
     const float *__restrict__ GD, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
     const float *__restrict__ dST, float *__restrict__ dS0, float *__restrict__ dSo,
     float *__restrict__ dUo, float *__restrict__ dRo, Tin *__restrict__ dv,
-    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV) {
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV,
+    DiagTiles dg) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AdjSmem<DK> &sm = *reinterpret_cast<AdjSmem<DK> *>(smem_raw);
   // the d_v slices of one (sequence, head) read the same K, Q, T and P: give them
@@ -329,6 +106,7 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
   // a chunk's tiles are loaded into registers while the chunk before it (in this reverse
   // order) is computed, and written to LDS when its turn comes
   RegTile<Tin, kChunk, DK, kAdjThreads> rk, rq;
+  RegTile<Tin, DIAG ? kChunk : 4, DIAG ? DK : 4, kAdjThreads> rkg;  // Kg (DIAG)
   RegTile<Tin, kChunk, kAdjBV, kAdjThreads> rdo;
   PackedTile<Tin, kAdjThreads> rt, rp;
   float rgd = 0.f;
@@ -336,14 +114,29 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     const int t0 = tb + c * kChunk, len = min(kChunk, te - t0);
     const size_t ch = (size_t)(cbase + c) * H + h;
     const size_t tok = (size_t)t0 * H + h;
-    rk.load(k + tok * DK, (size_t)H * DK, len, tid);
-    rq.load(q + tok * DK, (size_t)H * DK, len, tid);
+    if constexpr (DIAG) {  // the decayed tiles: all 64 rows, zero past a ragged end
+      const size_t t64 = ch * kChunk * DK;
+      rk.load(static_cast<const Tin *>(dg.kd) + t64, DK, kChunk, tid);
+      rq.load(static_cast<const Tin *>(dg.qg) + t64, DK, kChunk, tid);
+    } else {
+      rk.load(k + tok * DK, (size_t)H * DK, len, tid);
+      rq.load(q + tok * DK, (size_t)H * DK, len, tid);
+    }
     rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
     rt.load(Tm + ch * kTpbElems, tid);
     rp.load(Pm + ch * kTpbElems, tid);
     if (tid < 3 * kChunk) rgd = GD[ch * kGDFloats + tid];  // gam, dec, gamO
+    else if (DIAG && tid < 3 * kChunk + DK) rgd = dg.gc[ch * DK + tid - 3 * kChunk];
   };
-  if (nchunks > 0) issue(nchunks - 1);
+  auto issue_kg = [&](int c) {
+    if constexpr (DIAG)
+      rkg.load(static_cast<const Tin *>(dg.kg) + ((size_t)(cbase + c) * H + h) * kChunk * DK, DK,
+               kChunk, tid);
+  };
+  if (nchunks > 0) {
+    issue(nchunks - 1);
+    issue_kg(nchunks - 1);
+  }
   for (int c = nchunks - 1; c >= 0; --c) {
     const int t0 = tb + c * kChunk, len = min(kChunk, te - t0);
     const size_t ch = (size_t)(cbase + c) * H + h;
@@ -356,6 +149,7 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     if (tid < kChunk) sm.gam[tid] = rgd;
     else if (tid < 2 * kChunk) sm.dec[tid - kChunk] = rgd;
     else if (tid < 3 * kChunk) sm.gamO[tid - 2 * kChunk] = rgd;
+    else if (DIAG && tid < 3 * kChunk + DK) sm.gC[tid - 3 * kChunk] = rgd;
     __syncthreads();
     if (c > 0) issue(c - 1);
 
@@ -386,6 +180,11 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
       }
     }
     __syncthreads();
+    // DIAG: the key tile's readers (the dU products) are done: Kg takes its place for dS
+    if constexpr (DIAG) {
+      rkg.template store<DK + 4>(&sm.K[0][0], tid);
+      if (c > 0) issue_kg(c - 1);
+    }
     // dR = T^T dU
 #pragma unroll
     for (int x = 0; x < NU; ++x) {
@@ -414,7 +213,8 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
       }
     }
     // dS = exp(G_last) dS' + Q^T Diag(gamO) dO - K^T Diag(gam) dR: (DK / 16) x 2 tiles
-    //      (gamO = gam, over ||q_i|| under the normalised readout)
+    //      (gamO = gam, over ||q_i|| under the normalised readout; DIAG: exp(G_last) per key
+    //      channel, Qg and Kg in the tiles)
     const float gl = sm.gam[kChunk - 1];  // rows past a ragged end repeat G_last
     constexpr int NX = DK / 8 / NW;       // tiles per wavefront
     f32x4 nd[NX];
@@ -428,7 +228,10 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
           acc, lane, [&](int i, int kk) { return -sm.K[kk][16 * mi + i]; },
           [&](int kk, int j) { return sm.gam[kk] * sm.dR[kk][16 * tj + j]; });
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += gl * sm.dS[16 * mi + 4 * kq + e][16 * tj + r16];
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * mi + 4 * kq + e;
+        acc[e] += (DIAG ? sm.gC[row] : gl) * sm.dS[row][16 * tj + r16];
+      }
       nd[x] = acc;
     }
     __syncthreads();  // every read of this chunk's tiles and of dS' is done
@@ -465,48 +268,21 @@ struct AdjSmem16 {
   __bf16 dST[kAdjBV][LK];                    // dS'^T
   __bf16 dUT[kAdjBV][LC], dRgT[kAdjBV][LC];  // dU^T, (Diag(gam) dR)^T
   float gam[kChunk], dec[kChunk];
+  float gC[DK];  // diagonal gating: exp(G_last) per key channel
 };
-
-// gfx950 ds_read_b64_tr_b16: within each group of 16 lanes, lane d receives element d & 3 of
-// the 8-byte pieces addressed by lanes (d >> 2) + 4 i, i = 0..3.
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-__device__ __forceinline__ bf16x4 tr_read(const __bf16 *p) {
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(p)));
-}
-// Rows k .. k + 7 of column c0 + (lane & 15) of a row-major bf16 tile with row stride LD:
-// lane s of each 16-lane group addresses row k + (s >> 2) (+ 4), columns c0 + 4 (s & 3) .. + 3.
-template <int LD>
-__device__ __forceinline__ bf16x8 col8(const __bf16 *M, int c0, int k, int lane) {
-  const int s = lane & 15;
-  const __bf16 *p = M + (k + (s >> 2)) * LD + c0 + 4 * (s & 3);
-  const bf16x4 lo = tr_read(p), hi = tr_read(p + 4 * LD);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-// Row c0 + (lane & 15), elements k .. k + 7, of a row-major bf16 tile.
-template <int LD>
-__device__ __forceinline__ bf16x8 row8(const __bf16 *M, int c0, int k, int lane) {
-  return *reinterpret_cast<const bf16x8 *>(M + (c0 + (lane & 15)) * LD + k);
-}
-// acc += the 16 x 16 product with operand fragments fa(k), fb(k) for k = k0 + 8 kq.
-template <int KD, typename FA, typename FB>
-__device__ __forceinline__ f32x4 mmf(f32x4 acc, int lane, FA fa, FB fb) {
-  const int kq = lane >> 4;
-#pragma unroll
-  for (int k0 = 0; k0 < KD; k0 += 32)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa(k0 + 8 * kq), fb(k0 + 8 * kq), acc, 0, 0, 0);
-  return acc;
-}
 
 }  // namespace
 
-template <int DK>
+// DIAG as for kla_bwd_scan_kernel: Kd in the key tile for dU, then Kg; Qg in the query tile;
+// exp(G_last) per key channel.
+template <int DK, bool DIAG>
 __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ dO,
     const float *__restrict__ GD, const __bf16 *__restrict__ Tm, const __bf16 *__restrict__ Pm,
     const float *__restrict__ dST, float *__restrict__ dS0, __bf16 *__restrict__ dSo,
     __bf16 *__restrict__ dUo, __bf16 *__restrict__ dRo, __bf16 *__restrict__ dv,
-    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV) {
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV,
+    DiagTiles dg) {
   using SM = AdjSmem16<DK>;
   constexpr int LK = SM::LK, LC = SM::LC, LV = SM::LV;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -548,23 +324,41 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
   // a chunk's inputs are loaded into registers while the chunk before it (in this reverse
   // order) is computed, and staged when its turn comes
   RegTile<__bf16, kChunk, DK, kAdjThreads> rk, rq;
+  RegTile<__bf16, DIAG ? kChunk : 4, DIAG ? DK : 4, kAdjThreads> rkg;  // Kg (DIAG)
   RegTile<__bf16, kChunk, kAdjBV, kAdjThreads> rdo;
   PackedTile<__bf16, kAdjThreads> rt, rp;
   static_assert(RegTile<__bf16, kChunk, kAdjBV, kAdjThreads>::J == 1, "one dO quad per thread");
-  float rgo = 0.f, rgd = 0.f;  // gamO of this thread's dO row; gam or dec of token tid
+  // gamO of this thread's dO row; gam or dec of token tid (DIAG: exp(G_last) of channel
+  // tid - 128 for the next DK threads)
+  float rgo = 0.f, rgd = 0.f;
   auto issue = [&](int c) {
     const int t0 = tb + c * kChunk, len = min(kChunk, te - t0);
     const size_t ch = (size_t)(cbase + c) * H + h;
     const size_t tok = (size_t)t0 * H + h;
-    rk.load(k + tok * DK, (size_t)H * DK, len, tid);
-    rq.load(q + tok * DK, (size_t)H * DK, len, tid);
+    if constexpr (DIAG) {  // the decayed tiles: all 64 rows, zero past a ragged end
+      const size_t t64 = ch * kChunk * DK;
+      rk.load(static_cast<const __bf16 *>(dg.kd) + t64, DK, kChunk, tid);
+      rq.load(static_cast<const __bf16 *>(dg.qg) + t64, DK, kChunk, tid);
+    } else {
+      rk.load(k + tok * DK, (size_t)H * DK, len, tid);
+      rq.load(q + tok * DK, (size_t)H * DK, len, tid);
+    }
     rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
     rt.load(Tm + ch * kTpbElems, tid);
     rp.load(Pm + ch * kTpbElems, tid);
     rgo = GD[ch * kGDFloats + 2 * kChunk + tid / (kAdjBV / 4)];
     if (tid < 2 * kChunk) rgd = GD[ch * kGDFloats + tid];  // gam, dec
+    else if (DIAG && tid < 2 * kChunk + DK) rgd = dg.gc[ch * DK + tid - 2 * kChunk];
   };
-  if (nchunks > 0) issue(nchunks - 1);
+  auto issue_kg = [&](int c) {
+    if constexpr (DIAG)
+      rkg.load(static_cast<const __bf16 *>(dg.kg) + ((size_t)(cbase + c) * H + h) * kChunk * DK,
+               DK, kChunk, tid);
+  };
+  if (nchunks > 0) {
+    issue(nchunks - 1);
+    issue_kg(nchunks - 1);
+  }
   for (int c = nchunks - 1; c >= 0; --c) {
     const int t0 = tb + c * kChunk, len = min(kChunk, te - t0);
     const size_t ch = (size_t)(cbase + c) * H + h;
@@ -595,6 +389,7 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
     }
     if (tid < kChunk) sm.gam[tid] = rgd;
     else if (tid < 2 * kChunk) sm.dec[tid - kChunk] = rgd;
+    else if (DIAG && tid < 2 * kChunk + DK) sm.gC[tid - 2 * kChunk] = rgd;
     // dS' (the state in registers) as dS'^T for K dS', and to the workspace for the gradients
     // (bf16, the slice's d_k x 32 block contiguous)
     {
@@ -634,6 +429,11 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
       *reinterpret_cast<bf16x4 *>(&sm.dUT[16 * tj + r16][16 * ti + 4 * kq]) = b4;
     }
     __syncthreads();
+    // DIAG: the key tile's readers (the dU products) are done: Kg takes its place for dS
+    if constexpr (DIAG) {
+      rkg.template store<LK>(&sm.K[0][0], tid);
+      if (c > 0) issue_kg(c - 1);
+    }
     // ---- dR = T^T dU (the same tile); dV = dR on the chunk's tokens
     {
       const f32x4 rr = mmf<kChunk>(
@@ -653,12 +453,14 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
     }
     __syncthreads();
     // ---- dS = exp(G_last) dS' + Q^T Diag(gamO) dO - K^T Diag(gam) dR, on this wavefront's
-    //      tiles (gamO = gam, over ||q_i|| under the normalised readout)
+    //      tiles (gamO = gam, over ||q_i|| under the normalised readout; DIAG: exp(G_last)
+    //      per key channel, Qg and Kg in the tiles)
     const float gl = sm.gam[kChunk - 1];  // rows past a ragged end repeat G_last
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
       const int t = wid + NW * x, mi = t >> 1, sj = t & 1;
       f32x4 acc = dS[x] * gl;
+      if constexpr (DIAG) acc = dS[x] * *reinterpret_cast<const f32x4 *>(&sm.gC[16 * mi + 4 * kq]);
       acc = mmf<kChunk>(
           acc, lane, [&](int kk) { return col8<LK>(&sm.Q[0][0], 16 * mi, kk, lane); },
           [&](int kk) { return col8<LV>(&sm.dOg[0][0], 16 * sj, kk, lane); });
@@ -684,8 +486,6 @@ namespace {
 // LT: the element type of the d_v-loop tiles: the operand type of the inputs.  Every read of
 // them feeds a product in that precision, so bf16 storage loses nothing and halves the LDS
 // traffic of those products.
-// Row stride of the d_v-loop tiles, whole 16-byte units: 32 columns (40 bf16 or 36 fp32).
-template <typename LT> constexpr int ldl() { return sizeof(LT) == 2 ? 40 : 36; }
 
 template <typename LT, int DK>
 struct GradSmem {
@@ -1285,6 +1085,53 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   }
 }
 
+template <typename Tin, int DK, bool DIAG>
+static hipError_t launch_adjoint_t(int d_v, const void *q, const void *k, const void *dO,
+                                   const float *GD, const void *T, const void *P,
+                                   const float *dST, void *dSo, void *dU, void *dR, void *dv,
+                                   float *dS0, SeqTables t, int32_t n_seq, int32_t H,
+                                   const DiagTiles &dg, hipStream_t stream) {
+  const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
+  const int64_t scan_blocks = (int64_t)n_seq * H * (d_v / kAdjBV);
+  if (scan_blocks <= 0) return hipSuccess;
+  if constexpr (sizeof(Tin) == 2) {
+    const size_t sm16 = sizeof(AdjSmem16<DK>);
+    static_assert(sizeof(AdjSmem16<DK>) <= 160 * 1024, "LDS budget");
+    static bool attr16 = false;  // benign race: every thread sets the same value
+    if (!attr16) {
+      hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void *>(&kla_bwd_scan16_kernel<DK, DIAG>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm16);
+      if (e != hipSuccess) return e;
+      attr16 = true;
+    }
+    hipLaunchKernelGGL((kla_bwd_scan16_kernel<DK, DIAG>), dim3((unsigned)scan_blocks),
+                       dim3(kAdjThreads), sm16, stream, qt, kt, static_cast<const Tin *>(dO), GD,
+                       static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
+                       static_cast<__bf16 *>(dSo), static_cast<__bf16 *>(dU),
+                       static_cast<__bf16 *>(dR), static_cast<Tin *>(dv), t.cu, t.chunk_off, H,
+                       d_v, dg);
+  } else {
+    const size_t smA = sizeof(AdjSmem<DK>);
+    static_assert(sizeof(AdjSmem<DK>) <= 160 * 1024, "LDS budget");
+    static bool attr = false;  // benign race: every thread sets the same value
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void *>(&kla_bwd_scan_kernel<Tin, DK, DIAG>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smA);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    hipLaunchKernelGGL((kla_bwd_scan_kernel<Tin, DK, DIAG>), dim3((unsigned)scan_blocks),
+                       dim3(kAdjThreads), smA, stream, qt, kt, static_cast<const Tin *>(dO), GD,
+                       static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
+                       static_cast<float *>(dSo), static_cast<float *>(dU),
+                       static_cast<float *>(dR), static_cast<Tin *>(dv), t.cu, t.chunk_off, H,
+                       d_v, dg);
+  }
+  return hipGetLastError();
+}
+
 template <typename Tin, int DK>
 static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void *v,
                                const void *dO, const float *g, const float *eta, float eps,
@@ -1293,48 +1140,29 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
                                const void *SN, void *dSo, void *dU, void *dR, void *dq,
                                void *dk, void *dv, float *dg, float *deta, float *dS0,
                                SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
-                               hipStream_t stream) {
-  const size_t smA = sizeof(AdjSmem<DK>), smG = sizeof(GradSmem<Tin, DK>);
-  static_assert(sizeof(AdjSmem<DK>) <= 160 * 1024 && sizeof(GradSmem<Tin, DK>) <= 160 * 1024,
-                "LDS budget");
-  static bool attr_set = false;  // benign race: every thread sets the same values
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_bwd_scan_kernel<Tin, DK>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smA);
+                               hipStream_t stream, const DiagTiles *diag, const float *A) {
+  hipError_t e;
+  if (diag) {
+    e = launch_adjoint_t<Tin, DK, true>(d_v, q, k, dO, GD, T, P, dST, dSo, dU, dR, dv, dS0, t,
+                                        n_seq, H, *diag, stream);
     if (e != hipSuccess) return e;
+    return launch_bwd_grad_diag(sizeof(Tin) == 2 ? Dtype::BF16 : Dtype::F32, DK, d_v, q, k, v,
+                                dO, g, eta, eps, opts, diag->kg, X, A, SN, dSo, dU, dR, dq, dk,
+                                dg, deta, t, n_seq, n_chunks_ub, H, stream);
+  }
+  e = launch_adjoint_t<Tin, DK, false>(d_v, q, k, dO, GD, T, P, dST, dSo, dU, dR, dv, dS0, t,
+                                       n_seq, H, DiagTiles{}, stream);
+  if (e != hipSuccess) return e;
+  const size_t smG = sizeof(GradSmem<Tin, DK>);
+  static_assert(sizeof(GradSmem<Tin, DK>) <= 160 * 1024, "LDS budget");
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_bwd_grad_kernel<Tin, DK>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smG);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
-  const int64_t scan_blocks = (int64_t)n_seq * H * (d_v / kAdjBV);
-  if (scan_blocks > 0) {
-    if constexpr (sizeof(Tin) == 2) {
-      const size_t sm16 = sizeof(AdjSmem16<DK>);
-      static bool attr16 = false;  // benign race: every thread sets the same value
-      if (!attr16) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&kla_bwd_scan16_kernel<DK>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm16);
-        if (e != hipSuccess) return e;
-        attr16 = true;
-      }
-      hipLaunchKernelGGL((kla_bwd_scan16_kernel<DK>), dim3((unsigned)scan_blocks),
-                         dim3(kAdjThreads), sm16, stream, qt, kt, static_cast<const Tin *>(dO),
-                         GD, static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
-                         static_cast<__bf16 *>(dSo), static_cast<__bf16 *>(dU),
-                         static_cast<__bf16 *>(dR), static_cast<Tin *>(dv), t.cu, t.chunk_off, H,
-                         d_v);
-    } else {
-      hipLaunchKernelGGL((kla_bwd_scan_kernel<Tin, DK>), dim3((unsigned)scan_blocks),
-                         dim3(kAdjThreads), smA, stream, qt, kt, static_cast<const Tin *>(dO), GD,
-                         static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
-                         static_cast<float *>(dSo), static_cast<float *>(dU),
-                         static_cast<float *>(dR), static_cast<Tin *>(dv), t.cu, t.chunk_off, H,
-                         d_v);
-    }
-  }
   const int64_t grad_blocks = n_chunks_ub * H;
   if (grad_blocks > 0)
     hipLaunchKernelGGL((kla_bwd_grad_kernel<Tin, DK>), dim3((unsigned)grad_blocks),
@@ -1353,10 +1181,10 @@ hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, 
                       const float *X, const float *dST, const void *SN, void *dSo, void *dU,
                       void *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
                       SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
-                      hipStream_t stream) {
+                      hipStream_t stream, const DiagTiles *diag, const float *A) {
 #define KLA_BWD(TIN, DK_)                                                                     \
   return launch_bwd_t<TIN, DK_>(d_v, q, k, v, dO, g, eta, eps, opts, GD, T, P, X, dST, SN, dSo, dU, dR, \
-                                dq, dk, dv, dg, deta, dS0, t, n_seq, n_chunks_ub, H, stream);
+                                dq, dk, dv, dg, deta, dS0, t, n_seq, n_chunks_ub, H, stream, diag, A);
   if (dt == Dtype::BF16) {
     if (d_k == 128) { KLA_BWD(__bf16, 128) }
     KLA_BWD(__bf16, 64)

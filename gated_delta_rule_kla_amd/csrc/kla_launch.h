@@ -69,10 +69,13 @@ struct DiagTiles {
 
 // a1 + a2 under diagonal gating (g [n_tok, H, d_k]): b, T and P (packed blocks), unit decays
 // with the readout factor in GD, and the decayed tiles.  Reads the tables launch_plan wrote.
+// For the backward pass, X_out and A_out (non-null) also receive X = (I + Diag(b) A)^{-1} and
+// A itself per chunk-head, fp32, as ten packed 16 x 16 blocks like T.
 hipError_t launch_prep_diag(Dtype dt, int d_k, const void *q, const void *k, const float *g,
                             const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                             int32_t n_seq, int64_t n_chunks_ub, int32_t H, const DiagTiles &tiles,
-                            void *T_out, void *P_out, float *GD_out, hipStream_t stream);
+                            void *T_out, void *P_out, float *GD_out, hipStream_t stream,
+                            float *X_out = nullptr, float *A_out = nullptr);
 
 // Optional WY factors W = T Diag(exp G) K and U~ = T V (unit-check path).
 hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, const float *G,
@@ -82,7 +85,7 @@ hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, c
 // a3 + a4: sequential chunk scan with the output fused in; reads T, P and the per-chunk
 // decays GD that launch_prep wrote.  With diag (non-null), the diagonal-gated scan: K and Q
 // come from the decayed tiles, the state update uses K o exp(G_last - G) and the state decays
-// by exp(G_last) per key channel.  With SN (non-null; scalar gate only), every chunk's
+// by exp(G_last) per key channel.  With SN (non-null), every chunk's
 // incoming state, [chunk][H][d_k][d_v] in the operand type by global chunk number, for the
 // backward pass, and no outputs (q, P and o are not read or written and may be null).
 hipError_t launch_scan(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
@@ -131,13 +134,16 @@ hipError_t launch_scan_two_level(Dtype dt, int d_k, int d_v, const void *q, cons
 // operand type into dSo, dU and dR: fp32 row-major, or bf16 with each 32-column slice's block
 // contiguous; dv, and dS0 if non-null), then the per-chunk gradients dq, dk (operand type) and
 // dg, deta (fp32).  dST may be null (a zero cotangent of the final state).
+// Diagonal gating (diag non-null): after launch_prep_diag with X_out = X and A_out = A and
+// launch_scan with diag and SN; g and dg are [n_tok, H, d_k].
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
                       const CoefOpts &opts, const float *GD, const void *T, const void *P,
                       const float *X, const float *dST, const void *SN, void *dSo, void *dU,
                       void *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
                       SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
-                      hipStream_t stream);
+                      hipStream_t stream, const DiagTiles *diag = nullptr,
+                      const float *A = nullptr);
 
 // a5: one decode step.
 hipError_t launch_decode(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,

@@ -796,7 +796,9 @@ static hipError_t launch_scan_g(int d_v, const void *q, const void *k, const voi
                                 void *o, float *S_T, SeqTables t, int32_t n_seq, int32_t H,
                                 hipStream_t stream, const DiagTiles *dg, void *SN) {
   if (dg) {
-    if (SN) return hipErrorInvalidValue;  // no stored states under diagonal gating
+    if (SN)
+      return launch_scan_t<Tin, DK, true, true>(d_v, n_seq, q, k, v, GD, T, P, S0, o, S_T, t, H,
+                                                stream, dg, SN);
     return launch_scan_t<Tin, DK, true, false>(d_v, n_seq, q, k, v, GD, T, P, S0, o, S_T, t, H,
                                                stream, dg, nullptr);
   }

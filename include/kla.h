@@ -346,10 +346,17 @@ kla_status kla_prefill_backward(const void *q, const void *k, const void *v, con
                                 void *stream);
 
 /* kla_prefill_backward with options (NULL = the defaults): the coefficient
- * modes (beta_mode, pos_offset) and the normalised readout (normalize_q; the
- * gradient of a zero query is 0) are supported; diagonal_gate gives
- * KLA_ERR_UNSUPPORTED.  The forward arguments and options must be those of the
- * forward call whose gradients are wanted. */
+ * modes (beta_mode, pos_offset), the normalised readout (normalize_q; the
+ * gradient of a zero query is 0) and diagonal gating (diagonal_gate, paper
+ * Appendix B.5: g and dg are then [total_tokens, n_heads, d_k] fp32, the
+ * workspace is kla_prefill_backward_workspace_bytes_ex with the same options,
+ * and it also holds the decayed key and query tiles of the forward stage and
+ * every chunk's A = (K K^T per channel, decayed) in fp32).  precision other
+ * than KLA_PRECISION_BF16 gives KLA_ERR_UNSUPPORTED.  The forward arguments and
+ * options must be those of the forward call whose gradients are wanted. */
+size_t kla_prefill_backward_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens,
+                                               int32_t n_heads, int32_t d_k, int32_t d_v,
+                                               kla_dtype dtype, const kla_options *opts);
 kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, const float *g,
                                    const float *eta, float eps, const float *S0, const void *dO,
                                    const float *dS_T, void *dq, void *dk, void *dv, float *dg,

@@ -331,21 +331,40 @@ def test_backward_workspace_and_errors(lib):
         assert _bwd_call(lib, **over) == want, (over, lib.kla_last_error())
 
 
-def test_backward_ex_rejects_the_diagonal_gate(lib):
-    for opts in (kla.KlaOptions(0, 0, None, 1), kla.KlaOptions(0, 1, None, 1)):
-        st = lib.kla_prefill_backward_ex(
-            FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1e-6, None, FAKE * 6, None, FAKE * 7,
-            FAKE * 8, FAKE * 9, FAKE * 10, FAKE * 11, FAKE * 12, None, None, 2, 256, 4, 128, 128,
-            BF16, FAKE * 64, lib.kla_prefill_backward_workspace_bytes(2, 256, 4, 128, 128, BF16),
-            ctypes.pointer(opts), None)
-        assert st == UNSUPPORTED
-    bad = kla.KlaOptions(9, 0, None, 0)  # unknown coefficient mode
-    st = lib.kla_prefill_backward_ex(
+def _bwd_ex_call(lib, opts, ws_bytes, **over):
+    a = dict(n_seq=2, n_tok=256, H=4, dk_=128, dv_=128, dg=FAKE * 10)
+    a.update(over)
+    return lib.kla_prefill_backward_ex(
         FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, 1e-6, None, FAKE * 6, None, FAKE * 7,
-        FAKE * 8, FAKE * 9, FAKE * 10, FAKE * 11, FAKE * 12, None, None, 2, 256, 4, 128, 128,
-        BF16, FAKE * 64, lib.kla_prefill_backward_workspace_bytes(2, 256, 4, 128, 128, BF16),
-        ctypes.pointer(bad), None)
-    assert st == UNSUPPORTED
+        FAKE * 8, FAKE * 9, a["dg"], FAKE * 11, FAKE * 12, None, None, a["n_seq"], a["n_tok"],
+        a["H"], a["dk_"], a["dv_"], BF16, FAKE * 64, ws_bytes,
+        None if opts is None else ctypes.pointer(opts), None)
+
+
+def test_backward_diagonal_gate_workspace_and_errors(lib):
+    # Appendix B.5 (diagonal gating): the backward workspace adds the forward's decayed tiles
+    # K o exp(G), Q o exp(G), K o exp(G_last - G) ([64][d_k] per chunk-head, operand type) and
+    # exp(G_last) ([d_k] fp32), and every chunk's A (ten 16 x 16 fp32 blocks)
+    n_seq, n_tok, H, dk, dv = 2, 256, 4, 128, 128
+    nch = (n_tok + 63) // 64 + n_seq
+    diag = kla.KlaOptions(0, 0, None, 1)
+    nb = lib.kla_prefill_backward_workspace_bytes(n_seq, n_tok, H, dk, dv, BF16)
+    assert lib.kla_prefill_backward_workspace_bytes_ex(n_seq, n_tok, H, dk, dv, BF16, None) == nb
+    nd = lib.kla_prefill_backward_workspace_bytes_ex(n_seq, n_tok, H, dk, dv, BF16,
+                                                     ctypes.pointer(diag))
+    assert nd >= nb + nch * H * (3 * 64 * dk * 2 + 4 * dk + 4 * 10 * 256)
+    assert nd % 256 == 0
+    assert lib.kla_prefill_backward_workspace_bytes_ex(n_seq, n_tok, H, 96, dv, BF16,
+                                                       ctypes.pointer(diag)) == 0
+    # the scalar-gate workspace is too small for the diagonal gate
+    assert _bwd_ex_call(lib, diag, nb) == WORKSPACE
+    # dg is [n_tok, H, d_k] fp32 under diagonal gating: 512 KiB here, so a dg starting 256 KiB
+    # below eta overlaps it (a scalar gate's 4 KiB dg would not)
+    assert _bwd_ex_call(lib, diag, nd, dg=FAKE * 5 - (256 << 10)) == INVALID
+    assert "overlap" in lib.kla_last_error().decode()
+    # unknown coefficient mode, and a precision the backward does not take
+    assert _bwd_ex_call(lib, kla.KlaOptions(9, 0, None, 0), nb) == UNSUPPORTED
+    assert _bwd_ex_call(lib, kla.KlaOptions(0, 0, None, 1, 0, 1), nd) == UNSUPPORTED
 
 
 def test_noalloc_rejects_a_problem_beyond_its_static_scratch(lib):
