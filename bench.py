@@ -371,7 +371,40 @@ def main():
                             "storing every chunk's state, the adjoint scan and the per-chunk "
                             "gradients"}
         log(f"backward: {bwd_ms:.3f} ms/step")
-        del wsb, ct
+        del wsb
+        # the same under diagonal gating (g per key channel, Appendix B.5), its own workspace
+        gen = torch.Generator(device=dev).manual_seed(ki.BASE_SEED + 78)
+        gd = (w.g_low * torch.rand(*s0["k"].shape, generator=gen, device=dev)).contiguous()
+        wsbd = torch.empty(kla.kla_prefill_backward_workspace_bytes(
+            n_seq, n_tok, H, dk, dv, s0["q"].dtype, diagonal_gate=True),
+            dtype=torch.uint8, device=dev)
+
+        def bdstep():
+            return kla.kla_prefill_backward(s0["q"], s0["k"], s0["v"], gd, s0["eta"],
+                                            base["eps"], ct["dO"], S0=s0["S0"],
+                                            dS_T=ct["dS_T"], n_seq=n_seq, workspace=wsbd)
+        for _ in range(2):
+            bdstep()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.backward_steps):
+            bdstep()
+        e1.record()
+        torch.cuda.synchronize()
+        bwdd_ms = e0.elapsed_time(e1) / args.backward_steps
+        # g read and dg written per key channel (fp32) instead of per token-head
+        bwdd_bytes = (n_tok * H * (es * (4 * dk + 3 * dv) + 8 * dk + 8)
+                      + 3 * n_seq * H * dk * dv * 4)
+        bwdd_gbs = bwdd_bytes / (bwdd_ms * 1e-3) / 1e9
+        backward["diagonal_gate"] = {
+            "ms_per_step": bwdd_ms, "tokens_per_s": n_tok / (bwdd_ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": bwdd_gbs, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": bwdd_gbs / PEAK_HBM_GBS,
+                         "algorithmic_bytes_per_step": bwdd_bytes},
+            "workspace_bytes": wsbd.numel(),
+            "note": "g per key channel [n_tok, H, d_k] ~ U(g_low, 0); dg of that shape"}
+        log(f"backward (diagonal gate): {bwdd_ms:.3f} ms/step")
+        del wsbd, ct, gd
     del sets
 
     # ---------------------------------------------------------------- decode

@@ -54,12 +54,12 @@ struct GradDiagSmem {
     } lp;
     struct {  // after it
       LT Q[kChunk][LK];          // query rows (not normalised)
-      float G[kChunk][LGG];      // G in log2 units, per channel
+      float GT[DK][kChunk + 4];  // G^T: per channel, G in log2 units down the rows
       // dP^ and dT (then W = dT Diag(b) X^T, then dA), adjacent: after the products they
       // hold dG ([64][LGG])
       float dP[kChunk][LDC], dT[kChunk][LDC];
       __bf16 dPb[TR ? kChunk : 1][TR ? LG : 8], dAb[TR ? kChunk : 1][TR ? LG : 8];
-      float tot[NPART][DK];      // per-part totals of the G prefix
+      float tot[NPART][DK];      // per-part totals of the G prefix, then of the dg suffix
     } pa;
   } u;
   float b[kChunk], den[kChunk], db[kChunk], db_deta[kChunk], rqn[kChunk];
@@ -110,9 +110,12 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
 
-  // ---- X (packed fp32 blocks), the key rows (kept in registers for after the d_v loop,
-  //      their squared norms now), Kg for the loop; b and its derivative in eta
+  // ---- X (packed fp32 blocks), the key rows (their squared norms now; kept in registers
+  //      for after the d_v loop), Kg for the loop, eta, and the first d_v block: all issued
+  //      before any is waited for
   constexpr int kXPieces = kTpbElems / 4;
+  constexpr int NM = DK / 32;  // 64 x DK tiles per wavefront: rows 16 (wid & 3), columns 16 tj
+  const int mti = wid & 3;
   float eta_l = 0.f;
   if (wid == 0 && lane < len) eta_l = eta[tok + (size_t)lane * H];
   f32x4 xr[2];
@@ -121,9 +124,52 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
     const int e = tid + kGradThreads * x;
     if (e < kXPieces) xr[x] = *reinterpret_cast<const f32x4 *>(Xp + ch * kTpbElems + 4 * e);
   }
-  RegTile<Tin, kChunk, DK, kGradThreads> rkr, rkg;
+  RegTile<Tin, kChunk, DK, kGradThreads> rkr, rkg, rq;
   rkr.load(k + tok * DK, (size_t)H * DK, len, tid);
   rkg.load(KG + ch * kChunk * DK, DK, kChunk, tid);
+  const Tin *Sb = SN + ch * DK * (size_t)DV;
+  const Tin *Sob = dSo + ch * DK * (size_t)DV;
+  const Tin *dUb = dUo + ch * kChunk * (size_t)DV, *dRb = dRo + ch * kChunk * (size_t)DV;
+  // dS', dU and dR as the adjoint scan left them: bf16, each 32-column slice's block
+  // contiguous; fp32, row-major over all d_v columns
+  constexpr bool SLM = sizeof(Tin) == 2;
+  RegTile<Tin, DK, kAdjBV, kGradThreads> rs, rso;
+  RegTile<Tin, kChunk, kAdjBV, kGradThreads> rv, rdo, rdu, rdr;
+  auto issue = [&](int v0) {
+    rs.load(Sb + v0, (size_t)DV, DK, tid);
+    rv.load(v + tok * DV + v0, (size_t)H * DV, len, tid);
+    rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
+    if constexpr (SLM) {
+      rso.load(Sob + (size_t)v0 * DK, kAdjBV, DK, tid);
+      rdu.load(dUb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
+      rdr.load(dRb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
+    } else {
+      rso.load(Sob + v0, (size_t)DV, DK, tid);
+      rdu.load(dUb + v0, (size_t)DV, kChunk, tid);
+      rdr.load(dRb + v0, (size_t)DV, kChunk, tid);
+    }
+  };
+  issue(0);
+  // what the work after the d_v loop reads, loaded while its last block is computed: the query
+  // rows, g at this thread's channel gc and rows gp RPP .., and A at this lane's entries of the
+  // dL tiles
+  const int gc = tid % DK, gp = tid / DK;
+  float Gr[RPP], ar[2][4];
+  // (every load unconditional, from a clamped in-range address, and masked afterwards: a load
+  // under a branch is waited for inside it)
+  auto issue_tail = [&]() {
+    rq.load(q + tok * DK, (size_t)H * DK, len, tid);
+#pragma unroll
+    for (int r = 0; r < RPP; ++r)
+      Gr[r] = g[(tok + (size_t)min(gp * RPP + r, len - 1) * H) * DK + gc];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int t = wid + 8 * x, I = t >> 2, J = min(t & 3, I);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ar[x][e] = Ap[ch * kTpbElems + (I * (I + 1) / 2 + J) * 256 + (4 * kq + e) * 16 + r16];
+    }
+  };
   rkr.sqnorms(sm.den, tid);
   rkg.template store<LK>(&sm.K[0][0], tid);
 #pragma unroll
@@ -160,41 +206,16 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
   // ---- the contractions over d_v, 32 columns at a time: Y = Kg S -> R = V - Y, U = T R;
   //      qa = dO S^T, ka = dR S^T, kb = U dS'^T (64 x DK), dP^ = dO U^T and dT = dU R^T (their
   //      lower blocks), and <S, dS'> per channel
-  constexpr int NM = DK / 32;  // 64 x DK tiles per wavefront: rows 16 (wid & 3), columns 16 tj
-  const int mti = wid & 3;
   f32x4 qa[NM], ka[NM], kb[NM], pt[3];
 #pragma unroll
   for (int m = 0; m < NM; ++m) qa[m] = ka[m] = kb[m] = zero4();
 #pragma unroll
   for (int x = 0; x < 3; ++x) pt[x] = zero4();
-  const Tin *Sb = SN + ch * DK * (size_t)DV;
-  const Tin *Sob = dSo + ch * DK * (size_t)DV;
-  const Tin *dUb = dUo + ch * kChunk * (size_t)DV, *dRb = dRo + ch * kChunk * (size_t)DV;
-  // dS', dU and dR as the adjoint scan left them: bf16, each 32-column slice's block
-  // contiguous; fp32, row-major over all d_v columns
-  constexpr bool SLM = sizeof(Tin) == 2;
-  RegTile<Tin, DK, kAdjBV, kGradThreads> rs, rso;
-  RegTile<Tin, kChunk, kAdjBV, kGradThreads> rv, rdo, rdu, rdr;
   constexpr int NSJ = decltype(rs)::J;
   float scp[NSJ];  // this thread's rows of S (piece tid + 512 j, row (tid + 512 j) / 8)
 #pragma unroll
   for (int j = 0; j < NSJ; ++j) scp[j] = 0.f;
-  auto issue = [&](int v0) {
-    rs.load(Sb + v0, (size_t)DV, DK, tid);
-    rv.load(v + tok * DV + v0, (size_t)H * DV, len, tid);
-    rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
-    if constexpr (SLM) {
-      rso.load(Sob + (size_t)v0 * DK, kAdjBV, DK, tid);
-      rdu.load(dUb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
-      rdr.load(dRb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
-    } else {
-      rso.load(Sob + v0, (size_t)DV, DK, tid);
-      rdu.load(dUb + v0, (size_t)DV, kChunk, tid);
-      rdr.load(dRb + v0, (size_t)DV, kChunk, tid);
-    }
-  };
-  issue(0);
-  for (int v0 = 0; v0 < DV; v0 += kAdjBV) {
+  auto block = [&](int v0, bool last) __attribute__((always_inline)) {
     __syncthreads();  // the previous block's reads (and the first stores) are done
     rs.template store<LDL>(&sm.u.lp.S[0][0], tid);
     rso.template store<LDL>(&sm.u.lp.So[0][0], tid);
@@ -208,7 +229,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
     rdu.template store<LDL>(&sm.u.lp.dU[0][0], tid);
     rdr.template store<LDL>(&sm.u.lp.dR[0][0], tid);
     __syncthreads();
-    if (v0 + kAdjBV < DV) issue(v0 + kAdjBV);
+    if (last) issue_tail(); else issue(v0 + kAdjBV);
     const int yi = wid >> 1, yj = wid & 1;  // this wavefront's 16 x 16 tile of R and U
     {
       f32x4 y;
@@ -273,7 +294,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
               [&](int j, int kk) { return &sm.u.lp.R[16 * J + j][kk]; });
       }
     }
-  }
+  };
+  for (int v0 = 0; v0 + kAdjBV < DV; v0 += kAdjBV) block(v0, false);
+  block(DV - kAdjBV, true);  // d_v >= 64: at least two blocks
   // <S, dS'> per channel: the 8 lanes holding a row of S sum their partials
 #pragma unroll
   for (int j = 0; j < NSJ; ++j) {
@@ -285,23 +308,16 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
   }
   __syncthreads();  // the loop's LDS is free
 
-  // ---- the key and query rows; G per channel (log2 units), first within parts of RPP rows;
-  //      dP^ and dT (lower, zeros above; bf16: also dP^ as a bf16 tile)
+  // ---- the key and query rows (and the squared query norms); G per channel (log2 units),
+  //      first within parts of RPP rows; dP^ and dT (lower, zeros above; bf16: also dP^ as a
+  //      bf16 tile)
   rkr.template store<LK>(&sm.K[0][0], tid);
-  stage_rows<DK, LK, kGradThreads>(&sm.u.pa.Q[0][0], q + tok * DK, (size_t)H * DK, len, tid,
-                                   sm.qq);
-  const int gc = tid % DK, gp = tid / DK;  // this thread's channel and part of the G prefix
-  float Gr[RPP];
-  {
+  rq.template store<LK>(&sm.u.pa.Q[0][0], tid);
+  rq.sqnorms(sm.qq, tid);
 #pragma unroll
-    for (int r = 0; r < RPP; ++r) {
-      const int row = gp * RPP + r;
-      Gr[r] = row < len ? g[(tok + (size_t)row * H) * DK + gc] * kLog2e : 0.f;
-    }
-#pragma unroll
-    for (int r = 1; r < RPP; ++r) Gr[r] += Gr[r - 1];
-    sm.u.pa.tot[gp][gc] = Gr[RPP - 1];
-  }
+  for (int r = 0; r < RPP; ++r)
+    Gr[r] = (gp * RPP + r < len ? Gr[r] * kLog2e : 0.f) + (r > 0 ? Gr[r - 1] : 0.f);
+  sm.u.pa.tot[gp][gc] = Gr[RPP - 1];
   for (int e = tid; e < kChunk * kChunk; e += kGradThreads) {
     const int r = e >> 6, cc = e & 63;
     if ((cc >> 4) > (r >> 4)) {
@@ -337,7 +353,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
 #pragma unroll
     for (int r = 0; r < RPP; ++r) {
       Gr[r] += carry;
-      sm.u.pa.G[gp * RPP + r][gc] = Gr[r];
+      sm.u.pa.GT[gc][gp * RPP + r] = Gr[r];
     }
   }
   if (tid < kChunk) {
@@ -362,7 +378,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int t = wid + 8 * x, I = t >> 2, J = t & 3;
-    w[x] = mm_tile<kChunk>(
+    w[x] = mmt<Tin, kChunk>(
         zero4(), lane, [&](int i, int kk) { return sm.u.pa.dT[16 * I + i][kk] * sm.b[kk]; },
         [&](int kk, int j) { return sm.X[16 * J + j][kk]; });
   }
@@ -375,7 +391,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
     for (int e = 0; e < 4; ++e) sm.u.pa.dT[16 * I + 4 * kq + e][16 * J + r16] = w[x][e];
   }
   {
-    const float g32 = sm.u.pa.G[32][gc];
+    const float g32 = sm.u.pa.GT[gc][32];
     float sp = 0.f;
 #pragma unroll
     for (int r = 0; r < RPP; ++r) sp = fmaxf(sp, fabsf(Gr[r] - g32));
@@ -390,19 +406,15 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
     const int t = wid + 8 * x, I = t >> 2, J = t & 3;
     f32x4 acc = zero4();
     if (J <= I)
-      acc = mm_tile<kChunk>(
+      acc = mmt<Tin, kChunk>(
           acc, lane, [&](int i, int kk) { return sm.X[kk][16 * I + i]; },
           [&](int kk, int j) { return sm.u.pa.dT[kk][16 * J + j]; });
     float zr4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * I + 4 * kq + e, col = 16 * J + r16;
-      const bool lower = col < row;
-      const float dl = lower ? -acc[e] : 0.f;
-      const float av =
-          lower ? Ap[ch * kTpbElems + (I * (I + 1) / 2 + J) * 256 + (row & 15) * 16 + (col & 15)]
-                : 0.f;
-      zr4[e] = dl * av;
+      const float dl = col < row ? -acc[e] : 0.f;
+      zr4[e] = col < row ? dl * ar[x][e] : 0.f;  // (ar holds another block's entry above)
       dl4[x][e] = sm.b[row] * dl;  // dA
     }
 #pragma unroll
@@ -426,71 +438,108 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
   if (tid < kChunk) sm.db[tid] += sm.zr[0][tid] + sm.zr[1][tid] + sm.zr[2][tid] + sm.zr[3][tid];
 
   // ---- F1, H1 and Z on this wavefront's tiles (rows 16 mti + 4 kq + e, column 16 tj + r16)
-  const float (*Gt)[LGG] = sm.u.pa.G;
+  constexpr int LGT = kChunk + 4;
+  const float (*GT)[LGT] = sm.u.pa.GT;
   const float (*dAf)[LDC] = sm.u.pa.dT;
   const float (*dPf)[LDC] = sm.u.pa.dP;
+  auto g4 = [&](int c, int r) { return *reinterpret_cast<const f32x4 *>(&GT[c][r]); };
   f32x4 F1[NM], H1[NM], Zc[NM];
+  // the matrix-core form on tile m (all of its 16 channels within 2^64 of row 32); the left
+  // operands (rows of dA and dP^, and their columns for Z) are the same for every tile of the
+  // wavefront and read once
+  [[maybe_unused]] bf16x8 wfa[2], wfp[2], wfat[2], wfpt[2];
+  auto load_w = [&]() {
+    if constexpr (TR) {
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const int tj = (wid >> 2) + 2 * m, col = 16 * tj + r16;
-    F1[m] = H1[m] = Zc[m] = zero4();
-    bool fast = false;
-    if constexpr (TR) fast = __all(__int_as_float(sm.span[col]) <= 64.f);
-    if (fast) {
-      if constexpr (TR) {
-        const float g32 = Gt[32][col];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int kk = 32 * x + 8 * kq;
-          const bf16x8 kc = col8<LK>(&sm.K[0][0], 16 * tj, kk, lane);
-          const bf16x8 qc = col8<LK>(&sm.u.pa.Q[0][0], 16 * tj, kk, lane);
-          bf16x8 kf, ke, qe;
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const int j = kk + s;
-            const float d = g32 - Gt[j][col];
-            const float f = exp2_fast(d), fr = exp2_fast(-d);
-            const float kj = to_f32(kc[s]);
-            kf[s] = from_f32<__bf16>(kj * f);
-            ke[s] = from_f32<__bf16>(kj * fr);
-            qe[s] = from_f32<__bf16>(to_f32(qc[s]) * sm.rqn[j] * fr);
-          }
-          const bf16x8 fa = row8<LG>(&sm.u.pa.dAb[0][0], 16 * mti, kk, lane);
-          const bf16x8 fp = row8<LG>(&sm.u.pa.dPb[0][0], 16 * mti, kk, lane);
-          const bf16x8 fat = col8<LG>(&sm.u.pa.dAb[0][0], 16 * mti, kk, lane);
-          const bf16x8 fpt = col8<LG>(&sm.u.pa.dPb[0][0], 16 * mti, kk, lane);
-          F1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, kf, F1[m], 0, 0, 0);
-          H1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp, kf, H1[m], 0, 0, 0);
-          Zc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fat, ke, Zc[m], 0, 0, 0);
-          Zc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fpt, qe, Zc[m], 0, 0, 0);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float d = Gt[16 * mti + 4 * kq + e][col] - g32;
-          const float ef = exp2_fast(d), fr = exp2_fast(-d);
-          F1[m][e] *= ef;
-          H1[m][e] *= ef;
-          Zc[m][e] *= fr;
-        }
+      for (int x = 0; x < 2; ++x) {
+        const int kk = 32 * x + 8 * kq;
+        wfa[x] = row8<LG>(&sm.u.pa.dAb[0][0], 16 * mti, kk, lane);
+        wfp[x] = row8<LG>(&sm.u.pa.dPb[0][0], 16 * mti, kk, lane);
+        wfat[x] = col8<LG>(&sm.u.pa.dAb[0][0], 16 * mti, kk, lane);
+        wfpt[x] = col8<LG>(&sm.u.pa.dPb[0][0], 16 * mti, kk, lane);
       }
-    } else {
-      // directly: Gamma = exp2(-|G_i - G_j|), the right value on every term whose dA or dP^
-      // entry is not zero (j <= i for F1 and H1, j >= i for Z)
-      float Gi[4];
+    }
+  };
+  auto prod_fast = [&](int m) __attribute__((always_inline)) {
+    if constexpr (TR) {
+      const int tj = (wid >> 2) + 2 * m, col = 16 * tj + r16;
+      const float g32 = GT[col][32];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Gi[e] = Gt[16 * mti + 4 * kq + e][col];
-      for (int j = 0; j < kChunk; ++j) {
-        const float kj = to_f32(sm.K[j][col]);
-        const float qj = to_f32(sm.u.pa.Q[j][col]) * sm.rqn[j];
-        const float Gj = Gt[j][col];
+      for (int x = 0; x < 2; ++x) {
+        const int kk = 32 * x + 8 * kq;
+        const bf16x8 kc = col8<LK>(&sm.K[0][0], 16 * tj, kk, lane);
+        const bf16x8 qc = col8<LK>(&sm.u.pa.Q[0][0], 16 * tj, kk, lane);
+        const f32x4 gj0 = g4(col, kk), gj1 = g4(col, kk + 4);
+        const f32x4 rq0 = *reinterpret_cast<const f32x4 *>(&sm.rqn[kk]);
+        const f32x4 rq1 = *reinterpret_cast<const f32x4 *>(&sm.rqn[kk + 4]);
+        bf16x8 kf, ke, qe;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * mti + 4 * kq + e;
-          const float t = exp2_fast(-fabsf(Gi[e] - Gj));
-          F1[m][e] += dAf[i][j] * kj * t;
-          H1[m][e] += dPf[i][j] * kj * t;
-          Zc[m][e] += t * (dAf[j][i] * kj + dPf[j][i] * qj);
+        for (int s = 0; s < 8; ++s) {
+          const float d = g32 - (s < 4 ? gj0[s] : gj1[s - 4]);
+          const float f = exp2_fast(d), fr = exp2_fast(-d);
+          const float kj = to_f32(kc[s]);
+          kf[s] = from_f32<__bf16>(kj * f);
+          ke[s] = from_f32<__bf16>(kj * fr);
+          qe[s] = from_f32<__bf16>(to_f32(qc[s]) * (s < 4 ? rq0[s] : rq1[s - 4]) * fr);
         }
+        F1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfa[x], kf, F1[m], 0, 0, 0);
+        H1[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfp[x], kf, H1[m], 0, 0, 0);
+        Zc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfat[x], ke, Zc[m], 0, 0, 0);
+        Zc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfpt[x], qe, Zc[m], 0, 0, 0);
+      }
+      const f32x4 gi = g4(col, 16 * mti + 4 * kq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = gi[e] - g32;
+        const float ef = exp2_fast(d), fr = exp2_fast(-d);
+        F1[m][e] *= ef;
+        H1[m][e] *= ef;
+        Zc[m][e] *= fr;
+      }
+    }
+  };
+  // term by term: Gamma = exp2(-|G_i - G_j|), the right value on every term whose dA or dP^
+  // entry is not zero (j <= i for F1 and H1, j >= i for Z)
+  auto prod_direct = [&](int m) {
+    const int tj = (wid >> 2) + 2 * m, col = 16 * tj + r16;
+    const f32x4 gi = g4(col, 16 * mti + 4 * kq);
+    for (int j = 0; j < kChunk; ++j) {
+      const float kj = to_f32(sm.K[j][col]);
+      const float qj = to_f32(sm.u.pa.Q[j][col]) * sm.rqn[j];
+      const float Gj = GT[col][j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * mti + 4 * kq + e;
+        const float t = exp2_fast(-fabsf(gi[e] - Gj));
+        F1[m][e] += dAf[i][j] * kj * t;
+        H1[m][e] += dPf[i][j] * kj * t;
+        Zc[m][e] += t * (dAf[j][i] * kj + dPf[j][i] * qj);
+      }
+    }
+  };
+  bool all_fast = false;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) F1[m] = H1[m] = Zc[m] = zero4();
+  if constexpr (TR) {
+    bool f = true;
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      f = f && __int_as_float(sm.span[16 * ((wid >> 2) + 2 * m) + r16]) <= 64.f;
+    all_fast = __all(f);
+  }
+  if (all_fast) {
+    load_w();
+#pragma unroll
+    for (int m = 0; m < NM; ++m) prod_fast(m);
+  } else {
+    for (int m = 0; m < NM; ++m) {
+      bool fast = false;
+      if constexpr (TR) fast = __all(__int_as_float(sm.span[16 * ((wid >> 2) + 2 * m) + r16]) <= 64.f);
+      if (fast) {
+        load_w();
+        prod_fast(m);
+      } else {
+        prod_direct(m);
       }
     }
   }
@@ -502,28 +551,38 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
                 "dG fits in the place of dP and dT");
   f32x4 dqh[NM];
   float qd[4] = {0.f, 0.f, 0.f, 0.f};
+  // this lane's four rows: the readout factor and the coefficient's key-norm term
+  const int row0 = 16 * mti + 4 * kq;
+  const f32x4 rq4 = *reinterpret_cast<const f32x4 *>(&sm.rqn[row0]);
+  f32x4 cb4;
+  {
+    const f32x4 den4 = *reinterpret_cast<const f32x4 *>(&sm.den[row0]);
+    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sm.b[row0]);
+    const f32x4 db4 = *reinterpret_cast<const f32x4 *>(&sm.db[row0]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      cb4[e] = opts.beta_mode != kBetaGated && den4[e] != 0.f
+                   ? -2.f * b4[e] * db4[e] * __builtin_amdgcn_rcpf(den4[e])
+                   : 0.f;
+  }
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const int tj = (wid >> 2) + 2 * m, col = 16 * tj + r16;
-    const float gl = Gt[kChunk - 1][col];
+    const float gl = GT[col][kChunk - 1];
+    const f32x4 gi = g4(col, row0);
     float kbs = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * mti + 4 * kq + e;
-      const float Gi = Gt[row][col];
-      const float E = exp2_fast(Gi), D = exp2_fast(gl - Gi);
+      const int row = row0 + e;
+      const float E = exp2_fast(gi[e]), D = exp2_fast(gl - gi[e]);
       const float kic = to_f32(sm.K[row][col]);
-      const float qh = to_f32(sm.u.pa.Q[row][col]) * sm.rqn[row];
+      const float qh = to_f32(sm.u.pa.Q[row][col]) * rq4[e];
       const float ta = E * qa[m][e], tk = E * ka[m][e], tb = D * kb[m][e];
       const float dqv = ta + H1[m][e];
       dqh[m][e] = dqv;
       qd[e] += qh * dqv;
-      const float den = sm.den[row];
-      const float cb = opts.beta_mode != kBetaGated && den != 0.f
-                           ? -2.f * sm.b[row] * sm.db[row] * __builtin_amdgcn_rcpf(den)
-                           : 0.f;
-      const float dkv = -tk + tb + F1[m][e] + Zc[m][e] + cb * kic;
-      dGt[row][col] = qh * (ta + H1[m][e]) - kic * (tk + tb - F1[m][e] + Zc[m][e]);
+      const float dkv = -tk + tb + F1[m][e] + Zc[m][e] + cb4[e] * kic;
+      dGt[row][col] = qh * dqv - kic * (tk + tb - F1[m][e] + Zc[m][e]);
       kbs += kic * tb;
       if (row < len) dk[(tok + (size_t)row * H) * DK + col] = from_f32<Tin>(dkv);
     }
@@ -555,21 +614,26 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
       if (row < len) dq[(tok + (size_t)row * H) * DK + col] = from_f32<Tin>(dqv);
     }
   }
-  // ---- dg: per channel the reverse prefix of dG over the chunk's rows, with the terms of
-  //      G_last at row len - 1; deta
-  if (tid < DK) {
-    const int cc = tid;
-    const float gl = Gt[kChunk - 1][cc];
-    float acc = exp2_fast(gl) * sm.sc[cc] + sm.kbs[0][cc] + sm.kbs[1][cc] + sm.kbs[2][cc] +
-                sm.kbs[3][cc];
-    for (int i = len - 1; i >= 0; --i) {
-      acc += dGt[i][cc];
-      dg[(tok + (size_t)i * H) * DK + cc] = acc;
+  // ---- dg: per channel the reverse prefix of dG over the chunk's rows (rows past a ragged
+  //      end hold 0), in parts of RPP rows, with the terms of G_last (whose position is
+  //      len - 1, so they reach every written row); deta
+  float sf[RPP];
+#pragma unroll
+  for (int r = RPP - 1; r >= 0; --r) sf[r] = dGt[gp * RPP + r][gc] + (r < RPP - 1 ? sf[r + 1] : 0.f);
+  sm.u.pa.tot[gp][gc] = sf[0];
+  __syncthreads();
+  {
+    float carry = exp2_fast(GT[gc][kChunk - 1]) * sm.sc[gc] + sm.kbs[0][gc] + sm.kbs[1][gc] +
+                  sm.kbs[2][gc] + sm.kbs[3][gc];
+#pragma unroll
+    for (int p = 1; p < NPART; ++p) carry += p > gp ? sm.u.pa.tot[p][gc] : 0.f;
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) {
+      const int row = gp * RPP + r;
+      if (row < len) dg[(tok + (size_t)row * H) * DK + gc] = sf[r] + carry;
     }
-  } else if (tid < DK + kChunk) {
-    const int i = tid - DK;
-    if (i < len) deta[tok + (size_t)i * H] = sm.db[i] * sm.db_deta[i];
   }
+  if (tid < len) deta[tok + (size_t)tid * H] = sm.db[tid] * sm.db_deta[tid];
 }
 
 template <typename Tin, int DK>
