@@ -219,13 +219,13 @@ size_t kla_prefill_workspace_bytes(int32_t n_seq, int32_t total_tokens, int32_t 
 namespace {
 
 // Backward workspace: the forward layout, then per chunk-head the incoming states S and the
-// cotangents dS' of the outgoing ones ([d_k][d_v]), dU and dR ([64][d_v] each), all in the
-// operand type, and X = (I + L)^{-1} (fp32 packed blocks, kTpbElems floats).
+// cotangents dS' of the outgoing ones ([d_k][d_v]), dU ([64][d_v]) and X = (I + L)^{-1}
+// (packed blocks, kTpbElems elements), all in the operand type (dR goes to dv, an output).
 // Diagonal gating adds the forward's decayed tiles (in the forward layout) and A itself
-// (fp32 packed blocks, like X).
+// (packed blocks like X).
 struct BwdLayout {
   WsLayout fw;
-  size_t off_SN, off_dSo, off_dU, off_dR, off_X, off_A = 0, total;
+  size_t off_SN, off_dSo, off_dU, off_X, off_A = 0, total;
 };
 
 BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k, int64_t d_v,
@@ -238,12 +238,11 @@ BwdLayout bwd_layout(int64_t n_seq, int64_t total_tokens, int64_t H, int64_t d_k
   b.off_SN = b.fw.total;
   b.off_dSo = align256(b.off_SN + es * nch * (size_t)H * (size_t)d_k * (size_t)d_v);
   b.off_dU = align256(b.off_dSo + st);
-  b.off_dR = align256(b.off_dU + ut);
-  b.off_X = align256(b.off_dR + ut);
-  b.total = align256(b.off_X + sizeof(float) * nch * (size_t)H * kla::kTpbElems);
+  b.off_X = align256(b.off_dU + ut);
+  b.total = align256(b.off_X + es * nch * (size_t)H * kla::kTpbElems);
   if (diag) {
     b.off_A = b.total;
-    b.total = align256(b.off_A + sizeof(float) * nch * (size_t)H * kla::kTpbElems);
+    b.total = align256(b.off_A + es * nch * (size_t)H * kla::kTpbElems);
   }
   return b;
 }
@@ -351,7 +350,7 @@ kla_status enqueue_prepare_diag(const void *q, const void *k, const float *g, co
                                 float eps, const kla::CoefOpts &opts, const int32_t *cu_seqlens,
                                 int32_t n_seq, int32_t total_tokens, int32_t n_heads, int32_t d_k,
                                 kla_dtype dtype, void *workspace, hipStream_t s,
-                                float *X_out = nullptr, float *A_out = nullptr) {
+                                void *X_out = nullptr, void *A_out = nullptr) {
   const WsViews wv = ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, true);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
   kla_status st =
@@ -367,7 +366,7 @@ kla_status enqueue_prepare(const void *q, const void *k, const float *g, const f
                            const kla::CoefOpts &opts, const int32_t *cu_seqlens, int32_t n_seq,
                            int32_t total_tokens, int32_t n_heads, int32_t d_k, kla_dtype dtype,
                            void *workspace, hipStream_t s, bool split = false,
-                           float *X_out = nullptr, float *LC_out = nullptr) {
+                           void *X_out = nullptr, float *LC_out = nullptr) {
   const WsViews wv =
       ws_views(workspace, n_seq, total_tokens, n_heads, d_k, dtype, false, 0, 0, split);
   const int64_t nch_ub = kla::chunk_upper_bound(n_seq, total_tokens);
@@ -602,8 +601,8 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear any stale error from unrelated work
   char *ws = static_cast<char *>(workspace);
-  float *Xbuf = reinterpret_cast<float *>(ws + bl.off_X);
-  float *Abuf = diag ? reinterpret_cast<float *>(ws + bl.off_A) : nullptr;
+  void *Xbuf = ws + bl.off_X;
+  void *Abuf = diag ? ws + bl.off_A : nullptr;
   if (diag)
     st = enqueue_prepare_diag(q, k, g, eta, eps, co, cu_seqlens, n_seq, total_tokens, n_heads,
                               d_k, dtype, workspace, s, Xbuf, Abuf);
@@ -620,7 +619,7 @@ kla_status kla_prefill_backward_ex(const void *q, const void *k, const void *v, 
     return st;
   if ((st = hip_status(
            kla::launch_bwd(to_dt(dtype), d_k, d_v, q, k, v, dO, g, eta, eps, co, wv.GD, wv.T, wv.P,
-                           Xbuf, dS_T, SN, ws + bl.off_dSo, ws + bl.off_dU, ws + bl.off_dR, dq,
+                           Xbuf, dS_T, SN, ws + bl.off_dSo, ws + bl.off_dU, dq,
                            dk, dv, dg, deta, dS0,
                            wv.tabs, n_seq, kla::chunk_upper_bound(n_seq, total_tokens), n_heads,
                            s, diag ? &wv.diag : nullptr, Abuf),

@@ -27,12 +27,12 @@
 //     dG_last += exp(G_last) <dS', S> + sum_j dec_j k_j.(U dS'^T)_j,
 //     dg_t = sum of dG_i over the chunk's positions i >= t.
 // After the forward kernels have run again (the prep, which also stores every chunk's
-// X = (I + Diag(b) A)^{-1} in fp32, then the chunk scan storing every chunk's incoming state
+// X = (I + Diag(b) A)^{-1} in the operand type, then the chunk scan storing every chunk's incoming state
 // S), two kernels finish the job:
 //   kla_bwd_scan_kernel  the adjoint scan: sequential over the chunks in reverse, parallel over
 //                        (sequence, head, 32-column slice) since the columns of dS are
-//                        independent given the tiles; stores dS', dU and dR per chunk, writes
-//                        dV and dS0.
+//                        independent given the tiles; stores dS' and dU per chunk, writes
+//                        dV (= dR, which the gradient kernel reads back) and dS0.
 //   kla_bwd_grad_kernel  one workgroup per (chunk, head): the contractions over d_v with the
 //                        stored S and dS', then the chunk-local algebra, dq, dk, dg, deta.
 // Tiles sit in LDS in fp32 (the gradient kernel's d_v-loop tiles in the operand type).
@@ -73,9 +73,8 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ dO,
     const float *__restrict__ GD, const Tin *__restrict__ Tm, const Tin *__restrict__ Pm,
     const float *__restrict__ dST, float *__restrict__ dS0, float *__restrict__ dSo,
-    float *__restrict__ dUo, float *__restrict__ dRo, Tin *__restrict__ dv,
-    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV,
-    DiagTiles dg) {
+    float *__restrict__ dUo, Tin *__restrict__ dv, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, int H, int DV, DiagTiles dg) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AdjSmem<DK> &sm = *reinterpret_cast<AdjSmem<DK> *>(smem_raw);
   // the d_v slices of one (sequence, head) read the same K, Q, T and P: give them
@@ -196,15 +195,14 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan_kernel(
       for (int e = 0; e < 4; ++e) sm.dR[16 * ti + 4 * kq + e][16 * tj + r16] = rr[e];
     }
     __syncthreads();
-    // dU and dR to the workspace; dV = dR on the chunk's tokens
+    // dU to the workspace; dV = dR on the chunk's tokens
     {
-      float *du = dUo + ch * kChunk * (size_t)DV + v0, *dr = dRo + ch * kChunk * (size_t)DV + v0;
+      float *du = dUo + ch * kChunk * (size_t)DV + v0;
       for (int e = tid; e < kChunk * kAdjBV / 4; e += kAdjThreads) {
         const int r = e / (kAdjBV / 4), c4 = 4 * (e % (kAdjBV / 4));
         const f32x4 u = *reinterpret_cast<const f32x4 *>(&sm.dU[r][c4]);
         const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.dR[r][c4]);
         *reinterpret_cast<f32x4 *>(du + (size_t)r * DV + c4) = u;
-        *reinterpret_cast<f32x4 *>(dr + (size_t)r * DV + c4) = x;
         if (r < len) {
           Tin *o = dv + (tok + (size_t)r * H) * DV + v0 + c4;
 #pragma unroll
@@ -280,9 +278,8 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ dO,
     const float *__restrict__ GD, const __bf16 *__restrict__ Tm, const __bf16 *__restrict__ Pm,
     const float *__restrict__ dST, float *__restrict__ dS0, __bf16 *__restrict__ dSo,
-    __bf16 *__restrict__ dUo, __bf16 *__restrict__ dRo, __bf16 *__restrict__ dv,
-    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int H, int DV,
-    DiagTiles dg) {
+    __bf16 *__restrict__ dUo, __bf16 *__restrict__ dv, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, int H, int DV, DiagTiles dg) {
   using SM = AdjSmem16<DK>;
   constexpr int LK = SM::LK, LC = SM::LC, LV = SM::LV;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -439,13 +436,11 @@ __global__ __launch_bounds__(kAdjThreads) void kla_bwd_scan16_kernel(
       const f32x4 rr = mmf<kChunk>(
           zero4(), lane, [&](int kk) { return col8<LC>(&sm.T[0][0], 16 * ti, kk, lane); },
           [&](int kk) { return row8<LC>(&sm.dUT[0][0], 16 * tj, kk, lane); });
-      __bf16 *dr = dRo + ch * kChunk * (size_t)DV + (size_t)v0 * kChunk;
       bf16x4 b4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * ti + 4 * kq + e, col = 16 * tj + r16;
         const __bf16 rb = from_f32<__bf16>(rr[e]);
-        dr[row * kAdjBV + col] = rb;
         if (row < len) dv[(tok + (size_t)row * H) * DV + v0 + col] = rb;
         b4[e] = from_f32<__bf16>(sm.gam[row] * rr[e]);
       }
@@ -542,7 +537,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ dO, const float *__restrict__ g, const float *__restrict__ eta,
     float eps, CoefOpts opts, const Tin *__restrict__ SN, const Tin *__restrict__ dSo,
-    const Tin *__restrict__ dUo, const Tin *__restrict__ dRo, const float *__restrict__ Xp,
+    const Tin *__restrict__ dUo, const Tin *__restrict__ dvp, const Tin *__restrict__ Xp,
     Tin *__restrict__ dq, Tin *__restrict__ dk, float *__restrict__ dg, float *__restrict__ deta,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq, int H,
     int DV) {
@@ -571,8 +566,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kq = lane >> 4;
 
-  // ---- X = (I + Diag(b) A)^{-1}: the prep kernel's packed fp32 blocks (ten 16 x 16 blocks on
-  //      and below the diagonal, 640 pieces of four), loaded first, stored after the key rows
+  // ---- X = (I + Diag(b) A)^{-1}: the prep kernel's packed blocks in the operand type (ten
+  //      16 x 16 blocks on and below the diagonal, 640 pieces of four), loaded first, stored
+  //      (as fp32) after the key rows
   constexpr int kXPieces = kTpbElems / 4;
   // g and eta of token `lane`, for wavefront 0 (the decays and b), loaded first
   float g_l = 0.f, eta_l = 0.f;
@@ -580,11 +576,12 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     g_l = g[tok + (size_t)lane * H];
     eta_l = eta[tok + (size_t)lane * H];
   }
-  f32x4 xr[2];
+  typename Raw4<Tin>::type xr[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int e = tid + kGradThreads * x;
-    if (e < kXPieces) xr[x] = *reinterpret_cast<const f32x4 *>(Xp + ch * kTpbElems + 4 * e);
+    if (e < kXPieces)
+      xr[x] = *reinterpret_cast<const typename Raw4<Tin>::type *>(Xp + ch * kTpbElems + 4 * e);
   }
   // ---- K rows (and, bf16, Q rows) with their squared norms; G, b, the decays
   RegTile<Tin, kChunk, DK, kGradThreads> rk;
@@ -604,7 +601,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
       int I, J;
       lower_block(e >> 6, I, J);
       const int r = (e >> 2) & 15, c4 = 4 * (e & 3);
-      *reinterpret_cast<f32x4 *>(&sm.X[16 * I + r][16 * J + c4]) = xr[x];
+      *reinterpret_cast<f32x4 *>(&sm.X[16 * I + r][16 * J + c4]) = cvt4(xr[x]);
     }
   }
   if (tid < 6 * 64) {  // the six blocks above the diagonal are zero
@@ -683,9 +680,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
   float sc = 0.f;
   const Tin *Sb = SN + ch * DK * (size_t)DV;
   const Tin *Sob = dSo + ch * DK * (size_t)DV;
-  const Tin *dUb = dUo + ch * kChunk * (size_t)DV, *dRb = dRo + ch * kChunk * (size_t)DV;
-  // dS', dU and dR as the adjoint scan left them: bf16, each 32-column slice's block
-  // contiguous; fp32, row-major over all d_v columns
+  const Tin *dUb = dUo + ch * kChunk * (size_t)DV;
+  // dS' and dU as the adjoint scan left them: bf16, each 32-column slice's block contiguous;
+  // fp32, row-major over all d_v columns; dR = dV, token rows
   constexpr bool SLM = sizeof(Tin) == 2;
   // each 32-column block is loaded into registers while the one before it is computed
   RegTile<Tin, DK, kAdjBV, kGradThreads> rs, rso;
@@ -694,14 +691,13 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
     rs.load(Sb + v0, (size_t)DV, DK, tid);
     rv.load(v + tok * DV + v0, (size_t)H * DV, len, tid);
     rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
+    rdr.load(dvp + tok * DV + v0, (size_t)H * DV, len, tid);
     if constexpr (SLM) {
       rso.load(Sob + (size_t)v0 * DK, kAdjBV, DK, tid);
       rdu.load(dUb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
-      rdr.load(dRb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
     } else {
       rso.load(Sob + v0, (size_t)DV, DK, tid);
       rdu.load(dUb + v0, (size_t)DV, kChunk, tid);
-      rdr.load(dRb + v0, (size_t)DV, kChunk, tid);
     }
   };
   issue(0);
@@ -1088,7 +1084,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_kernel(
 template <typename Tin, int DK, bool DIAG>
 static hipError_t launch_adjoint_t(int d_v, const void *q, const void *k, const void *dO,
                                    const float *GD, const void *T, const void *P,
-                                   const float *dST, void *dSo, void *dU, void *dR, void *dv,
+                                   const float *dST, void *dSo, void *dU, void *dv,
                                    float *dS0, SeqTables t, int32_t n_seq, int32_t H,
                                    const DiagTiles &dg, hipStream_t stream) {
   const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
@@ -1109,8 +1105,7 @@ static hipError_t launch_adjoint_t(int d_v, const void *q, const void *k, const 
                        dim3(kAdjThreads), sm16, stream, qt, kt, static_cast<const Tin *>(dO), GD,
                        static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
                        static_cast<__bf16 *>(dSo), static_cast<__bf16 *>(dU),
-                       static_cast<__bf16 *>(dR), static_cast<Tin *>(dv), t.cu, t.chunk_off, H,
-                       d_v, dg);
+                       static_cast<Tin *>(dv), t.cu, t.chunk_off, H, d_v, dg);
   } else {
     const size_t smA = sizeof(AdjSmem<DK>);
     static_assert(sizeof(AdjSmem<DK>) <= 160 * 1024, "LDS budget");
@@ -1126,8 +1121,7 @@ static hipError_t launch_adjoint_t(int d_v, const void *q, const void *k, const 
                        dim3(kAdjThreads), smA, stream, qt, kt, static_cast<const Tin *>(dO), GD,
                        static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
                        static_cast<float *>(dSo), static_cast<float *>(dU),
-                       static_cast<float *>(dR), static_cast<Tin *>(dv), t.cu, t.chunk_off, H,
-                       d_v, dg);
+                       static_cast<Tin *>(dv), t.cu, t.chunk_off, H, d_v, dg);
   }
   return hipGetLastError();
 }
@@ -1136,21 +1130,21 @@ template <typename Tin, int DK>
 static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void *v,
                                const void *dO, const float *g, const float *eta, float eps,
                                const CoefOpts &opts, const float *GD, const void *T,
-                               const void *P, const float *X, const float *dST,
-                               const void *SN, void *dSo, void *dU, void *dR, void *dq,
-                               void *dk, void *dv, float *dg, float *deta, float *dS0,
-                               SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
-                               hipStream_t stream, const DiagTiles *diag, const float *A) {
+                               const void *P, const void *X, const float *dST,
+                               const void *SN, void *dSo, void *dU, void *dq, void *dk,
+                               void *dv, float *dg, float *deta, float *dS0, SeqTables t,
+                               int32_t n_seq, int64_t n_chunks_ub, int32_t H,
+                               hipStream_t stream, const DiagTiles *diag, const void *A) {
   hipError_t e;
   if (diag) {
-    e = launch_adjoint_t<Tin, DK, true>(d_v, q, k, dO, GD, T, P, dST, dSo, dU, dR, dv, dS0, t,
+    e = launch_adjoint_t<Tin, DK, true>(d_v, q, k, dO, GD, T, P, dST, dSo, dU, dv, dS0, t,
                                         n_seq, H, *diag, stream);
     if (e != hipSuccess) return e;
     return launch_bwd_grad_diag(sizeof(Tin) == 2 ? Dtype::BF16 : Dtype::F32, DK, d_v, q, k, v,
-                                dO, g, eta, eps, opts, diag->kg, X, A, SN, dSo, dU, dR, dq, dk,
+                                dO, g, eta, eps, opts, diag->kg, X, A, SN, dSo, dU, dv, dq, dk,
                                 dg, deta, t, n_seq, n_chunks_ub, H, stream);
   }
-  e = launch_adjoint_t<Tin, DK, false>(d_v, q, k, dO, GD, T, P, dST, dSo, dU, dR, dv, dS0, t,
+  e = launch_adjoint_t<Tin, DK, false>(d_v, q, k, dO, GD, T, P, dST, dSo, dU, dv, dS0, t,
                                        n_seq, H, DiagTiles{}, stream);
   if (e != hipSuccess) return e;
   const size_t smG = sizeof(GradSmem<Tin, DK>);
@@ -1169,21 +1163,21 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
                        dim3(kGradThreads), smG, stream, qt, kt, static_cast<const Tin *>(v),
                        static_cast<const Tin *>(dO), g, eta, eps, opts,
                        static_cast<const Tin *>(SN), static_cast<const Tin *>(dSo),
-                       static_cast<const Tin *>(dU), static_cast<const Tin *>(dR), X,
-                       static_cast<Tin *>(dq), static_cast<Tin *>(dk), dg, deta, t.cu,
-                       t.chunk_off, n_seq, H, d_v);
+                       static_cast<const Tin *>(dU), static_cast<const Tin *>(dv),
+                       static_cast<const Tin *>(X), static_cast<Tin *>(dq),
+                       static_cast<Tin *>(dk), dg, deta, t.cu, t.chunk_off, n_seq, H, d_v);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
                       const CoefOpts &opts, const float *GD, const void *T, const void *P,
-                      const float *X, const float *dST, const void *SN, void *dSo, void *dU,
-                      void *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
+                      const void *X, const float *dST, const void *SN, void *dSo, void *dU,
+                      void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
                       SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
-                      hipStream_t stream, const DiagTiles *diag, const float *A) {
+                      hipStream_t stream, const DiagTiles *diag, const void *A) {
 #define KLA_BWD(TIN, DK_)                                                                     \
-  return launch_bwd_t<TIN, DK_>(d_v, q, k, v, dO, g, eta, eps, opts, GD, T, P, X, dST, SN, dSo, dU, dR, \
+  return launch_bwd_t<TIN, DK_>(d_v, q, k, v, dO, g, eta, eps, opts, GD, T, P, X, dST, SN, dSo, dU, \
                                 dq, dk, dv, dg, deta, dS0, t, n_seq, n_chunks_ub, H, stream, diag, A);
   if (dt == Dtype::BF16) {
     if (d_k == 128) { KLA_BWD(__bf16, 128) }

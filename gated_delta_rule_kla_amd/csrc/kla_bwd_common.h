@@ -277,13 +277,13 @@ template <typename LT> constexpr int ldl() { return sizeof(LT) == 2 ? 40 : 36; }
 }  // namespace
 
 // The per-chunk gradient kernel under diagonal gating (kla_bwd_diag.hip): Kg, X and A from
-// launch_prep_diag, SN from the states-only scan, dS', dU and dR from the adjoint scan; writes
-// dq, dk (operand type), dg ([n_tok, H, d_k]) and deta (fp32).
+// launch_prep_diag, SN from the states-only scan, dS', dU and dR (= dv) from the adjoint scan;
+// writes dq, dk (operand type), dg ([n_tok, H, d_k]) and deta (fp32).
 hipError_t launch_bwd_grad_diag(Dtype dt, int d_k, int d_v, const void *q, const void *k,
                                 const void *v, const void *dO, const float *g, const float *eta,
-                                float eps, const CoefOpts &opts, const void *KG, const float *X,
-                                const float *A, const void *SN, const void *dSo, const void *dU,
-                                const void *dR, void *dq, void *dk, float *dg, float *deta,
+                                float eps, const CoefOpts &opts, const void *KG, const void *X,
+                                const void *A, const void *SN, const void *dSo, const void *dU,
+                                const void *dv, void *dq, void *dk, float *dg, float *deta,
                                 SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                                 hipStream_t stream);
 

@@ -9,7 +9,7 @@
 //   A_ij = sum_c k_ic k_jc Gamma_ijc (j < i),  P^_ij = sum_c q^_ic k_jc Gamma_ijc (j <= i),
 //   X = (I + Diag(b) A)^{-1},  T = X Diag(b),
 //   R = V - Kg S,  U = T R,  O = Q^g S + P^ U,  S' = Diag(exp(G_last)) S + Kd^T U.
-// The adjoint scan hands over dU, dR (= dV) and dS' per chunk; this kernel forms the rest by
+// The adjoint scan hands over dU, dR (as dV) and dS' per chunk; this kernel forms the rest by
 // reverse-mode differentiation of the lines above:
 //   qa = dO S^T, ka = dR S^T, kb = U dS'^T (64 x d_k),  sc_c = sum_v S_cv dS'_cv,
 //   dP^ = lower(dO U^T),  dT = lower(dU R^T),  dX = dT Diag(b),
@@ -77,9 +77,9 @@ template <typename Tin, int DK>
 __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const Tin *__restrict__ dO, const float *__restrict__ g, const float *__restrict__ eta,
-    float eps, CoefOpts opts, const Tin *__restrict__ KG, const float *__restrict__ Xp,
-    const float *__restrict__ Ap, const Tin *__restrict__ SN, const Tin *__restrict__ dSo,
-    const Tin *__restrict__ dUo, const Tin *__restrict__ dRo, Tin *__restrict__ dq,
+    float eps, CoefOpts opts, const Tin *__restrict__ KG, const Tin *__restrict__ Xp,
+    const Tin *__restrict__ Ap, const Tin *__restrict__ SN, const Tin *__restrict__ dSo,
+    const Tin *__restrict__ dUo, const Tin *__restrict__ dvp, Tin *__restrict__ dq,
     Tin *__restrict__ dk, float *__restrict__ dg, float *__restrict__ deta,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int n_seq, int H,
     int DV) {
@@ -118,20 +118,21 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
   const int mti = wid & 3;
   float eta_l = 0.f;
   if (wid == 0 && lane < len) eta_l = eta[tok + (size_t)lane * H];
-  f32x4 xr[2];
+  typename Raw4<Tin>::type xr[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int e = tid + kGradThreads * x;
-    if (e < kXPieces) xr[x] = *reinterpret_cast<const f32x4 *>(Xp + ch * kTpbElems + 4 * e);
+    if (e < kXPieces)
+      xr[x] = *reinterpret_cast<const typename Raw4<Tin>::type *>(Xp + ch * kTpbElems + 4 * e);
   }
   RegTile<Tin, kChunk, DK, kGradThreads> rkr, rkg, rq;
   rkr.load(k + tok * DK, (size_t)H * DK, len, tid);
   rkg.load(KG + ch * kChunk * DK, DK, kChunk, tid);
   const Tin *Sb = SN + ch * DK * (size_t)DV;
   const Tin *Sob = dSo + ch * DK * (size_t)DV;
-  const Tin *dUb = dUo + ch * kChunk * (size_t)DV, *dRb = dRo + ch * kChunk * (size_t)DV;
-  // dS', dU and dR as the adjoint scan left them: bf16, each 32-column slice's block
-  // contiguous; fp32, row-major over all d_v columns
+  const Tin *dUb = dUo + ch * kChunk * (size_t)DV;
+  // dS' and dU as the adjoint scan left them: bf16, each 32-column slice's block contiguous;
+  // fp32, row-major over all d_v columns; dR = dV, token rows
   constexpr bool SLM = sizeof(Tin) == 2;
   RegTile<Tin, DK, kAdjBV, kGradThreads> rs, rso;
   RegTile<Tin, kChunk, kAdjBV, kGradThreads> rv, rdo, rdu, rdr;
@@ -139,14 +140,13 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
     rs.load(Sb + v0, (size_t)DV, DK, tid);
     rv.load(v + tok * DV + v0, (size_t)H * DV, len, tid);
     rdo.load(dO + tok * DV + v0, (size_t)H * DV, len, tid);
+    rdr.load(dvp + tok * DV + v0, (size_t)H * DV, len, tid);
     if constexpr (SLM) {
       rso.load(Sob + (size_t)v0 * DK, kAdjBV, DK, tid);
       rdu.load(dUb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
-      rdr.load(dRb + (size_t)v0 * kChunk, kAdjBV, kChunk, tid);
     } else {
       rso.load(Sob + v0, (size_t)DV, DK, tid);
       rdu.load(dUb + v0, (size_t)DV, kChunk, tid);
-      rdr.load(dRb + v0, (size_t)DV, kChunk, tid);
     }
   };
   issue(0);
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
       const int t = wid + 8 * x, I = t >> 2, J = min(t & 3, I);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        ar[x][e] = Ap[ch * kTpbElems + (I * (I + 1) / 2 + J) * 256 + (4 * kq + e) * 16 + r16];
+        ar[x][e] = to_f32(Ap[ch * kTpbElems + (I * (I + 1) / 2 + J) * 256 + (4 * kq + e) * 16 + r16]);
     }
   };
   rkr.sqnorms(sm.den, tid);
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
       int I, J;
       lower_block(e >> 6, I, J);
       const int r = (e >> 2) & 15, c4 = 4 * (e & 3);
-      *reinterpret_cast<f32x4 *>(&sm.X[16 * I + r][16 * J + c4]) = xr[x];
+      *reinterpret_cast<f32x4 *>(&sm.X[16 * I + r][16 * J + c4]) = cvt4(xr[x]);
     }
   }
   if (tid < 6 * 64) {  // the six blocks above the diagonal are zero
@@ -639,9 +639,9 @@ __global__ __launch_bounds__(kGradThreads) void kla_bwd_grad_diag_kernel(
 template <typename Tin, int DK>
 static hipError_t launch_grad_diag_t(int d_v, const void *q, const void *k, const void *v,
                                      const void *dO, const float *g, const float *eta, float eps,
-                                     const CoefOpts &opts, const void *KG, const float *X,
-                                     const float *A, const void *SN, const void *dSo,
-                                     const void *dU, const void *dR, void *dq, void *dk,
+                                     const CoefOpts &opts, const void *KG, const void *X,
+                                     const void *A, const void *SN, const void *dSo,
+                                     const void *dU, const void *dv, void *dq, void *dk,
                                      float *dg, float *deta, SeqTables t, int32_t n_seq,
                                      int64_t n_chunks_ub, int32_t H, hipStream_t stream) {
   const size_t smG = sizeof(GradDiagSmem<Tin, DK>);
@@ -661,23 +661,24 @@ static hipError_t launch_grad_diag_t(int d_v, const void *q, const void *k, cons
                      dim3(kGradThreads), smG, stream, static_cast<const Tin *>(q),
                      static_cast<const Tin *>(k), static_cast<const Tin *>(v),
                      static_cast<const Tin *>(dO), g, eta, eps, opts,
-                     static_cast<const Tin *>(KG), X, A, static_cast<const Tin *>(SN),
+                     static_cast<const Tin *>(KG), static_cast<const Tin *>(X),
+                     static_cast<const Tin *>(A), static_cast<const Tin *>(SN),
                      static_cast<const Tin *>(dSo), static_cast<const Tin *>(dU),
-                     static_cast<const Tin *>(dR), static_cast<Tin *>(dq), static_cast<Tin *>(dk),
+                     static_cast<const Tin *>(dv), static_cast<Tin *>(dq), static_cast<Tin *>(dk),
                      dg, deta, t.cu, t.chunk_off, n_seq, H, d_v);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_grad_diag(Dtype dt, int d_k, int d_v, const void *q, const void *k,
                                 const void *v, const void *dO, const float *g, const float *eta,
-                                float eps, const CoefOpts &opts, const void *KG, const float *X,
-                                const float *A, const void *SN, const void *dSo, const void *dU,
-                                const void *dR, void *dq, void *dk, float *dg, float *deta,
+                                float eps, const CoefOpts &opts, const void *KG, const void *X,
+                                const void *A, const void *SN, const void *dSo, const void *dU,
+                                const void *dv, void *dq, void *dk, float *dg, float *deta,
                                 SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                                 hipStream_t stream) {
 #define KLA_GRAD_DIAG(TIN, DK_)                                                                  \
   return launch_grad_diag_t<TIN, DK_>(d_v, q, k, v, dO, g, eta, eps, opts, KG, X, A, SN, dSo, dU, \
-                                      dR, dq, dk, dg, deta, t, n_seq, n_chunks_ub, H, stream);
+                                      dv, dq, dk, dg, deta, t, n_seq, n_chunks_ub, H, stream);
   if (dt == Dtype::BF16) {
     if (d_k == 128) { KLA_GRAD_DIAG(__bf16, 128) }
     KLA_GRAD_DIAG(__bf16, 64)

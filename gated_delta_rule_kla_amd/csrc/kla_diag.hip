@@ -185,7 +185,7 @@ __global__ __launch_bounds__(DK * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     const float *__restrict__ eta, float eps, CoefOpts opts, SeqTables tabs, int n_seq, int H,
     Tin *__restrict__ T_out, Tin *__restrict__ P_out, float *__restrict__ GD_out,
     Tin *__restrict__ KG_out, Tin *__restrict__ QG_out, Tin *__restrict__ KD_out,
-    float *__restrict__ GC_out, float *__restrict__ X_out, float *__restrict__ A_out) {
+    float *__restrict__ GC_out, Tin *__restrict__ X_out, Tin *__restrict__ A_out) {
   constexpr int NW = DK / 32;
   static_assert(NW >= 2, "wavefronts 0 and 1 finish the chunk");
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -486,14 +486,14 @@ __global__ __launch_bounds__(DK * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
     for (int b = 0; b < 10; ++b) Aa[b] += sm.u.t.pa[w][b][lane];
-  if (A_out) {  // the backward pass: A itself (fp32, packed blocks, zero on the diagonal)
-    float *A_task = A_out + (size_t)task * kTpbElems;
+  if (A_out) {  // the backward pass: A itself (packed blocks, zero on the diagonal)
+    Tin *A_task = A_out + (size_t)task * kTpbElems;
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
       for (int J = 0; J <= I; ++J) {
         const f32x4 av = Aa[I * (I + 1) / 2 + J];
-        out_put<float>(A_task, true, 16 * I + r16, 16 * J + 4 * kq, av[0], av[1], av[2], av[3]);
+        out_put<Tin>(A_task, true, 16 * I + r16, 16 * J + 4 * kq, av[0], av[1], av[2], av[3]);
       }
   }
   {
@@ -519,12 +519,12 @@ __global__ __launch_bounds__(DK * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
   wave_lds_sync();
   Tin *T_task = T_out + (size_t)task * kTpbElems;
-  float *X_task = X_out ? X_out + (size_t)task * kTpbElems : nullptr;
+  Tin *X_task = X_out ? X_out + (size_t)task * kTpbElems : nullptr;
   chunk_inverse<false>(Lr, sm.ps, [] { wave_lds_sync(); },
                        [&](int row, int col, const f32x4 &x, const f32x4 &bv) {
                          out_put<Tin>(T_task, true, row, col, x[0] * bv[0], x[1] * bv[1],
                                       x[2] * bv[2], x[3] * bv[3]);
-                         if (X_task) out_put<float>(X_task, true, row, col, x[0], x[1], x[2], x[3]);
+                         if (X_task) out_put<Tin>(X_task, true, row, col, x[0], x[1], x[2], x[3]);
                        });
 }
 
@@ -533,7 +533,7 @@ static hipError_t launch_prep_diag_t(const void *q, const void *k, const float *
                                      const float *eta, float eps, const CoefOpts &opts,
                                      SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                                      const DiagTiles &dt, void *T_out, void *P_out,
-                                     float *GD_out, float *X_out, float *A_out,
+                                     float *GD_out, void *X_out, void *A_out,
                                      hipStream_t stream) {
   const size_t smem = sizeof(DiagSmem<DK>);
   static_assert(sizeof(DiagSmem<DK>) <= 80 * 1024, "two workgroups to a compute unit");
@@ -555,7 +555,7 @@ static hipError_t launch_prep_diag_t(const void *q, const void *k, const float *
                      static_cast<Tin *>(const_cast<void *>(dt.kg)),
                      static_cast<Tin *>(const_cast<void *>(dt.qg)),
                      static_cast<Tin *>(const_cast<void *>(dt.kd)), const_cast<float *>(dt.gc),
-                     X_out, A_out);
+                     static_cast<Tin *>(X_out), static_cast<Tin *>(A_out));
   return hipGetLastError();
 }
 
@@ -563,7 +563,7 @@ hipError_t launch_prep_diag(Dtype dt, int d_k, const void *q, const void *k, con
                             const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                             int32_t n_seq, int64_t n_chunks_ub, int32_t H, const DiagTiles &tiles,
                             void *T_out, void *P_out, float *GD_out, hipStream_t stream,
-                            float *X_out, float *A_out) {
+                            void *X_out, void *A_out) {
 #define KLA_PREP_DIAG(TIN, DK_)                                                                \
   return launch_prep_diag_t<TIN, DK_>(q, k, g, eta, eps, opts, t, n_seq, n_chunks_ub, H, tiles, \
                                       T_out, P_out, GD_out, X_out, A_out, stream);

@@ -49,8 +49,8 @@ constexpr int kGDFloats = 3 * 64;
 // rows divided by ||q_i|| under the normalised readout).  G_out / beta_out (per token) and
 // GD_out (per chunk-head decay factors) are each optional.  tp_split (bf16, packed): T and
 // P as hi = bf16(x) and lo = bf16(x - hi) blocks, the lo blocks after the hi ones of each
-// chunk-head (twice the packed size).  X_out (optional): X = (I + L)^{-1} itself in fp32,
-// packed blocks (kTpbElems floats per chunk-head), for the backward pass.  LC_out (optional):
+// chunk-head (twice the packed size).  X_out (optional): X = (I + L)^{-1} itself in the
+// operand type, packed blocks (kTpbElems elements per chunk-head), for the backward pass.  LC_out (optional):
 // per chunk-head the natural log of a bound on the spectral norm of the chunk's homogeneous
 // state map, G_last + sum_t ln max(1, |1 - b_t ||k_t||^2|).
 hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const float *g,
@@ -58,7 +58,7 @@ hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const fl
                        int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
                        const PlanArgs &pa, hipStream_t stream, bool tp_split = false,
-                       float *X_out = nullptr, float *LC_out = nullptr);
+                       void *X_out = nullptr, float *LC_out = nullptr);
 
 // Diagonal gating: the decayed key and query tiles per chunk-head ([64][d_k] each, operand
 // type) K o exp(G), Q o exp(G), K o exp(G_last - G), and exp(G_last) ([d_k] fp32).
@@ -70,12 +70,12 @@ struct DiagTiles {
 // a1 + a2 under diagonal gating (g [n_tok, H, d_k]): b, T and P (packed blocks), unit decays
 // with the readout factor in GD, and the decayed tiles.  Reads the tables launch_plan wrote.
 // For the backward pass, X_out and A_out (non-null) also receive X = (I + Diag(b) A)^{-1} and
-// A itself per chunk-head, fp32, as ten packed 16 x 16 blocks like T.
+// A itself per chunk-head, in the operand type, as ten packed 16 x 16 blocks like T.
 hipError_t launch_prep_diag(Dtype dt, int d_k, const void *q, const void *k, const float *g,
                             const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                             int32_t n_seq, int64_t n_chunks_ub, int32_t H, const DiagTiles &tiles,
                             void *T_out, void *P_out, float *GD_out, hipStream_t stream,
-                            float *X_out = nullptr, float *A_out = nullptr);
+                            void *X_out = nullptr, void *A_out = nullptr);
 
 // Optional WY factors W = T Diag(exp G) K and U~ = T V (unit-check path).
 hipError_t launch_wy(Dtype dt, int d_k, int d_v, const void *k, const void *v, const float *G,
@@ -130,20 +130,20 @@ hipError_t launch_scan_two_level(Dtype dt, int d_k, int d_v, const void *q, cons
                                  const SegArgs &sa, float *NM, float *Sin, hipStream_t stream);
 
 // The backward pass after launch_prep (with the same opts, and X_out = X) and launch_scan
-// with SN: the adjoint scan (per chunk-head dS' ([d_k][d_v]), dU and dR ([64][d_v]) in the
-// operand type into dSo, dU and dR: fp32 row-major, or bf16 with each 32-column slice's block
-// contiguous; dv, and dS0 if non-null), then the per-chunk gradients dq, dk (operand type) and
-// dg, deta (fp32).  dST may be null (a zero cotangent of the final state).
-// Diagonal gating (diag non-null): after launch_prep_diag with X_out = X and A_out = A and
-// launch_scan with diag and SN; g and dg are [n_tok, H, d_k].
+// with SN: the adjoint scan (per chunk-head dS' ([d_k][d_v]) and dU ([64][d_v]) in the
+// operand type into dSo and dU: fp32 row-major, or bf16 with each 32-column slice's block
+// contiguous; dv = dR, and dS0 if non-null), then the per-chunk gradients (which read dR back
+// from dv) dq, dk (operand type) and dg, deta (fp32).  dST may be null (a zero cotangent of
+// the final state).  Diagonal gating (diag non-null): after launch_prep_diag with X_out = X and
+// A_out = A and launch_scan with diag and SN; g and dg are [n_tok, H, d_k].
 hipError_t launch_bwd(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,
                       const void *dO, const float *g, const float *eta, float eps,
                       const CoefOpts &opts, const float *GD, const void *T, const void *P,
-                      const float *X, const float *dST, const void *SN, void *dSo, void *dU,
-                      void *dR, void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
+                      const void *X, const float *dST, const void *SN, void *dSo, void *dU,
+                      void *dq, void *dk, void *dv, float *dg, float *deta, float *dS0,
                       SeqTables t, int32_t n_seq, int64_t n_chunks_ub, int32_t H,
                       hipStream_t stream, const DiagTiles *diag = nullptr,
-                      const float *A = nullptr);
+                      const void *A = nullptr);
 
 // a5: one decode step.
 hipError_t launch_decode(Dtype dt, int d_k, int d_v, const void *q, const void *k, const void *v,

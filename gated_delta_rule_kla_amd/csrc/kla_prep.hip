@@ -248,7 +248,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
     int32_t *__restrict__ chunk_off, int n_seq, int H, float *__restrict__ G_out,
     float *__restrict__ beta_out, TOut *__restrict__ T_out, Tin *__restrict__ P_out,
     float *__restrict__ GD_out, CoefOpts opts, PlanArgs pa, int tp_split,
-    float *__restrict__ X_out, float *__restrict__ LC_out) {
+    Tin *__restrict__ X_out, float *__restrict__ LC_out) {
   __shared__ PrepSmem sm;
   const Planner pl = make_planner(pa, SeqTables{cu, chunk_off}, n_seq);
   write_tables(pl);
@@ -415,13 +415,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sizeof(Tin) 
       for (int j = i + 1; j < 4; ++j)
         out_put<TOut>(T_task, false, 16 * i + r16, 16 * j + 4 * kg, 0.f, 0.f, 0.f, 0.f);
   }
-  float *X_task = X_out ? X_out + (size_t)task * kTpbElems : nullptr;
+  Tin *X_task = X_out ? X_out + (size_t)task * kTpbElems : nullptr;
   chunk_T<Tin, NKS, false>(
       kf, gd, bme, G2me, sm, [] { lds_barrier(); },
       [&](int row, int col, const f32x4 &x, const f32x4 &bv) {
         out_put<TOut>(T_task, t_packed, row, col, x[0] * bv[0], x[1] * bv[1], x[2] * bv[2],
                       x[3] * bv[3], tp_split != 0);
-        if (X_task) out_put<float>(X_task, true, row, col, x[0], x[1], x[2], x[3]);
+        if (X_task) out_put<Tin>(X_task, true, row, col, x[0], x[1], x[2], x[3]);
       });
 }
 
@@ -431,7 +431,7 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
                                 int64_t n_chunks_ub, int32_t H, float *G_out, float *beta_out,
                                 void *T_out, bool t_fp32, void *P_out, float *GD_out,
                                 const PlanArgs &pa, hipStream_t stream, bool tp_split,
-                                float *X_out, float *LC_out) {
+                                void *X_out, float *LC_out) {
   if (n_chunks_ub <= 0 || H <= 0) return hipSuccess;
   if (tp_split && (sizeof(Tin) != 2 || t_fp32 || !GD_out)) return hipErrorInvalidValue;
   const int64_t tasks = n_chunks_ub * H;
@@ -442,13 +442,13 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
   if (t_fp32 || sizeof(Tin) == 4)
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, float>), grid, dim3(64), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
-                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts, pa, 0, X_out,
-                       LC_out);
+                       G_out, beta_out, static_cast<float *>(T_out), pp, GD_out, opts, pa, 0,
+                       static_cast<Tin *>(X_out), LC_out);
   else
     hipLaunchKernelGGL((kla_prep_kernel<Tin, DK, Tin>), grid, dim3(64), 0, stream, qq,
                        static_cast<const Tin *>(k), g, eta, eps, t.cu, t.chunk_off, n_seq, H,
                        G_out, beta_out, static_cast<Tin *>(T_out), pp, GD_out, opts, pa,
-                       tp_split ? 1 : 0, X_out, LC_out);
+                       tp_split ? 1 : 0, static_cast<Tin *>(X_out), LC_out);
   return hipGetLastError();
 }
 
@@ -456,7 +456,7 @@ hipError_t launch_prep(Dtype dt, int d_k, const void *q, const void *k, const fl
                        const float *eta, float eps, const CoefOpts &opts, SeqTables t,
                        int32_t n_seq, int64_t n_chunks_ub, int32_t H, float *G_out,
                        float *beta_out, void *T_out, bool t_fp32, void *P_out, float *GD_out,
-                       const PlanArgs &pa, hipStream_t stream, bool tp_split, float *X_out,
+                       const PlanArgs &pa, hipStream_t stream, bool tp_split, void *X_out,
                        float *LC_out) {
   if (dt == Dtype::BF16) {
     if (d_k == 128)

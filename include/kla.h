@@ -324,10 +324,10 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const
  *   dS0         [n_seq, n_heads, d_k, d_v] fp32 (written), or NULL
  *   workspace   device buffer of at least kla_prefill_backward_workspace_bytes
  *               bytes, 256-byte aligned; contents are scratch.  It holds the
- *               forward chunk stage run again (with every chunk's
- *               (I + L)^{-1} in fp32), and in the element type `dtype` (bf16
- *               for bf16 inputs) every chunk's incoming state, the cotangent
- *               of its outgoing state and its dU and dR.
+ *               forward chunk stage run again, and in the element type `dtype`
+ *               (bf16 for bf16 inputs) every chunk's (I + L)^{-1}, incoming
+ *               state, the cotangent of its outgoing state and its dU (dv,
+ *               written first, is read back as the chunks' dR).
  * The gradient buffers must not overlap each other, the inputs or the
  * workspace.  q, k, v, dO, dq, dk and dv must be 16-byte aligned; g, eta, S0,
  * dS_T, dg, deta and dS0 4-byte aligned.  Size limits and errors as for
@@ -351,7 +351,7 @@ kla_status kla_prefill_backward(const void *q, const void *k, const void *v, con
  * Appendix B.5: g and dg are then [total_tokens, n_heads, d_k] fp32, the
  * workspace is kla_prefill_backward_workspace_bytes_ex with the same options,
  * and it also holds the decayed key and query tiles of the forward stage and
- * every chunk's A = (K K^T per channel, decayed) in fp32).  precision other
+ * every chunk's A = (K K^T per channel, decayed) in the element type).  precision other
  * than KLA_PRECISION_BF16 gives KLA_ERR_UNSUPPORTED.  The forward arguments and
  * options must be those of the forward call whose gradients are wanted. */
 size_t kla_prefill_backward_workspace_bytes_ex(int32_t n_seq, int32_t total_tokens,
