@@ -62,18 +62,24 @@ def run_case(kla, inp, ct, tol, with_state=True, with_dst=True):
 
 
 CASES = {
-    # name: (workload, overrides)
-    "tiny_fp32_T256_d64": (0, dict()),
-    "fp32_ragged_packed": (0, dict(lens=(150, 64, 5, 0, 1, 70), H=2)),
-    "bf16_d128_T300": (1, dict(T=300, n_seq=2, H=3)),
-    "bf16_packed_dv256": (4, dict(lens=(100, 0, 200, 33), H=2)),
+    # name: (workload, overrides, dtype override or None)
+    "tiny_fp32_T256_d64": (0, dict(), None),
+    "fp32_ragged_packed": (0, dict(lens=(150, 64, 5, 0, 1, 70), H=2), None),
+    "fp32_d128_T200": (1, dict(T=200, n_seq=1, H=2), torch.float32),
+    "bf16_d64_T260": (0, dict(T=260, H=2), torch.bfloat16),
+    "bf16_d128_T300": (1, dict(T=300, n_seq=2, H=3), None),
+    "bf16_packed_dv256": (4, dict(lens=(100, 0, 200, 33), H=2), None),
 }
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_backward_matches_oracle(kla, case):
-    w, over = CASES[case]
+    w, over, dt = CASES[case]
     inp = ki.prefill_inputs(w, **over)
+    if dt is not None:
+        for name in ("q", "k", "v"):
+            inp[name] = inp[name].to(dt).contiguous()
+        inp["dtype"] = dt
     if inp["S0"] is None:  # give every case a nonzero incoming state
         gen = torch.Generator().manual_seed(7)
         inp["S0"] = 0.3 * torch.randn(inp["n_seq"], inp["q"].shape[1], inp["k"].shape[-1],

@@ -69,19 +69,26 @@ def run_case(kla, inp, ct, tol, **variant):
 
 
 CASES = {
-    # name: (workload, overrides)
-    "tiny_fp32_T256_d64": (0, dict()),
-    "fp32_ragged_packed": (0, dict(lens=(150, 64, 5, 0, 1, 70), H=2)),
-    "bf16_d128_T300": (1, dict(T=300, n_seq=2, H=3)),
+    # name: (workload, overrides, dtype override or None)
+    "tiny_fp32_T256_d64": (0, dict(), None),
+    "fp32_ragged_packed": (0, dict(lens=(150, 64, 5, 0, 1, 70), H=2), None),
+    "fp32_d128_T200": (1, dict(T=200, n_seq=1, H=2), torch.float32),
+    "bf16_d64_T260": (0, dict(T=260, H=2), torch.bfloat16),
+    "bf16_d128_T300": (1, dict(T=300, n_seq=2, H=3), None),
     # g ~ U(-2, 0) per channel: many channels leave the 2^64 window within a chunk
-    "bf16_packed_dv256_strong": (4, dict(lens=(100, 0, 200, 33), H=2)),
+    "bf16_packed_dv256_strong": (4, dict(lens=(100, 0, 200, 33), H=2), None),
 }
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_diagonal_backward_matches_oracle(kla, case):
-    w, over = CASES[case]
-    inp = with_state(ki.prefill_inputs(w, diag=True, **over), 7)
+    w, over, dt = CASES[case]
+    inp = ki.prefill_inputs(w, diag=True, **over)
+    if dt is not None:
+        for name in ("q", "k", "v"):
+            inp[name] = inp[name].to(dt).contiguous()
+        inp["dtype"] = dt
+    inp = with_state(inp, 7)
     ct = ki.cotangents(inp, seed=3000 + len(case))
     print(f"case {case}", flush=True)
     run_case(kla, inp, ct, TOL[inp["dtype"]])
