@@ -156,6 +156,24 @@ __device__ __forceinline__ bool warm_start(const SegArgs &sa, int seq, int h, in
   return __all(ok);
 }
 
+// For at most 64 sequences of mixed lengths, the sequence of rank r when they are ordered
+// longest first (ties by index); -1 otherwise (equal lengths, or more sequences).  Lane l
+// ranks sequence l against the others; the answer is the lane whose rank is r, the same in
+// every lane of the wavefront.
+__device__ __forceinline__ int longest_first(const int32_t *__restrict__ cu, int n_seq, int r) {
+  if (n_seq > kWave) return -1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int len = lane < n_seq ? cu[lane + 1] - cu[lane] : -1;
+  if (!__any(lane < n_seq && len != __shfl(len, 0, kWave))) return -1;
+  int rank = 0;
+  for (int m = 0; m < n_seq; ++m) {
+    const int lm = __shfl(len, m, kWave);
+    rank += (lm > len || (lm == len && m < lane)) ? 1 : 0;
+  }
+  const unsigned long long hit = __ballot(lane < n_seq && rank == r);
+  return hit ? (int)__builtin_ctzll(hit) : r;  // ranks are a permutation: one lane hits
+}
+
 template <typename Tin, int DK, typename SHP, bool DIAG, bool STATES, int MODE,
           bool SPLIT = false>
 __global__ __launch_bounds__(SHP::THREADS)
@@ -192,7 +210,18 @@ void kla_scan_kernel(
   const int nblk = gridDim.x, b = blockIdx.x;
   const int pidx = (nblk % 8 == 0) ? (b % 8) * (nblk / 8) + b / 8 : b;
   const int slice = pidx % nsl, sh = pidx / nsl;
-  const int h = sh % H, n = sh / H;  // n: the sequence, or the unit of the two-level scan
+  // Packed sequences of mixed lengths: the sequential scan takes its units head-major, the
+  // sequences longest first within a head, so that one XCD's contiguous share of the units
+  // holds every sequence of its heads and the longest start first (they balance over XCDs
+  // and CUs).  Otherwise sequence-major.
+  int h = sh % H, n = sh / H;  // n: the sequence, or the unit of the two-level scan
+  if constexpr (MODE == kScanSeq) {
+    const int hm = sh / n_seq, nm = longest_first(cu, n_seq, sh - hm * n_seq);
+    if (nm >= 0) {
+      h = hm;
+      n = nm;
+    }
+  }
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, kg = lane >> 4;
   const bool consumer = wid < kConsumers;
