@@ -118,17 +118,16 @@ def test_decode_diagonal_gate(kla, dtype, dk, dv, B, H):
     w = ki.Workload(92, "decode-diag", B, H, dk, dv, dtype, T=1, s0_var=0.05, decode_steps=3,
                     g_low=-1.0)
     d = to_dev(ki.decode_inputs(w, diag=True))
-    pick = list(range(B)) if B <= 8 else [0, 1, 7, 31, 62, 63]
     S = d["S"].clone()
-    So = d["S"][pick].double().cpu().numpy()
+    So = d["S"].double().cpu().numpy()
     for t in range(3):
         o, S = kla.kla_decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t],
                                    d["eps"], S, inplace=(t == 1))
-        oo, So = oracle.decode(d["q"][t][pick], d["k"][t][pick], d["v"][t][pick],
-                               d["g"][t][pick], d["eta"][t][pick], d["eps"], So)
+        oo, So = oracle.decode(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t],
+                               d["eps"], So)
         torch.cuda.synchronize()
-        check(o[pick], oo, TOL[dtype], "o t")
-        check(S[pick], So, TOL[dtype], "S t")
+        check(o, oo, TOL[dtype], "o t")
+        check(S, So, TOL[dtype], "S t")
 
 
 # ------------------------------------------------------------------ diagonal gating (prefill)
@@ -221,12 +220,12 @@ def test_prefill_diagonal_equal_channels_match_scalar_gate(kla):
 
 # ------------------------------------------------------------- variants at the full layer size
 @pytest.mark.parametrize("variant", ["diagonal_gate", "gated_unit_keys", "normalised_inv_sqrt_t"])
-def test_variants_full_workload_sampled(kla, variant):
+def test_variants_full_workload(kla, variant):
     """The prefill workload at full size (4 sequences x 4096 tokens x 16 heads, d = 128, bf16,
     random S0) in the bench launch configuration, once per variant: the diagonal gate (g per
     key channel), the gated delta rule on unit-norm keys, and the readout divided by ||q_t||
-    with the 1/sqrt(t) coefficient and position offsets.  The oracle checks two sampled
-    (sequence, head) pairs, every token and the final state of each."""
+    with the 1/sqrt(t) coefficient and position offsets.  Every output and final state
+    against the oracle, and each (sequence, head) on its own scale."""
     d = ki.prefill_inputs(1, diag=(variant == "diagonal_gate"))
     kw = {}
     if variant == "gated_unit_keys":
@@ -242,15 +241,18 @@ def test_variants_full_workload_sampled(kla, variant):
     o, ST = run_prefill_diag(kla, dev, **{key: (val.cuda() if isinstance(val, torch.Tensor)
                                                 else val) for key, val in kw.items()})
     T = d["q"].shape[0] // d["n_seq"]
-    for n, h in ((1, 3), (3, 15)):
+    okw = dict(kw)
+    if "pos_offset" in okw:
+        okw["pos_offset"] = pos.numpy()
+    oo, So = oracle.prefill(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"], S0=d["S0"],
+                            cu_seqlens=np.arange(d["n_seq"] + 1) * T, **okw)
+    check(o, oo, TOL[torch.bfloat16], "o")
+    check(ST, So, TOL[torch.bfloat16], "S_T")
+    oh = o.double().cpu().numpy()
+    worst = 0.0
+    for n in range(d["n_seq"]):
         sl = slice(n * T, (n + 1) * T)
-        pk = lambda t: t[sl, h:h + 1]
-        okw = dict(kw)
-        if "pos_offset" in okw:
-            okw["pos_offset"] = pos[n:n + 1].numpy()
-        oo, So = oracle.prefill(pk(d["q"]), pk(d["k"]), pk(d["v"]), pk(d["g"]), pk(d["eta"]),
-                                d["eps"], S0=d["S0"][n:n + 1, h:h + 1],
-                                cu_seqlens=np.array([0, T]), **okw)
-        print(f"sequence {n}, head {h}", flush=True)
-        check(o[sl, h:h + 1], oo, TOL[torch.bfloat16], "o")
-        check(ST[n:n + 1, h:h + 1], So, TOL[torch.bfloat16], "S_T")
+        for h in range(d["q"].shape[1]):
+            worst = max(worst, err(oh[sl, h], oo[sl, h]), err(ST[n, h], So[n, h]))
+    print(f"  worst per-(sequence, head) err {worst:.3e}", flush=True)
+    assert worst < TOL[torch.bfloat16]
