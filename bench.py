@@ -68,6 +68,18 @@ def csrc_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def measured_traffic():
     """HBM bytes per scan launch from the committed rocprofv3 counter summary, or None if
     the kernels changed since the counters were taken."""
@@ -154,6 +166,15 @@ def main():
         e_end.record()
         torch.cuda.synchronize()
         ms = e_start.elapsed_time(e_end) / steps
+        # the same calls timed one by one (an event pair around each), for the median and min
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            evc[i][0].record()
+            whole(sets[i % len(sets)])
+            evc[i][1].record()
+        torch.cuda.synchronize()
+        per_call = sorted(e[0].elapsed_time(e[1]) for e in evc)
+        calls = {"median_ms": per_call[len(per_call) // 2], "min_ms": per_call[0]}
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         for i in range(steps):
             s = sets[i % len(sets)]
@@ -166,8 +187,8 @@ def main():
         torch.cuda.synchronize()
         prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
         if meta.get("two_level"):
-            return ms, prep, ms - prep
-        return ms, prep, sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+            return ms, prep, ms - prep, calls
+        return ms, prep, sum(e[1].elapsed_time(e[2]) for e in ev) / steps, calls
 
     def make_set(inp, dev, ws_bytes, dtype):
         n_tok, H, dk = inp["q"].shape
@@ -190,7 +211,7 @@ def main():
         two_level = inp["cu_seqlens"] is None and ws_b != kla.kla_prefill_workspace_bytes(
             inp["n_seq"], n_tok, H_, dk_, dv_, wl.dtype, scan_segments=1)
         meta = {"n_seq": inp["n_seq"], "d_v": dv_, "eps": inp["eps"], "two_level": two_level}
-        ms, prep, scan = time_prefill([s], meta, steps, warmup)
+        ms, prep, scan, _ = time_prefill([s], meta, steps, warmup)
         nb, nf = prefill_bytes_flops(n_tok, inp["n_seq"], H_, dk_, dv_, es)
         out = {"workload": wl.name, "tokens": n_tok, "ms_per_call": ms, "prep_ms": prep,
                "scan_ms": scan, "scan": "two-level" if two_level else "sequential",
@@ -218,7 +239,33 @@ def main():
                              "tokens_per_s": inp["n_seq"] / (dms * 1e-3),
                              "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                              "note": "state of 16.8 MB stays in the last-level cache"}
-            del dd, S
+            # the same steps captured once into a HIP graph and replayed (no per-call host
+            # work): what a serving loop gets at this small batch, where launches dominate
+            S.copy_(s["S_T"])
+
+            def loop():
+                for i in range(nd):
+                    kla.kla_decode_step(dd["q"][i], dd["k"][i], dd["v"][i], dd["g"][i],
+                                        dd["eta"][i], dd["eps"], S, o=od, inplace=True)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                loop()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                loop()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            gms = e0.elapsed_time(e1) / nd
+            out["decode"]["graph_ms_per_step"] = gms
+            out["decode"]["graph_tokens_per_s"] = inp["n_seq"] / (gms * 1e-3)
+            del graph, dd, S
         log(f"{wl.name}: {ms:.3f} ms/call (prep {prep:.3f}, scan {scan:.3f}), "
             f"{n_tok / (ms * 1e-3):.3e} tok/s")
         del inp, s
@@ -238,7 +285,7 @@ def main():
     K = args.steps
     log(f"timing {K} prefill steps")
     t0 = time.perf_counter()
-    ms_per_step, prep_ms, scan_ms = time_prefill(sets, {"n_seq": n_seq, "d_v": dv,
+    ms_per_step, prep_ms, scan_ms, call_stats = time_prefill(sets, {"n_seq": n_seq, "d_v": dv,
                                                         "eps": base["eps"]}, K, args.warmup)
     wall = time.perf_counter() - t0
     tok_per_s = n_tok / (ms_per_step * 1e-3)
@@ -464,7 +511,8 @@ def main():
         oracle.prefill(qc, kc, vc, gc, ec, base["eps"], S0=sc, cu_seqlens=cu)
         cpu_s = time.perf_counter() - t0
         cpu = {"value": n_tok / cpu_s, "unit": "tokens/s", "cores": oracle.max_threads(),
-               "kind": "oracle",
+               "kind": "oracle", "host_cpus": len(os.sched_getaffinity(0)),
+               "cpu_model": cpu_model(),
                "sample": f"the whole prefill workload ({n_seq} seq x {H} heads x "
                          f"{n_tok // n_seq} tokens, d=128) through the fp64 tokenwise oracle, "
                          f"{cpu_s:.2f} s wall"}
@@ -501,7 +549,10 @@ def main():
         "step": {"hbm_frac": step_gbs / PEAK_HBM_GBS, "mfma_frac": mfma_frac,
                  "algorithmic_bytes": prefill_bytes, "algorithmic_flops": flops_prefill,
                  "note": "prep + scan, the same algorithmic bytes and flops over the step time"},
-        "prefill": {"mfma_frac": mfma_frac, "prep_ms": prep_ms, "scan_ms": scan_ms},
+        "prefill": {"mfma_frac": mfma_frac, "prep_ms": prep_ms, "scan_ms": scan_ms,
+                    "call_ms_median": call_stats["median_ms"], "call_ms_min": call_stats["min_ms"],
+                    "call_note": "the same calls timed one by one (an event pair each); "
+                                 "ms_per_step is one event pair around all of them"},
         "workloads": others,
         "decode": {"workload": wd.name, "tokens_per_s": wd.n_seq / (dec_ms * 1e-3),
                    "ms_per_step": dec_ms, "steps": nd,
