@@ -37,7 +37,12 @@
  *     pass over the data): g finite and <= 0, eta finite (normally in (0, 1]),
  *     no NaN/Inf in q, k, v, S0 (NaN propagates).
  *   - The library is stateless and thread-safe; concurrent calls on different
- *     streams are independent provided their buffers do not overlap.
+ *     streams are independent provided their buffers do not overlap
+ *     (kla_prefill_chunked_noalloc aside: its scratch is one static array per GPU).
+ *   - A call enqueues kernels only (no allocation, memset, copy or host
+ *     synchronisation), so it may be captured into a HIP graph on `stream` and
+ *     replayed; the captured pointers, sizes and scalars are fixed, and the
+ *     buffers behind them must stay alive while the graph is in use.
  */
 #ifndef KLA_H_
 #define KLA_H_
