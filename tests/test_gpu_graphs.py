@@ -113,3 +113,46 @@ def test_prefill_graph_replay(kla, segments):
         print(f"replay {rep}", flush=True)
         assert torch.equal(o, oe), f"replay {rep}: o differs"
         assert torch.equal(ST, Se), f"replay {rep}: S_T differs"
+
+
+def test_noalloc_prefill_graph_replay(kla):
+    """The allocation-free prefill entry point (its scratch a static array per GPU) captured into
+    a graph on packed input with a ragged tail, replayed three times on new inputs; each
+    replay against an eager call of the same entry point on the same inputs."""
+    import ctypes
+    lib = kla.load_library()
+    lens, H, dk, dv = (700, 0, 1300, 64, 333), 4, 128, 128
+    n_seq, n_tok = len(lens), sum(lens)
+
+    def draw(seed):
+        w = ki.Workload(seed, "graph-noalloc", n_seq, H, dk, dv, torch.bfloat16, lens=lens,
+                        s0_var=0.01)
+        return ki.prefill_inputs(w)
+
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in draw(71).items()}
+    o = torch.empty(n_tok, H, dv, dtype=torch.bfloat16, device=DEV)
+    ST = torch.empty(n_seq, H, dk, dv, dtype=torch.float32, device=DEV)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def call(out, st):
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        rc = lib.kla_prefill_chunked_noalloc(
+            p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]), p(d["eta"]), d["eps"], p(d["S0"]),
+            p(out), p(st), p(d["cu_seqlens"]), None, n_seq, n_tok, H, dk, dv, 1, None, stream)
+        assert rc == 0, lib.kla_last_error().decode()
+
+    graph = capture(lambda: call(o, ST))
+    for rep in range(3):
+        new = draw(7100 + rep)
+        for name in ("q", "k", "v", "g", "eta", "S0"):
+            d[name].copy_(new[name])
+        oe, Se = torch.empty_like(o), torch.empty_like(ST)
+        call(oe, Se)
+        torch.cuda.synchronize()
+        o.zero_()
+        ST.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"replay {rep}", flush=True)
+        assert torch.equal(o, oe), f"replay {rep}: o differs"
+        assert torch.equal(ST, Se), f"replay {rep}: S_T differs"
