@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the KLA forward hot path on one MI355X (prints ONE JSON line).
 
-A step is one chunkwise prefill (plan + prep/UT kernel, then the chunk-scan kernel
+A step is one chunkwise prefill (the prep/UT kernel, then the chunk-scan kernel
 with the fused output) over the layer-scale workload: B=4 sequences, H=16 heads,
 T=4096 tokens, d_k=d_v=128, bf16 q/k/v, fp32 g/eta/state, chunk 64, random S0.
 ``value`` is prefill tokens/s over the timed steps.  Four copies of the inputs and
@@ -13,11 +13,14 @@ decode workload (B=256, H=16, d=128, fp32 state from N(0, 0.05), 512 consecutive
 in-place steps with fresh bf16 q/k/v and fp32 g/eta per step), and times the fp64
 CPU oracle on the host cores as a reported baseline.
 
-Per-kernel durations come from HIP events recorded on the launch stream inside the
-timed loop: the prefill is issued as its two halves (kla_prefill_prepare, then
-kla_prefill_scan), which is exactly what kla_prefill_chunked enqueues.
+Per-kernel durations come from HIP events recorded on the launch stream in a pass right
+after the timed loop, over the same rotating inputs: each call issued as its two halves
+(kla_prefill_prepare, then kla_prefill_scan, exactly what kla_prefill_chunked enqueues)
+with an event before, between and after them.  A third pass times the same calls one by
+one (an event pair each) for the median and minimum call time.
 
-Algorithmic work (per token-head, C = 64; the survey's minimum for the chunkwise method):
+Algorithmic work (per token-head, C = 64; the minimum any chunkwise implementation moves and
+multiplies):
   prefill bytes      = 2 (2 d_k + d_v) e + 8 + 2 d_v e        (q, k, v, g, eta read; o written)
                        + 8 d_k d_v per (sequence, head)        (S0 read, S_T written), e = 2 (bf16)
                      = 1064 B per token-head on the layer workload (d = 128, T = 4096)
@@ -129,7 +132,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     def prefill_bytes_flops(n_tok, n_seq, H, dk, dv, es):
-        """The survey's algorithmic bytes and MFMA flops of one prefill call."""
+        """The algorithmic bytes and MFMA flops of one prefill call (the formulas above)."""
         th = n_tok * H
         nb = th * (es * (2 * dk + dv) + 8 + es * dv) + 2 * n_seq * H * dk * dv * 4
         nf = th * (6 * dk * dv + (CHUNK - 1) * dk + (CHUNK + 1) * (2 * dk + 2 * dv))
