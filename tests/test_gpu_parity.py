@@ -415,18 +415,18 @@ def test_hard_projection_bf16_reads_back_values(kla):
     check(o, d["v"].double().cpu().numpy(), 2e-2, "o")
 
 
-def _config0_keys_hard_bf16(T, H, dk, dv):
-    """Config 0's draws (keys with norms 10^U(-1, 1)) in bf16, hard variant."""
-    w = ki.Workload(0, "c0-bf16", 1, H, dk, dv, torch.bfloat16, T=T)
+def _spread_keys_hard_bf16(T, H, dk, dv):
+    """The tiny workload's draws (keys with norms 10^U(-1, 1)) in bf16, hard variant."""
+    w = ki.Workload(0, "spread-bf16", 1, H, dk, dv, torch.bfloat16, T=T)
     return to_dev(ki.hard_variant(ki.prefill_inputs(w)))
 
 
 @pytest.mark.parametrize("T,H,dk,dv", [(256, 1, 64, 64), (300, 2, 128, 128)])
-def test_hard_projection_bf16_config0_keys_split_precision(kla, T, H, dk, dv):
+def test_hard_projection_bf16_spread_key_norms_split_precision(kla, T, H, dk, dv):
     """Theorem 1 on bf16 inputs with keys whose norms span 100x: with split precision (T R,
     P U and the state update on hi/lo bf16 operand pairs) o_t = v_t, and o matches the
     oracle."""
-    d = _config0_keys_hard_bf16(T, H, dk, dv)
+    d = _spread_keys_hard_bf16(T, H, dk, dv)
     o, _ = kla.kla_prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
                                    n_seq=1, precision="split")
     torch.cuda.synchronize()
@@ -439,8 +439,8 @@ def test_hard_projection_bf16_config0_keys_split_precision(kla, T, H, dk, dv):
                    "k S~ + e cancels terms of size ||k|| |S| down to |v|, and bf16 operands "
                    "(2^-9) leave a measured error of 0.10-0.20 against the 2e-2 bar; the split "
                    "precision mode holds it")
-def test_hard_projection_bf16_config0_keys_bf16_operands(kla):
-    d = _config0_keys_hard_bf16(300, 2, 128, 128)
+def test_hard_projection_bf16_spread_key_norms_bf16_operands(kla):
+    d = _spread_keys_hard_bf16(300, 2, 128, 128)
     o, _ = run_prefill(kla, d, S0=False)
     check(o, d["v"].double().cpu().numpy(), 2e-2, "o vs v")
 
