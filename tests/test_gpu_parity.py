@@ -288,6 +288,35 @@ def test_prefill_long_context_full(kla):
     check(ST, So, 2e-2, "ST")
 
 
+def test_prefill_beyond_2g_elements(kla):
+    """Packed input whose second sequence starts past element 2^31 of q, k, v and o
+    (1,048,768 + 200 tokens x 16 heads x d = 128, bf16, about 4.3 GB per token tensor): every
+    index into the token tensors, the workspace and the states must be 64-bit there.  The far
+    sequence's outputs and final state against the oracle, and the long sequence's last chunk
+    (also past element 2^31) against the oracle started from the state a device prefill of
+    the chunks before it leaves."""
+    L0, L1, H = 1048768, 200, 16
+    assert L0 * H * 128 > 2 ** 31
+    w = ki.Workload(98, "far", 2, H, 128, 128, torch.bfloat16, lens=(L0, L1), s0_var=0.01)
+    d = ki.prefill_inputs(w, device=DEV)
+    o, ST = run_prefill(kla, d)
+    sl = slice(L0, L0 + L1)
+    cpu = lambda t: t[sl].cpu()
+    oo, So = oracle.prefill(cpu(d["q"]), cpu(d["k"]), cpu(d["v"]), cpu(d["g"]), cpu(d["eta"]),
+                            d["eps"], S0=d["S0"][1:2].cpu())
+    check(o[sl], oo, 2e-2, "o, far sequence")
+    check(ST[1:2], So, 2e-2, "S_T, far sequence")
+    head = slice(0, L0 - 64)
+    _, S_mid = kla.kla_prefill_chunked(d["q"][head], d["k"][head], d["v"][head], d["g"][head],
+                                       d["eta"][head], d["eps"], S0=d["S0"][0:1], n_seq=1)
+    tail = slice(L0 - 64, L0)
+    ct = lambda t: t[tail].cpu()
+    ot, St = oracle.prefill(ct(d["q"]), ct(d["k"]), ct(d["v"]), ct(d["g"]), ct(d["eta"]),
+                            d["eps"], S0=S_mid.cpu())
+    check(o[tail], ot, 2e-2, "o, long sequence's last chunk")
+    check(ST[0:1], St, 2e-2, "S_T, long sequence")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("n_seq,T,H,dk,dv,G,S0,weak", [
     (1, 64 * 9 + 13, 2, 128, 128, 3, True, False),   # ragged last segment
