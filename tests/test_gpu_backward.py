@@ -104,6 +104,32 @@ def test_backward_strong_decay(kla):
     run_case(kla, inp, ct, TOL[torch.float32])
 
 
+def test_backward_beyond_2g_elements(kla):
+    """Packed input whose second sequence starts past element 2^31 of q, k, v, dO and the
+    gradients (8,388,736 + 200 tokens x 2 heads x d = 128, bf16): the far sequence's
+    gradients against the oracle (sequences are independent)."""
+    L0, L1, H = 8388736, 200, 2
+    assert L0 * H * 128 > 2 ** 31
+    w = ki.Workload(99, "far", 2, H, 128, 128, torch.bfloat16, lens=(L0, L1), s0_var=0.01)
+    inp = ki.prefill_inputs(w, device=DEV)
+    ct = ki.cotangents(inp, seed=4242, device=DEV)
+    grads = kla.kla_prefill_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["eta"],
+                                     inp["eps"], ct["dO"], S0=inp["S0"], dS_T=ct["dS_T"],
+                                     cu_seqlens=inp["cu_seqlens"], n_seq=2)
+    torch.cuda.synchronize()
+    sl = slice(L0, L0 + L1)
+    f64 = lambda t: t.double().cpu().numpy()
+    pick = lambda t: f64(t[sl])
+    ref = ob.prefill_backward(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), pick(inp["g"]),
+                              pick(inp["eta"]), inp["eps"], pick(ct["dO"]),
+                              S0=f64(inp["S0"][1:2]), dS_T=f64(ct["dS_T"][1:2]))
+    got = [x[sl] for x in grads[:5]] + [grads[5][1:2]]
+    for name, x, y in zip(NAMES, got, ref):
+        e = err(x, y)
+        print(f"  {name}: err {e:.3e} (bar {TOL[torch.bfloat16]:g})", flush=True)
+        assert e < TOL[torch.bfloat16], f"{name}: err {e:.3e}"
+
+
 def test_backward_full_workload_sampled(kla):
     inp = ki.prefill_inputs(1)
     ct = ki.cotangents(inp, seed=2024)

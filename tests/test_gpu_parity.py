@@ -131,6 +131,28 @@ def test_decode_from_prefill_built_32k_state(kla):
     check(S, Sd, 2e-2, "decode S")
 
 
+def test_decode_state_beyond_2g_elements(kla):
+    """131,200 (sequence, head) items of d = 128 (an 8.6 GB fp32 state, 2^31 elements end
+    inside item 131,072), two in-place steps: the last 64 items against the oracle."""
+    B, H = 8200, 16
+    assert B * H * 128 * 128 > 2 ** 31
+    w = ki.Workload(93, "decode-far", B, H, 128, 128, torch.bfloat16, T=1, s0_var=0.05,
+                    decode_steps=2)
+    d = ki.decode_inputs(w, device=DEV)
+    tail = slice(B - 4, B)  # 4 sequences x 16 heads
+    So = d["S"][tail].double().cpu().numpy()
+    S = d["S"]
+    for t in range(2):
+        o, S = kla.kla_decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["eta"][t],
+                                   d["eps"], S, inplace=True)
+        cpu = lambda x: x[t][tail].cpu()
+        oo, So = oracle.decode(cpu(d["q"]), cpu(d["k"]), cpu(d["v"]), cpu(d["g"]),
+                               cpu(d["eta"]), d["eps"], So)
+        torch.cuda.synchronize()
+        check(o[tail], oo, 2e-2, "o, last items")
+        check(S[tail], So, 2e-2, "S, last items")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_decode_many_items(kla, dtype):
     """6144 (sequence, head) items: the launch shape with one 512-lane workgroup per item (the
