@@ -689,12 +689,13 @@ void kla_scan_kernel(
         const bool fl = c >= 1, is = c + DIST < nchunks;
         if (fl) p_flush(c - 1, sm.slot[(c - 1) % NSLOT]);
         if (is) p_issue(c + DIST, sm.slot[(c + DIST) % NSLOT]);
-        // chunk c + 1 must be in LDS before the barrier that starts it; what was issued
-        // after its loads (this step's stores and loads) may stay in flight
+        // chunk c + 1 must be in LDS before the barrier that starts it; this step's chunk
+        // c + 2 loads may stay in flight.  The vector-memory counter returns loads in order
+        // among themselves but not relative to stores: a store issued after chunk c + 1's
+        // loads can complete before them.  So the count left outstanding is the later loads
+        // alone (pending stores only make the wait stricter), never loads plus stores.
         if (DIST == 2) {
-          if (fl && is) wait_vmcnt<NST + DP::PER_WAVE>();
-          else if (is) wait_vmcnt<DP::PER_WAVE>();
-          else if (fl) wait_vmcnt<NST>();
+          if (is) wait_vmcnt<DP::PER_WAVE>();
           else wait_vmcnt<0>();
         } else {
           wait_vmcnt<0>();
