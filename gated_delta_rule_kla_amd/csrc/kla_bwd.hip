@@ -1093,14 +1093,11 @@ static hipError_t launch_adjoint_t(int d_v, const void *q, const void *k, const 
   if constexpr (sizeof(Tin) == 2) {
     const size_t sm16 = sizeof(AdjSmem16<DK>);
     static_assert(sizeof(AdjSmem16<DK>) <= 160 * 1024, "LDS budget");
-    static bool attr16 = false;  // benign race: every thread sets the same value
-    if (!attr16) {
-      hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void *>(&kla_bwd_scan16_kernel<DK, DIAG>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm16);
-      if (e != hipSuccess) return e;
-      attr16 = true;
-    }
+  static std::atomic<bool> attr16[kMaxDeviceOrdinals];
+  if (hipError_t ea = set_lds_limit_once(
+          reinterpret_cast<const void *>(&kla_bwd_scan16_kernel<DK, DIAG>), (int)sm16, attr16);
+      ea != hipSuccess)
+    return ea;
     hipLaunchKernelGGL((kla_bwd_scan16_kernel<DK, DIAG>), dim3((unsigned)scan_blocks),
                        dim3(kAdjThreads), sm16, stream, qt, kt, static_cast<const Tin *>(dO), GD,
                        static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
@@ -1109,14 +1106,11 @@ static hipError_t launch_adjoint_t(int d_v, const void *q, const void *k, const 
   } else {
     const size_t smA = sizeof(AdjSmem<DK>);
     static_assert(sizeof(AdjSmem<DK>) <= 160 * 1024, "LDS budget");
-    static bool attr = false;  // benign race: every thread sets the same value
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void *>(&kla_bwd_scan_kernel<Tin, DK, DIAG>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smA);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
+  static std::atomic<bool> attr[kMaxDeviceOrdinals];
+  if (hipError_t ea = set_lds_limit_once(
+          reinterpret_cast<const void *>(&kla_bwd_scan_kernel<Tin, DK, DIAG>), (int)smA, attr);
+      ea != hipSuccess)
+    return ea;
     hipLaunchKernelGGL((kla_bwd_scan_kernel<Tin, DK, DIAG>), dim3((unsigned)scan_blocks),
                        dim3(kAdjThreads), smA, stream, qt, kt, static_cast<const Tin *>(dO), GD,
                        static_cast<const Tin *>(T), static_cast<const Tin *>(P), dST, dS0,
@@ -1149,13 +1143,11 @@ static hipError_t launch_bwd_t(int d_v, const void *q, const void *k, const void
   if (e != hipSuccess) return e;
   const size_t smG = sizeof(GradSmem<Tin, DK>);
   static_assert(sizeof(GradSmem<Tin, DK>) <= 160 * 1024, "LDS budget");
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_bwd_grad_kernel<Tin, DK>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smG);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> attr_set[kMaxDeviceOrdinals];
+  if (hipError_t ea = set_lds_limit_once(
+          reinterpret_cast<const void *>(&kla_bwd_grad_kernel<Tin, DK>), (int)smG, attr_set);
+      ea != hipSuccess)
+    return ea;
   const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
   const int64_t grad_blocks = n_chunks_ub * H;
   if (grad_blocks > 0)

@@ -646,14 +646,11 @@ static hipError_t launch_grad_diag_t(int d_v, const void *q, const void *k, cons
                                      int64_t n_chunks_ub, int32_t H, hipStream_t stream) {
   const size_t smG = sizeof(GradDiagSmem<Tin, DK>);
   static_assert(sizeof(GradDiagSmem<Tin, DK>) <= 160 * 1024, "LDS budget");
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_bwd_grad_diag_kernel<Tin, DK>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smG);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> attr_set[kMaxDeviceOrdinals];
+  if (hipError_t ea = set_lds_limit_once(
+          reinterpret_cast<const void *>(&kla_bwd_grad_diag_kernel<Tin, DK>), (int)smG, attr_set);
+      ea != hipSuccess)
+    return ea;
   const int64_t blocks = n_chunks_ub * H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;

@@ -537,14 +537,11 @@ static hipError_t launch_prep_diag_t(const void *q, const void *k, const float *
                                      hipStream_t stream) {
   const size_t smem = sizeof(DiagSmem<DK>);
   static_assert(sizeof(DiagSmem<DK>) <= 80 * 1024, "two workgroups to a compute unit");
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&kla_prep_diag_kernel<Tin, DK>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> attr_set[kMaxDeviceOrdinals];
+  if (hipError_t ea = set_lds_limit_once(
+          reinterpret_cast<const void *>(&kla_prep_diag_kernel<Tin, DK>), (int)smem, attr_set);
+      ea != hipSuccess)
+    return ea;
   const int64_t blocks = n_chunks_ub * H;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;

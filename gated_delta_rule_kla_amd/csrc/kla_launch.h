@@ -5,11 +5,30 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kla_device.h"
 
 namespace kla {
 
 enum class Dtype { F32 = 0, BF16 = 1 };
+
+// Raises kernel `fn`'s dynamic LDS limit to `bytes` on the current device, once per device
+// (the attribute belongs to the device's copy of the kernel).  `done` is the launcher's own
+// table of flags, one per device ordinal; concurrent first calls both set the same value.
+constexpr int kMaxDeviceOrdinals = 64;
+inline hipError_t set_lds_limit_once(const void *fn, int bytes,
+                                     std::atomic<bool> (&done)[kMaxDeviceOrdinals]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDeviceOrdinals && done[dev].load(std::memory_order_acquire))
+    return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDeviceOrdinals)
+    done[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 // Sequence tables the plan kernel writes into the workspace:
 //   cu[n]        sanitised token offset of sequence n (n = 0..n_seq)

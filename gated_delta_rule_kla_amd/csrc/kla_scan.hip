@@ -760,14 +760,11 @@ static hipError_t launch_scan_s(int DVs, int64_t units, const void *q, const voi
                     offsetof(SLT, gamO) == offsetof(SLT, gam) + 512,
                 "the decay block is fetched as one contiguous 768-byte piece");
   const size_t smem = sizeof(SMT);
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP, DIAG, STATES, MODE, SPLIT>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<bool> attr_set[kMaxDeviceOrdinals];
+  if (hipError_t ea = set_lds_limit_once(
+          reinterpret_cast<const void *>(&kla_scan_kernel<Tin, DK, SHP, DIAG, STATES, MODE, SPLIT>), (int)smem, attr_set);
+      ea != hipSuccess)
+    return ea;
   const int64_t blocks = units * H * (DVs / SHP::BV);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
