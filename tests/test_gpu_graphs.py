@@ -156,3 +156,41 @@ def test_noalloc_prefill_graph_replay(kla):
         print(f"replay {rep}", flush=True)
         assert torch.equal(o, oe), f"replay {rep}: o differs"
         assert torch.equal(ST, Se), f"replay {rep}: S_T differs"
+
+
+@pytest.mark.parametrize("diag", [False, True])
+def test_backward_graph_replay(kla, diag):
+    """The backward pass (2 sequences x 640 tokens x 2 heads, d = 128, bf16; scalar or
+    per-channel gate) captured with its outputs and workspace allocated inside the capture
+    (torch's graph pool), replayed three times on new inputs and cotangents; every gradient
+    against an eager call on the same inputs bit for bit."""
+    n_seq, T, H = 2, 640, 2
+    base = ki.prefill_inputs(1, T=T, n_seq=n_seq, H=H, diag=diag)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in base.items()}
+    ct = {k: v.to(DEV) for k, v in ki.cotangents(base, seed=900).items()}
+    out = {}
+
+    def call():
+        return kla.kla_prefill_backward(d["q"], d["k"], d["v"], d["g"], d["eta"], d["eps"],
+                                        ct["dO"], S0=d["S0"], dS_T=ct["dS_T"], n_seq=n_seq)
+
+    def captured():
+        out["grads"] = call()
+
+    graph = capture(captured)
+    for rep in range(3):
+        new = ki.prefill_inputs(1, T=T, n_seq=n_seq, H=H, diag=diag, seed=6000 + rep)
+        for name in ("q", "k", "v", "g", "eta", "S0"):
+            d[name].copy_(new[name])
+        nct = ki.cotangents(new, seed=6100 + rep)
+        ct["dO"].copy_(nct["dO"])
+        ct["dS_T"].copy_(nct["dS_T"])
+        ref = [x.clone() for x in call()]
+        torch.cuda.synchronize()
+        for x in out["grads"]:
+            x.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"replay {rep}", flush=True)
+        for name, x, y in zip(("dq", "dk", "dv", "dg", "deta", "dS0"), out["grads"], ref):
+            assert torch.equal(x, y), f"replay {rep}: {name} differs"
