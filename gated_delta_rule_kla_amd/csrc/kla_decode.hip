@@ -118,11 +118,26 @@ __global__ __launch_bounds__(NT) void kla_decode_kernel(
   }
 }
 
-// Launch shape by the number of (sequence, head) items: below kDecodeSplitBelow, two 128-lane
-// workgroups per item, so that there are enough workgroups to keep HBM busy; from there on, one
-// 512-lane workgroup per item.  Both measured best on their side of the threshold
-// (256 x 16 items: 5.64 TB/s; 512 x 16 items: 5.79 TB/s).
+// Launch shape by the number of (sequence, head) items: below kDecodeSplitBelow, several
+// 128-lane workgroups per item, so that there are enough workgroups to keep HBM busy (four of
+// 128-byte row pieces where d_k = 128 and d_v >= 128, else two); from there on, one 512-lane
+// workgroup per item.  Measured on 256 x 16 items at d = 128: four 5.67-5.69 TB/s, two
+// 5.61-5.64 (5.73 against 5.54 under diagonal gating); four is slower at d_k = 64 and collapses
+// at d_v = 64 (64-byte pieces); 512 x 16 items and up, one workgroup: 5.79 TB/s.
 constexpr int64_t kDecodeSplitBelow = 5120;
+
+template <typename Tin, int DK, int DV, int NS, int NT>
+static void launch_decode_shape(int64_t units, const Tin *qt, const Tin *kt, const Tin *vt,
+                                const float *g, const float *eta, float eps,
+                                const CoefOpts &opts, int32_t H, const float *S, Tin *ot,
+                                float *S_new, hipStream_t stream) {
+  if (opts.diag_gate)
+    hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, NS, NT, true>), dim3((unsigned)units),
+                       dim3(NT), 0, stream, qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
+  else
+    hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, NS, NT, false>), dim3((unsigned)units),
+                       dim3(NT), 0, stream, qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
+}
 
 template <typename Tin, int DK, int DV>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
@@ -131,27 +146,20 @@ static hipError_t launch_decode_t(const void *q, const void *k, const void *v, c
                                   int32_t H, hipStream_t stream) {
   const int64_t items = (int64_t)batch * H;
   if (items <= 0) return hipSuccess;
-  if (2 * items > 0x7fffffff) return hipErrorInvalidValue;  // grid size
+  // grid: items workgroups from kDecodeSplitBelow items on, at most 4 x kDecodeSplitBelow below
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
   const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
   const Tin *vt = static_cast<const Tin *>(v);
   Tin *ot = static_cast<Tin *>(o);
-  const bool small = items < kDecodeSplitBelow;
-  const dim3 grid((unsigned)(small ? 2 * items : items)), block(small ? 128 : 512);
-  if (opts.diag_gate) {
-    if (small)
-      hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 2, 128, true>), grid, block, 0, stream,
-                         qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
-    else
-      hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 1, 512, true>), grid, block, 0, stream,
-                         qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
-  } else {
-    if (small)
-      hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 2, 128, false>), grid, block, 0, stream,
-                         qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
-    else
-      hipLaunchKernelGGL((kla_decode_kernel<Tin, DK, DV, 1, 512, false>), grid, block, 0, stream,
-                         qt, kt, vt, g, eta, eps, opts, H, S, ot, S_new);
-  }
+  if (items >= kDecodeSplitBelow)
+    launch_decode_shape<Tin, DK, DV, 1, 512>(items, qt, kt, vt, g, eta, eps, opts, H, S, ot,
+                                             S_new, stream);
+  else if constexpr (DK == 128 && DV >= 128)
+    launch_decode_shape<Tin, DK, DV, 4, 128>(4 * items, qt, kt, vt, g, eta, eps, opts, H, S, ot,
+                                             S_new, stream);
+  else
+    launch_decode_shape<Tin, DK, DV, 2, 128>(2 * items, qt, kt, vt, g, eta, eps, opts, H, S, ot,
+                                             S_new, stream);
   return hipGetLastError();
 }
 
