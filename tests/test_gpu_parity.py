@@ -156,8 +156,8 @@ def test_decode_state_beyond_2g_elements(kla):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_decode_many_items(kla, dtype):
     """6144 (sequence, head) items: the launch shape with one 512-lane workgroup per item (the
-    smaller cases above take two 128-lane workgroups per item).  Every output and state
-    element against the oracle."""
+    smaller cases above take four 128-lane workgroups per item at d_k = 128 and d_v >= 128,
+    two otherwise).  Every output and state element against the oracle."""
     w = ki.Workload(91, "decode-many", 64, 96, 64, 128, dtype, T=1, s0_var=0.05, decode_steps=2)
     d = to_dev(ki.decode_inputs(w))
     S = d["S"].clone()
