@@ -118,12 +118,13 @@ __global__ __launch_bounds__(NT) void kla_decode_kernel(
   }
 }
 
-// Launch shape by the number of (sequence, head) items: below kDecodeSplitBelow, several
-// 128-lane workgroups per item, so that there are enough workgroups to keep HBM busy (four of
-// 128-byte row pieces where d_k = 128 and d_v >= 128, else two); from there on, one 512-lane
-// workgroup per item.  Measured on 256 x 16 items at d = 128: four 5.67-5.69 TB/s, two
-// 5.61-5.64 (5.73 against 5.54 under diagonal gating); four is slower at d_k = 64 and collapses
-// at d_v = 64 (64-byte pieces); 512 x 16 items and up, one workgroup: 5.79 TB/s.
+// Launch shape.  Where d_k = 128 and d_v >= 128: four 128-lane workgroups per (sequence,
+// head) item, each taking a quarter of the columns (128-byte row pieces).  Elsewhere, by the
+// number of items: below kDecodeSplitBelow two 128-lane workgroups per item, so that there are
+// enough workgroups to keep HBM busy, from there on one 512-lane workgroup per item.  Measured
+// at d = 128: 256 x 16 items, four 5.80 TB/s against two 5.64 (5.73 against 5.54 under
+// diagonal gating); 512 x 16 and 1024 x 16 items, four 5.74-5.81 against one 5.67-5.74 (two of
+// 256 lanes: 5.56-5.66).  Four are slower at d_k = 64 and collapse at d_v = 64 (64-byte pieces).
 constexpr int64_t kDecodeSplitBelow = 5120;
 
 template <typename Tin, int DK, int DV, int NS, int NT>
@@ -146,16 +147,19 @@ static hipError_t launch_decode_t(const void *q, const void *k, const void *v, c
                                   int32_t H, hipStream_t stream) {
   const int64_t items = (int64_t)batch * H;
   if (items <= 0) return hipSuccess;
-  // grid: items workgroups from kDecodeSplitBelow items on, at most 4 x kDecodeSplitBelow below
-  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  if (items > 0x7fffffff) return hipErrorInvalidValue;  // grid size of the widest shape
   const Tin *qt = static_cast<const Tin *>(q), *kt = static_cast<const Tin *>(k);
   const Tin *vt = static_cast<const Tin *>(v);
   Tin *ot = static_cast<Tin *>(o);
+  if constexpr (DK == 128 && DV >= 128) {
+    if (4 * items <= 0x7fffffff) {
+      launch_decode_shape<Tin, DK, DV, 4, 128>(4 * items, qt, kt, vt, g, eta, eps, opts, H, S,
+                                               ot, S_new, stream);
+      return hipGetLastError();
+    }
+  }
   if (items >= kDecodeSplitBelow)
     launch_decode_shape<Tin, DK, DV, 1, 512>(items, qt, kt, vt, g, eta, eps, opts, H, S, ot,
-                                             S_new, stream);
-  else if constexpr (DK == 128 && DV >= 128)
-    launch_decode_shape<Tin, DK, DV, 4, 128>(4 * items, qt, kt, vt, g, eta, eps, opts, H, S, ot,
                                              S_new, stream);
   else
     launch_decode_shape<Tin, DK, DV, 2, 128>(2 * items, qt, kt, vt, g, eta, eps, opts, H, S, ot,
